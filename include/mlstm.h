@@ -1,0 +1,164 @@
+/*
+ * mlstm.h -- C ABI of the MI355X (gfx950) mLSTM matrix-memory cell forward.
+ *
+ * The cell (xLSTM guide, aifetchly blog, "mLSTM: Matrix Key-Value Memory and
+ * Covariance Updates", recurrent formulation; stabiliser from "The Stabilizer
+ * State" of the same guide), per batch entry b and head h:
+ *
+ *   log f_t = logsigmoid(f~_t)         forget gate, carried in log space
+ *   i_t     = exp(i~_t)                exponential input gate
+ *   m_t     = max(log f_t + m_{t-1}, i~_t)
+ *   C~_t    = exp(log f_t + m_{t-1} - m_t) C~_{t-1} + exp(i~_t - m_t) v_t k_t^T
+ *   n~_t    = exp(log f_t + m_{t-1} - m_t) n~_{t-1} + exp(i~_t - m_t) k_t
+ *   h_t     = sigmoid(o~_t) * (C~_t q_t) / max(|n~_t . q_t|, exp(-m_t))
+ *
+ * which equals h_t = o_t * C_t q_t / max(|n_t . q_t|, 1) in true units
+ * (C = exp(m) C~, n = exp(m) n~). Keys are used as given: any 1/sqrt(d_qk)
+ * scaling belongs to the caller's key projection.
+ *
+ * Conventions for every entry point:
+ *  - All pointers are DEVICE pointers (hipMalloc / torch CUDA tensors) unless
+ *    said otherwise; all arrays are contiguous, row-major, 16-byte aligned.
+ *  - q, k: [B, H, T, d_qk]; v, o_pre, h: [B, H, T, d_v], all of `dtype`.
+ *    i_pre, f_pre: [B, H, T] float32 (gate PREactivations).
+ *  - State: C [B, H, d_v, d_qk] float32 (the pages' orientation C = v k^T,
+ *    row index = value dimension), n [B, H, d_qk] float32, m [B, H] float32,
+ *    all in stabilised units (C~, n~, m).
+ *  - The caller owns every buffer and the stream. The library never
+ *    allocates or frees memory and never synchronises; work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the null stream) and errors of the
+ *    asynchronous execution surface at the caller's next synchronisation.
+ *  - Return value: MLSTM_OK (0) or a negative mlstm_status. Argument checks
+ *    run on the host before anything is enqueued; on an error nothing is
+ *    enqueued. mlstm_last_error() describes the most recent error of the
+ *    calling thread.
+ */
+#ifndef MLSTM_H_
+#define MLSTM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLSTM_ABI_VERSION 1
+
+typedef enum mlstm_status {
+  MLSTM_OK = 0,
+  MLSTM_ERR_NULLPTR = -1,      /* a required pointer is NULL */
+  MLSTM_ERR_BAD_SHAPE = -2,    /* a size is negative/zero where it must not be, or not a supported multiple */
+  MLSTM_ERR_BAD_DTYPE = -3,    /* dtype is neither MLSTM_FP32 nor MLSTM_BF16 */
+  MLSTM_ERR_MISALIGNED = -4,   /* a pointer is not 16-byte aligned */
+  MLSTM_ERR_ALIAS = -5,        /* an output overlaps an input or another output */
+  MLSTM_ERR_WORKSPACE = -6,    /* workspace NULL or smaller than the size query returns */
+  MLSTM_ERR_UNSUPPORTED = -7,  /* valid but outside what this build implements (e.g. d_qk) */
+  MLSTM_ERR_HIP = -8           /* the HIP runtime reported an error at launch */
+} mlstm_status;
+
+typedef enum mlstm_dtype {
+  MLSTM_FP32 = 0,  /* float32 inputs/outputs, float32 MFMA (16x16x4) arithmetic */
+  MLSTM_BF16 = 1   /* bfloat16 inputs/outputs, bf16 MFMA (16x16x32) with float32 accumulation */
+} mlstm_dtype;
+
+/* Arguments of a full-sequence forward (chunkwise or parallel form). */
+typedef struct mlstm_fwd_args {
+  int64_t B, H, T;        /* batch, heads, tokens; B, H >= 1, T >= 0 */
+  int64_t d_qk, d_v;      /* head dims: d_qk in {64, 128, 256} (fp32: {64, 128}); d_v a multiple of 64 */
+  int32_t dtype;          /* mlstm_dtype of q, k, v, o_pre, h */
+  const void* q;          /* [B,H,T,d_qk] */
+  const void* k;          /* [B,H,T,d_qk] */
+  const void* v;          /* [B,H,T,d_v]  */
+  const void* o_pre;      /* [B,H,T,d_v]  output-gate preactivation */
+  const float* i_pre;     /* [B,H,T]      input-gate preactivation */
+  const float* f_pre;     /* [B,H,T]      forget-gate preactivation */
+  void* h;                /* [B,H,T,d_v]  output (written) */
+  const float* C0;        /* optional initial state [B,H,d_v,d_qk]; NULL = zero state */
+  const float* n0;        /* [B,H,d_qk]; required iff C0 != NULL */
+  const float* m0;        /* [B,H];      required iff C0 != NULL */
+  float* C_out;           /* optional final state [B,H,d_v,d_qk]; NULL = not written */
+  float* n_out;           /* [B,H,d_qk]; required iff C_out != NULL */
+  float* m_out;           /* [B,H];      required iff C_out != NULL */
+} mlstm_fwd_args;
+
+/*
+ * Chunkwise-parallel forward for full sequences (xLSTM guide, "Exploit
+ * Chunkwise Hardware Kernels for Production Training": sequences split into
+ * chunks; dense matrix products inside a chunk, the state passed between
+ * chunks). `chunk` is the number of tokens between stored states: a multiple
+ * of 64 in [64, 8192]; T need not be a multiple of it (the last chunk is
+ * ragged). Kernels: gate prefix sums, the inter-chunk state pass (carries C~,
+ * n~, m across chunks in float32 and stores each chunk's start state), and the
+ * intra-chunk output kernel (decay-masked Q K^T, P V and the carried-state
+ * term on MFMA). The workspace holds the per-chunk start states (bf16 for
+ * MLSTM_BF16, float32 for MLSTM_FP32) and per-token gate prefix sums; its size
+ * comes from mlstm_fwd_chunkwise_workspace_size(). Outputs must not overlap
+ * inputs, each other or the workspace.
+ */
+size_t mlstm_fwd_chunkwise_workspace_size(const mlstm_fwd_args* args, int chunk);
+int mlstm_fwd_chunkwise(const mlstm_fwd_args* args, int chunk, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Parallel (dual, quadratic) form for short sequences (xLSTM guide, "The
+ * Dual Formulation": decay matrix log D_tj = sum_{l=j+1..t} log f_l + i~_j
+ * for j <= t; H~ = (D o Q K^T) V divided row-wise by the same sum with V
+ * replaced by ones, floored at 1). Tiled over 64x64 key blocks with the exact
+ * row stabiliser computed from prefix maxima, so no T x T matrix is stored.
+ * 1 <= T <= 8192 (T = 0 is accepted and only copies/zeroes the state). The
+ * final state, if requested, comes from the state pass run as one chunk.
+ */
+size_t mlstm_fwd_parallel_workspace_size(const mlstm_fwd_args* args);
+int mlstm_fwd_parallel(const mlstm_fwd_args* args, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Arguments of one recurrent decode step. */
+typedef struct mlstm_step_args {
+  int64_t B, H;           /* B, H >= 1 */
+  int64_t d_qk, d_v;      /* d_qk a multiple of 64 in [64, 512]; d_v a multiple of 32 */
+  int32_t dtype;          /* mlstm_dtype of q, k, v, o_pre, h (state is always float32) */
+  const void* q;          /* [B,H,d_qk] */
+  const void* k;          /* [B,H,d_qk] */
+  const void* v;          /* [B,H,d_v]  */
+  const void* o_pre;      /* [B,H,d_v]  */
+  const float* i_pre;     /* [B,H] */
+  const float* f_pre;     /* [B,H] */
+  float* C;               /* [B,H,d_v,d_qk] state, updated IN PLACE */
+  const float* n_in;      /* [B,H,d_qk] state before the step */
+  const float* m_in;      /* [B,H]      state before the step */
+  float* n_out;           /* [B,H,d_qk] state after the step; must not overlap n_in (ping-pong) */
+  float* m_out;           /* [B,H]      state after the step; must not overlap m_in */
+  void* h;                /* [B,H,d_v]  output */
+} mlstm_step_args;
+
+/*
+ * One token of recurrent inference (xLSTM guide, recurrent formulation
+ * "Inference Mode"; constant memory per step). Reads and rewrites C once
+ * (bandwidth-bound); n and m are ping-ponged because every workgroup of a
+ * head reads the old n, m while one of them writes the new ones.
+ */
+int mlstm_step(const mlstm_step_args* args, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* mlstm_status_string(int status);
+/* Message of the calling thread's most recent error ("" if none). */
+const char* mlstm_last_error(void);
+/* MLSTM_ABI_VERSION of the loaded library. */
+int mlstm_abi_version(void);
+
+/*
+ * Profiling hook, not needed for computing. When `before` and `after` are
+ * non-NULL hipEvent_t handles, every later launch of kernel `kernel_id`
+ * (0 = gate prefix sums, 1 = inter-chunk state pass, 2 = intra-chunk output,
+ * 3 = decode step) is bracketed by hipEventRecord(before, stream) and
+ * hipEventRecord(after, stream) on the launch stream, until the hook is
+ * cleared by passing NULLs. Process-wide; not thread-safe.
+ */
+int mlstm_set_launch_events(int kernel_id, void* before, void* after);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLSTM_H_ */

@@ -1,1 +1,14 @@
-"""mLSTM matrix-memory cell forward on MI355X (gfx950): HIP kernels behind a C ABI."""
+"""mLSTM matrix-memory cell forward on MI355X (gfx950): HIP kernels behind a C ABI.
+
+The entry points mirror include/mlstm.h: mlstm_fwd_chunkwise (full
+sequences), mlstm_fwd_parallel (short sequences) and mlstm_step (recurrent
+decode). They take torch tensors for device memory and run only the HIP
+library; a missing library raises.
+"""
+from ._lib import (  # noqa: F401
+    MlstmError,
+    mlstm_fwd_chunkwise,
+    mlstm_fwd_parallel,
+    mlstm_step,
+    set_launch_events,
+)

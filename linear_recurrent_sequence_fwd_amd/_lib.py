@@ -1,0 +1,243 @@
+"""ctypes binding of libmlstm.so: the C ABI declared in include/mlstm.h.
+
+Argument marshalling only. Tensors supply device memory and the current
+stream; every step of the computation runs in the library's HIP kernels.
+If the library is missing the calls raise; there is no other code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_int, c_int32, c_int64, c_size_t, c_void_p, c_char_p
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmlstm.so")
+
+MLSTM_FP32, MLSTM_BF16 = 0, 1
+STATUS = {
+    0: "MLSTM_OK", -1: "MLSTM_ERR_NULLPTR", -2: "MLSTM_ERR_BAD_SHAPE", -3: "MLSTM_ERR_BAD_DTYPE",
+    -4: "MLSTM_ERR_MISALIGNED", -5: "MLSTM_ERR_ALIAS", -6: "MLSTM_ERR_WORKSPACE",
+    -7: "MLSTM_ERR_UNSUPPORTED", -8: "MLSTM_ERR_HIP",
+}
+KERNEL_IDS = {"gate": 0, "state": 1, "out": 2, "step": 3}
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", c_int64), ("H", c_int64), ("T", c_int64), ("d_qk", c_int64), ("d_v", c_int64),
+        ("dtype", c_int32),
+        ("q", c_void_p), ("k", c_void_p), ("v", c_void_p), ("o_pre", c_void_p),
+        ("i_pre", c_void_p), ("f_pre", c_void_p), ("h", c_void_p),
+        ("C0", c_void_p), ("n0", c_void_p), ("m0", c_void_p),
+        ("C_out", c_void_p), ("n_out", c_void_p), ("m_out", c_void_p),
+    ]
+
+
+class StepArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", c_int64), ("H", c_int64), ("d_qk", c_int64), ("d_v", c_int64), ("dtype", c_int32),
+        ("q", c_void_p), ("k", c_void_p), ("v", c_void_p), ("o_pre", c_void_p),
+        ("i_pre", c_void_p), ("f_pre", c_void_p),
+        ("C", c_void_p), ("n_in", c_void_p), ("m_in", c_void_p),
+        ("n_out", c_void_p), ("m_out", c_void_p), ("h", c_void_p),
+    ]
+
+
+class MlstmError(RuntimeError):
+    def __init__(self, code: int, what: str, detail: str):
+        super().__init__(f"{what} failed: {STATUS.get(code, code)}: {detail}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library with argument types set (loaded once)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m linear_recurrent_sequence_fwd_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        L.mlstm_fwd_chunkwise_workspace_size.argtypes = [P(FwdArgs), c_int]
+        L.mlstm_fwd_chunkwise_workspace_size.restype = c_size_t
+        L.mlstm_fwd_chunkwise.argtypes = [P(FwdArgs), c_int, c_void_p, c_size_t, c_void_p]
+        L.mlstm_fwd_chunkwise.restype = c_int
+        L.mlstm_fwd_parallel_workspace_size.argtypes = [P(FwdArgs)]
+        L.mlstm_fwd_parallel_workspace_size.restype = c_size_t
+        L.mlstm_fwd_parallel.argtypes = [P(FwdArgs), c_void_p, c_size_t, c_void_p]
+        L.mlstm_fwd_parallel.restype = c_int
+        L.mlstm_step.argtypes = [P(StepArgs), c_void_p]
+        L.mlstm_step.restype = c_int
+        L.mlstm_status_string.argtypes = [c_int]
+        L.mlstm_status_string.restype = c_char_p
+        L.mlstm_last_error.argtypes = []
+        L.mlstm_last_error.restype = c_char_p
+        L.mlstm_abi_version.argtypes = []
+        L.mlstm_abi_version.restype = c_int
+        L.mlstm_set_launch_events.argtypes = [c_int, c_void_p, c_void_p]
+        L.mlstm_set_launch_events.restype = c_int
+        _lib = L
+    return _lib
+
+
+def _check(code: int, what: str) -> None:
+    if code != 0:
+        raise MlstmError(code, what, lib().mlstm_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MLSTM_BF16
+    if t.dtype == torch.float32:
+        return MLSTM_FP32
+    raise TypeError(f"q/k/v/o_pre must be float32 or bfloat16, got {t.dtype}")
+
+
+def _require(t, name, shape, dtype):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fwd_args(q, k, v, o_pre, i_pre, f_pre, h, C0=None, n0=None, m0=None,
+             C_out=None, n_out=None, m_out=None) -> FwdArgs:
+    """Fill the argument struct of a forward call from tensors (shapes checked)."""
+    import torch
+    B, H, T, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    for name, t, shp in (("q", q, (B, H, T, K)), ("k", k, (B, H, T, K)), ("v", v, (B, H, T, V)),
+                         ("o_pre", o_pre, (B, H, T, V)), ("h", h, (B, H, T, V))):
+        _require(t, name, shp, dt)
+    _require(i_pre, "i_pre", (B, H, T), torch.float32)
+    _require(f_pre, "f_pre", (B, H, T), torch.float32)
+    if C0 is not None:
+        _require(C0, "C0", (B, H, V, K), torch.float32)
+        _require(n0, "n0", (B, H, K), torch.float32)
+        _require(m0, "m0", (B, H), torch.float32)
+    if C_out is not None:
+        _require(C_out, "C_out", (B, H, V, K), torch.float32)
+        _require(n_out, "n_out", (B, H, K), torch.float32)
+        _require(m_out, "m_out", (B, H), torch.float32)
+    return FwdArgs(B, H, T, K, V, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o_pre),
+                   _ptr(i_pre), _ptr(f_pre), _ptr(h), _ptr(C0), _ptr(n0), _ptr(m0),
+                   _ptr(C_out), _ptr(n_out), _ptr(m_out))
+
+
+def chunkwise_workspace_bytes(args: FwdArgs, chunk: int) -> int:
+    return int(lib().mlstm_fwd_chunkwise_workspace_size(ctypes.byref(args), chunk))
+
+
+def parallel_workspace_bytes(args: FwdArgs) -> int:
+    return int(lib().mlstm_fwd_parallel_workspace_size(ctypes.byref(args)))
+
+
+def _workspace(nbytes, device, workspace):
+    import torch
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace smaller than {nbytes} bytes")
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _state_out(q, v, want):
+    import torch
+    if not want:
+        return None, None, None
+    B, H, _, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    return (torch.empty((B, H, V, K), dtype=torch.float32, device=dev),
+            torch.empty((B, H, K), dtype=torch.float32, device=dev),
+            torch.empty((B, H), dtype=torch.float32, device=dev))
+
+
+def mlstm_fwd_chunkwise(q, k, v, o_pre, i_pre, f_pre, chunk=64, C0=None, n0=None, m0=None,
+                        return_state=False, h=None, workspace=None, stream=None):
+    """Chunkwise forward. Returns h, or (h, (C, n, m)) when return_state."""
+    import torch
+    if h is None:
+        h = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    C_out, n_out, m_out = _state_out(q, v, return_state)
+    args = fwd_args(q, k, v, o_pre, i_pre, f_pre, h, C0, n0, m0, C_out, n_out, m_out)
+    nbytes = chunkwise_workspace_bytes(args, chunk)
+    ws = _workspace(nbytes, q.device, workspace)
+    _check(lib().mlstm_fwd_chunkwise(ctypes.byref(args), int(chunk), _ptr(ws), nbytes, _stream(stream)),
+           "mlstm_fwd_chunkwise")
+    return (h, (C_out, n_out, m_out)) if return_state else h
+
+
+def mlstm_fwd_parallel(q, k, v, o_pre, i_pre, f_pre, C0=None, n0=None, m0=None,
+                       return_state=False, h=None, workspace=None, stream=None):
+    """Parallel (dual) form for T <= 8192. Returns h, or (h, (C, n, m))."""
+    import torch
+    if h is None:
+        h = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    C_out, n_out, m_out = _state_out(q, v, return_state)
+    args = fwd_args(q, k, v, o_pre, i_pre, f_pre, h, C0, n0, m0, C_out, n_out, m_out)
+    nbytes = parallel_workspace_bytes(args)
+    ws = _workspace(nbytes, q.device, workspace)
+    _check(lib().mlstm_fwd_parallel(ctypes.byref(args), _ptr(ws), nbytes, _stream(stream)),
+           "mlstm_fwd_parallel")
+    return (h, (C_out, n_out, m_out)) if return_state else h
+
+
+def step_args(q, k, v, o_pre, i_pre, f_pre, C, n_in, m_in, n_out, m_out, h) -> StepArgs:
+    import torch
+    B, H, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    for name, t, shp in (("q", q, (B, H, K)), ("k", k, (B, H, K)), ("v", v, (B, H, V)),
+                         ("o_pre", o_pre, (B, H, V)), ("h", h, (B, H, V))):
+        _require(t, name, shp, dt)
+    for name, t, shp in (("i_pre", i_pre, (B, H)), ("f_pre", f_pre, (B, H)), ("C", C, (B, H, V, K)),
+                         ("n_in", n_in, (B, H, K)), ("m_in", m_in, (B, H)),
+                         ("n_out", n_out, (B, H, K)), ("m_out", m_out, (B, H))):
+        _require(t, name, shp, torch.float32)
+    return StepArgs(B, H, K, V, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o_pre),
+                    _ptr(i_pre), _ptr(f_pre), _ptr(C), _ptr(n_in), _ptr(m_in), _ptr(n_out),
+                    _ptr(m_out), _ptr(h))
+
+
+def mlstm_step(q, k, v, o_pre, i_pre, f_pre, C, n_in, m_in, n_out=None, m_out=None, h=None,
+               stream=None):
+    """One decode step; C is updated in place. Returns (h, n_out, m_out)."""
+    import torch
+    if h is None:
+        h = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    if n_out is None:
+        n_out = torch.empty_like(n_in)
+    if m_out is None:
+        m_out = torch.empty_like(m_in)
+    args = step_args(q, k, v, o_pre, i_pre, f_pre, C, n_in, m_in, n_out, m_out, h)
+    _check(lib().mlstm_step(ctypes.byref(args), _stream(stream)), "mlstm_step")
+    return h, n_out, m_out
+
+
+def set_launch_events(kernel: str, before, after) -> None:
+    """Bracket every later launch of `kernel` with the given hipEvent_t handles (ints or None)."""
+    _check(lib().mlstm_set_launch_events(KERNEL_IDS[kernel], before, after), "mlstm_set_launch_events")

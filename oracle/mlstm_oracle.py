@@ -36,12 +36,15 @@ Functions:
   mlstm_rows               h at chosen time indices from the parallel (dual)
                            closed form of the same cell, for sampled checks
                            at sizes where the full recurrence is too slow
+  mlstm_final_state        the state after a whole sequence from the
+                           sum-of-products form of C_T (one matrix product)
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["logsigmoid", "sigmoid", "mlstm_step", "mlstm_recurrent", "mlstm_rows"]
+__all__ = ["logsigmoid", "sigmoid", "mlstm_step", "mlstm_recurrent", "mlstm_rows",
+           "mlstm_final_state"]
 
 
 def logsigmoid(x):
@@ -160,3 +163,39 @@ def mlstm_rows(q, k, v, i_pre, f_pre, o_pre, rows, C0=None, n0=None, m0=None):
             out[..., r, :] = sigmoid(o_pre[..., t, :]) * num / den[..., None]
     return out
 
+
+
+def mlstm_final_state(k, v, i_pre, f_pre, C0=None, n0=None, m0=None):
+    """State (C~_T, n~_T, m_T) after the whole sequence, float64.
+
+    Sum-of-products form of the matrix memory (nareshka notes, "B. mLSTM",
+    parallelisation formula; xLSTM guide, dual formulation):
+        C_T = sum_j (prod_{l=j+1..T} f_l) i_j v_j k_j^T + (prod_{l=1..T} f_l) C_0
+    and the same weights on k_j for n_T. The log weight of token j is
+    sum_{l=j+1..T} log f_l + i~_j and that of the initial state
+    sum_{l=1..T} log f_l + m_0 (m_0 = 0 without an initial state, as in the
+    recurrence); m_T is the largest of them, which is the recurrence's
+    running max, and C~ = exp(-m_T) C.
+
+    k [..., T, d_qk]; v [..., T, d_v]; i_pre, f_pre [..., T].
+    """
+    k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
+    i_pre = np.asarray(i_pre, np.float64)
+    log_f = logsigmoid(f_pre)
+    lead = k.shape[:-2]
+    rev = np.cumsum(log_f[..., :0:-1], axis=-1)      # sums over l = T-1, T-1..T-2, ...
+    suffix = np.concatenate([rev[..., ::-1], np.zeros(lead + (1,))], axis=-1)
+    with np.errstate(invalid="ignore"):
+        log_w = suffix + i_pre
+    m_init = np.zeros(lead) if m0 is None else np.asarray(m0, np.float64)
+    log_w0 = np.sum(log_f, axis=-1) + m_init
+    m = np.maximum(np.max(log_w, axis=-1), log_w0)
+    with np.errstate(over="ignore", invalid="ignore"):
+        w = np.exp(log_w - m[..., None])
+        w0 = np.exp(log_w0 - m)
+    C = np.matmul(np.swapaxes(w[..., None] * v, -1, -2), k)
+    n = np.matmul(w[..., None, :], k)[..., 0, :]
+    if C0 is not None:
+        C = C + w0[..., None, None] * np.asarray(C0, np.float64)
+        n = n + w0[..., None] * np.asarray(n0, np.float64)
+    return C, n, m

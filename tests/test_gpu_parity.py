@@ -1,0 +1,387 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Bar: max|h_gpu - h_ref| <= tol * max|h_ref| with tol = 1e-4 for float32
+inputs and 2e-2 for bfloat16 inputs; every output finite. States are
+compared in true units (exp(m) C~), relative to the oracle's largest entry.
+Outputs are pre-filled with NaN so that an unwritten element fails.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from linear_recurrent_sequence_fwd_amd.configs import CONFIGS
+from linear_recurrent_sequence_fwd_amd.inputs import make_fwd_inputs, make_state, make_step_inputs
+from oracle import mlstm_oracle as orc
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+NAMES = ("q", "k", "v", "i_pre", "f_pre", "o_pre")
+
+
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_recurrent_sequence_fwd_amd as M
+    return M
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.cuda()
+
+
+def dev_inputs(x):
+    d = x["dtype"]
+    return {"q": dev(x["q"], d), "k": dev(x["k"], d), "v": dev(x["v"], d),
+            "o_pre": dev(x["o_pre"], d), "i_pre": dev(x["i_pre"], "fp32"),
+            "f_pre": dev(x["f_pre"], "fp32")}
+
+
+def nan_like(t):
+    return torch.full_like(t, float("nan"))
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def rel_err(got, ref):
+    assert np.all(np.isfinite(got)), "non-finite output"
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def state_err(gpu_state, ref_state):
+    C, n, m = (host(t) for t in gpu_state)
+    Cr, nr, mr = ref_state
+    sc = np.exp(m - mr)
+    return (rel_err(sc[..., None, None] * C, Cr), rel_err(sc[..., None] * n, nr))
+
+
+def oracle(x, **state):
+    return orc.mlstm_recurrent(*[x[n] for n in NAMES], **state)
+
+
+def run_chunkwise(M, d, chunk, **kw):
+    h = nan_like(d["v"])
+    out = M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["o_pre"], d["i_pre"], d["f_pre"],
+                                chunk=chunk, h=h, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_parallel(M, d, **kw):
+    h = nan_like(d["v"])
+    out = M.mlstm_fwd_parallel(d["q"], d["k"], d["v"], d["o_pre"], d["i_pre"], d["f_pre"], h=h, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+# ------------------------------------------------------------------ decode step
+
+def test_step_tiny_fp32_matches_recurrence():
+    M = _lib()
+    cfg = CONFIGS["tiny"]
+    x = make_fwd_inputs(1, 1, cfg["T"], cfg["d_qk"], cfg["d_v"], "fp32", seed=0)
+    say("step tiny fp32, 256 steps")
+    h_ref, st_ref = oracle(x)
+    d = dev_inputs(x)
+    C = torch.zeros((1, 1, 64, 64), device="cuda")
+    n = torch.zeros((1, 1, 64), device="cuda")
+    m = torch.zeros((1, 1), device="cuda")
+    n2, m2 = torch.empty_like(n), torch.empty_like(m)
+    hs = []
+    for t in range(cfg["T"]):
+        h = torch.full((1, 1, 64), float("nan"), device="cuda")
+        M.mlstm_step(d["q"][:, :, t].contiguous(), d["k"][:, :, t].contiguous(),
+                     d["v"][:, :, t].contiguous(), d["o_pre"][:, :, t].contiguous(),
+                     d["i_pre"][:, :, t].contiguous(), d["f_pre"][:, :, t].contiguous(),
+                     C, n, m, n2, m2, h)
+        hs.append(h)
+        n, n2, m, m2 = n2, n, m2, m
+    torch.cuda.synchronize()
+    h = np.stack([host(t) for t in hs], axis=2)
+    assert rel_err(h, h_ref) <= TOL["fp32"]
+    ec, en = state_err((C, n, m), st_ref)
+    assert ec <= TOL["fp32"] and en <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("dtype,K,V", [("bf16", 128, 96), ("fp32", 192, 40), ("bf16", 512, 64)])
+def test_step_from_random_state(dtype, K, V):
+    M = _lib()
+    B, H, steps = 2, 3, 12
+    say(f"step {dtype} K={K} V={V}")
+    st = make_state(B, H, K, V, seed=4, m_scale=2.0)
+    C = torch.from_numpy(st["C"]).cuda()
+    n = torch.from_numpy(st["n"]).cuda()
+    m = torch.from_numpy(st["m"]).cuda()
+    Cr, nr, mr = (st[a].astype(np.float64) for a in ("C", "n", "m"))
+    n2, m2 = torch.empty_like(n), torch.empty_like(m)
+    for s in range(steps):
+        x = make_step_inputs(B, H, K, V, step=s, dtype=dtype, seed=5)
+        if s == 3:
+            x["f_pre"][0, 1] = -np.inf     # complete forgetting in one head
+            x["i_pre"][1, 2] = 40.0        # a strong write
+        h_ref, Cr, nr, mr = orc.mlstm_step(x["q"], x["k"], x["v"], x["i_pre"], x["f_pre"],
+                                           x["o_pre"], Cr, nr, mr)
+        d = {a: dev(x[a], dtype if a in ("q", "k", "v", "o_pre") else "fp32") for a in NAMES}
+        h = torch.full((B, H, V), float("nan"), device="cuda",
+                       dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+        M.mlstm_step(d["q"], d["k"], d["v"], d["o_pre"], d["i_pre"], d["f_pre"], C, n, m, n2, m2, h)
+        torch.cuda.synchronize()
+        assert rel_err(host(h), h_ref) <= TOL[dtype], f"step {s}"
+        n, n2, m, m2 = n2, n, m2, m
+    ec, en = state_err((C, n, m), (Cr, nr, mr))
+    assert ec <= 1e-4 and en <= 1e-4
+
+
+# ------------------------------------------------------------------ small forwards
+
+@pytest.mark.parametrize("T,chunk", [(256, 64), (256, 128), (200, 64), (130, 192), (1, 64), (64, 64)])
+def test_chunkwise_tiny_fp32(T, chunk):
+    M = _lib()
+    say(f"chunkwise fp32 T={T} chunk={chunk}")
+    x = make_fwd_inputs(1, 1, T, 64, 64, "fp32", seed=0)
+    h_ref, st_ref = oracle(x)
+    h, st = run_chunkwise(M, dev_inputs(x), chunk, return_state=True)
+    assert rel_err(host(h), h_ref) <= TOL["fp32"]
+    ec, en = state_err(st, st_ref)
+    assert ec <= TOL["fp32"] and en <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("T", [256, 1, 77])
+def test_parallel_tiny_fp32(T):
+    M = _lib()
+    say(f"parallel fp32 T={T}")
+    x = make_fwd_inputs(1, 1, T, 64, 64, "fp32", seed=0)
+    h_ref, st_ref = oracle(x)
+    h, st = run_parallel(M, dev_inputs(x), return_state=True)
+    assert rel_err(host(h), h_ref) <= TOL["fp32"]
+    ec, en = state_err(st, st_ref)
+    assert ec <= TOL["fp32"] and en <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("dtype,K,V,T,chunk", [
+    ("bf16", 128, 192, 333, 64), ("bf16", 128, 192, 333, 128), ("bf16", 64, 128, 500, 256),
+    ("bf16", 256, 512, 300, 128), ("fp32", 128, 128, 321, 64), ("fp32", 64, 192, 150, 128),
+])
+def test_chunkwise_with_initial_state(dtype, K, V, T, chunk):
+    M = _lib()
+    B, H = 2, 2
+    say(f"chunkwise {dtype} K={K} V={V} T={T} chunk={chunk} with state")
+    x = make_fwd_inputs(B, H, T, K, V, dtype, seed=1, i_std=2.0)
+    st = make_state(B, H, K, V, seed=2)
+    h_ref, st_ref = oracle(x, C0=st["C"], n0=st["n"], m0=st["m"])
+    d = dev_inputs(x)
+    h, sto = run_chunkwise(M, d, chunk, C0=torch.from_numpy(st["C"]).cuda(),
+                           n0=torch.from_numpy(st["n"]).cuda(), m0=torch.from_numpy(st["m"]).cuda(),
+                           return_state=True)
+    assert rel_err(host(h), h_ref) <= TOL[dtype]
+    ec, en = state_err(sto, st_ref)
+    assert ec <= TOL[dtype] and en <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,K,V,T", [("bf16", 128, 192, 333), ("fp32", 64, 64, 256),
+                                         ("bf16", 256, 512, 200)])
+def test_parallel_with_initial_state(dtype, K, V, T):
+    M = _lib()
+    B, H = 2, 2
+    say(f"parallel {dtype} K={K} V={V} T={T} with state")
+    x = make_fwd_inputs(B, H, T, K, V, dtype, seed=3, i_std=2.0)
+    st = make_state(B, H, K, V, seed=4)
+    h_ref, st_ref = oracle(x, C0=st["C"], n0=st["n"], m0=st["m"])
+    h, sto = run_parallel(M, dev_inputs(x), C0=torch.from_numpy(st["C"]).cuda(),
+                          n0=torch.from_numpy(st["n"]).cuda(), m0=torch.from_numpy(st["m"]).cuda(),
+                          return_state=True)
+    assert rel_err(host(h), h_ref) <= TOL[dtype]
+    ec, en = state_err(sto, st_ref)
+    assert ec <= TOL[dtype] and en <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_extreme_preactivations(dtype):
+    M = _lib()
+    say(f"extreme preactivations {dtype}")
+    rng = np.random.default_rng(7)
+    B, H, T, K, V = 1, 2, 300, 64, 64
+    x = make_fwd_inputs(B, H, T, K, V, dtype, seed=8)
+    x["i_pre"] = rng.choice([-100.0, 100.0, 0.0, 2.0, -3.0], size=(B, H, T)).astype(np.float32)
+    x["f_pre"] = rng.choice([-100.0, 100.0, np.inf, -np.inf, 3.0, 3.0, 3.0],
+                            size=(B, H, T)).astype(np.float32)
+    h_ref, _ = oracle(x)
+    d = dev_inputs(x)
+    for chunk in (64, 128):
+        h = run_chunkwise(M, d, chunk)
+        assert rel_err(host(h), h_ref) <= TOL[dtype], f"chunk {chunk}"
+    h = run_parallel(M, d)
+    assert rel_err(host(h), h_ref) <= TOL[dtype], "parallel"
+
+
+def test_empty_sequence_copies_state():
+    M = _lib()
+    say("T=0")
+    st = make_state(1, 2, 64, 64, seed=9)
+    x = make_fwd_inputs(1, 2, 0, 64, 64, "fp32", seed=9)
+    d = dev_inputs(x)
+    C0, n0, m0 = (torch.from_numpy(st[a]).cuda() for a in ("C", "n", "m"))
+    for fn in (run_chunkwise, run_parallel):
+        kw = {"chunk": 64} if fn is run_chunkwise else {}
+        h, (C, n, m) = fn(M, d, C0=C0, n0=n0, m0=m0, return_state=True, **kw)
+        assert h.numel() == 0
+        assert torch.equal(C, C0) and torch.equal(n, n0) and torch.equal(m, m0)
+
+
+def test_run_twice_bitwise_identical():
+    M = _lib()
+    say("determinism")
+    x = make_fwd_inputs(2, 4, 700, 128, 256, "bf16", seed=10)
+    d = dev_inputs(x)
+    a = run_chunkwise(M, d, 128)
+    b = run_chunkwise(M, d, 128)
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ the five workloads
+
+@pytest.mark.parametrize("entry", ["chunkwise", "parallel"])
+def test_config_tiny(entry):
+    M = _lib()
+    cfg = CONFIGS["tiny"]
+    say(f"config tiny {entry}")
+    x = make_fwd_inputs(cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"], "fp32", seed=0)
+    h_ref, _ = oracle(x)
+    d = dev_inputs(x)
+    h = run_chunkwise(M, d, 64) if entry == "chunkwise" else run_parallel(M, d)
+    assert rel_err(host(h), h_ref) <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("seed,i_std", [(0, 1.0), (1, 6.0)])
+def test_config_mid(seed, i_std):
+    M = _lib()
+    cfg = CONFIGS["mid"]
+    say(f"config mid seed={seed} i_std={i_std}")
+    x = make_fwd_inputs(cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"], "bf16", seed=seed,
+                        i_std=i_std)
+    h_ref, st_ref = oracle(x)
+    d = dev_inputs(x)
+    h, st = run_chunkwise(M, d, 64, return_state=True)
+    assert rel_err(host(h), h_ref) <= TOL["bf16"]
+    ec, en = state_err(st, st_ref)
+    assert ec <= TOL["bf16"] and en <= TOL["bf16"]
+    hp = run_parallel(M, d)
+    assert rel_err(host(hp), h_ref) <= TOL["bf16"]
+
+
+def _sampled_rows(T):
+    rows = sorted({0, 1, 63, 64, 65, T // 3, T // 2 + 7, T - 65, T - 2, T - 1})
+    return [r for r in rows if 0 <= r < T]
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_config_7b_layer(chunk):
+    M = _lib()
+    cfg = CONFIGS["7b_layer"]
+    say(f"config 7b_layer chunk={chunk}")
+    x = make_fwd_inputs(cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"], "bf16", seed=0)
+    d = dev_inputs(x)
+    h, st = run_chunkwise(M, d, chunk, return_state=True)
+    rows = _sampled_rows(cfg["T"])
+    h_ref = orc.mlstm_rows(*[x[n] for n in NAMES], rows=rows)
+    assert rel_err(host(h[:, :, rows]), h_ref) <= TOL["bf16"]
+    st_ref = orc.mlstm_final_state(x["k"], x["v"], x["i_pre"], x["f_pre"])
+    ec, en = state_err(st, st_ref)
+    assert ec <= TOL["bf16"] and en <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_config_long_context(chunk):
+    M = _lib()
+    cfg = CONFIGS["long_context"]
+    say(f"config long_context chunk={chunk}")
+    x = make_fwd_inputs(cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"], "bf16", seed=0)
+    d = dev_inputs(x)
+    h, st = run_chunkwise(M, d, chunk, return_state=True)
+    T = cfg["T"]
+    rows = [0, 4097, T // 2 + 3, T - 1]
+    heads = [0, 5]
+    sub = {n: x[n][:, heads] for n in NAMES}
+    h_ref = orc.mlstm_rows(*[sub[n] for n in NAMES], rows=rows)
+    assert rel_err(host(h[:, heads][:, :, rows]), h_ref) <= TOL["bf16"]
+    assert bool(torch.isfinite(h.float()).all())
+    st_ref = orc.mlstm_final_state(sub["k"], sub["v"], sub["i_pre"], sub["f_pre"])
+    ec, en = state_err(tuple(t[:, heads] for t in st), st_ref)
+    assert ec <= TOL["bf16"] and en <= TOL["bf16"]
+
+
+def test_config_decode():
+    """512-token prefill (state from the oracle's closed form), then 1000 steps.
+
+    All 64 x 8 heads run on the GPU; the oracle follows 8 sampled heads
+    through every step.
+    """
+    M = _lib()
+    cfg = CONFIGS["decode"]
+    B, H, K, V = cfg["B"], cfg["H"], cfg["d_qk"], cfg["d_v"]
+    say("config decode prefill")
+    pre = make_fwd_inputs(B, H, cfg["prefill"], K, V, "fp32", seed=0)
+    Cr, nr, mr = orc.mlstm_final_state(pre["k"], pre["v"], pre["i_pre"], pre["f_pre"])
+    C = torch.from_numpy(Cr.astype(np.float32)).cuda()
+    n = torch.from_numpy(nr.astype(np.float32)).cuda()
+    m = torch.from_numpy(mr.astype(np.float32)).cuda()
+    sample = [(0, 0), (3, 7), (17, 2), (31, 5), (40, 1), (52, 6), (63, 3), (63, 7)]
+    bi = np.array([s[0] for s in sample]); hi = np.array([s[1] for s in sample])
+    Cs, ns, ms = (C.cpu().numpy()[bi, hi].astype(np.float64), n.cpu().numpy()[bi, hi].astype(np.float64),
+                  m.cpu().numpy()[bi, hi].astype(np.float64))
+    n2, m2 = torch.empty_like(n), torch.empty_like(m)
+    worst = 0.0
+    say("config decode steps")
+    for s in range(cfg["steps"]):
+        x = make_step_inputs(B, H, K, V, step=s, dtype="fp32", seed=1)
+        d = {a: torch.from_numpy(x[a]).cuda() for a in NAMES}
+        h = torch.full((B, H, V), float("nan"), device="cuda")
+        M.mlstm_step(d["q"], d["k"], d["v"], d["o_pre"], d["i_pre"], d["f_pre"], C, n, m, n2, m2, h)
+        n, n2, m, m2 = n2, n, m2, m
+        hr, Cs, ns, ms = orc.mlstm_step(*[x[a][bi, hi] for a in ("q", "k", "v", "i_pre", "f_pre", "o_pre")],
+                                        Cs, ns, ms)
+        hg = host(h[bi, hi])
+        worst = max(worst, rel_err(hg, hr))
+        if s % 250 == 0:
+            say(f"decode step {s} worst so far {worst:.2e}")
+    assert worst <= TOL["fp32"]
+    ec, en = state_err((C[bi, hi], n[bi, hi], m[bi, hi]), (Cs, ns, ms))
+    assert ec <= TOL["fp32"] and en <= TOL["fp32"]
+
+
+def test_chunkwise_prefill_then_steps():
+    """State hand-off: bf16 chunkwise prefill on the GPU, then float32 decode steps."""
+    M = _lib()
+    B, H, K, V, T1, T2 = 2, 4, 256, 512, 512, 40
+    say("prefill -> steps hand-off")
+    x = make_fwd_inputs(B, H, T1 + T2, K, V, "bf16", seed=11)
+    h_ref, st_ref = oracle(x)
+    d = dev_inputs(x)
+    pre = {a: t[:, :, :T1].contiguous() for a, t in d.items()}
+    h1, (C, n, m) = M.mlstm_fwd_chunkwise(pre["q"], pre["k"], pre["v"], pre["o_pre"], pre["i_pre"],
+                                          pre["f_pre"], chunk=128, return_state=True)
+    n2, m2 = torch.empty_like(n), torch.empty_like(m)
+    hs = [h1.float()]
+    for t in range(T1, T1 + T2):
+        step = {a: d[a][:, :, t].contiguous() for a in d}
+        h, _, _ = M.mlstm_step(step["q"], step["k"], step["v"], step["o_pre"], step["i_pre"],
+                               step["f_pre"], C, n, m, n2, m2)
+        hs.append(h.float()[:, :, None])
+        n, n2, m, m2 = n2, n, m2, m
+    torch.cuda.synchronize()
+    h = torch.cat(hs, dim=2).cpu().numpy().astype(np.float64)
+    assert rel_err(h, h_ref) <= TOL["bf16"]
+    ec, en = state_err((C, n, m), st_ref)
+    assert ec <= TOL["bf16"] and en <= TOL["bf16"]

@@ -281,6 +281,30 @@ def test_stabiliser_invariance():
     assert _relerr(hr, ha[[0, 20, 44]]) < 1e-12
 
 
+def test_final_state_closed_form_matches_recurrence():
+    x = make_fwd_inputs(2, 2, 57, 6, 5, dtype="fp32", seed=16, i_std=3.0)
+    args = [x[n].astype(np.float64) for n in ("q", "k", "v", "i_pre", "f_pre", "o_pre")]
+    args[4][0, 1, 20] = -np.inf          # a zero forget gate in one head
+    _, (C, n, m) = orc.mlstm_recurrent(*args)
+    C2, n2, m2 = orc.mlstm_final_state(args[1], args[2], args[3], args[4])
+    np.testing.assert_allclose(m2, m, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(C2, C, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(n2, n, rtol=1e-12, atol=1e-13)
+    st = make_state(2, 2, 6, 5, seed=3)
+    C0, n0, m0 = (st[n_].astype(np.float64) for n_ in ("C", "n", "m"))
+    _, (C, n, m) = orc.mlstm_recurrent(*args, C0=C0, n0=n0, m0=m0)
+    C2, n2, m2 = orc.mlstm_final_state(args[1], args[2], args[3], args[4], C0=C0, n0=n0, m0=m0)
+    np.testing.assert_allclose(m2, m, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(C2, C, rtol=1e-12, atol=1e-13)
+    # and against the literal product form of C_T in true units (one head)
+    f = 1 / (1 + np.exp(-args[4][1, 0]))
+    ig = np.exp(args[3][1, 0])
+    T = f.shape[0]
+    Ct = sum(np.prod(f[j + 1:]) * ig[j] * np.outer(args[2][1, 0, j], args[1][1, 0, j]) for j in range(T))
+    Ct = Ct + np.prod(f) * np.exp(m0[1, 0]) * C0[1, 0]
+    np.testing.assert_allclose(np.exp(m2[1, 0]) * C2[1, 0], Ct, rtol=1e-12)
+
+
 def test_extreme_preactivations_finite_and_exact():
     rng = np.random.default_rng(14)
     T, K, V = 48, 6, 5
