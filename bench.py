@@ -1,0 +1,338 @@
+"""Benchmark of the mLSTM cell forward on one MI355X.
+
+One step = one full chunkwise forward (gate prefix sums, inter-chunk state
+pass, intra-chunk output kernel) over the 7B-layer-shaped workload
+(B=1, H=8, T=8192, d_qk=256, d_v=512, bf16 q/k/v/o and h, float32 gates),
+inputs resident in HBM. Prints ONE JSON line on stdout; progress goes to
+stderr.
+
+Extra keys: per-kernel average durations from HIP events recorded around
+every launch inside the timed region, the roofline of the dominant kernel,
+the chunk sweep, the decode step (B=64, H=8, float32 state) in % of HBM
+bandwidth, and the oracle timed on the host cores (a baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12            # B/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5166e15   # flop/s dense bf16: 256 CU x 2.4 GHz x 4096 flop/clk
+METRIC = "mLSTM fwd tokens/s at 7B-layer shape, % bf16 MFMA peak; decode step % HBM BW"
+WORKLOAD = dict(B=1, H=8, T=8192, d_qk=256, d_v=512)
+DECODE = dict(B=64, H=8, d_qk=256, d_v=512, prefill=512)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "out_kernel_7b_layer_traffic.md")
+KERNEL_SRC = os.path.join(ROOT, "linear_recurrent_sequence_fwd_amd", "csrc", "mlstm_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+# ---------------------------------------------------------------- algorithmic work
+
+def fwd_bytes(B, H, T, K, V, chunk):
+    """Algorithmic HBM bytes of the whole forward: q, k, v, o read once, h
+    written once (bf16), float32 gates read once, the final float32 state."""
+    return B * H * (T * (2 * K + 2 * K + 2 * V + 2 * V + 2 * V + 4 + 4) + 4 * (V * K + K + 1))
+
+
+def fwd_flops(B, H, T, K, V, chunk):
+    """Flops at chunk L: per token-head 2KV (state update) + 2KV (state
+    readout) + L K (causal half of Q K^T) + L V (causal half of P V) + 2K + L."""
+    return B * H * T * (4 * K * V + chunk * (K + V) + 2 * K + chunk)
+
+
+def kernel_bytes(name, B, H, T, K, V, chunk):
+    """Algorithmic bytes one launch of a kernel must move (inputs read once,
+    outputs written once), at the 7B-layer shape with bf16 data."""
+    BH = B * H
+    Nc = -(-T // chunk)
+    state = V * K * 2 + K * 4 + 8                  # one bf16 chunk-start state, n, m
+    gate_tok = 3 * 8 + 4                           # u, b, mp (float64) and rs (int32)
+    if name == "gate":
+        return BH * T * (4 + 4 + gate_tok) + BH * Nc * (8 + 8 + 4)
+    if name == "state":
+        return BH * T * (2 * K + 2 * V + 8) + BH * Nc * (state + 8 + 8 + 4) + BH * (4 * V * K + 4 * K + 4)
+    if name == "out":
+        return BH * T * (2 * K + 2 * K + 2 * V + 2 * V + 2 * V + gate_tok) + BH * (Nc - 1) * state
+    raise KeyError(name)
+
+
+def decode_bytes(B, H, K, V):
+    """Algorithmic bytes of one decode step: read and write the float32 state
+    (C, n, m), read q, k, v, o and the gates, write h (all float32)."""
+    BH = B * H
+    return BH * (2 * (V * K + K + 1) * 4 + (2 * K + 2 * V) * 4 + 8 + V * 4)
+
+
+# ---------------------------------------------------------------- the runs
+
+def make_device_inputs(torch, cfg, dtype="bf16", seed=0):
+    from linear_recurrent_sequence_fwd_amd.inputs import make_fwd_inputs
+    x = make_fwd_inputs(cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"], dtype, seed=seed)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    d = {n: torch.from_numpy(x[n]).to("cuda").to(tdt) for n in ("q", "k", "v", "o_pre")}
+    for n in ("i_pre", "f_pre"):
+        d[n] = torch.from_numpy(x[n]).to("cuda")
+    return x, d
+
+
+def time_chunkwise(torch, M, L, ev, d, chunk, steps, warmup, kernels=("gate", "state", "out")):
+    from linear_recurrent_sequence_fwd_amd import _lib
+    h = torch.empty_like(d["v"])
+    args = _lib.fwd_args(d["q"], d["k"], d["v"], d["o_pre"], d["i_pre"], d["f_pre"], h)
+    nbytes = _lib.chunkwise_workspace_bytes(args, chunk)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    lib, pargs, wsp = _lib.lib(), ctypes.byref(args), ws.data_ptr()
+
+    def one():     # arguments marshalled once; the loop only enqueues
+        code = lib.mlstm_fwd_chunkwise(pargs, chunk, wsp, nbytes, stream)
+        if code:
+            raise RuntimeError(lib.mlstm_last_error().decode())
+
+    for _ in range(warmup):
+        one()
+    pairs = {k: ev.create(2 * steps) for k in kernels}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for k in kernels:
+            M.set_launch_events(k, pairs[k][2 * i], pairs[k][2 * i + 1])
+        one()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    for k in kernels:
+        M.set_launch_events(k, None, None)
+    per_kernel = {}
+    for k in kernels:
+        ms = [ev.elapsed_ms(pairs[k][2 * i], pairs[k][2 * i + 1]) for i in range(steps)]
+        per_kernel[k] = sum(ms) / len(ms) * 1e3      # us
+        ev.destroy(pairs[k])
+    return elapsed, per_kernel
+
+
+def time_decode(torch, M, ev, steps, warmup):
+    from linear_recurrent_sequence_fwd_amd.inputs import make_step_inputs
+    cfg = DECODE
+    B, H, K, V = cfg["B"], cfg["H"], cfg["d_qk"], cfg["d_v"]
+    # state from a 512-token chunkwise prefill of the 7B-layer distributions
+    _, pre = make_device_inputs(torch, dict(B=B, H=H, T=cfg["prefill"], d_qk=K, d_v=V), "bf16", seed=3)
+    _, (C, n, m) = M.mlstm_fwd_chunkwise(pre["q"], pre["k"], pre["v"], pre["o_pre"], pre["i_pre"],
+                                         pre["f_pre"], chunk=128, return_state=True)
+    del pre
+    pool = []
+    for s in range(8):
+        x = make_step_inputs(B, H, K, V, step=s, dtype="fp32", seed=4)
+        pool.append({a: torch.from_numpy(x[a]).to("cuda") for a in ("q", "k", "v", "o_pre", "i_pre", "f_pre")})
+    from linear_recurrent_sequence_fwd_amd import _lib
+    n2, m2 = torch.empty_like(n), torch.empty_like(m)
+    h = torch.empty((B, H, V), device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    bufs = [(n, m, n2, m2), (n2, m2, n, m)]
+    lib = _lib.lib()
+    # arguments marshalled once per (input set, ping-pong parity); the loop only enqueues
+    structs = [[_lib.step_args(x["q"], x["k"], x["v"], x["o_pre"], x["i_pre"], x["f_pre"], C, *bufs[p], h)
+                for p in range(2)] for x in pool]
+
+    def one(i):
+        code = lib.mlstm_step(ctypes.byref(structs[i % len(pool)][i % 2]), stream)
+        if code:
+            raise RuntimeError(lib.mlstm_last_error().decode())
+
+    for i in range(warmup):
+        one(i)
+    evs = ev.create(2 * steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        M.set_launch_events("step", evs[2 * i], evs[2 * i + 1])
+        one(warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    M.set_launch_events("step", None, None)
+    k_us = sum(ev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)) / steps * 1e3
+    ev.destroy(evs)
+    assert bool(torch.isfinite(h).all())
+    return elapsed, k_us
+
+
+def cpu_baseline(x, budget_s=15.0):
+    """The oracle recurrence on the host, all heads, as many leading tokens as fit the budget."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle.mlstm_oracle import mlstm_step
+    names = ("q", "k", "v", "i_pre", "f_pre", "o_pre")
+    a = {n: x[n][0].astype(np.float64) for n in names}     # [H, T, ...]
+    H, T, K = a["q"].shape
+    V = a["v"].shape[-1]
+    C = np.zeros((H, V, K)); n = np.zeros((H, K)); m = np.zeros(H)
+    done = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while done < T and time.perf_counter() - t0 < budget_s:
+            t = done
+            _, C, n, m = mlstm_step(a["q"][:, t], a["k"][:, t], a["v"][:, t], a["i_pre"][:, t],
+                                    a["f_pre"][:, t], a["o_pre"][:, t], C, n, m)
+            done += 1
+        el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 NumPy step recurrence, B=1 H={H} d_qk={K} d_v={V}, first {done} of "
+                      f"{T} tokens ({el:.1f} s, one thread)"}
+
+
+def traffic_from_profile():
+    """HBM bytes per launch of the output kernel from the committed counter
+    summary, if it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != sha:
+        return None
+    return float(m_b.group(1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--chunk", type=int, default=256)
+    ap.add_argument("--sweep", type=str, default="64,128,256", help="chunk sizes reported besides --chunk")
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py runs on one GPU only: the mLSTM path here is a single-GPU build "
+              f"(--gpus {args.gpus} requested). Heads and batch shard with no exchange; see the "
+              f"design notes for the multi-GPU plan.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_recurrent_sequence_fwd_amd as M
+    from linear_recurrent_sequence_fwd_amd import _lib
+    _lib.lib()
+    ev = HipEvents()
+    cfg = WORKLOAD
+    B, H, T, K, V = cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"]
+
+    log(f"[bench] inputs 7B-layer B={B} H={H} T={T} d_qk={K} d_v={V} bf16")
+    x, d = make_device_inputs(torch, cfg, "bf16", seed=0)
+
+    log(f"[bench] chunkwise chunk={args.chunk}: warmup {args.warmup}, steps {args.steps}")
+    elapsed, per_k = time_chunkwise(torch, M, _lib, ev, d, args.chunk, args.steps, args.warmup)
+    ms_step = elapsed / args.steps * 1e3
+    tok_s = B * T * args.steps / elapsed
+    flops = fwd_flops(B, H, T, K, V, args.chunk)
+    flops_ci = B * H * T * 4 * K * V
+    path_bytes = fwd_bytes(B, H, T, K, V, args.chunk)
+    dom = max(per_k, key=per_k.get)
+    kb = kernel_bytes(dom, B, H, T, K, V, args.chunk)
+    achieved = kb / (per_k[dom] * 1e-6)
+    traffic = traffic_from_profile() if dom == "out" else None
+    log(f"[bench] {ms_step:.3f} ms/step, {tok_s:.3e} tokens/s, kernels us {per_k}")
+
+    sweep = {}
+    for L in [int(s) for s in args.sweep.split(",") if s]:
+        if L == args.chunk:
+            continue
+        el, pk = time_chunkwise(torch, M, _lib, ev, d, L, max(5, args.steps // 2), 2)
+        st = max(5, args.steps // 2)
+        sweep[str(L)] = {"ms_per_step": el / st * 1e3, "tokens_per_s": B * T * st / el,
+                         "mfma_frac": fwd_flops(B, H, T, K, V, L) / (el / st) / MFMA_BF16_PEAK,
+                         "kernel_us": pk}
+        log(f"[bench] sweep chunk={L}: {el / st * 1e3:.3f} ms/step")
+
+    out = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded PCG64 draws with the 7B-layer distributions)",
+        "config": {"workload": "mLSTM chunkwise forward, 7B-layer shape", "B": B, "H": H, "T": T,
+                   "d_qk": K, "d_v": V, "chunk": args.chunk, "inputs": "bf16 q/k/v/o, fp32 gates",
+                   "parallelism": "single GPU"},
+        "mfma_frac": flops / (ms_step * 1e-3) / MFMA_BF16_PEAK,
+        "mfma_frac_chunk_independent": flops_ci / (ms_step * 1e-3) / MFMA_BF16_PEAK,
+        "hbm_frac_path": path_bytes / (ms_step * 1e-3) / HBM_PEAK,
+        "kernel_us": per_k,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK,
+                     "traffic": traffic},
+        "sweep": sweep,
+    }
+    del d
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        log(f"[bench] decode B={DECODE['B']} H={DECODE['H']} steps {args.decode_steps}")
+        el, k_us = time_decode(torch, M, ev, args.decode_steps, 20)
+        us_step = el / args.decode_steps * 1e6
+        db = decode_bytes(DECODE["B"], DECODE["H"], DECODE["d_qk"], DECODE["d_v"])
+        out["decode"] = {"workload": "mlstm_step B=64 H=8 d_qk=256 d_v=512 fp32 state",
+                         "us_per_step": us_step, "kernel_us": k_us,
+                         "tokens_per_s": DECODE["B"] / (us_step * 1e-6),
+                         "achieved_GBps": db / (k_us * 1e-6) / 1e9,
+                         "hbm_frac": db / (k_us * 1e-6) / HBM_PEAK,
+                         "hbm_frac_wall": db / (us_step * 1e-6) / HBM_PEAK}
+        log(f"[bench] decode {us_step:.1f} us/step wall, kernel {k_us:.1f} us")
+
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -56,6 +56,9 @@ def lib() -> ctypes.CDLL:
     """The loaded library with argument types set (loaded once)."""
     global _lib
     if _lib is None:
+        # torch's HIP runtime carries the same soname; loading torch first
+        # makes the library bind to it, so torch streams and events are valid.
+        import torch  # noqa: F401
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                                "`python -m linear_recurrent_sequence_fwd_amd.build`")

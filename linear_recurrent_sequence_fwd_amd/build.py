@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmlstm.so")
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, "mlstm_kernels.hip"), os.path.join(CSRC, "mlstm_abi.cpp")]
+SOURCES = [os.path.join(CSRC, "mlstm_kernels.hip"), os.path.join(CSRC, "mlstm_bf16.hip"),
+           os.path.join(CSRC, "mlstm_abi.cpp")]
 
 # Packed-fp32 VALU instructions are turned off for all device code.
 HIPCC_FLAGS = [

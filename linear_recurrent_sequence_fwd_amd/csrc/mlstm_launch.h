@@ -71,4 +71,13 @@ hipError_t launch_out(const FwdLaunch& a, const GateBuffers& gb, const ChunkStat
 hipError_t launch_copy_state(const FwdLaunch& a, hipStream_t s);
 hipError_t launch_step(const StepLaunch& a, hipStream_t s);
 
+// bfloat16 kernels with transposed LDS operand loads (mlstm_bf16.hip). The
+// state pass takes any d_v multiple of 64; the output kernel needs
+// bf16_fast_path() (d_v a multiple of 128).
+bool bf16_fast_path(const FwdLaunch& a);
+hipError_t launch_state_bf16(const FwdLaunch& a, const GateBuffers& gb, const ChunkStates& cs,
+                             hipStream_t s);
+hipError_t launch_out_bf16(const FwdLaunch& a, const GateBuffers& gb, const ChunkStates& cs,
+                           hipStream_t s);
+
 }  // namespace mlstm_impl
