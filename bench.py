@@ -244,6 +244,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -259,6 +261,16 @@ def main():
     ev = HipEvents()
     cfg = WORKLOAD
     B, H, T, K, V = cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"]
+
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {n} bytes read and written per launch, 3 launches")
+        del src, dst
 
     log(f"[bench] inputs 7B-layer B={B} H={H} T={T} d_qk={K} d_v={V} bf16")
     x, d = make_device_inputs(torch, cfg, "bf16", seed=0)

@@ -103,7 +103,7 @@ int validate_fwd(const mlstm_fwd_args* a) {
 }
 
 struct WsLayout {
-  size_t u, b, mp, rs, g, U, R, Cs, ns, ms, total;
+  size_t u, b, mp, rs, w0, g, U, R, Cs, ns, ms, total;
 };
 
 WsLayout layout(int64_t BH, int64_t T, int64_t Nc, int64_t K, int64_t V, int64_t cs_elem, bool states) {
@@ -114,6 +114,7 @@ WsLayout layout(int64_t BH, int64_t T, int64_t Nc, int64_t K, int64_t V, int64_t
   w.b = take(BH * T * 8);
   w.mp = take(BH * T * 8);
   w.rs = take(BH * T * 4);
+  w.w0 = take(BH * T * 4);
   w.g = take(BH * Nc * 8);
   w.U = take(BH * Nc * 8);
   w.R = take(BH * Nc * 4);
@@ -132,6 +133,7 @@ mlstm_impl::GateBuffers gate_buffers(char* ws, const WsLayout& w) {
   gb.b = reinterpret_cast<double*>(ws + w.b);
   gb.mp = reinterpret_cast<double*>(ws + w.mp);
   gb.rs = reinterpret_cast<int*>(ws + w.rs);
+  gb.w0 = reinterpret_cast<float*>(ws + w.w0);
   gb.g = reinterpret_cast<double*>(ws + w.g);
   gb.U = reinterpret_cast<double*>(ws + w.U);
   gb.R = reinterpret_cast<int*>(ws + w.R);

@@ -38,6 +38,18 @@ __device__ __forceinline__ bf16x8 ld_frag_tr(const __bf16* X, int P, int kin0, i
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Calls f(std::integral_constant<int, s>) for s = 0..N-1, unrolled.
+template <typename F, int... S>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, S...>) {
+  (f(std::integral_constant<int, S>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+constexpr int kStatePrefetch = 4;   // token blocks in flight per state-pass workgroup
+
 __device__ __forceinline__ bf16x8 zero8() {
   bf16x8 z;
 #pragma unroll
@@ -68,15 +80,20 @@ struct StateArgsB {
 };
 
 // One workgroup per (head, 64 k x 64 v tile of C^T), four waves of 32 x 32.
-// Walks the sequence in 64-token blocks: block b's K and V rows are loaded two
-// blocks ahead into registers, written to LDS buffer b%2 (V scaled by the
-// block's weights w_j), then contracted over tokens on MFMA. At each chunk
-// start the carried tile is stored (bf16) and rescaled. The normaliser n is
-// the same contraction with V replaced by ones; the waves with wv = 0 of the
+// Walks the sequence in 64-token blocks. Block b's K and V rows and weights
+// are loaded NPF blocks ahead into registers (issued in the order they are
+// consumed, so the in-order vmcnt waits never drain the ring), written to LDS
+// buffer b%2 with V scaled by the chunk-local weights w0_j = exp(u_j - U_c),
+// and contracted over tokens on MFMA into a per-chunk accumulator. At the
+// chunk's end the carried tile becomes decay*C + alpha*acc_chunk with
+// Rm = max(m_prev, U_c), decay = exp(m_prev - Rm), alpha = exp(U_c - Rm), and
+// m advances to g_c + Rm; at the next chunk's start it is stored (bf16). The
+// chunk scalars (g, U, R) are loaded one chunk ahead. The normaliser n is the
+// same contraction with V replaced by ones: the waves with wv = 0 of the
 // v-tile-0 workgroups compute it as one more 16-column MFMA tile, with each
 // weight split into two bf16 terms (w = hi + lo) so that n keeps about 17
-// bits: rows where n^T q nearly cancels would magnify a bf16-rounded n.
-template <int K>
+// bits, because rows where n^T q nearly cancels would magnify a rounded n.
+template <int K, int NPF>
 __global__ __launch_bounds__(kThreads) void state_kernel_bf16(StateArgsB a) {
   constexpr int KT = K / 64;
   constexpr int P = kTile + 16;     // LDS row pitch (elements)
@@ -93,12 +110,12 @@ __global__ __launch_bounds__(kThreads) void state_kernel_bf16(StateArgsB a) {
   const int wk = w & 1, wv = w >> 1;
   const bool n_tile = (vt == 0) && (wv == 0);
 
-  f32x4 acc[2][2], nacc[2];
+  f32x4 acc[2][2], tacc[2][2], nacc[2], tn[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    nacc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    nacc[x] = tn[x] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int y = 0; y < 2; ++y) acc[x][y] = tacc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   double m_prev = 0.0;
   if (a.C0) {
@@ -116,42 +133,51 @@ __global__ __launch_bounds__(kThreads) void state_kernel_bf16(StateArgsB a) {
     m_prev = (double)a.m0[bh];
   }
 
-  const __bf16* kb = a.k + bh * T * K + 64 * kt;
-  const __bf16* vbp = a.v + bh * T * V + 64 * vt;
-  const double* ub = a.gb.u + bh * T;
+  // this thread stages rows r0 and r0 + 32 of each block, columns 8 cg .. 8 cg + 7
+  const int r0 = tid >> 3, cg = tid & 7;
+  const __bf16* kp = a.k + (bh * T + r0) * K + 64 * kt + 8 * cg;
+  const __bf16* vp = a.v + (bh * T + r0) * V + 64 * vt + 8 * cg;
+  const float* wp = a.gb.w0 + bh * T + r0;
   const int nsb = (int)((T + kTile - 1) / kTile);
 
-  // prefetch ring: two blocks in flight, two 16-byte vectors of K and V per thread
-  bf16x8 pk[2][2], pv[2][2];
-  double pu[2][2];
-  auto issue = [&](int sb, int slot) {
+  bf16x8 pk[NPF][2], pv[NPF][2];
+  float pw[NPF][2];
+#pragma unroll
+  for (int s = 0; s < NPF; ++s)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) { pk[s][e] = zero8(); pv[s][e] = zero8(); pw[s][e] = 0.f; }
+  // rows beyond T keep finite stale values in pk/pv and weight 0
+  auto issue = [&](int sb, auto slot_c) {
+    constexpr int SLOT = decltype(slot_c)::value;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int it = tid + kThreads * e;
-      const int row = it >> 3, cg = it & 7;
-      const int64_t t = (int64_t)sb * kTile + row;
-      if (sb < nsb && t < T) {
-        pk[slot][e] = *reinterpret_cast<const bf16x8*>(kb + t * K + 8 * cg);
-        pv[slot][e] = *reinterpret_cast<const bf16x8*>(vbp + t * V + 8 * cg);
-        pu[slot][e] = ub[t];
+      const int64_t t = (int64_t)sb * kTile + r0 + 32 * e;
+      const int64_t off = (int64_t)sb * kTile + 32 * e;
+      if (t < T) {
+        pk[SLOT][e] = *reinterpret_cast<const bf16x8*>(kp + off * K);
+        pv[SLOT][e] = *reinterpret_cast<const bf16x8*>(vp + off * V);
+        pw[SLOT][e] = wp[off];
       } else {
-        pk[slot][e] = zero8();
-        pv[slot][e] = zero8();
-        pu[slot][e] = -INFINITY;
+        pw[SLOT][e] = 0.f;
       }
     }
   };
 
-  double Rm = 0.0, m_next = 0.0;
-  int Rc = -1;
+  // chunk scalars: current (cg_, cU, cR) and the next chunk's, loaded a chunk ahead
+  double cgv = a.gb.g[bh * a.Nc], cUv = a.gb.U[bh * a.Nc];
+  int cRv = a.gb.R[bh * a.Nc];
+  double ngv = 0.0, nUv = 0.0;
+  int nRv = -1;
+  int64_t c = 0;
+  int jc = 0;
+  int Lc = (int)min((int64_t)a.L, T);
+  float decay = 1.f, alpha = 1.f;
+  double m_next = 0.0;
+
   auto body = [&](int sb, auto slot_c) {
     constexpr int SLOT = decltype(slot_c)::value;
-    const int64_t tb = (int64_t)sb * kTile;
-    const int64_t c = tb / a.L;
-    const int64_t t0 = c * a.L;
-    const int jc = (int)(tb - t0);
-    const int Lc = (int)min((int64_t)a.L, T - t0);
-    if (jc == 0) {
+    if (sb >= nsb) return;
+    if (jc == 0) {   // chunk start: store the carried state, derive this chunk's scalars
       if (a.Cs) {
         __bf16* Cs = a.Cs + (bh * a.Nc + c) * V * K;
 #pragma unroll
@@ -169,26 +195,22 @@ __global__ __launch_bounds__(kThreads) void state_kernel_bf16(StateArgsB a) {
         }
         if (tile == 0 && tid == 0) a.ms[bh * a.Nc + c] = m_prev;
       }
-      const double gc = a.gb.g[bh * a.Nc + c];
-      const double Uc = a.gb.U[bh * a.Nc + c];
-      Rc = a.gb.R[bh * a.Nc + c];
-      Rm = fmax(Rc >= 0 ? -INFINITY : m_prev, Uc);
+      double Rm = fmax(cRv >= 0 ? -INFINITY : m_prev, cUv);
       if (Rm == -INFINITY) Rm = 0.0;
-      const float decay = Rc >= 0 ? 0.f : expf((float)(m_prev - Rm));
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        nacc[x] *= decay;
-#pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] *= decay;
+      decay = cRv >= 0 ? 0.f : expf((float)(m_prev - Rm));
+      alpha = cUv == -INFINITY ? 0.f : expf((float)(cUv - Rm));
+      m_next = cgv + Rm;
+      if (c + 1 < a.Nc) {
+        ngv = a.gb.g[bh * a.Nc + c + 1];
+        nUv = a.gb.U[bh * a.Nc + c + 1];
+        nRv = a.gb.R[bh * a.Nc + c + 1];
       }
-      m_next = gc + Rm;
     }
     const int buf = sb & 1;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const int it = tid + kThreads * e;
-      const int row = it >> 3, cg = it & 7;
-      const float wf = (jc + row < Lc && jc + row >= Rc) ? expf((float)(pu[SLOT][e] - Rm)) : 0.f;
+      const int row = r0 + 32 * e;
+      const float wf = pw[SLOT][e];
       *reinterpret_cast<bf16x8*>(&sK[buf][row * P + 8 * cg]) = pk[SLOT][e];
       *reinterpret_cast<bf16x8*>(&sV[buf][row * P + 8 * cg]) = scale8(pv[SLOT][e], wf);
       if (cg == 0) {
@@ -197,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void state_kernel_bf16(StateArgsB a) {
         sw[buf][1][row] = (__bf16)(wf - (float)hi);
       }
     }
-    issue(sb + 2, SLOT);
+    if (sb + NPF < nsb) issue(sb + NPF, slot_c);
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < kTile; kk += 32) {
@@ -209,23 +231,39 @@ __global__ __launch_bounds__(kThreads) void state_kernel_bf16(StateArgsB a) {
 #pragma unroll
       for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] = mma(A[x], B[y], acc[x][y]);
+        for (int y = 0; y < 2; ++y) tacc[x][y] = mma(A[x], B[y], tacc[x][y]);
       if (n_tile) {
         const bf16x8 Bh = *reinterpret_cast<const bf16x8*>(&sw[buf][0][kk + 8 * g]);
         const bf16x8 Bl = *reinterpret_cast<const bf16x8*>(&sw[buf][1][kk + 8 * g]);
 #pragma unroll
-        for (int x = 0; x < 2; ++x) nacc[x] = mma(A[x], Bl, mma(A[x], Bh, nacc[x]));
+        for (int x = 0; x < 2; ++x) tn[x] = mma(A[x], Bl, mma(A[x], Bh, tn[x]));
       }
     }
-    if (jc + kTile >= Lc) m_prev = m_next;
+    jc += kTile;
+    if (jc >= Lc) {   // chunk end: fold the chunk's contribution into the carried state
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        nacc[x] = decay * nacc[x] + alpha * tn[x];
+        tn[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          acc[x][y] = decay * acc[x][y] + alpha * tacc[x][y];
+          tacc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      m_prev = m_next;
+      ++c;
+      jc = 0;
+      Lc = (int)min((int64_t)a.L, T - c * a.L);
+      cgv = ngv; cUv = nUv; cRv = nRv;
+    }
   };
 
-  issue(0, 0);
-  issue(1, 1);
-  for (int sb = 0; sb < nsb; sb += 2) {
-    body(sb, std::integral_constant<int, 0>{});
-    if (sb + 1 < nsb) body(sb + 1, std::integral_constant<int, 1>{});
-  }
+  static_for<NPF>([&](auto s) {
+    if (decltype(s)::value < nsb) issue(decltype(s)::value, s);
+  });
+  for (int sb = 0; sb < nsb; sb += NPF)
+    static_for<NPF>([&](auto s) { body(sb + decltype(s)::value, s); });
 
   if (a.C_out) {
     float* Co = a.C_out + bh * V * K;
@@ -260,25 +298,36 @@ struct OutArgsB {
   int L;
 };
 
-constexpr int kOutThreads = 512;   // eight wave64
+constexpr float kLog2e = 1.4426950408889634f;
 
-// One workgroup per (head, 64-row query tile, 128*NT value columns). Wave w
-// owns all 64 rows of the columns [16 NT w, 16 NT (w+1)) of the block. The
-// score tile S^T (keys x rows) is split as (w mod 4) -> 16 keys,
-// (w / 4) -> 32 rows, with the keys' rows of K read straight from global
-// memory; P goes through LDS, V is staged row-major and read transposed.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// One workgroup per (head, 64-row query tile, 64*NT value columns), four
+// waves; wave w owns all 64 rows of the block's columns [16 NT w, 16 NT (w+1))
+// and the 16 keys [16 w, 16 w + 16) of each score tile. LDS stays under 80 KiB
+// so that two workgroups share a CU. Global loads are issued in the order they
+// are consumed (Q, n, state fragments a few k-steps ahead, then per key block
+// K fragments and the V tile one block ahead, the O tile during the last
+// block). Decay weights use float32 exponents relative to the first row's
+// stabiliser, exp2(log2e (u_j - ref) - log2e (r_t - ref)).
 template <int K, int NT>
-__global__ __launch_bounds__(kOutThreads) void out_kernel_bf16(OutArgsB a) {
-  constexpr int VB = 128 * NT;
-  constexpr int QP = K + 16;
-  constexpr int VP = VB + 16;
-  constexpr int PP = kTile + 16;
-  constexpr int VVEC = kTile * VB / 8 / kOutThreads;   // 16-byte V vectors per thread
+__global__ __launch_bounds__(kThreads, 2) void out_kernel_bf16(OutArgsB a) {
+  constexpr int VB = 64 * NT;
+  constexpr int QP = K + 8;
+  constexpr int VP = VB + 8;
+  constexpr int PP = kTile + 8;
+  constexpr int VVEC = kTile * VB / 8 / kThreads;   // 16-byte V/O vectors per thread
+  constexpr int QVEC = kTile * K / 8 / kThreads;    // 16-byte Q vectors per thread
+  constexpr int KS = K / 32;                         // k-steps of the contractions over d_qk
+  constexpr int D = 2;                               // state k-steps in flight
   __shared__ __attribute__((aligned(16))) __bf16 sQ[kTile * QP];
   __shared__ __attribute__((aligned(16))) __bf16 sV[kTile * VP];
   __shared__ __attribute__((aligned(16))) __bf16 sP[kTile * PP];
-  __shared__ __attribute__((aligned(16))) double s_r[kTile], s_u[2][kTile];
-  __shared__ __attribute__((aligned(16))) float s_sc[kTile], s_fl[kTile], s_dn[kTile], s_den[4][kTile];
+  __shared__ __attribute__((aligned(16))) float sn[K];
+  __shared__ __attribute__((aligned(16))) float s_u2[2][kTile];
+  __shared__ __attribute__((aligned(16))) float s_r2[kTile], s_sc[kTile], s_fl[kTile], s_dn[kTile];
+  __shared__ __attribute__((aligned(16))) float s_den[4][kTile];
   __shared__ __attribute__((aligned(16))) int s_rs[kTile];
 
   const int64_t V = a.V, T = a.T, BH = a.BH;
@@ -294,56 +343,114 @@ __global__ __launch_bounds__(kOutThreads) void out_kernel_bf16(OutArgsB a) {
   const int nrows = (int)min((int64_t)kTile, T - row0);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
-  const int col0 = w * 16 * NT;                 // wave's first column within the block
+  const int col0 = w * 16 * NT;
 
-  // carried state of this chunk: per-chunk states, or the caller's initial state
   const bool chunk_states = a.Cs != nullptr;
   const bool has_state = chunk_states ? (c > 0 || !a.zero_first) : (a.C0f != nullptr);
   const double m_prev = !has_state ? 0.0
                         : (chunk_states ? a.ms[bh * a.Nc + c] : (double)a.m0[bh]);
+  const int64_t vrow0 = vb * VB + col0;
 
-  if (tid < kTile) {
-    double r = 0.0;
-    float sc = 0.f, fl = 1.f;
-    int rs = 0;
-    if (tid < nrows) {
-      const int64_t t = bh * T + row0 + tid;
-      rs = a.gb.rs[t];
-      const bool carry = has_state && rs < 0;
-      r = fmax(carry ? m_prev : -INFINITY, a.gb.mp[t]);
-      if (r == -INFINITY) r = 0.0;
-      sc = carry ? expf((float)(m_prev - r)) : 0.f;
-      fl = expf((float)(-(a.gb.b[t] + r)));
-    }
-    s_r[tid] = r;
-    s_sc[tid] = sc;
-    s_fl[tid] = fl;
-    s_rs[tid] = rs;
-    s_u[0][tid] = tid < (int)min((int64_t)kTile, T - t0) ? a.gb.u[bh * T + t0 + tid] : -INFINITY;
-  }
-  {  // Q tile, row-major
-    constexpr int QV = K / 8;
+  // ---------------- prologue: loads in consumption order
+  bf16x8 pq[QVEC];
+  {
     const __bf16* qg = a.q + (bh * T + row0) * K;
-    for (int it = tid; it < kTile * QV; it += kOutThreads) {
-      const int row = it / QV, cv = it % QV;
-      const bf16x8 x = row < nrows ? *reinterpret_cast<const bf16x8*>(qg + (int64_t)row * K + 8 * cv) : zero8();
-      *reinterpret_cast<bf16x8*>(&sQ[row * QP + 8 * cv]) = x;
+#pragma unroll
+    for (int e = 0; e < QVEC; ++e) {
+      const int it = tid + kThreads * e;
+      const int row = it / (K / 8), cv = it % (K / 8);
+      pq[e] = row < nrows ? *reinterpret_cast<const bf16x8*>(qg + (int64_t)row * K + 8 * cv) : zero8();
     }
   }
-  // V tile of key block 0 in flight while the carried-state term runs
-  bf16x8 pv[VVEC];
-  auto issue_v = [&](int jb) {
-    const int64_t key0 = t0 + (int64_t)jb * kTile;
-    const int nkeys = (int)min((int64_t)kTile, T - key0);
-    const __bf16* vg = a.v + (bh * T + key0) * V + vb * VB;
+  float nval = 0.f;
+  const float* nsrc = !has_state ? nullptr : (chunk_states ? a.ns + (bh * a.Nc + c) * K : a.n0 + bh * K);
+  if (has_state && tid < K) nval = nsrc[tid];
+  // row data (threads 0..63): stabiliser inputs of row tid and of row 0 (the reference)
+  double mp_t = 0.0, b_t = 0.0, mp_0 = 0.0, u_k = -INFINITY;
+  int rs_t = 0, rs_0 = 0;
+  if (tid < kTile) {
+    const int64_t tb = bh * T + row0;
+    mp_0 = a.gb.mp[tb];
+    rs_0 = a.gb.rs[tb];
+    if (tid < nrows) {
+      mp_t = a.gb.mp[tb + tid];
+      b_t = a.gb.b[tb + tid];
+      rs_t = a.gb.rs[tb + tid];
+    }
+    if (t0 + tid < T) u_k = a.gb.u[bh * T + t0 + tid];
+  }
+  bf16x8 Bst[D][NT];
+  const __bf16* Cst = chunk_states ? a.Cs + (bh * a.Nc + c) * V * K : nullptr;
+  const float* Cf = chunk_states ? nullptr : (a.C0f ? a.C0f + bh * V * K : nullptr);
+  auto load_state = [&](int s, auto slot_c) {
+    constexpr int SL = decltype(slot_c)::value;
 #pragma unroll
-    for (int e = 0; e < VVEC; ++e) {
-      const int it = tid + kOutThreads * e;
-      const int row = it / (VB / 8), cv = it % (VB / 8);
-      pv[e] = row < nkeys ? *reinterpret_cast<const bf16x8*>(vg + (int64_t)row * V + 8 * cv) : zero8();
+    for (int y = 0; y < NT; ++y) {
+      const int64_t off = (vrow0 + 16 * y + i) * K + 32 * s + 8 * g;
+      if (Cst) {
+        Bst[SL][y] = *reinterpret_cast<const bf16x8*>(Cst + off);
+      } else {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(Cf + off);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(Cf + off + 4);
+        bf16x8 r;
+        r[0] = (__bf16)x0[0]; r[1] = (__bf16)x0[1]; r[2] = (__bf16)x0[2]; r[3] = (__bf16)x0[3];
+        r[4] = (__bf16)x1[0]; r[5] = (__bf16)x1[1]; r[6] = (__bf16)x1[2]; r[7] = (__bf16)x1[3];
+        Bst[SL][y] = r;
+      }
     }
   };
-  issue_v(0);
+  if (has_state) {
+    static_for<D>([&](auto s) {
+      if (decltype(s)::value < KS) load_state(decltype(s)::value, s);
+    });
+  }
+  bf16x8 Kf[KS];
+  auto load_k = [&](int jb) {
+    const int64_t key = t0 + (int64_t)jb * kTile + 16 * w + i;
+    const __bf16* kg = a.k + (bh * T + key) * K + 8 * g;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) Kf[s] = key < T ? *reinterpret_cast<const bf16x8*>(kg + 32 * s) : zero8();
+  };
+  load_k(0);
+  bf16x8 pv[VVEC];
+  auto load_tile = [&](const __bf16* src, int64_t rows_valid) {   // 64 rows x VB columns, row pitch V
+#pragma unroll
+    for (int e = 0; e < VVEC; ++e) {
+      const int it = tid + kThreads * e;
+      const int row = it / (VB / 8), cv = it % (VB / 8);
+      pv[e] = row < rows_valid ? *reinterpret_cast<const bf16x8*>(src + (int64_t)row * V + 8 * cv) : zero8();
+    }
+  };
+  load_tile(a.v + (bh * T + t0) * V + vb * VB, min((int64_t)kTile, T - t0));
+
+  // ---------------- prologue: LDS fills
+#pragma unroll
+  for (int e = 0; e < QVEC; ++e) {
+    const int it = tid + kThreads * e;
+    const int row = it / (K / 8), cv = it % (K / 8);
+    *reinterpret_cast<bf16x8*>(&sQ[row * QP + 8 * cv]) = pq[e];
+  }
+  if (tid < K) sn[tid] = nval;
+  double ref = 0.0;
+  if (tid < kTile) {
+    const bool carry0 = has_state && rs_0 < 0;
+    ref = fmax(carry0 ? m_prev : -INFINITY, mp_0);
+    if (ref == -INFINITY) ref = 0.0;
+    float r2 = 0.f, sc = 0.f, fl = 1.f;
+    if (tid < nrows) {
+      const bool carry = has_state && rs_t < 0;
+      double r = fmax(carry ? m_prev : -INFINITY, mp_t);
+      if (r == -INFINITY) r = 0.0;
+      r2 = (float)((r - ref) * (double)kLog2e);
+      sc = carry ? expf((float)(m_prev - r)) : 0.f;
+      fl = expf((float)(-(b_t + r)));
+    }
+    s_r2[tid] = r2;
+    s_sc[tid] = sc;
+    s_fl[tid] = fl;
+    s_rs[tid] = rs_t;
+    s_u2[0][tid] = (float)((u_k - ref) * (double)kLog2e);
+  }
   __syncthreads();
 
   f32x4 acc[4][NT];
@@ -352,52 +459,28 @@ __global__ __launch_bounds__(kOutThreads) void out_kernel_bf16(OutArgsB a) {
 #pragma unroll
     for (int y = 0; y < NT; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // ---------------- carried-state term: (Q C~^T) scaled per row, and sc_t (q_t . n~)
   if (has_state) {
-    {  // normaliser of the carried state: sc_t (q_t . n~)
-      const int row = tid >> 3, part = tid & 7;
-      const float* nst = chunk_states ? a.ns + (bh * a.Nc + c) * K : a.n0 + bh * K;
+    {
+      const int row = tid >> 2, part = tid & 3;
       float d = 0.f;
-#pragma unroll
-      for (int kk = part * (K / 8); kk < (part + 1) * (K / 8); ++kk) d += (float)sQ[row * QP + kk] * nst[kk];
+#pragma unroll 8
+      for (int kk = part * (K / 4); kk < (part + 1) * (K / 4); ++kk) d += (float)sQ[row * QP + kk] * sn[kk];
       d += __shfl_xor(d, 1, 64);
       d += __shfl_xor(d, 2, 64);
-      d += __shfl_xor(d, 4, 64);
       if (part == 0) s_dn[row] = d * s_sc[row];
     }
-    const int64_t vrow0 = vb * VB + col0;
-    if (chunk_states) {
-      const __bf16* Cst = a.Cs + (bh * a.Nc + c) * V * K;
-#pragma unroll 2
-      for (int kk = 0; kk < K; kk += 32) {
-        bf16x8 A[4], B[NT];
+    static_for<KS>([&](auto s_c) {
+      constexpr int s = decltype(s_c)::value;
+      bf16x8 A[4];
 #pragma unroll
-        for (int y = 0; y < NT; ++y)
-          B[y] = *reinterpret_cast<const bf16x8*>(Cst + (vrow0 + 16 * y + i) * K + kk + 8 * g);
+      for (int x = 0; x < 4; ++x) A[x] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * x + i) * QP + 32 * s + 8 * g]);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) A[x] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * x + i) * QP + kk + 8 * g]);
+      for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-          for (int y = 0; y < NT; ++y) acc[x][y] = mma(A[x], B[y], acc[x][y]);
-      }
-    } else {
-      const float* Cst = a.C0f + bh * V * K;
-      for (int kk = 0; kk < K; kk += 32) {
-        bf16x8 A[4], B[NT];
-#pragma unroll
-        for (int y = 0; y < NT; ++y) {
-          const float* p = Cst + (vrow0 + 16 * y + i) * K + kk + 8 * g;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) B[y][e] = (__bf16)p[e];
-        }
-#pragma unroll
-        for (int x = 0; x < 4; ++x) A[x] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * x + i) * QP + kk + 8 * g]);
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-#pragma unroll
-          for (int y = 0; y < NT; ++y) acc[x][y] = mma(A[x], B[y], acc[x][y]);
-      }
-    }
+        for (int y = 0; y < NT; ++y) acc[x][y] = mma(A[x], Bst[s % D][y], acc[x][y]);
+      if constexpr (s + D < KS) load_state(s + D, std::integral_constant<int, s % D>{});
+    });
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -410,66 +493,63 @@ __global__ __launch_bounds__(kOutThreads) void out_kernel_bf16(OutArgsB a) {
     s_dn[tid] = 0.f;
   }
 
-  // intra-chunk blocks: keys of block jb <= st
-  const int jt = w & 3;            // this wave's 16 keys of the score tile
-  const int tp = w >> 2;           // this wave's 32 rows (two 16-row tiles)
-  float rsum[2] = {0.f, 0.f};
+  // ---------------- intra-chunk key blocks jb = 0..st
+  float rsum[4] = {0.f, 0.f, 0.f, 0.f};
   for (int jb = 0; jb <= st; ++jb) {
     const int64_t key0 = t0 + (int64_t)jb * kTile;
     __syncthreads();   // previous block's P V done: sV, sP free
 #pragma unroll
     for (int e = 0; e < VVEC; ++e) {
-      const int it = tid + kOutThreads * e;
+      const int it = tid + kThreads * e;
       const int row = it / (VB / 8), cv = it % (VB / 8);
       *reinterpret_cast<bf16x8*>(&sV[row * VP + 8 * cv]) = pv[e];
     }
+    double u_next = -INFINITY;
     if (jb < st) {
-      issue_v(jb + 1);
-      if (tid < kTile) {
-        const int64_t key1 = key0 + kTile;
-        s_u[(jb + 1) & 1][tid] = key1 + tid < T ? a.gb.u[bh * T + key1 + tid] : -INFINITY;
-      }
+      load_tile(a.v + (bh * T + key0 + kTile) * V + vb * VB, min((int64_t)kTile, T - key0 - kTile));
+      if (tid < kTile && key0 + kTile + tid < T) u_next = a.gb.u[bh * T + key0 + kTile + tid];
+    } else {
+      load_tile(a.o + (bh * T + row0) * V + vb * VB, nrows);   // O tile for the epilogue
     }
-    // S^T tile: 16 keys x 32 rows for this wave
-    bf16x8 Kf[K / 32];
-    {
-      const int64_t key = key0 + 16 * jt + i;
-      const __bf16* kg = a.k + (bh * T + key) * K + 8 * g;
+    // S^T: this wave's 16 keys x 64 rows
+    f32x4 sacc[4];
 #pragma unroll
-      for (int s = 0; s < K / 32; ++s)
-        Kf[s] = key < T ? *reinterpret_cast<const bf16x8*>(kg + 32 * s) : zero8();
-    }
-    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int z = 0; z < 4; ++z) sacc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < K / 32; ++s) {
+    for (int s = 0; s < KS; ++s) {
 #pragma unroll
-      for (int z = 0; z < 2; ++z) {
-        const bf16x8 B = *reinterpret_cast<const bf16x8*>(&sQ[(32 * tp + 16 * z + i) * QP + 32 * s + 8 * g]);
+      for (int z = 0; z < 4; ++z) {
+        const bf16x8 B = *reinterpret_cast<const bf16x8*>(&sQ[(16 * z + i) * QP + 32 * s + 8 * g]);
         sacc[z] = mma(Kf[s], B, sacc[z]);
       }
     }
+    if (jb < st) load_k(jb + 1);
+    // P = S o D: lane holds S^T[j = 16 w + 4 g + r][t = 16 z + i]
+    float u2[4];
 #pragma unroll
-    for (int z = 0; z < 2; ++z) {
-      const int tl = 32 * tp + 16 * z + i;        // row of this lane
-      const int tq = st * kTile + tl;             // its position in the chunk
-      const double rr = s_r[tl];
+    for (int r = 0; r < 4; ++r) u2[r] = s_u2[jb & 1][16 * w + 4 * g + r];
+#pragma unroll
+    for (int z = 0; z < 4; ++z) {
+      const int tl = 16 * z + i;
+      const int tq = st * kTile + tl;
+      const float r2 = s_r2[tl];
       const int rs = s_rs[tl];
-      bf16x4 pk;
+      bf16x4 pk4;
       float psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int jl = 16 * jt + 4 * g + r;
-        const int jk = jb * kTile + jl;
+        const int jk = jb * kTile + 16 * w + 4 * g + r;
         const bool keep = (tl < nrows) && (jk <= tq) && (jk >= rs);
-        const float p = keep ? sacc[z][r] * expf((float)(s_u[jb & 1][jl] - rr)) : 0.f;
+        const float p = keep ? sacc[z][r] * fast_exp2(u2[r] - r2) : 0.f;
         psum += p;
-        pk[r] = (__bf16)p;
+        pk4[r] = (__bf16)p;
       }
-      *reinterpret_cast<bf16x4*>(&sP[tl * PP + 16 * jt + 4 * g]) = pk;
+      *reinterpret_cast<bf16x4*>(&sP[tl * PP + 16 * w + 4 * g]) = pk4;
       psum += __shfl_xor(psum, 16, 64);
       psum += __shfl_xor(psum, 32, 64);
       rsum[z] += psum;
     }
+    if (jb < st && tid < kTile) s_u2[(jb + 1) & 1][tid] = (float)((u_next - ref) * (double)kLog2e);
     __syncthreads();   // sP and sV complete
 #pragma unroll
     for (int jj = 0; jj < kTile; jj += 32) {
@@ -486,17 +566,16 @@ __global__ __launch_bounds__(kOutThreads) void out_kernel_bf16(OutArgsB a) {
   }
   if (g == 0) {
 #pragma unroll
-    for (int z = 0; z < 2; ++z) s_den[jt][32 * tp + 16 * z + i] = rsum[z];
+    for (int z = 0; z < 4; ++z) s_den[w][16 * z + i] = rsum[z];
   }
-  __syncthreads();   // all P V done; s_den complete; sV free for the output tile
+  __syncthreads();   // all P V done; s_den complete; sV free
 
-  // output gate: stage O through LDS, combine in registers, write h back through LDS
-  const int64_t obase = (bh * T + row0) * V + vb * VB;
-  for (int it = tid; it < kTile * VB / 8; it += kOutThreads) {
+  // ---------------- output gate and normalisation, staged through LDS
+#pragma unroll
+  for (int e = 0; e < VVEC; ++e) {
+    const int it = tid + kThreads * e;
     const int row = it / (VB / 8), cv = it % (VB / 8);
-    const bf16x8 x = row < nrows ? *reinterpret_cast<const bf16x8*>(a.o + obase + (int64_t)row * V + 8 * cv)
-                                 : zero8();
-    *reinterpret_cast<bf16x8*>(&sV[row * VP + 8 * cv]) = x;
+    *reinterpret_cast<bf16x8*>(&sV[row * VP + 8 * cv]) = pv[e];
   }
   __syncthreads();
 #pragma unroll
@@ -505,15 +584,19 @@ __global__ __launch_bounds__(kOutThreads) void out_kernel_bf16(OutArgsB a) {
     for (int r = 0; r < 4; ++r) {
       const int tl = 16 * x + 4 * g + r;
       const float den = s_den[0][tl] + s_den[1][tl] + s_den[2][tl] + s_den[3][tl] + s_dn[tl];
-      const float inv = 1.f / fmaxf(fmaxf(fabsf(den), s_fl[tl]), FLT_MIN);
+      const float inv = fast_rcp(fmaxf(fmaxf(fabsf(den), s_fl[tl]), FLT_MIN));
 #pragma unroll
       for (int y = 0; y < NT; ++y) {
         __bf16* p = &sV[tl * VP + col0 + 16 * y + i];
-        *p = (__bf16)(sigmoid((float)*p) * acc[x][y][r] * inv);
+        const float og = fast_rcp(1.f + fast_exp2(-kLog2e * (float)*p));
+        *p = (__bf16)(og * acc[x][y][r] * inv);
       }
     }
   __syncthreads();
-  for (int it = tid; it < kTile * VB / 8; it += kOutThreads) {
+  const int64_t obase = (bh * T + row0) * V + vb * VB;
+#pragma unroll
+  for (int e = 0; e < VVEC; ++e) {
+    const int it = tid + kThreads * e;
     const int row = it / (VB / 8), cv = it % (VB / 8);
     if (row < nrows)
       *reinterpret_cast<bf16x8*>(a.h + obase + (int64_t)row * V + 8 * cv) =
@@ -534,7 +617,7 @@ hipError_t run_state_b(const FwdLaunch& f, const GateBuffers& gb, const ChunkSta
   a.T = f.T; a.Nc = f.Nc; a.V = f.V; a.BH = f.BH; a.L = f.L;
   const int64_t grid = f.BH * (K / 64) * (f.V / 64);
   mark_before(K_STATE, s);
-  hipLaunchKernelGGL((state_kernel_bf16<K>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((state_kernel_bf16<K, kStatePrefetch>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   mark_after(K_STATE, s);
   return hipGetLastError();
 }
@@ -555,16 +638,16 @@ hipError_t run_out_b(const FwdLaunch& f, const GateBuffers& gb, const ChunkState
   a.zero_first = f.C0 == nullptr;
   a.T = f.T; a.Nc = f.Nc; a.V = f.V; a.BH = f.BH; a.L = f.L;
   const int64_t nqt = (f.T + kTile - 1) / kTile;
-  const int64_t grid = f.BH * nqt * (f.V / (128 * NT));
+  const int64_t grid = f.BH * nqt * (f.V / (64 * NT));
   mark_before(K_OUT, s);
-  hipLaunchKernelGGL((out_kernel_bf16<K, NT>), dim3((unsigned)grid), dim3(kOutThreads), 0, s, a);
+  hipLaunchKernelGGL((out_kernel_bf16<K, NT>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   mark_after(K_OUT, s);
   return hipGetLastError();
 }
 
 template <int K>
 hipError_t run_out_b_nt(const FwdLaunch& f, const GateBuffers& gb, const ChunkStates& cs, hipStream_t s) {
-  const int64_t nv = f.V / 128;
+  const int64_t nv = f.V / 64;
   if (nv % 4 == 0) return run_out_b<K, 4>(f, gb, cs, s);
   if (nv % 2 == 0) return run_out_b<K, 2>(f, gb, cs, s);
   return run_out_b<K, 1>(f, gb, cs, s);
@@ -572,7 +655,7 @@ hipError_t run_out_b_nt(const FwdLaunch& f, const GateBuffers& gb, const ChunkSt
 
 }  // namespace
 
-bool bf16_fast_path(const FwdLaunch& f) { return f.bf16 && f.V % 128 == 0; }
+bool bf16_fast_path(const FwdLaunch& f) { return f.bf16 && f.V % 64 == 0; }
 
 hipError_t launch_state_bf16(const FwdLaunch& f, const GateBuffers& gb, const ChunkStates& cs, hipStream_t s) {
   switch (f.K) {

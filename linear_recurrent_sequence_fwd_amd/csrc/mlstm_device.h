@@ -15,6 +15,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "mlstm_launch.h"
 

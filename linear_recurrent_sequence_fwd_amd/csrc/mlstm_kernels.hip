@@ -96,11 +96,19 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateArgs a) {
     a.gb.mp[base + j] = cur.v;
     a.gb.rs[base + j] = rcur;
   }
+  __shared__ double sU;
+  __shared__ int sR;
   if (j0 < j1 && j1 == Lc) {
     a.gb.g[bh * a.Nc + c] = run;
     a.gb.U[bh * a.Nc + c] = cur.v;
     a.gb.R[bh * a.Nc + c] = rcur;
+    sU = cur.v;
+    sR = rcur;
   }
+  __syncthreads();
+  // chunk-local weights of the state update: exp(u_j - U) <= 1, zero before a reset
+  for (int j = j0; j < j1; ++j)
+    a.gb.w0[base + j] = (j >= sR && sU != -INFINITY) ? expf((float)(a.gb.u[base + j] - sU)) : 0.f;
 }
 
 // ------------------------------------------------------------------ state pass

@@ -23,6 +23,7 @@ struct GateBuffers {
   double* g;    // chunk total of b
   double* U;    // mp at the chunk's last token
   int* R;       // rs at the chunk's last token
+  float* w0;    // exp(u_j - U) for keys at or after the chunk's last zero forget gate, else 0
 };
 
 // Chunk-start states written by the state pass: Cs [BH][Nc][V][K] (bf16 or

@@ -158,17 +158,17 @@ def test_workspace_checks_and_size():
     need = lib.mlstm_fwd_chunkwise_workspace_size(ctypes.byref(a), 128)
     BH, T, Nc, K, V = 6, 1000, 8, 128, 192
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    expect = 3 * al(BH * T * 8) + al(BH * T * 4) + 2 * al(BH * Nc * 8) + al(BH * Nc * 4) \
+    expect = 3 * al(BH * T * 8) + 2 * al(BH * T * 4) + 2 * al(BH * Nc * 8) + al(BH * Nc * 4) \
         + al(BH * Nc * V * K * 2) + al(BH * Nc * K * 4) + al(BH * Nc * 8)
     assert need == expect
     assert chunkwise(a, chunk=128, ws=None, ws_bytes=need) == WORKSPACE
     assert chunkwise(a, chunk=128, ws=a._next(need), ws_bytes=need - 1) == WORKSPACE
     p = lib.mlstm_fwd_parallel_workspace_size(ctypes.byref(a))
-    assert p == 3 * al(BH * T * 8) + al(BH * T * 4) + 2 * al(BH * 8) + al(BH * 4)
+    assert p == 3 * al(BH * T * 8) + 2 * al(BH * T * 4) + 2 * al(BH * 8) + al(BH * 4)
     # fp32 stores float32 chunk states
     b = fake_fwd(B=1, H=1, T=256, K=64, V=64, dtype=L.MLSTM_FP32)
     nb = lib.mlstm_fwd_chunkwise_workspace_size(ctypes.byref(b), 64)
-    assert nb == 3 * al(256 * 8) + al(256 * 4) + 2 * al(4 * 8) + al(4 * 4) + al(4 * 64 * 64 * 4) \
+    assert nb == 3 * al(256 * 8) + 2 * al(256 * 4) + 2 * al(4 * 8) + al(4 * 4) + al(4 * 64 * 64 * 4) \
         + al(4 * 64 * 4) + al(4 * 8)
 
 
