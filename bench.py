@@ -1,7 +1,8 @@
 """Benchmark of the mLSTM cell forward on one MI355X.
 
-One step = one full chunkwise forward (gate prefix sums, inter-chunk state
-pass, intra-chunk output kernel) over the 7B-layer-shaped workload
+One step = one full chunkwise forward (gate prefix sums per 64-token tile,
+the chunks' end states and their in-order fold, the fused tile kernel that
+produces h) over the 7B-layer-shaped workload
 (B=1, H=8, T=8192, d_qk=256, d_v=512, bf16 q/k/v/o and h, float32 gates),
 inputs resident in HBM. Prints ONE JSON line on stdout; progress goes to
 stderr.
@@ -30,8 +31,10 @@ MFMA_BF16_PEAK = 2.5166e15   # flop/s dense bf16: 256 CU x 2.4 GHz x 4096 flop/c
 METRIC = "mLSTM fwd tokens/s at 7B-layer shape, % bf16 MFMA peak; decode step % HBM BW"
 WORKLOAD = dict(B=1, H=8, T=8192, d_qk=256, d_v=512)
 DECODE = dict(B=64, H=8, d_qk=256, d_v=512, prefill=512)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "out_kernel_7b_layer_traffic.md")
-KERNEL_SRC = os.path.join(ROOT, "linear_recurrent_sequence_fwd_amd", "csrc", "mlstm_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_kernel_7b_layer_traffic.md")
+KERNEL_SRC = os.path.join(ROOT, "linear_recurrent_sequence_fwd_amd", "csrc", "mlstm_fused.hip")
+TILE = 64                    # tokens per tile: the length of the quadratic (intra-tile) form
+LABELS = {"gate": "gate", "state": "chunk_states", "out": "fused"}
 
 
 def log(*a):
@@ -74,25 +77,29 @@ def fwd_bytes(B, H, T, K, V, chunk):
     return B * H * (T * (2 * K + 2 * K + 2 * V + 2 * V + 2 * V + 4 + 4) + 4 * (V * K + K + 1))
 
 
-def fwd_flops(B, H, T, K, V, chunk):
-    """Flops at chunk L: per token-head 2KV (state update) + 2KV (state
-    readout) + L K (causal half of Q K^T) + L V (causal half of P V) + 2K + L."""
-    return B * H * T * (4 * K * V + chunk * (K + V) + 2 * K + chunk)
+def fwd_flops(B, H, T, K, V):
+    """Flops of the method as computed: per token-head 2KV (state readout
+    q C~^T) + 2KV (state update) + TILE K (causal half of Q K^T over a tile)
+    + TILE V (causal half of P V)."""
+    return B * H * T * (4 * K * V + TILE * (K + V))
 
 
 def kernel_bytes(name, B, H, T, K, V, chunk):
     """Algorithmic bytes one launch of a kernel must move (inputs read once,
     outputs written once), at the 7B-layer shape with bf16 data."""
     BH = B * H
-    Nc = -(-T // chunk)
-    state = V * K * 2 + K * 4 + 8                  # one bf16 chunk-start state, n, m
+    Nt = -(-T // TILE)
+    S = -(-Nt // (chunk // TILE))
+    state = 4 * (V * K + K) + 8                    # one float32 chunk state C~, n~ and its stabiliser
     gate_tok = 3 * 8 + 4                           # u, b, mp (float64) and rs (int32)
     if name == "gate":
-        return BH * T * (4 + 4 + gate_tok) + BH * Nc * (8 + 8 + 4)
-    if name == "state":
-        return BH * T * (2 * K + 2 * V + 8) + BH * Nc * (state + 8 + 8 + 4) + BH * (4 * V * K + 4 * K + 4)
-    if name == "out":
-        return BH * T * (2 * K + 2 * K + 2 * V + 2 * V + 2 * V + gate_tok) + BH * (Nc - 1) * state
+        return BH * T * (4 + 4 + gate_tok + 4) + BH * Nt * (8 + 8 + 4)
+    if name == "state":                            # chunks' end states: K, V of chunks 0..S-2; fold
+        t_loc = min(T, (S - 1) * chunk)
+        return BH * t_loc * (2 * K + 2 * V + 8) + BH * (S - 1) * (3 * state + 8)
+    if name == "out":                              # fused tiles: q, k, v, o in, h out, start/final states
+        return BH * T * (2 * K + 2 * K + 2 * V + 2 * V + 2 * V + gate_tok) + BH * Nt * 20 \
+            + BH * (S - 1) * state + BH * state
     raise KeyError(name)
 
 
@@ -238,8 +245,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--chunk", type=int, default=256)
-    ap.add_argument("--sweep", type=str, default="64,128,256", help="chunk sizes reported besides --chunk")
+    ap.add_argument("--chunk", type=int, default=1024,
+                    help="chunk length: the state is materialised at chunk starts (multiple of 64)")
+    ap.add_argument("--sweep", type=str, default="512,2048", help="chunk sizes reported besides --chunk")
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -279,13 +287,25 @@ def main():
     elapsed, per_k = time_chunkwise(torch, M, _lib, ev, d, args.chunk, args.steps, args.warmup)
     ms_step = elapsed / args.steps * 1e3
     tok_s = B * T * args.steps / elapsed
-    flops = fwd_flops(B, H, T, K, V, args.chunk)
+    flops = fwd_flops(B, H, T, K, V)
     flops_ci = B * H * T * 4 * K * V
     path_bytes = fwd_bytes(B, H, T, K, V, args.chunk)
     dom = max(per_k, key=per_k.get)
+    t_dom = per_k[dom] * 1e-6
     kb = kernel_bytes(dom, B, H, T, K, V, args.chunk)
-    achieved = kb / (per_k[dom] * 1e-6)
-    traffic = traffic_from_profile() if dom == "out" else None
+    # the fused kernel carries all of the method's flops; the others are bandwidth work
+    kf = flops if dom == "out" else 0.0
+    hbm_f, mfma_f = kb / t_dom / HBM_PEAK, kf / t_dom / MFMA_BF16_PEAK
+    if mfma_f > hbm_f:
+        roof = {"bound": "mfma", "achieved": kf / t_dom / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
+                "unit": "TFLOP/s", "frac": mfma_f}
+    else:
+        roof = {"bound": "hbm", "achieved": kb / t_dom / 1e9, "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": hbm_f}
+    roof = {"kernel": LABELS[dom], **roof, "hbm_frac": hbm_f, "mfma_frac": mfma_f,
+            "algorithmic_bytes": kb, "algorithmic_flops": kf,
+            "traffic": traffic_from_profile() if dom == "out" else None}
+    per_k = {LABELS[k]: v for k, v in per_k.items()}
     log(f"[bench] {ms_step:.3f} ms/step, {tok_s:.3e} tokens/s, kernels us {per_k}")
 
     sweep = {}
@@ -295,8 +315,8 @@ def main():
         el, pk = time_chunkwise(torch, M, _lib, ev, d, L, max(5, args.steps // 2), 2)
         st = max(5, args.steps // 2)
         sweep[str(L)] = {"ms_per_step": el / st * 1e3, "tokens_per_s": B * T * st / el,
-                         "mfma_frac": fwd_flops(B, H, T, K, V, L) / (el / st) / MFMA_BF16_PEAK,
-                         "kernel_us": pk}
+                         "mfma_frac": flops / (el / st) / MFMA_BF16_PEAK,
+                         "kernel_us": {LABELS[k]: v for k, v in pk.items()}}
         log(f"[bench] sweep chunk={L}: {el / st * 1e3:.3f} ms/step")
 
     out = {
@@ -313,15 +333,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded PCG64 draws with the 7B-layer distributions)",
         "config": {"workload": "mLSTM chunkwise forward, 7B-layer shape", "B": B, "H": H, "T": T,
-                   "d_qk": K, "d_v": V, "chunk": args.chunk, "inputs": "bf16 q/k/v/o, fp32 gates",
+                   "d_qk": K, "d_v": V, "chunk": args.chunk, "tile": TILE,
+                   "inputs": "bf16 q/k/v/o, fp32 gates",
                    "parallelism": "single GPU"},
         "mfma_frac": flops / (ms_step * 1e-3) / MFMA_BF16_PEAK,
         "mfma_frac_chunk_independent": flops_ci / (ms_step * 1e-3) / MFMA_BF16_PEAK,
         "hbm_frac_path": path_bytes / (ms_step * 1e-3) / HBM_PEAK,
         "kernel_us": per_k,
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK,
-                     "traffic": traffic},
+        "roofline": roof,
         "sweep": sweep,
     }
     del d

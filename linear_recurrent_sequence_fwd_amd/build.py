@@ -18,12 +18,15 @@ LIB = os.path.join(PKG, "libmlstm.so")
 ARCH = "gfx950"
 
 SOURCES = [os.path.join(CSRC, "mlstm_kernels.hip"), os.path.join(CSRC, "mlstm_bf16.hip"),
-           os.path.join(CSRC, "mlstm_abi.cpp")]
+           os.path.join(CSRC, "mlstm_fused.hip"), os.path.join(CSRC, "mlstm_abi.cpp")]
 
-# Packed-fp32 VALU instructions are turned off for all device code.
+# Packed-fp32 VALU instructions are turned off for all device code; MFMA
+# accumulators are allocated as VGPRs (the fused kernels apply VALU work to
+# them every tile, which the AGPR form turns into copies).
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
 ]
 

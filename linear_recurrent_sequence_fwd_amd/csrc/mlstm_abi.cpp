@@ -104,6 +104,7 @@ int validate_fwd(const mlstm_fwd_args* a) {
 
 struct WsLayout {
   size_t u, b, mp, rs, w0, g, U, R, Cs, ns, ms, total;
+  size_t Cseg, nseg, mloc, mstart, Gseg;
 };
 
 WsLayout layout(int64_t BH, int64_t T, int64_t Nc, int64_t K, int64_t V, int64_t cs_elem, bool states) {
@@ -123,6 +124,39 @@ WsLayout layout(int64_t BH, int64_t T, int64_t Nc, int64_t K, int64_t V, int64_t
     w.ns = take(BH * Nc * K * 4);
     w.ms = take(BH * Nc * 8);
   }
+  w.total = off;
+  return w;
+}
+
+// bf16 with d_v a multiple of 128 runs the fused kernels: per-64-token gate
+// data, and per chunk its local end state (later its start state).
+bool use_fused(const mlstm_fwd_args* a) {
+  return mlstm_impl::fused_path(a->dtype == MLSTM_BF16, a->d_qk, a->d_v);
+}
+
+struct FusedShape {
+  int64_t Nt, TPS, S;
+};
+
+FusedShape fused_shape(int64_t T, int chunk) {
+  FusedShape f;
+  f.Nt = (T + 63) / 64;
+  f.TPS = chunk / 64;
+  f.S = (f.Nt + f.TPS - 1) / f.TPS;
+  return f;
+}
+
+WsLayout layout_fused(int64_t BH, int64_t T, int chunk, int64_t K, int64_t V) {
+  const FusedShape fs = fused_shape(T, chunk);
+  WsLayout w = layout(BH, T, fs.Nt, K, V, 4, false);
+  size_t off = w.total;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  const int64_t ns = fs.S - 1;
+  w.Cseg = take(BH * ns * V * K * 4);
+  w.nseg = take(BH * ns * K * 4);
+  w.mloc = take(BH * ns * 8);
+  w.mstart = take(BH * ns * 8);
+  w.Gseg = take(BH * ns * 8);
   w.total = off;
   return w;
 }
@@ -194,6 +228,7 @@ extern "C" {
 size_t mlstm_fwd_chunkwise_workspace_size(const mlstm_fwd_args* a, int chunk) {
   if (!a || a->T <= 0 || chunk < 64 || chunk % 64 != 0 || chunk > kMaxChunk) return 0;
   if (a->B < 1 || a->H < 1 || a->d_qk < 1 || a->d_v < 1) return 0;
+  if (use_fused(a)) return layout_fused(a->B * a->H, a->T, chunk, a->d_qk, a->d_v).total;
   const int64_t Nc = (a->T + chunk - 1) / chunk;
   return layout(a->B * a->H, a->T, Nc, a->d_qk, a->d_v, a->dtype == MLSTM_BF16 ? 2 : 4, true).total;
 }
@@ -213,6 +248,22 @@ int mlstm_fwd_chunkwise(const mlstm_fwd_args* a, int chunk, void* workspace, siz
   const size_t need = mlstm_fwd_chunkwise_workspace_size(a, chunk);
   if ((st = check_workspace(a, workspace, workspace_bytes, need))) return st;
   char* ws = static_cast<char*>(workspace);
+  if (use_fused(a)) {
+    const FusedShape fs = fused_shape(a->T, chunk);
+    const mlstm_impl::FwdLaunch ft = fwd_launch(a, 64, fs.Nt);
+    const WsLayout w = layout_fused(ft.BH, ft.T, chunk, ft.K, ft.V);
+    const mlstm_impl::GateBuffers gb = gate_buffers(ws, w);
+    mlstm_impl::SegStates ss;
+    ss.C = reinterpret_cast<float*>(ws + w.Cseg);
+    ss.n = reinterpret_cast<float*>(ws + w.nseg);
+    ss.mloc = reinterpret_cast<double*>(ws + w.mloc);
+    ss.mstart = reinterpret_cast<double*>(ws + w.mstart);
+    ss.G = reinterpret_cast<double*>(ws + w.Gseg);
+    ss.S = (int)fs.S;
+    ss.TPS = (int)fs.TPS;
+    if ((st = hip_status(mlstm_impl::launch_gate(ft, gb, s), "gate kernel"))) return st;
+    return hip_status(mlstm_impl::launch_fused(ft, gb, ss, s), "fused kernels");
+  }
   const WsLayout w = layout(f.BH, f.T, Nc, f.K, f.V, f.bf16 ? 2 : 4, true);
   const mlstm_impl::GateBuffers gb = gate_buffers(ws, w);
   mlstm_impl::ChunkStates cs;

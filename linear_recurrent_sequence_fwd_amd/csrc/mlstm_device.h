@@ -117,7 +117,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 // Exclusive prefix over the 256 threads of a workgroup, one value per thread.
 // `sbuf` holds at least 4 elements of LDS. Contains barriers: call uniformly.
-__device__ double block_excl_sum(double x, double* sbuf) {
+__device__ inline double block_excl_sum(double x, double* sbuf) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   double incl = x;
 #pragma unroll
@@ -135,7 +135,7 @@ __device__ double block_excl_sum(double x, double* sbuf) {
   return off + excl;
 }
 
-__device__ int block_excl_max_int(int x, int* sbuf) {
+__device__ inline int block_excl_max_int(int x, int* sbuf) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int incl = x;
 #pragma unroll
@@ -162,7 +162,7 @@ __device__ __forceinline__ SegMax seg_combine(SegMax l, SegMax r) {
   return SegMax{l.f | r.f, r.f ? r.v : fmax(l.v, r.v)};
 }
 
-__device__ SegMax block_excl_segmax(SegMax x, int* sflag, double* sval) {
+__device__ inline SegMax block_excl_segmax(SegMax x, int* sflag, double* sval) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   SegMax incl = x;
 #pragma unroll

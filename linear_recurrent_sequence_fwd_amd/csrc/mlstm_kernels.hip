@@ -20,7 +20,8 @@
 //
 // Kernels:
 //   gate_kernel   per (head, chunk): b, u, the masked prefix max of u, reset
-//                 positions, chunk totals.
+//                 positions, chunk totals (gate64_kernel: one wave per
+//                 64-token chunk).
 //   state_kernel  per (head, 64x64 tile of C): walks the chunks in order,
 //                 stores each chunk's start state and carries C~ (float32 in
 //                 MFMA accumulators) with C~ <- a C~ + K_c^T diag(w) V_c.
@@ -109,6 +110,59 @@ __global__ __launch_bounds__(kThreads) void gate_kernel(GateArgs a) {
   // chunk-local weights of the state update: exp(u_j - U) <= 1, zero before a reset
   for (int j = j0; j < j1; ++j)
     a.gb.w0[base + j] = (j >= sR && sU != -INFINITY) ? expf((float)(a.gb.u[base + j] - sU)) : 0.f;
+}
+
+// One wave per 64-token chunk (four chunks per workgroup), one token per lane:
+// the same quantities as gate_kernel with the scans done across the wave.
+// The running max restarts at a zero forget gate: lane t takes lane t - d's
+// partial max only when t - d is at or after its own last reset.
+__global__ __launch_bounds__(kThreads) void gate64_kernel(GateArgs a) {
+  const int64_t chunk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (chunk >= a.BH * a.Nc) return;   // whole waves only
+  const int64_t c = chunk % a.Nc, bh = chunk / a.Nc;
+  const int lane = threadIdx.x & 63;
+  const int64_t t0 = c * kTile;
+  const int Lc = (int)min((int64_t)kTile, a.T - t0);
+  const bool valid = lane < Lc;
+  const int64_t base = bh * a.T + t0;
+  const float fi = valid ? a.f_pre[base + lane] : 0.f;
+  const float ii = valid ? a.i_pre[base + lane] : 0.f;
+  const float lf = log_sigmoid(fi);
+  const bool reset = valid && lf == -INFINITY;
+  double b = (valid && !reset) ? (double)lf : 0.0;
+  int rs = reset ? lane : -1;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double yb = __shfl_up(b, d, 64);
+    const int yr = __shfl_up(rs, d, 64);
+    if (lane >= d) {
+      b += yb;
+      rs = max(rs, yr);
+    }
+  }
+  const double u = valid ? (double)ii - b : -INFINITY;
+  double mp = u;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double y = __shfl_up(mp, d, 64);
+    if (lane >= d && lane - d >= rs) mp = fmax(mp, y);
+  }
+  const int last = Lc - 1;
+  const double gc = __shfl(b, last, 64);
+  const double Uc = __shfl(mp, last, 64);
+  const int Rc = __shfl(rs, last, 64);
+  if (valid) {
+    a.gb.b[base + lane] = b;
+    a.gb.u[base + lane] = u;
+    a.gb.mp[base + lane] = mp;
+    a.gb.rs[base + lane] = rs;
+    a.gb.w0[base + lane] = (lane >= Rc && Uc != -INFINITY) ? expf((float)(u - Uc)) : 0.f;
+  }
+  if (lane == 0) {
+    a.gb.g[bh * a.Nc + c] = gc;
+    a.gb.U[bh * a.Nc + c] = Uc;
+    a.gb.R[bh * a.Nc + c] = Rc;
+  }
 }
 
 // ------------------------------------------------------------------ state pass
@@ -684,7 +738,10 @@ hipError_t launch_gate(const FwdLaunch& f, const GateBuffers& gb, hipStream_t s)
   a.T = f.T; a.Nc = f.Nc; a.BH = f.BH; a.L = f.L;
   a.gb = gb;
   mark_before(K_GATE, s);
-  hipLaunchKernelGGL(gate_kernel, dim3((unsigned)(f.BH * f.Nc)), dim3(kThreads), 0, s, a);
+  if (f.L == kTile)
+    hipLaunchKernelGGL(gate64_kernel, dim3((unsigned)((f.BH * f.Nc + 3) / 4)), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(gate_kernel, dim3((unsigned)(f.BH * f.Nc)), dim3(kThreads), 0, s, a);
   mark_after(K_GATE, s);
   return hipGetLastError();
 }

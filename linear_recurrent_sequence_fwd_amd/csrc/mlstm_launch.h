@@ -34,6 +34,21 @@ struct ChunkStates {
   double* ms;
 };
 
+// Chunk states of the fused path (mlstm_fused.hip), S chunks of TPS 64-token
+// tiles: C [BH][S-1][V][K] and n [BH][S-1][K] float32 hold each chunk's local
+// end state and then, folded in order, the start states of chunks 1..S-1;
+// mloc, mstart and G [BH][S-1] float64 are the local end stabiliser, the start
+// stabiliser and the chunk's log-forget total.
+struct SegStates {
+  float* C;
+  float* n;
+  double* mloc;
+  double* mstart;
+  double* G;
+  int S;
+  int TPS;
+};
+
 struct FwdLaunch {
   int64_t BH, T, K, V;
   int L;           // chunk length (multiple of 64)
@@ -80,5 +95,10 @@ hipError_t launch_state_bf16(const FwdLaunch& a, const GateBuffers& gb, const Ch
                              hipStream_t s);
 hipError_t launch_out_bf16(const FwdLaunch& a, const GateBuffers& gb, const ChunkStates& cs,
                            hipStream_t s);
+
+// Fused path (mlstm_fused.hip): bf16 with d_v a multiple of 128. `a` counts
+// 64-token tiles (a.L == 64, a.Nc tiles); the gate buffers are per tile.
+bool fused_path(int bf16, int64_t K, int64_t V);
+hipError_t launch_fused(const FwdLaunch& a, const GateBuffers& gb, const SegStates& ss, hipStream_t s);
 
 }  // namespace mlstm_impl
