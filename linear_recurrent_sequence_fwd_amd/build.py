@@ -20,9 +20,11 @@ ARCH = "gfx950"
 SOURCES = [os.path.join(CSRC, "mlstm_kernels.hip"), os.path.join(CSRC, "mlstm_bf16.hip"),
            os.path.join(CSRC, "mlstm_fused.hip"), os.path.join(CSRC, "mlstm_abi.cpp")]
 
-# Packed-fp32 VALU instructions are turned off for all device code; MFMA
-# accumulators are allocated as VGPRs (the fused kernels apply VALU work to
-# them every tile, which the AGPR form turns into copies).
+# Packed-fp32 VALU instructions are turned off for all device code. MFMA
+# builtins are compiled in the VGPR form: with accumulators in AGPRs this
+# compiler copies loop-carried accumulators between registers around every
+# MFMA. (The fused kernels keep their carried state in AGPRs through explicit
+# in-place MFMAs.)
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

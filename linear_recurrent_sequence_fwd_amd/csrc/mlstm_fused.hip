@@ -31,7 +31,7 @@ namespace {
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int kVB = 128;                     // value columns per workgroup
-constexpr double kMaxDefer = 50.0;           // largest pending log decay kept out of the accumulators
+constexpr double kMaxDefer = 70.0;           // largest pending log decay kept out of the accumulators
 constexpr float kLog2eF = 1.4426950408889634f;
 
 // Transposed operand fragment from a row-major LDS tile X (row pitch P):
@@ -58,10 +58,13 @@ __device__ __forceinline__ bf16x8 frag_split(const __bf16* X, int P, int row, in
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__device__ __forceinline__ bf16x8 pack_bf16(f32x4 a, f32x4 b) {
+__device__ __forceinline__ bf16x8 pack_bf16(const f32x4& a, const f32x4& b) {
   bf16x8 r;
-  r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)a[2]; r[3] = (__bf16)a[3];
-  r[4] = (__bf16)b[0]; r[5] = (__bf16)b[1]; r[6] = (__bf16)b[2]; r[7] = (__bf16)b[3];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (__bf16)a[e];
+    r[4 + e] = (__bf16)b[e];
+  }
   return r;
 }
 
@@ -90,54 +93,73 @@ struct SegArgs {
   int S;                     // chunks
 };
 
+// Waves per workgroup: the output kernel runs eight (16 value columns each,
+// two waves per SIMD), the local end-state kernel four (32 columns each: half
+// the transposed K reads per MFMA, and its state fits in VGPRs).
+template <bool LOCAL> struct SegWaves { static constexpr int value = LOCAL ? 4 : 8; };
+
 template <int K, bool LOCAL>
 struct SegLds {
-  static constexpr int QP = K + 16;       // sQ/sK row pitch: 8 dwords mod 32 banks
-  static constexpr int VP = kVB + 16;     // sV row pitch
+  static constexpr int QP = K + 16;       // sQ row pitch (16-byte operand reads)
+  static constexpr int KP = K + 8;        // sK row pitch (8-byte and transposed reads)
+  static constexpr int VP = kVB + 8;      // sV row pitch (transposed reads)
   static constexpr int OP = kVB + 8;      // sO row pitch
   static constexpr int PP = kTile + 8;    // sP row pitch
   static constexpr int oQ = 0;
   static constexpr int oK = oQ + (LOCAL ? 0 : kTile * QP * 2);
-  static constexpr int oV = oK + kTile * QP * 2;
+  static constexpr int oV = oK + kTile * KP * 2;
   static constexpr int oO = oV + kTile * VP * 2;
   static constexpr int oP = oO + (LOCAL ? 0 : kTile * OP * 2);
-  static constexpr int oN = oP + (LOCAL ? 0 : kTile * PP * 2);
-  static constexpr int oW = oN + (LOCAL ? 0 : K * 4);
-  static constexpr int oRow = oW + kTile * 4;
-  static constexpr int oDen = oRow + (LOCAL ? 0 : 5 * kTile * 4);
-  static constexpr int bytes = oDen + (LOCAL ? 0 : 8 * kTile * 4);
+  static constexpr int oNb = oP + (LOCAL ? 0 : kTile * PP * 2);   // bf16 [3][K]: n~ hi, lo, zero
+  static constexpr int oW = oNb + (LOCAL ? 0 : 3 * K * 2);        // float [64] key weights
+  static constexpr int oWb = oW + kTile * 4;                      // bf16 [3][64]: weights hi, lo, zero
+  static constexpr int oRow = oWb + 3 * kTile * 2;
+  static constexpr int oDen = oRow + (LOCAL ? 0 : 6 * kTile * 4);
+  static constexpr int bytes = oDen + (LOCAL ? 0 : (4 + SegWaves<LOCAL>::value) * kTile * 4);
 };
 
-// Wave w owns value columns [32 w, 32 w + 32) of the workgroup's 128 and
-// keeps C~^T[k][v] for all k of them: register r of Ct[kx][y] in lane (g, i)
-// is k = 16 kx + 4 g + r, v = 32 w + 16 y + i. The normaliser is carried in
-// Nacc: for k = 16 kx + 4 g + r with kx in this wave's quarter, lane i = 0
-// holds the part weighted by the bf16 high halves of the weights and lane
-// i = 1 the part weighted by the low halves; n~ is their sum.
-template <int K, bool LOCAL>
-__global__ __launch_bounds__(kThreads, 1) void seg_kernel(SegArgs a) {
+// Wave w owns value columns [16 WY w, 16 WY (w + 1)) of the workgroup's 128
+// and keeps C~^T[k][v] for all k of them in registers: register r of
+// Ct[kx][y] in lane (g, i) is k = 16 kx + 4 g + r, v = 16 (WY w + y) + i. The
+// normaliser n~ is carried as two MFMA columns (lane i = 0: the sum weighted
+// by the bf16 high halves of the key weights, i = 1: by the low halves) in
+// Nacc, for the 16-row tiles kx = KXW w .. KXW w + KXW - 1. The output
+// kernel (eight waves, WY = 1) takes Q K^T in blocks of 16 keys [16 (w & 3),
+// +16) x 32 rows [32 (w >> 2), +32) and forms H^T (value columns as MFMA
+// rows), so that a lane holds four consecutive columns of one output row.
+//
+// RESCALE = false is the variant for chunks whose pending decay never exceeds
+// kMaxDefer (checked up front from the gate scalars alone); it holds no
+// rescaling code. Other chunks take RESCALE = true.
+template <int K, bool LOCAL, bool RESCALE>
+__device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
   using L = SegLds<K, LOCAL>;
-  constexpr int QP = L::QP, VP = L::VP, OP = L::OP, PP = L::PP;
-  constexpr int KS = K / 32;     // 32-deep steps over d_qk
-  constexpr int KX = K / 16;     // 16-row tiles of C^T along d_qk
-  constexpr int KXW = KX / 4;    // normaliser tiles per wave
-  constexpr int QV = K / 32;     // 16-byte vectors per thread of a 64 x K tile
-  constexpr int VV = 4;          // 16-byte vectors per thread of a 64 x 128 tile
-  __shared__ __attribute__((aligned(16))) char smem[L::bytes];
+  constexpr int QP = L::QP, KP = L::KP, VP = L::VP, OP = L::OP, PP = L::PP;
+  constexpr int KS = K / 32;                                   // 32-deep steps over d_qk
+  constexpr int KX = K / 16;                                   // 16-row tiles of C^T along d_qk
+  constexpr int NW = SegWaves<LOCAL>::value;
+  constexpr int NT = 64 * NW;                                  // threads
+  constexpr int WY = kVB / 16 / NW;                            // 16-column tiles per wave
+  constexpr int KXW = KX >= NW ? KX / NW : 1;                  // normaliser tiles per wave
+  constexpr int QV = kTile * K / 8 / NT;                       // 16-byte vectors per thread, 64 x K tile
+  constexpr int VV = kTile * kVB / 8 / NT;                     // 16-byte vectors per thread, 64 x 128 tile
+  static_assert(LOCAL || WY == 1, "the output kernel assumes one column tile per wave");
   __bf16* sQ = reinterpret_cast<__bf16*>(smem + L::oQ);
   __bf16* sK = reinterpret_cast<__bf16*>(smem + L::oK);
   __bf16* sV = reinterpret_cast<__bf16*>(smem + L::oV);
   __bf16* sO = reinterpret_cast<__bf16*>(smem + L::oO);
   __bf16* sP = reinterpret_cast<__bf16*>(smem + L::oP);
-  float* sn = reinterpret_cast<float*>(smem + L::oN);
+  __bf16* snb = reinterpret_cast<__bf16*>(smem + L::oNb);
   float* s_w = reinterpret_cast<float*>(smem + L::oW);
+  __bf16* swb = reinterpret_cast<__bf16*>(smem + L::oWb);
   float* s_r2 = reinterpret_cast<float*>(smem + L::oRow);
   float* s_sc = s_r2 + kTile;
   float* s_fl = s_sc + kTile;
   float* s_u2 = s_fl + kTile;
   int* s_rs = reinterpret_cast<int*>(s_u2 + kTile);
-  float* s_den = reinterpret_cast<float*>(smem + L::oDen);   // [4][64] row sums of P per wave
-  float* s_dn = s_den + 4 * kTile;                           // [4][64] q . n~ partials per wave
+  float* s_inv = s_u2 + kTile + kTile;                       // [64] 1 / denominator of each row
+  float* s_den = reinterpret_cast<float*>(smem + L::oDen);   // [4][64] row sums of P per key group
+  float* s_dn = s_den + 4 * kTile;                           // [NW][64] q . n~ partials per wave
 
   const int64_t BH = a.BH, T = a.T, V = a.V, Nt = a.Nt;
   const int nvb = (int)(V / kVB);
@@ -152,11 +174,12 @@ __global__ __launch_bounds__(kThreads, 1) void seg_kernel(SegArgs a) {
   // may run must sit behind a real branch.
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 15, g = lane >> 4;
+  const int kg = w & 3, zh = w >> 2;
   const int64_t vcol0 = (int64_t)vb * kVB;
   const int64_t nseg1 = a.S - 1;
 
   // ---------------- carried state
-  f32x4 Ct[KX][2];
+  f32x4 Ct[KX][WY];
   f32x4 Nacc[KXW];
   double m_prev;
   bool has_state;
@@ -180,20 +203,24 @@ __global__ __launch_bounds__(kThreads, 1) void seg_kernel(SegArgs a) {
 #pragma unroll
   for (int kx = 0; kx < KX; ++kx)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
-      Ct[kx][y] = Cinit ? *reinterpret_cast<const f32x4*>(Cinit + (vcol0 + 32 * w + 16 * y + i) * K + 16 * kx + 4 * g)
+    for (int y = 0; y < WY; ++y)
+      Ct[kx][y] = Cinit ? *reinterpret_cast<const f32x4*>(Cinit + (vcol0 + 16 * (WY * w + y) + i) * K + 16 * kx + 4 * g)
                         : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int x = 0; x < KXW; ++x) {
     const int kx = w * KXW + x;
-    Nacc[x] = (ninit && i == 0) ? *reinterpret_cast<const f32x4*>(ninit + 16 * kx + 4 * g)
-                                : f32x4{0.f, 0.f, 0.f, 0.f};
+    Nacc[x] = (ninit && i == 0 && kx < KX) ? *reinterpret_cast<const f32x4*>(ninit + 16 * kx + 4 * g)
+                                           : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // The tiles' decays are not applied to the accumulators one by one (a VALU
-  // pass over 128 accumulator registers per tile): the registers hold X with
-  // C~ = exp(logD) X, n~ = exp(logD) Xn, new keys enter with weight
-  // exp(u_j - Rm - logD), and X is rescaled only when logD would fall below
-  // -kMaxDefer (or on a zero decay).
+  // zero rows of the two-column normaliser operands
+  if (tid < kTile) swb[2 * kTile + tid] = (__bf16)0.f;
+  if constexpr (!LOCAL) {
+    for (int k = tid; k < K; k += NT) snb[2 * K + k] = (__bf16)0.f;
+  }
+  // The tiles' decays are not applied to the accumulators one by one: the
+  // registers hold X with C~ = exp(logD) X, n~ = exp(logD) Xn, new keys enter
+  // with weight exp(u_j - Rm - logD), and X is rescaled only when logD would
+  // fall below -kMaxDefer (or on a zero decay).
   double logD = 0.0;
   double Gsum = 0.0;
   bool reset_seen = false;
@@ -211,14 +238,14 @@ __global__ __launch_bounds__(kThreads, 1) void seg_kernel(SegArgs a) {
     const int64_t tok0 = bh * T + t0;
 #pragma unroll
     for (int e = 0; e < QV; ++e) {
-      const int it = tid + kThreads * e;
+      const int it = tid + NT * e;
       const int row = min(it / (K / 8), last), cv = it % (K / 8);
       if constexpr (!LOCAL) pq[e] = *reinterpret_cast<const bf16x8*>(a.q + (tok0 + row) * K + 8 * cv);
       pk[e] = *reinterpret_cast<const bf16x8*>(a.k + (tok0 + row) * K + 8 * cv);
     }
 #pragma unroll
     for (int e = 0; e < VV; ++e) {
-      const int it = tid + kThreads * e;
+      const int it = tid + NT * e;
       const int row = min(it / (kVB / 8), last), cv = it % (kVB / 8);
       pv[e] = *reinterpret_cast<const bf16x8*>(a.v + (tok0 + row) * V + vcol0 + 8 * cv);
       if constexpr (!LOCAL) po[e] = *reinterpret_cast<const bf16x8*>(a.o + (tok0 + row) * V + vcol0 + 8 * cv);
@@ -247,14 +274,21 @@ __global__ __launch_bounds__(kThreads, 1) void seg_kernel(SegArgs a) {
     // ---------------- stage tile tau
 #pragma unroll
     for (int e = 0; e < QV; ++e) {
-      const int it = tid + kThreads * e;
+      const int it = tid + NT * e;
       const int row = it / (K / 8), cv = it % (K / 8);
-      if constexpr (!LOCAL) *reinterpret_cast<bf16x8*>(&sQ[row * QP + 8 * cv]) = pq[e];
-      *reinterpret_cast<bf16x8*>(&sK[row * QP + 8 * cv]) = pk[e];
+      if constexpr (!LOCAL) {
+        // within each 32-column block the columns are stored in the order in
+        // which the operand fragments take them (4 g .. 4 g + 3, then 16 + 4 g ..)
+        const int blk = cv >> 2, j = cv & 3;
+        const int p0 = 32 * blk + 8 * (2 * (j & 1)) + 4 * (j >> 1);
+        *reinterpret_cast<bf16x4*>(&sQ[row * QP + p0]) = __builtin_shufflevector(pq[e], pq[e], 0, 1, 2, 3);
+        *reinterpret_cast<bf16x4*>(&sQ[row * QP + p0 + 8]) = __builtin_shufflevector(pq[e], pq[e], 4, 5, 6, 7);
+      }
+      *reinterpret_cast<bf16x8*>(&sK[row * KP + 8 * cv]) = pk[e];
     }
 #pragma unroll
     for (int e = 0; e < VV; ++e) {
-      const int it = tid + kThreads * e;
+      const int it = tid + NT * e;
       const int row = it / (kVB / 8), cv = it % (kVB / 8);
       *reinterpret_cast<bf16x8*>(&sV[row * VP + 8 * cv]) = pv[e];
       if constexpr (!LOCAL) *reinterpret_cast<bf16x8*>(&sO[row * OP + 8 * cv]) = po[e];
@@ -268,12 +302,17 @@ __global__ __launch_bounds__(kThreads, 1) void seg_kernel(SegArgs a) {
     const bool live = Rm != -INFINITY;
     const double ld = (t_R >= 0 || m_prev == -INFINITY || !live) ? -INFINITY : m_prev - Rm;
     const double m_next = live ? t_g + Rm : -INFINITY;
-    // deferred decay after this tile: keep logD + ld, or rescale X by it
-    const bool rescale = logD + ld < -kMaxDefer;
+    // deferred decay after this tile: keep logD + ld, or rescale X by it (a
+    // scalar, so that the rescale below is a branch)
+    const bool rescale = __builtin_amdgcn_readfirstlane(logD + ld < -kMaxDefer ? 1 : 0) != 0;
     const double logD_next = rescale ? 0.0 : logD + ld;
     if (tid < kTile) {
       const int j = tid;
-      s_w[j] = (j >= t_R && j < Lc && t_U != -INFINITY && live) ? expf((float)(r_u - Rm - logD_next)) : 0.f;
+      const float wj = (j >= t_R && j < Lc && t_U != -INFINITY && live) ? expf((float)(r_u - Rm - logD_next)) : 0.f;
+      s_w[j] = wj;
+      const __bf16 whi = (__bf16)wj;
+      swb[j] = whi;
+      swb[kTile + j] = (__bf16)(wj - (float)whi);
       if constexpr (!LOCAL) {
         // row stabiliser r_t = max(m_prev if no zero gate at or before t, prefix max of u)
         const bool carry0 = has_state && r_rs0 < 0;
@@ -291,13 +330,25 @@ __global__ __launch_bounds__(kThreads, 1) void seg_kernel(SegArgs a) {
       }
     }
     if constexpr (!LOCAL) {
-      // n~ for the q . n~ term of this tile
+      // n~ of this tile as bf16 hi + lo in the fragment order of sQ
 #pragma unroll
       for (int x = 0; x < KXW; ++x) {
-        f32x4 nv;
+        const int kx = w * KXW + x;
+        if (kx < KX) {
+          bf16x4 hi4, lo4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) nv[r] = Nacc[x][r] + __shfl_xor(Nacc[x][r], 1, 64);
-        if (i == 0) *reinterpret_cast<f32x4*>(&sn[16 * (w * KXW + x) + 4 * g]) = nv;
+          for (int r = 0; r < 4; ++r) {
+            const float nr = Nacc[x][r] + __shfl_xor(Nacc[x][r], 1, 64);
+            const __bf16 hi = (__bf16)nr;
+            hi4[r] = hi;
+            lo4[r] = (__bf16)(nr - (float)hi);
+          }
+          const int pos = 32 * (kx >> 1) + 8 * g + 4 * (kx & 1);
+          if (i == 0) {
+            *reinterpret_cast<bf16x4*>(&snb[pos]) = hi4;
+            *reinterpret_cast<bf16x4*>(&snb[K + pos]) = lo4;
+          }
+        }
       }
     }
     if constexpr (LOCAL) {
@@ -308,126 +359,117 @@ __global__ __launch_bounds__(kThreads, 1) void seg_kernel(SegArgs a) {
     if (tau + 1 < tile1) issue(tau + 1);
 
     if constexpr (!LOCAL) {
-      // ---------------- Q K^T (this wave's 16 keys x 64 rows), Q C~^T, q . n~
-      f32x4 sacc[4], acc[4][2], dacc[4];
+      // ---------------- Q K^T (16 keys x 32 rows) and (Q C~^T)^T (16 columns x 64 rows)
+      f32x4 sacc[2], acc[4];
+      sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        sacc[z] = dacc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc[z][0] = acc[z][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int z = 0; z < 4; ++z) acc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
       unroll<KS>([&](auto s_c) {
         constexpr int s = decltype(s_c)::value;
-        bf16x8 A[4];
+        bf16x8 fa[4];
 #pragma unroll
-        for (int z = 0; z < 4; ++z) A[z] = frag_split(sQ, QP, 16 * z + i, 32 * s);
-        const bf16x8 Kf = frag_split(sK, QP, 16 * w + i, 32 * s);
-#pragma unroll
-        for (int z = 0; z < 4; ++z) sacc[z] = mma(Kf, A[z], sacc[z]);
-        bf16x8 Bc[2];
-#pragma unroll
-        for (int y = 0; y < 2; ++y) Bc[y] = pack_bf16(Ct[2 * s][y], Ct[2 * s + 1][y]);
-#pragma unroll
-        for (int z = 0; z < 4; ++z)
-#pragma unroll
-          for (int y = 0; y < 2; ++y) acc[z][y] = mma(A[z], Bc[y], acc[z][y]);
-        if (w == (s & 3)) {
-          const f32x4 n0v = *reinterpret_cast<const f32x4*>(&sn[32 * s + 4 * g]);
-          const f32x4 n1v = *reinterpret_cast<const f32x4*>(&sn[32 * s + 16 + 4 * g]);
-          bf16x8 Bn;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float nval = e < 4 ? n0v[e] : n1v[e - 4];
-            const __bf16 hi = (__bf16)nval;
-            const __bf16 lo = (__bf16)(nval - (float)hi);
-            Bn[e] = i == 0 ? hi : (i == 1 ? lo : (__bf16)0.f);
-          }
-#pragma unroll
-          for (int z = 0; z < 4; ++z) dacc[z] = mma(A[z], Bn, dacc[z]);
+        for (int z = 0; z < 4; ++z) fa[z] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * z + i) * QP + 32 * s + 8 * g]);
+        const bf16x8 fk = frag_split(sK, KP, 16 * kg + i, 32 * s);
+        if (zh == 0) {   // scalar branch: a register array takes static indices only
+          sacc[0] = mma(fk, fa[0], sacc[0]);
+          sacc[1] = mma(fk, fa[1], sacc[1]);
+        } else {
+          sacc[0] = mma(fk, fa[2], sacc[0]);
+          sacc[1] = mma(fk, fa[3], sacc[1]);
         }
+        const bf16x8 Bc = pack_bf16(Ct[2 * s][0], Ct[2 * s + 1][0]);
+#pragma unroll
+        for (int z = 0; z < 4; ++z) acc[z] = mma(Bc, fa[z], acc[z]);
+        __builtin_amdgcn_sched_barrier(0);
       });
-      // q . n~ partial of this wave (normaliser columns hi + lo)
+      // ---------------- q . n~: wave w takes the 32-deep step s = w of d_qk
+      {
+        f32x4 dacc[4];
 #pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        f32x4 d;
+        for (int z = 0; z < 4; ++z) dacc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (w < KS) {
+          const bf16x8 Bn = *reinterpret_cast<const bf16x8*>(&snb[min(i, 2) * K + 32 * w + 8 * g]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) d[r] = dacc[z][r] + __shfl_xor(dacc[z][r], 1, 64);
-        if (i == 0) *reinterpret_cast<f32x4*>(&s_dn[w * kTile + 16 * z + 4 * g]) = d;
-      }
-      // the carried-state term enters row t with weight exp(m_prev - r_t)
+          for (int z = 0; z < 4; ++z) {
+            const bf16x8 fa = *reinterpret_cast<const bf16x8*>(&sQ[(16 * z + i) * QP + 32 * w + 8 * g]);
+            dacc[z] = mma(fa, Bn, dacc[z]);
+          }
+        }
 #pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        const f32x4 sc = *reinterpret_cast<const f32x4*>(&s_sc[16 * z + 4 * g]);
+        for (int z = 0; z < 4; ++z) {
+          f32x4 d;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[z][0][r] *= sc[r];
-          acc[z][1][r] *= sc[r];
+          for (int r = 0; r < 4; ++r) d[r] = dacc[z][r] + __shfl_xor(dacc[z][r], 1, 64);
+          if (i == 0) *reinterpret_cast<f32x4*>(&s_dn[w * kTile + 16 * z + 4 * g]) = d;
         }
       }
-      // ---------------- P = S o D: lane holds S^T[j = 16 w + 4 g + r][t = 16 z + i]
-      const f32x4 u2 = *reinterpret_cast<const f32x4*>(&s_u2[16 * w + 4 * g]);
+      // the carried-state term enters row t with weight exp(m_prev - r_t + logD);
+      // acc[z] register r in lane (g, i) is H^T[v = 16 w + 4 g + r][t = 16 z + i]
 #pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        const int tl = 16 * z + i;
+      for (int z = 0; z < 4; ++z) acc[z] *= s_sc[16 * z + i];
+      // ---------------- P = S o D: lane holds S^T[j = 16 kg + 4 g + r][t = 16 z + i]
+      const f32x4 u2 = *reinterpret_cast<const f32x4*>(&s_u2[16 * kg + 4 * g]);
+#pragma unroll
+      for (int zz = 0; zz < 2; ++zz) {
+        const int tl = 16 * (2 * zh + zz) + i;
         const float r2 = s_r2[tl];
         const int rs = s_rs[tl];
         bf16x4 pk4;
         float psum = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int jk = 16 * w + 4 * g + r;
+          const int jk = 16 * kg + 4 * g + r;
           const bool keep = (tl < Lc) && (jk <= tl) && (jk >= rs);
-          const float p = keep ? sacc[z][r] * __builtin_amdgcn_exp2f(u2[r] - r2) : 0.f;
+          const float p = keep ? sacc[zz][r] * __builtin_amdgcn_exp2f(u2[r] - r2) : 0.f;
           psum += p;
           pk4[r] = (__bf16)p;
         }
-        *reinterpret_cast<bf16x4*>(&sP[tl * PP + 16 * w + 4 * g]) = pk4;
+        *reinterpret_cast<bf16x4*>(&sP[tl * PP + 16 * kg + 4 * g]) = pk4;
         psum += __shfl_xor(psum, 16, 64);
         psum += __shfl_xor(psum, 32, 64);
-        if (g == 0) s_den[w * kTile + tl] = psum;
+        if (g == 0) s_den[kg * kTile + tl] = psum;
       }
       __syncthreads();   // sP, s_den, s_dn complete
-      // ---------------- P V
+      if (w == 0) {   // 1 / max(|n~^T q|, floor) of row t = lane
+        const int t = lane;
+        float den = s_den[t] + s_den[kTile + t] + s_den[2 * kTile + t] + s_den[3 * kTile + t];
+        float dn = 0.f;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) dn += s_dn[q * kTile + t];
+        const float d = den + s_sc[t] * dn;
+        s_inv[t] = __builtin_amdgcn_rcpf(fmaxf(fmaxf(fabsf(d), s_fl[t]), FLT_MIN));
+      }
+      // ---------------- (P V)^T
 #pragma unroll
       for (int jj = 0; jj < kTile; jj += 32) {
-        bf16x8 A[4], B[2];
+        bf16x8 B[4];
 #pragma unroll
-        for (int z = 0; z < 4; ++z) A[z] = *reinterpret_cast<const bf16x8*>(&sP[(16 * z + i) * PP + jj + 8 * g]);
+        for (int z = 0; z < 4; ++z) B[z] = *reinterpret_cast<const bf16x8*>(&sP[(16 * z + i) * PP + jj + 8 * g]);
+        const bf16x8 A = frag_tr(sV, VP, jj, 16 * w);
 #pragma unroll
-        for (int y = 0; y < 2; ++y) B[y] = frag_tr(sV, VP, jj, 32 * w + 16 * y);
-#pragma unroll
-        for (int z = 0; z < 4; ++z)
-#pragma unroll
-          for (int y = 0; y < 2; ++y) acc[z][y] = mma(A[z], B[y], acc[z][y]);
+        for (int z = 0; z < 4; ++z) acc[z] = mma(A, B[z], acc[z]);
       }
-      // ---------------- normaliser, output gate; h staged in place of O
+      __syncthreads();   // s_inv complete
+      // ---------------- normaliser, output gate; h staged in place of O, four
+      // consecutive columns of one row per lane
 #pragma unroll
       for (int z = 0; z < 4; ++z) {
-        const int t4 = 16 * z + 4 * g;
-        f32x4 den = *reinterpret_cast<const f32x4*>(&s_den[t4]);
-        f32x4 dn = *reinterpret_cast<const f32x4*>(&s_dn[t4]);
-#pragma unroll
-        for (int ww = 1; ww < 4; ++ww) {
-          den += *reinterpret_cast<const f32x4*>(&s_den[ww * kTile + t4]);
-          dn += *reinterpret_cast<const f32x4*>(&s_dn[ww * kTile + t4]);
-        }
-        const f32x4 sc = *reinterpret_cast<const f32x4*>(&s_sc[t4]);
-        const f32x4 fl = *reinterpret_cast<const f32x4*>(&s_fl[t4]);
+        const int t = 16 * z + i;
+        const float inv = s_inv[t];
+        __bf16* p = &sO[t * OP + 16 * w + 4 * g];
+        const bf16x4 o4 = *reinterpret_cast<const bf16x4*>(p);
+        bf16x4 h4;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float d = den[r] + sc[r] * dn[r];
-          const float inv = __builtin_amdgcn_rcpf(fmaxf(fmaxf(fabsf(d), fl[r]), FLT_MIN));
-#pragma unroll
-          for (int y = 0; y < 2; ++y) {
-            __bf16* p = &sO[(t4 + r) * OP + 32 * w + 16 * y + i];
-            const float og = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2eF * (float)*p));
-            *p = (__bf16)(og * acc[z][y][r] * inv);
-          }
+          const float og = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2eF * (float)o4[r]));
+          h4[r] = (__bf16)(og * acc[z][r] * inv);
         }
+        *reinterpret_cast<bf16x4*>(p) = h4;
       }
       __syncthreads();   // h tile complete
 #pragma unroll
       for (int e = 0; e < VV; ++e) {
-        const int it = tid + kThreads * e;
+        const int it = tid + NT * e;
         const int row = it / (kVB / 8), cv = it % (kVB / 8);
         if (row < Lc)
           *reinterpret_cast<bf16x8*>(a.h + (tok0 + row) * V + vcol0 + 8 * cv) =
@@ -436,41 +478,45 @@ __global__ __launch_bounds__(kThreads, 1) void seg_kernel(SegArgs a) {
     }
 
     // ---------------- state update: C~ <- decay C~ + K^T diag(w) V, n~ likewise
-    if (rescale) {   // uniform over the workgroup
-      const float f = (float)exp(logD + ld);
+    if constexpr (RESCALE) {
+      if (rescale) {   // uniform over the workgroup
+        const float f = (float)exp(logD + ld);
 #pragma unroll
-      for (int kx = 0; kx < KX; ++kx) {
-        Ct[kx][0] *= f;
-        Ct[kx][1] *= f;
+        for (int kx = 0; kx < KX; ++kx)
+#pragma unroll
+          for (int y = 0; y < WY; ++y) Ct[kx][y] *= f;
+#pragma unroll
+        for (int x = 0; x < KXW; ++x) Nacc[x] *= f;
       }
-#pragma unroll
-      for (int x = 0; x < KXW; ++x) Nacc[x] *= f;
     }
 #pragma unroll
     for (int ts = 0; ts < kTile; ts += 32) {
       const f32x4 wa = *reinterpret_cast<const f32x4*>(&s_w[ts + 8 * g]);
       const f32x4 wb = *reinterpret_cast<const f32x4*>(&s_w[ts + 8 * g + 4]);
-      bf16x8 Bv[2], Bw;
+      bf16x8 Bv[WY];
 #pragma unroll
-      for (int y = 0; y < 2; ++y) {
-        const bf16x8 raw = frag_tr(sV, VP, ts, 32 * w + 16 * y);
+      for (int y = 0; y < WY; ++y) {
+        const bf16x8 raw = frag_tr(sV, VP, ts, 16 * (WY * w + y));
 #pragma unroll
         for (int e = 0; e < 8; ++e) Bv[y][e] = (__bf16)((float)raw[e] * (e < 4 ? wa[e] : wb[e - 4]));
       }
+      const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&swb[min(i, 2) * kTile + ts + 8 * g]);
+      // transposed K fragments through a ring of kRing registers: the read of
+      // tile kx + kRing - 1 is issued before the MFMAs of tile kx
+      constexpr int kRing = 4;
+      bf16x8 Ak[kRing];
+      unroll<kRing - 1>([&](auto p_c) {
+        constexpr int p = decltype(p_c)::value;
+        if constexpr (p < KX) Ak[p] = frag_tr(sK, KP, ts, 16 * p);
+      });
+      unroll<KX>([&](auto kx_c) {
+        constexpr int kx = decltype(kx_c)::value;
+        if constexpr (kx + kRing - 1 < KX) Ak[(kx + kRing - 1) % kRing] = frag_tr(sK, KP, ts, 16 * (kx + kRing - 1));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float wt = e < 4 ? wa[e] : wb[e - 4];
-        const __bf16 hi = (__bf16)wt;
-        const __bf16 lo = (__bf16)(wt - (float)hi);
-        Bw[e] = i == 0 ? hi : (i == 1 ? lo : (__bf16)0.f);
-      }
-#pragma unroll
-      for (int kx = 0; kx < KX; ++kx) {
-        const bf16x8 Ak = frag_tr(sK, QP, ts, 16 * kx);
-        Ct[kx][0] = mma(Ak, Bv[0], Ct[kx][0]);
-        Ct[kx][1] = mma(Ak, Bv[1], Ct[kx][1]);
-        if (kx / KXW == w) Nacc[kx % KXW] = mma(Ak, Bw, Nacc[kx % KXW]);
-      }
+        for (int y = 0; y < WY; ++y) Ct[kx][y] = mma(Ak[kx % kRing], Bv[y], Ct[kx][y]);
+        if (kx / KXW == w) Nacc[kx % KXW] = mma(Ak[kx % kRing], Bw, Nacc[kx % KXW]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
     m_prev = m_next;
     logD = logD_next;
@@ -498,18 +544,77 @@ __global__ __launch_bounds__(kThreads, 1) void seg_kernel(SegArgs a) {
 #pragma unroll
     for (int kx = 0; kx < KX; ++kx)
 #pragma unroll
-      for (int y = 0; y < 2; ++y)
-        *reinterpret_cast<f32x4*>(Cdst + (vcol0 + 32 * w + 16 * y + i) * K + 16 * kx + 4 * g) = fD * Ct[kx][y];
+      for (int y = 0; y < WY; ++y)
+        *reinterpret_cast<f32x4*>(Cdst + (vcol0 + 16 * (WY * w + y) + i) * K + 16 * kx + 4 * g) = fD * Ct[kx][y];
   }
   if (ndst) {
 #pragma unroll
     for (int x = 0; x < KXW; ++x) {
+      const int kx = w * KXW + x;
       f32x4 nv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) nv[r] = fD * (Nacc[x][r] + __shfl_xor(Nacc[x][r], 1, 64));
-      if (i == 0) *reinterpret_cast<f32x4*>(ndst + 16 * (w * KXW + x) + 4 * g) = nv;
+      if (i == 0 && kx < KX) *reinterpret_cast<f32x4*>(ndst + 16 * kx + 4 * g) = nv;
     }
   }
+}
+
+// True when some tile of the chunk would need the accumulators rescaled:
+// the pending decay logD + ld falls below -kMaxDefer while the state is not
+// known to be zero. Follows the same float64 steps as the tile loop, from the
+// tile scalars only (lanes load 64 tiles at a time, the scan runs on
+// shuffles); the result is uniform over the workgroup.
+__device__ bool chunk_needs_rescale(const SegArgs& a, int64_t bh, int64_t tile0, int64_t tile1, double m,
+                                    bool zero, bool local) {
+  const int lane = threadIdx.x & 63;
+  double logD = 0.0;
+  for (int64_t base = tile0; base < tile1; base += 64) {
+    const int n = (int)min((int64_t)64, tile1 - base);
+    const int64_t t = bh * a.Nt + base + min(lane, n - 1);
+    const double gv = a.gb.g[t], Uv = a.gb.U[t];
+    const int Rv = a.gb.R[t];
+    for (int j = 0; j < n; ++j) {
+      const double gj = __shfl(gv, j, 64), Uj = __shfl(Uv, j, 64);
+      const int Rj = __shfl(Rv, j, 64);
+      double Rm = fmax(Rj >= 0 ? -INFINITY : m, Uj);
+      if (!local && Rm == -INFINITY) Rm = 0.0;
+      const bool live = Rm != -INFINITY;
+      const double ld = (Rj >= 0 || m == -INFINITY || !live) ? -INFINITY : m - Rm;
+      if (logD + ld < -kMaxDefer) {
+        if (!zero) return true;
+        logD = 0.0;
+      } else {
+        logD += ld;
+      }
+      m = live ? gj + Rm : -INFINITY;
+      if (live && Uj != -INFINITY) zero = false;
+    }
+  }
+  return false;
+}
+
+template <int K, bool LOCAL>
+__global__ __launch_bounds__(64 * SegWaves<LOCAL>::value, 1) void seg_kernel(SegArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[SegLds<K, LOCAL>::bytes];
+  const int64_t bh = blockIdx.x % a.BH;
+  const int seg = (int)(blockIdx.x / a.BH / (a.V / kVB));
+  const int64_t tile0 = (int64_t)seg * a.TPS;
+  const int64_t tile1 = min(tile0 + a.TPS, a.Nt);
+  double m = -INFINITY;
+  bool zero = true;
+  if (!LOCAL) {
+    if (seg == 0) {
+      m = a.C0 ? (double)a.m0[bh] : 0.0;
+      zero = a.C0 == nullptr;
+    } else {
+      m = a.mstart[bh * (a.S - 1) + seg - 1];
+      zero = false;
+    }
+  }
+  if (chunk_needs_rescale(a, bh, tile0, tile1, m, zero, LOCAL))
+    seg_body<K, LOCAL, true>(a, smem);
+  else
+    seg_body<K, LOCAL, false>(a, smem);
 }
 
 // ------------------------------------------------------------------ chunk combine
@@ -593,7 +698,7 @@ hipError_t run_seg(const FwdLaunch& f, const GateBuffers& gb, const SegStates& s
   const int64_t nvb = f.V / kVB;
   if (ss.S > 1) {
     mark_before(K_STATE, s);
-    hipLaunchKernelGGL((seg_kernel<K, true>), dim3((unsigned)(f.BH * nvb * (ss.S - 1))), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((seg_kernel<K, true>), dim3((unsigned)(f.BH * nvb * (ss.S - 1))), dim3(64 * SegWaves<true>::value), 0, s, a);
     CombineArgs c;
     c.C0 = f.C0; c.n0 = f.n0; c.m0 = f.m0;
     c.Cseg = ss.C; c.nseg = ss.n; c.mloc = ss.mloc; c.mstart = ss.mstart; c.Gseg = ss.G;
@@ -606,7 +711,7 @@ hipError_t run_seg(const FwdLaunch& f, const GateBuffers& gb, const SegStates& s
     if (e != hipSuccess) return e;
   }
   mark_before(K_OUT, s);
-  hipLaunchKernelGGL((seg_kernel<K, false>), dim3((unsigned)(f.BH * nvb * ss.S)), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((seg_kernel<K, false>), dim3((unsigned)(f.BH * nvb * ss.S)), dim3(64 * SegWaves<false>::value), 0, s, a);
   mark_after(K_OUT, s);
   return hipGetLastError();
 }
