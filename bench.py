@@ -72,9 +72,10 @@ class HipEvents:
 # ---------------------------------------------------------------- algorithmic work
 
 def fwd_bytes(B, H, T, K, V, chunk):
-    """Algorithmic HBM bytes of the whole forward: q, k, v, o read once, h
-    written once (bf16), float32 gates read once, the final float32 state."""
-    return B * H * (T * (2 * K + 2 * K + 2 * V + 2 * V + 2 * V + 4 + 4) + 4 * (V * K + K + 1))
+    """Algorithmic HBM bytes of the whole forward as timed (no final state
+    requested): q, k, v, o read once and h written once (bf16), float32 gates
+    read once."""
+    return B * H * T * (2 * K + 2 * K + 2 * V + 2 * V + 2 * V + 4 + 4)
 
 
 def fwd_flops(B, H, T, K, V):
@@ -97,9 +98,9 @@ def kernel_bytes(name, B, H, T, K, V, chunk):
     if name == "state":                            # chunks' end states: K, V of chunks 0..S-2; fold
         t_loc = min(T, (S - 1) * chunk)
         return BH * t_loc * (2 * K + 2 * V + 8) + BH * (S - 1) * (3 * state + 8)
-    if name == "out":                              # fused tiles: q, k, v, o in, h out, start/final states
+    if name == "out":                              # fused tiles: q, k, v, o in, h out, chunk start states
         return BH * T * (2 * K + 2 * K + 2 * V + 2 * V + 2 * V + gate_tok) + BH * Nt * 20 \
-            + BH * (S - 1) * state + BH * state
+            + BH * (S - 1) * state
     raise KeyError(name)
 
 
