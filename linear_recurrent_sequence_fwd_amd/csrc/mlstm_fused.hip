@@ -38,8 +38,8 @@ constexpr float kLog2eF = 1.4426950408889634f;
 // lane l (i = l%16, g = l/16) receives X[kin0 + 8g + e][n0 + i], e = 0..7.
 // ds_read_b64_tr_b16 hands lane i of each 16-lane group element (i mod 4) of
 // the 8-byte rows addressed by lanes 4e + i/4 of that group.
-__device__ __forceinline__ bf16x8 frag_tr(const __bf16* X, int P, int kin0, int n0) {
-  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+__device__ __forceinline__ bf16x8 frag_tr(const __bf16* X, int P, int kin0, int n0, int lane) {
+  const int i = lane & 15, g = lane >> 4;
   const __bf16* p = X + (kin0 + 8 * g + (i >> 2)) * P + n0 + 4 * (i & 3);
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
   const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * P));
@@ -50,12 +50,31 @@ __device__ __forceinline__ bf16x8 frag_tr(const __bf16* X, int P, int kin0, int 
 // layout of C^T: lane (g, i) receives X[row][k0 + 4g + e] for e = 0..3 and
 // X[row][k0 + 16 + 4g + e - 4] for e = 4..7. A contraction is a sum, so any
 // permutation of its index works as long as both operands use it.
-__device__ __forceinline__ bf16x8 frag_split(const __bf16* X, int P, int row, int k0) {
-  const int g = (threadIdx.x & 63) >> 4;
+__device__ __forceinline__ bf16x8 frag_split(const __bf16* X, int P, int row, int k0, int lane) {
+  const int g = lane >> 4;
   const __bf16* p = X + row * P + k0 + 4 * g;
   const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
   const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// threadIdx.x through an opaque register move. Lane-dependent LDS and global
+// addresses derived from it are recomputed in the phase that uses them
+// instead of being hoisted out of the tile loop, where the compiler keeps
+// dozens of them live across the whole tile (and spills them: a spill reload
+// waits for every load in flight, including the next tile's prefetch).
+__device__ __forceinline__ int fresh_tid() {
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+  return t;
+}
+
+struct Lanes {
+  int tid, lane, i, g;   // thread, lane, lane % 16, lane / 16
+};
+__device__ __forceinline__ Lanes fresh_lanes() {
+  const int t = fresh_tid();
+  return Lanes{t, t & 63, t & 15, (t & 63) >> 4};
 }
 
 __device__ __forceinline__ bf16x8 pack_bf16(const f32x4& a, const f32x4& b) {
@@ -233,6 +252,8 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
   double t_g = 0.0, t_U = 0.0;
   int t_R = -1;
   auto issue = [&](int64_t tau) {
+    const Lanes ln = fresh_lanes();
+    const int tid = ln.tid, lane = ln.lane;
     const int64_t t0 = tau * kTile;
     const int last = (int)min((int64_t)kTile, T - t0) - 1;
     const int64_t tok0 = bh * T + t0;
@@ -272,9 +293,10 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
 
     __syncthreads();   // the previous tile's LDS reads are done
     // ---------------- stage tile tau
+    const Lanes ls = fresh_lanes();
 #pragma unroll
     for (int e = 0; e < QV; ++e) {
-      const int it = tid + NT * e;
+      const int it = ls.tid + NT * e;
       const int row = it / (K / 8), cv = it % (K / 8);
       if constexpr (!LOCAL) {
         // within each 32-column block the columns are stored in the order in
@@ -288,7 +310,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
     }
 #pragma unroll
     for (int e = 0; e < VV; ++e) {
-      const int it = tid + NT * e;
+      const int it = ls.tid + NT * e;
       const int row = it / (kVB / 8), cv = it % (kVB / 8);
       *reinterpret_cast<bf16x8*>(&sV[row * VP + 8 * cv]) = pv[e];
       if constexpr (!LOCAL) *reinterpret_cast<bf16x8*>(&sO[row * OP + 8 * cv]) = po[e];
@@ -306,8 +328,8 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
     // scalar, so that the rescale below is a branch)
     const bool rescale = __builtin_amdgcn_readfirstlane(logD + ld < -kMaxDefer ? 1 : 0) != 0;
     const double logD_next = rescale ? 0.0 : logD + ld;
-    if (tid < kTile) {
-      const int j = tid;
+    if (ls.tid < kTile) {
+      const int j = ls.tid;
       const float wj = (j >= t_R && j < Lc && t_U != -INFINITY && live) ? expf((float)(r_u - Rm - logD_next)) : 0.f;
       s_w[j] = wj;
       const __bf16 whi = (__bf16)wj;
@@ -343,8 +365,8 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
             hi4[r] = hi;
             lo4[r] = (__bf16)(nr - (float)hi);
           }
-          const int pos = 32 * (kx >> 1) + 8 * g + 4 * (kx & 1);
-          if (i == 0) {
+          const int pos = 32 * (kx >> 1) + 8 * ls.g + 4 * (kx & 1);
+          if (ls.i == 0) {
             *reinterpret_cast<bf16x4*>(&snb[pos]) = hi4;
             *reinterpret_cast<bf16x4*>(&snb[K + pos]) = lo4;
           }
@@ -364,12 +386,13 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
       sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int z = 0; z < 4; ++z) acc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const Lanes l1 = fresh_lanes();
       unroll<KS>([&](auto s_c) {
         constexpr int s = decltype(s_c)::value;
         bf16x8 fa[4];
 #pragma unroll
-        for (int z = 0; z < 4; ++z) fa[z] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * z + i) * QP + 32 * s + 8 * g]);
-        const bf16x8 fk = frag_split(sK, KP, 16 * kg + i, 32 * s);
+        for (int z = 0; z < 4; ++z) fa[z] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * z + l1.i) * QP + 32 * s + 8 * l1.g]);
+        const bf16x8 fk = frag_split(sK, KP, 16 * kg + l1.i, 32 * s, l1.lane);
         if (zh == 0) {   // scalar branch: a register array takes static indices only
           sacc[0] = mma(fk, fa[0], sacc[0]);
           sacc[1] = mma(fk, fa[1], sacc[1]);
@@ -384,6 +407,8 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
       });
       // ---------------- q . n~: wave w takes the 32-deep step s = w of d_qk
       {
+        const Lanes ln = fresh_lanes();
+        const int i = ln.i, g = ln.g;
         f32x4 dacc[4];
 #pragma unroll
         for (int z = 0; z < 4; ++z) dacc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -405,9 +430,11 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
       }
       // the carried-state term enters row t with weight exp(m_prev - r_t + logD);
       // acc[z] register r in lane (g, i) is H^T[v = 16 w + 4 g + r][t = 16 z + i]
+      const Lanes lp = fresh_lanes();
 #pragma unroll
-      for (int z = 0; z < 4; ++z) acc[z] *= s_sc[16 * z + i];
+      for (int z = 0; z < 4; ++z) acc[z] *= s_sc[16 * z + lp.i];
       // ---------------- P = S o D: lane holds S^T[j = 16 kg + 4 g + r][t = 16 z + i]
+      const int i = lp.i, g = lp.g;
       const f32x4 u2 = *reinterpret_cast<const f32x4*>(&s_u2[16 * kg + 4 * g]);
 #pragma unroll
       for (int zz = 0; zz < 2; ++zz) {
@@ -431,7 +458,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
       }
       __syncthreads();   // sP, s_den, s_dn complete
       if (w == 0) {   // 1 / max(|n~^T q|, floor) of row t = lane
-        const int t = lane;
+        const int t = fresh_lanes().lane;
         float den = s_den[t] + s_den[kTile + t] + s_den[2 * kTile + t] + s_den[3 * kTile + t];
         float dn = 0.f;
 #pragma unroll
@@ -440,23 +467,25 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
         s_inv[t] = __builtin_amdgcn_rcpf(fmaxf(fmaxf(fabsf(d), s_fl[t]), FLT_MIN));
       }
       // ---------------- (P V)^T
+      const Lanes lv = fresh_lanes();
 #pragma unroll
       for (int jj = 0; jj < kTile; jj += 32) {
         bf16x8 B[4];
 #pragma unroll
-        for (int z = 0; z < 4; ++z) B[z] = *reinterpret_cast<const bf16x8*>(&sP[(16 * z + i) * PP + jj + 8 * g]);
-        const bf16x8 A = frag_tr(sV, VP, jj, 16 * w);
+        for (int z = 0; z < 4; ++z) B[z] = *reinterpret_cast<const bf16x8*>(&sP[(16 * z + lv.i) * PP + jj + 8 * lv.g]);
+        const bf16x8 A = frag_tr(sV, VP, jj, 16 * w, lv.lane);
 #pragma unroll
         for (int z = 0; z < 4; ++z) acc[z] = mma(A, B[z], acc[z]);
       }
       __syncthreads();   // s_inv complete
       // ---------------- normaliser, output gate; h staged in place of O, four
       // consecutive columns of one row per lane
+      const Lanes le = fresh_lanes();
 #pragma unroll
       for (int z = 0; z < 4; ++z) {
-        const int t = 16 * z + i;
+        const int t = 16 * z + le.i;
         const float inv = s_inv[t];
-        __bf16* p = &sO[t * OP + 16 * w + 4 * g];
+        __bf16* p = &sO[t * OP + 16 * w + 4 * le.g];
         const bf16x4 o4 = *reinterpret_cast<const bf16x4*>(p);
         bf16x4 h4;
 #pragma unroll
@@ -467,9 +496,10 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
         *reinterpret_cast<bf16x4*>(p) = h4;
       }
       __syncthreads();   // h tile complete
+      const Lanes lh = fresh_lanes();
 #pragma unroll
       for (int e = 0; e < VV; ++e) {
-        const int it = tid + NT * e;
+        const int it = lh.tid + NT * e;
         const int row = it / (kVB / 8), cv = it % (kVB / 8);
         if (row < Lc)
           *reinterpret_cast<bf16x8*>(a.h + (tok0 + row) * V + vcol0 + 8 * cv) =
@@ -491,27 +521,28 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
     }
 #pragma unroll
     for (int ts = 0; ts < kTile; ts += 32) {
-      const f32x4 wa = *reinterpret_cast<const f32x4*>(&s_w[ts + 8 * g]);
-      const f32x4 wb = *reinterpret_cast<const f32x4*>(&s_w[ts + 8 * g + 4]);
+      const Lanes lu = fresh_lanes();
+      const f32x4 wa = *reinterpret_cast<const f32x4*>(&s_w[ts + 8 * lu.g]);
+      const f32x4 wb = *reinterpret_cast<const f32x4*>(&s_w[ts + 8 * lu.g + 4]);
       bf16x8 Bv[WY];
 #pragma unroll
       for (int y = 0; y < WY; ++y) {
-        const bf16x8 raw = frag_tr(sV, VP, ts, 16 * (WY * w + y));
+        const bf16x8 raw = frag_tr(sV, VP, ts, 16 * (WY * w + y), lu.lane);
 #pragma unroll
         for (int e = 0; e < 8; ++e) Bv[y][e] = (__bf16)((float)raw[e] * (e < 4 ? wa[e] : wb[e - 4]));
       }
-      const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&swb[min(i, 2) * kTile + ts + 8 * g]);
+      const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&swb[min(lu.i, 2) * kTile + ts + 8 * lu.g]);
       // transposed K fragments through a ring of kRing registers: the read of
       // tile kx + kRing - 1 is issued before the MFMAs of tile kx
       constexpr int kRing = 4;
       bf16x8 Ak[kRing];
       unroll<kRing - 1>([&](auto p_c) {
         constexpr int p = decltype(p_c)::value;
-        if constexpr (p < KX) Ak[p] = frag_tr(sK, KP, ts, 16 * p);
+        if constexpr (p < KX) Ak[p] = frag_tr(sK, KP, ts, 16 * p, lu.lane);
       });
       unroll<KX>([&](auto kx_c) {
         constexpr int kx = decltype(kx_c)::value;
-        if constexpr (kx + kRing - 1 < KX) Ak[(kx + kRing - 1) % kRing] = frag_tr(sK, KP, ts, 16 * (kx + kRing - 1));
+        if constexpr (kx + kRing - 1 < KX) Ak[(kx + kRing - 1) % kRing] = frag_tr(sK, KP, ts, 16 * (kx + kRing - 1), lu.lane);
 #pragma unroll
         for (int y = 0; y < WY; ++y) Ct[kx][y] = mma(Ak[kx % kRing], Bv[y], Ct[kx][y]);
         if (kx / KXW == w) Nacc[kx % KXW] = mma(Ak[kx % kRing], Bw, Nacc[kx % KXW]);
