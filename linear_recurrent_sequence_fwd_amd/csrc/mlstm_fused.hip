@@ -251,32 +251,48 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
   int r_rs = -1, r_rs0 = -1;
   double t_g = 0.0, t_U = 0.0;
   int t_R = -1;
-  auto issue = [&](int64_t tau) {
+  // Tile pointers are wave-uniform (scalar registers); the per-lane parts
+  // are 32-bit element offsets within the tile. The loads of the next tile
+  // go out in parts (mask bits: 1 q, 2 k, 4 v and o, 8 gate data) spread
+  // over the phases of the current one: a wave that issues all of them at
+  // once stalls until the address unit has taken them.
+  auto issue = [&](int64_t tau, int parts) {
     const Lanes ln = fresh_lanes();
-    const int tid = ln.tid, lane = ln.lane;
+    const unsigned tid = (unsigned)ln.tid, lane = (unsigned)ln.lane;
     const int64_t t0 = tau * kTile;
-    const int last = (int)min((int64_t)kTile, T - t0) - 1;
+    const unsigned last = (unsigned)(min((int64_t)kTile, T - t0) - 1);
     const int64_t tok0 = bh * T + t0;
+    if (parts & 3) {
+      const __bf16* qt = a.q + tok0 * K;
+      const __bf16* kt = a.k + tok0 * K;
 #pragma unroll
-    for (int e = 0; e < QV; ++e) {
-      const int it = tid + NT * e;
-      const int row = min(it / (K / 8), last), cv = it % (K / 8);
-      if constexpr (!LOCAL) pq[e] = *reinterpret_cast<const bf16x8*>(a.q + (tok0 + row) * K + 8 * cv);
-      pk[e] = *reinterpret_cast<const bf16x8*>(a.k + (tok0 + row) * K + 8 * cv);
+      for (int e = 0; e < QV; ++e) {
+        const unsigned it = tid + NT * e;
+        const unsigned off = min(it / (K / 8), last) * K + 8 * (it % (K / 8));
+        if constexpr (!LOCAL) {
+          if (parts & 1) pq[e] = *reinterpret_cast<const bf16x8*>(qt + off);
+        }
+        if (parts & 2) pk[e] = *reinterpret_cast<const bf16x8*>(kt + off);
+      }
     }
+    if (parts & 4) {
+      const __bf16* vt = a.v + tok0 * V + vcol0;
+      const __bf16* ot = a.o + tok0 * V + vcol0;
 #pragma unroll
-    for (int e = 0; e < VV; ++e) {
-      const int it = tid + NT * e;
-      const int row = min(it / (kVB / 8), last), cv = it % (kVB / 8);
-      pv[e] = *reinterpret_cast<const bf16x8*>(a.v + (tok0 + row) * V + vcol0 + 8 * cv);
-      if constexpr (!LOCAL) po[e] = *reinterpret_cast<const bf16x8*>(a.o + (tok0 + row) * V + vcol0 + 8 * cv);
+      for (int e = 0; e < VV; ++e) {
+        const unsigned it = tid + NT * e;
+        const unsigned off = min(it / (kVB / 8), last) * (unsigned)V + 8 * (it % (kVB / 8));
+        pv[e] = *reinterpret_cast<const bf16x8*>(vt + off);
+        if constexpr (!LOCAL) po[e] = *reinterpret_cast<const bf16x8*>(ot + off);
+      }
     }
-    const int j = min(lane, last);
-    r_u = a.gb.u[tok0 + j];
+    if (!(parts & 8)) return;
+    const unsigned j = min(lane, last);
+    r_u = (a.gb.u + tok0)[j];
     if constexpr (!LOCAL) {
-      r_mp = a.gb.mp[tok0 + j];
-      r_b = a.gb.b[tok0 + j];
-      r_rs = a.gb.rs[tok0 + j];
+      r_mp = (a.gb.mp + tok0)[j];
+      r_b = (a.gb.b + tok0)[j];
+      r_rs = (a.gb.rs + tok0)[j];
       r_mp0 = a.gb.mp[tok0];
       r_rs0 = a.gb.rs[tok0];
     }
@@ -285,7 +301,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
     t_R = a.gb.R[bh * Nt + tau];
   };
 
-  issue(tile0);
+  issue(tile0, 15);
   for (int64_t tau = tile0; tau < tile1; ++tau) {
     const int64_t t0 = tau * kTile;
     const int Lc = (int)min((int64_t)kTile, T - t0);
@@ -328,15 +344,21 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
     // scalar, so that the rescale below is a branch)
     const bool rescale = __builtin_amdgcn_readfirstlane(logD + ld < -kMaxDefer ? 1 : 0) != 0;
     const double logD_next = rescale ? 0.0 : logD + ld;
-    if (ls.tid < kTile) {
-      const int j = ls.tid;
+    // Per-key and per-row tile data, lane j = token j of the tile; the
+    // quantities are split over the first waves (every wave holds the
+    // tile's gate data).
+    if (w == 0) {
+      const int j = ls.lane;
       const float wj = (j >= t_R && j < Lc && t_U != -INFINITY && live) ? expf((float)(r_u - Rm - logD_next)) : 0.f;
       s_w[j] = wj;
       const __bf16 whi = (__bf16)wj;
       swb[j] = whi;
       swb[kTile + j] = (__bf16)(wj - (float)whi);
-      if constexpr (!LOCAL) {
+    }
+    if constexpr (!LOCAL) {
+      if (w >= 1 && w <= 3) {
         // row stabiliser r_t = max(m_prev if no zero gate at or before t, prefix max of u)
+        const int j = ls.lane;
         const bool carry0 = has_state && r_rs0 < 0;
         double ref = fmax(carry0 ? m_prev : -INFINITY, r_mp0);
         if (ref == -INFINITY) ref = 0.0;
@@ -344,11 +366,15 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
         const bool carry = has_state && r_rs < 0;
         double r = fmax(carry ? m_prev : -INFINITY, r_mp);
         if (r == -INFINITY) r = 0.0;
-        s_r2[j] = valid ? (float)((r - ref) * (double)kLog2eF) : 0.f;
-        s_sc[j] = (valid && carry) ? expf((float)(m_prev - r + logD)) : 0.f;
-        s_fl[j] = valid ? expf((float)(-(r_b + r))) : 1.f;
-        s_rs[j] = r_rs;
-        s_u2[j] = valid ? (float)((r_u - ref) * (double)kLog2eF) : -INFINITY;
+        if (w == 1) {
+          s_r2[j] = valid ? (float)((r - ref) * (double)kLog2eF) : 0.f;
+          s_u2[j] = valid ? (float)((r_u - ref) * (double)kLog2eF) : -INFINITY;
+          s_rs[j] = r_rs;
+        } else if (w == 2) {
+          s_sc[j] = (valid && carry) ? expf((float)(m_prev - r + logD)) : 0.f;
+        } else {
+          s_fl[j] = valid ? expf((float)(-(r_b + r))) : 1.f;
+        }
       }
     }
     if constexpr (!LOCAL) {
@@ -378,7 +404,8 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
       reset_seen = reset_seen || t_R >= 0;
     }
     __syncthreads();   // tile tau staged
-    if (tau + 1 < tile1) issue(tau + 1);
+    const bool more = tau + 1 < tile1;
+    if (more) issue(tau + 1, LOCAL ? 15 : 1);
 
     if constexpr (!LOCAL) {
       // ---------------- Q K^T (16 keys x 32 rows) and (Q C~^T)^T (16 columns x 64 rows)
@@ -428,6 +455,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
           if (i == 0) *reinterpret_cast<f32x4*>(&s_dn[w * kTile + 16 * z + 4 * g]) = d;
         }
       }
+      if (more) issue(tau + 1, 2);
       // the carried-state term enters row t with weight exp(m_prev - r_t + logD);
       // acc[z] register r in lane (g, i) is H^T[v = 16 w + 4 g + r][t = 16 z + i]
       const Lanes lp = fresh_lanes();
@@ -477,6 +505,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
 #pragma unroll
         for (int z = 0; z < 4; ++z) acc[z] = mma(A, B[z], acc[z]);
       }
+      if (more) issue(tau + 1, 4);
       __syncthreads();   // s_inv complete
       // ---------------- normaliser, output gate; h staged in place of O, four
       // consecutive columns of one row per lane
@@ -495,14 +524,16 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
         }
         *reinterpret_cast<bf16x4*>(p) = h4;
       }
+      if (more) issue(tau + 1, 8);
       __syncthreads();   // h tile complete
       const Lanes lh = fresh_lanes();
+      __bf16* ht = a.h + tok0 * V + vcol0;
 #pragma unroll
       for (int e = 0; e < VV; ++e) {
-        const int it = lh.tid + NT * e;
-        const int row = it / (kVB / 8), cv = it % (kVB / 8);
-        if (row < Lc)
-          *reinterpret_cast<bf16x8*>(a.h + (tok0 + row) * V + vcol0 + 8 * cv) =
+        const unsigned it = (unsigned)lh.tid + NT * e;
+        const unsigned row = it / (kVB / 8), cv = it % (kVB / 8);
+        if (row < (unsigned)Lc)
+          *reinterpret_cast<bf16x8*>(ht + row * (unsigned)V + 8 * cv) =
               *reinterpret_cast<const bf16x8*>(&sO[row * OP + 8 * cv]);
       }
     }
