@@ -124,6 +124,9 @@ def make_device_inputs(torch, cfg, dtype="bf16", seed=0):
 
 
 def time_chunkwise(torch, M, L, ev, d, chunk, steps, warmup, kernels=("gate", "state", "out")):
+    """Wall time of `steps` forward calls with no profiling hooks, then the
+    average duration of each kernel group from HIP events recorded around its
+    launches in a second, separate pass of the same number of calls."""
     from linear_recurrent_sequence_fwd_amd import _lib
     h = torch.empty_like(d["v"])
     args = _lib.fwd_args(d["q"], d["k"], d["v"], d["o_pre"], d["i_pre"], d["f_pre"], h)
@@ -139,15 +142,18 @@ def time_chunkwise(torch, M, L, ev, d, chunk, steps, warmup, kernels=("gate", "s
 
     for _ in range(warmup):
         one()
-    pairs = {k: ev.create(2 * steps) for k in kernels}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(steps):
+        one()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    pairs = {k: ev.create(2 * steps) for k in kernels}
     for i in range(steps):
         for k in kernels:
             M.set_launch_events(k, pairs[k][2 * i], pairs[k][2 * i + 1])
         one()
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
     for k in kernels:
         M.set_launch_events(k, None, None)
     per_kernel = {}
@@ -188,14 +194,17 @@ def time_decode(torch, M, ev, steps, warmup):
 
     for i in range(warmup):
         one(i)
-    evs = ev.create(2 * steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        M.set_launch_events("step", evs[2 * i], evs[2 * i + 1])
         one(warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    evs = ev.create(2 * steps)     # per-launch durations: a second pass with the event hook
+    for i in range(steps):
+        M.set_launch_events("step", evs[2 * i], evs[2 * i + 1])
+        one(warmup + steps + i)
+    torch.cuda.synchronize()
     M.set_launch_events("step", None, None)
     k_us = sum(ev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)) / steps * 1e3
     ev.destroy(evs)

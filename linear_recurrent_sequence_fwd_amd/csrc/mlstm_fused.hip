@@ -31,6 +31,9 @@ namespace {
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 constexpr int kVB = 128;                     // value columns per workgroup
+#ifndef RING_L
+#define RING_L 6
+#endif
 constexpr double kMaxDefer = 70.0;           // largest pending log decay kept out of the accumulators
 constexpr float kLog2eF = 1.4426950408889634f;
 
@@ -405,7 +408,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
     }
     __syncthreads();   // tile tau staged
     const bool more = tau + 1 < tile1;
-    if (more) issue(tau + 1, LOCAL ? 15 : 1);
+    if (more) issue(tau + 1, LOCAL ? 2 : 1);
 
     if constexpr (!LOCAL) {
       // ---------------- Q K^T (16 keys x 32 rows) and (Q C~^T)^T (16 columns x 64 rows)
@@ -563,9 +566,12 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
         for (int e = 0; e < 8; ++e) Bv[y][e] = (__bf16)((float)raw[e] * (e < 4 ? wa[e] : wb[e - 4]));
       }
       const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&swb[min(lu.i, 2) * kTile + ts + 8 * lu.g]);
+      if constexpr (LOCAL) {
+        if (ts == 32 && more) issue(tau + 1, 12);   // v and gate data of the next tile
+      }
       // transposed K fragments through a ring of kRing registers: the read of
       // tile kx + kRing - 1 is issued before the MFMAs of tile kx
-      constexpr int kRing = 4;
+      constexpr int kRing = LOCAL ? RING_L : 4;
       bf16x8 Ak[kRing];
       unroll<kRing - 1>([&](auto p_c) {
         constexpr int p = decltype(p_c)::value;
@@ -576,9 +582,15 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
         if constexpr (kx + kRing - 1 < KX) Ak[(kx + kRing - 1) % kRing] = frag_tr(sK, KP, ts, 16 * (kx + kRing - 1), lu.lane);
 #pragma unroll
         for (int y = 0; y < WY; ++y) Ct[kx][y] = mma(Ak[kx % kRing], Bv[y], Ct[kx][y]);
-        if (kx / KXW == w) Nacc[kx % KXW] = mma(Ak[kx % kRing], Bw, Nacc[kx % KXW]);
         __builtin_amdgcn_sched_barrier(0);
       });
+      // n~ tiles of this wave: their K fragments are read again rather than
+      // picked out of the ring under a branch per tile
+#pragma unroll
+      for (int x = 0; x < KXW; ++x) {
+        if (KX >= NW || w * KXW + x < KX)
+          Nacc[x] = mma(frag_tr(sK, KP, ts, 16 * min(w * KXW + x, KX - 1), lu.lane), Bw, Nacc[x]);
+      }
     }
     m_prev = m_next;
     logD = logD_next;
