@@ -104,7 +104,7 @@ int validate_fwd(const mlstm_fwd_args* a) {
 
 struct WsLayout {
   size_t u, b, mp, rs, w0, g, U, R, Cs, ns, ms, total;
-  size_t Cseg, nseg, mloc, mstart, Gseg;
+  size_t Cseg, nseg, mloc, mstart, Gseg, wb;
 };
 
 WsLayout layout(int64_t BH, int64_t T, int64_t Nc, int64_t K, int64_t V, int64_t cs_elem, bool states) {
@@ -157,6 +157,7 @@ WsLayout layout_fused(int64_t BH, int64_t T, int chunk, int64_t K, int64_t V) {
   w.mloc = take(BH * ns * 8);
   w.mstart = take(BH * ns * 8);
   w.Gseg = take(BH * ns * 8);
+  w.wb = take(BH * fs.Nt * 2 * 64 * 2);
   w.total = off;
   return w;
 }
@@ -168,6 +169,7 @@ mlstm_impl::GateBuffers gate_buffers(char* ws, const WsLayout& w) {
   gb.mp = reinterpret_cast<double*>(ws + w.mp);
   gb.rs = reinterpret_cast<int*>(ws + w.rs);
   gb.w0 = reinterpret_cast<float*>(ws + w.w0);
+  gb.wb = nullptr;
   gb.g = reinterpret_cast<double*>(ws + w.g);
   gb.U = reinterpret_cast<double*>(ws + w.U);
   gb.R = reinterpret_cast<int*>(ws + w.R);
@@ -252,7 +254,8 @@ int mlstm_fwd_chunkwise(const mlstm_fwd_args* a, int chunk, void* workspace, siz
     const FusedShape fs = fused_shape(a->T, chunk);
     const mlstm_impl::FwdLaunch ft = fwd_launch(a, 64, fs.Nt);
     const WsLayout w = layout_fused(ft.BH, ft.T, chunk, ft.K, ft.V);
-    const mlstm_impl::GateBuffers gb = gate_buffers(ws, w);
+    mlstm_impl::GateBuffers gb = gate_buffers(ws, w);
+    gb.wb = reinterpret_cast<uint16_t*>(ws + w.wb);
     mlstm_impl::SegStates ss;
     ss.C = reinterpret_cast<float*>(ws + w.Cseg);
     ss.n = reinterpret_cast<float*>(ws + w.nseg);

@@ -29,6 +29,8 @@ namespace mlstm_impl {
 namespace {
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
 
 constexpr int kVB = 128;                     // value columns per workgroup
 #ifndef RING_L
@@ -49,17 +51,23 @@ __device__ __forceinline__ bf16x8 frag_tr(const __bf16* X, int P, int kin0, int 
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Row-major operand fragment whose contraction index follows the accumulator
-// layout of C^T: lane (g, i) receives X[row][k0 + 4g + e] for e = 0..3 and
-// X[row][k0 + 16 + 4g + e - 4] for e = 4..7. A contraction is a sum, so any
-// permutation of its index works as long as both operands use it.
-__device__ __forceinline__ bf16x8 frag_split(const __bf16* X, int P, int row, int k0, int lane) {
-  const int g = lane >> 4;
-  const __bf16* p = X + row * P + k0 + 4 * g;
-  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(p);
-  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(p + 16);
+// Transposed K fragment for 16-row tile kx = 2 s + h of the state C~^T, in
+// the register layout where row 4 c + r of the tile holds k = 32 s + 8 c + 4 h
+// + r: lane (g, i) receives X[kin0 + 8 g + e][32 s + 4 h + 8 (i / 4) + i % 4].
+// With this layout the tiles 2 s and 2 s + 1 of a lane hold the eight
+// consecutive k = 32 s + 8 g .. + 7, the order of a plain 16-byte row read of
+// Q or K, so the state packs directly into operand fragments.
+__device__ __forceinline__ bf16x8 frag_trk(const __bf16* X, int P, int kin0, int kx, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  const __bf16* p = X + (kin0 + 8 * g + (i >> 2)) * P + 32 * (kx >> 1) + 4 * (kx & 1) + 8 * (i & 3);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * P));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+
+// Offset along d_qk of the four consecutive k that lane group g holds in
+// register tile kx of the state (see frag_trk).
+__device__ __forceinline__ int state_k0(int kx, int g) { return 32 * (kx >> 1) + 8 * g + 4 * (kx & 1); }
 
 // threadIdx.x through an opaque register move. Lane-dependent LDS and global
 // addresses derived from it are recomputed in the phase that uses them
@@ -123,7 +131,7 @@ template <bool LOCAL> struct SegWaves { static constexpr int value = LOCAL ? 4 :
 template <int K, bool LOCAL>
 struct SegLds {
   static constexpr int QP = K + 16;       // sQ row pitch (16-byte operand reads)
-  static constexpr int KP = K + 8;        // sK row pitch (8-byte and transposed reads)
+  static constexpr int KP = K + 32;       // sK row pitch: 16 dwords mod 64 banks, conflict-free for frag_trk
   static constexpr int VP = kVB + 8;      // sV row pitch (transposed reads)
   static constexpr int OP = kVB + 8;      // sO row pitch
   static constexpr int PP = kTile + 8;    // sP row pitch
@@ -142,7 +150,7 @@ struct SegLds {
 
 // Wave w owns value columns [16 WY w, 16 WY (w + 1)) of the workgroup's 128
 // and keeps C~^T[k][v] for all k of them in registers: register r of
-// Ct[kx][y] in lane (g, i) is k = 16 kx + 4 g + r, v = 16 (WY w + y) + i. The
+// Ct[kx][y] in lane (g, i) is k = state_k0(kx, g) + r, v = 16 (WY w + y) + i. The
 // normaliser n~ is carried as two MFMA columns (lane i = 0: the sum weighted
 // by the bf16 high halves of the key weights, i = 1: by the low halves) in
 // Nacc, for the 16-row tiles kx = KXW w .. KXW w + KXW - 1. The output
@@ -226,12 +234,12 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
   for (int kx = 0; kx < KX; ++kx)
 #pragma unroll
     for (int y = 0; y < WY; ++y)
-      Ct[kx][y] = Cinit ? *reinterpret_cast<const f32x4*>(Cinit + (vcol0 + 16 * (WY * w + y) + i) * K + 16 * kx + 4 * g)
+      Ct[kx][y] = Cinit ? *reinterpret_cast<const f32x4*>(Cinit + (vcol0 + 16 * (WY * w + y) + i) * K + state_k0(kx, g))
                         : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int x = 0; x < KXW; ++x) {
     const int kx = w * KXW + x;
-    Nacc[x] = (ninit && i == 0 && kx < KX) ? *reinterpret_cast<const f32x4*>(ninit + 16 * kx + 4 * g)
+    Nacc[x] = (ninit && i == 0 && kx < KX) ? *reinterpret_cast<const f32x4*>(ninit + state_k0(kx, g))
                                            : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   // zero rows of the two-column normaliser operands
@@ -317,14 +325,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
     for (int e = 0; e < QV; ++e) {
       const int it = ls.tid + NT * e;
       const int row = it / (K / 8), cv = it % (K / 8);
-      if constexpr (!LOCAL) {
-        // within each 32-column block the columns are stored in the order in
-        // which the operand fragments take them (4 g .. 4 g + 3, then 16 + 4 g ..)
-        const int blk = cv >> 2, j = cv & 3;
-        const int p0 = 32 * blk + 8 * (2 * (j & 1)) + 4 * (j >> 1);
-        *reinterpret_cast<bf16x4*>(&sQ[row * QP + p0]) = __builtin_shufflevector(pq[e], pq[e], 0, 1, 2, 3);
-        *reinterpret_cast<bf16x4*>(&sQ[row * QP + p0 + 8]) = __builtin_shufflevector(pq[e], pq[e], 4, 5, 6, 7);
-      }
+      if constexpr (!LOCAL) *reinterpret_cast<bf16x8*>(&sQ[row * QP + 8 * cv]) = pq[e];
       *reinterpret_cast<bf16x8*>(&sK[row * KP + 8 * cv]) = pk[e];
     }
 #pragma unroll
@@ -394,7 +395,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
             hi4[r] = hi;
             lo4[r] = (__bf16)(nr - (float)hi);
           }
-          const int pos = 32 * (kx >> 1) + 8 * ls.g + 4 * (kx & 1);
+          const int pos = state_k0(kx, ls.g);
           if (ls.i == 0) {
             *reinterpret_cast<bf16x4*>(&snb[pos]) = hi4;
             *reinterpret_cast<bf16x4*>(&snb[K + pos]) = lo4;
@@ -422,7 +423,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
         bf16x8 fa[4];
 #pragma unroll
         for (int z = 0; z < 4; ++z) fa[z] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * z + l1.i) * QP + 32 * s + 8 * l1.g]);
-        const bf16x8 fk = frag_split(sK, KP, 16 * kg + l1.i, 32 * s, l1.lane);
+        const bf16x8 fk = *reinterpret_cast<const bf16x8*>(&sK[(16 * kg + l1.i) * KP + 32 * s + 8 * l1.g]);
         if (zh == 0) {   // scalar branch: a register array takes static indices only
           sacc[0] = mma(fk, fa[0], sacc[0]);
           sacc[1] = mma(fk, fa[1], sacc[1]);
@@ -575,11 +576,12 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
       bf16x8 Ak[kRing];
       unroll<kRing - 1>([&](auto p_c) {
         constexpr int p = decltype(p_c)::value;
-        if constexpr (p < KX) Ak[p] = frag_tr(sK, KP, ts, 16 * p, lu.lane);
+        if constexpr (p < KX) Ak[p] = frag_trk(sK, KP, ts, p, lu.lane);
       });
       unroll<KX>([&](auto kx_c) {
         constexpr int kx = decltype(kx_c)::value;
-        if constexpr (kx + kRing - 1 < KX) Ak[(kx + kRing - 1) % kRing] = frag_tr(sK, KP, ts, 16 * (kx + kRing - 1), lu.lane);
+        if constexpr (kx + kRing - 1 < KX) Ak[(kx + kRing - 1) % kRing] = frag_trk(sK, KP, ts, kx + kRing - 1, lu.lane);
+
 #pragma unroll
         for (int y = 0; y < WY; ++y) Ct[kx][y] = mma(Ak[kx % kRing], Bv[y], Ct[kx][y]);
         __builtin_amdgcn_sched_barrier(0);
@@ -589,7 +591,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
 #pragma unroll
       for (int x = 0; x < KXW; ++x) {
         if (KX >= NW || w * KXW + x < KX)
-          Nacc[x] = mma(frag_tr(sK, KP, ts, 16 * min(w * KXW + x, KX - 1), lu.lane), Bw, Nacc[x]);
+          Nacc[x] = mma(frag_trk(sK, KP, ts, min(w * KXW + x, KX - 1), lu.lane), Bw, Nacc[x]);
       }
     }
     m_prev = m_next;
@@ -619,7 +621,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
     for (int kx = 0; kx < KX; ++kx)
 #pragma unroll
       for (int y = 0; y < WY; ++y)
-        *reinterpret_cast<f32x4*>(Cdst + (vcol0 + 16 * (WY * w + y) + i) * K + 16 * kx + 4 * g) = fD * Ct[kx][y];
+        *reinterpret_cast<f32x4*>(Cdst + (vcol0 + 16 * (WY * w + y) + i) * K + state_k0(kx, g)) = fD * Ct[kx][y];
   }
   if (ndst) {
 #pragma unroll
@@ -628,16 +630,23 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
       f32x4 nv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) nv[r] = fD * (Nacc[x][r] + __shfl_xor(Nacc[x][r], 1, 64));
-      if (i == 0 && kx < KX) *reinterpret_cast<f32x4*>(ndst + 16 * kx + 4 * g) = nv;
+      if (i == 0 && kx < KX) *reinterpret_cast<f32x4*>(ndst + state_k0(kx, g)) = nv;
     }
   }
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+  const unsigned lo = __builtin_amdgcn_readlane((unsigned)u, lane);
+  const unsigned hi = __builtin_amdgcn_readlane((unsigned)(u >> 32), lane);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
 }
 
 // True when some tile of the chunk would need the accumulators rescaled:
 // the pending decay logD + ld falls below -kMaxDefer while the state is not
 // known to be zero. Follows the same float64 steps as the tile loop, from the
 // tile scalars only (lanes load 64 tiles at a time, the scan runs on
-// shuffles); the result is uniform over the workgroup.
+// lane reads); the result is uniform over the workgroup.
 __device__ bool chunk_needs_rescale(const SegArgs& a, int64_t bh, int64_t tile0, int64_t tile1, double m,
                                     bool zero, bool local) {
   const int lane = threadIdx.x & 63;
@@ -648,8 +657,8 @@ __device__ bool chunk_needs_rescale(const SegArgs& a, int64_t bh, int64_t tile0,
     const double gv = a.gb.g[t], Uv = a.gb.U[t];
     const int Rv = a.gb.R[t];
     for (int j = 0; j < n; ++j) {
-      const double gj = __shfl(gv, j, 64), Uj = __shfl(Uv, j, 64);
-      const int Rj = __shfl(Rv, j, 64);
+      const double gj = readlane_f64(gv, j), Uj = readlane_f64(Uv, j);
+      const int Rj = __builtin_amdgcn_readlane(Rv, j);
       double Rm = fmax(Rj >= 0 ? -INFINITY : m, Uj);
       if (!local && Rm == -INFINITY) Rm = 0.0;
       const bool live = Rm != -INFINITY;
@@ -689,6 +698,275 @@ __global__ __launch_bounds__(64 * SegWaves<LOCAL>::value, 1) void seg_kernel(Seg
     seg_body<K, LOCAL, true>(a, smem);
   else
     seg_body<K, LOCAL, false>(a, smem);
+}
+
+// ------------------------------------------------------------------ chunk-local end states
+
+// The chunks' local end states (every chunk but the last, all of whose
+// tiles are full): C~loc = sum over the chunk's tiles of the decayed K^T
+// diag(w) V, computed by the same stabilised tile recurrence as the output
+// kernel, starting from nothing. The compute waves (LocWaves) each own an
+// equal share of the d_qk rows of C~^T for all 128 value columns (state in
+// VGPRs), so every K^T
+// fragment is read from LDS by one wave only and scaled there by the key
+// weights; the V fragments are shared. A fifth wave only moves data: it copies tile tau + 1
+// (K, the workgroup's 128 columns of V, the keys' in-tile weights w0 and the
+// tile's gate scalars) straight into the other half of a double-buffered LDS
+// area with direct-to-LDS loads while the compute waves work on tile tau.
+// One barrier per tile; the compute waves issue no global loads in the loop.
+constexpr int kMaxTiles = 8192 / kTile;   // tiles per chunk at the largest chunk
+
+// Scalars of a chunk's local end state, scanned once from the tile gate
+// scalars (the same float64 steps as the output kernel's tile loop, from an
+// empty state): per tile the factor exp(U - Rm - logD_next) that turns the
+// in-tile weights w0 into the key weights, and the factor that rescales the
+// accumulators before the tile (1 when the decay is kept pending).
+struct LocScan {
+  double m, logD, G;
+  bool reset, any_rescale;
+};
+__device__ LocScan local_scan(const SegArgs& a, int64_t bh, int64_t tile0, int ntiles, float* s_cw, float* s_rf) {
+  const int lane = threadIdx.x & 63;
+  LocScan r{-INFINITY, 0.0, 0.0, false, false};
+  bool zero = true;
+  for (int base = 0; base < ntiles; base += 64) {
+    const int n = min(64, ntiles - base);
+    const int64_t t = bh * a.Nt + tile0 + base + min(lane, n - 1);
+    const double gv = a.gb.g[t], Uv = a.gb.U[t];
+    const int Rv = a.gb.R[t];
+    for (int j = 0; j < n; ++j) {
+      const double gj = readlane_f64(gv, j), Uj = readlane_f64(Uv, j);
+      const int Rj = __builtin_amdgcn_readlane(Rv, j);
+      const double Rm = fmax(Rj >= 0 ? -INFINITY : r.m, Uj);
+      const bool live = Rm != -INFINITY;
+      const double ld = (Rj >= 0 || r.m == -INFINITY || !live) ? -INFINITY : r.m - Rm;
+      const bool rescale = r.logD + ld < -kMaxDefer;
+      const double logD_next = rescale ? 0.0 : r.logD + ld;
+      const bool scale = rescale && !zero;   // rescaling a zero state is a no-op
+      if (lane == 0) {
+        s_cw[base + j] = (live && Uj != -INFINITY) ? expf((float)(Uj - Rm - logD_next)) : 0.f;
+        s_rf[base + j] = scale ? (float)exp(r.logD + ld) : 1.f;
+      }
+      r.any_rescale = r.any_rescale || scale;
+      r.m = live ? gj + Rm : -INFINITY;
+      r.logD = logD_next;
+      r.G += gj;
+      r.reset = r.reset || Rj >= 0;
+      if (live && Uj != -INFINITY) zero = false;
+    }
+  }
+  return r;
+}
+
+template <int K>
+struct LocLds {
+  static constexpr int KP = K + 16;                 // 8 dwords mod 64 banks: conflict-free for frag_tr
+  static constexpr int VP = kVB + 8;
+  static constexpr int CPRK = KP / 8;               // 16-byte chunks per LDS row of K
+  static constexpr int CPRV = VP / 8;
+  static constexpr int kBytes = kTile * KP * 2;     // = 1024 * CPRK: CPRK direct loads
+  static constexpr int vBytes = kTile * VP * 2;     // = 1024 * CPRV
+  static constexpr int oK = 0;                      // [2] K tiles
+  static constexpr int oV = oK + 2 * kBytes;        // [2] V tiles
+  static constexpr int oW = oV + 2 * vBytes;        // [2][64] float w0
+  static constexpr int oWb = oW + 2 * kTile * 4;       // [2][3][64] bf16: w0 hi, w0 lo, zero
+  static constexpr int oCw = oWb + 2 * 3 * kTile * 2;   // [kMaxTiles] float: tile weight factor
+  static constexpr int oRf = oCw + kMaxTiles * 4;       // [kMaxTiles] float: accumulator rescale (1 = none)
+  static constexpr int bytes = oRf + kMaxTiles * 4;
+};
+// Compute waves of local_kernel: eight (two per SIMD, 32 d_qk rows each) when
+// d_qk allows, else four.
+template <int K> struct LocWaves { static constexpr int value = K >= 128 ? 8 : 4; };
+
+// The loader wave of local_kernel: tile tau + 1 into the free half of the
+// double buffer while the compute waves work on tile tau.
+template <int K>
+__device__ __forceinline__ void local_loader(const SegArgs& a, char* smem) {
+  using L = LocLds<K>;
+  const int64_t BH = a.BH, T = a.T, V = a.V, Nt = a.Nt;
+  const int nvb = (int)(V / kVB);
+  const int64_t bh = blockIdx.x % BH;
+  const int64_t rest = blockIdx.x / BH;
+  const int vb = (int)(rest % nvb);
+  const int seg = (int)(rest / nvb);
+  const int64_t tile0 = (int64_t)seg * a.TPS;
+  const int64_t tile1 = tile0 + a.TPS;
+  const int64_t vcol0 = (int64_t)vb * kVB;
+  // ---------------- loader wave: per-lane source offsets of the direct
+  // loads (chunk c = 64 n + lane of a tile's padded LDS image lies in row
+  // c / CPR; padding chunks repeat the row's last data chunk)
+  const int lane = threadIdx.x & 63;
+  unsigned offk[L::CPRK], offv[L::CPRV];
+#pragma unroll
+  for (int n = 0; n < L::CPRK; ++n) {
+    const int c = 64 * n + lane, row = c / L::CPRK, ch = min(c % L::CPRK, K / 8 - 1);
+    offk[n] = (unsigned)(row * K + 8 * ch);
+  }
+#pragma unroll
+  for (int n = 0; n < L::CPRV; ++n) {
+    const int c = 64 * n + lane, row = c / L::CPRV, ch = min(c % L::CPRV, kVB / 8 - 1);
+    offv[n] = (unsigned)(row * V + 8 * ch);
+  }
+  auto dma = [&](int64_t tau, int buf) {
+    const __bf16* kt = a.k + (bh * T + tau * kTile) * K;
+    const __bf16* vt = a.v + (bh * T + tau * kTile) * V + vcol0;
+    char* kd = smem + L::oK + buf * L::kBytes;
+    char* vd = smem + L::oV + buf * L::vBytes;
+#pragma unroll
+    for (int n = 0; n < L::CPRK; ++n)
+      __builtin_amdgcn_global_load_lds((global_void*)(kt + offk[n]), (lds_void*)(kd + 1024 * n), 16, 0, 0);
+#pragma unroll
+    for (int n = 0; n < L::CPRV; ++n)
+      __builtin_amdgcn_global_load_lds((global_void*)(vt + offv[n]), (lds_void*)(vd + 1024 * n), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((global_void*)(a.gb.w0 + bh * T + tau * kTile + lane),
+                                     (lds_void*)(smem + L::oW + buf * kTile * 4), 4, 0, 0);
+    if (lane < 16)   // hi and lo rows of the split weights, 256 bytes
+      __builtin_amdgcn_global_load_lds((global_void*)(a.gb.wb + (bh * Nt + tau) * 2 * kTile + 8 * lane),
+                                       (lds_void*)(smem + L::oWb + buf * 3 * kTile * 2), 16, 0, 0);
+  };
+  dma(tile0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int64_t tau = tile0; tau < tile1; ++tau) {
+    __syncthreads();   // tile tau published; the other buffer is free
+    if (tau + 1 < tile1) dma(tau + 1, (int)((tau + 1 - tile0) & 1));
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+}
+
+template <int K, bool RESCALE>
+__device__ __forceinline__ void local_body(const SegArgs& a, char* smem, const LocScan& sc) {
+  using L = LocLds<K>;
+  constexpr int KP = L::KP, VP = L::VP;
+  constexpr int KX = K / 16, NW = LocWaves<K>::value, KXW = KX / NW, VY = kVB / 16;
+  static_assert(KX % NW == 0, "KX / NW row tiles per compute wave");
+  const int64_t BH = a.BH, T = a.T, V = a.V, Nt = a.Nt;
+  const int nvb = (int)(V / kVB);
+  const int64_t bh = blockIdx.x % BH;
+  const int64_t rest = blockIdx.x / BH;
+  const int vb = (int)(rest % nvb);
+  const int seg = (int)(rest / nvb);
+  const int64_t tile0 = (int64_t)seg * a.TPS;
+  const int64_t tile1 = tile0 + a.TPS;
+  const int64_t vcol0 = (int64_t)vb * kVB;
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+
+  // ---------------- compute waves: register r of Ct[x][y] in lane (g, i) is
+  // C~^T[k = 16 (KXW w + x) + 4 g + r][v = 16 y + i]
+  f32x4 Ct[KXW][VY];
+  f32x4 Nacc[KXW];
+#pragma unroll
+  for (int x = 0; x < KXW; ++x) {
+#pragma unroll
+    for (int y = 0; y < VY; ++y) Ct[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Nacc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float* s_cw = reinterpret_cast<const float*>(smem + L::oCw);
+  const float* s_rf = reinterpret_cast<const float*>(smem + L::oRf);
+  for (int64_t tau = tile0; tau < tile1; ++tau) {
+    __syncthreads();   // tile tau in buffer buf
+    const int j = (int)(tau - tile0), buf = j & 1;
+    const __bf16* sK = reinterpret_cast<const __bf16*>(smem + L::oK + buf * L::kBytes);
+    const __bf16* sV = reinterpret_cast<const __bf16*>(smem + L::oV + buf * L::vBytes);
+    const float* s_w0 = reinterpret_cast<const float*>(smem + L::oW + buf * kTile * 4);
+    const __bf16* swb = reinterpret_cast<const __bf16*>(smem + L::oWb + buf * 3 * kTile * 2);
+    // keys enter with weight exp(u_j - Rm - logD_next) = w0_j cw
+    const float cw = s_cw[j];
+    if constexpr (RESCALE) {
+      const float f = s_rf[j];
+      if (__builtin_amdgcn_readfirstlane(f != 1.f ? 1 : 0)) {
+#pragma unroll
+        for (int x = 0; x < KXW; ++x) {
+#pragma unroll
+          for (int y = 0; y < VY; ++y) Ct[x][y] *= f;
+          Nacc[x] *= f;
+        }
+      }
+    }
+#pragma unroll
+    for (int ts = 0; ts < kTile; ts += 32) {
+      const Lanes lu = fresh_lanes();
+      f32x4 wa = *reinterpret_cast<const f32x4*>(&s_w0[ts + 8 * lu.g]);
+      f32x4 wb = *reinterpret_cast<const f32x4*>(&s_w0[ts + 8 * lu.g + 4]);
+      wa *= cw;
+      wb *= cw;
+      // n~ operand: column 0 the bf16 high parts of w0, column 1 the low
+      // parts, the rest zero; the product is scaled by cw in float32
+      const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&swb[min(lu.i, 2) * kTile + ts + 8 * lu.g]);
+      // this wave's K^T fragments: raw for n~, scaled by the key weights for C~
+      bf16x8 As[KXW], Kr[KXW], Bv[4];
+#pragma unroll
+      for (int x = 0; x < KXW; ++x) Kr[x] = frag_tr(sK, KP, ts, 16 * (KXW * w + x), lu.lane);
+      unroll<3>([&](auto y_c) {
+        constexpr int y = decltype(y_c)::value;
+        if constexpr (y < VY) Bv[y] = frag_tr(sV, VP, ts, 16 * y, lu.lane);
+      });
+#pragma unroll
+      for (int x = 0; x < KXW; ++x) {
+        const bf16x8 raw = Kr[x];
+        Nacc[x] += cw * mma(raw, Bw, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int e = 0; e < 8; ++e) As[x][e] = (__bf16)((float)raw[e] * (e < 4 ? wa[e] : wb[e - 4]));
+      }
+      // V fragments through a ring of kRing: the read of column tile
+      // y + kRing - 1 is issued before the MFMAs of tile y
+      constexpr int kRing = 4;
+      unroll<VY>([&](auto y_c) {
+        constexpr int y = decltype(y_c)::value;
+        if constexpr (y + kRing - 1 < VY) Bv[(y + kRing - 1) % kRing] = frag_tr(sV, VP, ts, 16 * (y + kRing - 1), lu.lane);
+#pragma unroll
+        for (int x = 0; x < KXW; ++x) Ct[x][y] = mma(As[x], Bv[y % kRing], Ct[x][y]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+  }
+  const float fD = (float)exp(sc.logD);
+  const Lanes le = fresh_lanes();
+  const int64_t sidx = bh * (a.S - 1) + seg;
+  float* Cdst = a.Cseg + sidx * V * K;
+#pragma unroll
+  for (int x = 0; x < KXW; ++x)
+#pragma unroll
+    for (int y = 0; y < VY; ++y)
+      *reinterpret_cast<f32x4*>(Cdst + (vcol0 + 16 * y + le.i) * K + 16 * (KXW * w + x) + 4 * le.g) = fD * Ct[x][y];
+  if (vb == 0) {
+    float* ndst = a.nseg + sidx * K;
+#pragma unroll
+    for (int x = 0; x < KXW; ++x) {
+      f32x4 nv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) nv[r] = fD * (Nacc[x][r] + __shfl_xor(Nacc[x][r], 1, 64));
+      if (le.i == 0) *reinterpret_cast<f32x4*>(ndst + 16 * (KXW * w + x) + 4 * le.g) = nv;
+    }
+    if (w == 0 && le.lane == 0) {
+      a.mloc[sidx] = sc.m;
+      a.Gseg[sidx] = sc.reset ? -INFINITY : sc.G;
+    }
+  }
+}
+
+template <int K>
+__global__ __launch_bounds__(64 * (LocWaves<K>::value + 1)) void local_kernel(SegArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[LocLds<K>::bytes];
+  if (__builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) == LocWaves<K>::value) {
+    local_loader<K>(a, smem);   // starts the first tile's copy at once
+    return;
+  }
+  const int64_t bh = blockIdx.x % a.BH;
+  const int seg = (int)(blockIdx.x / a.BH / (a.V / kVB));
+  const int64_t tile0 = (int64_t)seg * a.TPS;
+  using L = LocLds<K>;
+  // zero rows of the split-weight operands (published by the first barrier);
+  // every compute wave writes the same tile table and reads only its own writes
+  if (threadIdx.x < kTile) {
+    reinterpret_cast<__bf16*>(smem + L::oWb)[2 * kTile + threadIdx.x] = (__bf16)0.f;
+    reinterpret_cast<__bf16*>(smem + L::oWb + 3 * kTile * 2)[2 * kTile + threadIdx.x] = (__bf16)0.f;
+  }
+  const LocScan sc = local_scan(a, bh, tile0, a.TPS, reinterpret_cast<float*>(smem + L::oCw),
+                                reinterpret_cast<float*>(smem + L::oRf));
+  if (sc.any_rescale)
+    local_body<K, true>(a, smem, sc);
+  else
+    local_body<K, false>(a, smem, sc);
 }
 
 // ------------------------------------------------------------------ chunk combine
@@ -772,7 +1050,7 @@ hipError_t run_seg(const FwdLaunch& f, const GateBuffers& gb, const SegStates& s
   const int64_t nvb = f.V / kVB;
   if (ss.S > 1) {
     mark_before(K_STATE, s);
-    hipLaunchKernelGGL((seg_kernel<K, true>), dim3((unsigned)(f.BH * nvb * (ss.S - 1))), dim3(64 * SegWaves<true>::value), 0, s, a);
+    hipLaunchKernelGGL((local_kernel<K>), dim3((unsigned)(f.BH * nvb * (ss.S - 1))), dim3(64 * (LocWaves<K>::value + 1)), 0, s, a);
     CombineArgs c;
     c.C0 = f.C0; c.n0 = f.n0; c.m0 = f.m0;
     c.Cseg = ss.C; c.nseg = ss.n; c.mloc = ss.mloc; c.mstart = ss.mstart; c.Gseg = ss.G;

@@ -158,6 +158,14 @@ __global__ __launch_bounds__(kThreads) void gate64_kernel(GateArgs a) {
     a.gb.rs[base + lane] = rs;
     a.gb.w0[base + lane] = (lane >= Rc && Uc != -INFINITY) ? expf((float)(u - Uc)) : 0.f;
   }
+  if (a.gb.wb) {
+    const float w0 = (valid && lane >= Rc && Uc != -INFINITY) ? expf((float)(u - Uc)) : 0.f;
+    const __bf16 hi = (__bf16)w0;
+    const __bf16 lo = (__bf16)(w0 - (float)hi);
+    uint16_t* dst = a.gb.wb + (bh * a.Nc + c) * 2 * kTile;
+    dst[lane] = __builtin_bit_cast(uint16_t, hi);
+    dst[kTile + lane] = __builtin_bit_cast(uint16_t, lo);
+  }
   if (lane == 0) {
     a.gb.g[bh * a.Nc + c] = gc;
     a.gb.U[bh * a.Nc + c] = Uc;

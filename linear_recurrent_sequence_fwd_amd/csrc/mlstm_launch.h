@@ -24,6 +24,8 @@ struct GateBuffers {
   double* U;    // mp at the chunk's last token
   int* R;       // rs at the chunk's last token
   float* w0;    // exp(u_j - U) for keys at or after the chunk's last zero forget gate, else 0
+  uint16_t* wb; // 64-token tiles only, [BH][Nt][2][64]: bfloat16 bits of w0 (hi) and of
+                // w0 - hi (lo), a two-term split of w0; null when not wanted
 };
 
 // Chunk-start states written by the state pass: Cs [BH][Nc][V][K] (bf16 or
