@@ -80,6 +80,22 @@ __device__ __forceinline__ int fresh_tid() {
   return t;
 }
 
+// Cross-lane sums without the LDS permute path: x + x of lane l ^ 1 (DPP
+// quad permutation), and the sum over the four 16-lane rows of lanes with
+// the same l % 16 (row swaps by 16 and 32 lanes). Every lane of a pair adds
+// the two values in the same order, so the results agree bit for bit.
+__device__ __forceinline__ float sum_xor1(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float sum_rows(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __builtin_bit_cast(float, (unsigned)a[0]) + __builtin_bit_cast(float, (unsigned)a[1]);
+  const unsigned v = __builtin_bit_cast(unsigned, y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __builtin_bit_cast(float, (unsigned)b[0]) + __builtin_bit_cast(float, (unsigned)b[1]);
+}
+
 struct Lanes {
   int tid, lane, i, g;   // thread, lane, lane % 16, lane / 16
 };
@@ -390,7 +406,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
           bf16x4 hi4, lo4;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float nr = Nacc[x][r] + __shfl_xor(Nacc[x][r], 1, 64);
+            const float nr = sum_xor1(Nacc[x][r]);
             const __bf16 hi = (__bf16)nr;
             hi4[r] = hi;
             lo4[r] = (__bf16)(nr - (float)hi);
@@ -455,7 +471,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
         for (int z = 0; z < 4; ++z) {
           f32x4 d;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) d[r] = dacc[z][r] + __shfl_xor(dacc[z][r], 1, 64);
+          for (int r = 0; r < 4; ++r) d[r] = sum_xor1(dacc[z][r]);
           if (i == 0) *reinterpret_cast<f32x4*>(&s_dn[w * kTile + 16 * z + 4 * g]) = d;
         }
       }
@@ -484,8 +500,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
           pk4[r] = (__bf16)p;
         }
         *reinterpret_cast<bf16x4*>(&sP[tl * PP + 16 * kg + 4 * g]) = pk4;
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
+        psum = sum_rows(psum);
         if (g == 0) s_den[kg * kTile + tl] = psum;
       }
       __syncthreads();   // sP, s_den, s_dn complete
@@ -629,7 +644,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
       const int kx = w * KXW + x;
       f32x4 nv;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) nv[r] = fD * (Nacc[x][r] + __shfl_xor(Nacc[x][r], 1, 64));
+      for (int r = 0; r < 4; ++r) nv[r] = fD * sum_xor1(Nacc[x][r]);
       if (i == 0 && kx < KX) *reinterpret_cast<f32x4*>(ndst + state_k0(kx, g)) = nv;
     }
   }
@@ -934,7 +949,7 @@ __device__ __forceinline__ void local_body(const SegArgs& a, char* smem, const L
     for (int x = 0; x < KXW; ++x) {
       f32x4 nv;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) nv[r] = fD * (Nacc[x][r] + __shfl_xor(Nacc[x][r], 1, 64));
+      for (int r = 0; r < 4; ++r) nv[r] = fD * sum_xor1(Nacc[x][r]);
       if (le.i == 0) *reinterpret_cast<f32x4*>(ndst + 16 * (KXW * w + x) + 4 * le.g) = nv;
     }
     if (w == 0 && le.lane == 0) {
