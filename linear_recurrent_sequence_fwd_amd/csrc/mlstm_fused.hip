@@ -7,17 +7,21 @@
 // Training"), organised so that the d_v x d_qk state never leaves the chip
 // inside a chunk:
 //
-//   seg_kernel<LOCAL>  one workgroup per (head, 128 value columns, chunk).
+//   local_kernel       one workgroup per (head, 128 value columns, chunk but
+//                      the last): the chunk's own end state from an empty
+//                      state, C~loc = sum of decayed K^T diag(w) V over its
+//                      tiles on MFMA; a loader wave streams the tiles into
+//                      double-buffered LDS with direct-to-LDS loads.
+//   seg_combine_kernel folds the chunks' local end states in order into the
+//                      start state of every chunk (elementwise, float32).
+//   out_kernel_fused   one workgroup per (head, 128 value columns, chunk).
 //                      Holds its 128 x d_qk slice of C~ (float32) in MFMA
 //                      accumulators and walks the chunk in 64-token tiles.
 //                      Per tile: Q K^T on MFMA, decay mask and stabiliser in
 //                      registers, P V and Q C~^T on MFMA, normaliser and output
 //                      gate, then C~ <- a C~ + K^T diag(w) V on MFMA and the
 //                      same for n~ (a two-column MFMA tile carrying the weights
-//                      as bf16 hi + lo). The LOCAL variant only accumulates the
-//                      chunk's own end state from zero (no outputs).
-//   seg_combine_kernel folds the chunks' local end states in order into the
-//                      start state of every chunk (elementwise, float32).
+//                      as bf16 hi + lo).
 //
 // Chunks are independent given their start states, so the sequence dimension
 // supplies the parallelism that the few heads of a large layer lack.
@@ -33,9 +37,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void global_void;
 
 constexpr int kVB = 128;                     // value columns per workgroup
-#ifndef RING_L
-#define RING_L 6
-#endif
 constexpr double kMaxDefer = 70.0;           // largest pending log decay kept out of the accumulators
 constexpr float kLog2eF = 1.4426950408889634f;
 
@@ -139,73 +140,98 @@ struct SegArgs {
   int S;                     // chunks
 };
 
-// Waves per workgroup: the output kernel runs eight (16 value columns each,
-// two waves per SIMD), the local end-state kernel four (32 columns each: half
-// the transposed K reads per MFMA, and its state fits in VGPRs).
-template <bool LOCAL> struct SegWaves { static constexpr int value = LOCAL ? 4 : 8; };
+constexpr int kOutWaves = 8;   // output kernel: 16 value columns per wave, two waves per SIMD
 
-template <int K, bool LOCAL>
-struct SegLds {
+// LDS of the output kernel. The tile's per-key and per-row data and the
+// normaliser operand are double-buffered: waves 0-3 (which finish the state
+// update first) prepare tile tau + 1's copy at the end of tile tau.
+template <int K>
+struct OutLds {
   static constexpr int QP = K + 16;       // sQ row pitch (16-byte operand reads)
   static constexpr int KP = K + 32;       // sK row pitch: 16 dwords mod 64 banks, conflict-free for frag_trk
   static constexpr int VP = kVB + 8;      // sV row pitch (transposed reads)
   static constexpr int OP = kVB + 8;      // sO row pitch
   static constexpr int PP = kTile + 8;    // sP row pitch
   static constexpr int oQ = 0;
-  static constexpr int oK = oQ + (LOCAL ? 0 : kTile * QP * 2);
+  static constexpr int oK = oQ + kTile * QP * 2;
   static constexpr int oV = oK + kTile * KP * 2;
   static constexpr int oO = oV + kTile * VP * 2;
-  static constexpr int oP = oO + (LOCAL ? 0 : kTile * OP * 2);
-  static constexpr int oNb = oP + (LOCAL ? 0 : kTile * PP * 2);   // bf16 [3][K]: n~ hi, lo, zero
-  static constexpr int oW = oNb + (LOCAL ? 0 : 3 * K * 2);        // float [64] key weights
-  static constexpr int oWb = oW + kTile * 4;                      // bf16 [3][64]: weights hi, lo, zero
-  static constexpr int oRow = oWb + 3 * kTile * 2;
-  static constexpr int oDen = oRow + (LOCAL ? 0 : 6 * kTile * 4);
-  static constexpr int bytes = oDen + (LOCAL ? 0 : (4 + SegWaves<LOCAL>::value) * kTile * 4);
+  static constexpr int oP = oO + kTile * OP * 2;
+  // double-buffered tile data, [2] of:
+  static constexpr int nbBytes = 3 * K * 2;          // bf16 [3][K]: n~ hi, lo, zero
+  static constexpr int wBytes = kTile * 4;           // float [64] key weights
+  static constexpr int wbBytes = 3 * kTile * 2;      // bf16 [3][64]: weights hi, lo, zero
+  static constexpr int rowBytes = 5 * kTile * 4;     // r2, sc, fl, u2 (float), rs (int), [64] each
+  static constexpr int infoBytes = 16;               // tile info: rescale flag (int), factor (float)
+  static constexpr int bufBytes = nbBytes + wBytes + wbBytes + rowBytes + infoBytes;
+  static constexpr int oBuf = oP + kTile * PP * 2;
+  static constexpr int oInv = oBuf + 2 * bufBytes;   // float [64] 1 / denominator of each row
+  static constexpr int oDen = oInv + kTile * 4;      // float [4][64] row sums of P per key group
+  static constexpr int oDn = oDen + 4 * kTile * 4;   // float [8][64] q . n~ partials per wave
+  static constexpr int oFin = oDn + kOutWaves * kTile * 4;   // double [2]: final m, logD
+  static constexpr int bytes = oFin + 16;
 };
 
-// Wave w owns value columns [16 WY w, 16 WY (w + 1)) of the workgroup's 128
-// and keeps C~^T[k][v] for all k of them in registers: register r of
-// Ct[kx][y] in lane (g, i) is k = state_k0(kx, g) + r, v = 16 (WY w + y) + i. The
-// normaliser n~ is carried as two MFMA columns (lane i = 0: the sum weighted
-// by the bf16 high halves of the key weights, i = 1: by the low halves) in
-// Nacc, for the 16-row tiles kx = KXW w .. KXW w + KXW - 1. The output
-// kernel (eight waves, WY = 1) takes Q K^T in blocks of 16 keys [16 (w & 3),
-// +16) x 32 rows [32 (w >> 2), +32) and forms H^T (value columns as MFMA
-// rows), so that a lane holds four consecutive columns of one output row.
+// Wave w owns value columns [16 w, 16 w + 16) of the workgroup's 128 and
+// keeps C~^T[k][v] for all k of them in registers: register r of Ct[kx] in
+// lane (g, i) is k = state_k0(kx, g) + r, v = 16 w + i. The normaliser n~ is
+// carried as two MFMA columns (lane i = 0: the sum weighted by the bf16 high
+// parts of the key weights, i = 1: by the low parts) in Nacc, for the 16-row
+// tiles kx = KXW w .. KXW w + KXW - 1. Q K^T is taken in blocks of 16 keys
+// [16 (w & 3), +16) x 32 rows [32 (w >> 2), +32); H is formed transposed
+// (value columns as MFMA rows), so that a lane holds four consecutive
+// columns of one output row.
 //
-// RESCALE = false is the variant for chunks whose pending decay never exceeds
-// kMaxDefer (checked up front from the gate scalars alone); it holds no
-// rescaling code. Other chunks take RESCALE = true.
-template <int K, bool LOCAL, bool RESCALE>
-__device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
-  using L = SegLds<K, LOCAL>;
+// The tiles' decays are not applied to the accumulators one by one: the
+// registers hold X with C~ = exp(logD) X, n~ = exp(logD) Xn, new keys enter
+// with weight exp(u_j - Rm - logD_next), and X is rescaled only when logD
+// would fall below -kMaxDefer (or on a zero decay). RESCALE = false is the
+// variant for chunks where that never happens (checked up front from the gate
+// scalars alone); it holds no rescaling code.
+template <int K, bool RESCALE>
+__device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
+  using L = OutLds<K>;
   constexpr int QP = L::QP, KP = L::KP, VP = L::VP, OP = L::OP, PP = L::PP;
   constexpr int KS = K / 32;                                   // 32-deep steps over d_qk
   constexpr int KX = K / 16;                                   // 16-row tiles of C^T along d_qk
-  constexpr int NW = SegWaves<LOCAL>::value;
+  constexpr int NW = kOutWaves;
   constexpr int NT = 64 * NW;                                  // threads
-  constexpr int WY = kVB / 16 / NW;                            // 16-column tiles per wave
   constexpr int KXW = KX >= NW ? KX / NW : 1;                  // normaliser tiles per wave
   constexpr int QV = kTile * K / 8 / NT;                       // 16-byte vectors per thread, 64 x K tile
   constexpr int VV = kTile * kVB / 8 / NT;                     // 16-byte vectors per thread, 64 x 128 tile
-  static_assert(LOCAL || WY == 1, "the output kernel assumes one column tile per wave");
   __bf16* sQ = reinterpret_cast<__bf16*>(smem + L::oQ);
   __bf16* sK = reinterpret_cast<__bf16*>(smem + L::oK);
   __bf16* sV = reinterpret_cast<__bf16*>(smem + L::oV);
   __bf16* sO = reinterpret_cast<__bf16*>(smem + L::oO);
   __bf16* sP = reinterpret_cast<__bf16*>(smem + L::oP);
-  __bf16* snb = reinterpret_cast<__bf16*>(smem + L::oNb);
-  float* s_w = reinterpret_cast<float*>(smem + L::oW);
-  __bf16* swb = reinterpret_cast<__bf16*>(smem + L::oWb);
-  float* s_r2 = reinterpret_cast<float*>(smem + L::oRow);
-  float* s_sc = s_r2 + kTile;
-  float* s_fl = s_sc + kTile;
-  float* s_u2 = s_fl + kTile;
-  int* s_rs = reinterpret_cast<int*>(s_u2 + kTile);
-  float* s_inv = s_u2 + kTile + kTile;                       // [64] 1 / denominator of each row
-  float* s_den = reinterpret_cast<float*>(smem + L::oDen);   // [4][64] row sums of P per key group
-  float* s_dn = s_den + 4 * kTile;                           // [NW][64] q . n~ partials per wave
+  float* s_inv = reinterpret_cast<float*>(smem + L::oInv);
+  float* s_den = reinterpret_cast<float*>(smem + L::oDen);
+  float* s_dn = reinterpret_cast<float*>(smem + L::oDn);
+  double* s_fin = reinterpret_cast<double*>(smem + L::oFin);
+  // views of one half of the double-buffered tile data
+  struct TileBuf {
+    __bf16* nb;
+    float* w;
+    __bf16* wb;
+    float *r2, *sc, *fl, *u2;
+    int* rs;
+    int* info;
+  };
+  auto tile_buf = [&](int b) {
+    char* base = smem + L::oBuf + b * L::bufBytes;
+    TileBuf t;
+    t.nb = reinterpret_cast<__bf16*>(base);
+    t.w = reinterpret_cast<float*>(base + L::nbBytes);
+    t.wb = reinterpret_cast<__bf16*>(base + L::nbBytes + L::wBytes);
+    float* row = reinterpret_cast<float*>(base + L::nbBytes + L::wBytes + L::wbBytes);
+    t.r2 = row;
+    t.sc = row + kTile;
+    t.fl = row + 2 * kTile;
+    t.u2 = row + 3 * kTile;
+    t.rs = reinterpret_cast<int*>(row + 4 * kTile);
+    t.info = reinterpret_cast<int*>(row + 5 * kTile);
+    return t;
+  };
 
   const int64_t BH = a.BH, T = a.T, V = a.V, Nt = a.Nt;
   const int nvb = (int)(V / kVB);
@@ -225,51 +251,40 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
   const int64_t nseg1 = a.S - 1;
 
   // ---------------- carried state
-  f32x4 Ct[KX][WY];
+  f32x4 Ct[KX];
   f32x4 Nacc[KXW];
-  double m_prev;
+  double m_start;
   bool has_state;
   const float* Cinit = nullptr;
   const float* ninit = nullptr;
-  if constexpr (LOCAL) {
-    m_prev = -INFINITY;   // empty: the local state starts from nothing
-    has_state = false;
-  } else if (seg == 0) {
+  if (seg == 0) {
     Cinit = a.C0 ? a.C0 + bh * V * K : nullptr;
     ninit = a.C0 ? a.n0 + bh * K : nullptr;
-    m_prev = a.C0 ? (double)a.m0[bh] : 0.0;
+    m_start = a.C0 ? (double)a.m0[bh] : 0.0;
     has_state = a.C0 != nullptr;
   } else {
     const int64_t sidx = bh * nseg1 + seg - 1;
     Cinit = a.Cseg + sidx * V * K;
     ninit = a.nseg + sidx * K;
-    m_prev = a.mstart[sidx];
+    m_start = a.mstart[sidx];
     has_state = true;
   }
 #pragma unroll
   for (int kx = 0; kx < KX; ++kx)
-#pragma unroll
-    for (int y = 0; y < WY; ++y)
-      Ct[kx][y] = Cinit ? *reinterpret_cast<const f32x4*>(Cinit + (vcol0 + 16 * (WY * w + y) + i) * K + state_k0(kx, g))
-                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    Ct[kx] = Cinit ? *reinterpret_cast<const f32x4*>(Cinit + (vcol0 + 16 * w + i) * K + state_k0(kx, g))
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int x = 0; x < KXW; ++x) {
     const int kx = w * KXW + x;
     Nacc[x] = (ninit && i == 0 && kx < KX) ? *reinterpret_cast<const f32x4*>(ninit + state_k0(kx, g))
                                            : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // zero rows of the two-column normaliser operands
-  if (tid < kTile) swb[2 * kTile + tid] = (__bf16)0.f;
-  if constexpr (!LOCAL) {
-    for (int k = tid; k < K; k += NT) snb[2 * K + k] = (__bf16)0.f;
+  // zero rows of the two-column normaliser operands, both halves
+  for (int b = 0; b < 2; ++b) {
+    const TileBuf tb = tile_buf(b);
+    if (tid < kTile) tb.wb[2 * kTile + tid] = (__bf16)0.f;
+    for (int k = tid; k < K; k += NT) tb.nb[2 * K + k] = (__bf16)0.f;
   }
-  // The tiles' decays are not applied to the accumulators one by one: the
-  // registers hold X with C~ = exp(logD) X, n~ = exp(logD) Xn, new keys enter
-  // with weight exp(u_j - Rm - logD), and X is rescaled only when logD would
-  // fall below -kMaxDefer (or on a zero decay).
-  double logD = 0.0;
-  double Gsum = 0.0;
-  bool reset_seen = false;
 
   // ---------------- next-tile registers; loads are unconditional (rows clamped
   // into the tile) so that no branch forces the load counter to drain
@@ -296,9 +311,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
       for (int e = 0; e < QV; ++e) {
         const unsigned it = tid + NT * e;
         const unsigned off = min(it / (K / 8), last) * K + 8 * (it % (K / 8));
-        if constexpr (!LOCAL) {
-          if (parts & 1) pq[e] = *reinterpret_cast<const bf16x8*>(qt + off);
-        }
+        if (parts & 1) pq[e] = *reinterpret_cast<const bf16x8*>(qt + off);
         if (parts & 2) pk[e] = *reinterpret_cast<const bf16x8*>(kt + off);
       }
     }
@@ -310,38 +323,120 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
         const unsigned it = tid + NT * e;
         const unsigned off = min(it / (kVB / 8), last) * (unsigned)V + 8 * (it % (kVB / 8));
         pv[e] = *reinterpret_cast<const bf16x8*>(vt + off);
-        if constexpr (!LOCAL) po[e] = *reinterpret_cast<const bf16x8*>(ot + off);
+        po[e] = *reinterpret_cast<const bf16x8*>(ot + off);
       }
     }
-    if (!(parts & 8)) return;
+    if (!(parts & 8) || w >= 4) return;   // the gate data feed the tile preparation of waves 0-3
     const unsigned j = min(lane, last);
     r_u = (a.gb.u + tok0)[j];
-    if constexpr (!LOCAL) {
-      r_mp = (a.gb.mp + tok0)[j];
-      r_b = (a.gb.b + tok0)[j];
-      r_rs = (a.gb.rs + tok0)[j];
-      r_mp0 = a.gb.mp[tok0];
-      r_rs0 = a.gb.rs[tok0];
-    }
+    r_mp = (a.gb.mp + tok0)[j];
+    r_b = (a.gb.b + tok0)[j];
+    r_rs = (a.gb.rs + tok0)[j];
+    r_mp0 = a.gb.mp[tok0];
+    r_rs0 = a.gb.rs[tok0];
     t_g = a.gb.g[bh * Nt + tau];
     t_U = a.gb.U[bh * Nt + tau];
     t_R = a.gb.R[bh * Nt + tau];
   };
 
+  // n~ of the next tile as bf16 hi + lo in the fragment order of sQ (every
+  // wave its own tiles)
+  auto put_n = [&](const TileBuf& tb) {
+    const Lanes ln = fresh_lanes();
+#pragma unroll
+    for (int x = 0; x < KXW; ++x) {
+      const int kx = w * KXW + x;
+      if (kx < KX) {
+        bf16x4 hi4, lo4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float nr = sum_xor1(Nacc[x][r]);
+          const __bf16 hi = (__bf16)nr;
+          hi4[r] = hi;
+          lo4[r] = (__bf16)(nr - (float)hi);
+        }
+        const int pos = state_k0(kx, ln.g);
+        if (ln.i == 0) {
+          *reinterpret_cast<bf16x4*>(&tb.nb[pos]) = hi4;
+          *reinterpret_cast<bf16x4*>(&tb.nb[K + pos]) = lo4;
+        }
+      }
+    }
+  };
+
+  // Tile scalars and the per-key / per-row data of tile tau (waves 0-3, from
+  // the gate registers of tau and the stabiliser chain m, logD at its start):
+  // Rm = max(m if no zero forget gate in the tile, U), the decay exp(m - Rm),
+  // key weights exp(u_j - Rm - logD_next), and the row stabiliser r_t =
+  // max(m if no zero gate at or before t, prefix max of u).
+  auto prep = [&](int64_t tau, const TileBuf& tb, double m, double logD, bool state) -> void {
+    const int Lc = (int)min((int64_t)kTile, T - tau * kTile);
+    double Rm = fmax(t_R >= 0 ? -INFINITY : m, t_U);
+    if (Rm == -INFINITY) Rm = 0.0;
+    const double ld = (t_R >= 0 || m == -INFINITY) ? -INFINITY : m - Rm;
+    const bool rescale = logD + ld < -kMaxDefer;
+    const double logD_next = rescale ? 0.0 : logD + ld;
+    const int j = fresh_lanes().lane;
+    if (w == 0) {
+      const float wj = (j >= t_R && j < Lc && t_U != -INFINITY) ? expf((float)(r_u - Rm - logD_next)) : 0.f;
+      tb.w[j] = wj;
+      const __bf16 whi = (__bf16)wj;
+      tb.wb[j] = whi;
+      tb.wb[kTile + j] = (__bf16)(wj - (float)whi);
+      if (j == 0) {
+        tb.info[0] = rescale ? 1 : 0;
+        tb.info[1] = __builtin_bit_cast(int, rescale ? (float)exp(logD + ld) : 1.f);
+      }
+    } else {
+      const bool carry0 = state && r_rs0 < 0;
+      double ref = fmax(carry0 ? m : -INFINITY, r_mp0);
+      if (ref == -INFINITY) ref = 0.0;
+      const bool valid = j < Lc;
+      const bool carry = state && r_rs < 0;
+      double r = fmax(carry ? m : -INFINITY, r_mp);
+      if (r == -INFINITY) r = 0.0;
+      if (w == 1) {
+        tb.r2[j] = valid ? (float)((r - ref) * (double)kLog2eF) : 0.f;
+        tb.u2[j] = valid ? (float)((r_u - ref) * (double)kLog2eF) : -INFINITY;
+        tb.rs[j] = r_rs;
+      } else if (w == 2) {
+        tb.sc[j] = (valid && carry) ? expf((float)(m - r + logD)) : 0.f;
+      } else {
+        tb.fl[j] = valid ? expf((float)(-(r_b + r))) : 1.f;
+      }
+    }
+  };
+  // the chain of the stabiliser over the tiles, carried by waves 0-3
+  double m_chain = m_start, logD_chain = 0.0;
+  auto advance = [&](double& m, double& logD) {
+    double Rm = fmax(t_R >= 0 ? -INFINITY : m, t_U);
+    if (Rm == -INFINITY) Rm = 0.0;
+    const double ld = (t_R >= 0 || m == -INFINITY) ? -INFINITY : m - Rm;
+    logD = logD + ld < -kMaxDefer ? 0.0 : logD + ld;
+    m = t_g + Rm;
+  };
+
   issue(tile0, 15);
+  if (w < 4) {
+    prep(tile0, tile_buf(0), m_chain, logD_chain, has_state);
+    advance(m_chain, logD_chain);
+  }
+  put_n(tile_buf(0));
   for (int64_t tau = tile0; tau < tile1; ++tau) {
     const int64_t t0 = tau * kTile;
     const int Lc = (int)min((int64_t)kTile, T - t0);
     const int64_t tok0 = bh * T + t0;
+    const int buf = (int)((tau - tile0) & 1);
+    const TileBuf tb = tile_buf(buf);
 
-    __syncthreads();   // the previous tile's LDS reads are done
+    __syncthreads();   // the previous tile's LDS reads are done; tile data of tau prepared
     // ---------------- stage tile tau
     const Lanes ls = fresh_lanes();
 #pragma unroll
     for (int e = 0; e < QV; ++e) {
       const int it = ls.tid + NT * e;
       const int row = it / (K / 8), cv = it % (K / 8);
-      if constexpr (!LOCAL) *reinterpret_cast<bf16x8*>(&sQ[row * QP + 8 * cv]) = pq[e];
+      *reinterpret_cast<bf16x8*>(&sQ[row * QP + 8 * cv]) = pq[e];
       *reinterpret_cast<bf16x8*>(&sK[row * KP + 8 * cv]) = pk[e];
     }
 #pragma unroll
@@ -349,222 +444,146 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
       const int it = ls.tid + NT * e;
       const int row = it / (kVB / 8), cv = it % (kVB / 8);
       *reinterpret_cast<bf16x8*>(&sV[row * VP + 8 * cv]) = pv[e];
-      if constexpr (!LOCAL) *reinterpret_cast<bf16x8*>(&sO[row * OP + 8 * cv]) = po[e];
-    }
-    // tile scalars of the state update: Rm = max(m_prev, U) (U alone after a
-    // zero forget gate), decay exp(m_prev - Rm), key weights exp(u_j - Rm)
-    double Rm = fmax(t_R >= 0 ? -INFINITY : m_prev, t_U);
-    if constexpr (!LOCAL) {
-      if (Rm == -INFINITY) Rm = 0.0;
-    }
-    const bool live = Rm != -INFINITY;
-    const double ld = (t_R >= 0 || m_prev == -INFINITY || !live) ? -INFINITY : m_prev - Rm;
-    const double m_next = live ? t_g + Rm : -INFINITY;
-    // deferred decay after this tile: keep logD + ld, or rescale X by it (a
-    // scalar, so that the rescale below is a branch)
-    const bool rescale = __builtin_amdgcn_readfirstlane(logD + ld < -kMaxDefer ? 1 : 0) != 0;
-    const double logD_next = rescale ? 0.0 : logD + ld;
-    // Per-key and per-row tile data, lane j = token j of the tile; the
-    // quantities are split over the first waves (every wave holds the
-    // tile's gate data).
-    if (w == 0) {
-      const int j = ls.lane;
-      const float wj = (j >= t_R && j < Lc && t_U != -INFINITY && live) ? expf((float)(r_u - Rm - logD_next)) : 0.f;
-      s_w[j] = wj;
-      const __bf16 whi = (__bf16)wj;
-      swb[j] = whi;
-      swb[kTile + j] = (__bf16)(wj - (float)whi);
-    }
-    if constexpr (!LOCAL) {
-      if (w >= 1 && w <= 3) {
-        // row stabiliser r_t = max(m_prev if no zero gate at or before t, prefix max of u)
-        const int j = ls.lane;
-        const bool carry0 = has_state && r_rs0 < 0;
-        double ref = fmax(carry0 ? m_prev : -INFINITY, r_mp0);
-        if (ref == -INFINITY) ref = 0.0;
-        const bool valid = j < Lc;
-        const bool carry = has_state && r_rs < 0;
-        double r = fmax(carry ? m_prev : -INFINITY, r_mp);
-        if (r == -INFINITY) r = 0.0;
-        if (w == 1) {
-          s_r2[j] = valid ? (float)((r - ref) * (double)kLog2eF) : 0.f;
-          s_u2[j] = valid ? (float)((r_u - ref) * (double)kLog2eF) : -INFINITY;
-          s_rs[j] = r_rs;
-        } else if (w == 2) {
-          s_sc[j] = (valid && carry) ? expf((float)(m_prev - r + logD)) : 0.f;
-        } else {
-          s_fl[j] = valid ? expf((float)(-(r_b + r))) : 1.f;
-        }
-      }
-    }
-    if constexpr (!LOCAL) {
-      // n~ of this tile as bf16 hi + lo in the fragment order of sQ
-#pragma unroll
-      for (int x = 0; x < KXW; ++x) {
-        const int kx = w * KXW + x;
-        if (kx < KX) {
-          bf16x4 hi4, lo4;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float nr = sum_xor1(Nacc[x][r]);
-            const __bf16 hi = (__bf16)nr;
-            hi4[r] = hi;
-            lo4[r] = (__bf16)(nr - (float)hi);
-          }
-          const int pos = state_k0(kx, ls.g);
-          if (ls.i == 0) {
-            *reinterpret_cast<bf16x4*>(&snb[pos]) = hi4;
-            *reinterpret_cast<bf16x4*>(&snb[K + pos]) = lo4;
-          }
-        }
-      }
-    }
-    if constexpr (LOCAL) {
-      Gsum += t_g;
-      reset_seen = reset_seen || t_R >= 0;
+      *reinterpret_cast<bf16x8*>(&sO[row * OP + 8 * cv]) = po[e];
     }
     __syncthreads();   // tile tau staged
     const bool more = tau + 1 < tile1;
-    if (more) issue(tau + 1, LOCAL ? 2 : 1);
+    if (more) issue(tau + 1, 1);
 
-    if constexpr (!LOCAL) {
-      // ---------------- Q K^T (16 keys x 32 rows) and (Q C~^T)^T (16 columns x 64 rows)
-      f32x4 sacc[2], acc[4];
-      sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // ---------------- Q K^T (16 keys x 32 rows) and (Q C~^T)^T (16 columns x 64 rows)
+    f32x4 sacc[2], acc[4];
+    sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int z = 0; z < 4; ++z) acc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const Lanes l1 = fresh_lanes();
-      unroll<KS>([&](auto s_c) {
-        constexpr int s = decltype(s_c)::value;
-        bf16x8 fa[4];
+    for (int z = 0; z < 4; ++z) acc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const Lanes l1 = fresh_lanes();
+    unroll<KS>([&](auto s_c) {
+      constexpr int s = decltype(s_c)::value;
+      bf16x8 fa[4];
 #pragma unroll
-        for (int z = 0; z < 4; ++z) fa[z] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * z + l1.i) * QP + 32 * s + 8 * l1.g]);
-        const bf16x8 fk = *reinterpret_cast<const bf16x8*>(&sK[(16 * kg + l1.i) * KP + 32 * s + 8 * l1.g]);
-        if (zh == 0) {   // scalar branch: a register array takes static indices only
-          sacc[0] = mma(fk, fa[0], sacc[0]);
-          sacc[1] = mma(fk, fa[1], sacc[1]);
-        } else {
-          sacc[0] = mma(fk, fa[2], sacc[0]);
-          sacc[1] = mma(fk, fa[3], sacc[1]);
-        }
-        const bf16x8 Bc = pack_bf16(Ct[2 * s][0], Ct[2 * s + 1][0]);
+      for (int z = 0; z < 4; ++z) fa[z] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * z + l1.i) * QP + 32 * s + 8 * l1.g]);
+      const bf16x8 fk = *reinterpret_cast<const bf16x8*>(&sK[(16 * kg + l1.i) * KP + 32 * s + 8 * l1.g]);
+      if (zh == 0) {   // scalar branch: a register array takes static indices only
+        sacc[0] = mma(fk, fa[0], sacc[0]);
+        sacc[1] = mma(fk, fa[1], sacc[1]);
+      } else {
+        sacc[0] = mma(fk, fa[2], sacc[0]);
+        sacc[1] = mma(fk, fa[3], sacc[1]);
+      }
+      const bf16x8 Bc = pack_bf16(Ct[2 * s], Ct[2 * s + 1]);
 #pragma unroll
-        for (int z = 0; z < 4; ++z) acc[z] = mma(Bc, fa[z], acc[z]);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      // ---------------- q . n~: wave w takes the 32-deep step s = w of d_qk
-      {
-        const Lanes ln = fresh_lanes();
-        const int i = ln.i, g = ln.g;
-        f32x4 dacc[4];
+      for (int z = 0; z < 4; ++z) acc[z] = mma(Bc, fa[z], acc[z]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // ---------------- q . n~: wave w takes the 32-deep step s = w of d_qk
+    {
+      const Lanes ln = fresh_lanes();
+      f32x4 dacc[4];
 #pragma unroll
-        for (int z = 0; z < 4; ++z) dacc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (w < KS) {
-          const bf16x8 Bn = *reinterpret_cast<const bf16x8*>(&snb[min(i, 2) * K + 32 * w + 8 * g]);
-#pragma unroll
-          for (int z = 0; z < 4; ++z) {
-            const bf16x8 fa = *reinterpret_cast<const bf16x8*>(&sQ[(16 * z + i) * QP + 32 * w + 8 * g]);
-            dacc[z] = mma(fa, Bn, dacc[z]);
-          }
-        }
+      for (int z = 0; z < 4; ++z) dacc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (w < KS) {
+        const bf16x8 Bn = *reinterpret_cast<const bf16x8*>(&tb.nb[min(ln.i, 2) * K + 32 * w + 8 * ln.g]);
 #pragma unroll
         for (int z = 0; z < 4; ++z) {
-          f32x4 d;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) d[r] = sum_xor1(dacc[z][r]);
-          if (i == 0) *reinterpret_cast<f32x4*>(&s_dn[w * kTile + 16 * z + 4 * g]) = d;
+          const bf16x8 fa = *reinterpret_cast<const bf16x8*>(&sQ[(16 * z + ln.i) * QP + 32 * w + 8 * ln.g]);
+          dacc[z] = mma(fa, Bn, dacc[z]);
         }
       }
-      if (more) issue(tau + 1, 2);
-      // the carried-state term enters row t with weight exp(m_prev - r_t + logD);
-      // acc[z] register r in lane (g, i) is H^T[v = 16 w + 4 g + r][t = 16 z + i]
-      const Lanes lp = fresh_lanes();
 #pragma unroll
-      for (int z = 0; z < 4; ++z) acc[z] *= s_sc[16 * z + lp.i];
-      // ---------------- P = S o D: lane holds S^T[j = 16 kg + 4 g + r][t = 16 z + i]
-      const int i = lp.i, g = lp.g;
-      const f32x4 u2 = *reinterpret_cast<const f32x4*>(&s_u2[16 * kg + 4 * g]);
+      for (int z = 0; z < 4; ++z) {
+        f32x4 d;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) d[r] = sum_xor1(dacc[z][r]);
+        if (ln.i == 0) *reinterpret_cast<f32x4*>(&s_dn[w * kTile + 16 * z + 4 * ln.g]) = d;
+      }
+    }
+    if (more) issue(tau + 1, 2);
+    // the carried-state term enters row t with weight exp(m_prev - r_t + logD);
+    // acc[z] register r in lane (g, i) is H^T[v = 16 w + 4 g + r][t = 16 z + i]
+    const Lanes lp = fresh_lanes();
+#pragma unroll
+    for (int z = 0; z < 4; ++z) acc[z] *= tb.sc[16 * z + lp.i];
+    // ---------------- P = S o D: lane holds S^T[j = 16 kg + 4 g + r][t = 16 z + i]
+    {
+      const f32x4 u2 = *reinterpret_cast<const f32x4*>(&tb.u2[16 * kg + 4 * lp.g]);
 #pragma unroll
       for (int zz = 0; zz < 2; ++zz) {
-        const int tl = 16 * (2 * zh + zz) + i;
-        const float r2 = s_r2[tl];
-        const int rs = s_rs[tl];
+        const int tl = 16 * (2 * zh + zz) + lp.i;
+        const float r2 = tb.r2[tl];
+        const int rs = tb.rs[tl];
         bf16x4 pk4;
         float psum = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int jk = 16 * kg + 4 * g + r;
+          const int jk = 16 * kg + 4 * lp.g + r;
           const bool keep = (tl < Lc) && (jk <= tl) && (jk >= rs);
           const float p = keep ? sacc[zz][r] * __builtin_amdgcn_exp2f(u2[r] - r2) : 0.f;
           psum += p;
           pk4[r] = (__bf16)p;
         }
-        *reinterpret_cast<bf16x4*>(&sP[tl * PP + 16 * kg + 4 * g]) = pk4;
+        *reinterpret_cast<bf16x4*>(&sP[tl * PP + 16 * kg + 4 * lp.g]) = pk4;
         psum = sum_rows(psum);
-        if (g == 0) s_den[kg * kTile + tl] = psum;
+        if (lp.g == 0) s_den[kg * kTile + tl] = psum;
       }
-      __syncthreads();   // sP, s_den, s_dn complete
-      if (w == 0) {   // 1 / max(|n~^T q|, floor) of row t = lane
-        const int t = fresh_lanes().lane;
-        float den = s_den[t] + s_den[kTile + t] + s_den[2 * kTile + t] + s_den[3 * kTile + t];
-        float dn = 0.f;
+    }
+    __syncthreads();   // sP, s_den, s_dn complete
+    if (w == 0) {   // 1 / max(|n~^T q|, floor) of row t = lane
+      const int t = fresh_lanes().lane;
+      const float den = s_den[t] + s_den[kTile + t] + s_den[2 * kTile + t] + s_den[3 * kTile + t];
+      float dn = 0.f;
 #pragma unroll
-        for (int q = 0; q < NW; ++q) dn += s_dn[q * kTile + t];
-        const float d = den + s_sc[t] * dn;
-        s_inv[t] = __builtin_amdgcn_rcpf(fmaxf(fmaxf(fabsf(d), s_fl[t]), FLT_MIN));
+      for (int q = 0; q < NW; ++q) dn += s_dn[q * kTile + t];
+      const float d = den + tb.sc[t] * dn;
+      s_inv[t] = __builtin_amdgcn_rcpf(fmaxf(fmaxf(fabsf(d), tb.fl[t]), FLT_MIN));
+    }
+    // ---------------- (P V)^T
+    const Lanes lv = fresh_lanes();
+#pragma unroll
+    for (int jj = 0; jj < kTile; jj += 32) {
+      bf16x8 B[4];
+#pragma unroll
+      for (int z = 0; z < 4; ++z) B[z] = *reinterpret_cast<const bf16x8*>(&sP[(16 * z + lv.i) * PP + jj + 8 * lv.g]);
+      const bf16x8 A = frag_tr(sV, VP, jj, 16 * w, lv.lane);
+#pragma unroll
+      for (int z = 0; z < 4; ++z) acc[z] = mma(A, B[z], acc[z]);
+    }
+    if (more) issue(tau + 1, 4);
+    __syncthreads();   // s_inv complete
+    // ---------------- normaliser, output gate; h staged in place of O, four
+    // consecutive columns of one row per lane
+    const Lanes le = fresh_lanes();
+#pragma unroll
+    for (int z = 0; z < 4; ++z) {
+      const int t = 16 * z + le.i;
+      const float inv = s_inv[t];
+      __bf16* p = &sO[t * OP + 16 * w + 4 * le.g];
+      const bf16x4 o4 = *reinterpret_cast<const bf16x4*>(p);
+      bf16x4 h4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float og = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2eF * (float)o4[r]));
+        h4[r] = (__bf16)(og * acc[z][r] * inv);
       }
-      // ---------------- (P V)^T
-      const Lanes lv = fresh_lanes();
+      *reinterpret_cast<bf16x4*>(p) = h4;
+    }
+    if (more) issue(tau + 1, 8);
+    __syncthreads();   // h tile complete
+    const Lanes lh = fresh_lanes();
+    __bf16* ht = a.h + tok0 * V + vcol0;
 #pragma unroll
-      for (int jj = 0; jj < kTile; jj += 32) {
-        bf16x8 B[4];
-#pragma unroll
-        for (int z = 0; z < 4; ++z) B[z] = *reinterpret_cast<const bf16x8*>(&sP[(16 * z + lv.i) * PP + jj + 8 * lv.g]);
-        const bf16x8 A = frag_tr(sV, VP, jj, 16 * w, lv.lane);
-#pragma unroll
-        for (int z = 0; z < 4; ++z) acc[z] = mma(A, B[z], acc[z]);
-      }
-      if (more) issue(tau + 1, 4);
-      __syncthreads();   // s_inv complete
-      // ---------------- normaliser, output gate; h staged in place of O, four
-      // consecutive columns of one row per lane
-      const Lanes le = fresh_lanes();
-#pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        const int t = 16 * z + le.i;
-        const float inv = s_inv[t];
-        __bf16* p = &sO[t * OP + 16 * w + 4 * le.g];
-        const bf16x4 o4 = *reinterpret_cast<const bf16x4*>(p);
-        bf16x4 h4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float og = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2eF * (float)o4[r]));
-          h4[r] = (__bf16)(og * acc[z][r] * inv);
-        }
-        *reinterpret_cast<bf16x4*>(p) = h4;
-      }
-      if (more) issue(tau + 1, 8);
-      __syncthreads();   // h tile complete
-      const Lanes lh = fresh_lanes();
-      __bf16* ht = a.h + tok0 * V + vcol0;
-#pragma unroll
-      for (int e = 0; e < VV; ++e) {
-        const unsigned it = (unsigned)lh.tid + NT * e;
-        const unsigned row = it / (kVB / 8), cv = it % (kVB / 8);
-        if (row < (unsigned)Lc)
-          *reinterpret_cast<bf16x8*>(ht + row * (unsigned)V + 8 * cv) =
-              *reinterpret_cast<const bf16x8*>(&sO[row * OP + 8 * cv]);
-      }
+    for (int e = 0; e < VV; ++e) {
+      const unsigned it = (unsigned)lh.tid + NT * e;
+      const unsigned row = it / (kVB / 8), cv = it % (kVB / 8);
+      if (row < (unsigned)Lc)
+        *reinterpret_cast<bf16x8*>(ht + row * (unsigned)V + 8 * cv) =
+            *reinterpret_cast<const bf16x8*>(&sO[row * OP + 8 * cv]);
     }
 
     // ---------------- state update: C~ <- decay C~ + K^T diag(w) V, n~ likewise
     if constexpr (RESCALE) {
-      if (rescale) {   // uniform over the workgroup
-        const float f = (float)exp(logD + ld);
+      if (__builtin_amdgcn_readfirstlane(tb.info[0])) {   // uniform over the workgroup
+        const float f = __builtin_bit_cast(float, tb.info[1]);
 #pragma unroll
-        for (int kx = 0; kx < KX; ++kx)
-#pragma unroll
-          for (int y = 0; y < WY; ++y) Ct[kx][y] *= f;
+        for (int kx = 0; kx < KX; ++kx) Ct[kx] *= f;
 #pragma unroll
         for (int x = 0; x < KXW; ++x) Nacc[x] *= f;
       }
@@ -572,22 +591,18 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
 #pragma unroll
     for (int ts = 0; ts < kTile; ts += 32) {
       const Lanes lu = fresh_lanes();
-      const f32x4 wa = *reinterpret_cast<const f32x4*>(&s_w[ts + 8 * lu.g]);
-      const f32x4 wb = *reinterpret_cast<const f32x4*>(&s_w[ts + 8 * lu.g + 4]);
-      bf16x8 Bv[WY];
+      const f32x4 wa = *reinterpret_cast<const f32x4*>(&tb.w[ts + 8 * lu.g]);
+      const f32x4 wb = *reinterpret_cast<const f32x4*>(&tb.w[ts + 8 * lu.g + 4]);
+      bf16x8 Bv;
+      {
+        const bf16x8 raw = frag_tr(sV, VP, ts, 16 * w, lu.lane);
 #pragma unroll
-      for (int y = 0; y < WY; ++y) {
-        const bf16x8 raw = frag_tr(sV, VP, ts, 16 * (WY * w + y), lu.lane);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Bv[y][e] = (__bf16)((float)raw[e] * (e < 4 ? wa[e] : wb[e - 4]));
+        for (int e = 0; e < 8; ++e) Bv[e] = (__bf16)((float)raw[e] * (e < 4 ? wa[e] : wb[e - 4]));
       }
-      const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&swb[min(lu.i, 2) * kTile + ts + 8 * lu.g]);
-      if constexpr (LOCAL) {
-        if (ts == 32 && more) issue(tau + 1, 12);   // v and gate data of the next tile
-      }
+      const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&tb.wb[min(lu.i, 2) * kTile + ts + 8 * lu.g]);
       // transposed K fragments through a ring of kRing registers: the read of
       // tile kx + kRing - 1 is issued before the MFMAs of tile kx
-      constexpr int kRing = LOCAL ? RING_L : 4;
+      constexpr int kRing = 4;
       bf16x8 Ak[kRing];
       unroll<kRing - 1>([&](auto p_c) {
         constexpr int p = decltype(p_c)::value;
@@ -596,9 +611,7 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
       unroll<KX>([&](auto kx_c) {
         constexpr int kx = decltype(kx_c)::value;
         if constexpr (kx + kRing - 1 < KX) Ak[(kx + kRing - 1) % kRing] = frag_trk(sK, KP, ts, kx + kRing - 1, lu.lane);
-
-#pragma unroll
-        for (int y = 0; y < WY; ++y) Ct[kx][y] = mma(Ak[kx % kRing], Bv[y], Ct[kx][y]);
+        Ct[kx] = mma(Ak[kx % kRing], Bv, Ct[kx]);
         __builtin_amdgcn_sched_barrier(0);
       });
       // n~ tiles of this wave: their K fragments are read again rather than
@@ -609,43 +622,43 @@ __device__ __forceinline__ void seg_body(const SegArgs& a, char* smem) {
           Nacc[x] = mma(frag_trk(sK, KP, ts, min(w * KXW + x, KX - 1), lu.lane), Bw, Nacc[x]);
       }
     }
-    m_prev = m_next;
-    logD = logD_next;
-    has_state = true;
-  }
-  const float fD = (float)exp(logD);
-
-  // ---------------- end state of the chunk
-  float* Cdst = nullptr;
-  float* ndst = nullptr;
-  if constexpr (LOCAL) {
-    const int64_t sidx = bh * nseg1 + seg;
-    Cdst = a.Cseg + sidx * V * K;
-    ndst = vb == 0 ? a.nseg + sidx * K : nullptr;
-    if (vb == 0 && tid == 0) {
-      a.mloc[sidx] = m_prev;
-      a.Gseg[sidx] = reset_seen ? -INFINITY : Gsum;
+    // ---------------- the next tile's data into the other half (its readers
+    // start after the next top barrier; this half's last readers were in tile
+    // tau - 1)
+    if (more) {
+      const TileBuf nb = tile_buf(buf ^ 1);
+      put_n(nb);
+      if (w < 4) {
+        prep(tau + 1, nb, m_chain, logD_chain, true);
+        advance(m_chain, logD_chain);
+      }
     }
-  } else if (seg == a.S - 1 && a.C_out) {
-    Cdst = a.C_out + bh * V * K;
-    ndst = vb == 0 ? a.n_out + bh * K : nullptr;
-    if (vb == 0 && tid == 0) a.m_out[bh] = (float)m_prev;
   }
-  if (Cdst) {
+  if (w == 0 && lane == 0) {
+    s_fin[0] = m_chain;
+    s_fin[1] = logD_chain;
+  }
+  __syncthreads();   // final stabiliser chain published
+  const double m_fin = s_fin[0], logD_fin = s_fin[1];
+  const float fD = (float)exp(logD_fin);
+
+  // ---------------- final state of the sequence
+  if (seg == a.S - 1 && a.C_out) {
+    float* Cdst = a.C_out + bh * V * K;
 #pragma unroll
     for (int kx = 0; kx < KX; ++kx)
+      *reinterpret_cast<f32x4*>(Cdst + (vcol0 + 16 * w + i) * K + state_k0(kx, g)) = fD * Ct[kx];
+    if (vb == 0) {
+      float* ndst = a.n_out + bh * K;
 #pragma unroll
-      for (int y = 0; y < WY; ++y)
-        *reinterpret_cast<f32x4*>(Cdst + (vcol0 + 16 * (WY * w + y) + i) * K + state_k0(kx, g)) = fD * Ct[kx][y];
-  }
-  if (ndst) {
+      for (int x = 0; x < KXW; ++x) {
+        const int kx = w * KXW + x;
+        f32x4 nv;
 #pragma unroll
-    for (int x = 0; x < KXW; ++x) {
-      const int kx = w * KXW + x;
-      f32x4 nv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) nv[r] = fD * sum_xor1(Nacc[x][r]);
-      if (i == 0 && kx < KX) *reinterpret_cast<f32x4*>(ndst + state_k0(kx, g)) = nv;
+        for (int r = 0; r < 4; ++r) nv[r] = fD * sum_xor1(Nacc[x][r]);
+        if (i == 0 && kx < KX) *reinterpret_cast<f32x4*>(ndst + state_k0(kx, g)) = nv;
+      }
+      if (tid == 0) a.m_out[bh] = (float)m_fin;
     }
   }
 }
@@ -657,13 +670,12 @@ __device__ __forceinline__ double readlane_f64(double x, int lane) {
   return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
 }
 
-// True when some tile of the chunk would need the accumulators rescaled:
-// the pending decay logD + ld falls below -kMaxDefer while the state is not
-// known to be zero. Follows the same float64 steps as the tile loop, from the
-// tile scalars only (lanes load 64 tiles at a time, the scan runs on
-// lane reads); the result is uniform over the workgroup.
-__device__ bool chunk_needs_rescale(const SegArgs& a, int64_t bh, int64_t tile0, int64_t tile1, double m,
-                                    bool zero, bool local) {
+// True when some tile of the chunk would need the output kernel's
+// accumulators rescaled: the pending decay logD + ld falls below -kMaxDefer
+// while the state is not known to be zero. Follows the same float64 steps as
+// the tile loop, from the tile scalars only (lanes load 64 tiles at a time,
+// the scan runs on lane reads); the result is uniform over the workgroup.
+__device__ bool chunk_needs_rescale(const SegArgs& a, int64_t bh, int64_t tile0, int64_t tile1, double m, bool zero) {
   const int lane = threadIdx.x & 63;
   double logD = 0.0;
   for (int64_t base = tile0; base < tile1; base += 64) {
@@ -675,44 +687,41 @@ __device__ bool chunk_needs_rescale(const SegArgs& a, int64_t bh, int64_t tile0,
       const double gj = readlane_f64(gv, j), Uj = readlane_f64(Uv, j);
       const int Rj = __builtin_amdgcn_readlane(Rv, j);
       double Rm = fmax(Rj >= 0 ? -INFINITY : m, Uj);
-      if (!local && Rm == -INFINITY) Rm = 0.0;
-      const bool live = Rm != -INFINITY;
-      const double ld = (Rj >= 0 || m == -INFINITY || !live) ? -INFINITY : m - Rm;
+      if (Rm == -INFINITY) Rm = 0.0;
+      const double ld = (Rj >= 0 || m == -INFINITY) ? -INFINITY : m - Rm;
       if (logD + ld < -kMaxDefer) {
         if (!zero) return true;
         logD = 0.0;
       } else {
         logD += ld;
       }
-      m = live ? gj + Rm : -INFINITY;
-      if (live && Uj != -INFINITY) zero = false;
+      m = gj + Rm;
+      if (Uj != -INFINITY) zero = false;
     }
   }
   return false;
 }
 
-template <int K, bool LOCAL>
-__global__ __launch_bounds__(64 * SegWaves<LOCAL>::value, 1) void seg_kernel(SegArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[SegLds<K, LOCAL>::bytes];
+template <int K>
+__global__ __launch_bounds__(64 * kOutWaves, 1) void out_kernel_fused(SegArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[OutLds<K>::bytes];
   const int64_t bh = blockIdx.x % a.BH;
   const int seg = (int)(blockIdx.x / a.BH / (a.V / kVB));
   const int64_t tile0 = (int64_t)seg * a.TPS;
   const int64_t tile1 = min(tile0 + a.TPS, a.Nt);
-  double m = -INFINITY;
-  bool zero = true;
-  if (!LOCAL) {
-    if (seg == 0) {
-      m = a.C0 ? (double)a.m0[bh] : 0.0;
-      zero = a.C0 == nullptr;
-    } else {
-      m = a.mstart[bh * (a.S - 1) + seg - 1];
-      zero = false;
-    }
+  double m;
+  bool zero;
+  if (seg == 0) {
+    m = a.C0 ? (double)a.m0[bh] : 0.0;
+    zero = a.C0 == nullptr;
+  } else {
+    m = a.mstart[bh * (a.S - 1) + seg - 1];
+    zero = false;
   }
-  if (chunk_needs_rescale(a, bh, tile0, tile1, m, zero, LOCAL))
-    seg_body<K, LOCAL, true>(a, smem);
+  if (chunk_needs_rescale(a, bh, tile0, tile1, m, zero))
+    out_body<K, true>(a, smem);
   else
-    seg_body<K, LOCAL, false>(a, smem);
+    out_body<K, false>(a, smem);
 }
 
 // ------------------------------------------------------------------ chunk-local end states
@@ -1078,7 +1087,7 @@ hipError_t run_seg(const FwdLaunch& f, const GateBuffers& gb, const SegStates& s
     if (e != hipSuccess) return e;
   }
   mark_before(K_OUT, s);
-  hipLaunchKernelGGL((seg_kernel<K, false>), dim3((unsigned)(f.BH * nvb * ss.S)), dim3(64 * SegWaves<false>::value), 0, s, a);
+  hipLaunchKernelGGL((out_kernel_fused<K>), dim3((unsigned)(f.BH * nvb * ss.S)), dim3(64 * kOutWaves), 0, s, a);
   mark_after(K_OUT, s);
   return hipGetLastError();
 }
