@@ -298,7 +298,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   // go out in parts (mask bits: 1 q, 2 k, 4 v and o, 8 gate data) spread
   // over the phases of the current one: a wave that issues all of them at
   // once stalls until the address unit has taken them.
-  auto issue = [&](int64_t tau, int parts) {
+  auto issue = [&](int64_t tau, int parts, unsigned qmask = ~0u) {
     const Lanes ln = fresh_lanes();
     const unsigned tid = (unsigned)ln.tid, lane = (unsigned)ln.lane;
     const int64_t t0 = tau * kTile;
@@ -311,7 +311,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       for (int e = 0; e < QV; ++e) {
         const unsigned it = tid + NT * e;
         const unsigned off = min(it / (K / 8), last) * K + 8 * (it % (K / 8));
-        if (parts & 1) pq[e] = *reinterpret_cast<const bf16x8*>(qt + off);
+        if ((parts & 1) && ((qmask >> e) & 1)) pq[e] = *reinterpret_cast<const bf16x8*>(qt + off);
         if (parts & 2) pk[e] = *reinterpret_cast<const bf16x8*>(kt + off);
       }
     }
@@ -448,7 +448,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     }
     __syncthreads();   // tile tau staged
     const bool more = tau + 1 < tile1;
-    if (more) issue(tau + 1, 1);
+    const int64_t tn = more ? tau + 1 : tau;   // on the last tile the q loads repeat this tile
 
     // ---------------- Q K^T (16 keys x 32 rows) and (Q C~^T)^T (16 columns x 64 rows)
     f32x4 sacc[2], acc[4];
@@ -472,6 +472,8 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       const bf16x8 Bc = pack_bf16(Ct[2 * s], Ct[2 * s + 1]);
 #pragma unroll
       for (int z = 0; z < 4; ++z) acc[z] = mma(Bc, fa[z], acc[z]);
+      // the next tile's q, one 16-byte vector per lane every KS / QV steps
+      if constexpr (s % (KS / QV) == 0) issue(tn, 1, 1u << (s / (KS / QV)));
       __builtin_amdgcn_sched_barrier(0);
     });
     // ---------------- q . n~: wave w takes the 32-deep step s = w of d_qk
