@@ -88,11 +88,14 @@ typedef struct mlstm_fwd_args {
  * chunks; dense matrix products inside a chunk, the state passed between
  * chunks). `chunk` is the number of tokens between stored states: a multiple
  * of 64 in [64, 8192]; T need not be a multiple of it (the last chunk is
- * ragged). Kernels: gate prefix sums, the inter-chunk state pass (carries C~,
- * n~, m across chunks in float32 and stores each chunk's start state), and the
- * intra-chunk output kernel (decay-masked Q K^T, P V and the carried-state
- * term on MFMA). The workspace holds the per-chunk start states (bf16 for
- * MLSTM_BF16, float32 for MLSTM_FP32) and per-token gate prefix sums; its size
+ * ragged). Kernels: gate prefix sums over 64-token tiles; the inter-chunk
+ * state (each chunk's local end state, then their in-order fold into every
+ * chunk's start state, all float32); and the output kernel, which walks each
+ * chunk's tiles from its start state with decay-masked Q K^T, P V, the
+ * carried-state term and the state update on MFMA. (bfloat16 with d_v a
+ * multiple of 128; other shapes run a two-pass variant that stores every
+ * chunk's start state, bf16 for MLSTM_BF16, float32 for MLSTM_FP32.) The
+ * workspace holds those states and the per-token gate prefix sums; its size
  * comes from mlstm_fwd_chunkwise_workspace_size(). Outputs must not overlap
  * inputs, each other or the workspace.
  */
