@@ -450,7 +450,10 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     const bool more = tau + 1 < tile1;
     const int64_t tn = more ? tau + 1 : tau;   // on the last tile the q loads repeat this tile
 
-    // ---------------- Q K^T (16 keys x 32 rows) and (Q C~^T)^T (16 columns x 64 rows)
+    // ---------------- Q K^T (16 keys x 32 rows) and (Q C~^T)^T (16 columns x 64 rows).
+    // Register row group z holds rows 16 zg(z) .. + 15 with zg(z) = (z + 2 zh) & 3,
+    // so that every wave's Q K^T rows are its groups 0 and 1 (no branch on zh).
+    auto zg = [&](int z) { return (z + 2 * zh) & 3; };
     f32x4 sacc[2], acc[4];
     sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -460,15 +463,10 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       constexpr int s = decltype(s_c)::value;
       bf16x8 fa[4];
 #pragma unroll
-      for (int z = 0; z < 4; ++z) fa[z] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * z + l1.i) * QP + 32 * s + 8 * l1.g]);
+      for (int z = 0; z < 4; ++z) fa[z] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * zg(z) + l1.i) * QP + 32 * s + 8 * l1.g]);
       const bf16x8 fk = *reinterpret_cast<const bf16x8*>(&sK[(16 * kg + l1.i) * KP + 32 * s + 8 * l1.g]);
-      if (zh == 0) {   // scalar branch: a register array takes static indices only
-        sacc[0] = mma(fk, fa[0], sacc[0]);
-        sacc[1] = mma(fk, fa[1], sacc[1]);
-      } else {
-        sacc[0] = mma(fk, fa[2], sacc[0]);
-        sacc[1] = mma(fk, fa[3], sacc[1]);
-      }
+      sacc[0] = mma(fk, fa[0], sacc[0]);
+      sacc[1] = mma(fk, fa[1], sacc[1]);
       const bf16x8 Bc = pack_bf16(Ct[2 * s], Ct[2 * s + 1]);
 #pragma unroll
       for (int z = 0; z < 4; ++z) acc[z] = mma(Bc, fa[z], acc[z]);
@@ -500,10 +498,10 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     }
     if (more) issue(tau + 1, 2);
     // the carried-state term enters row t with weight exp(m_prev - r_t + logD);
-    // acc[z] register r in lane (g, i) is H^T[v = 16 w + 4 g + r][t = 16 z + i]
+    // acc[z] register r in lane (g, i) is H^T[v = 16 w + 4 g + r][t = 16 zg(z) + i]
     const Lanes lp = fresh_lanes();
 #pragma unroll
-    for (int z = 0; z < 4; ++z) acc[z] *= tb.sc[16 * z + lp.i];
+    for (int z = 0; z < 4; ++z) acc[z] *= tb.sc[16 * zg(z) + lp.i];
     // ---------------- P = S o D: lane holds S^T[j = 16 kg + 4 g + r][t = 16 z + i]
     {
       const f32x4 u2 = *reinterpret_cast<const f32x4*>(&tb.u2[16 * kg + 4 * lp.g]);
@@ -543,7 +541,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     for (int jj = 0; jj < kTile; jj += 32) {
       bf16x8 B[4];
 #pragma unroll
-      for (int z = 0; z < 4; ++z) B[z] = *reinterpret_cast<const bf16x8*>(&sP[(16 * z + lv.i) * PP + jj + 8 * lv.g]);
+      for (int z = 0; z < 4; ++z) B[z] = *reinterpret_cast<const bf16x8*>(&sP[(16 * zg(z) + lv.i) * PP + jj + 8 * lv.g]);
       const bf16x8 A = frag_tr(sV, VP, jj, 16 * w, lv.lane);
 #pragma unroll
       for (int z = 0; z < 4; ++z) acc[z] = mma(A, B[z], acc[z]);
@@ -555,7 +553,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     const Lanes le = fresh_lanes();
 #pragma unroll
     for (int z = 0; z < 4; ++z) {
-      const int t = 16 * z + le.i;
+      const int t = 16 * zg(z) + le.i;
       const float inv = s_inv[t];
       __bf16* p = &sO[t * OP + 16 * w + 4 * le.g];
       const bf16x4 o4 = *reinterpret_cast<const bf16x4*>(p);
