@@ -39,6 +39,9 @@ typedef __attribute__((address_space(1))) void global_void;
 constexpr int kVB = 128;                     // value columns per workgroup
 constexpr double kMaxDefer = 70.0;           // largest pending log decay kept out of the accumulators
 constexpr float kLog2eF = 1.4426950408889634f;
+constexpr int kWaitLgkm0 = 0xC07F;           // s_waitcnt lgkmcnt(0), other counters untouched
+constexpr int kBufferDword3 = 0x00020000;    // buffer resource word 3 for raw (unformatted) access on gfx9
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 // Transposed operand fragment from a row-major LDS tile X (row pitch P):
 // lane l (i = l%16, g = l/16) receives X[kin0 + 8g + e][n0 + i], e = 0..7.
@@ -97,6 +100,31 @@ __device__ __forceinline__ float sum_rows(float x) {
   return __builtin_bit_cast(float, (unsigned)b[0]) + __builtin_bit_cast(float, (unsigned)b[1]);
 }
 
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+  const unsigned lo = __builtin_amdgcn_readlane((unsigned)u, lane);
+  const unsigned hi = __builtin_amdgcn_readlane((unsigned)(u >> 32), lane);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
+// Workgroup barrier for LDS traffic only: waits for the wave's own LDS
+// operations but, unlike __syncthreads, not for its global memory
+// operations or direct-to-LDS loads in flight (their consumers wait for
+// them explicitly). The empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Raw buffer resource over `bytes` bytes from p: stores beyond the range are
+// dropped and loads beyond it return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kBufferDword3);
+}
+
 struct Lanes {
   int tid, lane, i, g;   // thread, lane, lane % 16, lane / 16
 };
@@ -142,21 +170,69 @@ struct SegArgs {
 
 constexpr int kOutWaves = 8;   // output kernel: 16 value columns per wave, two waves per SIMD
 
-// LDS of the output kernel. The tile's per-key and per-row data and the
-// normaliser operand are double-buffered: waves 0-3 (which finish the state
-// update first) prepare tile tau + 1's copy at the end of tile tau.
+// A 64-row bf16 tile (rows of E elements at a stride of RS elements in global
+// memory; rows past `last` repeat row `last`) is copied into LDS rows of pitch
+// P elements with direct-to-LDS buffer loads. Load n fills the 64 consecutive
+// 16-byte chunks 64 n .. 64 n + 63 of the padded LDS image (chunk c lies in
+// row c / (P / 8); padding chunks repeat the row's last data chunk), so the
+// image takes P / 8 loads, issued in rounds: in round r wave w issues load
+// min(NW r + w, P / 8 - 1) (a wave past the last load repeats it, the same
+// bytes to the same place, so that every wave issues one load per round).
+// The data are in LDS once the issuing wave's load counter has drained.
+template <int P, int NW>
+struct DmaTile {
+  static constexpr int kLoads = P / 8;
+  static constexpr int kRounds = (kLoads + NW - 1) / NW;
+  static __device__ __forceinline__ int load(int w, int r) { return min(NW * r + w, kLoads - 1); }
+};
+// Byte offset in the tile of the chunk that lane `lane` of load n copies.
+template <int E, int P>
+__device__ __forceinline__ unsigned dma_src_off(int n, unsigned lane, unsigned rs, unsigned last) {
+  constexpr unsigned CPR = P / 8;
+  const unsigned c = 64u * (unsigned)n + lane;
+  const unsigned row = min(c / CPR, last), ch = min(c % CPR, (unsigned)(E / 8 - 1));
+  return 2u * (row * rs + 8u * ch);
+}
+
+// Two 8-byte values per lane exchanged between the lanes l and l ^ 16 of a
+// pair of 16-lane rows: afterwards a lane in an even row holds (its own x1,
+// its partner's x1) and a lane in an odd row (its partner's x0, its own x0).
+// Applied again it undoes itself on the same layout, so it serves both to
+// form 16-byte row pieces for stores and to split 16-byte loads.
+__device__ __forceinline__ void swap_rows16(bf16x4& x1, bf16x4& x0) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 a = __builtin_bit_cast(u32x2, x1), b = __builtin_bit_cast(u32x2, x0);
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a[d], b[d], false, false);
+    a[d] = r[0];
+    b[d] = r[1];
+  }
+  x1 = __builtin_bit_cast(bf16x4, a);
+  x0 = __builtin_bit_cast(bf16x4, b);
+}
+
+// LDS of the output kernel. Q, K and V arrive by direct-to-LDS copies issued
+// by the compute waves during the previous tile: K (read in the first and in
+// the last phase of a tile) is double-buffered, Q is refilled once Q K^T and
+// q . n~ are done, V once P V is done (the state update reuses the P V
+// operand fragments). O is read into registers and H written from registers.
+// The tile's per-key and per-row data and the normaliser operand are
+// double-buffered: waves 0-3 (which finish the state update first) prepare
+// tile tau + 1's copy at the end of tile tau.
 template <int K>
 struct OutLds {
-  static constexpr int QP = K + 16;       // sQ row pitch (16-byte operand reads)
+  static constexpr int QP = K + 16;       // sQ row pitch: 8 dwords mod 64 banks, conflict-free 16-byte row reads
   static constexpr int KP = K + 32;       // sK row pitch: 16 dwords mod 64 banks, conflict-free for frag_trk
   static constexpr int VP = kVB + 8;      // sV row pitch (transposed reads)
-  static constexpr int OP = kVB + 8;      // sO row pitch
   static constexpr int PP = kTile + 8;    // sP row pitch
+  static constexpr int qBytes = kTile * QP * 2;
+  static constexpr int kBytes = kTile * KP * 2;
+  static constexpr int vBytes = kTile * VP * 2;
   static constexpr int oQ = 0;
-  static constexpr int oK = oQ + kTile * QP * 2;
-  static constexpr int oV = oK + kTile * KP * 2;
-  static constexpr int oO = oV + kTile * VP * 2;
-  static constexpr int oP = oO + kTile * OP * 2;
+  static constexpr int oK = oQ + qBytes;  // [2]
+  static constexpr int oV = oK + 2 * kBytes;
+  static constexpr int oP = oV + vBytes;
   // double-buffered tile data, [2] of:
   static constexpr int nbBytes = 3 * K * 2;          // bf16 [3][K]: n~ hi, lo, zero
   static constexpr int wBytes = kTile * 4;           // float [64] key weights
@@ -191,18 +267,13 @@ struct OutLds {
 template <int K, bool RESCALE>
 __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   using L = OutLds<K>;
-  constexpr int QP = L::QP, KP = L::KP, VP = L::VP, OP = L::OP, PP = L::PP;
+  constexpr int QP = L::QP, KP = L::KP, VP = L::VP, PP = L::PP;
   constexpr int KS = K / 32;                                   // 32-deep steps over d_qk
   constexpr int KX = K / 16;                                   // 16-row tiles of C^T along d_qk
   constexpr int NW = kOutWaves;
-  constexpr int NT = 64 * NW;                                  // threads
   constexpr int KXW = KX >= NW ? KX / NW : 1;                  // normaliser tiles per wave
-  constexpr int QV = kTile * K / 8 / NT;                       // 16-byte vectors per thread, 64 x K tile
-  constexpr int VV = kTile * kVB / 8 / NT;                     // 16-byte vectors per thread, 64 x 128 tile
   __bf16* sQ = reinterpret_cast<__bf16*>(smem + L::oQ);
-  __bf16* sK = reinterpret_cast<__bf16*>(smem + L::oK);
   __bf16* sV = reinterpret_cast<__bf16*>(smem + L::oV);
-  __bf16* sO = reinterpret_cast<__bf16*>(smem + L::oO);
   __bf16* sP = reinterpret_cast<__bf16*>(smem + L::oP);
   float* s_inv = reinterpret_cast<float*>(smem + L::oInv);
   float* s_den = reinterpret_cast<float*>(smem + L::oDen);
@@ -249,6 +320,9 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   const int kg = w & 3, zh = w >> 2;
   const int64_t vcol0 = (int64_t)vb * kVB;
   const int64_t nseg1 = a.S - 1;
+  // Register row group z of H^T holds rows 16 zg(z) .. + 15, so that every
+  // wave's Q K^T rows are its groups 0 and 1 (no branch on zh).
+  auto zg = [&](int z) { return (z + 2 * zh) & 3; };
 
   // ---------------- carried state
   f32x4 Ct[KX];
@@ -283,57 +357,91 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   for (int b = 0; b < 2; ++b) {
     const TileBuf tb = tile_buf(b);
     if (tid < kTile) tb.wb[2 * kTile + tid] = (__bf16)0.f;
-    for (int k = tid; k < K; k += NT) tb.nb[2 * K + k] = (__bf16)0.f;
+    for (int k = tid; k < K; k += 64 * NW) tb.nb[2 * K + k] = (__bf16)0.f;
   }
 
-  // ---------------- next-tile registers; loads are unconditional (rows clamped
-  // into the tile) so that no branch forces the load counter to drain
-  bf16x8 pq[QV], pk[QV], pv[VV], po[VV];
-  double r_u = 0.0, r_mp = 0.0, r_b = 0.0, r_mp0 = 0.0;
-  int r_rs = -1, r_rs0 = -1;
+  // ---------------- copies of the next tile. Rows past the sequence end are
+  // clamped into the tile (their results are masked), so no load depends on
+  // a per-lane branch.
+  auto last_row = [&](int64_t tau) { return (unsigned)(min((int64_t)kTile, T - tau * kTile) - 1); };
+  using DQ = DmaTile<QP, NW>;
+  using DK = DmaTile<KP, NW>;
+  using DV = DmaTile<VP, NW>;
+  constexpr int RQ = DQ::kRounds, RK = DK::kRounds, RV = DV::kRounds;
+  // slots 0-4 take the K rounds, slots 4-8 the Q and V rounds
+  static_assert(RK <= 5 && RQ <= 5 && RV <= 5, "copy rounds fit their slots");
+  // Per-lane source offsets of this wave's copy rounds for a full tile,
+  // computed once; a ragged last tile recomputes them with its rows clamped.
+  unsigned offQ[RQ], offK[RK], offV[RV];
+#pragma unroll
+  for (int r = 0; r < RQ; ++r) offQ[r] = dma_src_off<K, QP>(DQ::load(w, r), (unsigned)lane, (unsigned)K, kTile - 1);
+#pragma unroll
+  for (int r = 0; r < RK; ++r) offK[r] = dma_src_off<K, KP>(DK::load(w, r), (unsigned)lane, (unsigned)K, kTile - 1);
+#pragma unroll
+  for (int r = 0; r < RV; ++r) offV[r] = dma_src_off<kVB, VP>(DV::load(w, r), (unsigned)lane, (unsigned)V, kTile - 1);
+  auto dma_issue = [&](const __amdgpu_buffer_rsrc_t& src, unsigned off, char* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)dst, 16, (int)off, 0, 0, 0);
+  };
+  auto dma_q = [&](int64_t tau, int r) {
+    const unsigned last = last_row(tau);
+    const auto src = buffer_rsrc(a.q + (bh * T + tau * kTile) * K, (last + 1) * (unsigned)K * 2u);
+    const int n = DQ::load(w, r);
+    char* dst = smem + L::oQ + 1024 * n;
+    if (last == kTile - 1) dma_issue(src, offQ[r], dst);
+    else dma_issue(src, dma_src_off<K, QP>(n, (unsigned)fresh_lanes().lane, (unsigned)K, last), dst);
+  };
+  auto dma_k = [&](int64_t tau, int b, int r) {
+    const unsigned last = last_row(tau);
+    const auto src = buffer_rsrc(a.k + (bh * T + tau * kTile) * K, (last + 1) * (unsigned)K * 2u);
+    const int n = DK::load(w, r);
+    char* dst = smem + L::oK + b * L::kBytes + 1024 * n;
+    if (last == kTile - 1) dma_issue(src, offK[r], dst);
+    else dma_issue(src, dma_src_off<K, KP>(n, (unsigned)fresh_lanes().lane, (unsigned)K, last), dst);
+  };
+  auto dma_v = [&](int64_t tau, int r) {
+    const unsigned last = last_row(tau);
+    const auto src = buffer_rsrc(a.v + (bh * T + tau * kTile) * V + vcol0, (last * (unsigned)V + kVB) * 2u);
+    const int n = DV::load(w, r);
+    char* dst = smem + L::oV + 1024 * n;
+    if (last == kTile - 1) dma_issue(src, offV[r], dst);
+    else dma_issue(src, dma_src_off<kVB, VP>(n, (unsigned)fresh_lanes().lane, (unsigned)V, last), dst);
+  };
+  // O straight into the registers of the epilogue. Register pair p holds,
+  // once split by swap_rows16, columns 16 w + 4 g .. + 3 of rows 16 zg(z) + i
+  // for z = 2 p (po[2p]) and z = 2 p + 1 (po[2p + 1]); it is loaded as one
+  // 16-byte row piece per lane: a lane in an even 16-lane row takes row
+  // z = 2 p + 1, one in an odd row takes row z = 2 p, columns 16 w + 4 (g & 2) .. + 7.
+  // The same per-lane offsets address the H stores. Both go through a buffer
+  // resource over the tile's valid rows: loads past it return zero (their
+  // rows' results are never stored) and stores past it are dropped.
+  bf16x4 po[4];
+  unsigned offO[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const unsigned t = 16 * zg((g & 1) ? 2 * p : 2 * p + 1) + i;
+    offO[p] = 2u * (t * (unsigned)V + 16 * w + 4 * (g & 2));
+  }
+  auto tile_rsrc_vo = [&](const __bf16* base, int64_t tau) {
+    return buffer_rsrc(base + (bh * T + tau * kTile) * V + vcol0, (last_row(tau) * (unsigned)V + kVB) * 2u);
+  };
+  auto load_o = [&](int64_t tau, int p) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc_vo(a.o, tau), (int)offO[p], 0, 0);
+    const bf16x8 y = __builtin_bit_cast(bf16x8, x);
+    po[2 * p + 1] = __builtin_shufflevector(y, y, 0, 1, 2, 3);
+    po[2 * p] = __builtin_shufflevector(y, y, 4, 5, 6, 7);
+  };
+  // gate data of the next tile, for the tile preparation of waves 0-3
+  double r_u = 0.0, r_mp = 0.0, r_b = 0.0;
+  int r_rs = -1;
   double t_g = 0.0, t_U = 0.0;
   int t_R = -1;
-  // Tile pointers are wave-uniform (scalar registers); the per-lane parts
-  // are 32-bit element offsets within the tile. The loads of the next tile
-  // go out in parts (mask bits: 1 q, 2 k, 4 v and o, 8 gate data) spread
-  // over the phases of the current one: a wave that issues all of them at
-  // once stalls until the address unit has taken them.
-  auto issue = [&](int64_t tau, int parts, unsigned qmask = ~0u) {
-    const Lanes ln = fresh_lanes();
-    const unsigned tid = (unsigned)ln.tid, lane = (unsigned)ln.lane;
-    const int64_t t0 = tau * kTile;
-    const unsigned last = (unsigned)(min((int64_t)kTile, T - t0) - 1);
-    const int64_t tok0 = bh * T + t0;
-    if (parts & 3) {
-      const __bf16* qt = a.q + tok0 * K;
-      const __bf16* kt = a.k + tok0 * K;
-#pragma unroll
-      for (int e = 0; e < QV; ++e) {
-        const unsigned it = tid + NT * e;
-        const unsigned off = min(it / (K / 8), last) * K + 8 * (it % (K / 8));
-        if ((parts & 1) && ((qmask >> e) & 1)) pq[e] = *reinterpret_cast<const bf16x8*>(qt + off);
-        if (parts & 2) pk[e] = *reinterpret_cast<const bf16x8*>(kt + off);
-      }
-    }
-    if (parts & 4) {
-      const __bf16* vt = a.v + tok0 * V + vcol0;
-      const __bf16* ot = a.o + tok0 * V + vcol0;
-#pragma unroll
-      for (int e = 0; e < VV; ++e) {
-        const unsigned it = tid + NT * e;
-        const unsigned off = min(it / (kVB / 8), last) * (unsigned)V + 8 * (it % (kVB / 8));
-        pv[e] = *reinterpret_cast<const bf16x8*>(vt + off);
-        po[e] = *reinterpret_cast<const bf16x8*>(ot + off);
-      }
-    }
-    if (!(parts & 8) || w >= 4) return;   // the gate data feed the tile preparation of waves 0-3
-    const unsigned j = min(lane, last);
+  auto load_gate = [&](int64_t tau) {
+    const unsigned j = min((unsigned)fresh_lanes().lane, last_row(tau));
+    const int64_t tok0 = bh * T + tau * kTile;
     r_u = (a.gb.u + tok0)[j];
     r_mp = (a.gb.mp + tok0)[j];
     r_b = (a.gb.b + tok0)[j];
     r_rs = (a.gb.rs + tok0)[j];
-    r_mp0 = a.gb.mp[tok0];
-    r_rs0 = a.gb.rs[tok0];
     t_g = a.gb.g[bh * Nt + tau];
     t_U = a.gb.U[bh * Nt + tau];
     t_R = a.gb.R[bh * Nt + tau];
@@ -388,8 +496,8 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
         tb.info[1] = __builtin_bit_cast(int, rescale ? (float)exp(logD + ld) : 1.f);
       }
     } else {
-      const bool carry0 = state && r_rs0 < 0;
-      double ref = fmax(carry0 ? m : -INFINITY, r_mp0);
+      const bool carry0 = state && __builtin_amdgcn_readlane(r_rs, 0) < 0;   // lane 0 holds the first token
+      double ref = fmax(carry0 ? m : -INFINITY, readlane_f64(r_mp, 0));
       if (ref == -INFINITY) ref = 0.0;
       const bool valid = j < Lc;
       const bool carry = state && r_rs < 0;
@@ -416,44 +524,49 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     m = t_g + Rm;
   };
 
-  issue(tile0, 15);
+  for (int r = 0; r < RK; ++r) dma_k(tile0, 0, r);
+  for (int r = 0; r < RQ; ++r) dma_q(tile0, r);
+  for (int r = 0; r < RV; ++r) dma_v(tile0, r);
   if (w < 4) {
+    load_gate(tile0);
     prep(tile0, tile_buf(0), m_chain, logD_chain, has_state);
     advance(m_chain, logD_chain);
   }
   put_n(tile_buf(0));
+  __builtin_amdgcn_s_waitcnt(0);   // the loop's first wait leaves the last two operations out
   for (int64_t tau = tile0; tau < tile1; ++tau) {
     const int64_t t0 = tau * kTile;
     const int Lc = (int)min((int64_t)kTile, T - t0);
     const int64_t tok0 = bh * T + t0;
     const int buf = (int)((tau - tile0) & 1);
     const TileBuf tb = tile_buf(buf);
+    const __bf16* sK = reinterpret_cast<const __bf16*>(smem + L::oK + buf * L::kBytes);
 
-    __syncthreads();   // the previous tile's LDS reads are done; tile data of tau prepared
-    // ---------------- stage tile tau
-    const Lanes ls = fresh_lanes();
-#pragma unroll
-    for (int e = 0; e < QV; ++e) {
-      const int it = ls.tid + NT * e;
-      const int row = it / (K / 8), cv = it % (K / 8);
-      *reinterpret_cast<bf16x8*>(&sQ[row * QP + 8 * cv]) = pq[e];
-      *reinterpret_cast<bf16x8*>(&sK[row * KP + 8 * cv]) = pk[e];
-    }
-#pragma unroll
-    for (int e = 0; e < VV; ++e) {
-      const int it = ls.tid + NT * e;
-      const int row = it / (kVB / 8), cv = it % (kVB / 8);
-      *reinterpret_cast<bf16x8*>(&sV[row * VP + 8 * cv]) = pv[e];
-      *reinterpret_cast<bf16x8*>(&sO[row * OP + 8 * cv]) = po[e];
-    }
-    __syncthreads();   // tile tau staged
+    // this wave's copies of tile tau have landed (and its H stores of tile
+    // tau - 1, which were issued last, have completed)
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();   // tile tau in LDS, its tile data prepared; tile tau - 1's reads done
     const bool more = tau + 1 < tile1;
-    const int64_t tn = more ? tau + 1 : tau;   // on the last tile the q loads repeat this tile
+    // The copies of the next tile and the register loads go out
+    // unconditionally (on the last tile they repeat it into buffers nobody
+    // reads any more), so that every wave issues the same memory operations on
+    // every tile and the compiler's waits for loaded registers are exact.
+    const int64_t tn = more ? tau + 1 : tau;
+    // V^T fragments of P V and of the state update. The transposed LDS reads
+    // of a tile (these and the state update's) all come before the tile's
+    // copies are issued: such a read waits for every direct-to-LDS load of the
+    // wave in flight.
+    bf16x8 Av[kTile / 32];
+    {
+      const Lanes lv = fresh_lanes();
+#pragma unroll
+      for (int jb = 0; jb < kTile / 32; ++jb) Av[jb] = frag_tr(sV, VP, 32 * jb, 16 * w, lv.lane);
+    }
+    if (w < 4) load_gate(tn);   // consumed by the preparation of tile tau + 1 at the end of this one
+    load_o(tau, 0);
+    load_o(tau, 1);
 
-    // ---------------- Q K^T (16 keys x 32 rows) and (Q C~^T)^T (16 columns x 64 rows).
-    // Register row group z holds rows 16 zg(z) .. + 15 with zg(z) = (z + 2 zh) & 3,
-    // so that every wave's Q K^T rows are its groups 0 and 1 (no branch on zh).
-    auto zg = [&](int z) { return (z + 2 * zh) & 3; };
+    // ---------------- Q K^T (16 keys x 32 rows) and (Q C~^T)^T (16 columns x 64 rows)
     f32x4 sacc[2], acc[4];
     sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -470,10 +583,70 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       const bf16x8 Bc = pack_bf16(Ct[2 * s], Ct[2 * s + 1]);
 #pragma unroll
       for (int z = 0; z < 4; ++z) acc[z] = mma(Bc, fa[z], acc[z]);
-      // the next tile's q, one 16-byte vector per lane every KS / QV steps
-      if constexpr (s % (KS / QV) == 0) issue(tn, 1, 1u << (s / (KS / QV)));
-      __builtin_amdgcn_sched_barrier(0);
     });
+
+    // ---------------- state update: C~ <- decay C~ + K^T diag(w) V, n~ likewise
+    // (Q C~^T above used the state at the start of the tile)
+    if constexpr (RESCALE) {
+      if (__builtin_amdgcn_readfirstlane(tb.info[0])) {   // uniform over the workgroup
+        const float f = __builtin_bit_cast(float, tb.info[1]);
+#pragma unroll
+        for (int kx = 0; kx < KX; ++kx) Ct[kx] *= f;
+#pragma unroll
+        for (int x = 0; x < KXW; ++x) Nacc[x] *= f;
+      }
+    }
+#pragma unroll
+    for (int jb = 0; jb < kTile / 32; ++jb) {
+      const int ts = 32 * jb;
+      const Lanes lu = fresh_lanes();
+      const f32x4 wa = *reinterpret_cast<const f32x4*>(&tb.w[ts + 8 * lu.g]);
+      const f32x4 wb = *reinterpret_cast<const f32x4*>(&tb.w[ts + 8 * lu.g + 4]);
+      bf16x8 Bv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Bv[e] = (__bf16)((float)Av[jb][e] * (e < 4 ? wa[e] : wb[e - 4]));
+      const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&tb.wb[min(lu.i, 2) * kTile + ts + 8 * lu.g]);
+      // transposed K fragments through a ring of kRing registers: the read of
+      // tile kx + kRing - 1 is issued before the MFMAs of tile kx
+      constexpr int kRing = 4;
+      bf16x8 Ak[kRing];
+      unroll<kRing - 1>([&](auto p_c) {
+        constexpr int p = decltype(p_c)::value;
+        if constexpr (p < KX) Ak[p] = frag_trk(sK, KP, ts, p, lu.lane);
+      });
+      unroll<KX>([&](auto kx_c) {
+        constexpr int kx = decltype(kx_c)::value;
+        if constexpr (kx + kRing - 1 < KX) Ak[(kx + kRing - 1) % kRing] = frag_trk(sK, KP, ts, kx + kRing - 1, lu.lane);
+        Ct[kx] = mma(Ak[kx % kRing], Bv, Ct[kx]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // n~ tiles of this wave: their K fragments are read again rather than
+      // picked out of the ring under a branch per tile
+#pragma unroll
+      for (int x = 0; x < KXW; ++x) {
+        if (KX >= NW || w * KXW + x < KX)
+          Nacc[x] = mma(frag_trk(sK, KP, ts, min(w * KXW + x, KX - 1), lu.lane), Bw, Nacc[x]);
+      }
+    }
+    // The registers loaded at the top of the tile are taken here, before any
+    // copy is issued: with copies or stores in flight the compiler can only
+    // wait for all of the wave's memory operations. O is split into its
+    // epilogue layout; the gate registers are marked as needed.
+    swap_rows16(po[1], po[0]);
+    swap_rows16(po[3], po[2]);
+    if (w < 4) asm volatile("" ::"v"(r_u), "v"(r_mp), "v"(r_b), "v"(r_rs));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---------------- copies of the next tile from here on. Slot q issues
+    // round q of K (into the other half; its last readers were in tile tau -
+    // 1) and, after the barrier that ends their reads in this tile, rounds
+    // q - 4 of Q and V.
+    auto copy_slot = [&](int q) {
+      if (q < RK) dma_k(tn, buf ^ 1, q);
+      if (q >= 4 && q - 4 < RQ) dma_q(tn, q - 4);
+      if (q >= 4 && q - 4 < RV) dma_v(tn, q - 4);
+    };
+    copy_slot(0);
     // ---------------- q . n~: wave w takes the 32-deep step s = w of d_qk
     {
       const Lanes ln = fresh_lanes();
@@ -488,6 +661,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
           dacc[z] = mma(fa, Bn, dacc[z]);
         }
       }
+      copy_slot(1);
 #pragma unroll
       for (int z = 0; z < 4; ++z) {
         f32x4 d;
@@ -496,7 +670,6 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
         if (ln.i == 0) *reinterpret_cast<f32x4*>(&s_dn[w * kTile + 16 * z + 4 * ln.g]) = d;
       }
     }
-    if (more) issue(tau + 1, 2);
     // the carried-state term enters row t with weight exp(m_prev - r_t + logD);
     // acc[z] register r in lane (g, i) is H^T[v = 16 w + 4 g + r][t = 16 zg(z) + i]
     const Lanes lp = fresh_lanes();
@@ -523,9 +696,11 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
         *reinterpret_cast<bf16x4*>(&sP[tl * PP + 16 * kg + 4 * lp.g]) = pk4;
         psum = sum_rows(psum);
         if (lp.g == 0) s_den[kg * kTile + tl] = psum;
+        copy_slot(2 + zz);
       }
     }
-    __syncthreads();   // sP, s_den, s_dn complete
+    lds_barrier();   // sP, s_den, s_dn complete; Q and V of tile tau no longer read from LDS
+    copy_slot(4);
     if (w == 0) {   // 1 / max(|n~^T q|, floor) of row t = lane
       const int t = fresh_lanes().lane;
       const float den = s_den[t] + s_den[kTile + t] + s_den[2 * kTile + t] + s_den[3 * kTile + t];
@@ -536,91 +711,47 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       s_inv[t] = __builtin_amdgcn_rcpf(fmaxf(fmaxf(fabsf(d), tb.fl[t]), FLT_MIN));
     }
     // ---------------- (P V)^T
-    const Lanes lv = fresh_lanes();
+    {
+      const Lanes lv = fresh_lanes();
 #pragma unroll
-    for (int jj = 0; jj < kTile; jj += 32) {
-      bf16x8 B[4];
+      for (int jb = 0; jb < kTile / 32; ++jb) {
+        bf16x8 B[4];
 #pragma unroll
-      for (int z = 0; z < 4; ++z) B[z] = *reinterpret_cast<const bf16x8*>(&sP[(16 * zg(z) + lv.i) * PP + jj + 8 * lv.g]);
-      const bf16x8 A = frag_tr(sV, VP, jj, 16 * w, lv.lane);
+        for (int z = 0; z < 4; ++z) B[z] = *reinterpret_cast<const bf16x8*>(&sP[(16 * zg(z) + lv.i) * PP + 32 * jb + 8 * lv.g]);
 #pragma unroll
-      for (int z = 0; z < 4; ++z) acc[z] = mma(A, B[z], acc[z]);
-    }
-    if (more) issue(tau + 1, 4);
-    __syncthreads();   // s_inv complete
-    // ---------------- normaliser, output gate; h staged in place of O, four
-    // consecutive columns of one row per lane
-    const Lanes le = fresh_lanes();
-#pragma unroll
-    for (int z = 0; z < 4; ++z) {
-      const int t = 16 * zg(z) + le.i;
-      const float inv = s_inv[t];
-      __bf16* p = &sO[t * OP + 16 * w + 4 * le.g];
-      const bf16x4 o4 = *reinterpret_cast<const bf16x4*>(p);
-      bf16x4 h4;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float og = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2eF * (float)o4[r]));
-        h4[r] = (__bf16)(og * acc[z][r] * inv);
-      }
-      *reinterpret_cast<bf16x4*>(p) = h4;
-    }
-    if (more) issue(tau + 1, 8);
-    __syncthreads();   // h tile complete
-    const Lanes lh = fresh_lanes();
-    __bf16* ht = a.h + tok0 * V + vcol0;
-#pragma unroll
-    for (int e = 0; e < VV; ++e) {
-      const unsigned it = (unsigned)lh.tid + NT * e;
-      const unsigned row = it / (kVB / 8), cv = it % (kVB / 8);
-      if (row < (unsigned)Lc)
-        *reinterpret_cast<bf16x8*>(ht + row * (unsigned)V + 8 * cv) =
-            *reinterpret_cast<const bf16x8*>(&sO[row * OP + 8 * cv]);
-    }
-
-    // ---------------- state update: C~ <- decay C~ + K^T diag(w) V, n~ likewise
-    if constexpr (RESCALE) {
-      if (__builtin_amdgcn_readfirstlane(tb.info[0])) {   // uniform over the workgroup
-        const float f = __builtin_bit_cast(float, tb.info[1]);
-#pragma unroll
-        for (int kx = 0; kx < KX; ++kx) Ct[kx] *= f;
-#pragma unroll
-        for (int x = 0; x < KXW; ++x) Nacc[x] *= f;
+        for (int z = 0; z < 4; ++z) acc[z] = mma(Av[jb], B[z], acc[z]);
+        copy_slot(5 + jb);
       }
     }
+    lds_barrier();   // s_inv complete
+    // ---------------- normaliser, output gate: a lane forms four consecutive
+    // columns of one row per register group and stores them, paired with its
+    // partner's, as 16-byte row pieces straight to H (the layout of load_o);
+    // rows past the sequence end fall outside the buffer range and are dropped
+    {
+      const Lanes le = fresh_lanes();
+      bf16x8 hv[2];
 #pragma unroll
-    for (int ts = 0; ts < kTile; ts += 32) {
-      const Lanes lu = fresh_lanes();
-      const f32x4 wa = *reinterpret_cast<const f32x4*>(&tb.w[ts + 8 * lu.g]);
-      const f32x4 wb = *reinterpret_cast<const f32x4*>(&tb.w[ts + 8 * lu.g + 4]);
-      bf16x8 Bv;
-      {
-        const bf16x8 raw = frag_tr(sV, VP, ts, 16 * w, lu.lane);
+      for (int p = 0; p < 2; ++p) {
+        bf16x4 h4[2];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) Bv[e] = (__bf16)((float)raw[e] * (e < 4 ? wa[e] : wb[e - 4]));
+        for (int zz = 0; zz < 2; ++zz) {
+          const int z = 2 * p + zz;
+          const float inv = s_inv[16 * zg(z) + le.i];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float og = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2eF * (float)po[z][r]));
+            h4[zz][r] = (__bf16)(og * acc[z][r] * inv);
+          }
+        }
+        swap_rows16(h4[1], h4[0]);
+        hv[p] = __builtin_shufflevector(h4[1], h4[0], 0, 1, 2, 3, 4, 5, 6, 7);
+        copy_slot(7 + p);
       }
-      const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&tb.wb[min(lu.i, 2) * kTile + ts + 8 * lu.g]);
-      // transposed K fragments through a ring of kRing registers: the read of
-      // tile kx + kRing - 1 is issued before the MFMAs of tile kx
-      constexpr int kRing = 4;
-      bf16x8 Ak[kRing];
-      unroll<kRing - 1>([&](auto p_c) {
-        constexpr int p = decltype(p_c)::value;
-        if constexpr (p < KX) Ak[p] = frag_trk(sK, KP, ts, p, lu.lane);
-      });
-      unroll<KX>([&](auto kx_c) {
-        constexpr int kx = decltype(kx_c)::value;
-        if constexpr (kx + kRing - 1 < KX) Ak[(kx + kRing - 1) % kRing] = frag_trk(sK, KP, ts, kx + kRing - 1, lu.lane);
-        Ct[kx] = mma(Ak[kx % kRing], Bv, Ct[kx]);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      // n~ tiles of this wave: their K fragments are read again rather than
-      // picked out of the ring under a branch per tile
+      // the two stores are this wave's last memory operations of the tile
+      const __amdgpu_buffer_rsrc_t hr = tile_rsrc_vo(a.h, tau);
 #pragma unroll
-      for (int x = 0; x < KXW; ++x) {
-        if (KX >= NW || w * KXW + x < KX)
-          Nacc[x] = mma(frag_trk(sK, KP, ts, min(w * KXW + x, KX - 1), lu.lane), Bw, Nacc[x]);
-      }
+      for (int p = 0; p < 2; ++p) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hv[p]), hr, (int)offO[p], 0, 0);
     }
     // ---------------- the next tile's data into the other half (its readers
     // start after the next top barrier; this half's last readers were in tile
@@ -634,6 +765,9 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       }
     }
   }
+  // the last tile's copies (repeats into unread buffers) land before the
+  // workgroup can end and give up its LDS
+  __builtin_amdgcn_s_waitcnt(0);
   if (w == 0 && lane == 0) {
     s_fin[0] = m_chain;
     s_fin[1] = logD_chain;
@@ -661,13 +795,6 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       if (tid == 0) a.m_out[bh] = (float)m_fin;
     }
   }
-}
-
-__device__ __forceinline__ double readlane_f64(double x, int lane) {
-  const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
-  const unsigned lo = __builtin_amdgcn_readlane((unsigned)u, lane);
-  const unsigned hi = __builtin_amdgcn_readlane((unsigned)(u >> 32), lane);
-  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
 }
 
 // True when some tile of the chunk would need the output kernel's
