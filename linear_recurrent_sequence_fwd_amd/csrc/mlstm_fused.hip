@@ -168,7 +168,7 @@ struct SegArgs {
   int S;                     // chunks
 };
 
-constexpr int kOutWaves = 8;   // output kernel: 16 value columns per wave, two waves per SIMD
+constexpr int kOutWaves = 8;   // output kernel: two halves of d_qk x four 32-column groups, two waves per SIMD
 
 // A 64-row bf16 tile (rows of E elements at a stride of RS elements in global
 // memory; rows past `last` repeat row `last`) is copied into LDS rows of pitch
@@ -212,14 +212,13 @@ __device__ __forceinline__ void swap_rows16(bf16x4& x1, bf16x4& x0) {
   x0 = __builtin_bit_cast(bf16x4, b);
 }
 
-// LDS of the output kernel. Q, K and V arrive by direct-to-LDS copies issued
-// by the compute waves during the previous tile: K (read in the first and in
-// the last phase of a tile) is double-buffered, Q is refilled once Q K^T and
-// q . n~ are done, V once P V is done (the state update reuses the P V
-// operand fragments). O is read into registers and H written from registers.
-// The tile's per-key and per-row data and the normaliser operand are
-// double-buffered: waves 0-3 (which finish the state update first) prepare
-// tile tau + 1's copy at the end of tile tau.
+// LDS of the output kernel. Q, K and V arrive by direct-to-LDS copies that
+// the compute waves issue in the second half of the previous tile, once the
+// tile's reads of the single buffers are over; O is read into registers and H
+// written from registers. The tile's per-key and per-row data and the
+// normaliser operand are double-buffered: waves 0-3 prepare tile tau + 1's
+// copy at the end of tile tau. The exchange area carries the partial sums that
+// the two waves of a value-column group (one per half of d_qk) hand each other.
 template <int K>
 struct OutLds {
   static constexpr int QP = K + 16;       // sQ row pitch: 8 dwords mod 64 banks, conflict-free 16-byte row reads
@@ -229,9 +228,10 @@ struct OutLds {
   static constexpr int qBytes = kTile * QP * 2;
   static constexpr int kBytes = kTile * KP * 2;
   static constexpr int vBytes = kTile * VP * 2;
+  static constexpr int kXchg = 6;                    // f32x4 registers a wave hands its partner
   static constexpr int oQ = 0;
-  static constexpr int oK = oQ + qBytes;  // [2]
-  static constexpr int oV = oK + 2 * kBytes;
+  static constexpr int oK = oQ + qBytes;
+  static constexpr int oV = oK + kBytes;
   static constexpr int oP = oV + vBytes;
   // double-buffered tile data, [2] of:
   static constexpr int nbBytes = 3 * K * 2;          // bf16 [3][K]: n~ hi, lo, zero
@@ -244,19 +244,27 @@ struct OutLds {
   static constexpr int oInv = oBuf + 2 * bufBytes;   // float [64] 1 / denominator of each row
   static constexpr int oDen = oInv + kTile * 4;      // float [4][64] row sums of P per key group
   static constexpr int oDn = oDen + 4 * kTile * 4;   // float [8][64] q . n~ partials per wave
-  static constexpr int oFin = oDn + kOutWaves * kTile * 4;   // double [2]: final m, logD
+  static constexpr int oX = oDn + kOutWaves * kTile * 4;     // f32x4 [8 waves][kXchg][64 lanes]
+  static constexpr int oFin = oX + kOutWaves * kXchg * 64 * 16;   // double [2]: final m, logD
   static constexpr int bytes = oFin + 16;
 };
 
-// Wave w owns value columns [16 w, 16 w + 16) of the workgroup's 128 and
-// keeps C~^T[k][v] for all k of them in registers: register r of Ct[kx] in
-// lane (g, i) is k = state_k0(kx, g) + r, v = 16 w + i. The normaliser n~ is
-// carried as two MFMA columns (lane i = 0: the sum weighted by the bf16 high
-// parts of the key weights, i = 1: by the low parts) in Nacc, for the 16-row
-// tiles kx = KXW w .. KXW w + KXW - 1. Q K^T is taken in blocks of 16 keys
-// [16 (w & 3), +16) x 32 rows [32 (w >> 2), +32); H is formed transposed
-// (value columns as MFMA rows), so that a lane holds four consecutive
-// columns of one output row.
+// Wave w = 4 kh + cg owns value columns [32 cg, 32 cg + 32) of the
+// workgroup's 128 and keeps C~^T[k][v] for the half kh of d_qk, k in
+// [K/2 kh, K/2 kh + K/2), in registers: register r of Ct[x][cv] in lane
+// (g, i) is k = K/2 kh + state_k0(x, g) + r, v = 32 cg + 16 cv + i. Waves w
+// and w + 4 (same columns, the two halves of d_qk) form a pair.
+//
+// Q C~^T and Q K^T are contractions over d_qk: each wave forms them over its
+// half for all 64 rows (value columns and keys as MFMA rows, H and S
+// transposed), hands the partial sums of the partner's rows (rows 32 (1 - kh)
+// .. + 31) to the partner through LDS and adds the partner's for its own rows
+// 32 kh .. + 31. Afterwards wave (kh, cg) holds H^T for its 32 columns and its
+// 32 rows, and S^T for keys [16 cg, +16) and its rows (register group z is
+// rows 16 zg(z) .. + 15, zg(z) = (z + 2 kh) & 3: groups 0 and 1 are the
+// wave's own rows). The normaliser n~ is carried as two MFMA columns (lane
+// i = 0: the sum weighted by the bf16 high parts of the key weights, i = 1: by
+// the low parts) in Nacc, for KXN 16-row tiles of the wave's half of d_qk.
 //
 // The tiles' decays are not applied to the accumulators one by one: the
 // registers hold X with C~ = exp(logD) X, n~ = exp(logD) Xn, new keys enter
@@ -268,16 +276,21 @@ template <int K, bool RESCALE>
 __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   using L = OutLds<K>;
   constexpr int QP = L::QP, KP = L::KP, VP = L::VP, PP = L::PP;
+  constexpr int KH = K / 2;                                    // d_qk rows per half
+  constexpr int KSH = KH / 32;                                 // 32-deep steps per half
+  constexpr int KXH = KH / 16;                                 // 16-row state tiles per half
   constexpr int KS = K / 32;                                   // 32-deep steps over d_qk
-  constexpr int KX = K / 16;                                   // 16-row tiles of C^T along d_qk
   constexpr int NW = kOutWaves;
-  constexpr int KXW = KX >= NW ? KX / NW : 1;                  // normaliser tiles per wave
+  constexpr int KXN = KXH >= 4 ? KXH / 4 : 1;                  // normaliser tiles per wave
+  static_assert(KSH >= 1 && KXH % 2 == 0, "d_qk halves of whole 32-deep steps");
   __bf16* sQ = reinterpret_cast<__bf16*>(smem + L::oQ);
+  const __bf16* sK = reinterpret_cast<const __bf16*>(smem + L::oK);
   __bf16* sV = reinterpret_cast<__bf16*>(smem + L::oV);
   __bf16* sP = reinterpret_cast<__bf16*>(smem + L::oP);
   float* s_inv = reinterpret_cast<float*>(smem + L::oInv);
   float* s_den = reinterpret_cast<float*>(smem + L::oDen);
   float* s_dn = reinterpret_cast<float*>(smem + L::oDn);
+  f32x4* s_x = reinterpret_cast<f32x4*>(smem + L::oX);
   double* s_fin = reinterpret_cast<double*>(smem + L::oFin);
   // views of one half of the double-buffered tile data
   struct TileBuf {
@@ -317,16 +330,17 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   // may run must sit behind a real branch.
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 15, g = lane >> 4;
-  const int kg = w & 3, zh = w >> 2;
+  const int cg = w & 3, kh = w >> 2;
+  const int kg = cg;                                           // key block of the wave's S^T
   const int64_t vcol0 = (int64_t)vb * kVB;
   const int64_t nseg1 = a.S - 1;
-  // Register row group z of H^T holds rows 16 zg(z) .. + 15, so that every
-  // wave's Q K^T rows are its groups 0 and 1 (no branch on zh).
-  auto zg = [&](int z) { return (z + 2 * zh) & 3; };
+  auto zg = [&](int z) { return (z + 2 * kh) & 3; };
+  // global 16-row tile of d_qk of the wave's local tile x
+  auto kxg = [&](int x) { return KXH * kh + x; };
 
   // ---------------- carried state
-  f32x4 Ct[KX];
-  f32x4 Nacc[KXW];
+  f32x4 Ct[KXH][2];
+  f32x4 Nacc[KXN];
   double m_start;
   bool has_state;
   const float* Cinit = nullptr;
@@ -344,15 +358,18 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     has_state = true;
   }
 #pragma unroll
-  for (int kx = 0; kx < KX; ++kx)
-    Ct[kx] = Cinit ? *reinterpret_cast<const f32x4*>(Cinit + (vcol0 + 16 * w + i) * K + state_k0(kx, g))
-                   : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int x = 0; x < KXH; ++x)
 #pragma unroll
-  for (int x = 0; x < KXW; ++x) {
-    const int kx = w * KXW + x;
-    Nacc[x] = (ninit && i == 0 && kx < KX) ? *reinterpret_cast<const f32x4*>(ninit + state_k0(kx, g))
-                                           : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+    for (int cv = 0; cv < 2; ++cv)
+      Ct[x][cv] = Cinit ? *reinterpret_cast<const f32x4*>(Cinit + (vcol0 + 32 * cg + 16 * cv + i) * K + state_k0(kxg(x), g))
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+  // normaliser tiles of the wave: local tiles KXN cg .. + KXN - 1 of its half
+  auto nx = [&](int x) { return KXN * cg + x; };
+  auto n_live = [&](int x) { return nx(x) < KXH; };
+#pragma unroll
+  for (int x = 0; x < KXN; ++x)
+    Nacc[x] = (ninit && i == 0 && n_live(x)) ? *reinterpret_cast<const f32x4*>(ninit + state_k0(kxg(nx(x)), g))
+                                            : f32x4{0.f, 0.f, 0.f, 0.f};
   // zero rows of the two-column normaliser operands, both halves
   for (int b = 0; b < 2; ++b) {
     const TileBuf tb = tile_buf(b);
@@ -368,7 +385,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   using DK = DmaTile<KP, NW>;
   using DV = DmaTile<VP, NW>;
   constexpr int RQ = DQ::kRounds, RK = DK::kRounds, RV = DV::kRounds;
-  // slots 0-4 take the K rounds, slots 4-8 the Q and V rounds
+  // five issue slots after the barrier that ends the tile's reads of Q, K, V
   static_assert(RK <= 5 && RQ <= 5 && RV <= 5, "copy rounds fit their slots");
   // Per-lane source offsets of this wave's copy rounds for a full tile,
   // computed once; a ragged last tile recomputes them with its rows clamped.
@@ -390,11 +407,11 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     if (last == kTile - 1) dma_issue(src, offQ[r], dst);
     else dma_issue(src, dma_src_off<K, QP>(n, (unsigned)fresh_lanes().lane, (unsigned)K, last), dst);
   };
-  auto dma_k = [&](int64_t tau, int b, int r) {
+  auto dma_k = [&](int64_t tau, int r) {
     const unsigned last = last_row(tau);
     const auto src = buffer_rsrc(a.k + (bh * T + tau * kTile) * K, (last + 1) * (unsigned)K * 2u);
     const int n = DK::load(w, r);
-    char* dst = smem + L::oK + b * L::kBytes + 1024 * n;
+    char* dst = smem + L::oK + 1024 * n;
     if (last == kTile - 1) dma_issue(src, offK[r], dst);
     else dma_issue(src, dma_src_off<K, KP>(n, (unsigned)fresh_lanes().lane, (unsigned)K, last), dst);
   };
@@ -406,29 +423,30 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     if (last == kTile - 1) dma_issue(src, offV[r], dst);
     else dma_issue(src, dma_src_off<kVB, VP>(n, (unsigned)fresh_lanes().lane, (unsigned)V, last), dst);
   };
-  // O straight into the registers of the epilogue. Register pair p holds,
-  // once split by swap_rows16, columns 16 w + 4 g .. + 3 of rows 16 zg(z) + i
-  // for z = 2 p (po[2p]) and z = 2 p + 1 (po[2p + 1]); it is loaded as one
-  // 16-byte row piece per lane: a lane in an even 16-lane row takes row
-  // z = 2 p + 1, one in an odd row takes row z = 2 p, columns 16 w + 4 (g & 2) .. + 7.
-  // The same per-lane offsets address the H stores. Both go through a buffer
-  // resource over the tile's valid rows: loads past it return zero (their
-  // rows' results are never stored) and stores past it are dropped.
-  bf16x4 po[4];
+  // O straight into the registers of the epilogue. For column half cv the
+  // pair po[cv][1], po[cv][0] holds, once split by swap_rows16, columns
+  // 32 cg + 16 cv + 4 g .. + 3 of rows 16 zg(1) + i and 16 zg(0) + i; it is
+  // loaded as one 16-byte row piece per lane: a lane in an even 16-lane row
+  // takes row zg(1), one in an odd row takes row zg(0), columns
+  // 32 cg + 16 cv + 4 (g & 2) .. + 7. The same per-lane offsets address the
+  // H stores. Both go through a buffer resource over the tile's valid rows:
+  // loads past it return zero (their rows' results are never stored) and
+  // stores past it are dropped.
+  bf16x4 po[2][2];
   unsigned offO[2];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const unsigned t = 16 * zg((g & 1) ? 2 * p : 2 * p + 1) + i;
-    offO[p] = 2u * (t * (unsigned)V + 16 * w + 4 * (g & 2));
+  for (int cv = 0; cv < 2; ++cv) {
+    const unsigned t = 16 * zg((g & 1) ? 0 : 1) + i;
+    offO[cv] = 2u * (t * (unsigned)V + 32 * cg + 16 * cv + 4 * (g & 2));
   }
   auto tile_rsrc_vo = [&](const __bf16* base, int64_t tau) {
     return buffer_rsrc(base + (bh * T + tau * kTile) * V + vcol0, (last_row(tau) * (unsigned)V + kVB) * 2u);
   };
-  auto load_o = [&](int64_t tau, int p) {
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc_vo(a.o, tau), (int)offO[p], 0, 0);
+  auto load_o = [&](int64_t tau, int cv) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc_vo(a.o, tau), (int)offO[cv], 0, 0);
     const bf16x8 y = __builtin_bit_cast(bf16x8, x);
-    po[2 * p + 1] = __builtin_shufflevector(y, y, 0, 1, 2, 3);
-    po[2 * p] = __builtin_shufflevector(y, y, 4, 5, 6, 7);
+    po[cv][1] = __builtin_shufflevector(y, y, 0, 1, 2, 3);
+    po[cv][0] = __builtin_shufflevector(y, y, 4, 5, 6, 7);
   };
   // gate data of the next tile, for the tile preparation of waves 0-3
   double r_u = 0.0, r_mp = 0.0, r_b = 0.0;
@@ -452,9 +470,8 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   auto put_n = [&](const TileBuf& tb) {
     const Lanes ln = fresh_lanes();
 #pragma unroll
-    for (int x = 0; x < KXW; ++x) {
-      const int kx = w * KXW + x;
-      if (kx < KX) {
+    for (int x = 0; x < KXN; ++x) {
+      if (n_live(x)) {
         bf16x4 hi4, lo4;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -463,7 +480,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
           hi4[r] = hi;
           lo4[r] = (__bf16)(nr - (float)hi);
         }
-        const int pos = state_k0(kx, ln.g);
+        const int pos = state_k0(kxg(nx(x)), ln.g);
         if (ln.i == 0) {
           *reinterpret_cast<bf16x4*>(&tb.nb[pos]) = hi4;
           *reinterpret_cast<bf16x4*>(&tb.nb[K + pos]) = lo4;
@@ -524,7 +541,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     m = t_g + Rm;
   };
 
-  for (int r = 0; r < RK; ++r) dma_k(tile0, 0, r);
+  for (int r = 0; r < RK; ++r) dma_k(tile0, r);
   for (int r = 0; r < RQ; ++r) dma_q(tile0, r);
   for (int r = 0; r < RV; ++r) dma_v(tile0, r);
   if (w < 4) {
@@ -533,14 +550,12 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     advance(m_chain, logD_chain);
   }
   put_n(tile_buf(0));
-  __builtin_amdgcn_s_waitcnt(0);   // the loop's first wait leaves the last two operations out
+  __builtin_amdgcn_s_waitcnt(0);
   for (int64_t tau = tile0; tau < tile1; ++tau) {
     const int64_t t0 = tau * kTile;
     const int Lc = (int)min((int64_t)kTile, T - t0);
-    const int64_t tok0 = bh * T + t0;
     const int buf = (int)((tau - tile0) & 1);
     const TileBuf tb = tile_buf(buf);
-    const __bf16* sK = reinterpret_cast<const __bf16*>(smem + L::oK + buf * L::kBytes);
 
     // this wave's copies of tile tau have landed (and its H stores of tile
     // tau - 1, which were issued last, have completed)
@@ -552,101 +567,57 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     // reads any more), so that every wave issues the same memory operations on
     // every tile and the compiler's waits for loaded registers are exact.
     const int64_t tn = more ? tau + 1 : tau;
-    // V^T fragments of P V and of the state update. The transposed LDS reads
-    // of a tile (these and the state update's) all come before the tile's
-    // copies are issued: such a read waits for every direct-to-LDS load of the
-    // wave in flight.
-    bf16x8 Av[kTile / 32];
+    // V^T fragments of P V and of the state update (columns 32 cg + 16 cv).
+    // The tile's transposed LDS reads all come before its copies are issued:
+    // such a read waits for every direct-to-LDS load of the wave in flight.
+    bf16x8 Av[kTile / 32][2];
     {
       const Lanes lv = fresh_lanes();
 #pragma unroll
-      for (int jb = 0; jb < kTile / 32; ++jb) Av[jb] = frag_tr(sV, VP, 32 * jb, 16 * w, lv.lane);
+      for (int jb = 0; jb < kTile / 32; ++jb)
+#pragma unroll
+        for (int cv = 0; cv < 2; ++cv) Av[jb][cv] = frag_tr(sV, VP, 32 * jb, 32 * cg + 16 * cv, lv.lane);
     }
     if (w < 4) load_gate(tn);   // consumed by the preparation of tile tau + 1 at the end of this one
     load_o(tau, 0);
     load_o(tau, 1);
 
-    // ---------------- Q K^T (16 keys x 32 rows) and (Q C~^T)^T (16 columns x 64 rows)
-    f32x4 sacc[2], acc[4];
-    sacc[0] = sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // ---------------- partial Q K^T (16 keys x 64 rows) and (Q C~^T)^T (32
+    // columns x 64 rows) over this wave's half of d_qk
+    f32x4 sacc[4], acc[4][2];
 #pragma unroll
-    for (int z = 0; z < 4; ++z) acc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int z = 0; z < 4; ++z) {
+      sacc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[z][0] = acc[z][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     const Lanes l1 = fresh_lanes();
-    unroll<KS>([&](auto s_c) {
+    unroll<KSH>([&](auto s_c) {
       constexpr int s = decltype(s_c)::value;
+      const int col = KH * kh + 32 * s + 8 * l1.g;
       bf16x8 fa[4];
 #pragma unroll
-      for (int z = 0; z < 4; ++z) fa[z] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * zg(z) + l1.i) * QP + 32 * s + 8 * l1.g]);
-      const bf16x8 fk = *reinterpret_cast<const bf16x8*>(&sK[(16 * kg + l1.i) * KP + 32 * s + 8 * l1.g]);
-      sacc[0] = mma(fk, fa[0], sacc[0]);
-      sacc[1] = mma(fk, fa[1], sacc[1]);
-      const bf16x8 Bc = pack_bf16(Ct[2 * s], Ct[2 * s + 1]);
+      for (int z = 0; z < 4; ++z) fa[z] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * zg(z) + l1.i) * QP + col]);
+      const bf16x8 fk = *reinterpret_cast<const bf16x8*>(&sK[(16 * kg + l1.i) * KP + col]);
 #pragma unroll
-      for (int z = 0; z < 4; ++z) acc[z] = mma(Bc, fa[z], acc[z]);
+      for (int z = 0; z < 4; ++z) sacc[z] = mma(fk, fa[z], sacc[z]);
+#pragma unroll
+      for (int cv = 0; cv < 2; ++cv) {
+        const bf16x8 Bc = pack_bf16(Ct[2 * s][cv], Ct[2 * s + 1][cv]);
+#pragma unroll
+        for (int z = 0; z < 4; ++z) acc[z][cv] = mma(Bc, fa[z], acc[z][cv]);
+      }
     });
-
-    // ---------------- state update: C~ <- decay C~ + K^T diag(w) V, n~ likewise
-    // (Q C~^T above used the state at the start of the tile)
-    if constexpr (RESCALE) {
-      if (__builtin_amdgcn_readfirstlane(tb.info[0])) {   // uniform over the workgroup
-        const float f = __builtin_bit_cast(float, tb.info[1]);
-#pragma unroll
-        for (int kx = 0; kx < KX; ++kx) Ct[kx] *= f;
-#pragma unroll
-        for (int x = 0; x < KXW; ++x) Nacc[x] *= f;
-      }
+    // the partner's rows (groups 2 and 3) to the exchange area
+    {
+      const Lanes lx = fresh_lanes();
+      f32x4* xo = s_x + w * L::kXchg * 64 + lx.lane;
+      xo[0] = acc[2][0];
+      xo[64] = acc[2][1];
+      xo[128] = acc[3][0];
+      xo[192] = acc[3][1];
+      xo[256] = sacc[2];
+      xo[320] = sacc[3];
     }
-#pragma unroll
-    for (int jb = 0; jb < kTile / 32; ++jb) {
-      const int ts = 32 * jb;
-      const Lanes lu = fresh_lanes();
-      const f32x4 wa = *reinterpret_cast<const f32x4*>(&tb.w[ts + 8 * lu.g]);
-      const f32x4 wb = *reinterpret_cast<const f32x4*>(&tb.w[ts + 8 * lu.g + 4]);
-      bf16x8 Bv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Bv[e] = (__bf16)((float)Av[jb][e] * (e < 4 ? wa[e] : wb[e - 4]));
-      const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&tb.wb[min(lu.i, 2) * kTile + ts + 8 * lu.g]);
-      // transposed K fragments through a ring of kRing registers: the read of
-      // tile kx + kRing - 1 is issued before the MFMAs of tile kx
-      constexpr int kRing = 4;
-      bf16x8 Ak[kRing];
-      unroll<kRing - 1>([&](auto p_c) {
-        constexpr int p = decltype(p_c)::value;
-        if constexpr (p < KX) Ak[p] = frag_trk(sK, KP, ts, p, lu.lane);
-      });
-      unroll<KX>([&](auto kx_c) {
-        constexpr int kx = decltype(kx_c)::value;
-        if constexpr (kx + kRing - 1 < KX) Ak[(kx + kRing - 1) % kRing] = frag_trk(sK, KP, ts, kx + kRing - 1, lu.lane);
-        Ct[kx] = mma(Ak[kx % kRing], Bv, Ct[kx]);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      // n~ tiles of this wave: their K fragments are read again rather than
-      // picked out of the ring under a branch per tile
-#pragma unroll
-      for (int x = 0; x < KXW; ++x) {
-        if (KX >= NW || w * KXW + x < KX)
-          Nacc[x] = mma(frag_trk(sK, KP, ts, min(w * KXW + x, KX - 1), lu.lane), Bw, Nacc[x]);
-      }
-    }
-    // The registers loaded at the top of the tile are taken here, before any
-    // copy is issued: with copies or stores in flight the compiler can only
-    // wait for all of the wave's memory operations. O is split into its
-    // epilogue layout; the gate registers are marked as needed.
-    swap_rows16(po[1], po[0]);
-    swap_rows16(po[3], po[2]);
-    if (w < 4) asm volatile("" ::"v"(r_u), "v"(r_mp), "v"(r_b), "v"(r_rs));
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---------------- copies of the next tile from here on. Slot q issues
-    // round q of K (into the other half; its last readers were in tile tau -
-    // 1) and, after the barrier that ends their reads in this tile, rounds
-    // q - 4 of Q and V.
-    auto copy_slot = [&](int q) {
-      if (q < RK) dma_k(tn, buf ^ 1, q);
-      if (q >= 4 && q - 4 < RQ) dma_q(tn, q - 4);
-      if (q >= 4 && q - 4 < RV) dma_v(tn, q - 4);
-    };
-    copy_slot(0);
     // ---------------- q . n~: wave w takes the 32-deep step s = w of d_qk
     {
       const Lanes ln = fresh_lanes();
@@ -661,7 +632,6 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
           dacc[z] = mma(fa, Bn, dacc[z]);
         }
       }
-      copy_slot(1);
 #pragma unroll
       for (int z = 0; z < 4; ++z) {
         f32x4 d;
@@ -670,17 +640,97 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
         if (ln.i == 0) *reinterpret_cast<f32x4*>(&s_dn[w * kTile + 16 * z + 4 * ln.g]) = d;
       }
     }
+
+    // ---------------- state update: C~ <- decay C~ + K^T diag(w) V, n~ likewise
+    // (Q C~^T above used the state at the start of the tile)
+    if constexpr (RESCALE) {
+      if (__builtin_amdgcn_readfirstlane(tb.info[0])) {   // uniform over the workgroup
+        const float f = __builtin_bit_cast(float, tb.info[1]);
+#pragma unroll
+        for (int x = 0; x < KXH; ++x) {
+          Ct[x][0] *= f;
+          Ct[x][1] *= f;
+        }
+#pragma unroll
+        for (int x = 0; x < KXN; ++x) Nacc[x] *= f;
+      }
+    }
+#pragma unroll
+    for (int jb = 0; jb < kTile / 32; ++jb) {
+      const int ts = 32 * jb;
+      const Lanes lu = fresh_lanes();
+      const f32x4 wa = *reinterpret_cast<const f32x4*>(&tb.w[ts + 8 * lu.g]);
+      const f32x4 wb = *reinterpret_cast<const f32x4*>(&tb.w[ts + 8 * lu.g + 4]);
+      bf16x8 Bv[2];
+#pragma unroll
+      for (int cv = 0; cv < 2; ++cv)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Bv[cv][e] = (__bf16)((float)Av[jb][cv][e] * (e < 4 ? wa[e] : wb[e - 4]));
+      const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&tb.wb[min(lu.i, 2) * kTile + ts + 8 * lu.g]);
+      // transposed K fragments through a ring of kRing registers: the read of
+      // tile x + kRing - 1 is issued before the MFMAs of tile x
+      constexpr int kRing = 4;
+      bf16x8 Ak[kRing];
+      unroll<kRing - 1>([&](auto p_c) {
+        constexpr int p = decltype(p_c)::value;
+        if constexpr (p < KXH) Ak[p] = frag_trk(sK, KP, ts, kxg(p), lu.lane);
+      });
+      unroll<KXH>([&](auto x_c) {
+        constexpr int x = decltype(x_c)::value;
+        if constexpr (x + kRing - 1 < KXH) Ak[(x + kRing - 1) % kRing] = frag_trk(sK, KP, ts, kxg(x + kRing - 1), lu.lane);
+        Ct[x][0] = mma(Ak[x % kRing], Bv[0], Ct[x][0]);
+        Ct[x][1] = mma(Ak[x % kRing], Bv[1], Ct[x][1]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      // n~ tiles of this wave: their K fragments are read again rather than
+      // picked out of the ring under a branch per tile
+#pragma unroll
+      for (int x = 0; x < KXN; ++x) {
+        if (KXH >= 4 || n_live(x))
+          Nacc[x] = mma(frag_trk(sK, KP, ts, kxg(min(nx(x), KXH - 1)), lu.lane), Bw, Nacc[x]);
+      }
+    }
+    // The registers loaded at the top of the tile are taken here, before any
+    // copy is issued: with copies or stores in flight the compiler can only
+    // wait for all of the wave's memory operations. O is split into its
+    // epilogue layout; the gate registers are marked as needed.
+    swap_rows16(po[0][1], po[0][0]);
+    swap_rows16(po[1][1], po[1][0]);
+    if (w < 4) asm volatile("" ::"v"(r_u), "v"(r_mp), "v"(r_b), "v"(r_rs));
+    lds_barrier();   // the exchange area is complete; Q, K and V of tile tau no longer read from LDS
+    // ---------------- copies of the next tile, in five slots from here on
+    auto copy_slot = [&](int q) {
+      if (q < RK) dma_k(tn, q);
+      if (q < RQ) dma_q(tn, q);
+      if (q < RV) dma_v(tn, q);
+    };
+    copy_slot(0);
+    // ---------------- the partner's partial sums for this wave's rows
+    {
+      const Lanes lx = fresh_lanes();
+      const f32x4* xi = s_x + (w ^ 4) * L::kXchg * 64 + lx.lane;
+      acc[0][0] += xi[0];
+      acc[0][1] += xi[64];
+      acc[1][0] += xi[128];
+      acc[1][1] += xi[192];
+      sacc[0] += xi[256];
+      sacc[1] += xi[320];
+    }
     // the carried-state term enters row t with weight exp(m_prev - r_t + logD);
-    // acc[z] register r in lane (g, i) is H^T[v = 16 w + 4 g + r][t = 16 zg(z) + i]
+    // acc[z][cv] register r in lane (g, i) is H^T[v = 32 cg + 16 cv + 4 g + r][t = 16 zg(z) + i]
     const Lanes lp = fresh_lanes();
 #pragma unroll
-    for (int z = 0; z < 4; ++z) acc[z] *= tb.sc[16 * zg(z) + lp.i];
-    // ---------------- P = S o D: lane holds S^T[j = 16 kg + 4 g + r][t = 16 z + i]
+    for (int z = 0; z < 2; ++z) {
+      const float sc = tb.sc[16 * zg(z) + lp.i];
+      acc[z][0] *= sc;
+      acc[z][1] *= sc;
+    }
+    // ---------------- P = S o D: lane holds S^T[j = 16 kg + 4 g + r][t = 16 zg(zz) + i]
     {
       const f32x4 u2 = *reinterpret_cast<const f32x4*>(&tb.u2[16 * kg + 4 * lp.g]);
 #pragma unroll
       for (int zz = 0; zz < 2; ++zz) {
-        const int tl = 16 * (2 * zh + zz) + lp.i;
+        const int tl = 16 * (2 * kh + zz) + lp.i;
         const float r2 = tb.r2[tl];
         const int rs = tb.rs[tl];
         bf16x4 pk4;
@@ -696,11 +746,10 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
         *reinterpret_cast<bf16x4*>(&sP[tl * PP + 16 * kg + 4 * lp.g]) = pk4;
         psum = sum_rows(psum);
         if (lp.g == 0) s_den[kg * kTile + tl] = psum;
-        copy_slot(2 + zz);
+        copy_slot(1 + zz);
       }
     }
-    lds_barrier();   // sP, s_den, s_dn complete; Q and V of tile tau no longer read from LDS
-    copy_slot(4);
+    lds_barrier();   // sP, s_den, s_dn complete
     if (w == 0) {   // 1 / max(|n~^T q|, floor) of row t = lane
       const int t = fresh_lanes().lane;
       const float den = s_den[t] + s_den[kTile + t] + s_den[2 * kTile + t] + s_den[3 * kTile + t];
@@ -710,48 +759,55 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       const float d = den + tb.sc[t] * dn;
       s_inv[t] = __builtin_amdgcn_rcpf(fmaxf(fmaxf(fabsf(d), tb.fl[t]), FLT_MIN));
     }
-    // ---------------- (P V)^T
+    // ---------------- (P V)^T for the wave's rows; rows 0-31 have no keys
+    // 32-63 (causal), so the half kh = 0 takes only the first 32 keys
     {
       const Lanes lv = fresh_lanes();
 #pragma unroll
       for (int jb = 0; jb < kTile / 32; ++jb) {
-        bf16x8 B[4];
+        if (jb == 0 || kh == 1) {
+          bf16x8 B[2];
 #pragma unroll
-        for (int z = 0; z < 4; ++z) B[z] = *reinterpret_cast<const bf16x8*>(&sP[(16 * zg(z) + lv.i) * PP + 32 * jb + 8 * lv.g]);
+          for (int z = 0; z < 2; ++z) B[z] = *reinterpret_cast<const bf16x8*>(&sP[(16 * zg(z) + lv.i) * PP + 32 * jb + 8 * lv.g]);
 #pragma unroll
-        for (int z = 0; z < 4; ++z) acc[z] = mma(Av[jb], B[z], acc[z]);
-        copy_slot(5 + jb);
+          for (int z = 0; z < 2; ++z) {
+            acc[z][0] = mma(Av[jb][0], B[z], acc[z][0]);
+            acc[z][1] = mma(Av[jb][1], B[z], acc[z][1]);
+          }
+        }
+        copy_slot(3 + jb);
       }
     }
     lds_barrier();   // s_inv complete
-    // ---------------- normaliser, output gate: a lane forms four consecutive
-    // columns of one row per register group and stores them, paired with its
-    // partner's, as 16-byte row pieces straight to H (the layout of load_o);
-    // rows past the sequence end fall outside the buffer range and are dropped
+    // ---------------- normaliser, output gate: per column half a lane forms
+    // four consecutive columns of each of its two rows and stores them, paired
+    // with its partner lane's, as 16-byte row pieces straight to H (the layout
+    // of load_o); rows past the sequence end fall outside the buffer range and
+    // are dropped
     {
       const Lanes le = fresh_lanes();
+      float inv[2];
+#pragma unroll
+      for (int z = 0; z < 2; ++z) inv[z] = s_inv[16 * zg(z) + le.i];
       bf16x8 hv[2];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
+      for (int cv = 0; cv < 2; ++cv) {
         bf16x4 h4[2];
 #pragma unroll
-        for (int zz = 0; zz < 2; ++zz) {
-          const int z = 2 * p + zz;
-          const float inv = s_inv[16 * zg(z) + le.i];
+        for (int z = 0; z < 2; ++z) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float og = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2eF * (float)po[z][r]));
-            h4[zz][r] = (__bf16)(og * acc[z][r] * inv);
+            const float og = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2eF * (float)po[cv][z][r]));
+            h4[z][r] = (__bf16)(og * acc[z][cv][r] * inv[z]);
           }
         }
         swap_rows16(h4[1], h4[0]);
-        hv[p] = __builtin_shufflevector(h4[1], h4[0], 0, 1, 2, 3, 4, 5, 6, 7);
-        copy_slot(7 + p);
+        hv[cv] = __builtin_shufflevector(h4[1], h4[0], 0, 1, 2, 3, 4, 5, 6, 7);
       }
       // the two stores are this wave's last memory operations of the tile
       const __amdgpu_buffer_rsrc_t hr = tile_rsrc_vo(a.h, tau);
 #pragma unroll
-      for (int p = 0; p < 2; ++p) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hv[p]), hr, (int)offO[p], 0, 0);
+      for (int cv = 0; cv < 2; ++cv) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hv[cv]), hr, (int)offO[cv], 0, 0);
     }
     // ---------------- the next tile's data into the other half (its readers
     // start after the next top barrier; this half's last readers were in tile
@@ -780,17 +836,18 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   if (seg == a.S - 1 && a.C_out) {
     float* Cdst = a.C_out + bh * V * K;
 #pragma unroll
-    for (int kx = 0; kx < KX; ++kx)
-      *reinterpret_cast<f32x4*>(Cdst + (vcol0 + 16 * w + i) * K + state_k0(kx, g)) = fD * Ct[kx];
+    for (int x = 0; x < KXH; ++x)
+#pragma unroll
+      for (int cv = 0; cv < 2; ++cv)
+        *reinterpret_cast<f32x4*>(Cdst + (vcol0 + 32 * cg + 16 * cv + i) * K + state_k0(kxg(x), g)) = fD * Ct[x][cv];
     if (vb == 0) {
       float* ndst = a.n_out + bh * K;
 #pragma unroll
-      for (int x = 0; x < KXW; ++x) {
-        const int kx = w * KXW + x;
+      for (int x = 0; x < KXN; ++x) {
         f32x4 nv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) nv[r] = fD * sum_xor1(Nacc[x][r]);
-        if (i == 0 && kx < KX) *reinterpret_cast<f32x4*>(ndst + state_k0(kx, g)) = nv;
+        if (i == 0 && n_live(x)) *reinterpret_cast<f32x4*>(ndst + state_k0(kxg(nx(x)), g)) = nv;
       }
       if (tid == 0) a.m_out[bh] = (float)m_fin;
     }
