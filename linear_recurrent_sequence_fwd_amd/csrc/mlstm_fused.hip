@@ -680,15 +680,12 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
         if constexpr (x + kRing - 1 < KXH) Ak[(x + kRing - 1) % kRing] = frag_trk(sK, KP, ts, kxg(x + kRing - 1), lu.lane);
         Ct[x][0] = mma(Ak[x % kRing], Bv[0], Ct[x][0]);
         Ct[x][1] = mma(Ak[x % kRing], Bv[1], Ct[x][1]);
+        // the wave's n~ tiles take the same K fragments (scalar branch)
+#pragma unroll
+        for (int xn = 0; xn < KXN; ++xn)
+          if (nx(xn) == x) Nacc[xn] = mma(Ak[x % kRing], Bw, Nacc[xn]);
         __builtin_amdgcn_sched_barrier(0);
       });
-      // n~ tiles of this wave: their K fragments are read again rather than
-      // picked out of the ring under a branch per tile
-#pragma unroll
-      for (int x = 0; x < KXN; ++x) {
-        if (KXH >= 4 || n_live(x))
-          Nacc[x] = mma(frag_trk(sK, KP, ts, kxg(min(nx(x), KXH - 1)), lu.lane), Bw, Nacc[x]);
-      }
     }
     // The registers loaded at the top of the tile are taken here, before any
     // copy is issued: with copies or stores in flight the compiler can only
