@@ -510,7 +510,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       tb.wb[kTile + j] = (__bf16)(wj - (float)whi);
       if (j == 0) {
         tb.info[0] = rescale ? 1 : 0;
-        tb.info[1] = __builtin_bit_cast(int, rescale ? (float)exp(logD + ld) : 1.f);
+        tb.info[1] = __builtin_bit_cast(int, rescale ? expf((float)(logD + ld)) : 1.f);   // below e^-70
       }
     } else {
       const bool carry0 = state && __builtin_amdgcn_readlane(r_rs, 0) < 0;   // lane 0 holds the first token
@@ -922,42 +922,114 @@ __global__ __launch_bounds__(64 * kOutWaves, 1) void out_kernel_fused(SegArgs a)
 constexpr int kMaxTiles = 8192 / kTile;   // tiles per chunk at the largest chunk
 
 // Scalars of a chunk's local end state, scanned once from the tile gate
-// scalars (the same float64 steps as the output kernel's tile loop, from an
-// empty state): per tile the factor exp(U - Rm - logD_next) that turns the
+// scalars with the same float64 steps as the output kernel's tile loop, from
+// an empty state: per tile the factor exp(U - Rm - logD_next) that turns the
 // in-tile weights w0 into the key weights, and the factor that rescales the
-// accumulators before the tile (1 when the decay is kept pending).
+// accumulators before the tile (1 when the decay is kept pending); at the end
+// the chunk's m, logD, log-forget total G and whether it holds a zero gate.
 struct LocScan {
-  double m, logD, G;
-  bool reset, any_rescale;
+  double m = -INFINITY, logD = 0.0, G = 0.0;
+  bool reset = false, zero = true, any_rescale = false;
+  // one tile with gate scalars gj, Uj, Rj; lane 0 writes its factors
+  __device__ void step(double gj, double Uj, int Rj, float* cw, float* rf) {
+    const double Rm = fmax(Rj >= 0 ? -INFINITY : m, Uj);
+    const bool live = Rm != -INFINITY;
+    const double ld = (Rj >= 0 || m == -INFINITY || !live) ? -INFINITY : m - Rm;
+    const bool rescale = logD + ld < -kMaxDefer;
+    const double logD_next = rescale ? 0.0 : logD + ld;
+    const bool scale = rescale && !zero;   // rescaling a zero state is a no-op
+    if ((threadIdx.x & 63) == 0) {
+      *cw = (live && Uj != -INFINITY) ? expf((float)(Uj - Rm - logD_next)) : 0.f;
+      // the factor is below e^-70 (or zero): a float exp of the rounded
+      // argument is as good as a float64 one and far cheaper
+      *rf = scale ? expf((float)(logD + ld)) : 1.f;
+    }
+    any_rescale = any_rescale || scale;
+    m = live ? gj + Rm : -INFINITY;
+    logD = logD_next;
+    G += gj;
+    reset = reset || Rj >= 0;
+    if (live && Uj != -INFINITY) zero = false;
+  }
 };
+
+// The same scan for up to 64 tiles at once, lane j taking tile j of the batch
+// (gate scalars g, U, R of its tile; n tiles, carry-in state c). The chain
+// m' = g + max(m, or -inf after a zero gate, U) is the max-plus map
+// x -> max(x + a, b) with a = g (-inf on a zero gate) and b = g + U; these
+// maps compose associatively, (a1, b1) then (a2, b2) giving (a1 + a2,
+// max(b1 + a2, b2)), so an inclusive lane scan gives m after every tile. The
+// pending decay logD is a prefix sum of ld that restarts at the tiles whose
+// ld is -inf. The one case that does not fit, logD + ld falling below
+// -kMaxDefer on a finite ld, returns false with c unchanged (the caller then
+// takes the batch step by step).
+__device__ bool local_scan_batch(double g, double U, int R, int n, LocScan& c, float* cw, float* rf) {
+  const int lane = threadIdx.x & 63;
+  const bool act = lane < n;
+  double a = act ? (R >= 0 ? -INFINITY : g) : 0.0;
+  double b = act ? g + U : -INFINITY;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double ap = __shfl_up(a, d), bp = __shfl_up(b, d);
+    if (lane >= d) {
+      b = fmax(bp + a, b);
+      a = ap + a;
+    }
+  }
+  const double m_after = fmax(c.m + a, b);
+  double m_before = __shfl_up(m_after, 1);
+  if (lane == 0) m_before = c.m;
+  const double Rm = fmax(R >= 0 ? -INFINITY : m_before, U);
+  const bool live = Rm != -INFINITY;
+  const double ld = (R >= 0 || m_before == -INFINITY || !live) ? -INFINITY : m_before - Rm;
+  // segmented prefix sum of ld, segments starting after the -inf tiles
+  const bool flag = act && ld == -INFINITY;
+  bool f = flag;
+  double sm = (act && !flag) ? ld : 0.0;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double sp = __shfl_up(sm, d);
+    const bool fp = __shfl_up((int)f, d) != 0;
+    if (lane >= d) {
+      sm = f ? sm : sp + sm;
+      f = f || fp;
+    }
+  }
+  const double logD_next = f ? sm : c.logD + sm;
+  double logD_before = __shfl_up(logD_next, 1);
+  if (lane == 0) logD_before = c.logD;
+  if (__any(act && !flag && logD_before + ld < -kMaxDefer)) return false;
+  const bool nonzero = act && live && U != -INFINITY;
+  const unsigned long long nzmask = __ballot(nonzero);
+  const bool zero_before = c.zero && (nzmask & ((1ull << lane) - 1ull)) == 0ull;
+  const bool scale = flag && !zero_before;   // rescaling a zero state is a no-op
+  if (act) {
+    cw[lane] = nonzero ? expf((float)(U - Rm - logD_next)) : 0.f;
+    rf[lane] = scale ? expf((float)(logD_before + ld)) : 1.f;   // zero: ld is -inf here
+  }
+  double gs = act ? g : 0.0;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) gs += __shfl_xor(gs, d);
+  c.m = __shfl(m_after, n - 1);
+  c.logD = __shfl(logD_next, n - 1);
+  c.G += gs;
+  c.reset = c.reset || __any(act && R >= 0);
+  c.zero = c.zero && nzmask == 0ull;
+  c.any_rescale = c.any_rescale || __any(scale);
+  return true;
+}
+
 __device__ LocScan local_scan(const SegArgs& a, int64_t bh, int64_t tile0, int ntiles, float* s_cw, float* s_rf) {
   const int lane = threadIdx.x & 63;
-  LocScan r{-INFINITY, 0.0, 0.0, false, false};
-  bool zero = true;
+  LocScan r;
   for (int base = 0; base < ntiles; base += 64) {
     const int n = min(64, ntiles - base);
     const int64_t t = bh * a.Nt + tile0 + base + min(lane, n - 1);
     const double gv = a.gb.g[t], Uv = a.gb.U[t];
     const int Rv = a.gb.R[t];
-    for (int j = 0; j < n; ++j) {
-      const double gj = readlane_f64(gv, j), Uj = readlane_f64(Uv, j);
-      const int Rj = __builtin_amdgcn_readlane(Rv, j);
-      const double Rm = fmax(Rj >= 0 ? -INFINITY : r.m, Uj);
-      const bool live = Rm != -INFINITY;
-      const double ld = (Rj >= 0 || r.m == -INFINITY || !live) ? -INFINITY : r.m - Rm;
-      const bool rescale = r.logD + ld < -kMaxDefer;
-      const double logD_next = rescale ? 0.0 : r.logD + ld;
-      const bool scale = rescale && !zero;   // rescaling a zero state is a no-op
-      if (lane == 0) {
-        s_cw[base + j] = (live && Uj != -INFINITY) ? expf((float)(Uj - Rm - logD_next)) : 0.f;
-        s_rf[base + j] = scale ? (float)exp(r.logD + ld) : 1.f;
-      }
-      r.any_rescale = r.any_rescale || scale;
-      r.m = live ? gj + Rm : -INFINITY;
-      r.logD = logD_next;
-      r.G += gj;
-      r.reset = r.reset || Rj >= 0;
-      if (live && Uj != -INFINITY) zero = false;
+    if (!local_scan_batch(gv, Uv, Rv, n, r, s_cw + base, s_rf + base)) {
+      for (int j = 0; j < n; ++j)
+        r.step(readlane_f64(gv, j), readlane_f64(Uv, j), __builtin_amdgcn_readlane(Rv, j), s_cw + base + j, s_rf + base + j);
     }
   }
   return r;
