@@ -226,6 +226,31 @@ def test_extreme_preactivations(dtype):
     assert rel_err(host(h), h_ref) <= TOL[dtype], "parallel"
 
 
+@pytest.mark.parametrize("K,V,T", [(128, 256, 700), (256, 128, 330)])
+def test_extreme_preactivations_fused(K, V, T):
+    """bf16 with d_v a multiple of 128 (the fused path): zero and saturated
+    forget gates, input gates jumping by 200, so that tiles reset, deferred
+    decays cross the deferral limit (accumulator rescales in the output pass
+    and the step-by-step fallback of the chunk-local scan), over several
+    chunks and a ragged last tile."""
+    M = _lib()
+    say(f"extreme preactivations fused K={K} V={V} T={T}")
+    rng = np.random.default_rng(11)
+    B, H = 1, 2
+    x = make_fwd_inputs(B, H, T, K, V, "bf16", seed=12)
+    x["i_pre"] = rng.choice([-100.0, 100.0, 0.0, 2.0, -3.0], size=(B, H, T)).astype(np.float32)
+    x["f_pre"] = rng.choice([-100.0, 100.0, np.inf, -np.inf, 3.0, 3.0, 3.0],
+                            size=(B, H, T)).astype(np.float32)
+    h_ref, st_ref = oracle(x)
+    d = dev_inputs(x)
+    for chunk in (64, 128, 192):
+        h, st = run_chunkwise(M, d, chunk, return_state=True)
+        assert bool(torch.isfinite(h.float()).all()), f"chunk {chunk}"
+        assert rel_err(host(h), h_ref) <= TOL["bf16"], f"chunk {chunk}"
+        ec, en = state_err(st, st_ref)
+        assert ec <= TOL["bf16"] and en <= TOL["bf16"], f"chunk {chunk}"
+
+
 def test_empty_sequence_copies_state():
     M = _lib()
     say("T=0")
