@@ -241,8 +241,8 @@ struct OutLds {
   static constexpr int infoBytes = 16;               // tile info: rescale flag (int), factor (float)
   static constexpr int bufBytes = nbBytes + wBytes + wbBytes + rowBytes + infoBytes;
   static constexpr int oBuf = oP + kTile * PP * 2;
-  static constexpr int oInv = oBuf + 2 * bufBytes;   // float [64] 1 / denominator of each row
-  static constexpr int oDen = oInv + kTile * 4;      // float [4][64] row sums of P per key group
+  static constexpr int oDnm = oBuf + 2 * bufBytes;   // float [64] denominator max(|n~^T q|, floor) of each row
+  static constexpr int oDen = oDnm + kTile * 4;      // float [4][64] row sums of P per key group
   static constexpr int oDn = oDen + 4 * kTile * 4;   // float [8][64] q . n~ partials per wave
   static constexpr int oX = oDn + kOutWaves * kTile * 4;     // f32x4 [8 waves][kXchg][64 lanes]
   static constexpr int oFin = oX + kOutWaves * kXchg * 64 * 16;   // double [2]: final m, logD
@@ -287,7 +287,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   const __bf16* sK = reinterpret_cast<const __bf16*>(smem + L::oK);
   __bf16* sV = reinterpret_cast<__bf16*>(smem + L::oV);
   __bf16* sP = reinterpret_cast<__bf16*>(smem + L::oP);
-  float* s_inv = reinterpret_cast<float*>(smem + L::oInv);
+  float* s_dnm = reinterpret_cast<float*>(smem + L::oDnm);
   float* s_den = reinterpret_cast<float*>(smem + L::oDen);
   float* s_dn = reinterpret_cast<float*>(smem + L::oDn);
   f32x4* s_x = reinterpret_cast<f32x4*>(smem + L::oX);
@@ -747,14 +747,14 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       }
     }
     lds_barrier();   // sP, s_den, s_dn complete
-    if (w == 0) {   // 1 / max(|n~^T q|, floor) of row t = lane
+    if (w == 0) {   // max(|n~^T q|, floor) of row t = lane
       const int t = fresh_lanes().lane;
       const float den = s_den[t] + s_den[kTile + t] + s_den[2 * kTile + t] + s_den[3 * kTile + t];
       float dn = 0.f;
 #pragma unroll
       for (int q = 0; q < NW; ++q) dn += s_dn[q * kTile + t];
       const float d = den + tb.sc[t] * dn;
-      s_inv[t] = __builtin_amdgcn_rcpf(fmaxf(fmaxf(fabsf(d), tb.fl[t]), FLT_MIN));
+      s_dnm[t] = fmaxf(fmaxf(fabsf(d), tb.fl[t]), FLT_MIN);
     }
     // ---------------- (P V)^T for the wave's rows; rows 0-31 have no keys
     // 32-63 (causal), so the half kh = 0 takes only the first 32 keys
@@ -775,7 +775,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
         copy_slot(3 + jb);
       }
     }
-    lds_barrier();   // s_inv complete
+    lds_barrier();   // s_dnm complete
     // ---------------- normaliser, output gate: per column half a lane forms
     // four consecutive columns of each of its two rows and stores them, paired
     // with its partner lane's, as 16-byte row pieces straight to H (the layout
@@ -783,9 +783,9 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     // are dropped
     {
       const Lanes le = fresh_lanes();
-      float inv[2];
+      float dnm[2];
 #pragma unroll
-      for (int z = 0; z < 2; ++z) inv[z] = s_inv[16 * zg(z) + le.i];
+      for (int z = 0; z < 2; ++z) dnm[z] = s_dnm[16 * zg(z) + le.i];
       bf16x8 hv[2];
 #pragma unroll
       for (int cv = 0; cv < 2; ++cv) {
@@ -794,8 +794,9 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
         for (int z = 0; z < 2; ++z) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float og = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-kLog2eF * (float)po[cv][z][r]));
-            h4[z][r] = (__bf16)(og * acc[z][cv][r] * inv[z]);
+            // sigmoid(o) / D = 1 / ((1 + e^-o) D)
+            const float e = __builtin_amdgcn_exp2f(-kLog2eF * (float)po[cv][z][r]);
+            h4[z][r] = (__bf16)(acc[z][cv][r] * __builtin_amdgcn_rcpf(fmaf(e, dnm[z], dnm[z])));
           }
         }
         swap_rows16(h4[1], h4[0]);
