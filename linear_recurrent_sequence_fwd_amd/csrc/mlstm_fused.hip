@@ -269,10 +269,9 @@ struct OutLds {
 // The tiles' decays are not applied to the accumulators one by one: the
 // registers hold X with C~ = exp(logD) X, n~ = exp(logD) Xn, new keys enter
 // with weight exp(u_j - Rm - logD_next), and X is rescaled only when logD
-// would fall below -kMaxDefer (or on a zero decay). RESCALE = false is the
-// variant for chunks where that never happens (checked up front from the gate
-// scalars alone); it holds no rescaling code.
-template <int K, bool RESCALE>
+// would fall below -kMaxDefer (or on a zero decay); the tile data carry a
+// flag for that, one scalar branch per tile.
+template <int K>
 __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   using L = OutLds<K>;
   constexpr int QP = L::QP, KP = L::KP, VP = L::VP, PP = L::PP;
@@ -643,17 +642,15 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
 
     // ---------------- state update: C~ <- decay C~ + K^T diag(w) V, n~ likewise
     // (Q C~^T above used the state at the start of the tile)
-    if constexpr (RESCALE) {
-      if (__builtin_amdgcn_readfirstlane(tb.info[0])) {   // uniform over the workgroup
-        const float f = __builtin_bit_cast(float, tb.info[1]);
+    if (__builtin_amdgcn_readfirstlane(tb.info[0])) {   // uniform over the workgroup
+      const float f = __builtin_bit_cast(float, tb.info[1]);
 #pragma unroll
-        for (int x = 0; x < KXH; ++x) {
-          Ct[x][0] *= f;
-          Ct[x][1] *= f;
-        }
-#pragma unroll
-        for (int x = 0; x < KXN; ++x) Nacc[x] *= f;
+      for (int x = 0; x < KXH; ++x) {
+        Ct[x][0] *= f;
+        Ct[x][1] *= f;
       }
+#pragma unroll
+      for (int x = 0; x < KXN; ++x) Nacc[x] *= f;
     }
 #pragma unroll
     for (int jb = 0; jb < kTile / 32; ++jb) {
@@ -852,58 +849,10 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   }
 }
 
-// True when some tile of the chunk would need the output kernel's
-// accumulators rescaled: the pending decay logD + ld falls below -kMaxDefer
-// while the state is not known to be zero. Follows the same float64 steps as
-// the tile loop, from the tile scalars only (lanes load 64 tiles at a time,
-// the scan runs on lane reads); the result is uniform over the workgroup.
-__device__ bool chunk_needs_rescale(const SegArgs& a, int64_t bh, int64_t tile0, int64_t tile1, double m, bool zero) {
-  const int lane = threadIdx.x & 63;
-  double logD = 0.0;
-  for (int64_t base = tile0; base < tile1; base += 64) {
-    const int n = (int)min((int64_t)64, tile1 - base);
-    const int64_t t = bh * a.Nt + base + min(lane, n - 1);
-    const double gv = a.gb.g[t], Uv = a.gb.U[t];
-    const int Rv = a.gb.R[t];
-    for (int j = 0; j < n; ++j) {
-      const double gj = readlane_f64(gv, j), Uj = readlane_f64(Uv, j);
-      const int Rj = __builtin_amdgcn_readlane(Rv, j);
-      double Rm = fmax(Rj >= 0 ? -INFINITY : m, Uj);
-      if (Rm == -INFINITY) Rm = 0.0;
-      const double ld = (Rj >= 0 || m == -INFINITY) ? -INFINITY : m - Rm;
-      if (logD + ld < -kMaxDefer) {
-        if (!zero) return true;
-        logD = 0.0;
-      } else {
-        logD += ld;
-      }
-      m = gj + Rm;
-      if (Uj != -INFINITY) zero = false;
-    }
-  }
-  return false;
-}
-
 template <int K>
 __global__ __launch_bounds__(64 * kOutWaves, 1) void out_kernel_fused(SegArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[OutLds<K>::bytes];
-  const int64_t bh = blockIdx.x % a.BH;
-  const int seg = (int)(blockIdx.x / a.BH / (a.V / kVB));
-  const int64_t tile0 = (int64_t)seg * a.TPS;
-  const int64_t tile1 = min(tile0 + a.TPS, a.Nt);
-  double m;
-  bool zero;
-  if (seg == 0) {
-    m = a.C0 ? (double)a.m0[bh] : 0.0;
-    zero = a.C0 == nullptr;
-  } else {
-    m = a.mstart[bh * (a.S - 1) + seg - 1];
-    zero = false;
-  }
-  if (chunk_needs_rescale(a, bh, tile0, tile1, m, zero))
-    out_body<K, true>(a, smem);
-  else
-    out_body<K, false>(a, smem);
+  out_body<K>(a, smem);
 }
 
 // ------------------------------------------------------------------ chunk-local end states
