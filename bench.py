@@ -250,6 +250,49 @@ def traffic_from_profile():
     return float(m_b.group(1))
 
 
+def measure_clock(torch, d, chunk, steps=20, iters=250):
+    """Shader clock (MHz) while the chunkwise forward runs. The probe wave sleeps
+    on a side stream (default priority) while `steps` forward calls run on the
+    current stream; its shader-clock ticks over its constant-rate ticks, times
+    that counter's rate, give the clock. The rate itself (nominally 100 MHz) is
+    taken from an event-timed probe run alone, whose own clock is reported as
+    the idle figure. iters = 250 sleeps last about 1 ms, well inside the
+    forward calls."""
+    from linear_recurrent_sequence_fwd_amd import _lib
+    ticks = torch.zeros(4, dtype=torch.int64, device="cuda")
+    # rate of the constant counter, and the clock with nothing else running
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    _lib.clock_probe(ticks, iters)
+    e0.record()
+    _lib.clock_probe(ticks, iters)
+    e1.record()
+    torch.cuda.synchronize()
+    t = ticks.cpu().tolist()
+    rt_mhz = (t[3] - t[2]) / (e0.elapsed_time(e1) * 1e3)
+    idle_mhz = (t[1] - t[0]) / (t[3] - t[2]) * rt_mhz
+    # the clock under the forward pass
+    h = torch.empty_like(d["v"])
+    args = _lib.fwd_args(d["q"], d["k"], d["v"], d["o_pre"], d["i_pre"], d["f_pre"], h)
+    nbytes = _lib.chunkwise_workspace_bytes(args, chunk)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    main_stream = torch.cuda.current_stream()
+    stream = ctypes.c_void_p(main_stream.cuda_stream)
+    lib, pargs, wsp = _lib.lib(), ctypes.byref(args), ws.data_ptr()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        _lib.clock_probe(ticks, iters)
+    for _ in range(steps):
+        code = lib.mlstm_fwd_chunkwise(pargs, chunk, wsp, nbytes, stream)
+        if code:
+            raise RuntimeError(lib.mlstm_last_error().decode())
+    torch.cuda.synchronize()
+    t = ticks.cpu().tolist()
+    load_mhz = (t[1] - t[0]) / (t[3] - t[2]) * rt_mhz
+    return {"under_load_mhz": load_mhz, "idle_mhz": idle_mhz, "realtime_counter_mhz": rt_mhz,
+            "method": "s_memtime over s_memrealtime of one sleeping wave beside the forward calls"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -329,6 +372,10 @@ def main():
                          "kernel_us": {LABELS[k]: v for k, v in pk.items()}}
         log(f"[bench] sweep chunk={L}: {el / st * 1e3:.3f} ms/step")
 
+    clock = measure_clock(torch, d, args.chunk)
+    log(f"[bench] shader clock during the forward: {clock['under_load_mhz']:.0f} MHz "
+        f"(idle {clock['idle_mhz']:.0f} MHz, constant counter {clock['realtime_counter_mhz']:.1f} MHz)")
+
     out = {
         "metric": METRIC,
         "value": tok_s,
@@ -352,6 +399,7 @@ def main():
         "kernel_us": per_k,
         "roofline": roof,
         "sweep": sweep,
+        "clock": clock,
     }
     del d
     torch.cuda.empty_cache()

@@ -160,6 +160,20 @@ int mlstm_abi_version(void);
  */
 int mlstm_set_launch_events(int kernel_id, void* before, void* after);
 
+/*
+ * Measurement helper, not needed for computing: the shader clock while other
+ * work runs. Launches one wave that sleeps `iters` times s_sleep 127 (about
+ * 8k shader cycles each; iters in [1, 2^24]) and writes the shader-clock
+ * counter (s_memtime) at its start and end to ticks[0], ticks[1], and the
+ * constant-rate counter (s_memrealtime) to ticks[2], ticks[3]: four uint64 in
+ * caller-owned, 8-byte-aligned device memory. Launched on a second stream
+ * just before a workload, the ratio of the two differences times the
+ * constant counter's rate is the clock under that workload. Asynchronous on
+ * `stream`; returns MLSTM_ERR_NULLPTR, MLSTM_ERR_BAD_SHAPE or
+ * MLSTM_ERR_MISALIGNED on bad arguments before anything is enqueued.
+ */
+int mlstm_clock_probe(unsigned long long* ticks, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.mlstm_abi_version.restype = c_int
         L.mlstm_set_launch_events.argtypes = [c_int, c_void_p, c_void_p]
         L.mlstm_set_launch_events.restype = c_int
+        L.mlstm_clock_probe.argtypes = [c_void_p, c_int, c_void_p]
+        L.mlstm_clock_probe.restype = c_int
         _lib = L
     return _lib
 
@@ -244,3 +246,11 @@ def mlstm_step(q, k, v, o_pre, i_pre, f_pre, C, n_in, m_in, n_out=None, m_out=No
 def set_launch_events(kernel: str, before, after) -> None:
     """Bracket every later launch of `kernel` with the given hipEvent_t handles (ints or None)."""
     _check(lib().mlstm_set_launch_events(KERNEL_IDS[kernel], before, after), "mlstm_set_launch_events")
+
+
+def clock_probe(ticks, iters: int, stream=None) -> None:
+    """Launch the clock probe; `ticks` is a 4-element int64 CUDA tensor that receives
+    the shader-clock counter (start, end) and the constant-rate counter (start, end)."""
+    import torch
+    _require(ticks, "ticks", (4,), torch.int64)
+    _check(lib().mlstm_clock_probe(_ptr(ticks), int(iters), _stream(stream)), "mlstm_clock_probe")

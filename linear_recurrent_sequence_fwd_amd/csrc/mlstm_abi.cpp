@@ -367,6 +367,13 @@ const char* mlstm_last_error(void) { return g_last_error.c_str(); }
 
 int mlstm_abi_version(void) { return MLSTM_ABI_VERSION; }
 
+int mlstm_clock_probe(unsigned long long* ticks, int iters, void* stream) {
+  if (!ticks) return fail(MLSTM_ERR_NULLPTR, "ticks is required");
+  if (iters < 1 || iters > (1 << 24)) return fail(MLSTM_ERR_BAD_SHAPE, "iters must be in [1, 2^24]");
+  if (reinterpret_cast<uintptr_t>(ticks) % 8) return fail(MLSTM_ERR_MISALIGNED, "ticks must be 8-byte aligned");
+  return hip_status(mlstm_impl::launch_clock_probe(ticks, iters, static_cast<hipStream_t>(stream)), "clock probe");
+}
+
 int mlstm_set_launch_events(int kernel_id, void* before, void* after) {
   if (kernel_id < 0 || kernel_id >= mlstm_impl::K_COUNT)
     return fail(MLSTM_ERR_BAD_SHAPE, "kernel_id must be 0..3");

@@ -806,6 +806,29 @@ hipError_t launch_copy_state(const FwdLaunch& f, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Clock probe: one wave that sleeps `iters` times s_sleep 127 (about 8k
+// shader cycles each) and records the shader-clock counter (s_memtime) and
+// the constant-rate counter (s_memrealtime) before and after. Launched beside
+// other work, the two differences give the shader clock under that work.
+__global__ __launch_bounds__(64) void clock_probe_kernel(unsigned long long* ticks, int iters) {
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) __builtin_amdgcn_s_sleep(127);
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    ticks[0] = t0;
+    ticks[1] = t1;
+    ticks[2] = r0;
+    ticks[3] = r1;
+  }
+}
+
+hipError_t launch_clock_probe(unsigned long long* ticks, int iters, hipStream_t s) {
+  hipLaunchKernelGGL(clock_probe_kernel, dim3(1), dim3(64), 0, s, ticks, iters);
+  return hipGetLastError();
+}
+
 hipError_t launch_step(const StepLaunch& st, hipStream_t s) {
 #define MLSTM_STEP_CASE(KK)                                        \
   case KK:                                                         \

@@ -88,6 +88,9 @@ hipError_t launch_out(const FwdLaunch& a, const GateBuffers& gb, const ChunkStat
 // T == 0: final state = initial state (or zero).
 hipError_t launch_copy_state(const FwdLaunch& a, hipStream_t s);
 hipError_t launch_step(const StepLaunch& a, hipStream_t s);
+// one sleeping wave; ticks[0..1]: shader-clock counter, ticks[2..3]:
+// constant-rate counter, at its start and end
+hipError_t launch_clock_probe(unsigned long long* ticks, int iters, hipStream_t s);
 
 // bfloat16 kernels with transposed LDS operand loads (mlstm_bf16.hip). The
 // state pass takes any d_v multiple of 64; the output kernel needs

@@ -250,3 +250,11 @@ def test_launch_event_hook_validation():
     lib = L.lib()
     assert lib.mlstm_set_launch_events(9, None, None) == BAD_SHAPE
     assert lib.mlstm_set_launch_events(2, None, None) == OK
+
+
+def test_clock_probe_validation():
+    lib = L.lib()
+    assert lib.mlstm_clock_probe(None, 100, None) == NULLPTR
+    assert lib.mlstm_clock_probe(0x7D0000000000, 0, None) == BAD_SHAPE
+    assert lib.mlstm_clock_probe(0x7D0000000000, 1 << 25, None) == BAD_SHAPE
+    assert lib.mlstm_clock_probe(0x7D0000000004, 100, None) == MISALIGNED

@@ -410,3 +410,23 @@ def test_chunkwise_prefill_then_steps():
     assert rel_err(h, h_ref) <= TOL["bf16"]
     ec, en = state_err((C, n, m), st_ref)
     assert ec <= TOL["bf16"] and en <= TOL["bf16"]
+
+
+def test_clock_probe_reads_a_plausible_clock():
+    """The measurement helper: both counters advance, the constant-rate counter
+    runs at about its nominal 100 MHz against HIP events, and the shader clock
+    it implies lies between 0.5 and 3 GHz."""
+    from linear_recurrent_sequence_fwd_amd import _lib as L
+    ticks = torch.zeros(4, dtype=torch.int64, device="cuda")
+    L.clock_probe(ticks, 50)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    L.clock_probe(ticks, 250)
+    e1.record()
+    torch.cuda.synchronize()
+    t = ticks.cpu().tolist()
+    assert t[1] > t[0] and t[3] > t[2]
+    rt_mhz = (t[3] - t[2]) / (e0.elapsed_time(e1) * 1e3)
+    assert 80.0 < rt_mhz < 120.0, rt_mhz
+    mhz = (t[1] - t[0]) / (t[3] - t[2]) * rt_mhz
+    assert 500.0 < mhz < 3000.0, mhz
