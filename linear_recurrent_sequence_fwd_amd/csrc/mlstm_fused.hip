@@ -16,12 +16,16 @@
 //                      start state of every chunk (elementwise, float32).
 //   out_kernel_fused   one workgroup per (head, 128 value columns, chunk).
 //                      Holds its 128 x d_qk slice of C~ (float32) in MFMA
-//                      accumulators and walks the chunk in 64-token tiles.
-//                      Per tile: Q K^T on MFMA, decay mask and stabiliser in
-//                      registers, P V and Q C~^T on MFMA, normaliser and output
-//                      gate, then C~ <- a C~ + K^T diag(w) V on MFMA and the
+//                      accumulators, split over its waves by halves of d_qk
+//                      and 32-column groups, and walks the chunk in 64-token
+//                      tiles. Per tile: Q K^T and Q C~^T on MFMA (partial sums
+//                      over each half of d_qk, exchanged through LDS), the
+//                      state update C~ <- a C~ + K^T diag(w) V on MFMA and the
 //                      same for n~ (a two-column MFMA tile carrying the weights
-//                      as bf16 hi + lo).
+//                      as bf16 hi + lo), decay mask and stabiliser in
+//                      registers, P V on MFMA, normaliser and output gate.
+//                      q, k and v reach LDS by direct-to-LDS copies issued one
+//                      tile ahead.
 //
 // Chunks are independent given their start states, so the sequence dimension
 // supplies the parallelism that the few heads of a large layer lack.
