@@ -282,7 +282,6 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   constexpr int KH = K / 2;                                    // d_qk rows per half
   constexpr int KSH = KH / 32;                                 // 32-deep steps per half
   constexpr int KXH = KH / 16;                                 // 16-row state tiles per half
-  constexpr int KS = K / 32;                                   // 32-deep steps over d_qk
   constexpr int NW = kOutWaves;
   constexpr int KXN = KXH >= 4 ? KXH / 4 : 1;                  // normaliser tiles per wave
   static_assert(KSH >= 1 && KXH % 2 == 0, "d_qk halves of whole 32-deep steps");
@@ -594,12 +593,19 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       acc[z][0] = acc[z][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const Lanes l1 = fresh_lanes();
+    // Q fragments of the wave's q . n~ step: its local step cg of d_qk (a wave
+    // with cg >= KSH has no such step; it keeps the last one, unused)
+    bf16x8 fq[4];
     unroll<KSH>([&](auto s_c) {
       constexpr int s = decltype(s_c)::value;
       const int col = KH * kh + 32 * s + 8 * l1.g;
       bf16x8 fa[4];
 #pragma unroll
       for (int z = 0; z < 4; ++z) fa[z] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * zg(z) + l1.i) * QP + col]);
+      if (s == min(cg, KSH - 1)) {
+#pragma unroll
+        for (int z = 0; z < 4; ++z) fq[z] = fa[z];
+      }
       const bf16x8 fk = *reinterpret_cast<const bf16x8*>(&sK[(16 * kg + l1.i) * KP + col]);
 #pragma unroll
       for (int z = 0; z < 4; ++z) sacc[z] = mma(fk, fa[z], sacc[z]);
@@ -621,26 +627,25 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       xo[256] = sacc[2];
       xo[320] = sacc[3];
     }
-    // ---------------- q . n~: wave w takes the 32-deep step s = w of d_qk
+    // ---------------- q . n~: the wave with cg < KSH takes the 32-deep step
+    // KSH kh + cg of d_qk for all rows (register group z: rows 16 zg(z) ..),
+    // the others contribute zeros
     {
       const Lanes ln = fresh_lanes();
       f32x4 dacc[4];
 #pragma unroll
       for (int z = 0; z < 4; ++z) dacc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (w < KS) {
-        const bf16x8 Bn = *reinterpret_cast<const bf16x8*>(&tb.nb[min(ln.i, 2) * K + 32 * w + 8 * ln.g]);
+      if (cg < KSH) {
+        const bf16x8 Bn = *reinterpret_cast<const bf16x8*>(&tb.nb[min(ln.i, 2) * K + KH * kh + 32 * cg + 8 * ln.g]);
 #pragma unroll
-        for (int z = 0; z < 4; ++z) {
-          const bf16x8 fa = *reinterpret_cast<const bf16x8*>(&sQ[(16 * z + ln.i) * QP + 32 * w + 8 * ln.g]);
-          dacc[z] = mma(fa, Bn, dacc[z]);
-        }
+        for (int z = 0; z < 4; ++z) dacc[z] = mma(fq[z], Bn, dacc[z]);
       }
 #pragma unroll
       for (int z = 0; z < 4; ++z) {
         f32x4 d;
 #pragma unroll
         for (int r = 0; r < 4; ++r) d[r] = sum_xor1(dacc[z][r]);
-        if (ln.i == 0) *reinterpret_cast<f32x4*>(&s_dn[w * kTile + 16 * z + 4 * ln.g]) = d;
+        if (ln.i == 0) *reinterpret_cast<f32x4*>(&s_dn[w * kTile + 16 * zg(z) + 4 * ln.g]) = d;
       }
     }
 
