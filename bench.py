@@ -164,6 +164,40 @@ def time_chunkwise(torch, M, L, ev, d, chunk, steps, warmup, kernels=("gate", "s
     return elapsed, per_kernel
 
 
+def time_chunkwise_graph(torch, d, chunk, steps, warmup):
+    """Wall time of `steps` replays of a HIP graph holding one forward call (its
+    four kernel launches), captured on torch's capture stream."""
+    from linear_recurrent_sequence_fwd_amd import _lib
+    h = torch.empty_like(d["v"])
+    args = _lib.fwd_args(d["q"], d["k"], d["v"], d["o_pre"], d["i_pre"], d["f_pre"], h)
+    nbytes = _lib.chunkwise_workspace_bytes(args, chunk)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    lib, pargs, wsp = _lib.lib(), ctypes.byref(args), ws.data_ptr()
+
+    def one():
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        code = lib.mlstm_fwd_chunkwise(pargs, chunk, wsp, nbytes, stream)
+        if code:
+            raise RuntimeError(lib.mlstm_last_error().decode())
+
+    one()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        one()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    del g
+    return elapsed
+
+
 def time_decode(torch, M, ev, steps, warmup):
     from linear_recurrent_sequence_fwd_amd.inputs import make_step_inputs
     cfg = DECODE
@@ -372,6 +406,9 @@ def main():
                          "kernel_us": {LABELS[k]: v for k, v in pk.items()}}
         log(f"[bench] sweep chunk={L}: {el / st * 1e3:.3f} ms/step")
 
+    g_el = time_chunkwise_graph(torch, d, args.chunk, args.steps, args.warmup)
+    log(f"[bench] chunkwise as a replayed HIP graph: {g_el / args.steps * 1e3:.3f} ms/step")
+
     clock = measure_clock(torch, d, args.chunk)
     log(f"[bench] shader clock during the forward: {clock['under_load_mhz']:.0f} MHz "
         f"(idle {clock['idle_mhz']:.0f} MHz, constant counter {clock['realtime_counter_mhz']:.1f} MHz)")
@@ -400,6 +437,7 @@ def main():
         "roofline": roof,
         "sweep": sweep,
         "clock": clock,
+        "graph_ms_per_step": g_el / args.steps * 1e3,
     }
     del d
     torch.cuda.empty_cache()

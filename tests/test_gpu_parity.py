@@ -5,6 +5,7 @@ inputs and 2e-2 for bfloat16 inputs; every output finite. States are
 compared in true units (exp(m) C~), relative to the oracle's largest entry.
 Outputs are pre-filled with NaN so that an unwritten element fails.
 """
+import ctypes
 import sys
 
 import numpy as np
@@ -410,6 +411,42 @@ def test_chunkwise_prefill_then_steps():
     assert rel_err(h, h_ref) <= TOL["bf16"]
     ec, en = state_err((C, n, m), st_ref)
     assert ec <= TOL["bf16"] and en <= TOL["bf16"]
+
+
+def test_chunkwise_graph_replays_match_eager():
+    """The fused forward captured in a HIP graph (no memsets or host syncs in the
+    path): three replays, with eager launches and synchronisations between them,
+    each equal bit for bit to the eager result."""
+    M = _lib()
+    say("graph replay")
+    from linear_recurrent_sequence_fwd_amd import _lib as L
+    x = make_fwd_inputs(1, 2, 1000, 128, 256, "bf16", seed=21)
+    d = dev_inputs(x)
+    ref = run_chunkwise(M, d, 128)
+    h = torch.empty_like(d["v"])
+    args = L.fwd_args(d["q"], d["k"], d["v"], d["o_pre"], d["i_pre"], d["f_pre"], h)
+    nbytes = L.chunkwise_workspace_bytes(args, 128)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    lib = L.lib()
+
+    def one():
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        assert lib.mlstm_fwd_chunkwise(ctypes.byref(args), 128, ws.data_ptr(), nbytes, stream) == 0
+
+    one()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        one()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        h.zero_()
+        other = run_chunkwise(M, d, 64)        # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(h, ref), f"replay {rep}"
+        assert other.shape == ref.shape
 
 
 def test_clock_probe_reads_a_plausible_clock():
