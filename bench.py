@@ -338,6 +338,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the replayed-graph timing")
+    ap.add_argument("--no-clock", action="store_true", help="skip the shader clock measurement")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -406,12 +408,17 @@ def main():
                          "kernel_us": {LABELS[k]: v for k, v in pk.items()}}
         log(f"[bench] sweep chunk={L}: {el / st * 1e3:.3f} ms/step")
 
-    g_el = time_chunkwise_graph(torch, d, args.chunk, args.steps, args.warmup)
-    log(f"[bench] chunkwise as a replayed HIP graph: {g_el / args.steps * 1e3:.3f} ms/step")
+    graph_ms = None
+    if not args.no_graph:
+        g_el = time_chunkwise_graph(torch, d, args.chunk, args.steps, args.warmup)
+        graph_ms = g_el / args.steps * 1e3
+        log(f"[bench] chunkwise as a replayed HIP graph: {graph_ms:.3f} ms/step")
 
-    clock = measure_clock(torch, d, args.chunk)
-    log(f"[bench] shader clock during the forward: {clock['under_load_mhz']:.0f} MHz "
-        f"(idle {clock['idle_mhz']:.0f} MHz, constant counter {clock['realtime_counter_mhz']:.1f} MHz)")
+    clock = None
+    if not args.no_clock:
+        clock = measure_clock(torch, d, args.chunk)
+        log(f"[bench] shader clock during the forward: {clock['under_load_mhz']:.0f} MHz "
+            f"(idle {clock['idle_mhz']:.0f} MHz, constant counter {clock['realtime_counter_mhz']:.1f} MHz)")
 
     out = {
         "metric": METRIC,
@@ -437,7 +444,7 @@ def main():
         "roofline": roof,
         "sweep": sweep,
         "clock": clock,
-        "graph_ms_per_step": g_el / args.steps * 1e3,
+        "graph_ms_per_step": graph_ms,
     }
     del d
     torch.cuda.empty_cache()
