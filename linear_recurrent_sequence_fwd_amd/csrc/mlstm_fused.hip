@@ -73,6 +73,25 @@ __device__ __forceinline__ bf16x8 frag_trk(const __bf16* X, int P, int kin0, int
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// frag_trk in two parts: lane_off_trk is the lane's element offset for tile
+// kx0 (even) at kin0 = 0, passed through an empty asm statement so that the
+// compiler keeps it whole; frag_trk_at adds the constant part of tile kx0 + x
+// at kin0. Each read address is then one step from the array X, which lets
+// the compiler tell which LDS array a read touches (and not wait for copies
+// in flight into other arrays).
+__device__ __forceinline__ int lane_off_trk(int P, int kx0, int lane) {
+  const int i = lane & 15, g = lane >> 4;
+  int off = (8 * g + (i >> 2)) * P + 16 * kx0 + 8 * (i & 3);
+  asm("" : "+v"(off));
+  return off;
+}
+__device__ __forceinline__ bf16x8 frag_trk_at(const __bf16* X, int off, int P, int kin0, int x) {
+  const __bf16* p = X + off + (kin0 * P + 32 * (x >> 1) + 4 * (x & 1));
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * P));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Offset along d_qk of the four consecutive k that lane group g holds in
 // register tile kx of the state (see frag_trk).
 __device__ __forceinline__ int state_k0(int kx, int g) { return 32 * (kx >> 1) + 8 * g + 4 * (kx & 1); }
@@ -217,9 +236,11 @@ __device__ __forceinline__ void swap_rows16(bf16x4& x1, bf16x4& x0) {
 }
 
 // LDS of the output kernel. Q, K and V arrive by direct-to-LDS copies that
-// the compute waves issue in the second half of the previous tile, once the
-// tile's reads of the single buffers are over; O is read into registers and H
-// written from registers. The tile's per-key and per-row data and the
+// the compute waves issue in the second half of the previous tile, each once
+// the tile's reads of its single buffer are over (Q and V after the exchange
+// barrier, K after the one that ends the state update); O is read into
+// registers and H written from registers. Q, K and V are arrays of their own
+// so that reads of one need not wait for copies in flight into another. The tile's per-key and per-row data and the
 // normaliser operand are double-buffered: waves 0-3 prepare tile tau + 1's
 // copy at the end of tile tau. The exchange area carries the partial sums that
 // the two waves of a value-column group (one per half of d_qk) hand each other.
@@ -233,10 +254,8 @@ struct OutLds {
   static constexpr int kBytes = kTile * KP * 2;
   static constexpr int vBytes = kTile * VP * 2;
   static constexpr int kXchg = 6;                    // f32x4 registers a wave hands its partner
-  static constexpr int oQ = 0;
-  static constexpr int oK = oQ + qBytes;
-  static constexpr int oV = oK + kBytes;
-  static constexpr int oP = oV + vBytes;
+  // sQ, sK and sV are arrays of their own; the rest shares one array at these offsets
+  static constexpr int oP = 0;
   // double-buffered tile data, [2] of:
   static constexpr int nbBytes = 3 * K * 2;          // bf16 [3][K]: n~ hi, lo, zero
   static constexpr int wBytes = kTile * 4;           // float [64] key weights
@@ -250,7 +269,8 @@ struct OutLds {
   static constexpr int oDn = oDen + 4 * kTile * 4;   // float [8][64] q . n~ partials per wave
   static constexpr int oX = oDn + kOutWaves * kTile * 4;     // f32x4 [8 waves][kXchg][64 lanes]
   static constexpr int oFin = oX + kOutWaves * kXchg * 64 * 16;   // double [2]: final m, logD
-  static constexpr int bytes = oFin + 16;
+  static constexpr int restBytes = oFin + 16;
+  static_assert(qBytes + kBytes + vBytes + restBytes <= 160 * 1024, "fits the LDS of a CU");
 };
 
 // Wave w = 4 kh + cg owns value columns [32 cg, 32 cg + 32) of the
@@ -276,7 +296,7 @@ struct OutLds {
 // would fall below -kMaxDefer (or on a zero decay); the tile data carry a
 // flag for that, one scalar branch per tile.
 template <int K>
-__device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
+__device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, char* lv, char* smem) {
   using L = OutLds<K>;
   constexpr int QP = L::QP, KP = L::KP, VP = L::VP, PP = L::PP;
   constexpr int KH = K / 2;                                    // d_qk rows per half
@@ -285,9 +305,9 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   constexpr int NW = kOutWaves;
   constexpr int KXN = KXH >= 4 ? KXH / 4 : 1;                  // normaliser tiles per wave
   static_assert(KSH >= 1 && KXH % 2 == 0, "d_qk halves of whole 32-deep steps");
-  __bf16* sQ = reinterpret_cast<__bf16*>(smem + L::oQ);
-  const __bf16* sK = reinterpret_cast<const __bf16*>(smem + L::oK);
-  __bf16* sV = reinterpret_cast<__bf16*>(smem + L::oV);
+  __bf16* sQ = reinterpret_cast<__bf16*>(lq);
+  const __bf16* sK = reinterpret_cast<const __bf16*>(lk);
+  __bf16* sV = reinterpret_cast<__bf16*>(lv);
   __bf16* sP = reinterpret_cast<__bf16*>(smem + L::oP);
   float* s_dnm = reinterpret_cast<float*>(smem + L::oDnm);
   float* s_den = reinterpret_cast<float*>(smem + L::oDen);
@@ -387,7 +407,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   using DK = DmaTile<KP, NW>;
   using DV = DmaTile<VP, NW>;
   constexpr int RQ = DQ::kRounds, RK = DK::kRounds, RV = DV::kRounds;
-  // five issue slots after the barrier that ends the tile's reads of Q, K, V
+  // five issue slots each: Q and V after the barrier that ends their reads, K after the one that ends its reads
   static_assert(RK <= 5 && RQ <= 5 && RV <= 5, "copy rounds fit their slots");
   // Per-lane source offsets of this wave's copy rounds for a full tile,
   // computed once; a ragged last tile recomputes them with its rows clamped.
@@ -405,7 +425,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     const unsigned last = last_row(tau);
     const auto src = buffer_rsrc(a.q + (bh * T + tau * kTile) * K, (last + 1) * (unsigned)K * 2u);
     const int n = DQ::load(w, r);
-    char* dst = smem + L::oQ + 1024 * n;
+    char* dst = lq + 1024 * n;
     if (last == kTile - 1) dma_issue(src, offQ[r], dst);
     else dma_issue(src, dma_src_off<K, QP>(n, (unsigned)fresh_lanes().lane, (unsigned)K, last), dst);
   };
@@ -413,7 +433,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     const unsigned last = last_row(tau);
     const auto src = buffer_rsrc(a.k + (bh * T + tau * kTile) * K, (last + 1) * (unsigned)K * 2u);
     const int n = DK::load(w, r);
-    char* dst = smem + L::oK + 1024 * n;
+    char* dst = lk + 1024 * n;
     if (last == kTile - 1) dma_issue(src, offK[r], dst);
     else dma_issue(src, dma_src_off<K, KP>(n, (unsigned)fresh_lanes().lane, (unsigned)K, last), dst);
   };
@@ -421,7 +441,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     const unsigned last = last_row(tau);
     const auto src = buffer_rsrc(a.v + (bh * T + tau * kTile) * V + vcol0, (last * (unsigned)V + kVB) * 2u);
     const int n = DV::load(w, r);
-    char* dst = smem + L::oV + 1024 * n;
+    char* dst = lv + 1024 * n;
     if (last == kTile - 1) dma_issue(src, offV[r], dst);
     else dma_issue(src, dma_src_off<kVB, VP>(n, (unsigned)fresh_lanes().lane, (unsigned)V, last), dst);
   };
@@ -436,6 +456,14 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   // stores past it are dropped.
   bf16x4 po[2][2];
   unsigned offO[2];
+  // The epilogue of tile tau (normaliser, output gate, H stores) runs in tile
+  // tau + 1: its arithmetic beside the first matrix phase, its two stores
+  // once that tile's loaded registers are taken. It needs the tile's H^T
+  // accumulators of the wave's own rows (eacc), its O (epo) and the row
+  // denominators s_dnm, which are rewritten only after the exchange barrier.
+  f32x4 eacc[2][2];
+  bf16x4 epo[2][2];
+  bf16x8 hv[2];
 #pragma unroll
   for (int cv = 0; cv < 2; ++cv) {
     const unsigned t = 16 * zg((g & 1) ? 0 : 1) + i;
@@ -468,8 +496,10 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
   };
 
   // n~ of the next tile as bf16 hi + lo in the fragment order of sQ (every
-  // wave its own tiles)
-  auto put_n = [&](const TileBuf& tb) {
+  // wave its own tiles) into half b of the tile data. The byte offset is kept
+  // whole (empty asm statement), so that each store is one step from the
+  // array and the compiler can tell it from the copies in flight.
+  auto put_n = [&](int b) {
     const Lanes ln = fresh_lanes();
 #pragma unroll
     for (int x = 0; x < KXN; ++x) {
@@ -482,10 +512,11 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
           hi4[r] = hi;
           lo4[r] = (__bf16)(nr - (float)hi);
         }
-        const int pos = state_k0(kxg(nx(x)), ln.g);
+        int off = L::oBuf + b * L::bufBytes + 2 * state_k0(kxg(nx(x)), ln.g);
+        asm("" : "+v"(off));
         if (ln.i == 0) {
-          *reinterpret_cast<bf16x4*>(&tb.nb[pos]) = hi4;
-          *reinterpret_cast<bf16x4*>(&tb.nb[K + pos]) = lo4;
+          *reinterpret_cast<bf16x4*>(smem + off) = hi4;
+          *reinterpret_cast<bf16x4*>(smem + off + 2 * K) = lo4;
         }
       }
     }
@@ -509,7 +540,9 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       tb.w[j] = wj;
       const __bf16 whi = (__bf16)wj;
       tb.wb[j] = whi;
-      tb.wb[kTile + j] = (__bf16)(wj - (float)whi);
+      int jl = kTile + j;   // kept whole: one step from the array (see put_n)
+      asm("" : "+v"(jl));
+      tb.wb[jl] = (__bf16)(wj - (float)whi);
       if (j == 0) {
         tb.info[0] = rescale ? 1 : 0;
         tb.info[1] = __builtin_bit_cast(int, rescale ? expf((float)(logD + ld)) : 1.f);   // below e^-70
@@ -543,6 +576,43 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     m = t_g + Rm;
   };
 
+  // ---------------- epilogue: per column half a lane forms four consecutive
+  // columns of each of its two rows and stores them, paired with its partner
+  // lane's, as 16-byte row pieces straight to H (the layout of load_o); rows
+  // past the sequence end fall outside the buffer range and are dropped
+  auto epi_math = [&]() {
+    const Lanes le = fresh_lanes();
+    float dnm[2];
+#pragma unroll
+    for (int z = 0; z < 2; ++z) dnm[z] = s_dnm[16 * zg(z) + le.i];
+#pragma unroll
+    for (int cv = 0; cv < 2; ++cv) {
+      bf16x4 h4[2];
+#pragma unroll
+      for (int z = 0; z < 2; ++z) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // sigmoid(o) / D = 1 / ((1 + e^-o) D)
+          const float e = __builtin_amdgcn_exp2f(-kLog2eF * (float)epo[cv][z][r]);
+          h4[z][r] = (__bf16)(eacc[z][cv][r] * __builtin_amdgcn_rcpf(fmaf(e, dnm[z], dnm[z])));
+        }
+      }
+      swap_rows16(h4[1], h4[0]);
+      hv[cv] = __builtin_shufflevector(h4[1], h4[0], 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  auto epi_store = [&](int64_t te) {
+    const __amdgpu_buffer_rsrc_t hr = tile_rsrc_vo(a.h, te);
+#pragma unroll
+    for (int cv = 0; cv < 2; ++cv) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hv[cv]), hr, (int)offO[cv], 0, 0);
+  };
+#pragma unroll
+  for (int cv = 0; cv < 2; ++cv) {
+    epo[cv][0] = epo[cv][1] = bf16x4{};
+    eacc[0][cv] = eacc[1][cv] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (tid < kTile) s_dnm[tid] = 1.f;   // read (unused) by the first tile's epilogue pass
+
   for (int r = 0; r < RK; ++r) dma_k(tile0, r);
   for (int r = 0; r < RQ; ++r) dma_q(tile0, r);
   for (int r = 0; r < RV; ++r) dma_v(tile0, r);
@@ -551,7 +621,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     prep(tile0, tile_buf(0), m_chain, logD_chain, has_state);
     advance(m_chain, logD_chain);
   }
-  put_n(tile_buf(0));
+  put_n(0);
   __builtin_amdgcn_s_waitcnt(0);
   for (int64_t tau = tile0; tau < tile1; ++tau) {
     const int64_t t0 = tau * kTile;
@@ -569,20 +639,10 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     // reads any more), so that every wave issues the same memory operations on
     // every tile and the compiler's waits for loaded registers are exact.
     const int64_t tn = more ? tau + 1 : tau;
-    // V^T fragments of P V and of the state update (columns 32 cg + 16 cv).
-    // The tile's transposed LDS reads all come before its copies are issued:
-    // such a read waits for every direct-to-LDS load of the wave in flight.
-    bf16x8 Av[kTile / 32][2];
-    {
-      const Lanes lv = fresh_lanes();
-#pragma unroll
-      for (int jb = 0; jb < kTile / 32; ++jb)
-#pragma unroll
-        for (int cv = 0; cv < 2; ++cv) Av[jb][cv] = frag_tr(sV, VP, 32 * jb, 32 * cg + 16 * cv, lv.lane);
-    }
     if (w < 4) load_gate(tn);   // consumed by the preparation of tile tau + 1 at the end of this one
     load_o(tau, 0);
     load_o(tau, 1);
+    epi_math();   // the previous tile's (on the first tile a pass whose result is dropped)
 
     // ---------------- partial Q K^T (16 keys x 64 rows) and (Q C~^T)^T (32
     // columns x 64 rows) over this wave's half of d_qk
@@ -593,19 +653,12 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       acc[z][0] = acc[z][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     const Lanes l1 = fresh_lanes();
-    // Q fragments of the wave's q . n~ step: its local step cg of d_qk (a wave
-    // with cg >= KSH has no such step; it keeps the last one, unused)
-    bf16x8 fq[4];
     unroll<KSH>([&](auto s_c) {
       constexpr int s = decltype(s_c)::value;
       const int col = KH * kh + 32 * s + 8 * l1.g;
       bf16x8 fa[4];
 #pragma unroll
       for (int z = 0; z < 4; ++z) fa[z] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * zg(z) + l1.i) * QP + col]);
-      if (s == min(cg, KSH - 1)) {
-#pragma unroll
-        for (int z = 0; z < 4; ++z) fq[z] = fa[z];
-      }
       const bf16x8 fk = *reinterpret_cast<const bf16x8*>(&sK[(16 * kg + l1.i) * KP + col]);
 #pragma unroll
       for (int z = 0; z < 4; ++z) sacc[z] = mma(fk, fa[z], sacc[z]);
@@ -627,6 +680,16 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       xo[256] = sacc[2];
       xo[320] = sacc[3];
     }
+    // V^T fragments of P V and of the state update (columns 32 cg + 16 cv),
+    // read before the copies into sV are issued
+    bf16x8 Av[kTile / 32][2];
+    {
+      const Lanes lv = fresh_lanes();
+#pragma unroll
+      for (int jb = 0; jb < kTile / 32; ++jb)
+#pragma unroll
+        for (int cv = 0; cv < 2; ++cv) Av[jb][cv] = frag_tr(sV, VP, 32 * jb, 32 * cg + 16 * cv, lv.lane);
+    }
     // ---------------- q . n~: the wave with cg < KSH takes the 32-deep step
     // KSH kh + cg of d_qk for all rows (register group z: rows 16 zg(z) ..),
     // the others contribute zeros
@@ -636,9 +699,13 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
 #pragma unroll
       for (int z = 0; z < 4; ++z) dacc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (cg < KSH) {
-        const bf16x8 Bn = *reinterpret_cast<const bf16x8*>(&tb.nb[min(ln.i, 2) * K + KH * kh + 32 * cg + 8 * ln.g]);
+        const int col = KH * kh + 32 * cg + 8 * ln.g;
+        const bf16x8 Bn = *reinterpret_cast<const bf16x8*>(&tb.nb[min(ln.i, 2) * K + col]);
 #pragma unroll
-        for (int z = 0; z < 4; ++z) dacc[z] = mma(fq[z], Bn, dacc[z]);
+        for (int z = 0; z < 4; ++z) {
+          const bf16x8 fq = *reinterpret_cast<const bf16x8*>(&sQ[(16 * zg(z) + ln.i) * QP + col]);
+          dacc[z] = mma(fq, Bn, dacc[z]);
+        }
       }
 #pragma unroll
       for (int z = 0; z < 4; ++z) {
@@ -649,50 +716,6 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
       }
     }
 
-    // ---------------- state update: C~ <- decay C~ + K^T diag(w) V, n~ likewise
-    // (Q C~^T above used the state at the start of the tile)
-    if (__builtin_amdgcn_readfirstlane(tb.info[0])) {   // uniform over the workgroup
-      const float f = __builtin_bit_cast(float, tb.info[1]);
-#pragma unroll
-      for (int x = 0; x < KXH; ++x) {
-        Ct[x][0] *= f;
-        Ct[x][1] *= f;
-      }
-#pragma unroll
-      for (int x = 0; x < KXN; ++x) Nacc[x] *= f;
-    }
-#pragma unroll
-    for (int jb = 0; jb < kTile / 32; ++jb) {
-      const int ts = 32 * jb;
-      const Lanes lu = fresh_lanes();
-      const f32x4 wa = *reinterpret_cast<const f32x4*>(&tb.w[ts + 8 * lu.g]);
-      const f32x4 wb = *reinterpret_cast<const f32x4*>(&tb.w[ts + 8 * lu.g + 4]);
-      bf16x8 Bv[2];
-#pragma unroll
-      for (int cv = 0; cv < 2; ++cv)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Bv[cv][e] = (__bf16)((float)Av[jb][cv][e] * (e < 4 ? wa[e] : wb[e - 4]));
-      const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&tb.wb[min(lu.i, 2) * kTile + ts + 8 * lu.g]);
-      // transposed K fragments through a ring of kRing registers: the read of
-      // tile x + kRing - 1 is issued before the MFMAs of tile x
-      constexpr int kRing = 4;
-      bf16x8 Ak[kRing];
-      unroll<kRing - 1>([&](auto p_c) {
-        constexpr int p = decltype(p_c)::value;
-        if constexpr (p < KXH) Ak[p] = frag_trk(sK, KP, ts, kxg(p), lu.lane);
-      });
-      unroll<KXH>([&](auto x_c) {
-        constexpr int x = decltype(x_c)::value;
-        if constexpr (x + kRing - 1 < KXH) Ak[(x + kRing - 1) % kRing] = frag_trk(sK, KP, ts, kxg(x + kRing - 1), lu.lane);
-        Ct[x][0] = mma(Ak[x % kRing], Bv[0], Ct[x][0]);
-        Ct[x][1] = mma(Ak[x % kRing], Bv[1], Ct[x][1]);
-        // the wave's n~ tiles take the same K fragments (scalar branch)
-#pragma unroll
-        for (int xn = 0; xn < KXN; ++xn)
-          if (nx(xn) == x) Nacc[xn] = mma(Ak[x % kRing], Bw, Nacc[xn]);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-    }
     // The registers loaded at the top of the tile are taken here, before any
     // copy is issued: with copies or stores in flight the compiler can only
     // wait for all of the wave's memory operations. O is split into its
@@ -700,14 +723,14 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     swap_rows16(po[0][1], po[0][0]);
     swap_rows16(po[1][1], po[1][0]);
     if (w < 4) asm volatile("" ::"v"(r_u), "v"(r_mp), "v"(r_b), "v"(r_rs));
-    lds_barrier();   // the exchange area is complete; Q, K and V of tile tau no longer read from LDS
-    // ---------------- copies of the next tile, in five slots from here on
-    auto copy_slot = [&](int q) {
-      if (q < RK) dma_k(tn, q);
+    if (tau > tile0) epi_store(tau - 1);
+    lds_barrier();   // the exchange area is complete; Q and V of tile tau no longer read from LDS
+    // ---------------- copies of the next tile's Q and V, in five slots from here on
+    auto copy_qv = [&](int q) {
       if (q < RQ) dma_q(tn, q);
       if (q < RV) dma_v(tn, q);
     };
-    copy_slot(0);
+    copy_qv(0);
     // ---------------- the partner's partial sums for this wave's rows
     {
       const Lanes lx = fresh_lanes();
@@ -721,15 +744,18 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     }
     // the carried-state term enters row t with weight exp(m_prev - r_t + logD);
     // acc[z][cv] register r in lane (g, i) is H^T[v = 32 cg + 16 cv + 4 g + r][t = 16 zg(z) + i]
-    const Lanes lp = fresh_lanes();
+    {
+      const Lanes lp = fresh_lanes();
 #pragma unroll
-    for (int z = 0; z < 2; ++z) {
-      const float sc = tb.sc[16 * zg(z) + lp.i];
-      acc[z][0] *= sc;
-      acc[z][1] *= sc;
+      for (int z = 0; z < 2; ++z) {
+        const float sc = tb.sc[16 * zg(z) + lp.i];
+        acc[z][0] *= sc;
+        acc[z][1] *= sc;
+      }
     }
     // ---------------- P = S o D: lane holds S^T[j = 16 kg + 4 g + r][t = 16 zg(zz) + i]
-    {
+    auto phase_p = [&]() {
+      const Lanes lp = fresh_lanes();
       const f32x4 u2 = *reinterpret_cast<const f32x4*>(&tb.u2[16 * kg + 4 * lp.g]);
 #pragma unroll
       for (int zz = 0; zz < 2; ++zz) {
@@ -749,10 +775,70 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
         *reinterpret_cast<bf16x4*>(&sP[tl * PP + 16 * kg + 4 * lp.g]) = pk4;
         psum = sum_rows(psum);
         if (lp.g == 0) s_den[kg * kTile + tl] = psum;
-        copy_slot(1 + zz);
+        copy_qv(1 + zz);
       }
-    }
-    lds_barrier();   // sP, s_den, s_dn complete
+    };
+    // ---------------- state update: C~ <- decay C~ + K^T diag(w) V, n~ likewise
+    // (Q C~^T above used the state at the start of the tile)
+    auto phase_u = [&]() {
+      if (__builtin_amdgcn_readfirstlane(tb.info[0])) {   // uniform over the workgroup
+        const float f = __builtin_bit_cast(float, tb.info[1]);
+#pragma unroll
+        for (int x = 0; x < KXH; ++x) {
+          Ct[x][0] *= f;
+          Ct[x][1] *= f;
+        }
+#pragma unroll
+        for (int x = 0; x < KXN; ++x) Nacc[x] *= f;
+      }
+#pragma unroll
+      for (int jb = 0; jb < kTile / 32; ++jb) {
+        const int ts = 32 * jb;
+        const Lanes lu = fresh_lanes();
+        const f32x4 wa = *reinterpret_cast<const f32x4*>(&tb.w[ts + 8 * lu.g]);
+        const f32x4 wb = *reinterpret_cast<const f32x4*>(&tb.w[ts + 8 * lu.g + 4]);
+        bf16x8 Bv[2];
+#pragma unroll
+        for (int cv = 0; cv < 2; ++cv)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) Bv[cv][e] = (__bf16)((float)Av[jb][cv][e] * (e < 4 ? wa[e] : wb[e - 4]));
+        const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&tb.wb[min(lu.i, 2) * kTile + ts + 8 * lu.g]);
+        // transposed K fragments through a ring of kRing registers: the read of
+        // tile x + kRing - 1 is issued before the MFMAs of tile x
+        constexpr int kRing = 4;
+        bf16x8 Ak[kRing];
+        const int koff = lane_off_trk(KP, kh * KXH, lu.lane);
+        unroll<kRing - 1>([&](auto p_c) {
+          constexpr int p = decltype(p_c)::value;
+          if constexpr (p < KXH) Ak[p] = frag_trk_at(sK, koff, KP, ts, p);
+        });
+        unroll<KXH>([&](auto x_c) {
+          constexpr int x = decltype(x_c)::value;
+          if constexpr (x + kRing - 1 < KXH) Ak[(x + kRing - 1) % kRing] = frag_trk_at(sK, koff, KP, ts, x + kRing - 1);
+          Ct[x][0] = mma(Ak[x % kRing], Bv[0], Ct[x][0]);
+          Ct[x][1] = mma(Ak[x % kRing], Bv[1], Ct[x][1]);
+          // the wave's n~ tiles take the same K fragments (scalar branch)
+#pragma unroll
+          for (int xn = 0; xn < KXN; ++xn)
+            if (nx(xn) == x) Nacc[xn] = mma(Ak[x % kRing], Bw, Nacc[xn]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        copy_qv(3 + jb);
+      }
+    };
+    // The two phases are independent: P is exponentials (VALU), the update
+    // matrix products. The two waves of a SIMD (the halves kh = 0 and 1 of one
+    // column group) take them in opposite orders, so that one wave's
+    // exponentials run beside the other's products.
+    phase_p();
+    phase_u();
+    // the next tile's K: after the barrier no wave reads K of tile tau
+    auto copy_k = [&](int r) {
+      if (r < RK) dma_k(tn, r);
+    };
+    lds_barrier();   // sP, s_den, s_dn complete; K of tile tau no longer read from LDS
+    copy_k(0);
+    copy_k(1);
     if (w == 0) {   // max(|n~^T q|, floor) of row t = lane
       const int t = fresh_lanes().lane;
       const float den = s_den[t] + s_den[kTile + t] + s_den[2 * kTile + t] + s_den[3 * kTile + t];
@@ -778,47 +864,24 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
             acc[z][1] = mma(Av[jb][1], B[z], acc[z][1]);
           }
         }
-        copy_slot(3 + jb);
+        copy_k(2 + jb);
       }
     }
-    lds_barrier();   // s_dnm complete
-    // ---------------- normaliser, output gate: per column half a lane forms
-    // four consecutive columns of each of its two rows and stores them, paired
-    // with its partner lane's, as 16-byte row pieces straight to H (the layout
-    // of load_o); rows past the sequence end fall outside the buffer range and
-    // are dropped
-    {
-      const Lanes le = fresh_lanes();
-      float dnm[2];
+    copy_k(4);
+    // this tile's epilogue operands, for the next tile
 #pragma unroll
-      for (int z = 0; z < 2; ++z) dnm[z] = s_dnm[16 * zg(z) + le.i];
-      bf16x8 hv[2];
+    for (int cv = 0; cv < 2; ++cv) {
+      epo[cv][0] = po[cv][0];
+      epo[cv][1] = po[cv][1];
 #pragma unroll
-      for (int cv = 0; cv < 2; ++cv) {
-        bf16x4 h4[2];
-#pragma unroll
-        for (int z = 0; z < 2; ++z) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            // sigmoid(o) / D = 1 / ((1 + e^-o) D)
-            const float e = __builtin_amdgcn_exp2f(-kLog2eF * (float)po[cv][z][r]);
-            h4[z][r] = (__bf16)(acc[z][cv][r] * __builtin_amdgcn_rcpf(fmaf(e, dnm[z], dnm[z])));
-          }
-        }
-        swap_rows16(h4[1], h4[0]);
-        hv[cv] = __builtin_shufflevector(h4[1], h4[0], 0, 1, 2, 3, 4, 5, 6, 7);
-      }
-      // the two stores are this wave's last memory operations of the tile
-      const __amdgpu_buffer_rsrc_t hr = tile_rsrc_vo(a.h, tau);
-#pragma unroll
-      for (int cv = 0; cv < 2; ++cv) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hv[cv]), hr, (int)offO[cv], 0, 0);
+      for (int z = 0; z < 2; ++z) eacc[z][cv] = acc[z][cv];
     }
     // ---------------- the next tile's data into the other half (its readers
     // start after the next top barrier; this half's last readers were in tile
     // tau - 1)
     if (more) {
       const TileBuf nb = tile_buf(buf ^ 1);
-      put_n(nb);
+      put_n(buf ^ 1);
       if (w < 4) {
         prep(tau + 1, nb, m_chain, logD_chain, true);
         advance(m_chain, logD_chain);
@@ -832,7 +895,11 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
     s_fin[0] = m_chain;
     s_fin[1] = logD_chain;
   }
-  __syncthreads();   // final stabiliser chain published
+  __syncthreads();   // final stabiliser chain and the last tile's row denominators published
+  if (tile1 > tile0) {
+    epi_math();
+    epi_store(tile1 - 1);
+  }
   const double m_fin = s_fin[0], logD_fin = s_fin[1];
   const float fD = (float)exp(logD_fin);
 
@@ -860,8 +927,14 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* smem) {
 
 template <int K>
 __global__ __launch_bounds__(64 * kOutWaves, 1) void out_kernel_fused(SegArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[OutLds<K>::bytes];
-  out_body<K>(a, smem);
+  // The copy targets are separate objects: the compiler then knows that a
+  // direct-to-LDS copy in flight into one of them does not touch the others,
+  // and reads those without waiting for it.
+  __shared__ __attribute__((aligned(16))) char lq[OutLds<K>::qBytes];
+  __shared__ __attribute__((aligned(16))) char lk[OutLds<K>::kBytes];
+  __shared__ __attribute__((aligned(16))) char lv[OutLds<K>::vBytes];
+  __shared__ __attribute__((aligned(16))) char smem[OutLds<K>::restBytes];
+  out_body<K>(a, lq, lk, lv, smem);
 }
 
 // ------------------------------------------------------------------ chunk-local end states
