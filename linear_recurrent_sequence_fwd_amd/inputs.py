@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the mLSTM cell forward and decode step.
+"""Seeded synthetic inputs for the mLSTM cell forward and decode step, and
+for the sLSTM cell forward (make_slstm_inputs, make_slstm_state).
 
 This module draws random numbers and nothing else of the method: it holds no
 gate activation, no recurrence and no normalisation. The same arrays feed the
@@ -29,6 +30,8 @@ __all__ = [
     "make_fwd_inputs",
     "make_step_inputs",
     "make_state",
+    "make_slstm_inputs",
+    "make_slstm_state",
 ]
 
 
@@ -111,3 +114,31 @@ def make_state(B: int, H: int, d_qk: int, d_v: int, seed: int = 0, m_scale: floa
     n = rng.standard_normal((B, H, d_qk), dtype=np.float32) * np.float32(0.5)
     m = rng.standard_normal((B, H), dtype=np.float32) * np.float32(m_scale)
     return {"C": C, "n": n, "m": m.astype(np.float32)}
+
+
+def make_slstm_inputs(B: int, H: int, T: int, D: int, seed: int = 0, f_mean: float = 0.0,
+                      r_scale: float = 0.5):
+    """Seeded sLSTM inputs: input-projected gate preactivations and the
+    recurrent matrices.
+
+    Draws, in this order, from ``Generator(PCG64(seed))`` in float32:
+    ``pre`` [B, T, 4, H, D] ~ N(0, 1) (gates i, f, z, o; the forget gate's
+    draws shifted by ``f_mean``), then ``R`` [H, 4, D, D] ~ N(0, 1) scaled by
+    r_scale / sqrt(D), so that R h keeps the size of one preactivation.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    pre = rng.standard_normal((B, T, 4, H, D), dtype=np.float32)
+    pre[:, :, 1] += np.float32(f_mean)
+    R = rng.standard_normal((H, 4, D, D), dtype=np.float32) * np.float32(r_scale / np.sqrt(D))
+    return np.ascontiguousarray(pre), np.ascontiguousarray(R, dtype=np.float32)
+
+
+def make_slstm_state(B: int, H: int, D: int, seed: int = 0):
+    """A seeded non-zero sLSTM state (c, n, m, h) [B, H, D], float32: n in
+    [0.5, 2), c = n * U(-1, 1), m ~ N(0, 1), h ~ U(-1, 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n = rng.uniform(0.5, 2.0, (B, H, D)).astype(np.float32)
+    c = (n * rng.uniform(-1.0, 1.0, (B, H, D))).astype(np.float32)
+    m = rng.standard_normal((B, H, D), dtype=np.float32)
+    h = rng.uniform(-1.0, 1.0, (B, H, D)).astype(np.float32)
+    return c, n, m, h

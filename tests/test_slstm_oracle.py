@@ -1,0 +1,140 @@
+"""Pins of the sLSTM CPU oracle against what the equations fix, by code that
+shares nothing with it (xLSTM guide, "The Twin Cells: sLSTM and mLSTM
+Mathematical Formulations", sLSTM step-by-step recurrent equations)."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import slstm_oracle as so
+from linear_recurrent_sequence_fwd_amd.inputs import make_slstm_inputs, make_slstm_state
+
+
+def _sig(x):
+    return 1.0 / (1.0 + math.exp(-x))
+
+
+def unstabilised_loops(pre, R, state=None):
+    """The same cell in true units (no running max), element by element with
+    plain Python floats: c = e^f~ c + e^i~ tanh(z~), n = e^f~ n + e^i~,
+    h = sigmoid(o~) c / n, gate preactivations P_t + R h_{t-1} per head."""
+    B, T, _, H, D = pre.shape
+    out = np.zeros((B, T, H, D))
+    for b in range(B):
+        for hh in range(H):
+            if state is None:
+                c = [0.0] * D
+                n = [0.0] * D
+                hp = [0.0] * D
+            else:
+                c0, n0, m0, h0 = state
+                # true units: C = e^m C~
+                c = [float(c0[b, hh, d]) * math.exp(float(m0[b, hh, d])) for d in range(D)]
+                n = [float(n0[b, hh, d]) * math.exp(float(m0[b, hh, d])) for d in range(D)]
+                hp = [float(h0[b, hh, d]) for d in range(D)]
+            for t in range(T):
+                g = [[float(pre[b, t, q, hh, d]) + sum(float(R[hh, q, d, j]) * hp[j] for j in range(D))
+                      for d in range(D)] for q in range(4)]
+                hn = []
+                for d in range(D):
+                    i_, f_, z_, o_ = g[0][d], g[1][d], g[2][d], g[3][d]
+                    c[d] = math.exp(f_) * c[d] + math.exp(i_) * math.tanh(z_)
+                    n[d] = math.exp(f_) * n[d] + math.exp(i_)
+                    hn.append(_sig(o_) * c[d] / n[d])
+                hp = hn
+                out[b, t, hh] = hn
+    return out
+
+
+def _rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+@pytest.mark.parametrize("seed,f_mean", [(0, 0.0), (1, -2.0), (2, 1.5)])
+def test_unstabilised_loops_agree(seed, f_mean):
+    pre, R = make_slstm_inputs(2, 2, 12, 3, seed=seed, f_mean=f_mean)
+    h, _ = so.slstm_recurrent(pre, R)
+    ref = unstabilised_loops(pre, R)
+    assert _rel(h, ref) < 1e-12
+
+
+def test_unstabilised_loops_agree_from_state():
+    pre, R = make_slstm_inputs(1, 2, 9, 4, seed=3)
+    st = make_slstm_state(1, 2, 4, seed=4)
+    h, _ = so.slstm_recurrent(pre, R, st)
+    ref = unstabilised_loops(pre, R, st)
+    assert _rel(h, ref) < 1e-12
+
+
+def test_no_recurrence_closed_form():
+    """R = 0: c_T / n_T is the weighted mean of tanh(z~_t) with weights
+    e^{i~_t} times the product of the later forget factors e^{f~_s}, written
+    with explicit products."""
+    pre, _ = make_slstm_inputs(1, 1, 10, 2, seed=5)
+    R = np.zeros((1, 4, 2, 2), dtype=np.float32)
+    h, _ = so.slstm_recurrent(pre, R)
+    T = pre.shape[1]
+    for d in range(2):
+        for tt in range(T):
+            num = den = 0.0
+            for t in range(tt + 1):
+                w = math.exp(float(pre[0, t, 0, 0, d]))
+                for s in range(t + 1, tt + 1):
+                    w *= math.exp(float(pre[0, s, 1, 0, d]))
+                num += w * math.tanh(float(pre[0, t, 2, 0, d]))
+                den += w
+            expect = _sig(float(pre[0, tt, 3, 0, d])) * num / den
+            assert abs(h[0, tt, 0, d] - expect) < 1e-13
+
+
+def test_single_step_from_zero_state():
+    """T = 1 from the zero state: c/n = tanh(z~) whatever the gates, so
+    h = sigmoid(o~) tanh(z~) (R h_0 = 0)."""
+    pre, R = make_slstm_inputs(3, 2, 1, 5, seed=6, f_mean=4.0)
+    h, (c, n, m, _) = so.slstm_recurrent(pre, R)
+    p = pre[:, 0].astype(np.float64)
+    expect = 1.0 / (1.0 + np.exp(-p[:, 3])) * np.tanh(p[:, 2])
+    assert np.max(np.abs(h[:, 0] - expect)) < 1e-15
+    assert np.array_equal(m, np.maximum(p[:, 1], p[:, 0]))
+
+
+def test_heads_and_batch_independent():
+    pre, R = make_slstm_inputs(2, 3, 8, 4, seed=7)
+    h, _ = so.slstm_recurrent(pre, R)
+    R2 = R.copy()
+    R2[1] *= -3.0
+    pre2 = pre.copy()
+    pre2[1, :, :, 2] += 1.0
+    h2, _ = so.slstm_recurrent(pre2, R2)
+    assert np.array_equal(h[:, :, 0], h2[:, :, 0])   # head 0 untouched
+    assert np.array_equal(h[0, :, 2], h2[0, :, 2])   # batch 0 of head 2 untouched
+    assert not np.allclose(h[:, :, 1], h2[:, :, 1])
+
+
+def test_split_and_resume():
+    pre, R = make_slstm_inputs(2, 2, 15, 3, seed=8)
+    h, st = so.slstm_recurrent(pre, R)
+    h1, st1 = so.slstm_recurrent(pre[:, :6], R)
+    h2, st2 = so.slstm_recurrent(pre[:, 6:], R, st1)
+    assert np.array_equal(np.concatenate([h1, h2], axis=1), h)
+    for a, b in zip(st, st2):
+        assert np.array_equal(a, b)
+
+
+def test_stabiliser_invariance():
+    """A shift s of the initial stabiliser with c~, n~ scaled by e^-s is the
+    same true state: h must not change."""
+    pre, R = make_slstm_inputs(1, 2, 10, 3, seed=9)
+    c0, n0, m0, h0 = (x.astype(np.float64) for x in make_slstm_state(1, 2, 3, seed=10))
+    ha, _ = so.slstm_recurrent(pre, R, (c0, n0, m0, h0))
+    s = 7.5
+    hb, _ = so.slstm_recurrent(pre, R, (c0 * math.exp(-s), n0 * math.exp(-s), m0 + s, h0))
+    assert _rel(hb, ha) < 1e-13
+
+
+def test_planted_mistake_is_caught():
+    """A dropped R term (the recurrence without mixing) must fail the pin
+    against the element loops."""
+    pre, R = make_slstm_inputs(1, 1, 6, 3, seed=11)
+    wrong, _ = so.slstm_recurrent(pre, np.zeros_like(R))
+    assert _rel(wrong, unstabilised_loops(pre, R)) > 1e-3
