@@ -2,8 +2,9 @@
 
 The entry points mirror include/mlstm.h: mlstm_fwd_chunkwise (full
 sequences), mlstm_fwd_parallel (short sequences) and mlstm_step (recurrent
-decode). They take torch tensors for device memory and run only the HIP
-library; a missing library raises.
+decode); and include/slstm.h: slstm_fwd (the sLSTM scalar-memory cell's
+recurrence over a sequence). They take torch tensors for device memory and
+run only the HIP library; a missing library raises.
 """
 from ._lib import (  # noqa: F401
     MlstmError,
@@ -11,4 +12,5 @@ from ._lib import (  # noqa: F401
     mlstm_fwd_parallel,
     mlstm_step,
     set_launch_events,
+    slstm_fwd,
 )

@@ -1,4 +1,5 @@
-"""ctypes binding of libmlstm.so: the C ABI declared in include/mlstm.h.
+"""ctypes binding of libmlstm.so: the C ABI declared in include/mlstm.h and
+include/slstm.h.
 
 Argument marshalling only. Tensors supply device memory and the current
 stream; every step of the computation runs in the library's HIP kernels.
@@ -43,6 +44,15 @@ class StepArgs(ctypes.Structure):
     ]
 
 
+class SlstmArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", c_int64), ("H", c_int64), ("T", c_int64), ("D", c_int64),
+        ("pre", c_void_p), ("R", c_void_p), ("h", c_void_p),
+        ("c0", c_void_p), ("n0", c_void_p), ("m0", c_void_p), ("h0", c_void_p),
+        ("c_out", c_void_p), ("n_out", c_void_p), ("m_out", c_void_p), ("h_out", c_void_p),
+    ]
+
+
 class MlstmError(RuntimeError):
     def __init__(self, code: int, what: str, detail: str):
         super().__init__(f"{what} failed: {STATUS.get(code, code)}: {detail}")
@@ -84,6 +94,8 @@ def lib() -> ctypes.CDLL:
         L.mlstm_set_launch_events.restype = c_int
         L.mlstm_clock_probe.argtypes = [c_void_p, c_int, c_void_p]
         L.mlstm_clock_probe.restype = c_int
+        L.slstm_fwd.argtypes = [P(SlstmArgs), c_void_p]
+        L.slstm_fwd.restype = c_int
         _lib = L
     return _lib
 
@@ -254,3 +266,30 @@ def clock_probe(ticks, iters: int, stream=None) -> None:
     import torch
     _require(ticks, "ticks", (4,), torch.int64)
     _check(lib().mlstm_clock_probe(_ptr(ticks), int(iters), _stream(stream)), "mlstm_clock_probe")
+
+
+def slstm_fwd(pre, R, state=None, want_state=False, h=None, stream=None):
+    """sLSTM forward over a sequence. pre [B, T, 4, H, D], R [H, 4, D, D] float32
+    device tensors; state = (c0, n0, m0, h0) [B, H, D] each or None. Returns h
+    [B, T, H, D], and the final (c, n, m, h) when want_state."""
+    import torch
+    if pre is None or R is None:
+        raise ValueError("pre and R are required")
+    B, T, four, H, D = pre.shape
+    if four != 4:
+        raise ValueError(f"pre must be [B, T, 4, H, D], got {tuple(pre.shape)}")
+    _require(pre, "pre", (B, T, 4, H, D), torch.float32)
+    _require(R, "R", (H, 4, D, D), torch.float32)
+    if h is None:
+        h = torch.empty((B, T, H, D), dtype=torch.float32, device=pre.device)
+    _require(h, "h", (B, T, H, D), torch.float32)
+    st_in = (None,) * 4 if state is None else tuple(state)
+    if state is not None:
+        for name, t in zip(("c0", "n0", "m0", "h0"), st_in):
+            _require(t, name, (B, H, D), torch.float32)
+    st_out = tuple(torch.empty((B, H, D), dtype=torch.float32, device=pre.device) for _ in range(4)) \
+        if want_state else (None,) * 4
+    args = SlstmArgs(B, H, T, D, _ptr(pre), _ptr(R), _ptr(h), *[_ptr(t) for t in st_in],
+                     *[_ptr(t) for t in st_out])
+    _check(lib().slstm_fwd(ctypes.byref(args), _stream(stream)), "slstm_fwd")
+    return (h, st_out) if want_state else h

@@ -18,7 +18,8 @@ LIB = os.path.join(PKG, "libmlstm.so")
 ARCH = "gfx950"
 
 SOURCES = [os.path.join(CSRC, "mlstm_kernels.hip"), os.path.join(CSRC, "mlstm_bf16.hip"),
-           os.path.join(CSRC, "mlstm_fused.hip"), os.path.join(CSRC, "mlstm_abi.cpp")]
+           os.path.join(CSRC, "mlstm_fused.hip"), os.path.join(CSRC, "slstm.hip"),
+           os.path.join(CSRC, "mlstm_abi.cpp")]
 
 # Packed-fp32 VALU instructions are turned off for all device code. MFMA
 # builtins are compiled in the VGPR form: with accumulators in AGPRs this

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "../../include/mlstm.h"
+#include "../../include/slstm.h"
 #include "mlstm_launch.h"
 
 namespace {
@@ -346,6 +347,42 @@ int mlstm_step(const mlstm_step_args* a, void* stream) {
   sl.C = a->C; sl.n_in = a->n_in; sl.m_in = a->m_in; sl.n_out = a->n_out; sl.m_out = a->m_out;
   sl.h = a->h;
   return hip_status(mlstm_impl::launch_step(sl, static_cast<hipStream_t>(stream)), "step kernel");
+}
+
+int slstm_fwd(const slstm_fwd_args* a, void* stream) {
+  g_last_error.clear();
+  if (!a) return fail(MLSTM_ERR_NULLPTR, "args is NULL");
+  if (a->B < 1 || a->H < 1 || a->T < 0 || a->D < 1)
+    return fail(MLSTM_ERR_BAD_SHAPE, "need B >= 1, H >= 1, T >= 0, D >= 1");
+  if (!mlstm_impl::slstm_supported(a->D)) return fail(MLSTM_ERR_UNSUPPORTED, "D must be 16, 32, 64 or 128");
+  if (a->B * a->H > INT32_MAX) return fail(MLSTM_ERR_UNSUPPORTED, "B * H above 2^31 - 1");
+  const bool any0 = a->c0 || a->n0 || a->m0 || a->h0, all0 = a->c0 && a->n0 && a->m0 && a->h0;
+  if (any0 && !all0) return fail(MLSTM_ERR_NULLPTR, "c0, n0, m0, h0 must be given together");
+  const bool anyo = a->c_out || a->n_out || a->m_out || a->h_out;
+  const bool allo = a->c_out && a->n_out && a->m_out && a->h_out;
+  if (anyo && !allo) return fail(MLSTM_ERR_NULLPTR, "c_out, n_out, m_out, h_out must be given together");
+  if (!a->R) return fail(MLSTM_ERR_NULLPTR, "R is required");
+  if (a->T > 0 && (!a->pre || !a->h)) return fail(MLSTM_ERR_NULLPTR, "pre and h are required when T > 0");
+  const void* v16[] = {a->pre, a->R, a->h, a->c0, a->n0, a->m0, a->h0, a->c_out, a->n_out, a->m_out, a->h_out};
+  for (const void* p : v16)
+    if (p && !aligned(p, 16)) return fail(MLSTM_ERR_MISALIGNED, "array pointers must be 16-byte aligned");
+  const int64_t BH = a->B * a->H, D = a->D;
+  const int64_t npre = BH * a->T * 4 * D * 4, nR = a->H * 4 * D * D * 4, nh = BH * a->T * D * 4, ns = BH * D * 4;
+  std::vector<Range> in = {make_range("pre", a->pre, npre), make_range("R", a->R, nR),
+                           make_range("c0", a->c0, ns), make_range("n0", a->n0, ns),
+                           make_range("m0", a->m0, ns), make_range("h0", a->h0, ns)};
+  std::vector<Range> out = {make_range("h", a->h, nh), make_range("c_out", a->c_out, ns),
+                            make_range("n_out", a->n_out, ns), make_range("m_out", a->m_out, ns),
+                            make_range("h_out", a->h_out, ns)};
+  int st = check_alias(in, out);
+  if (st) return st;
+  if (a->T == 0 && !a->c_out) return MLSTM_OK;
+  mlstm_impl::SlstmLaunch sl;
+  sl.B = a->B; sl.H = a->H; sl.T = a->T; sl.D = D;
+  sl.pre = a->pre; sl.R = a->R; sl.h = a->h;
+  sl.c0 = a->c0; sl.n0 = a->n0; sl.m0 = a->m0; sl.h0 = a->h0;
+  sl.c_out = a->c_out; sl.n_out = a->n_out; sl.m_out = a->m_out; sl.h_out = a->h_out;
+  return hip_status(mlstm_impl::launch_slstm(sl, static_cast<hipStream_t>(stream)), "sLSTM kernel");
 }
 
 const char* mlstm_status_string(int status) {

@@ -74,6 +74,19 @@ struct StepLaunch {
   void* h;
 };
 
+// sLSTM forward (slstm.hip): pre [B,T,4,H,D], R [H,4,D,D], h [B,T,H,D];
+// optional state [B,H,D] in (c0 == NULL: zero state) and out (c_out == NULL:
+// not written), all float32
+struct SlstmLaunch {
+  int64_t B, H, T, D;
+  const float *pre, *R;
+  float* h;
+  const float *c0, *n0, *m0, *h0;
+  float *c_out, *n_out, *m_out, *h_out;
+};
+bool slstm_supported(int64_t D);
+hipError_t launch_slstm(const SlstmLaunch& a, hipStream_t s);
+
 void set_launch_events(int kernel, hipEvent_t before, hipEvent_t after);
 
 hipError_t launch_gate(const FwdLaunch& a, const GateBuffers& gb, hipStream_t s);

@@ -1,0 +1,124 @@
+// sLSTM scalar-memory cell forward on gfx950 (xLSTM guide, aifetchly blog,
+// "The Twin Cells: sLSTM and mLSTM Mathematical Formulations", sLSTM
+// step-by-step recurrent equations).
+//
+// The recurrence is sequential in t: step t needs h_{t-1} of every cell of
+// the head before any of its gates can be formed. One workgroup per (batch
+// entry, head) therefore walks the whole sequence. Thread j of its 4 D
+// threads owns row j of the head's stacked recurrent matrix [4 D][D] (gate
+// j / D, cell j % D) in registers, so the matrix is read from memory once.
+// Per step:
+//   1. thread j: gate preactivation P_t[j] + R[j] . h_{t-1}, with h_{t-1}
+//      broadcast from LDS as 16-byte reads; P_{t+1} is prefetched;
+//   2. barrier; threads d < D take the four gates of cell d, update m, c, n
+//      in registers, form h_t[d], store it to HBM and to the other half of a
+//      double-buffered LDS vector;
+//   3. barrier.
+// The work per step is 4 D^2 fused multiply-adds spread over the workgroup
+// plus two barriers, so a step is bound by issue latency, not by HBM or the
+// ALUs; throughput comes from running the B * H sequences side by side.
+
+#include <hip/hip_runtime.h>
+
+#include <float.h>
+#include <stdint.h>
+
+#include "mlstm_launch.h"
+
+namespace mlstm_impl {
+namespace {
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+template <int D>
+__global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
+  constexpr int NT = 4 * D;
+  const int64_t H = a.H, T = a.T;
+  const int64_t b = blockIdx.x / H, hh = blockIdx.x % H;
+  const int j = threadIdx.x;
+  const int g = j / D, e = j % D;
+  __shared__ __attribute__((aligned(16))) float s_h[2][D];
+  __shared__ float s_g[NT];
+
+  // row j of the head's recurrent matrix: gate g of cell e
+  float r[D];
+  {
+    const f32x4v* src = reinterpret_cast<const f32x4v*>(a.R + ((hh * 4 + g) * D + e) * D);
+#pragma unroll
+    for (int k = 0; k < D / 4; ++k) {
+      const f32x4v x = src[k];
+      r[4 * k] = x[0];
+      r[4 * k + 1] = x[1];
+      r[4 * k + 2] = x[2];
+      r[4 * k + 3] = x[3];
+    }
+  }
+  // cell state: thread d < D owns cell d
+  const int64_t sidx = (b * H + hh) * D + j;
+  float c = 0.f, n = 0.f, m = 0.f, hv = 0.f;
+  if (j < D && a.c0) {
+    c = a.c0[sidx];
+    n = a.n0[sidx];
+    m = a.m0[sidx];
+    hv = a.h0[sidx];
+  }
+  if (j < D) s_h[0][j] = hv;
+  // P_t[j] sits at pre[((b T + t) 4 + g) H + hh) D + e]
+  const int64_t pstride = 4 * H * D;
+  const float* pre = a.pre + (b * T * 4 + g) * H * D + hh * D + e;
+  float* hout = a.h + (b * T * H + hh) * D + j;
+  float p_next = T > 0 ? pre[0] : 0.f;
+  __syncthreads();
+  for (int64_t t = 0; t < T; ++t) {
+    const float p = p_next;
+    if (t + 1 < T) p_next = pre[(t + 1) * pstride];
+    const f32x4v* hp = reinterpret_cast<const f32x4v*>(s_h[t & 1]);
+    float acc0 = p, acc1 = 0.f;   // two chains halve the dependent FMA latency
+#pragma unroll
+    for (int k = 0; k < D / 4; ++k) {
+      const f32x4v x = hp[k];
+      acc0 = fmaf(r[4 * k], x[0], acc0);
+      acc1 = fmaf(r[4 * k + 1], x[1], acc1);
+      acc0 = fmaf(r[4 * k + 2], x[2], acc0);
+      acc1 = fmaf(r[4 * k + 3], x[3], acc1);
+    }
+    s_g[j] = acc0 + acc1;
+    __syncthreads();   // all gate preactivations of step t formed
+    if (j < D) {
+      const float it = s_g[j], ft = s_g[D + j], zt = s_g[2 * D + j], ot = s_g[3 * D + j];
+      const float mn = fmaxf(m + ft, it);
+      const float fa = expf(ft + m - mn), ia = expf(it - mn);
+      c = fa * c + ia * tanhf(zt);
+      n = fa * n + ia;
+      m = mn;
+      hv = c / (fmaxf(n, FLT_MIN) * (1.f + expf(-ot)));   // sigmoid(o~) c / n
+      s_h[(t + 1) & 1][j] = hv;
+      hout[t * H * D] = hv;
+    }
+    __syncthreads();   // h_t published; s_g free for step t + 1
+  }
+  if (j < D && a.c_out) {
+    a.c_out[sidx] = c;
+    a.n_out[sidx] = n;
+    a.m_out[sidx] = m;
+    a.h_out[sidx] = hv;
+  }
+}
+
+}  // namespace
+
+bool slstm_supported(int64_t D) { return D == 16 || D == 32 || D == 64 || D == 128; }
+
+hipError_t launch_slstm(const SlstmLaunch& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.B * a.H));
+  switch (a.D) {
+    case 16: hipLaunchKernelGGL(slstm_kernel<16>, grid, dim3(64), 0, s, a); break;
+    case 32: hipLaunchKernelGGL(slstm_kernel<32>, grid, dim3(128), 0, s, a); break;
+    case 64: hipLaunchKernelGGL(slstm_kernel<64>, grid, dim3(256), 0, s, a); break;
+    case 128: hipLaunchKernelGGL(slstm_kernel<128>, grid, dim3(512), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mlstm_impl

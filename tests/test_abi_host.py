@@ -258,3 +258,71 @@ def test_clock_probe_validation():
     assert lib.mlstm_clock_probe(0x7D0000000000, 0, None) == BAD_SHAPE
     assert lib.mlstm_clock_probe(0x7D0000000000, 1 << 25, None) == BAD_SHAPE
     assert lib.mlstm_clock_probe(0x7D0000000004, 100, None) == MISALIGNED
+
+
+SLSTM_HEADER = os.path.join(ROOT, "include", "slstm.h")
+
+
+def test_library_exports_every_slstm_symbol():
+    text = re.sub(r"/\*.*?\*/", "", open(SLSTM_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(slstm_[a-z_]+)\s*\(", text)))
+    assert names == ["slstm_fwd"]
+    for n in names:
+        assert hasattr(L.lib(), n), n
+
+
+def fake_slstm(B=2, H=3, T=10, D=64, state_in=True, state_out=True):
+    base = [0x7C0000000000]
+
+    def take(nbytes):
+        p = base[0]
+        base[0] += (nbytes + 4095) // 4096 * 4096 + 4096
+        return p
+
+    BH = B * H
+    ns = BH * D * 4
+    sin = [take(ns) for _ in range(4)] if state_in else [None] * 4
+    sout = [take(ns) for _ in range(4)] if state_out else [None] * 4
+    return L.SlstmArgs(B, H, T, D, take(BH * T * 4 * D * 4), take(H * 4 * D * D * 4), take(BH * T * D * 4),
+                       *sin, *sout)
+
+
+def test_slstm_validation():
+    lib = L.lib()
+    assert lib.slstm_fwd(None, None) == NULLPTR
+    for field, value, code in (("B", 0, BAD_SHAPE), ("H", 0, BAD_SHAPE), ("T", -1, BAD_SHAPE),
+                               ("D", 0, BAD_SHAPE), ("D", 48, UNSUPPORTED), ("D", 256, UNSUPPORTED)):
+        a = fake_slstm()
+        setattr(a, field, value)
+        assert lib.slstm_fwd(ctypes.byref(a), None) == code, (field, value)
+    a = fake_slstm()
+    a.n0 = None
+    assert lib.slstm_fwd(ctypes.byref(a), None) == NULLPTR
+    a = fake_slstm()
+    a.h_out = None
+    assert lib.slstm_fwd(ctypes.byref(a), None) == NULLPTR
+    a = fake_slstm()
+    a.R = None
+    assert lib.slstm_fwd(ctypes.byref(a), None) == NULLPTR
+    a = fake_slstm()
+    a.pre = None
+    assert lib.slstm_fwd(ctypes.byref(a), None) == NULLPTR
+    a = fake_slstm()
+    a.h = a.h + 8
+    assert lib.slstm_fwd(ctypes.byref(a), None) == MISALIGNED
+    a = fake_slstm()
+    a.h = a.pre
+    assert lib.slstm_fwd(ctypes.byref(a), None) == ALIAS
+    a = fake_slstm()
+    a.c_out = a.c0
+    assert lib.slstm_fwd(ctypes.byref(a), None) == ALIAS
+    a = fake_slstm()
+    a.m_out = a.n_out
+    assert lib.slstm_fwd(ctypes.byref(a), None) == ALIAS
+
+
+def test_slstm_empty_sequence_without_state_is_a_noop():
+    a = fake_slstm(T=0, state_in=False, state_out=False)
+    a.pre = None
+    a.h = None
+    assert L.lib().slstm_fwd(ctypes.byref(a), None) == OK

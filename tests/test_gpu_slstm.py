@@ -1,0 +1,150 @@
+"""GPU parity of the sLSTM forward (through the C ABI) against the float64
+oracle of the sLSTM recurrent equations (xLSTM guide, "The Twin Cells: sLSTM
+and mLSTM Mathematical Formulations").
+
+Bar: max|h_gpu - h_ref| <= 1e-4 * max|h_ref| (float32 path; |h| <= 1); the
+final state in true units (exp(m) c, exp(m) n) within 1e-4 of the oracle's
+largest entry; every output finite. Outputs are pre-filled with NaN so that
+an unwritten element fails.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from linear_recurrent_sequence_fwd_amd.inputs import make_slstm_inputs, make_slstm_state
+from oracle import slstm_oracle as so
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_recurrent_sequence_fwd_amd import _lib as L
+    return L
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def host(t):
+    return t.cpu().numpy().astype(np.float64)
+
+
+def rel_err(got, ref):
+    assert np.all(np.isfinite(got)), "non-finite output"
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def run(L, pre, R, state=None, want_state=True):
+    B, T, _, H, D = pre.shape
+    h = torch.full((B, T, H, D), float("nan"), dtype=torch.float32, device="cuda")
+    st = None if state is None else tuple(dev(s) for s in state)
+    out = L.slstm_fwd(dev(pre), dev(R), state=st, want_state=want_state, h=h)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_state(gpu, ref, T):
+    """h and the readout ratio c / n to 1e-4. The true-unit scale exp(m) c,
+    exp(m) n is held to a bound from float32 arithmetic on the stabiliser:
+    with the exponential forget gate m grows by f~ each step, each step's
+    exponent f~ + m_{t-1} - m_t carries up to one float32 ulp of |m|, and
+    these add over at most T steps."""
+    c, n, m, hh = (host(t) for t in gpu)
+    cr, nr, mr, hr = ref
+    assert rel_err(hh, hr) <= TOL
+    assert rel_err(c / n, cr / nr) <= TOL
+    tol_scale = TOL + 2.0 * T * float(np.max(np.abs(mr))) * 2.0 ** -23
+    sc = np.exp(m - mr)
+    assert rel_err(sc * c, cr) <= tol_scale
+    assert rel_err(sc * n, nr) <= tol_scale
+
+
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_slstm_matches_oracle(D, with_state):
+    L = _lib()
+    B, H, T = 3, 2, 96
+    say(f"slstm B={B} H={H} T={T} D={D} state={with_state}")
+    pre, R = make_slstm_inputs(B, H, T, D, seed=D + with_state)
+    st = make_slstm_state(B, H, D, seed=7) if with_state else None
+    h, gst = run(L, pre, R, st)
+    ref, rst = so.slstm_recurrent(pre, R, st)
+    assert rel_err(host(h), ref) <= TOL
+    check_state(gst, rst, T)
+
+
+@pytest.mark.parametrize("f_mean", [-4.0, 4.0])
+def test_slstm_strong_and_weak_forgetting(f_mean):
+    L = _lib()
+    B, H, T, D = 2, 2, 200, 64
+    say(f"slstm f_mean={f_mean}")
+    pre, R = make_slstm_inputs(B, H, T, D, seed=11, f_mean=f_mean)
+    h, gst = run(L, pre, R)
+    ref, rst = so.slstm_recurrent(pre, R)
+    assert rel_err(host(h), ref) <= TOL
+    check_state(gst, rst, T)
+
+
+def test_slstm_long_sequence_full_width():
+    """D = 128 over 1024 steps, several sequences side by side."""
+    L = _lib()
+    B, H, T, D = 2, 4, 1024, 128
+    say(f"slstm long B={B} H={H} T={T} D={D}")
+    pre, R = make_slstm_inputs(B, H, T, D, seed=21)
+    h, gst = run(L, pre, R)
+    ref, rst = so.slstm_recurrent(pre, R)
+    assert rel_err(host(h), ref) <= TOL
+    check_state(gst, rst, T)
+
+
+def test_slstm_split_and_resume_bitwise():
+    """Two calls joined through the state equal one call bit for bit: the
+    state is carried in float32 in both cases."""
+    L = _lib()
+    B, H, T, D = 2, 3, 77, 32
+    say("slstm split/resume")
+    pre, R = make_slstm_inputs(B, H, T, D, seed=31)
+    h, st = run(L, pre, R)
+    h1, st1 = run(L, pre[:, :40], R)
+    h2, st2 = run(L, pre[:, 40:], R, state=tuple(host(s) for s in st1))
+    assert torch.equal(torch.cat([h1, h2], dim=1), h)
+    for a, b in zip(st, st2):
+        assert torch.equal(a, b)
+
+
+def test_slstm_empty_sequence_copies_state():
+    L = _lib()
+    B, H, D = 2, 2, 16
+    say("slstm T=0")
+    st = make_slstm_state(B, H, D, seed=41)
+    pre = np.zeros((B, 0, 4, H, D), dtype=np.float32)
+    R = make_slstm_inputs(1, H, 1, D, seed=42)[1]
+    h, out = run(L, pre, R, state=st)
+    assert h.numel() == 0
+    for a, b in zip(out, st):
+        assert np.array_equal(host(a), b.astype(np.float64))
+
+
+def test_slstm_heads_independent_on_gpu():
+    L = _lib()
+    B, H, T, D = 2, 3, 40, 64
+    say("slstm head independence")
+    pre, R = make_slstm_inputs(B, H, T, D, seed=51)
+    h = host(run(L, pre, R, want_state=False))
+    R2 = R.copy()
+    R2[2] *= -2.0
+    h2 = host(run(L, pre, R2, want_state=False))
+    assert np.array_equal(h[:, :, :2], h2[:, :, :2])
+    assert not np.allclose(h[:, :, 2], h2[:, :, 2])
