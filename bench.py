@@ -31,6 +31,8 @@ MFMA_BF16_PEAK = 2.5166e15   # flop/s dense bf16: 256 CU x 2.4 GHz x 4096 flop/c
 METRIC = "mLSTM fwd tokens/s at 7B-layer shape, % bf16 MFMA peak; decode step % HBM BW"
 WORKLOAD = dict(B=1, H=8, T=8192, d_qk=256, d_v=512)
 DECODE = dict(B=64, H=8, d_qk=256, d_v=512, prefill=512)
+SLSTM = dict(B=16, H=8, D=128, T=2048)   # sLSTM recurrence: 128 sequence-heads of 128 cells
+FP32_PEAK = 157.3e12          # flop/s float32 vector (FMA = 2 flops), 256 CUs
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_kernel_7b_layer_traffic.md")
 KERNEL_SRC = os.path.join(ROOT, "linear_recurrent_sequence_fwd_amd", "csrc", "mlstm_fused.hip")
 TILE = 64                    # tokens per tile: the length of the quadratic (intra-tile) form
@@ -246,6 +248,54 @@ def time_decode(torch, M, ev, steps, warmup):
     return elapsed, k_us
 
 
+def slstm_flops(B, H, T, D):
+    """Flops of the sLSTM recurrence as computed: per step and cell the four
+    recurrent dot products (2 * 4 * D) plus about 24 for the gates, the
+    stabiliser and the cell update."""
+    return B * H * T * D * (8 * D + 24)
+
+
+def time_slstm(torch, reps, warmup):
+    """Event-timed sLSTM forward calls (one kernel each) on the current stream."""
+    from linear_recurrent_sequence_fwd_amd import _lib
+    from linear_recurrent_sequence_fwd_amd.inputs import make_slstm_inputs
+    B, H, T, D = SLSTM["B"], SLSTM["H"], SLSTM["T"], SLSTM["D"]
+    pre, R = make_slstm_inputs(B, H, T, D, seed=5)
+    pre_d, R_d = torch.from_numpy(pre).cuda(), torch.from_numpy(R).cuda()
+    h = torch.empty((B, T, H, D), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        _lib.slstm_fwd(pre_d, R_d, h=h)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        _lib.slstm_fwd(pre_d, R_d, h=h)
+    e1.record()
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(h).all())
+    return e0.elapsed_time(e1) / reps * 1e-3, pre, R
+
+
+def slstm_cpu_baseline(pre, R, budget_s=8.0):
+    """The sLSTM oracle recurrence on one host thread over all sequences and
+    heads, as many leading steps as fit the budget."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle.slstm_oracle import slstm_step
+    B, T, _, H, D = pre.shape
+    c = np.zeros((B, H, D)); n = np.zeros((B, H, D)); m = np.zeros((B, H, D)); h = np.zeros((B, H, D))
+    done = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while done < T and time.perf_counter() - t0 < budget_s:
+            c, n, m, h = slstm_step(pre[:, done], R, c, n, m, h)
+            done += 1
+        el = time.perf_counter() - t0
+    return {"value": B * done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"float64 NumPy sLSTM step recurrence, B={B} H={H} D={D}, first {done} of {T} "
+                      f"steps ({el:.1f} s, one thread)"}
+
+
 def cpu_baseline(x, budget_s=15.0):
     """The oracle recurrence on the host, all heads, as many leading tokens as fit the budget."""
     import numpy as np
@@ -340,6 +390,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the replayed-graph timing")
     ap.add_argument("--no-clock", action="store_true", help="skip the shader clock measurement")
+    ap.add_argument("--no-slstm", action="store_true", help="skip the sLSTM recurrence measurement")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
@@ -461,6 +512,24 @@ def main():
                          "hbm_frac": db / (k_us * 1e-6) / HBM_PEAK,
                          "hbm_frac_wall": db / (us_step * 1e-6) / HBM_PEAK}
         log(f"[bench] decode {us_step:.1f} us/step wall, kernel {k_us:.1f} us")
+
+    if not args.no_slstm:
+        B, H, T, D = SLSTM["B"], SLSTM["H"], SLSTM["T"], SLSTM["D"]
+        log(f"[bench] sLSTM B={B} H={H} T={T} D={D}")
+        sec, pre, R = time_slstm(torch, 10, 2)
+        fl = slstm_flops(B, H, T, D)
+        # one workgroup per sequence-head runs on one CU: the launch can use at
+        # most B * H of the 256 CUs' float32 peak
+        peak = FP32_PEAK * min(1.0, B * H / 256)
+        out["slstm"] = {"workload": f"slstm_fwd B={B} H={H} D={D} T={T} float32",
+                        "ms_per_call": sec * 1e3, "us_per_step": sec / T * 1e6,
+                        "tokens_per_s": B * T / sec,
+                        "roofline": {"bound": "alu", "achieved": fl / sec / 1e12, "peak": peak / 1e12,
+                                     "unit": "TFLOP/s", "frac": fl / sec / peak,
+                                     "note": "float32 vector peak of the B*H CUs the launch occupies"}}
+        log(f"[bench] sLSTM {sec * 1e3:.3f} ms per call, {sec / T * 1e6:.3f} us per step")
+        if not args.no_cpu_baseline:
+            out["slstm"]["cpu_baseline"] = slstm_cpu_baseline(pre, R)
 
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
