@@ -67,18 +67,11 @@ __device__ __forceinline__ bf16x8 frag_tr(const __bf16* X, int P, int kin0, int 
 // With this layout the tiles 2 s and 2 s + 1 of a lane hold the eight
 // consecutive k = 32 s + 8 g .. + 7, the order of a plain 16-byte row read of
 // Q or K, so the state packs directly into operand fragments.
-__device__ __forceinline__ bf16x8 frag_trk(const __bf16* X, int P, int kin0, int kx, int lane) {
-  const int i = lane & 15, g = lane >> 4;
-  const __bf16* p = X + (kin0 + 8 * g + (i >> 2)) * P + 32 * (kx >> 1) + 4 * (kx & 1) + 8 * (i & 3);
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 4 * P));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// frag_trk in two parts: lane_off_trk is the lane's element offset for tile
-// kx0 (even) at kin0 = 0, passed through an empty asm statement so that the
-// compiler keeps it whole; frag_trk_at adds the constant part of tile kx0 + x
-// at kin0. Each read address is then one step from the array X, which lets
+//
+// The address is formed in two parts: lane_off_trk is the lane's element
+// offset for tile kx0 (even) at kin0 = 0, passed through an empty asm
+// statement so that the compiler keeps it whole; frag_trk_at adds the
+// constant part of tile kx0 + x at kin0. Each read address is then one step from the array X, which lets
 // the compiler tell which LDS array a read touches (and not wait for copies
 // in flight into other arrays).
 __device__ __forceinline__ int lane_off_trk(int P, int kx0, int lane) {
@@ -1158,7 +1151,7 @@ __device__ __forceinline__ void local_body(const SegArgs& a, char* smem, const L
   constexpr int KP = L::KP, VP = L::VP;
   constexpr int KX = K / 16, NW = LocWaves<K>::value, KXW = KX / NW, VY = kVB / 16;
   static_assert(KX % NW == 0, "KX / NW row tiles per compute wave");
-  const int64_t BH = a.BH, T = a.T, V = a.V, Nt = a.Nt;
+  const int64_t BH = a.BH, V = a.V;
   const int nvb = (int)(V / kVB);
   const int64_t bh = blockIdx.x % BH;
   const int64_t rest = blockIdx.x / BH;
