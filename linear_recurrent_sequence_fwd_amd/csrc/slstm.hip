@@ -9,11 +9,16 @@
 // j / D, cell j % D) in registers, so the matrix is read from memory once.
 // Per step:
 //   1. thread j: gate preactivation P_t[j] + R[j] . h_{t-1}, with h_{t-1}
-//      broadcast from LDS as 16-byte reads; P_{t+1} is prefetched;
+//      broadcast from LDS as 16-byte reads; P_{t+1} is prefetched. The
+//      threads of gate z apply tanh and those of gate o the sigmoid here, so
+//      that the four gates' waves share the transcendental work;
 //   2. barrier; threads d < D take the four gates of cell d, update m, c, n
 //      in registers, form h_t[d], store it to HBM and to the other half of a
 //      double-buffered LDS vector;
 //   3. barrier.
+// Exponentials use the hardware base-2 exponential with the argument scaled
+// by log2(e), tanh(x) = 1 - 2 / (exp(2x) + 1) and the divisions the hardware
+// reciprocal: a few ulp each, far inside the float32 bar of 1e-4.
 // The work per step is 4 D^2 fused multiply-adds spread over the workgroup
 // plus two barriers, so a step is bound by issue latency, not by HBM or the
 // ALUs; throughput comes from running the B * H sequences side by side.
@@ -29,6 +34,15 @@ namespace mlstm_impl {
 namespace {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+// 1 - 2 / (e^{2x} + 1): exact limits +-1 for large |x| (e^{2x} -> inf or 0)
+__device__ __forceinline__ float tanh_fast(float x) {
+  return fmaf(-2.f, __builtin_amdgcn_rcpf(exp_fast(2.f * x) + 1.f), 1.f);
+}
+__device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.f + exp_fast(-x)); }
 
 template <int D>
 __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
@@ -82,16 +96,17 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
       acc0 = fmaf(r[4 * k + 2], x[2], acc0);
       acc1 = fmaf(r[4 * k + 3], x[3], acc1);
     }
-    s_g[j] = acc0 + acc1;
-    __syncthreads();   // all gate preactivations of step t formed
+    const float gp = acc0 + acc1;
+    s_g[j] = g == 2 ? tanh_fast(gp) : (g == 3 ? sigmoid_fast(gp) : gp);
+    __syncthreads();   // all gates of step t formed
     if (j < D) {
       const float it = s_g[j], ft = s_g[D + j], zt = s_g[2 * D + j], ot = s_g[3 * D + j];
       const float mn = fmaxf(m + ft, it);
-      const float fa = expf(ft + m - mn), ia = expf(it - mn);
-      c = fa * c + ia * tanhf(zt);
+      const float fa = exp_fast(ft + m - mn), ia = exp_fast(it - mn);
+      c = fa * c + ia * zt;
       n = fa * n + ia;
       m = mn;
-      hv = c / (fmaxf(n, FLT_MIN) * (1.f + expf(-ot)));   // sigmoid(o~) c / n
+      hv = ot * c * __builtin_amdgcn_rcpf(fmaxf(n, FLT_MIN));   // sigmoid(o~) c / n
       s_h[(t + 1) & 1][j] = hv;
       hout[t * H * D] = hv;
     }
