@@ -93,7 +93,7 @@ def kernel_bytes(name, B, H, T, K, V, chunk):
     BH = B * H
     Nt = -(-T // TILE)
     S = -(-Nt // (chunk // TILE))
-    state = 2 * V * K + 4 * K + 8                  # one chunk state: C~ (bf16), n~ (float32), stabiliser
+    state = 4 * (V * K + K) + 8                    # one float32 chunk state C~, n~ and its stabiliser
     gate_tok = 3 * 8 + 4                           # u, b, mp (float64) and rs (int32)
     if name == "gate":
         return BH * T * (4 + 4 + gate_tok + 4) + BH * Nt * (8 + 8 + 4)

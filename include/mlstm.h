@@ -90,8 +90,7 @@ typedef struct mlstm_fwd_args {
  * of 64 in [64, 8192]; T need not be a multiple of it (the last chunk is
  * ragged). Kernels: gate prefix sums over 64-token tiles; the inter-chunk
  * state (each chunk's local end state, then their in-order fold into every
- * chunk's start state: float32 arithmetic, C~ stored in bf16 between the
- * kernels, n~ and the stabilisers in float32/float64); and the output kernel, which walks each
+ * chunk's start state, all float32); and the output kernel, which walks each
  * chunk's tiles from its start state with decay-masked Q K^T, P V, the
  * carried-state term and the state update on MFMA. (bfloat16 with d_v a
  * multiple of 128; other shapes run a two-pass variant that stores every

@@ -153,7 +153,7 @@ WsLayout layout_fused(int64_t BH, int64_t T, int chunk, int64_t K, int64_t V) {
   size_t off = w.total;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
   const int64_t ns = fs.S - 1;
-  w.Cseg = take(BH * ns * V * K * 2);   // bf16
+  w.Cseg = take(BH * ns * V * K * 4);
   w.nseg = take(BH * ns * K * 4);
   w.mloc = take(BH * ns * 8);
   w.mstart = take(BH * ns * 8);
@@ -258,7 +258,7 @@ int mlstm_fwd_chunkwise(const mlstm_fwd_args* a, int chunk, void* workspace, siz
     mlstm_impl::GateBuffers gb = gate_buffers(ws, w);
     gb.wb = reinterpret_cast<uint16_t*>(ws + w.wb);
     mlstm_impl::SegStates ss;
-    ss.C = reinterpret_cast<__bf16*>(ws + w.Cseg);
+    ss.C = reinterpret_cast<float*>(ws + w.Cseg);
     ss.n = reinterpret_cast<float*>(ws + w.nseg);
     ss.mloc = reinterpret_cast<double*>(ws + w.mloc);
     ss.mstart = reinterpret_cast<double*>(ws + w.mstart);

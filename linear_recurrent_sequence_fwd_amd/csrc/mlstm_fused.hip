@@ -13,9 +13,7 @@
 //                      tiles on MFMA; a loader wave streams the tiles into
 //                      double-buffered LDS with direct-to-LDS loads.
 //   seg_combine_kernel folds the chunks' local end states in order into the
-//                      start state of every chunk (elementwise, float32
-//                      arithmetic; C~ is stored in bf16 between the kernels,
-//                      as the chunk states of the two-pass bf16 path are).
+//                      start state of every chunk (elementwise, float32).
 //   out_kernel_fused   one workgroup per (head, 128 value columns, chunk).
 //                      Holds its 128 x d_qk slice of C~ (float32) in MFMA
 //                      accumulators, split over its waves by halves of d_qk
@@ -71,9 +69,9 @@ __device__ __forceinline__ bf16x8 frag_tr(const __bf16* X, int P, int kin0, int 
 // The address is formed in two parts: lane_off_trk is the lane's element
 // offset for tile kx0 (even) at kin0 = 0, passed through an empty asm
 // statement so that the compiler keeps it whole; frag_trk_at adds the
-// constant part of tile kx0 + x at kin0. Each read address is then one step from the array X, which lets
-// the compiler tell which LDS array a read touches (and not wait for copies
-// in flight into other arrays).
+// constant part of tile kx0 + x at kin0. Each read address is then one step
+// from the array X, which lets the compiler tell which LDS array a read
+// touches (and not wait for copies in flight into other arrays).
 __device__ __forceinline__ int lane_off_trk(int P, int kx0, int lane) {
   const int i = lane & 15, g = lane >> 4;
   int off = (8 * g + (i >> 2)) * P + 16 * kx0 + 8 * (i & 3);
@@ -175,7 +173,7 @@ struct SegArgs {
   __bf16* h;
   GateBuffers gb;            // per 64-token tile
   const float *C0, *n0, *m0;
-  __bf16* Cseg;              // [BH][S-1][V][K] bf16: chunk-local end states, then start states of chunks 1..S-1
+  float* Cseg;               // [BH][S-1][V][K]: chunk-local end states, then start states of chunks 1..S-1
   float* nseg;               // [BH][S-1][K]
   double* mloc;              // [BH][S-1] local end stabiliser
   double* mstart;            // [BH][S-1] stabiliser at the start of chunks 1..S-1
@@ -361,33 +359,25 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
   double m_start;
   bool has_state;
   const float* ninit = nullptr;
-  // the first chunk starts from the caller's float32 state (or zero), the
-  // others from the folded bf16 chunk states
-  auto state_off = [&](int x, int cv) { return (vcol0 + 32 * cg + 16 * cv + i) * K + state_k0(kxg(x), g); };
+  const float* Cinit = nullptr;
   if (seg == 0) {
-    const float* Cinit = a.C0 ? a.C0 + bh * V * K : nullptr;
+    Cinit = a.C0 ? a.C0 + bh * V * K : nullptr;
     ninit = a.C0 ? a.n0 + bh * K : nullptr;
     m_start = a.C0 ? (double)a.m0[bh] : 0.0;
     has_state = a.C0 != nullptr;
-#pragma unroll
-    for (int x = 0; x < KXH; ++x)
-#pragma unroll
-      for (int cv = 0; cv < 2; ++cv)
-        Ct[x][cv] = Cinit ? *reinterpret_cast<const f32x4*>(Cinit + state_off(x, cv)) : f32x4{0.f, 0.f, 0.f, 0.f};
   } else {
     const int64_t sidx = bh * nseg1 + seg - 1;
-    const __bf16* Cinit = a.Cseg + sidx * V * K;
+    Cinit = a.Cseg + sidx * V * K;
     ninit = a.nseg + sidx * K;
     m_start = a.mstart[sidx];
     has_state = true;
-#pragma unroll
-    for (int x = 0; x < KXH; ++x)
-#pragma unroll
-      for (int cv = 0; cv < 2; ++cv) {
-        const bf16x4 c4 = *reinterpret_cast<const bf16x4*>(Cinit + state_off(x, cv));
-        Ct[x][cv] = f32x4{(float)c4[0], (float)c4[1], (float)c4[2], (float)c4[3]};
-      }
   }
+#pragma unroll
+  for (int x = 0; x < KXH; ++x)
+#pragma unroll
+    for (int cv = 0; cv < 2; ++cv)
+      Ct[x][cv] = Cinit ? *reinterpret_cast<const f32x4*>(Cinit + (vcol0 + 32 * cg + 16 * cv + i) * K + state_k0(kxg(x), g))
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
   // normaliser tiles of the wave: local tiles KXN cg .. + KXN - 1 of its half
   auto nx = [&](int x) { return KXN * cg + x; };
   auto n_live = [&](int x) { return nx(x) < KXH; };
@@ -1234,15 +1224,12 @@ __device__ __forceinline__ void local_body(const SegArgs& a, char* smem, const L
   const float fD = (float)exp(sc.logD);
   const Lanes le = fresh_lanes();
   const int64_t sidx = bh * (a.S - 1) + seg;
-  __bf16* Cdst = a.Cseg + sidx * V * K;
+  float* Cdst = a.Cseg + sidx * V * K;
 #pragma unroll
   for (int x = 0; x < KXW; ++x)
 #pragma unroll
-    for (int y = 0; y < VY; ++y) {
-      const f32x4 c = fD * Ct[x][y];
-      *reinterpret_cast<bf16x4*>(Cdst + (vcol0 + 16 * y + le.i) * K + 16 * (KXW * w + x) + 4 * le.g) =
-          bf16x4{(__bf16)c[0], (__bf16)c[1], (__bf16)c[2], (__bf16)c[3]};
-    }
+    for (int y = 0; y < VY; ++y)
+      *reinterpret_cast<f32x4*>(Cdst + (vcol0 + 16 * y + le.i) * K + 16 * (KXW * w + x) + 4 * le.g) = fD * Ct[x][y];
   if (vb == 0) {
     float* ndst = a.nseg + sidx * K;
 #pragma unroll
@@ -1288,7 +1275,7 @@ __global__ __launch_bounds__(64 * (LocWaves<K>::value + 1)) void local_kernel(Se
 
 struct CombineArgs {
   const float *C0, *n0, *m0;
-  __bf16* Cseg;
+  float* Cseg;
   float* nseg;
   const double* mloc;
   double* mstart;
@@ -1301,54 +1288,33 @@ struct CombineArgs {
 // (C~, m) of chunk s and its local end state (C~loc, mloc) and log-forget total
 // G, the start of chunk s+1 is m' = max(m + G, mloc),
 // C~' = exp(m + G - m') C~ + exp(mloc - m') C~loc (the same for n~). Each
-// thread owns eight consecutive elements of one head's C~ (bf16) or n~
-// (float32) and carries the running start state in float32 registers; the
-// result overwrites the local state in place.
+// thread owns four consecutive floats of one head's C~ or n~; the result
+// overwrites the local state in place.
 __global__ __launch_bounds__(kThreads) void seg_combine_kernel(CombineArgs a) {
   const int64_t BH = a.BH;
   const int64_t bh = blockIdx.x % BH;
   const int64_t u = (blockIdx.x / BH) * kThreads + threadIdx.x;
-  const int64_t nc8 = a.V * a.K / 8, nn8 = a.K / 8;
-  if (u >= nc8 + nn8) return;
-  const bool is_n = u >= nc8;
-  const int64_t off = is_n ? (u - nc8) * 8 : u * 8;
+  const int64_t nc4 = a.V * a.K / 4, nn4 = a.K / 4;
+  if (u >= nc4 + nn4) return;
+  const bool is_n = u >= nc4;
+  const int64_t off = is_n ? (u - nc4) * 4 : u * 4;
   const int64_t stride = is_n ? a.K : a.V * a.K;
-  struct F8 {
-    f32x4 lo, hi;
-  };
-  auto ld8 = [&](int64_t sidx) -> F8 {
-    if (is_n) {
-      const float* p = a.nseg + off + sidx * stride;
-      return F8{*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4)};
-    }
-    const bf16x8 c = *reinterpret_cast<const bf16x8*>(a.Cseg + off + sidx * stride);
-    return F8{f32x4{(float)c[0], (float)c[1], (float)c[2], (float)c[3]},
-              f32x4{(float)c[4], (float)c[5], (float)c[6], (float)c[7]}};
-  };
-  auto st8 = [&](int64_t sidx, const F8& x) {
-    if (is_n) {
-      float* p = a.nseg + off + sidx * stride;
-      *reinterpret_cast<f32x4*>(p) = x.lo;
-      *reinterpret_cast<f32x4*>(p + 4) = x.hi;
-    } else {
-      *reinterpret_cast<bf16x8*>(a.Cseg + off + sidx * stride) =
-          bf16x8{(__bf16)x.lo[0], (__bf16)x.lo[1], (__bf16)x.lo[2], (__bf16)x.lo[3],
-                 (__bf16)x.hi[0], (__bf16)x.hi[1], (__bf16)x.hi[2], (__bf16)x.hi[3]};
-    }
-  };
-  F8 x = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  float* base = (is_n ? a.nseg : a.Cseg) + off;
+  f32x4 x = {0.f, 0.f, 0.f, 0.f};
   double m = 0.0;
   if (a.C0) {
-    const float* p = (is_n ? a.n0 + bh * a.K : a.C0 + bh * a.V * a.K) + off;
-    x = F8{*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4)};
+    x = *reinterpret_cast<const f32x4*>((is_n ? a.n0 + bh * a.K : a.C0 + bh * a.V * a.K) + off);
     m = (double)a.m0[bh];
   }
   const int64_t ns = a.S - 1;
   constexpr int B = 8;
   for (int64_t s0 = 0; s0 < ns; s0 += B) {
-    F8 y[B];
+    f32x4 y[B];
 #pragma unroll
-    for (int e = 0; e < B; ++e) y[e] = ld8(bh * ns + min(s0 + e, ns - 1));
+    for (int e = 0; e < B; ++e) {
+      const int64_t s = min(s0 + e, ns - 1);
+      y[e] = *reinterpret_cast<const f32x4*>(base + (bh * ns + s) * stride);
+    }
 #pragma unroll
     for (int e = 0; e < B; ++e) {
       const int64_t s = s0 + e;
@@ -1360,9 +1326,8 @@ __global__ __launch_bounds__(kThreads) void seg_combine_kernel(CombineArgs a) {
         if (mn == -INFINITY) mn = 0.0;
         const float al = mc == -INFINITY ? 0.f : expf((float)(mc - mn));
         const float be = ml == -INFINITY ? 0.f : expf((float)(ml - mn));
-        x.lo = al * x.lo + be * y[e].lo;
-        x.hi = al * x.hi + be * y[e].hi;
-        st8(sidx, x);
+        x = al * x + be * y[e];
+        *reinterpret_cast<f32x4*>(base + sidx * stride) = x;
         if (u == 0) a.mstart[sidx] = mn;
         m = mn;
       }
@@ -1392,7 +1357,7 @@ hipError_t run_seg(const FwdLaunch& f, const GateBuffers& gb, const SegStates& s
     c.C0 = f.C0; c.n0 = f.n0; c.m0 = f.m0;
     c.Cseg = ss.C; c.nseg = ss.n; c.mloc = ss.mloc; c.mstart = ss.mstart; c.Gseg = ss.G;
     c.V = f.V; c.K = K; c.BH = f.BH; c.S = ss.S;
-    const int64_t units = f.V * K / 8 + K / 8;
+    const int64_t units = f.V * K / 4 + K / 4;
     const int64_t blocks = (units + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(f.BH * blocks)), dim3(kThreads), 0, s, c);
     mark_after(K_STATE, s);

@@ -37,12 +37,12 @@ struct ChunkStates {
 };
 
 // Chunk states of the fused path (mlstm_fused.hip), S chunks of TPS 64-token
-// tiles: C [BH][S-1][V][K] bf16 and n [BH][S-1][K] float32 hold each chunk's
-// local end state and then, folded in order, the start states of chunks 1..S-1;
+// tiles: C [BH][S-1][V][K] and n [BH][S-1][K] float32 hold each chunk's local
+// end state and then, folded in order, the start states of chunks 1..S-1;
 // mloc, mstart and G [BH][S-1] float64 are the local end stabiliser, the start
 // stabiliser and the chunk's log-forget total.
 struct SegStates {
-  __bf16* C;
+  float* C;
   float* n;
   double* mloc;
   double* mstart;

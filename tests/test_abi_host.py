@@ -174,7 +174,7 @@ def test_workspace_checks_and_size():
 
 def test_fused_workspace_size():
     """bf16 with d_v a multiple of 128: per-token gate data, per-tile scalars and
-    split weights, and one state per chunk boundary (C~ in bf16, n~ in float32)."""
+    split weights, and one float32 state per chunk boundary."""
     lib = L.lib()
     a = fake_fwd(B=2, H=3, T=1000, K=128, V=256, dtype=L.MLSTM_BF16)
     need = lib.mlstm_fwd_chunkwise_workspace_size(ctypes.byref(a), 256)
@@ -184,7 +184,7 @@ def test_fused_workspace_size():
     ns = S - 1
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     expect = 3 * al(BH * T * 8) + 2 * al(BH * T * 4) + 2 * al(BH * Nt * 8) + al(BH * Nt * 4) \
-        + al(BH * ns * V * K * 2) + al(BH * ns * K * 4) + 3 * al(BH * ns * 8) + al(BH * Nt * 2 * 64 * 2)
+        + al(BH * ns * V * K * 4) + al(BH * ns * K * 4) + 3 * al(BH * ns * 8) + al(BH * Nt * 2 * 64 * 2)
     assert need == expect
 
 
