@@ -116,6 +116,13 @@ __device__ __forceinline__ float sum_rows(float x) {
   return __builtin_bit_cast(float, (unsigned)b[0]) + __builtin_bit_cast(float, (unsigned)b[1]);
 }
 
+// exp of a float64 argument in float32: the argument is scaled by log2(e) in
+// float64 and rounded once, then the hardware base-2 exponential (about one
+// ulp) takes it; results below the float32 normal range flush to zero.
+__device__ __forceinline__ float exp_f64arg(double x) {
+  return __builtin_amdgcn_exp2f((float)(x * 1.4426950408889634));
+}
+
 __device__ __forceinline__ double readlane_f64(double x, int lane) {
   const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
   const unsigned lo = __builtin_amdgcn_readlane((unsigned)u, lane);
@@ -529,7 +536,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
     const double logD_next = rescale ? 0.0 : logD + ld;
     const int j = fresh_lanes().lane;
     if (w == 0) {
-      const float wj = (j >= t_R && j < Lc && t_U != -INFINITY) ? expf((float)(r_u - Rm - logD_next)) : 0.f;
+      const float wj = (j >= t_R && j < Lc && t_U != -INFINITY) ? exp_f64arg(r_u - Rm - logD_next) : 0.f;
       tb.w[j] = wj;
       const __bf16 whi = (__bf16)wj;
       tb.wb[j] = whi;
@@ -553,9 +560,9 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
         tb.u2[j] = valid ? (float)((r_u - ref) * (double)kLog2eF) : -INFINITY;
         tb.rs[j] = r_rs;
       } else if (w == 2) {
-        tb.sc[j] = (valid && carry) ? expf((float)(m - r + logD)) : 0.f;
+        tb.sc[j] = (valid && carry) ? exp_f64arg(m - r + logD) : 0.f;
       } else {
-        tb.fl[j] = valid ? expf((float)(-(r_b + r))) : 1.f;
+        tb.fl[j] = valid ? exp_f64arg(-(r_b + r)) : 1.f;
       }
     }
   };
