@@ -15,9 +15,11 @@
  * library runs the recurrence. R mixes the cells of one head only (the xLSTM
  * paper's heads without memory mixing across heads); one head of width D is
  * a full recurrent matrix. The forget gate is exponential, as the equations
- * write it. c / n is evaluated as c / max(n, FLT_MIN): n > 0 always holds in
- * exact arithmetic, and the floor only keeps an underflowed first step from
- * the zero state (i~ - f~ < -87) finite.
+ * write it. Without a given state the recurrence starts from zero c, n, h;
+ * its stabiliser starts at -inf rather than the listing's 0, which changes
+ * neither h nor the true-unit state (exp(m) c, exp(m) n) and keeps n >= 1 at
+ * every step, so that c / n cannot underflow in float32 (a requested final
+ * state after T = 0 reports m = 0). Preactivations must be finite.
  *
  * Conventions are those of mlstm.h: DEVICE pointers, contiguous row-major
  * arrays, caller-owned buffers and stream, no allocation or synchronisation

@@ -67,9 +67,13 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
       r[4 * k + 3] = x[3];
     }
   }
-  // cell state: thread d < D owns cell d
+  // cell state: thread d < D owns cell d. The zero state starts from
+  // m_0 = -inf instead of 0: the same h and the same true-unit state in exact
+  // arithmetic (a stabiliser shift of an all-zero state changes nothing), and
+  // then n_t >= 1 at every step (m_t = i~_t gives exp(i~_t - m_t) = 1, else
+  // the forget factor is 1 and n_t >= n_{t-1}), so c / n cannot underflow.
   const int64_t sidx = (b * H + hh) * D + j;
-  float c = 0.f, n = 0.f, m = 0.f, hv = 0.f;
+  float c = 0.f, n = 0.f, m = -INFINITY, hv = 0.f;
   if (j < D && a.c0) {
     c = a.c0[sidx];
     n = a.n0[sidx];
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
   if (j < D && a.c_out) {
     a.c_out[sidx] = c;
     a.n_out[sidx] = n;
-    a.m_out[sidx] = m;
+    a.m_out[sidx] = (T == 0 && !a.c0) ? 0.f : m;   // the zero state reports m = 0
     a.h_out[sidx] = hv;
   }
 }

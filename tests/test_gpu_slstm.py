@@ -148,3 +148,22 @@ def test_slstm_heads_independent_on_gpu():
     h2 = host(run(L, pre, R2, want_state=False))
     assert np.array_equal(h[:, :, :2], h2[:, :, :2])
     assert not np.allclose(h[:, :, 2], h2[:, :, 2])
+
+
+def test_slstm_large_preactivations():
+    """Preactivations of size 30 (every gate saturated or near it): parity at
+    the same bar; preactivations of size 1e4: every output finite."""
+    L = _lib()
+    B, H, T, D = 2, 2, 64, 32
+    say("slstm large preactivations")
+    pre, R = make_slstm_inputs(B, H, T, D, seed=61)
+    big = (pre * 30.0).astype(np.float32)
+    h, gst = run(L, big, R)
+    ref, rst = so.slstm_recurrent(big, R)
+    assert rel_err(host(h), ref) <= TOL
+    check_state(gst, rst, T)
+    huge = (pre * 1.0e4).astype(np.float32)
+    h2, st2 = run(L, huge, R)
+    assert np.all(np.isfinite(host(h2)))
+    for t in st2:
+        assert np.all(np.isfinite(host(t)))
