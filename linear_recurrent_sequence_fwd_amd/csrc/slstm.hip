@@ -9,13 +9,16 @@
 // j / D, cell j % D) in registers, so the matrix is read from memory once.
 // Per step:
 //   1. thread j: gate preactivation P_t[j] + R[j] . h_{t-1}, with h_{t-1}
-//      broadcast from LDS as 16-byte reads; P_{t+1} is prefetched. The
+//      broadcast from LDS as 16-byte reads (P_t was loaded a block of 8
+//      steps earlier). The
 //      threads of gate z apply tanh and those of gate o the sigmoid here, so
 //      that the four gates' waves share the transcendental work;
 //   2. barrier; threads d < D take the four gates of cell d, update m, c, n
-//      in registers, form h_t[d], store it to HBM and to the other half of a
-//      double-buffered LDS vector;
+//      in registers and write h_t[d] into a ring of the last 8 steps' h in
+//      LDS (the next step reads it there);
 //   3. barrier.
+// Every 8 steps the ring goes to HBM and the next 8 steps' preactivations are
+// loaded, in one batch per thread.
 // Exponentials use the hardware base-2 exponential with the argument scaled
 // by log2(e), tanh(x) = 1 - 2 / (exp(2x) + 1) and the divisions the hardware
 // reciprocal: a few ulp each, far inside the float32 bar of 1e-4.
@@ -51,7 +54,11 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
   const int64_t b = blockIdx.x / H, hh = blockIdx.x % H;
   const int j = threadIdx.x;
   const int g = j / D, e = j % D;
-  __shared__ __attribute__((aligned(16))) float s_h[2][D];
+  // h of the last RB steps: the matrix-vector product of step t reads
+  // h_{t-1} here, and the block's h go to HBM together at the start of the
+  // next block (see below)
+  constexpr int RB = 8;   // (the asm statement below names its 8 registers)
+  __shared__ __attribute__((aligned(16))) float s_hr[RB][D];
   __shared__ float s_g[NT];
 
   // row j of the head's recurrent matrix: gate g of cell e
@@ -80,41 +87,71 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
     m = a.m0[sidx];
     hv = a.h0[sidx];
   }
-  if (j < D) s_h[0][j] = hv;
+  if (j < D) s_hr[RB - 1][j] = hv;
   // P_t[j] sits at pre[((b T + t) 4 + g) H + hh) D + e]
   const int64_t pstride = 4 * H * D;
   const float* pre = a.pre + (b * T * 4 + g) * H * D + hh * D + e;
   float* hout = a.h + (b * T * H + hh) * D + j;
-  float p_next = T > 0 ? pre[0] : 0.f;
-  __syncthreads();
-  for (int64_t t = 0; t < T; ++t) {
-    const float p = p_next;
-    if (t + 1 < T) p_next = pre[(t + 1) * pstride];
-    const f32x4v* hp = reinterpret_cast<const f32x4v*>(s_h[t & 1]);
-    float acc0 = p, acc1 = 0.f;   // two chains halve the dependent FMA latency
+  // The steps run in blocks of RB. At the start of a block the wave takes the
+  // preactivations loaded one block earlier, stores the previous block's h
+  // and loads the next block's preactivations. Loads and stores are then
+  // issued together once per block, and the one wait for loaded data
+  // (which, with stores in flight, waits for every memory operation of the
+  // wave) falls on operations a whole block old.
+  float pn[RB];
 #pragma unroll
-    for (int k = 0; k < D / 4; ++k) {
-      const f32x4v x = hp[k];
-      acc0 = fmaf(r[4 * k], x[0], acc0);
-      acc1 = fmaf(r[4 * k + 1], x[1], acc1);
-      acc0 = fmaf(r[4 * k + 2], x[2], acc0);
-      acc1 = fmaf(r[4 * k + 3], x[3], acc1);
+  for (int q = 0; q < RB; ++q) pn[q] = q < T ? pre[q * pstride] : 0.f;
+  __syncthreads();
+  for (int64_t t0 = 0; t0 < T; t0 += RB) {
+    float pc[RB];
+#pragma unroll
+    for (int q = 0; q < RB; ++q) pc[q] = pn[q];
+    // taken here, before this block's stores and loads are issued
+    asm volatile("" ::"v"(pc[0]), "v"(pc[1]), "v"(pc[2]), "v"(pc[3]), "v"(pc[4]), "v"(pc[5]), "v"(pc[6]),
+                 "v"(pc[7]));
+    if (t0 > 0 && j < D) {
+#pragma unroll
+      for (int q = 0; q < RB; ++q) hout[(t0 - RB + q) * H * D] = s_hr[q][j];
     }
-    const float gp = acc0 + acc1;
-    s_g[j] = g == 2 ? tanh_fast(gp) : (g == 3 ? sigmoid_fast(gp) : gp);
-    __syncthreads();   // all gates of step t formed
-    if (j < D) {
-      const float it = s_g[j], ft = s_g[D + j], zt = s_g[2 * D + j], ot = s_g[3 * D + j];
-      const float mn = fmaxf(m + ft, it);
-      const float fa = exp_fast(ft + m - mn), ia = exp_fast(it - mn);
-      c = fa * c + ia * zt;
-      n = fa * n + ia;
-      m = mn;
-      hv = ot * c * __builtin_amdgcn_rcpf(fmaxf(n, FLT_MIN));   // sigmoid(o~) c / n
-      s_h[(t + 1) & 1][j] = hv;
-      hout[t * H * D] = hv;
+#pragma unroll
+    for (int q = 0; q < RB; ++q) pn[q] = t0 + RB + q < T ? pre[(t0 + RB + q) * pstride] : 0.f;
+#pragma unroll
+    for (int q = 0; q < RB; ++q) {
+      const int64_t t = t0 + q;
+      if (t >= T) break;   // uniform over the workgroup
+      const float p = pc[q];
+      const f32x4v* hp = reinterpret_cast<const f32x4v*>(s_hr[(q + RB - 1) % RB]);
+      float acc0 = p, acc1 = 0.f;   // two chains halve the dependent FMA latency
+#pragma unroll
+      for (int k = 0; k < D / 4; ++k) {
+        const f32x4v x = hp[k];
+        acc0 = fmaf(r[4 * k], x[0], acc0);
+        acc1 = fmaf(r[4 * k + 1], x[1], acc1);
+        acc0 = fmaf(r[4 * k + 2], x[2], acc0);
+        acc1 = fmaf(r[4 * k + 3], x[3], acc1);
+      }
+      const float gp = acc0 + acc1;
+      s_g[j] = g == 2 ? tanh_fast(gp) : (g == 3 ? sigmoid_fast(gp) : gp);
+      __syncthreads();   // all gates of step t formed
+      if (j < D) {
+        const float it = s_g[j], ft = s_g[D + j], zt = s_g[2 * D + j], ot = s_g[3 * D + j];
+        const float mn = fmaxf(m + ft, it);
+        const float fa = exp_fast(ft + m - mn), ia = exp_fast(it - mn);
+        c = fa * c + ia * zt;
+        n = fa * n + ia;
+        m = mn;
+        hv = ot * c * __builtin_amdgcn_rcpf(fmaxf(n, FLT_MIN));   // sigmoid(o~) c / n
+        s_hr[q][j] = hv;
+      }
+      __syncthreads();   // h_t published; s_g free for step t + 1
     }
-    __syncthreads();   // h_t published; s_g free for step t + 1
+  }
+  // the last block's h (each thread stores what it wrote itself)
+  if (T > 0 && j < D) {
+    const int64_t tl = ((T - 1) / RB) * RB;
+#pragma unroll
+    for (int q = 0; q < RB; ++q)
+      if (tl + q < T) hout[(tl + q) * H * D] = s_hr[q][j];
   }
   if (j < D && a.c_out) {
     a.c_out[sidx] = c;
