@@ -43,7 +43,7 @@ typedef struct slstm_fwd_args {
   const float* pre;       /* [B,T,4,H,D] gate preactivations P_t, gates in the order i, f, z, o */
   const float* R;         /* [H,4,D,D] recurrent matrices: gate g of cell e gets sum_d R[h][g][e][d] h_{t-1}[d] */
   float* h;               /* [B,T,H,D] output (written) */
-  const float* c0;        /* optional initial state [B,H,D] each; all four NULL = zero state with m_0 = 0 */
+  const float* c0;        /* optional initial state [B,H,D] each; all four NULL = zero c, n, h (stabiliser as above) */
   const float* n0;
   const float* m0;
   const float* h0;

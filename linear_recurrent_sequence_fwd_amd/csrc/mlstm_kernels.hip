@@ -195,12 +195,6 @@ template <>
 __device__ __forceinline__ void store4<float>(float* p, f32x4 x) {
   *reinterpret_cast<f32x4*>(p) = x;
 }
-template <>
-__device__ __forceinline__ void store4<__bf16>(__bf16* p, f32x4 x) {
-  bf16x4 y;
-  y[0] = (__bf16)x[0]; y[1] = (__bf16)x[1]; y[2] = (__bf16)x[2]; y[3] = (__bf16)x[3];
-  *reinterpret_cast<bf16x4*>(p) = y;
-}
 
 // One workgroup per (head, 64 k x 64 v tile of C). The tile lives in MFMA
 // accumulators as C^T[k][v]: wave (wk, wv) holds 32 x 32 of it, lane l,
