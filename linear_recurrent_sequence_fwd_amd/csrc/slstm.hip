@@ -4,15 +4,18 @@
 //
 // The recurrence is sequential in t: step t needs h_{t-1} of every cell of
 // the head before any of its gates can be formed. One workgroup per (batch
-// entry, head) therefore walks the whole sequence. Thread j of its 4 D
-// threads owns row j of the head's stacked recurrent matrix [4 D][D] (gate
-// j / D, cell j % D) in registers, so the matrix is read from memory once.
+// entry, head) therefore walks the whole sequence. Its 4 D threads hold the
+// head's stacked recurrent matrix [4 D][D] (row g D + e: gate g of cell e) in
+// registers, so the matrix is read from memory once: the quad of threads
+// 4i..4i+3 holds rows 4i..4i+3, each thread one quarter of their columns.
 // Per step:
-//   1. thread j: gate preactivation P_t[j] + R[j] . h_{t-1}, with h_{t-1}
-//      broadcast from LDS as 16-byte reads (P_t was loaded a block of 8
-//      steps earlier). The
-//      threads of gate z apply tanh and those of gate o the sigmoid here, so
-//      that the four gates' waves share the transcendental work;
+//   1. each thread multiplies its 4 x D/4 block with its quarter of h_{t-1}
+//      (D/16 16-byte LDS reads, a quarter of what a whole row would need);
+//      two exchanges within the quad (DPP) leave row j's sum in thread j,
+//      which adds the preactivation P_t[j] (loaded a block of 8 steps
+//      earlier). The threads of gate z apply tanh and those of gate o the
+//      sigmoid here, so that the four gates' waves share the transcendental
+//      work;
 //   2. barrier; threads d < D take the four gates of cell d, update m, c, n
 //      in registers and write h_t[d] into a ring of the last 8 steps' h in
 //      LDS (the next step reads it there);
@@ -47,31 +50,48 @@ __device__ __forceinline__ float tanh_fast(float x) {
 }
 __device__ __forceinline__ float sigmoid_fast(float x) { return __builtin_amdgcn_rcpf(1.f + exp_fast(-x)); }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kQuadXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+
 template <int D>
 __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
   constexpr int NT = 4 * D;
+  constexpr int DS = D / 4;     // cells of h (columns of R) per thread
+  constexpr int HS = DS + 4;    // LDS stride of one quarter of h (the pad spreads the quarters over banks)
   const int64_t H = a.H, T = a.T;
   const int64_t b = blockIdx.x / H, hh = blockIdx.x % H;
   const int j = threadIdx.x;
   const int g = j / D, e = j % D;
-  // h of the last RB steps: the matrix-vector product of step t reads
-  // h_{t-1} here, and the block's h go to HBM together at the start of the
-  // next block (see below)
+  const int qd = j & 3;
+  // h of the last RB steps, each step's h as four padded quarters: the
+  // matrix-vector product of step t reads h_{t-1} here, and the block's h go
+  // to HBM together at the start of the next block (see below)
   constexpr int RB = 8;   // (the asm statement below names its 8 registers)
-  __shared__ __attribute__((aligned(16))) float s_hr[RB][D];
+  __shared__ __attribute__((aligned(16))) float s_hr[RB][4 * HS];
   __shared__ float s_g[NT];
+  auto hpos = [](int cell) { return (cell / DS) * HS + cell % DS; };
 
-  // row j of the head's recurrent matrix: gate g of cell e
-  float r[D];
-  {
-    const f32x4v* src = reinterpret_cast<const f32x4v*>(a.R + ((hh * 4 + g) * D + e) * D);
+  // The quad of threads 4i..4i+3 holds rows 4i..4i+3 of the head's stacked
+  // recurrent matrix [4 D][D] (row g D + e: gate g of cell e), thread 4i + q
+  // the columns of quarter q. Slot s of a thread holds row 4i + sigma(s),
+  // sigma = (0, 2, 1, 3), the order in which the two-step reduction below
+  // leaves row 4i + q's sum in thread 4i + q.
+  float r[4][DS];
 #pragma unroll
-    for (int k = 0; k < D / 4; ++k) {
+  for (int sl = 0; sl < 4; ++sl) {
+    const int row = (j & ~3) + ((sl & 1) << 1) + (sl >> 1);
+    const f32x4v* src = reinterpret_cast<const f32x4v*>(a.R + (hh * NT + row) * D + qd * DS);
+#pragma unroll
+    for (int k = 0; k < DS / 4; ++k) {
       const f32x4v x = src[k];
-      r[4 * k] = x[0];
-      r[4 * k + 1] = x[1];
-      r[4 * k + 2] = x[2];
-      r[4 * k + 3] = x[3];
+      r[sl][4 * k] = x[0];
+      r[sl][4 * k + 1] = x[1];
+      r[sl][4 * k + 2] = x[2];
+      r[sl][4 * k + 3] = x[3];
     }
   }
   // cell state: thread d < D owns cell d. The zero state starts from
@@ -87,7 +107,7 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
     m = a.m0[sidx];
     hv = a.h0[sidx];
   }
-  if (j < D) s_hr[RB - 1][j] = hv;
+  if (j < D) s_hr[RB - 1][hpos(j)] = hv;
   // P_t[j] sits at pre[((b T + t) 4 + g) H + hh) D + e]
   const int64_t pstride = 4 * H * D;
   const float* pre = a.pre + (b * T * 4 + g) * H * D + hh * D + e;
@@ -111,7 +131,7 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
                  "v"(pc[7]));
     if (t0 > 0 && j < D) {
 #pragma unroll
-      for (int q = 0; q < RB; ++q) hout[(t0 - RB + q) * H * D] = s_hr[q][j];
+      for (int q = 0; q < RB; ++q) hout[(t0 - RB + q) * H * D] = s_hr[q][hpos(j)];
     }
 #pragma unroll
     for (int q = 0; q < RB; ++q) pn[q] = t0 + RB + q < T ? pre[(t0 + RB + q) * pstride] : 0.f;
@@ -120,17 +140,23 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
       const int64_t t = t0 + q;
       if (t >= T) break;   // uniform over the workgroup
       const float p = pc[q];
-      const f32x4v* hp = reinterpret_cast<const f32x4v*>(s_hr[(q + RB - 1) % RB]);
-      float acc0 = p, acc1 = 0.f;   // two chains halve the dependent FMA latency
+      const f32x4v* hp = reinterpret_cast<const f32x4v*>(&s_hr[(q + RB - 1) % RB][qd * HS]);
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < D / 4; ++k) {
+      for (int k = 0; k < DS / 4; ++k) {
         const f32x4v x = hp[k];
-        acc0 = fmaf(r[4 * k], x[0], acc0);
-        acc1 = fmaf(r[4 * k + 1], x[1], acc1);
-        acc0 = fmaf(r[4 * k + 2], x[2], acc0);
-        acc1 = fmaf(r[4 * k + 3], x[3], acc1);
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl) acc[sl] = fmaf(r[sl][4 * k + c], x[c], acc[sl]);
       }
-      const float gp = acc0 + acc1;
+      // sum over the quad: after the exchange with the neighbour (lane ^ 1)
+      // a thread keeps two rows, after the one with lane ^ 2 a single row
+      const bool o1 = j & 1, o2 = j & 2;
+      float k0 = o1 ? acc[2] : acc[0], k1 = o1 ? acc[3] : acc[1];
+      k0 += dpp_f<kQuadXor1>(o1 ? acc[0] : acc[2]);
+      k1 += dpp_f<kQuadXor1>(o1 ? acc[1] : acc[3]);
+      const float gp = p + (o2 ? k1 : k0) + dpp_f<kQuadXor2>(o2 ? k0 : k1);
       s_g[j] = g == 2 ? tanh_fast(gp) : (g == 3 ? sigmoid_fast(gp) : gp);
       __syncthreads();   // all gates of step t formed
       if (j < D) {
@@ -141,7 +167,7 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
         n = fa * n + ia;
         m = mn;
         hv = ot * c * __builtin_amdgcn_rcpf(fmaxf(n, FLT_MIN));   // sigmoid(o~) c / n
-        s_hr[q][j] = hv;
+        s_hr[q][hpos(j)] = hv;
       }
       __syncthreads();   // h_t published; s_g free for step t + 1
     }
@@ -151,7 +177,7 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
     const int64_t tl = ((T - 1) / RB) * RB;
 #pragma unroll
     for (int q = 0; q < RB; ++q)
-      if (tl + q < T) hout[(tl + q) * H * D] = s_hr[q][j];
+      if (tl + q < T) hout[(tl + q) * H * D] = s_hr[q][hpos(j)];
   }
   if (j < D && a.c_out) {
     a.c_out[sidx] = c;
