@@ -48,10 +48,12 @@ def slstm_step(pre_t, R, c, n, m, h):
     pre_t [B, 4, H, D]: input-projected preactivations of i, f, z, o;
     R [H, 4, D, D]: per head and gate, row d' maps h_{t-1} of the head to the
     gate preactivation of cell d'; c, n, m, h [B, H, D]: the state.
-    Returns the new (c, n, m, h).
+    Returns the new (c, n, m, h), in the arrays' precision (float64 as
+    slstm_recurrent calls it by default).
     """
-    pre_t = np.asarray(pre_t, dtype=np.float64)
-    R = np.asarray(R, dtype=np.float64)
+    dt = np.asarray(c).dtype
+    pre_t = np.asarray(pre_t, dtype=dt)
+    R = np.asarray(R, dtype=dt)
     rec = np.einsum("hgij,bhj->bghi", R, h)          # R h_{t-1}, per head and gate
     g = pre_t + rec
     it, ft, zt, ot = g[:, 0], g[:, 1], g[:, 2], g[:, 3]
@@ -60,27 +62,31 @@ def slstm_step(pre_t, R, c, n, m, h):
     ia = np.exp(it - m_new)
     c_new = fa * c + ia * np.tanh(zt)
     n_new = fa * n + ia
-    h_new = sigmoid(ot) * c_new / n_new
+    h_new = sigmoid(ot).astype(dt) * c_new / n_new
     return c_new, n_new, m_new, h_new
 
 
-def slstm_recurrent(pre, R, state=None):
+def slstm_recurrent(pre, R, state=None, dtype=np.float64):
     """The step over a whole sequence.
 
     pre [B, T, 4, H, D], R [H, 4, D, D]; state = (c0, n0, m0, h0) [B, H, D] or
     None for the zero state with m_0 = 0. Returns h [B, T, H, D] and the final
     (c, n, m, h).
+
+    dtype=np.float32 evaluates the same equations in float32 arithmetic
+    instead of float64. Tests use it to measure the rounding error that any
+    float32 evaluation of the recurrence carries: with the exponential forget
+    gate the stabiliser m grows without bound over long sequences, and its
+    float32 resolution then sets the error of h.
     """
-    pre = np.asarray(pre, dtype=np.float64)
+    pre = np.asarray(pre, dtype=dtype)
+    R = np.asarray(R, dtype=dtype)
     B, T, _, H, D = pre.shape
     if state is None:
-        c = np.zeros((B, H, D))
-        n = np.zeros((B, H, D))
-        m = np.zeros((B, H, D))
-        h = np.zeros((B, H, D))
+        c, n, m, h = (np.zeros((B, H, D), dtype=dtype) for _ in range(4))
     else:
-        c, n, m, h = (np.asarray(s, dtype=np.float64).copy() for s in state)
-    out = np.zeros((B, T, H, D))
+        c, n, m, h = (np.asarray(s, dtype=dtype).copy() for s in state)
+    out = np.zeros((B, T, H, D), dtype=dtype)
     for t in range(T):
         c, n, m, h = slstm_step(pre[:, t], R, c, n, m, h)
         out[:, t] = h

@@ -167,3 +167,56 @@ def test_slstm_large_preactivations():
     assert np.all(np.isfinite(host(h2)))
     for t in st2:
         assert np.all(np.isfinite(host(t)))
+
+
+@pytest.mark.parametrize("T", [1, 5, 8, 9, 17, 23])
+def test_slstm_ragged_lengths(T):
+    """Lengths below, at and past the kernel's 8-step block, ending in either
+    half of its 16-step ring of h, against the oracle."""
+    L = _lib()
+    B, H, D = 2, 3, 32
+    say(f"slstm ragged T={T}")
+    pre, R = make_slstm_inputs(B, H, T, D, seed=70 + T)
+    st = make_slstm_state(B, H, D, seed=71)
+    h, gst = run(L, pre, R, st)
+    ref, rst = so.slstm_recurrent(pre, R, st)
+    assert rel_err(host(h), ref) <= TOL
+    check_state(gst, rst, T)
+
+
+def test_slstm_more_sequences_than_cus():
+    """B * H = 300 workgroups, more than the 256 compute units."""
+    L = _lib()
+    B, H, T, D = 75, 4, 24, 16
+    say(f"slstm B={B} H={H} T={T} D={D}")
+    pre, R = make_slstm_inputs(B, H, T, D, seed=81)
+    h, gst = run(L, pre, R)
+    ref, rst = so.slstm_recurrent(pre, R)
+    assert rel_err(host(h), ref) <= TOL
+    check_state(gst, rst, T)
+
+
+def test_slstm_full_benchmark_workload():
+    """The measured workload, B = 16, H = 8, D = 128, T = 2048, every output
+    against the oracle (some seconds on the host).
+
+    Over 2048 steps the stabiliser m of some cells reaches several hundred
+    (the exponential forget gate lets it grow as a random walk), where its
+    float32 spacing is ~3e-5, and the error of h in any float32 evaluation
+    passes 1e-4 on a few of the 134M outputs. The bar here is therefore
+    twice the error of the oracle's own equations evaluated in float32,
+    and 1e-4 at least."""
+    L = _lib()
+    B, H, T, D = 16, 8, 2048, 128
+    say(f"slstm full workload B={B} H={H} T={T} D={D}")
+    pre, R = make_slstm_inputs(B, H, T, D, seed=91)
+    h, gst = run(L, pre, R)
+    ref, rst = so.slstm_recurrent(pre, R)
+    h32, _ = so.slstm_recurrent(pre, R, dtype=np.float32)
+    bar = max(TOL, 2.0 * rel_err(h32.astype(np.float64), ref))
+    err = rel_err(host(h), ref)
+    say(f"slstm full workload: error {err:.3e}, float32 evaluation {bar / 2:.3e}")
+    assert err <= bar
+    c, n, m, hh = (host(t) for t in gst)
+    assert rel_err(hh, rst[3]) <= bar
+    assert rel_err(c / n, rst[0] / rst[1]) <= bar

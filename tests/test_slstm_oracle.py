@@ -138,3 +138,16 @@ def test_planted_mistake_is_caught():
     pre, R = make_slstm_inputs(1, 1, 6, 3, seed=11)
     wrong, _ = so.slstm_recurrent(pre, np.zeros_like(R))
     assert _rel(wrong, unstabilised_loops(pre, R)) > 1e-3
+
+
+def test_float32_evaluation_tracks_float64():
+    """The float32 evaluation mode (used to size a tolerance) runs the same
+    equations: on a short sequence it agrees with float64 to float32
+    rounding, and its arrays are float32."""
+    pre, R = make_slstm_inputs(2, 2, 40, 16, seed=5)
+    st = make_slstm_state(2, 2, 16, seed=6)
+    h64, s64 = so.slstm_recurrent(pre, R, st)
+    h32, s32 = so.slstm_recurrent(pre, R, st, dtype=np.float32)
+    assert h32.dtype == np.float32 and all(x.dtype == np.float32 for x in s32)
+    assert np.max(np.abs(h32 - h64)) <= 1e-5 * np.max(np.abs(h64))
+    assert np.max(np.abs(s32[2] - s64[2])) <= 1e-5 * np.max(np.abs(s64[2]))
