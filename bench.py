@@ -151,13 +151,13 @@ def time_chunkwise(torch, M, L, ev, d, chunk, steps, warmup, kernels=("gate", "s
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     pairs = {k: ev.create(2 * steps) for k in kernels}
+    arrays = [_lib.event_array([pairs[g][2 * i + e] if g in kernels else None
+                                for g in _lib.PROF_GROUPS for e in (0, 1)]) for i in range(steps)]
     for i in range(steps):
-        for k in kernels:
-            M.set_launch_events(k, pairs[k][2 * i], pairs[k][2 * i + 1])
-        one()
+        code = lib.mlstm_prof_fwd_chunkwise(pargs, chunk, wsp, nbytes, stream, arrays[i])
+        if code:
+            raise RuntimeError(lib.mlstm_last_error().decode())
     torch.cuda.synchronize()
-    for k in kernels:
-        M.set_launch_events(k, None, None)
     per_kernel = {}
     for k in kernels:
         ms = [ev.elapsed_ms(pairs[k][2 * i], pairs[k][2 * i + 1]) for i in range(steps)]
@@ -236,12 +236,14 @@ def time_decode(torch, M, ev, steps, warmup):
         one(warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    evs = ev.create(2 * steps)     # per-launch durations: a second pass with the event hook
+    evs = ev.create(2 * steps)     # per-launch durations: a second pass through the profiling call
     for i in range(steps):
-        M.set_launch_events("step", evs[2 * i], evs[2 * i + 1])
-        one(warmup + steps + i)
+        j = warmup + steps + i
+        code = lib.mlstm_prof_step(ctypes.byref(structs[j % len(pool)][j % 2]), stream, evs[2 * i],
+                                   evs[2 * i + 1])
+        if code:
+            raise RuntimeError(lib.mlstm_last_error().decode())
     torch.cuda.synchronize()
-    M.set_launch_events("step", None, None)
     k_us = sum(ev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)) / steps * 1e3
     ev.destroy(evs)
     assert bool(torch.isfinite(h).all())

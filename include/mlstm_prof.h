@@ -1,0 +1,62 @@
+/*
+ * mlstm_prof.h -- measurement entry points of the mLSTM library.
+ *
+ * Not needed for computing: the calls here do what the entry points of
+ * mlstm.h do and, in addition, record caller-owned HIP events on the launch
+ * stream around each group of kernels, so that a benchmark can time the
+ * kernels of one call. The events belong to that one call only; nothing is
+ * remembered between calls and nothing changes for any other call, stream or
+ * thread. Conventions, argument checks and status codes are those of mlstm.h.
+ */
+#ifndef MLSTM_PROF_H_
+#define MLSTM_PROF_H_
+
+#include <stddef.h>
+
+#include "mlstm.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Kernel groups of a chunkwise forward, in launch order. */
+#define MLSTM_PROF_GATE 0   /* gate prefix sums */
+#define MLSTM_PROF_STATE 1  /* inter-chunk state pass */
+#define MLSTM_PROF_OUT 2    /* intra-chunk output kernel */
+
+/*
+ * mlstm_fwd_chunkwise (same arguments, same result) that records
+ * events[2 g] before and events[2 g + 1] after kernel group g on `stream`,
+ * g = MLSTM_PROF_GATE, MLSTM_PROF_STATE, MLSTM_PROF_OUT. `events` points to
+ * six hipEvent_t handles created by the caller; a NULL handle is skipped. A
+ * group that a call does not launch records nothing. Returns
+ * MLSTM_ERR_NULLPTR for a NULL `events`.
+ */
+int mlstm_prof_fwd_chunkwise(const mlstm_fwd_args* args, int chunk, void* workspace,
+                             size_t workspace_bytes, void* stream, void* const* events);
+
+/*
+ * mlstm_step (same arguments, same result) that records the hipEvent_t
+ * `before` and `after` on `stream` around the step kernel (NULL: skipped).
+ */
+int mlstm_prof_step(const mlstm_step_args* args, void* stream, void* before, void* after);
+
+/*
+ * The shader clock while other work runs. Launches one wave that sleeps
+ * `iters` times s_sleep 127 (about 8k shader cycles each; iters in
+ * [1, 2^24]) and writes the shader-clock counter (s_memtime) at its start and
+ * end to ticks[0], ticks[1], and the constant-rate counter (s_memrealtime) to
+ * ticks[2], ticks[3]: four uint64 in caller-owned, 8-byte-aligned device
+ * memory. Launched on a second stream just before a workload, the ratio of
+ * the two differences times the constant counter's rate is the clock under
+ * that workload. Asynchronous on `stream`; returns MLSTM_ERR_NULLPTR,
+ * MLSTM_ERR_BAD_SHAPE or MLSTM_ERR_MISALIGNED on bad arguments before
+ * anything is enqueued.
+ */
+int mlstm_clock_probe(unsigned long long* ticks, int iters, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLSTM_PROF_H_ */

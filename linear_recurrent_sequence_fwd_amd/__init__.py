@@ -11,6 +11,5 @@ from ._lib import (  # noqa: F401
     mlstm_fwd_chunkwise,
     mlstm_fwd_parallel,
     mlstm_step,
-    set_launch_events,
     slstm_fwd,
 )

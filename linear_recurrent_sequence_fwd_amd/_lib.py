@@ -1,5 +1,5 @@
-"""ctypes binding of libmlstm.so: the C ABI declared in include/mlstm.h and
-include/slstm.h.
+"""ctypes binding of libmlstm.so: the C ABI declared in include/mlstm.h,
+include/slstm.h and (measurement entry points) include/mlstm_prof.h.
 
 Argument marshalling only. Tensors supply device memory and the current
 stream; every step of the computation runs in the library's HIP kernels.
@@ -20,7 +20,7 @@ STATUS = {
     -4: "MLSTM_ERR_MISALIGNED", -5: "MLSTM_ERR_ALIAS", -6: "MLSTM_ERR_WORKSPACE",
     -7: "MLSTM_ERR_UNSUPPORTED", -8: "MLSTM_ERR_HIP",
 }
-KERNEL_IDS = {"gate": 0, "state": 1, "out": 2, "step": 3}
+PROF_GROUPS = ("gate", "state", "out")   # kernel groups of mlstm_prof_fwd_chunkwise, in order
 
 
 class FwdArgs(ctypes.Structure):
@@ -90,8 +90,11 @@ def lib() -> ctypes.CDLL:
         L.mlstm_last_error.restype = c_char_p
         L.mlstm_abi_version.argtypes = []
         L.mlstm_abi_version.restype = c_int
-        L.mlstm_set_launch_events.argtypes = [c_int, c_void_p, c_void_p]
-        L.mlstm_set_launch_events.restype = c_int
+        L.mlstm_prof_fwd_chunkwise.argtypes = [P(FwdArgs), c_int, c_void_p, c_size_t, c_void_p,
+                                               P(c_void_p)]
+        L.mlstm_prof_fwd_chunkwise.restype = c_int
+        L.mlstm_prof_step.argtypes = [P(StepArgs), c_void_p, c_void_p, c_void_p]
+        L.mlstm_prof_step.restype = c_int
         L.mlstm_clock_probe.argtypes = [c_void_p, c_int, c_void_p]
         L.mlstm_clock_probe.restype = c_int
         L.slstm_fwd.argtypes = [P(SlstmArgs), c_void_p]
@@ -255,9 +258,12 @@ def mlstm_step(q, k, v, o_pre, i_pre, f_pre, C, n_in, m_in, n_out=None, m_out=No
     return h, n_out, m_out
 
 
-def set_launch_events(kernel: str, before, after) -> None:
-    """Bracket every later launch of `kernel` with the given hipEvent_t handles (ints or None)."""
-    _check(lib().mlstm_set_launch_events(KERNEL_IDS[kernel], before, after), "mlstm_set_launch_events")
+def event_array(events):
+    """A ctypes array of six hipEvent_t handles (ints or None) for
+    mlstm_prof_fwd_chunkwise: before/after of each group in PROF_GROUPS."""
+    if len(events) != 2 * len(PROF_GROUPS):
+        raise ValueError("six event handles are needed")
+    return (c_void_p * 6)(*events)
 
 
 def clock_probe(ticks, iters: int, stream=None) -> None:

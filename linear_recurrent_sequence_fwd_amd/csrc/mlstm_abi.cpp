@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "../../include/mlstm.h"
+#include "../../include/mlstm_prof.h"
 #include "../../include/slstm.h"
 #include "mlstm_launch.h"
 
@@ -177,8 +178,10 @@ mlstm_impl::GateBuffers gate_buffers(char* ws, const WsLayout& w) {
   return gb;
 }
 
-mlstm_impl::FwdLaunch fwd_launch(const mlstm_fwd_args* a, int L, int64_t Nc) {
+mlstm_impl::FwdLaunch fwd_launch(const mlstm_fwd_args* a, int L, int64_t Nc,
+                                 const hipEvent_t* marks = nullptr) {
   mlstm_impl::FwdLaunch f;
+  f.marks = marks;
   f.BH = a->B * a->H; f.T = a->T; f.K = a->d_qk; f.V = a->d_v;
   f.L = L; f.Nc = Nc; f.bf16 = a->dtype == MLSTM_BF16;
   f.q = a->q; f.k = a->k; f.v = a->v; f.o = a->o_pre;
@@ -236,8 +239,12 @@ size_t mlstm_fwd_chunkwise_workspace_size(const mlstm_fwd_args* a, int chunk) {
   return layout(a->B * a->H, a->T, Nc, a->d_qk, a->d_v, a->dtype == MLSTM_BF16 ? 2 : 4, true).total;
 }
 
-int mlstm_fwd_chunkwise(const mlstm_fwd_args* a, int chunk, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+}  // extern "C"
+
+namespace {
+
+int fwd_chunkwise(const mlstm_fwd_args* a, int chunk, void* workspace, size_t workspace_bytes,
+                  void* stream, const hipEvent_t* marks) {
   g_last_error.clear();
   int st = validate_fwd(a);
   if (st) return st;
@@ -246,14 +253,14 @@ int mlstm_fwd_chunkwise(const mlstm_fwd_args* a, int chunk, void* workspace, siz
   if ((st = check_grid(a))) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t Nc = a->T > 0 ? (a->T + chunk - 1) / chunk : 0;
-  mlstm_impl::FwdLaunch f = fwd_launch(a, chunk, Nc);
+  mlstm_impl::FwdLaunch f = fwd_launch(a, chunk, Nc, marks);
   if (a->T == 0) return hip_status(mlstm_impl::launch_copy_state(f, s), "state copy");
   const size_t need = mlstm_fwd_chunkwise_workspace_size(a, chunk);
   if ((st = check_workspace(a, workspace, workspace_bytes, need))) return st;
   char* ws = static_cast<char*>(workspace);
   if (use_fused(a)) {
     const FusedShape fs = fused_shape(a->T, chunk);
-    const mlstm_impl::FwdLaunch ft = fwd_launch(a, 64, fs.Nt);
+    const mlstm_impl::FwdLaunch ft = fwd_launch(a, 64, fs.Nt, marks);
     const WsLayout w = layout_fused(ft.BH, ft.T, chunk, ft.K, ft.V);
     mlstm_impl::GateBuffers gb = gate_buffers(ws, w);
     gb.wb = reinterpret_cast<uint16_t*>(ws + w.wb);
@@ -277,6 +284,15 @@ int mlstm_fwd_chunkwise(const mlstm_fwd_args* a, int chunk, void* workspace, siz
   if ((st = hip_status(mlstm_impl::launch_gate(f, gb, s), "gate kernel"))) return st;
   if ((st = hip_status(mlstm_impl::launch_state(f, gb, cs, s), "state kernel"))) return st;
   return hip_status(mlstm_impl::launch_out(f, gb, cs, s), "output kernel");
+}
+
+}  // namespace
+
+extern "C" {
+
+int mlstm_fwd_chunkwise(const mlstm_fwd_args* a, int chunk, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return fwd_chunkwise(a, chunk, workspace, workspace_bytes, stream, nullptr);
 }
 
 size_t mlstm_fwd_parallel_workspace_size(const mlstm_fwd_args* a) {
@@ -306,7 +322,11 @@ int mlstm_fwd_parallel(const mlstm_fwd_args* a, void* workspace, size_t workspac
   return MLSTM_OK;
 }
 
-int mlstm_step(const mlstm_step_args* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int step(const mlstm_step_args* a, void* stream, const hipEvent_t* marks) {
   g_last_error.clear();
   if (!a) return fail(MLSTM_ERR_NULLPTR, "args is NULL");
   if (a->dtype != MLSTM_FP32 && a->dtype != MLSTM_BF16)
@@ -346,8 +366,15 @@ int mlstm_step(const mlstm_step_args* a, void* stream) {
   sl.i_pre = a->i_pre; sl.f_pre = a->f_pre;
   sl.C = a->C; sl.n_in = a->n_in; sl.m_in = a->m_in; sl.n_out = a->n_out; sl.m_out = a->m_out;
   sl.h = a->h;
+  sl.marks = marks;
   return hip_status(mlstm_impl::launch_step(sl, static_cast<hipStream_t>(stream)), "step kernel");
 }
+
+}  // namespace
+
+extern "C" {
+
+int mlstm_step(const mlstm_step_args* a, void* stream) { return step(a, stream, nullptr); }
 
 int slstm_fwd(const slstm_fwd_args* a, void* stream) {
   g_last_error.clear();
@@ -411,11 +438,22 @@ int mlstm_clock_probe(unsigned long long* ticks, int iters, void* stream) {
   return hip_status(mlstm_impl::launch_clock_probe(ticks, iters, static_cast<hipStream_t>(stream)), "clock probe");
 }
 
-int mlstm_set_launch_events(int kernel_id, void* before, void* after) {
-  if (kernel_id < 0 || kernel_id >= mlstm_impl::K_COUNT)
-    return fail(MLSTM_ERR_BAD_SHAPE, "kernel_id must be 0..3");
-  mlstm_impl::set_launch_events(kernel_id, static_cast<hipEvent_t>(before), static_cast<hipEvent_t>(after));
-  return MLSTM_OK;
+int mlstm_prof_fwd_chunkwise(const mlstm_fwd_args* a, int chunk, void* workspace, size_t workspace_bytes,
+                             void* stream, void* const* events) {
+  if (!events) return fail(MLSTM_ERR_NULLPTR, "events is NULL");
+  hipEvent_t marks[2 * mlstm_impl::K_COUNT] = {};
+  for (int g = 0; g < 3; ++g) {
+    marks[2 * g] = static_cast<hipEvent_t>(events[2 * g]);
+    marks[2 * g + 1] = static_cast<hipEvent_t>(events[2 * g + 1]);
+  }
+  return fwd_chunkwise(a, chunk, workspace, workspace_bytes, stream, marks);
+}
+
+int mlstm_prof_step(const mlstm_step_args* a, void* stream, void* before, void* after) {
+  hipEvent_t marks[2 * mlstm_impl::K_COUNT] = {};
+  marks[2 * mlstm_impl::K_STEP] = static_cast<hipEvent_t>(before);
+  marks[2 * mlstm_impl::K_STEP + 1] = static_cast<hipEvent_t>(after);
+  return step(a, stream, marks);
 }
 
 }  // extern "C"

@@ -616,9 +616,9 @@ hipError_t run_state_b(const FwdLaunch& f, const GateBuffers& gb, const ChunkSta
   a.C_out = f.C_out; a.n_out = f.n_out; a.m_out = f.m_out;
   a.T = f.T; a.Nc = f.Nc; a.V = f.V; a.BH = f.BH; a.L = f.L;
   const int64_t grid = f.BH * (K / 64) * (f.V / 64);
-  mark_before(K_STATE, s);
+  mark_before(f.marks, K_STATE, s);
   hipLaunchKernelGGL((state_kernel_bf16<K, kStatePrefetch>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
-  mark_after(K_STATE, s);
+  mark_after(f.marks, K_STATE, s);
   return hipGetLastError();
 }
 
@@ -639,9 +639,9 @@ hipError_t run_out_b(const FwdLaunch& f, const GateBuffers& gb, const ChunkState
   a.T = f.T; a.Nc = f.Nc; a.V = f.V; a.BH = f.BH; a.L = f.L;
   const int64_t nqt = (f.T + kTile - 1) / kTile;
   const int64_t grid = f.BH * nqt * (f.V / (64 * NT));
-  mark_before(K_OUT, s);
+  mark_before(f.marks, K_OUT, s);
   hipLaunchKernelGGL((out_kernel_bf16<K, NT>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
-  mark_after(K_OUT, s);
+  mark_after(f.marks, K_OUT, s);
   return hipGetLastError();
 }
 

@@ -21,14 +21,13 @@
 
 namespace mlstm_impl {
 
-// Launch-event hooks (profiling only), defined in mlstm_kernels.hip.
-extern hipEvent_t g_ev_before[K_COUNT];
-extern hipEvent_t g_ev_after[K_COUNT];
-inline void mark_before(int k, hipStream_t s) {
-  if (g_ev_before[k] && g_ev_after[k]) (void)hipEventRecord(g_ev_before[k], s);
+// Events of the profiling entry points, recorded on the launch stream around
+// a kernel group when the call carries them (marks[2 k], marks[2 k + 1]).
+inline void mark_before(const hipEvent_t* marks, int k, hipStream_t s) {
+  if (marks && marks[2 * k]) (void)hipEventRecord(marks[2 * k], s);
 }
-inline void mark_after(int k, hipStream_t s) {
-  if (g_ev_before[k] && g_ev_after[k]) (void)hipEventRecord(g_ev_after[k], s);
+inline void mark_after(const hipEvent_t* marks, int k, hipStream_t s) {
+  if (marks && marks[2 * k + 1]) (void)hipEventRecord(marks[2 * k + 1], s);
 }
 
 namespace {

@@ -1358,7 +1358,7 @@ hipError_t run_seg(const FwdLaunch& f, const GateBuffers& gb, const SegStates& s
   a.TPS = ss.TPS; a.S = ss.S;
   const int64_t nvb = f.V / kVB;
   if (ss.S > 1) {
-    mark_before(K_STATE, s);
+    mark_before(f.marks, K_STATE, s);
     hipLaunchKernelGGL((local_kernel<K>), dim3((unsigned)(f.BH * nvb * (ss.S - 1))), dim3(64 * (LocWaves<K>::value + 1)), 0, s, a);
     CombineArgs c;
     c.C0 = f.C0; c.n0 = f.n0; c.m0 = f.m0;
@@ -1367,13 +1367,13 @@ hipError_t run_seg(const FwdLaunch& f, const GateBuffers& gb, const SegStates& s
     const int64_t units = f.V * K / 4 + K / 4;
     const int64_t blocks = (units + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(f.BH * blocks)), dim3(kThreads), 0, s, c);
-    mark_after(K_STATE, s);
+    mark_after(f.marks, K_STATE, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  mark_before(K_OUT, s);
+  mark_before(f.marks, K_OUT, s);
   hipLaunchKernelGGL((out_kernel_fused<K>), dim3((unsigned)(f.BH * nvb * ss.S)), dim3(64 * kOutWaves), 0, s, a);
-  mark_after(K_OUT, s);
+  mark_after(f.marks, K_OUT, s);
   return hipGetLastError();
 }
 

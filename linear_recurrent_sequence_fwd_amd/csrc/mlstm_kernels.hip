@@ -35,9 +35,6 @@
 
 namespace mlstm_impl {
 
-hipEvent_t g_ev_before[K_COUNT] = {nullptr, nullptr, nullptr, nullptr};
-hipEvent_t g_ev_after[K_COUNT] = {nullptr, nullptr, nullptr, nullptr};
-
 namespace {
 
 // ------------------------------------------------------------------ gate kernel
@@ -656,9 +653,9 @@ hipError_t run_state(const FwdLaunch& f, const GateBuffers& gb, const ChunkState
   a.C_out = f.C_out; a.n_out = f.n_out; a.m_out = f.m_out;
   a.T = f.T; a.Nc = f.Nc; a.V = f.V; a.L = f.L;
   const int64_t grid = f.BH * (K / 64) * (f.V / 64);
-  mark_before(K_STATE, s);
+  mark_before(f.marks, K_STATE, s);
   hipLaunchKernelGGL((state_kernel<TI, TS, K>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
-  mark_after(K_STATE, s);
+  mark_after(f.marks, K_STATE, s);
   return hipGetLastError();
 }
 
@@ -678,9 +675,9 @@ hipError_t run_out(const FwdLaunch& f, const GateBuffers& gb, const void* Cs, co
   a.T = f.T; a.Nc = f.Nc; a.V = f.V; a.L = f.L;
   const int64_t nqt = (f.T + kTile - 1) / kTile;
   const int64_t grid = f.BH * nqt * (f.V / (64 * NT));
-  mark_before(K_OUT, s);
+  mark_before(f.marks, K_OUT, s);
   hipLaunchKernelGGL((out_kernel<TI, TS, K, NT>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
-  mark_after(K_OUT, s);
+  mark_after(f.marks, K_OUT, s);
   return hipGetLastError();
 }
 
@@ -717,9 +714,9 @@ hipError_t run_step(const StepLaunch& st, hipStream_t s) {
   a.V = st.V;
   const int64_t nvb = (st.V + 4 * RPW - 1) / (4 * RPW);
   const int64_t grid = st.BH * nvb;
-  mark_before(K_STEP, s);
+  mark_before(st.marks, K_STEP, s);
   hipLaunchKernelGGL((step_kernel<TI, K, RPW>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
-  mark_after(K_STEP, s);
+  mark_after(st.marks, K_STEP, s);
   return hipGetLastError();
 }
 
@@ -727,24 +724,18 @@ hipError_t run_step(const StepLaunch& st, hipStream_t s) {
 
 // ------------------------------------------------------------------ launchers
 
-void set_launch_events(int kernel, hipEvent_t before, hipEvent_t after) {
-  if (kernel < 0 || kernel >= K_COUNT) return;
-  g_ev_before[kernel] = before;
-  g_ev_after[kernel] = after;
-}
-
 hipError_t launch_gate(const FwdLaunch& f, const GateBuffers& gb, hipStream_t s) {
   GateArgs a;
   a.i_pre = f.i_pre;
   a.f_pre = f.f_pre;
   a.T = f.T; a.Nc = f.Nc; a.BH = f.BH; a.L = f.L;
   a.gb = gb;
-  mark_before(K_GATE, s);
+  mark_before(f.marks, K_GATE, s);
   if (f.L == kTile)
     hipLaunchKernelGGL(gate64_kernel, dim3((unsigned)((f.BH * f.Nc + 3) / 4)), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(gate_kernel, dim3((unsigned)(f.BH * f.Nc)), dim3(kThreads), 0, s, a);
-  mark_after(K_GATE, s);
+  mark_after(f.marks, K_GATE, s);
   return hipGetLastError();
 }
 

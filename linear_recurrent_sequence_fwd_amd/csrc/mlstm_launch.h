@@ -61,6 +61,7 @@ struct FwdLaunch {
   void* h;
   const float *C0, *n0, *m0;
   float *C_out, *n_out, *m_out;
+  const hipEvent_t* marks;   // [K_COUNT][2] events around each kernel group, or null
 };
 
 struct StepLaunch {
@@ -72,6 +73,7 @@ struct StepLaunch {
   const float *n_in, *m_in;
   float *n_out, *m_out;
   void* h;
+  const hipEvent_t* marks;   // [K_COUNT][2] events around the step kernel, or null
 };
 
 // sLSTM forward (slstm.hip): pre [B,T,4,H,D], R [H,4,D,D], h [B,T,H,D];
@@ -86,8 +88,6 @@ struct SlstmLaunch {
 };
 bool slstm_supported(int64_t D);
 hipError_t launch_slstm(const SlstmLaunch& a, hipStream_t s);
-
-void set_launch_events(int kernel, hipEvent_t before, hipEvent_t after);
 
 hipError_t launch_gate(const FwdLaunch& a, const GateBuffers& gb, hipStream_t s);
 // Inter-chunk state pass; `cs` may have null Cs/ns/ms when no chunk-start

@@ -14,14 +14,15 @@ from linear_recurrent_sequence_fwd_amd import _lib as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mlstm.h")
+PROF_HEADER = os.path.join(ROOT, "include", "mlstm_prof.h")
 
 OK, NULLPTR, BAD_SHAPE, BAD_DTYPE, MISALIGNED, ALIAS, WORKSPACE, UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6, -7
 
 GB = 1 << 30
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(mlstm_[a-z_]+)\s*\(", text)))
 
@@ -29,10 +30,16 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = L.lib()
     names = declared_functions()
-    assert len(names) >= 9
+    assert len(names) >= 8
     for n in names:
         assert hasattr(lib, n), n
     assert lib.mlstm_abi_version() == 1
+    prof = declared_functions(PROF_HEADER)
+    assert prof == ["mlstm_clock_probe", "mlstm_prof_fwd_chunkwise", "mlstm_prof_step"]
+    for n in prof:
+        assert hasattr(lib, n), n
+    # the product header declares only the method's calls and the status/version helpers
+    assert not set(prof) & set(names)
 
 
 def test_status_strings():
@@ -246,10 +253,21 @@ def test_step_validation():
     assert lib.mlstm_step(ctypes.byref(a), None) == NULLPTR
 
 
-def test_launch_event_hook_validation():
+def test_profiling_entry_points_validate_like_the_plain_ones():
+    """The measurement calls run the same argument checks before anything is
+    enqueued, and the chunkwise one needs its event array."""
     lib = L.lib()
-    assert lib.mlstm_set_launch_events(9, None, None) == BAD_SHAPE
-    assert lib.mlstm_set_launch_events(2, None, None) == OK
+    a = fake_fwd()
+    ev = L.event_array([None] * 6)
+    assert lib.mlstm_prof_fwd_chunkwise(ctypes.byref(a), 64, None, 0, None, None) == NULLPTR
+    a.dtype = 7
+    assert lib.mlstm_prof_fwd_chunkwise(ctypes.byref(a), 64, None, 0, None, ev) == BAD_DTYPE
+    a = fake_fwd()
+    assert lib.mlstm_prof_fwd_chunkwise(ctypes.byref(a), 65, None, 0, None, ev) == BAD_SHAPE
+    assert lib.mlstm_prof_fwd_chunkwise(ctypes.byref(a), 64, None, 0, None, ev) == WORKSPACE
+    s = fake_step()
+    s.k = None
+    assert lib.mlstm_prof_step(ctypes.byref(s), None, None, None) == NULLPTR
 
 
 def test_clock_probe_validation():
