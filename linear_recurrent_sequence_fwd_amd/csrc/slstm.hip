@@ -21,9 +21,14 @@
 // The steps run in blocks of 8; during each block the previous block's h go
 // from the ring to HBM and the next block's preactivations are loaded, in one
 // batch per thread.
-// Exponentials use the hardware base-2 exponential with the argument scaled
-// by log2(e), tanh(x) = 1 - 2 / (exp(2x) + 1) and the divisions the hardware
-// reciprocal: a few ulp each, far inside the float32 bar of 1e-4.
+// The stabiliser m is carried in float64: with the exponential forget gate it
+// grows by f~ every step (to hundreds over long sequences), and the exponent
+// f~ + m_{t-1} - m_t, a small difference of large numbers, would otherwise
+// lose an ulp of m (3e-5 at m = 430) per step. The exponent is formed in
+// float64 and rounded once. Exponentials use the hardware base-2 exponential
+// with the argument scaled by log2(e), tanh(x) = 1 - 2 / (exp(2x) + 1) and
+// the divisions the hardware reciprocal: a few ulp each, far inside the
+// float32 bar of 1e-4.
 // The work per step is 4 D^2 fused multiply-adds spread over the workgroup,
 // five transcendentals per thread and one barrier: the step is bound by
 // vector-instruction issue on its one CU, not by HBM. Throughput comes from
@@ -88,19 +93,22 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
       r[g][4 * k + 3] = x[3];
     }
   }
-  // State of cell i, kept (identically) by all four threads of its quad. The
-  // zero state starts from m_0 = -inf instead of 0: the same h and the same
-  // true-unit state in exact arithmetic (a stabiliser shift of an all-zero
-  // state changes nothing), and then n_t >= 1 at every step (m_t = i~_t gives
+  // State of cell i, kept (identically) by all four threads of its quad. An
+  // empty state (no state given, or a given one with c = n = 0) starts from
+  // m_0 = -inf instead of its m: the same h and the same true-unit state in
+  // exact arithmetic (a stabiliser shift of an all-zero state changes
+  // nothing), and then n_t >= 1 at every step (m_t = i~_t gives
   // exp(i~_t - m_t) = 1, else the forget factor is 1 and n_t >= n_{t-1}), so
   // c / n cannot underflow.
   const int64_t sidx = (b * H + hh) * D + cell;
-  float c = 0.f, n = 0.f, m = -INFINITY, hv = 0.f;
+  float c = 0.f, n = 0.f, hv = 0.f, m_given = 0.f;
+  double m = -INFINITY;
   if (a.c0) {
     c = a.c0[sidx];
     n = a.n0[sidx];
-    m = a.m0[sidx];
+    m_given = a.m0[sidx];
     hv = a.h0[sidx];
+    if (c != 0.f || n != 0.f) m = (double)m_given;
   }
   if (qd == 0) s_hr[2 * RB - 1][hpos(cell)] = hv;
   // thread 4i + q loads P_t of gate q of cell i, at
@@ -156,16 +164,17 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
       for (int g = 0; g < 4; ++g) acc[g] += dpp_f<kQuadXor1>(acc[g]);
 #pragma unroll
       for (int g = 0; g < 4; ++g) acc[g] += dpp_f<kQuadXor2>(acc[g]);
-      const float it = acc[0], zt = tanh_fast(acc[2]);
-      const float mf = m + acc[1];
+      const double it = (double)acc[0];
+      const float zt = tanh_fast(acc[2]);
+      const double mf = m + (double)acc[1];
       // of the factors exp(f~ + m_{t-1} - m_t) and exp(i~ - m_t) the one of
       // the term that sets the new maximum is exactly 1
       const bool fkeep = mf >= it;
-      const float ex = exp_fast(fkeep ? it - mf : mf - it);
+      const float ex = exp_fast((float)(fkeep ? it - mf : mf - it));
       const float fa = fkeep ? 1.f : ex, ia = fkeep ? ex : 1.f;
       c = fa * c + ia * zt;
       n = fa * n + ia;
-      m = fmaxf(mf, it);
+      m = fmax(mf, it);
       // sigmoid(o~) c / n = c / (n (1 + exp(-o~))): one reciprocal
       hv = c * __builtin_amdgcn_rcpf(fmaxf(n, FLT_MIN) * (1.f + exp_fast(-acc[3])));
       if (qd == 0) s_hr[half + q][hpos(cell)] = hv;
@@ -181,9 +190,19 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
       if (tl + q < T) hout[(tl + q) * H * D] = s_hr[half + q][hpos(j)];
   }
   if (qd == 0 && a.c_out) {
-    a.c_out[sidx] = c;
-    a.n_out[sidx] = n;
-    a.m_out[sidx] = (T == 0 && !a.c0) ? 0.f : m;   // the zero state reports m = 0
+    if (T == 0) {   // after no step the state is returned as given (the zero state with m = 0)
+      a.c_out[sidx] = c;
+      a.n_out[sidx] = n;
+      a.m_out[sidx] = m_given;
+    } else {
+      // m leaves as float32; c and n take the factor exp(m - m32), so that
+      // exp(m32) c and exp(m32) n are the carried true-unit state
+      const float m32 = (float)m;
+      const float sc = exp_fast((float)(m - (double)m32));
+      a.c_out[sidx] = c * sc;
+      a.n_out[sidx] = n * sc;
+      a.m_out[sidx] = m32;
+    }
     a.h_out[sidx] = hv;
   }
 }

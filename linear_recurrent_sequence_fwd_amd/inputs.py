@@ -36,13 +36,22 @@ __all__ = [
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bit patterns."""
+    """Round float32 values to bfloat16 (nearest, ties to even); return uint16 bit patterns.
+
+    Works on the 32-bit patterns: adding 0x7FFF plus the lowest kept bit and
+    dropping the low half rounds to nearest even; no finite value or infinity
+    carries out of 32 bits. NaNs become the quiet NaN 0x7FC0.
+    """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    rounded = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        rounded = np.where(nan, np.uint16(0x7FC0), rounded)
+        rounded[nan] = np.uint16(0x7FC0)
     return rounded
 
 

@@ -55,20 +55,17 @@ def run(L, pre, R, state=None, want_state=True):
     return out
 
 
-def check_state(gpu, ref, T):
-    """h and the readout ratio c / n to 1e-4. The true-unit scale exp(m) c,
-    exp(m) n is held to a bound from float32 arithmetic on the stabiliser:
-    with the exponential forget gate m grows by f~ each step, each step's
-    exponent f~ + m_{t-1} - m_t carries up to one float32 ulp of |m|, and
-    these add over at most T steps."""
+def check_state(gpu, ref):
+    """h, the readout ratio c / n and the true-unit state exp(m) c, exp(m) n,
+    all to 1e-4 (the kernel carries the stabiliser in float64 and hands m out
+    as float32 with c, n rescaled to match)."""
     c, n, m, hh = (host(t) for t in gpu)
     cr, nr, mr, hr = ref
     assert rel_err(hh, hr) <= TOL
     assert rel_err(c / n, cr / nr) <= TOL
-    tol_scale = TOL + 2.0 * T * float(np.max(np.abs(mr))) * 2.0 ** -23
     sc = np.exp(m - mr)
-    assert rel_err(sc * c, cr) <= tol_scale
-    assert rel_err(sc * n, nr) <= tol_scale
+    assert rel_err(sc * c, cr) <= TOL
+    assert rel_err(sc * n, nr) <= TOL
 
 
 @pytest.mark.parametrize("D", [16, 32, 64, 128])
@@ -82,7 +79,7 @@ def test_slstm_matches_oracle(D, with_state):
     h, gst = run(L, pre, R, st)
     ref, rst = so.slstm_recurrent(pre, R, st)
     assert rel_err(host(h), ref) <= TOL
-    check_state(gst, rst, T)
+    check_state(gst, rst)
 
 
 @pytest.mark.parametrize("f_mean", [-4.0, 4.0])
@@ -94,7 +91,7 @@ def test_slstm_strong_and_weak_forgetting(f_mean):
     h, gst = run(L, pre, R)
     ref, rst = so.slstm_recurrent(pre, R)
     assert rel_err(host(h), ref) <= TOL
-    check_state(gst, rst, T)
+    check_state(gst, rst)
 
 
 def test_slstm_long_sequence_full_width():
@@ -106,12 +103,14 @@ def test_slstm_long_sequence_full_width():
     h, gst = run(L, pre, R)
     ref, rst = so.slstm_recurrent(pre, R)
     assert rel_err(host(h), ref) <= TOL
-    check_state(gst, rst, T)
+    check_state(gst, rst)
 
 
-def test_slstm_split_and_resume_bitwise():
-    """Two calls joined through the state equal one call bit for bit: the
-    state is carried in float32 in both cases."""
+def test_slstm_split_and_resume():
+    """Two calls joined through the state give the one-call result. The first
+    part is equal bit for bit; after the hand-off the only difference is the
+    rounding of m to float32 in the exported state (its c and n are rescaled
+    to the same true-unit state), a few float32 ulp of h."""
     L = _lib()
     B, H, T, D = 2, 3, 77, 32
     say("slstm split/resume")
@@ -119,9 +118,13 @@ def test_slstm_split_and_resume_bitwise():
     h, st = run(L, pre, R)
     h1, st1 = run(L, pre[:, :40], R)
     h2, st2 = run(L, pre[:, 40:], R, state=tuple(host(s) for s in st1))
-    assert torch.equal(torch.cat([h1, h2], dim=1), h)
-    for a, b in zip(st, st2):
-        assert torch.equal(a, b)
+    assert torch.equal(h1, h[:, :40])
+    assert rel_err(host(h2), host(h[:, 40:])) <= 1e-6
+    c, n, m, hh = (host(t) for t in st)
+    c2, n2, m2, hh2 = (host(t) for t in st2)
+    sc = np.exp(m2 - m)
+    assert rel_err(sc * c2, c) <= 1e-6 and rel_err(sc * n2, n) <= 1e-6
+    assert rel_err(hh2, hh) <= 1e-6
 
 
 def test_slstm_empty_sequence_copies_state():
@@ -161,7 +164,7 @@ def test_slstm_large_preactivations():
     h, gst = run(L, big, R)
     ref, rst = so.slstm_recurrent(big, R)
     assert rel_err(host(h), ref) <= TOL
-    check_state(gst, rst, T)
+    check_state(gst, rst)
     huge = (pre * 1.0e4).astype(np.float32)
     h2, st2 = run(L, huge, R)
     assert np.all(np.isfinite(host(h2)))
@@ -181,7 +184,7 @@ def test_slstm_ragged_lengths(T):
     h, gst = run(L, pre, R, st)
     ref, rst = so.slstm_recurrent(pre, R, st)
     assert rel_err(host(h), ref) <= TOL
-    check_state(gst, rst, T)
+    check_state(gst, rst)
 
 
 def test_slstm_more_sequences_than_cus():
@@ -193,30 +196,42 @@ def test_slstm_more_sequences_than_cus():
     h, gst = run(L, pre, R)
     ref, rst = so.slstm_recurrent(pre, R)
     assert rel_err(host(h), ref) <= TOL
-    check_state(gst, rst, T)
+    check_state(gst, rst)
 
 
 def test_slstm_full_benchmark_workload():
     """The measured workload, B = 16, H = 8, D = 128, T = 2048, every output
-    against the oracle (some seconds on the host).
-
-    Over 2048 steps the stabiliser m of some cells reaches several hundred
-    (the exponential forget gate lets it grow as a random walk), where its
-    float32 spacing is ~3e-5, and the error of h in any float32 evaluation
-    passes 1e-4 on a few of the 134M outputs. The bar here is therefore
-    twice the error of the oracle's own equations evaluated in float32,
-    and 1e-4 at least."""
+    and the final state against the oracle at the fixed bar of 1e-4 (some
+    seconds on the host). Over 2048 steps the stabiliser m of some cells
+    reaches several hundred, which the kernel carries in float64. For
+    context the error of the same equations evaluated in float32 throughout
+    is printed (it passes 1e-4 here); it is not part of any assertion."""
     L = _lib()
     B, H, T, D = 16, 8, 2048, 128
     say(f"slstm full workload B={B} H={H} T={T} D={D}")
     pre, R = make_slstm_inputs(B, H, T, D, seed=91)
     h, gst = run(L, pre, R)
     ref, rst = so.slstm_recurrent(pre, R)
-    h32, _ = so.slstm_recurrent(pre, R, dtype=np.float32)
-    bar = max(TOL, 2.0 * rel_err(h32.astype(np.float64), ref))
     err = rel_err(host(h), ref)
-    say(f"slstm full workload: error {err:.3e}, float32 evaluation {bar / 2:.3e}")
-    assert err <= bar
-    c, n, m, hh = (host(t) for t in gst)
-    assert rel_err(hh, rst[3]) <= bar
-    assert rel_err(c / n, rst[0] / rst[1]) <= bar
+    h32, _ = so.slstm_recurrent(pre, R, dtype=np.float32)
+    say(f"slstm full workload: error {err:.3e} (float32 evaluation of the equations: "
+        f"{rel_err(h32.astype(np.float64), ref):.3e}); max |m| {float(np.max(np.abs(rst[2]))):.1f}")
+    assert err <= TOL
+    check_state(gst, rst)
+
+
+def test_slstm_explicit_zero_state_large_preactivations():
+    """An explicit all-zero state (as an empty call returns it, m = 0) with
+    preactivations scaled by 30, so that f~ - i~ leaves the float32 exponent
+    range at the first step: the same outputs as from no state, against the
+    oracle started from that zero state."""
+    L = _lib()
+    B, H, T, D = 2, 2, 48, 32
+    say("slstm explicit zero state, preactivations x30")
+    pre, R = make_slstm_inputs(B, H, T, D, seed=62)
+    big = (pre * 30.0).astype(np.float32)
+    zero = tuple(np.zeros((B, H, D), dtype=np.float32) for _ in range(4))
+    h, gst = run(L, big, R, state=zero)
+    ref, rst = so.slstm_recurrent(big, R, zero)
+    assert rel_err(host(h), ref) <= TOL
+    check_state(gst, rst)
