@@ -21,11 +21,14 @@
 // The steps run in blocks of 8; during each block the previous block's h go
 // from the ring to HBM and the next block's preactivations are loaded, in one
 // batch per thread.
-// The stabiliser m is carried in float64: with the exponential forget gate it
-// grows by f~ every step (to hundreds over long sequences), and the exponent
-// f~ + m_{t-1} - m_t, a small difference of large numbers, would otherwise
-// lose an ulp of m (3e-5 at m = 430) per step. The exponent is formed in
-// float64 and rounded once. Exponentials use the hardware base-2 exponential
+// The cell state c, n, m is carried in float64. With the exponential forget
+// gate m grows by f~ every step (to hundreds over long sequences), and the
+// exponent f~ + m_{t-1} - m_t, a small difference of large numbers, would
+// lose an ulp of m (3e-5 at m = 430) per step in float32; c and n sum
+// thousands of weighted terms of both signs, and rounding them to float32 at
+// every step alone costs 1.1e-4 of max|h| over 2048 steps of the benchmark
+// workload. The factor exp(f~ + m_{t-1} - m_t) or exp(i~ - m_t) is taken
+// from its float64 exponent to about one float32 ulp. Exponentials use the hardware base-2 exponential
 // with the argument scaled by log2(e), tanh(x) = 1 - 2 / (exp(2x) + 1) and
 // the divisions the hardware reciprocal: a few ulp each, far inside the
 // float32 bar of 1e-4.
@@ -52,6 +55,17 @@ __device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp
 // 1 - 2 / (e^{2x} + 1): exact limits +-1 for large |x| (e^{2x} -> inf or 0)
 __device__ __forceinline__ float tanh_fast(float x) {
   return fmaf(-2.f, __builtin_amdgcn_rcpf(exp_fast(2.f * x) + 1.f), 1.f);
+}
+
+// exp(d) for a float64 argument d <= 0 (or -inf), to about one float32 ulp
+// whatever its size: d log2(e) = n + f with an integer n and f in [0, 1),
+// the hardware base-2 exponential of f, scaled by 2^n. (Rounding d log2(e)
+// itself to float32 would cost |d| float32 ulps, which the forget and input
+// factors would pass on to the state at every step.)
+__device__ __forceinline__ float exp_f64arg(double d) {
+  const double y = d * 1.4426950408889634;
+  const double n = fmax(floor(y), -200.0);   // below 2^-200 the result is 0 anyway
+  return ldexpf(__builtin_amdgcn_exp2f((float)(y - n)), (int)n);
 }
 
 template <int CTRL>
@@ -101,14 +115,14 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
   // exp(i~_t - m_t) = 1, else the forget factor is 1 and n_t >= n_{t-1}), so
   // c / n cannot underflow.
   const int64_t sidx = (b * H + hh) * D + cell;
-  float c = 0.f, n = 0.f, hv = 0.f, m_given = 0.f;
-  double m = -INFINITY;
+  float hv = 0.f, m_given = 0.f;
+  double c = 0.0, n = 0.0, m = -INFINITY;
   if (a.c0) {
-    c = a.c0[sidx];
-    n = a.n0[sidx];
+    c = (double)a.c0[sidx];
+    n = (double)a.n0[sidx];
     m_given = a.m0[sidx];
     hv = a.h0[sidx];
-    if (c != 0.f || n != 0.f) m = (double)m_given;
+    if (c != 0.0 || n != 0.0) m = (double)m_given;
   }
   if (qd == 0) s_hr[2 * RB - 1][hpos(cell)] = hv;
   // thread 4i + q loads P_t of gate q of cell i, at
@@ -146,9 +160,10 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
       if (t >= T) break;   // uniform over the workgroup
       const float p = pc[q];
       const f32x4v* hp = reinterpret_cast<const f32x4v*>(&s_hr[(half + q + 2 * RB - 1) % (2 * RB)][qd * HS]);
-      float acc[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) acc[g] = qd == g ? p : 0.f;
+      // the partial sums start from zero and P enters after them, so that the
+      // long chain of products is not rounded at the size of P (the forget
+      // gate's rounding errors add up in the state's weights over the steps)
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < DS / 4; ++k) {
         const f32x4v x = hp[k];
@@ -157,6 +172,8 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) acc[g] = fmaf(r[g][4 * k + cc], x[cc], acc[g]);
       }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) acc[g] += qd == g ? p : 0.f;
       // sum over the quad (lane ^ 1, then lane ^ 2): every thread of the quad
       // ends with the same four gate preactivations of its cell (each sum is
       // formed in the same order up to commuted operands, so bit for bit)
@@ -170,13 +187,13 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
       // of the factors exp(f~ + m_{t-1} - m_t) and exp(i~ - m_t) the one of
       // the term that sets the new maximum is exactly 1
       const bool fkeep = mf >= it;
-      const float ex = exp_fast((float)(fkeep ? it - mf : mf - it));
-      const float fa = fkeep ? 1.f : ex, ia = fkeep ? ex : 1.f;
-      c = fa * c + ia * zt;
-      n = fa * n + ia;
+      const float ex = exp_f64arg(fkeep ? it - mf : mf - it);
+      const double fa = fkeep ? 1.0 : (double)ex, ia = fkeep ? (double)ex : 1.0;
+      c = fma(fa, c, ia * (double)zt);
+      n = fma(fa, n, ia);
       m = fmax(mf, it);
       // sigmoid(o~) c / n = c / (n (1 + exp(-o~))): one reciprocal
-      hv = c * __builtin_amdgcn_rcpf(fmaxf(n, FLT_MIN) * (1.f + exp_fast(-acc[3])));
+      hv = (float)c * __builtin_amdgcn_rcpf(fmaxf((float)n, FLT_MIN) * (1.f + exp_fast(-acc[3])));
       if (qd == 0) s_hr[half + q][hpos(cell)] = hv;
       __syncthreads();   // h_t published
     }
@@ -191,16 +208,16 @@ __global__ __launch_bounds__(4 * D) void slstm_kernel(SlstmLaunch a) {
   }
   if (qd == 0 && a.c_out) {
     if (T == 0) {   // after no step the state is returned as given (the zero state with m = 0)
-      a.c_out[sidx] = c;
-      a.n_out[sidx] = n;
+      a.c_out[sidx] = (float)c;
+      a.n_out[sidx] = (float)n;
       a.m_out[sidx] = m_given;
     } else {
       // m leaves as float32; c and n take the factor exp(m - m32), so that
       // exp(m32) c and exp(m32) n are the carried true-unit state
       const float m32 = (float)m;
-      const float sc = exp_fast((float)(m - (double)m32));
-      a.c_out[sidx] = c * sc;
-      a.n_out[sidx] = n * sc;
+      const double sc = (double)exp_fast((float)(m - (double)m32));
+      a.c_out[sidx] = (float)(c * sc);
+      a.n_out[sidx] = (float)(n * sc);
       a.m_out[sidx] = m32;
     }
     a.h_out[sidx] = hv;
