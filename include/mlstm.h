@@ -143,6 +143,24 @@ typedef struct mlstm_step_args {
  */
 int mlstm_step(const mlstm_step_args* args, void* stream);
 
+/*
+ * mlstm_fwd_chunkwise without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments (minus the workspace),
+ * same result, same kernels. The scratch comes from a fixed device array of
+ * mlstm_fwd_chunkwise_noalloc_limit() bytes (64 MiB) that each GPU the
+ * library runs on holds until the process ends; the call allocates nothing.
+ * A call whose workspace would exceed it (mlstm_fwd_chunkwise_workspace_size
+ * above the limit, e.g. very long sequences with short chunks) returns
+ * MLSTM_ERR_UNSUPPORTED before anything is enqueued. All calls on one GPU
+ * share its array: calls that may overlap in time on one GPU (different
+ * streams, or different threads) race and must be serialised by the caller.
+ * The first call on a device looks up the array's address there
+ * (hipGetSymbolAddress) and may return MLSTM_ERR_HIP if that fails.
+ */
+size_t mlstm_fwd_chunkwise_noalloc_limit(void);
+int mlstm_fwd_chunkwise_noalloc(const mlstm_fwd_args* args, int chunk, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* mlstm_status_string(int status);
 /* Message of the calling thread's most recent error ("" if none). */

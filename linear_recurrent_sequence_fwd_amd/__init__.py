@@ -9,6 +9,7 @@ run only the HIP library; a missing library raises.
 from ._lib import (  # noqa: F401
     MlstmError,
     mlstm_fwd_chunkwise,
+    mlstm_fwd_chunkwise_noalloc,
     mlstm_fwd_parallel,
     mlstm_step,
     slstm_fwd,

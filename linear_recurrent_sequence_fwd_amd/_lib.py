@@ -78,6 +78,10 @@ def lib() -> ctypes.CDLL:
         L.mlstm_fwd_chunkwise_workspace_size.restype = c_size_t
         L.mlstm_fwd_chunkwise.argtypes = [P(FwdArgs), c_int, c_void_p, c_size_t, c_void_p]
         L.mlstm_fwd_chunkwise.restype = c_int
+        L.mlstm_fwd_chunkwise_noalloc_limit.argtypes = []
+        L.mlstm_fwd_chunkwise_noalloc_limit.restype = c_size_t
+        L.mlstm_fwd_chunkwise_noalloc.argtypes = [P(FwdArgs), c_int, c_void_p]
+        L.mlstm_fwd_chunkwise_noalloc.restype = c_int
         L.mlstm_fwd_parallel_workspace_size.argtypes = [P(FwdArgs)]
         L.mlstm_fwd_parallel_workspace_size.restype = c_size_t
         L.mlstm_fwd_parallel.argtypes = [P(FwdArgs), c_void_p, c_size_t, c_void_p]
@@ -208,6 +212,21 @@ def mlstm_fwd_chunkwise(q, k, v, o_pre, i_pre, f_pre, chunk=64, C0=None, n0=None
     ws = _workspace(nbytes, q.device, workspace)
     _check(lib().mlstm_fwd_chunkwise(ctypes.byref(args), int(chunk), _ptr(ws), nbytes, _stream(stream)),
            "mlstm_fwd_chunkwise")
+    return (h, (C_out, n_out, m_out)) if return_state else h
+
+
+def mlstm_fwd_chunkwise_noalloc(q, k, v, o_pre, i_pre, f_pre, chunk=64, C0=None, n0=None, m0=None,
+                                return_state=False, h=None, stream=None):
+    """Chunkwise forward through the no-allocation entry point (the library's
+    fixed per-device scratch instead of a workspace). Returns h, or
+    (h, (C, n, m)) when return_state. Outputs are allocated here unless given."""
+    import torch
+    if h is None:
+        h = torch.empty(v.shape, dtype=v.dtype, device=v.device)
+    C_out, n_out, m_out = _state_out(q, v, return_state)
+    args = fwd_args(q, k, v, o_pre, i_pre, f_pre, h, C0, n0, m0, C_out, n_out, m_out)
+    _check(lib().mlstm_fwd_chunkwise_noalloc(ctypes.byref(args), int(chunk), _stream(stream)),
+           "mlstm_fwd_chunkwise_noalloc")
     return (h, (C_out, n_out, m_out)) if return_state else h
 
 

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -454,6 +455,74 @@ int mlstm_prof_step(const mlstm_step_args* a, void* stream, void* before, void* 
   marks[2 * mlstm_impl::K_STEP] = static_cast<hipEvent_t>(before);
   marks[2 * mlstm_impl::K_STEP + 1] = static_cast<hipEvent_t>(after);
   return step(a, stream, marks);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ no-allocation entry point
+//
+// Scratch of mlstm_fwd_chunkwise_noalloc: a file-scope device array that
+// every GPU the library runs on holds, at its own address, until the process
+// ends. Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and is kept
+// in a per-device table. Every call on a GPU shares that GPU's array.
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t(64) << 20;   // 64 MiB per device
+constexpr int kMaxDevices = 64;
+
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device of `stream` (the current
+// device for the null stream), looked up on the first call for that device.
+int scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MLSTM_ERR_HIP, std::string("device of the stream: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MLSTM_ERR_UNSUPPORTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess)
+      return fail(MLSTM_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(MLSTM_ERR_HIP, std::string("hipSetDevice: ") + hipGetErrorString(e));
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !ptr)
+      return fail(MLSTM_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLSTM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mlstm_fwd_chunkwise_noalloc_limit(void) { return kScratchBytes; }
+
+int mlstm_fwd_chunkwise_noalloc(const mlstm_fwd_args* a, int chunk, void* stream) {
+  g_last_error.clear();
+  int st = validate_fwd(a);
+  if (st) return st;
+  if (chunk < 64 || chunk % 64 != 0 || chunk > kMaxChunk)
+    return fail(MLSTM_ERR_BAD_SHAPE, "chunk must be a multiple of 64 in [64, 8192]");
+  const size_t need = mlstm_fwd_chunkwise_workspace_size(a, chunk);
+  if (need > kScratchBytes)
+    return fail(MLSTM_ERR_UNSUPPORTED, "this call needs " + std::to_string(need) +
+                                           " bytes of scratch, above the 64 MiB of the no-allocation entry "
+                                           "point (use mlstm_fwd_chunkwise with a workspace, or a longer chunk)");
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_for_stream(static_cast<hipStream_t>(stream), &ws))) return st;
+  return fwd_chunkwise(a, chunk, ws, kScratchBytes, stream, nullptr);
 }
 
 }  // extern "C"

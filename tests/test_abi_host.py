@@ -253,6 +253,22 @@ def test_step_validation():
     assert lib.mlstm_step(ctypes.byref(a), None) == NULLPTR
 
 
+def test_noalloc_entry_point_limits():
+    """The no-allocation call validates like the workspace one and rejects a
+    problem whose workspace exceeds its fixed scratch before touching a device."""
+    lib = L.lib()
+    limit = lib.mlstm_fwd_chunkwise_noalloc_limit()
+    assert limit == 64 << 20
+    assert lib.mlstm_fwd_chunkwise_noalloc(None, 64, None) == NULLPTR
+    a = fake_fwd()
+    assert lib.mlstm_fwd_chunkwise_noalloc(ctypes.byref(a), 100, None) == BAD_SHAPE
+    big = fake_fwd(B=1, H=8, T=131072, K=256, V=512)
+    need = lib.mlstm_fwd_chunkwise_workspace_size(ctypes.byref(big), 64)
+    assert need > limit
+    assert lib.mlstm_fwd_chunkwise_noalloc(ctypes.byref(big), 64, None) == UNSUPPORTED
+    assert b"64 MiB" in lib.mlstm_last_error()
+
+
 def test_profiling_entry_points_validate_like_the_plain_ones():
     """The measurement calls run the same argument checks before anything is
     enqueued, and the chunkwise one needs its event array."""
