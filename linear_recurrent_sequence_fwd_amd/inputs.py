@@ -28,6 +28,7 @@ __all__ = [
     "bf16_bits",
     "bf16_round",
     "make_fwd_inputs",
+    "make_grad_output",
     "make_step_inputs",
     "make_state",
     "make_slstm_inputs",
@@ -91,6 +92,19 @@ def make_fwd_inputs(B: int, H: int, T: int, d_qk: int, d_v: int, dtype: str = "f
         "i_pre": i_pre.astype(np.float32), "f_pre": f_pre.astype(np.float32),
         "o_pre": _cast(o_pre, dtype), "dtype": dtype,
     }
+
+
+def make_grad_output(B: int, H: int, T: int, d_v: int, dtype: str = "fp32", seed: int = 0,
+                     scale: float = 1.0) -> np.ndarray:
+    """Upstream gradient dL/dh of a full-sequence forward, [B, H, T, d_v].
+
+    Drawn from its own stream ``PCG64([seed, 0xD0])`` so that it does not
+    shift the forward's draws: N(0, 1) times ``scale``, in float32, rounded to
+    bfloat16 for ``dtype == "bf16"`` like the forward's activations.
+    """
+    rng = np.random.Generator(np.random.PCG64([seed, 0xD0]))
+    dh = rng.standard_normal((B, H, T, d_v), dtype=np.float32) * np.float32(scale)
+    return _cast(dh, dtype)
 
 
 def make_step_inputs(B: int, H: int, d_qk: int, d_v: int, step: int, dtype: str = "fp32",

@@ -2,8 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY: used by tests/, the smoke check and the bench's CPU
 baseline, never by the product path. The C file is the same stabilised step
-recurrence as ``mlstm_oracle.mlstm_recurrent``, one sequence per host
-thread, so that whole outputs of the large workloads can be compared.
+recurrence as ``mlstm_oracle.mlstm_recurrent`` and the same reverse mode as
+``mlstm_grad.mlstm_backward``, one sequence per host thread, so that whole
+outputs of the large workloads can be compared.
 ``build()`` compiles it with gcc into oracle/libmlstm_ref.so; ``lib()`` builds
 it first when the library is missing or older than its source.
 """
@@ -42,6 +43,9 @@ def lib() -> ctypes.CDLL:
         P = ctypes.c_void_p
         L.mlstm_ref_run.argtypes = [ctypes.c_int64] * 4 + [P] * 6 + [P] * 4 + [ctypes.c_int]
         L.mlstm_ref_run.restype = ctypes.c_int
+        L.mlstm_ref_bwd.argtypes = ([ctypes.c_int64] * 4 + [P] * 7 + [P] * 3 + [P] * 9
+                                    + [ctypes.c_int64, ctypes.c_int])
+        L.mlstm_ref_bwd.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -103,3 +107,40 @@ def mlstm_step_c(q, k, v, i_pre, f_pre, o_pre, C, n, m, threads=None):
     if rc != 0:
         raise RuntimeError("mlstm_ref_run could not start its threads")
     return h.reshape(lead + (V,))
+
+
+def mlstm_backward_c(q, k, v, i_pre, f_pre, o_pre, dh, C0=None, n0=None, m0=None, threads=None,
+                     seg=0):
+    """Same contract as mlstm_grad.mlstm_backward for float32-representable
+    inputs: returns a dict of float64 arrays dq, dk, dv, di, df, do, dC0,
+    dn0, dm0. ``seg`` is the checkpoint interval of the reverse sweep (0:
+    about sqrt(T)); it changes memory, not results."""
+    q = _f32(q)
+    lead = q.shape[:-2]
+    T, K = q.shape[-2], q.shape[-1]
+    V = np.shape(v)[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    a = [_f32(x).reshape(BH, T, -1) for x in (q, k, v)]
+    g = [_f32(x).reshape(BH, T) for x in (i_pre, f_pre)]
+    o = _f32(o_pre).reshape(BH, T, V)
+    d = _f32(dh).reshape(BH, T, V)
+    st = [None, None, None]
+    if C0 is not None:
+        st = [np.ascontiguousarray(np.asarray(C0, np.float64).reshape(BH, V, K)),
+              np.ascontiguousarray(np.asarray(n0, np.float64).reshape(BH, K)),
+              np.ascontiguousarray(np.asarray(m0, np.float64).reshape(BH))]
+    out = {"dq": np.empty((BH, T, K)), "dk": np.empty((BH, T, K)), "dv": np.empty((BH, T, V)),
+           "di": np.empty((BH, T)), "df": np.empty((BH, T)), "do": np.empty((BH, T, V)),
+           "dC0": np.empty((BH, V, K)), "dn0": np.empty((BH, K)), "dm0": np.empty(BH)}
+    ptr = lambda x: None if x is None else x.ctypes.data  # noqa: E731
+    rc = lib().mlstm_ref_bwd(BH, T, K, V, a[0].ctypes.data, a[1].ctypes.data, a[2].ctypes.data,
+                             g[0].ctypes.data, g[1].ctypes.data, o.ctypes.data, d.ctypes.data,
+                             ptr(st[0]), ptr(st[1]), ptr(st[2]),
+                             *(out[n].ctypes.data for n in ("dq", "dk", "dv", "di", "df", "do",
+                                                            "dC0", "dn0", "dm0")),
+                             int(seg), threads or default_threads())
+    if rc != 0:
+        raise RuntimeError("mlstm_ref_bwd could not allocate its buffers or start its threads")
+    shapes = {"dq": (T, K), "dk": (T, K), "dv": (T, V), "di": (T,), "df": (T,), "do": (T, V),
+              "dC0": (V, K), "dn0": (K,), "dm0": ()}
+    return {n: out[n].reshape(lead + shapes[n]) for n in out}
