@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MLSTM_ABI_VERSION 1
+#define MLSTM_ABI_VERSION 2
 
 typedef enum mlstm_status {
   MLSTM_OK = 0,
@@ -92,9 +92,10 @@ typedef struct mlstm_fwd_args {
  * state (each chunk's local end state, then their in-order fold into every
  * chunk's start state, all float32); and the output kernel, which walks each
  * chunk's tiles from its start state with decay-masked Q K^T, P V, the
- * carried-state term and the state update on MFMA. (bfloat16 with d_v a
- * multiple of 128; other shapes run a two-pass variant that stores every
- * chunk's start state, bf16 for MLSTM_BF16, float32 for MLSTM_FP32.) The
+ * carried-state term (the float32 state as two bf16 terms for MLSTM_BF16)
+ * and the state update on MFMA. (bfloat16 with d_v a multiple of 128; other
+ * shapes run a two-pass variant that stores every chunk's start state in
+ * float32.) The
  * workspace holds those states and the per-token gate prefix sums; its size
  * comes from mlstm_fwd_chunkwise_workspace_size(). Outputs must not overlap
  * inputs, each other or the workspace.
@@ -160,6 +161,59 @@ int mlstm_step(const mlstm_step_args* args, void* stream);
  */
 size_t mlstm_fwd_chunkwise_noalloc_limit(void);
 int mlstm_fwd_chunkwise_noalloc(const mlstm_fwd_args* args, int chunk, void* stream);
+
+/* Arguments of a chunkwise backward pass (gradient of a loss through h). */
+typedef struct mlstm_bwd_args {
+  int64_t B, H, T;        /* as for the forward */
+  int64_t d_qk, d_v;      /* bf16: d_qk in {64, 128, 256}, d_v in {64, 128, 256, 512};
+                             fp32: d_qk in {64, 128}, d_v in {64, 128, 256} */
+  int32_t dtype;          /* mlstm_dtype of q, k, v, o_pre, h, dh and of dq, dk, dv, do_pre */
+  const void* q;          /* [B,H,T,d_qk] the forward's inputs */
+  const void* k;          /* [B,H,T,d_qk] */
+  const void* v;          /* [B,H,T,d_v]  */
+  const void* o_pre;      /* [B,H,T,d_v]  */
+  const float* i_pre;     /* [B,H,T]      */
+  const float* f_pre;     /* [B,H,T]      */
+  const void* h;          /* [B,H,T,d_v]  the forward's output for these inputs */
+  const void* dh;         /* [B,H,T,d_v]  dL/dh, the incoming gradient */
+  const float* C0;        /* the forward's initial state [B,H,d_v,d_qk], or NULL (zero state) */
+  const float* n0;        /* [B,H,d_qk]; required iff C0 != NULL */
+  const float* m0;        /* [B,H];      required iff C0 != NULL */
+  void* dq;               /* [B,H,T,d_qk] outputs (written) */
+  void* dk;               /* [B,H,T,d_qk] */
+  void* dv;               /* [B,H,T,d_v]  */
+  void* do_pre;           /* [B,H,T,d_v]  dL/d o_pre */
+  float* di_pre;          /* [B,H,T]      dL/d i_pre */
+  float* df_pre;          /* [B,H,T]      dL/d f_pre */
+  float* dC0;             /* optional [B,H,d_v,d_qk]: dL/d C0 (stabilised units), NULL = not wanted */
+  float* dn0;             /* [B,H,d_qk]; required iff dC0 != NULL */
+  float* dm0;             /* [B,H];      required iff dC0 != NULL */
+} mlstm_bwd_args;
+
+/*
+ * Chunkwise backward pass: the gradient of a loss L through the outputs h
+ * of mlstm_fwd_chunkwise with respect to q, k, v and the three gate
+ * preactivations, and (when dC0 is given) the initial state, for training
+ * (xLSTM guide, aifetchly blog: the dual and chunkwise forms are what make
+ * the mLSTM trainable in parallel, "The Dual Formulation: How mLSTM Enables
+ * Parallel GPU Training" and "Exploit Chunkwise Hardware Kernels for
+ * Production Training"). L reaches the cell only through h: no gradient of
+ * the final state is taken in. `h` must be the forward's output for the same
+ * inputs and initial state (it supplies num/den for the normaliser and
+ * output-gate terms). The chunk states are recomputed (gate prefix sums and
+ * the inter-chunk state pass, as in the forward); then per 64-row tile dq,
+ * dL/d o_pre and g = dh o / den; the chunks' end adjoints from the last
+ * chunk to the first; per 64-key tile dk, dv, dL/d i_pre; and the forget
+ * gate's gradient as suffix sums of q.dq - k.dk that stop at a zero forget
+ * gate. dC0 is the gradient with respect to the stabilised C~0 as passed
+ * (without C0: at the zero state, m0 = 0); dm0 = <dC0, C~0> + dn0 . n~0.
+ * `chunk`: multiple of 64 in [64, 8192]. Outputs must not overlap inputs,
+ * each other or the workspace (size from mlstm_bwd_chunkwise_workspace_size).
+ * Other shapes return MLSTM_ERR_UNSUPPORTED.
+ */
+size_t mlstm_bwd_chunkwise_workspace_size(const mlstm_bwd_args* args, int chunk);
+int mlstm_bwd_chunkwise(const mlstm_bwd_args* args, int chunk, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* mlstm_status_string(int status);

@@ -35,6 +35,22 @@ extern "C" {
 int mlstm_prof_fwd_chunkwise(const mlstm_fwd_args* args, int chunk, void* workspace,
                              size_t workspace_bytes, void* stream, void* const* events);
 
+/* Kernel groups of a chunkwise backward pass, in launch order. */
+#define MLSTM_PROF_BWD_FWD_GATE 0   /* the forward's gate prefix sums */
+#define MLSTM_PROF_BWD_FWD_STATE 1  /* the forward's inter-chunk state pass */
+#define MLSTM_PROF_BWD_DQ 2         /* dq, do~ and g per 64-row tile */
+#define MLSTM_PROF_BWD_STATE 3      /* chunk end adjoints, last chunk to first */
+#define MLSTM_PROF_BWD_DKV 4        /* dk, dv, di~ per 64-key tile */
+#define MLSTM_PROF_BWD_GATE 5       /* forget-gate suffix sums */
+
+/*
+ * mlstm_bwd_chunkwise (same arguments, same result) that records
+ * events[2 g] before and events[2 g + 1] after kernel group g, g = 0..5 as
+ * above: twelve caller-created hipEvent_t handles, NULL entries skipped.
+ */
+int mlstm_prof_bwd_chunkwise(const mlstm_bwd_args* args, int chunk, void* workspace,
+                             size_t workspace_bytes, void* stream, void* const* events);
+
 /*
  * mlstm_step (same arguments, same result) that records the hipEvent_t
  * `before` and `after` on `stream` around the step kernel (NULL: skipped).

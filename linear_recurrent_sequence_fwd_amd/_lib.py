@@ -21,6 +21,8 @@ STATUS = {
     -7: "MLSTM_ERR_UNSUPPORTED", -8: "MLSTM_ERR_HIP",
 }
 PROF_GROUPS = ("gate", "state", "out")   # kernel groups of mlstm_prof_fwd_chunkwise, in order
+# kernel groups of mlstm_prof_bwd_chunkwise, in order
+BWD_PROF_GROUPS = ("fwd_gate", "fwd_state", "dq", "adjoint", "dkv", "dgate")
 
 
 class FwdArgs(ctypes.Structure):
@@ -41,6 +43,19 @@ class StepArgs(ctypes.Structure):
         ("i_pre", c_void_p), ("f_pre", c_void_p),
         ("C", c_void_p), ("n_in", c_void_p), ("m_in", c_void_p),
         ("n_out", c_void_p), ("m_out", c_void_p), ("h", c_void_p),
+    ]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", c_int64), ("H", c_int64), ("T", c_int64), ("d_qk", c_int64), ("d_v", c_int64),
+        ("dtype", c_int32),
+        ("q", c_void_p), ("k", c_void_p), ("v", c_void_p), ("o_pre", c_void_p),
+        ("i_pre", c_void_p), ("f_pre", c_void_p), ("h", c_void_p), ("dh", c_void_p),
+        ("C0", c_void_p), ("n0", c_void_p), ("m0", c_void_p),
+        ("dq", c_void_p), ("dk", c_void_p), ("dv", c_void_p), ("do_pre", c_void_p),
+        ("di_pre", c_void_p), ("df_pre", c_void_p),
+        ("dC0", c_void_p), ("dn0", c_void_p), ("dm0", c_void_p),
     ]
 
 
@@ -86,6 +101,13 @@ def lib() -> ctypes.CDLL:
         L.mlstm_fwd_parallel_workspace_size.restype = c_size_t
         L.mlstm_fwd_parallel.argtypes = [P(FwdArgs), c_void_p, c_size_t, c_void_p]
         L.mlstm_fwd_parallel.restype = c_int
+        L.mlstm_bwd_chunkwise_workspace_size.argtypes = [P(BwdArgs), c_int]
+        L.mlstm_bwd_chunkwise_workspace_size.restype = c_size_t
+        L.mlstm_bwd_chunkwise.argtypes = [P(BwdArgs), c_int, c_void_p, c_size_t, c_void_p]
+        L.mlstm_bwd_chunkwise.restype = c_int
+        L.mlstm_prof_bwd_chunkwise.argtypes = [P(BwdArgs), c_int, c_void_p, c_size_t, c_void_p,
+                                               P(c_void_p)]
+        L.mlstm_prof_bwd_chunkwise.restype = c_int
         L.mlstm_step.argtypes = [P(StepArgs), c_void_p]
         L.mlstm_step.restype = c_int
         L.mlstm_status_string.argtypes = [c_int]
@@ -245,6 +267,75 @@ def mlstm_fwd_parallel(q, k, v, o_pre, i_pre, f_pre, C0=None, n0=None, m0=None,
     return (h, (C_out, n_out, m_out)) if return_state else h
 
 
+def bwd_args(q, k, v, o_pre, i_pre, f_pre, h, dh, grads, C0=None, n0=None, m0=None) -> BwdArgs:
+    """Fill the argument struct of a backward call from tensors (shapes
+    checked). `grads` maps dq, dk, dv, do, di, df (and optionally dC0, dn0,
+    dm0) to output tensors."""
+    import torch
+    B, H, T, K = q.shape
+    V = v.shape[-1]
+    dt = q.dtype
+    for name, t, shp in (("q", q, (B, H, T, K)), ("k", k, (B, H, T, K)), ("v", v, (B, H, T, V)),
+                         ("o_pre", o_pre, (B, H, T, V)), ("h", h, (B, H, T, V)),
+                         ("dh", dh, (B, H, T, V)), ("dq", grads["dq"], (B, H, T, K)),
+                         ("dk", grads["dk"], (B, H, T, K)), ("dv", grads["dv"], (B, H, T, V)),
+                         ("do", grads["do"], (B, H, T, V))):
+        _require(t, name, shp, dt)
+    for name, t in (("i_pre", i_pre), ("f_pre", f_pre), ("di", grads["di"]), ("df", grads["df"])):
+        _require(t, name, (B, H, T), torch.float32)
+    if C0 is not None:
+        _require(C0, "C0", (B, H, V, K), torch.float32)
+        _require(n0, "n0", (B, H, K), torch.float32)
+        _require(m0, "m0", (B, H), torch.float32)
+    dC0, dn0, dm0 = grads.get("dC0"), grads.get("dn0"), grads.get("dm0")
+    if dC0 is not None:
+        _require(dC0, "dC0", (B, H, V, K), torch.float32)
+        _require(dn0, "dn0", (B, H, K), torch.float32)
+        _require(dm0, "dm0", (B, H), torch.float32)
+    return BwdArgs(B, H, T, K, V, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o_pre),
+                   _ptr(i_pre), _ptr(f_pre), _ptr(h), _ptr(dh), _ptr(C0), _ptr(n0), _ptr(m0),
+                   _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["do"]),
+                   _ptr(grads["di"]), _ptr(grads["df"]), _ptr(dC0), _ptr(dn0), _ptr(dm0))
+
+
+def bwd_workspace_bytes(args: BwdArgs, chunk: int) -> int:
+    return int(lib().mlstm_bwd_chunkwise_workspace_size(ctypes.byref(args), chunk))
+
+
+def bwd_outputs(q, v, init_grad=False) -> dict:
+    """Freshly allocated gradient outputs for a backward call."""
+    import torch
+    B, H, T, K = q.shape
+    V = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    g = {"dq": torch.empty((B, H, T, K), dtype=dt, device=dev),
+         "dk": torch.empty((B, H, T, K), dtype=dt, device=dev),
+         "dv": torch.empty((B, H, T, V), dtype=dt, device=dev),
+         "do": torch.empty((B, H, T, V), dtype=dt, device=dev),
+         "di": torch.empty((B, H, T), dtype=torch.float32, device=dev),
+         "df": torch.empty((B, H, T), dtype=torch.float32, device=dev)}
+    if init_grad:
+        g["dC0"] = torch.empty((B, H, V, K), dtype=torch.float32, device=dev)
+        g["dn0"] = torch.empty((B, H, K), dtype=torch.float32, device=dev)
+        g["dm0"] = torch.empty((B, H), dtype=torch.float32, device=dev)
+    return g
+
+
+def mlstm_bwd_chunkwise(q, k, v, o_pre, i_pre, f_pre, h, dh, chunk=64, C0=None, n0=None, m0=None,
+                        init_grad=False, grads=None, workspace=None, stream=None):
+    """Chunkwise backward pass: gradients of a loss through h (dh = dL/dh).
+    Returns a dict with dq, dk, dv, do (of o_pre), di (of i_pre), df (of
+    f_pre) and, when init_grad, dC0, dn0, dm0. `h` is the forward's output."""
+    if grads is None:
+        grads = bwd_outputs(q, v, init_grad)
+    args = bwd_args(q, k, v, o_pre, i_pre, f_pre, h, dh, grads, C0, n0, m0)
+    nbytes = bwd_workspace_bytes(args, chunk)
+    ws = _workspace(nbytes, q.device, workspace)
+    _check(lib().mlstm_bwd_chunkwise(ctypes.byref(args), int(chunk), _ptr(ws), nbytes, _stream(stream)),
+           "mlstm_bwd_chunkwise")
+    return grads
+
+
 def step_args(q, k, v, o_pre, i_pre, f_pre, C, n_in, m_in, n_out, m_out, h) -> StepArgs:
     import torch
     B, H, K = q.shape
@@ -278,11 +369,12 @@ def mlstm_step(q, k, v, o_pre, i_pre, f_pre, C, n_in, m_in, n_out=None, m_out=No
 
 
 def event_array(events):
-    """A ctypes array of six hipEvent_t handles (ints or None) for
-    mlstm_prof_fwd_chunkwise: before/after of each group in PROF_GROUPS."""
-    if len(events) != 2 * len(PROF_GROUPS):
-        raise ValueError("six event handles are needed")
-    return (c_void_p * 6)(*events)
+    """A ctypes array of hipEvent_t handles (ints or None): six for
+    mlstm_prof_fwd_chunkwise (before/after of each group in PROF_GROUPS),
+    twelve for mlstm_prof_bwd_chunkwise (BWD_PROF_GROUPS)."""
+    if len(events) not in (2 * len(PROF_GROUPS), 2 * len(BWD_PROF_GROUPS)):
+        raise ValueError("six or twelve event handles are needed")
+    return (c_void_p * len(events))(*events)
 
 
 def clock_probe(ticks, iters: int, stream=None) -> None:

@@ -160,7 +160,7 @@ WsLayout layout_fused(int64_t BH, int64_t T, int chunk, int64_t K, int64_t V) {
   w.mloc = take(BH * ns * 8);
   w.mstart = take(BH * ns * 8);
   w.Gseg = take(BH * ns * 8);
-  w.wb = take(BH * fs.Nt * 2 * 64 * 2);
+  w.wb = take(BH * fs.Nt * 3 * 64 * 2);
   w.total = off;
   return w;
 }
@@ -237,7 +237,7 @@ size_t mlstm_fwd_chunkwise_workspace_size(const mlstm_fwd_args* a, int chunk) {
   if (a->B < 1 || a->H < 1 || a->d_qk < 1 || a->d_v < 1) return 0;
   if (use_fused(a)) return layout_fused(a->B * a->H, a->T, chunk, a->d_qk, a->d_v).total;
   const int64_t Nc = (a->T + chunk - 1) / chunk;
-  return layout(a->B * a->H, a->T, Nc, a->d_qk, a->d_v, a->dtype == MLSTM_BF16 ? 2 : 4, true).total;
+  return layout(a->B * a->H, a->T, Nc, a->d_qk, a->d_v, 4, true).total;
 }
 
 }  // extern "C"
@@ -276,7 +276,7 @@ int fwd_chunkwise(const mlstm_fwd_args* a, int chunk, void* workspace, size_t wo
     if ((st = hip_status(mlstm_impl::launch_gate(ft, gb, s), "gate kernel"))) return st;
     return hip_status(mlstm_impl::launch_fused(ft, gb, ss, s), "fused kernels");
   }
-  const WsLayout w = layout(f.BH, f.T, Nc, f.K, f.V, f.bf16 ? 2 : 4, true);
+  const WsLayout w = layout(f.BH, f.T, Nc, f.K, f.V, 4, true);
   const mlstm_impl::GateBuffers gb = gate_buffers(ws, w);
   mlstm_impl::ChunkStates cs;
   cs.Cs = ws + w.Cs;
@@ -321,6 +321,182 @@ int mlstm_fwd_parallel(const mlstm_fwd_args* a, void* workspace, size_t workspac
   if ((st = hip_status(mlstm_impl::launch_out(f, gb, none, s), "output kernel"))) return st;
   if (a->C_out) return hip_status(mlstm_impl::launch_state(f, gb, none, s), "state kernel");
   return MLSTM_OK;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ backward pass
+
+namespace {
+
+struct BwdLayout {
+  WsLayout fw;   // gate prefix data and the forward's chunk-start states
+  size_t G, dz, qdq, Es, es, Ms, total;
+};
+
+BwdLayout layout_bwd(int64_t BH, int64_t T, int64_t Nc, int64_t K, int64_t V, int64_t elem) {
+  BwdLayout b;
+  b.fw = layout(BH, T, Nc, K, V, 4, true);
+  size_t off = b.fw.total;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  b.G = take(BH * T * V * elem);
+  b.dz = take(BH * T * 4);
+  b.qdq = take(BH * T * 4);
+  b.Es = take(BH * Nc * V * K * 4);
+  b.es = take(BH * Nc * K * 4);
+  b.Ms = take(BH * Nc * 8);
+  b.total = off;
+  return b;
+}
+
+int validate_bwd(const mlstm_bwd_args* a, int chunk) {
+  if (!a) return fail(MLSTM_ERR_NULLPTR, "args is NULL");
+  if (a->dtype != MLSTM_FP32 && a->dtype != MLSTM_BF16)
+    return fail(MLSTM_ERR_BAD_DTYPE, "dtype must be MLSTM_FP32 or MLSTM_BF16");
+  if (a->B < 1 || a->H < 1 || a->T < 0 || a->d_qk < 1 || a->d_v < 1)
+    return fail(MLSTM_ERR_BAD_SHAPE, "need B >= 1, H >= 1, T >= 0, d_qk >= 1, d_v >= 1");
+  if (chunk < 64 || chunk % 64 != 0 || chunk > kMaxChunk)
+    return fail(MLSTM_ERR_BAD_SHAPE, "chunk must be a multiple of 64 in [64, 8192]");
+  if (a->d_qk % 64 != 0 || a->d_v % 64 != 0)
+    return fail(MLSTM_ERR_BAD_SHAPE, "d_qk and d_v must be multiples of 64");
+  if (!mlstm_impl::bwd_supported(a->dtype == MLSTM_BF16, a->d_qk, a->d_v))
+    return fail(MLSTM_ERR_UNSUPPORTED,
+                "backward shapes: bf16 d_qk in {64,128,256}, d_v in {64,128,256,512}; "
+                "fp32 d_qk in {64,128}, d_v in {64,128,256}");
+  const bool any0 = a->C0 || a->n0 || a->m0, all0 = a->C0 && a->n0 && a->m0;
+  if (any0 && !all0) return fail(MLSTM_ERR_NULLPTR, "C0, n0, m0 must be given together");
+  const bool anyd = a->dC0 || a->dn0 || a->dm0, alld = a->dC0 && a->dn0 && a->dm0;
+  if (anyd && !alld) return fail(MLSTM_ERR_NULLPTR, "dC0, dn0, dm0 must be given together");
+  if (a->T > 0 && (!a->q || !a->k || !a->v || !a->o_pre || !a->i_pre || !a->f_pre || !a->h || !a->dh ||
+                   !a->dq || !a->dk || !a->dv || !a->do_pre || !a->di_pre || !a->df_pre))
+    return fail(MLSTM_ERR_NULLPTR, "inputs, h, dh and the six gradient outputs are required when T > 0");
+  const void* v16[] = {a->q, a->k, a->v, a->o_pre, a->h, a->dh, a->dq, a->dk, a->dv, a->do_pre,
+                       a->C0, a->n0, a->dC0, a->dn0};
+  for (const void* p : v16)
+    if (p && !aligned(p, 16)) return fail(MLSTM_ERR_MISALIGNED, "array pointers must be 16-byte aligned");
+  const void* v4[] = {a->i_pre, a->f_pre, a->m0, a->di_pre, a->df_pre, a->dm0};
+  for (const void* p : v4)
+    if (p && !aligned(p, 4)) return fail(MLSTM_ERR_MISALIGNED, "gate and m pointers must be 4-byte aligned");
+  const int64_t BH = a->B * a->H;
+  if (BH * ((a->T + 63) / 64) > INT32_MAX || BH * (a->d_qk / 64) * (a->d_v / 64) > INT32_MAX)
+    return fail(MLSTM_ERR_UNSUPPORTED, "problem too large for one launch grid");
+  const int64_t es = a->dtype == MLSTM_BF16 ? 2 : 4;
+  const int64_t nqk = BH * a->T * a->d_qk * es, nv = BH * a->T * a->d_v * es, ng = BH * a->T * 4;
+  const int64_t nC = BH * a->d_v * a->d_qk * 4, nn = BH * a->d_qk * 4, nm = BH * 4;
+  std::vector<Range> in = {make_range("q", a->q, nqk), make_range("k", a->k, nqk),
+                           make_range("v", a->v, nv), make_range("o_pre", a->o_pre, nv),
+                           make_range("i_pre", a->i_pre, ng), make_range("f_pre", a->f_pre, ng),
+                           make_range("h", a->h, nv), make_range("dh", a->dh, nv),
+                           make_range("C0", a->C0, nC), make_range("n0", a->n0, nn),
+                           make_range("m0", a->m0, nm)};
+  std::vector<Range> out = {make_range("dq", a->dq, nqk), make_range("dk", a->dk, nqk),
+                            make_range("dv", a->dv, nv), make_range("do_pre", a->do_pre, nv),
+                            make_range("di_pre", a->di_pre, ng), make_range("df_pre", a->df_pre, ng),
+                            make_range("dC0", a->dC0, nC), make_range("dn0", a->dn0, nn),
+                            make_range("dm0", a->dm0, nm)};
+  int st = check_alias(in, out);
+  if (st) return st;
+  return MLSTM_OK;
+}
+
+size_t bwd_workspace_size(const mlstm_bwd_args* a, int chunk) {
+  if (!a || a->T <= 0 || chunk < 64 || chunk % 64 != 0 || chunk > kMaxChunk) return 0;
+  if (a->B < 1 || a->H < 1 || a->d_qk < 1 || a->d_v < 1) return 0;
+  const int64_t Nc = (a->T + chunk - 1) / chunk;
+  return layout_bwd(a->B * a->H, a->T, Nc, a->d_qk, a->d_v, a->dtype == MLSTM_BF16 ? 2 : 4).total;
+}
+
+int bwd_chunkwise(const mlstm_bwd_args* a, int chunk, void* workspace, size_t workspace_bytes, void* stream,
+                  const hipEvent_t* marks) {
+  g_last_error.clear();
+  int st = validate_bwd(a, chunk);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t BH = a->B * a->H;
+  const int64_t Nc = a->T > 0 ? (a->T + chunk - 1) / chunk : 0;
+  mlstm_impl::BwdLaunch b;
+  b.BH = BH; b.T = a->T; b.K = a->d_qk; b.V = a->d_v; b.L = chunk; b.Nc = Nc;
+  b.bf16 = a->dtype == MLSTM_BF16;
+  b.q = a->q; b.k = a->k; b.v = a->v; b.o = a->o_pre; b.h = a->h; b.dh = a->dh;
+  b.i_pre = a->i_pre; b.f_pre = a->f_pre;
+  b.dq = a->dq; b.dk = a->dk; b.dv = a->dv; b.dout = a->do_pre; b.di = a->di_pre; b.df = a->df_pre;
+  b.C0 = a->C0; b.n0 = a->n0; b.m0 = a->m0;
+  b.dC0 = a->dC0; b.dn0 = a->dn0; b.dm0 = a->dm0;
+  b.marks = marks;
+  const mlstm_impl::GateBuffers none_gb{};
+  const mlstm_impl::ChunkStates none_cs{nullptr, nullptr, nullptr};
+  const mlstm_impl::BwdBuffers none_bb{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  if (a->T == 0) return hip_status(mlstm_impl::launch_bwd(b, none_gb, none_cs, none_bb, s), "backward");
+  const size_t need = bwd_workspace_size(a, chunk);
+  if (!workspace) return fail(MLSTM_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, kAlign)) return fail(MLSTM_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(MLSTM_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  {
+    const int64_t es = b.bf16 ? 2 : 4;
+    const int64_t nqk = BH * a->T * a->d_qk * es, nv = BH * a->T * a->d_v * es, ng = BH * a->T * 4;
+    const int64_t nC = BH * a->d_v * a->d_qk * 4, nn = BH * a->d_qk * 4, nm = BH * 4;
+    const Range wr = make_range("workspace", workspace, (int64_t)need);
+    const Range other[] = {make_range("q", a->q, nqk), make_range("k", a->k, nqk), make_range("v", a->v, nv),
+                           make_range("o_pre", a->o_pre, nv), make_range("i_pre", a->i_pre, ng),
+                           make_range("f_pre", a->f_pre, ng), make_range("h", a->h, nv),
+                           make_range("dh", a->dh, nv), make_range("C0", a->C0, nC),
+                           make_range("n0", a->n0, nn), make_range("m0", a->m0, nm),
+                           make_range("dq", a->dq, nqk), make_range("dk", a->dk, nqk),
+                           make_range("dv", a->dv, nv), make_range("do_pre", a->do_pre, nv),
+                           make_range("di_pre", a->di_pre, ng), make_range("df_pre", a->df_pre, ng),
+                           make_range("dC0", a->dC0, nC), make_range("dn0", a->dn0, nn),
+                           make_range("dm0", a->dm0, nm)};
+    for (const Range& r : other)
+      if (overlap(wr, r)) return fail(MLSTM_ERR_ALIAS, std::string("workspace overlaps ") + r.name);
+  }
+  char* ws = static_cast<char*>(workspace);
+  const BwdLayout w = layout_bwd(BH, a->T, Nc, a->d_qk, a->d_v, b.bf16 ? 2 : 4);
+  const mlstm_impl::GateBuffers gb = gate_buffers(ws, w.fw);
+  mlstm_impl::ChunkStates cs;
+  cs.Cs = ws + w.fw.Cs;
+  cs.ns = reinterpret_cast<float*>(ws + w.fw.ns);
+  cs.ms = reinterpret_cast<double*>(ws + w.fw.ms);
+  mlstm_impl::BwdBuffers bb;
+  bb.G = ws + w.G;
+  bb.dz = reinterpret_cast<float*>(ws + w.dz);
+  bb.qdq = reinterpret_cast<float*>(ws + w.qdq);
+  bb.Es = ws + w.Es;
+  bb.es = reinterpret_cast<float*>(ws + w.es);
+  bb.Ms = reinterpret_cast<double*>(ws + w.Ms);
+  // the forward's gate prefix sums and chunk-start states (the K_GATE and
+  // K_STATE event slots coincide with the backward's first two groups)
+  mlstm_impl::FwdLaunch f{};
+  f.BH = BH; f.T = a->T; f.K = a->d_qk; f.V = a->d_v; f.L = chunk; f.Nc = Nc; f.bf16 = b.bf16;
+  f.q = a->q; f.k = a->k; f.v = a->v; f.o = a->o_pre;
+  f.i_pre = a->i_pre; f.f_pre = a->f_pre; f.h = nullptr;
+  f.C0 = a->C0; f.n0 = a->n0; f.m0 = a->m0;
+  f.C_out = nullptr; f.n_out = nullptr; f.m_out = nullptr;
+  f.marks = marks;
+  if ((st = hip_status(mlstm_impl::launch_gate(f, gb, s), "gate kernel"))) return st;
+  if ((st = hip_status(mlstm_impl::launch_state(f, gb, cs, s), "state kernel"))) return st;
+  return hip_status(mlstm_impl::launch_bwd(b, gb, cs, bb, s), "backward kernels");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mlstm_bwd_chunkwise_workspace_size(const mlstm_bwd_args* a, int chunk) {
+  return bwd_workspace_size(a, chunk);
+}
+
+int mlstm_bwd_chunkwise(const mlstm_bwd_args* a, int chunk, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return bwd_chunkwise(a, chunk, workspace, workspace_bytes, stream, nullptr);
+}
+
+int mlstm_prof_bwd_chunkwise(const mlstm_bwd_args* a, int chunk, void* workspace, size_t workspace_bytes,
+                             void* stream, void* const* events) {
+  if (!events) return fail(MLSTM_ERR_NULLPTR, "events is NULL");
+  hipEvent_t marks[2 * mlstm_impl::B_COUNT] = {};
+  for (int x = 0; x < 2 * mlstm_impl::B_COUNT; ++x) marks[x] = static_cast<hipEvent_t>(events[x]);
+  return bwd_chunkwise(a, chunk, workspace, workspace_bytes, stream, marks);
 }
 
 }  // extern "C"

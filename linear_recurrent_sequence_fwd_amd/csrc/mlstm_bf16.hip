@@ -71,7 +71,7 @@ struct StateArgsB {
   const __bf16* v;
   GateBuffers gb;
   const float *C0, *n0, *m0;
-  __bf16* Cs;
+  float* Cs;
   float* ns;
   double* ms;
   float *C_out, *n_out, *m_out;
@@ -87,11 +87,11 @@ struct StateArgsB {
 // and contracted over tokens on MFMA into a per-chunk accumulator. At the
 // chunk's end the carried tile becomes decay*C + alpha*acc_chunk with
 // Rm = max(m_prev, U_c), decay = exp(m_prev - Rm), alpha = exp(U_c - Rm), and
-// m advances to g_c + Rm; at the next chunk's start it is stored (bf16). The
+// m advances to g_c + Rm; at the next chunk's start it is stored (float32). The
 // chunk scalars (g, U, R) are loaded one chunk ahead. The normaliser n is the
 // same contraction with V replaced by ones: the waves with wv = 0 of the
 // v-tile-0 workgroups compute it as one more 16-column MFMA tile, with each
-// weight split into two bf16 terms (w = hi + lo) so that n keeps about 17
+// weight split into three bf16 terms (w = hi + lo + lo2) so that n keeps about 24
 // bits, because rows where n^T q nearly cancels would magnify a rounded n.
 template <int K, int NPF>
 __global__ __launch_bounds__(kThreads) void state_kernel_bf16(StateArgsB a) {
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void state_kernel_bf16(StateArgsB a) {
   constexpr int P = kTile + 16;     // LDS row pitch (elements)
   __shared__ __attribute__((aligned(16))) __bf16 sK[2][kTile * P];
   __shared__ __attribute__((aligned(16))) __bf16 sV[2][kTile * P];
-  __shared__ __attribute__((aligned(16))) __bf16 sw[2][2][kTile];   // [buffer][hi, lo][token]
+  __shared__ __attribute__((aligned(16))) __bf16 sw[2][3][kTile];   // [buffer][hi, lo, lo2][token]
 
   const int64_t BH = a.BH, V = a.V, T = a.T;
   const int64_t bh = blockIdx.x % BH;
@@ -179,17 +179,14 @@ __global__ __launch_bounds__(kThreads) void state_kernel_bf16(StateArgsB a) {
     if (sb >= nsb) return;
     if (jc == 0) {   // chunk start: store the carried state, derive this chunk's scalars
       if (a.Cs) {
-        __bf16* Cs = a.Cs + (bh * a.Nc + c) * V * K;
+        float* Cs = a.Cs + (bh * a.Nc + c) * V * K;
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
           const int kk = 64 * kt + 32 * wk + 16 * x + 4 * g;
 #pragma unroll
           for (int y = 0; y < 2; ++y) {
             const int64_t vv = 64 * vt + 32 * wv + 16 * y + i;
-            bf16x4 o;
-            o[0] = (__bf16)acc[x][y][0]; o[1] = (__bf16)acc[x][y][1];
-            o[2] = (__bf16)acc[x][y][2]; o[3] = (__bf16)acc[x][y][3];
-            *reinterpret_cast<bf16x4*>(Cs + vv * K + kk) = o;
+            *reinterpret_cast<f32x4*>(Cs + vv * K + kk) = acc[x][y];
           }
           if (n_tile && i == 0) *reinterpret_cast<f32x4*>(a.ns + (bh * a.Nc + c) * K + kk) = nacc[x];
         }
@@ -215,8 +212,11 @@ __global__ __launch_bounds__(kThreads) void state_kernel_bf16(StateArgsB a) {
       *reinterpret_cast<bf16x8*>(&sV[buf][row * P + 8 * cg]) = scale8(pv[SLOT][e], wf);
       if (cg == 0) {
         const __bf16 hi = (__bf16)wf;
+        const float rest = wf - (float)hi;
+        const __bf16 lo = (__bf16)rest;
         sw[buf][0][row] = hi;
-        sw[buf][1][row] = (__bf16)(wf - (float)hi);
+        sw[buf][1][row] = lo;
+        sw[buf][2][row] = (__bf16)(rest - (float)lo);
       }
     }
     if (sb + NPF < nsb) issue(sb + NPF, slot_c);
@@ -235,8 +235,9 @@ __global__ __launch_bounds__(kThreads) void state_kernel_bf16(StateArgsB a) {
       if (n_tile) {
         const bf16x8 Bh = *reinterpret_cast<const bf16x8*>(&sw[buf][0][kk + 8 * g]);
         const bf16x8 Bl = *reinterpret_cast<const bf16x8*>(&sw[buf][1][kk + 8 * g]);
+        const bf16x8 Bl2 = *reinterpret_cast<const bf16x8*>(&sw[buf][2][kk + 8 * g]);
 #pragma unroll
-        for (int x = 0; x < 2; ++x) tn[x] = mma(A[x], Bl, mma(A[x], Bh, tn[x]));
+        for (int x = 0; x < 2; ++x) tn[x] = mma(A[x], Bl2, mma(A[x], Bl, mma(A[x], Bh, tn[x])));
       }
     }
     jc += kTile;
@@ -287,7 +288,7 @@ struct OutArgsB {
   const __bf16 *q, *k, *v, *o;
   __bf16* h;
   GateBuffers gb;
-  const __bf16* Cs;  // chunk-start states [BH][Nc][V][K] (bf16), or null
+  const float* Cs;   // chunk-start states [BH][Nc][V][K] (float32), or null
   const float* ns;   // [BH][Nc][K]
   const double* ms;  // [BH][Nc]
   const float* C0f;  // initial state [BH][V][K] (float32) for the one-chunk form, or null
@@ -379,24 +380,18 @@ __global__ __launch_bounds__(kThreads, 2) void out_kernel_bf16(OutArgsB a) {
     }
     if (t0 + tid < T) u_k = a.gb.u[bh * T + t0 + tid];
   }
-  bf16x8 Bst[D][NT];
-  const __bf16* Cst = chunk_states ? a.Cs + (bh * a.Nc + c) * V * K : nullptr;
-  const float* Cf = chunk_states ? nullptr : (a.C0f ? a.C0f + bh * V * K : nullptr);
+  // float32 state fragments, split into bf16 hi + lo at their MFMAs: rows
+  // whose q is nearly orthogonal to a dominant key make C~ q a strongly
+  // cancelling sum, which one bf16 rounding of C~ would swamp
+  f32x4 Bst[D][NT][2];
+  const float* Cst = chunk_states ? a.Cs + (bh * a.Nc + c) * V * K : (a.C0f ? a.C0f + bh * V * K : nullptr);
   auto load_state = [&](int s, auto slot_c) {
     constexpr int SL = decltype(slot_c)::value;
 #pragma unroll
     for (int y = 0; y < NT; ++y) {
       const int64_t off = (vrow0 + 16 * y + i) * K + 32 * s + 8 * g;
-      if (Cst) {
-        Bst[SL][y] = *reinterpret_cast<const bf16x8*>(Cst + off);
-      } else {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(Cf + off);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(Cf + off + 4);
-        bf16x8 r;
-        r[0] = (__bf16)x0[0]; r[1] = (__bf16)x0[1]; r[2] = (__bf16)x0[2]; r[3] = (__bf16)x0[3];
-        r[4] = (__bf16)x1[0]; r[5] = (__bf16)x1[1]; r[6] = (__bf16)x1[2]; r[7] = (__bf16)x1[3];
-        Bst[SL][y] = r;
-      }
+      Bst[SL][y][0] = *reinterpret_cast<const f32x4*>(Cst + off);
+      Bst[SL][y][1] = *reinterpret_cast<const f32x4*>(Cst + off + 4);
     }
   };
   if (has_state) {
@@ -476,9 +471,19 @@ __global__ __launch_bounds__(kThreads, 2) void out_kernel_bf16(OutArgsB a) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) A[x] = *reinterpret_cast<const bf16x8*>(&sQ[(16 * x + i) * QP + 32 * s + 8 * g]);
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int y = 0; y < NT; ++y) {
+        const f32x4 x0 = Bst[s % D][y][0], x1 = Bst[s % D][y][1];
+        bf16x8 hi, lo;
 #pragma unroll
-        for (int y = 0; y < NT; ++y) acc[x][y] = mma(A[x], Bst[s % D][y], acc[x][y]);
+        for (int e = 0; e < 4; ++e) {
+          hi[e] = (__bf16)x0[e];
+          hi[4 + e] = (__bf16)x1[e];
+          lo[e] = (__bf16)(x0[e] - (float)hi[e]);
+          lo[4 + e] = (__bf16)(x1[e] - (float)hi[4 + e]);
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) acc[x][y] = mma(A[x], lo, mma(A[x], hi, acc[x][y]));
+      }
       if constexpr (s + D < KS) load_state(s + D, std::integral_constant<int, s % D>{});
     });
 #pragma unroll
@@ -611,7 +616,7 @@ hipError_t run_state_b(const FwdLaunch& f, const GateBuffers& gb, const ChunkSta
   a.v = static_cast<const __bf16*>(f.v);
   a.gb = gb;
   a.C0 = f.C0; a.n0 = f.n0; a.m0 = f.m0;
-  a.Cs = static_cast<__bf16*>(cs.Cs);
+  a.Cs = static_cast<float*>(cs.Cs);
   a.ns = cs.ns; a.ms = cs.ms;
   a.C_out = f.C_out; a.n_out = f.n_out; a.m_out = f.m_out;
   a.T = f.T; a.Nc = f.Nc; a.V = f.V; a.BH = f.BH; a.L = f.L;
@@ -631,7 +636,7 @@ hipError_t run_out_b(const FwdLaunch& f, const GateBuffers& gb, const ChunkState
   a.o = static_cast<const __bf16*>(f.o);
   a.h = static_cast<__bf16*>(f.h);
   a.gb = gb;
-  a.Cs = static_cast<const __bf16*>(cs.Cs);
+  a.Cs = static_cast<const float*>(cs.Cs);
   a.ns = cs.ns; a.ms = cs.ms;
   a.C0f = cs.Cs ? nullptr : f.C0;
   a.n0 = f.n0; a.m0 = f.m0;

@@ -1,0 +1,1092 @@
+// HIP kernels of the chunkwise mLSTM backward pass for gfx950: the gradients
+// of a loss through the cell's outputs h with respect to q, k, v, the three
+// gate preactivations and the initial state.
+//
+// The pages present the dual and chunkwise forms as what makes the mLSTM
+// trainable (xLSTM guide, aifetchly blog, "The Dual Formulation: How mLSTM
+// Enables Parallel GPU Training"; "Exploit Chunkwise Hardware Kernels for
+// Production Training"). This is the reverse mode of the same chunkwise
+// evaluation, in the notation of the forward kernels (mlstm_kernels.hip): a
+// chunk starting at t0 with carried stabiliser m_prev, b_t the in-chunk
+// cumulative log forget gate, u_j = i~_j - b_j, r_t the row stabiliser
+// (m_t = b_t + r_t), P_tj = exp(u_j - r_t) the decay weight of key j in row t
+// and sc_t = exp(m_prev - r_t) the weight of the carried state.
+//
+// With the stabilised denominator den_t = max(|z_t|, exp(-m_t)) (z_t the
+// stabilised n_t . q_t) the per-row quantities are
+//   g_t  = dh_t sigmoid(o~_t) / den_t
+//   dz_t = -sign(z_t) [|z_t| > exp(-m_t)] (dh_t . h_t) / den_t
+//   do~_t = dh_t h_t (1 - sigmoid(o~_t))
+// and, inside a chunk (intra) plus through the carried state (inter),
+//   dq_t = sum_j P_tj (g_t . v_j + dz_t) k_j + sc_t (C~^T g_t + dz_t n~)
+//   dk_j = sum_t P_tj (g_t . v_j + dz_t) q_t + w_j (A^T v_j + a)
+//   dv_j = sum_t P_tj (q_t . k_j) g_t + w_j A k_j
+//   di~_j = k_j . dk_j,   dlog f_l = sum_{t >= l} (q_t . dq_t - k_t . dk_t)
+// where (A, a) is the adjoint of the state at the chunk's end: every later
+// row s contributes g_s q_s^T (dz_s q_s) with true weight
+// exp(sum of log f from the chunk end to s) exp(-m_s), and w_j is key j's
+// weight to the chunk end. The forget-gate sum stops at a zero forget gate
+// (no weight crosses it), whose own gradient is 0.
+//
+// Kernels (after the forward's gate kernel and state pass, which give the
+// gate prefix data and every chunk's start state):
+//   bwd_dq_kernel     per (head, 64-row tile): the row denominators from
+//                     Q K^T over the chunk's key tiles, then g, dz, do~, dq
+//                     (G V^T and (P o (G V^T + dz)) K on MFMA, plus the
+//                     carried-state term G C~); writes g for the next two
+//   bwd_state_kernel  per (head, 64 x 64 tile of A): walks the chunks from
+//                     the last to the first, storing each chunk's end adjoint
+//                     and accumulating G^T diag(w) Q on MFMA
+//   bwd_dkv_kernel    per (head, 64-key tile): the end adjoint's term, then
+//                     the chunk's later query tiles: S = Q K^T, G V^T, and
+//                     dk += (P o (G V^T + dz))^T Q, dv += (P o S)^T G
+//   bwd_gate_kernel   per head: the forget-gate suffix sums and the
+//                     initial-state stabiliser gradient
+//
+// Operand fragments: every product is a sequence of 16x16x32 steps in which
+// lane (i, g) of the wave supplies A[i][8g .. 8g+7] and B[i][8g .. 8g+7]
+// (D = A B^T, D[4g + r][i] in register r). For bfloat16 that is one
+// v_mfma_f32_16x16x32_bf16; for float32 it is eight v_mfma_f32_16x16x4_f32,
+// the s-th taking element 8g + s of each lane, which covers the same 32
+// contraction indices in another order.
+
+#include "mlstm_device.h"
+
+namespace mlstm_impl {
+
+namespace {
+
+constexpr int kBT = 512;   // threads of the dq and dk/dv kernels: eight waves
+constexpr float kL2e = 1.4426950408889634f;
+
+typedef __attribute__((ext_vector_type(8))) float f32x8;
+typedef __attribute__((address_space(3))) bf16x4 lds_b4;
+
+template <typename T> struct Vec8;
+template <> struct Vec8<__bf16> { using type = bf16x8; };
+template <> struct Vec8<float> { using type = f32x8; };
+template <typename T> using vec8 = typename Vec8<T>::type;
+
+template <typename T> constexpr int lds_pad() { return sizeof(T) == 2 ? 8 : 4; }
+
+__device__ __forceinline__ bf16x8 load8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ f32x8 load8(const float* p) {
+  const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 y = *reinterpret_cast<const f32x4*>(p + 4);
+  return f32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+}
+__device__ __forceinline__ void store8(__bf16* p, bf16x8 x) { *reinterpret_cast<bf16x8*>(p) = x; }
+__device__ __forceinline__ void store8(float* p, f32x8 x) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
+__device__ __forceinline__ void store4(__bf16* p, f32x4 x) {
+  bf16x4 o;
+  o[0] = (__bf16)x[0]; o[1] = (__bf16)x[1]; o[2] = (__bf16)x[2]; o[3] = (__bf16)x[3];
+  *reinterpret_cast<bf16x4*>(p) = o;
+}
+__device__ __forceinline__ void store4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
+
+// x = hi + lo with hi the bfloat16 rounding of x and lo that of the rest;
+// for float32 operands hi = x and lo = 0.
+__device__ __forceinline__ void split8(const f32x8& x, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hi[e] = (__bf16)x[e];
+    lo[e] = (__bf16)(x[e] - (float)hi[e]);
+  }
+}
+__device__ __forceinline__ void split8(const f32x8& x, f32x8& hi, f32x8& lo) {
+  hi = x;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) lo[e] = 0.f;
+}
+
+template <typename T> __device__ __forceinline__ vec8<T> zero_v8() {
+  vec8<T> z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (T)0.f;
+  return z;
+}
+
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) { return mma(a, b, c); }
+__device__ __forceinline__ f32x4 mma32(f32x8 a, f32x8 b, f32x4 c) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = mma(a[s], b[s], c);
+  return c;
+}
+
+// lane (i, g): row r0 + i, elements k0 + 8g .. k0 + 8g + 7 of a row-major
+// array (LDS or global) with row pitch P
+template <typename T>
+__device__ __forceinline__ vec8<T> frag_rows(const T* X, int64_t P, int r0, int k0) {
+  const int lane = threadIdx.x & 63;
+  return load8(X + (int64_t)(r0 + (lane & 15)) * P + k0 + 8 * (lane >> 4));
+}
+// the same from global memory, zero for rows at or beyond `nrows`
+template <typename T>
+__device__ __forceinline__ vec8<T> frag_rows_lim(const T* X, int64_t P, int r0, int k0, int nrows) {
+  const int lane = threadIdx.x & 63;
+  const int r = r0 + (lane & 15);
+  return r < nrows ? load8(X + (int64_t)r * P + k0 + 8 * (lane >> 4)) : zero_v8<T>();
+}
+
+// lane (i, g): column n0 + i of rows k0 + 8g .. k0 + 8g + 7 of a row-major
+// LDS tile with row pitch P. bfloat16: two ds_read_b64_tr_b16, which hand
+// lane i of each 16-lane group element (i mod 4) of the 8-byte rows that
+// lanes 4e + i/4 address: lane l addressing row k0 + 8g + l/4, column
+// n0 + 4 (l mod 4) (and 4 rows further for the second) gives lane i column
+// n0 + i of the group's rows.
+__device__ __forceinline__ bf16x8 frag_cols(const __bf16* X, int P, int k0, int n0) {
+  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+  const __bf16* p = X + (k0 + 8 * g + (i >> 2)) * P + n0 + 4 * (i & 3);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)p);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)(p + 4 * P));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x8 frag_cols(const float* X, int P, int k0, int n0) {
+  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+  f32x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = X[(k0 + 8 * g + e) * P + n0 + i];
+  return r;
+}
+
+// Copy rows [0, 64) x columns [0, NC) of a row-major global array (row pitch
+// gp) into LDS (row pitch SP); rows at or beyond `nrows` become zero.
+template <int NT, typename T, int NC, int SP>
+__device__ __forceinline__ void stage(T* __restrict__ s, const T* __restrict__ g, int64_t gp, int nrows) {
+  constexpr int EV = 16 / sizeof(T);
+  constexpr int VPR = NC / EV;
+  for (int it = threadIdx.x; it < kTile * VPR; it += NT) {
+    const int row = it / VPR, cv = it % VPR;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (row < nrows) x = *reinterpret_cast<const f32x4*>(g + (int64_t)row * gp + cv * EV);
+    *reinterpret_cast<f32x4*>(s + row * SP + cv * EV) = x;
+  }
+}
+// Copy an LDS tile (row pitch SP) to rows [0, nrows) of a global array.
+template <int NT, typename T, int NC, int SP>
+__device__ __forceinline__ void unstage(T* __restrict__ g, int64_t gp, const T* __restrict__ s, int nrows) {
+  constexpr int EV = 16 / sizeof(T);
+  constexpr int VPR = NC / EV;
+  for (int it = threadIdx.x; it < kTile * VPR; it += NT) {
+    const int row = it / VPR, cv = it % VPR;
+    if (row < nrows)
+      *reinterpret_cast<f32x4*>(g + (int64_t)row * gp + cv * EV) =
+          *reinterpret_cast<const f32x4*>(s + row * SP + cv * EV);
+  }
+}
+
+struct BwdArgs {
+  const void *q, *k, *v, *o, *h, *dh;    // [BH][T][d] of the input dtype
+  const float *f_pre;
+  void *dq, *dk, *dv, *dout;             // [BH][T][d]
+  float *di, *df;                        // [BH][T]
+  GateBuffers gb;
+  const float* Cs;                       // forward chunk-start states [BH][Nc][V][K]
+  const float* ns;                       // [BH][Nc][K]
+  const double* ms;                      // [BH][Nc]
+  void* G;                               // g per token [BH][T][V]
+  float* dz;                             // dz per token [BH][T]
+  float* qdq;                            // q . dq per token [BH][T]
+  float* Es;                             // end adjoint of every chunk [BH][Nc][V][K], float32
+  float* es;                             // [BH][Nc][K]
+  double* Ms;                            // its log scale [BH][Nc] (-inf: zero)
+  const float *C0, *n0, *m0;             // initial state, or null
+  float *dC0, *dn0, *dm0;                // its gradient, or null
+  int zero_first;                        // no initial state: chunk 0 starts from zero
+  int64_t T, Nc, V, K, BH;
+  int L;
+};
+
+// Row stabiliser r_t of the forward (see the file comment) for token t of
+// chunk c; `carry` tells whether the carried state reaches row t.
+__device__ __forceinline__ double row_stab(const BwdArgs& a, int64_t bh, int64_t t, bool has_state,
+                                           double m_prev, bool* carry) {
+  const int rs = a.gb.rs[bh * a.T + t];
+  const bool cr = has_state && rs < 0;
+  double r = fmax(cr ? m_prev : -INFINITY, a.gb.mp[bh * a.T + t]);
+  if (r == -INFINITY) r = 0.0;
+  if (carry) *carry = cr;
+  return r;
+}
+
+// ------------------------------------------------------------------ dq kernel
+
+template <typename TI, int K, int V>
+struct DqLds {
+  static constexpr int PAD = lds_pad<TI>();
+  static constexpr int QP = K + PAD, GP = V + PAD, AP = kTile + PAD;
+  static constexpr int oQ = 0;
+  static constexpr int oK = oQ + kTile * QP * (int)sizeof(TI);
+  static constexpr int oG = oK + kTile * QP * (int)sizeof(TI);
+  static constexpr int oA = oG + kTile * GP * (int)sizeof(TI);
+  static constexpr int oF = oA + kTile * AP * (int)sizeof(TI);
+  // float arrays: u2, r2, sc, den, sg, dz [64] each; zp, qd [4][64]; n [K]; then int rs [64]
+  static constexpr int nF = 6 * kTile + 8 * kTile + K;
+  static constexpr int oI = oF + nF * 4;
+  static constexpr int bytes = oI + kTile * 4;
+  static_assert(bytes <= 160 * 1024, "fits the LDS of a CU");
+};
+
+template <typename TI, int K, int V>
+__global__ __launch_bounds__(kBT) void bwd_dq_kernel(BwdArgs a) {
+  using L = DqLds<TI, K, V>;
+  constexpr int QP = L::QP, GP = L::GP, AP = L::AP;
+  constexpr int CT = K / 64;   // 16-column output tiles per wave
+  __shared__ __attribute__((aligned(16))) char smem[L::bytes];
+  TI* sQ = reinterpret_cast<TI*>(smem + L::oQ);
+  TI* sK = reinterpret_cast<TI*>(smem + L::oK);
+  TI* sG = reinterpret_cast<TI*>(smem + L::oG);
+  TI* sA = reinterpret_cast<TI*>(smem + L::oA);
+  float* f = reinterpret_cast<float*>(smem + L::oF);
+  float *s_u2 = f, *s_r2 = f + 64, *s_sc = f + 128, *s_den = f + 192, *s_sg = f + 256, *s_dz = f + 320;
+  float *s_zp = f + 384, *s_qd = f + 640, *s_n = f + 896;
+  int* s_rs = reinterpret_cast<int*>(smem + L::oI);
+
+  const int64_t T = a.T, BH = a.BH;
+  const int64_t bh = blockIdx.x % BH;
+  const int64_t row0 = (int64_t)(blockIdx.x / BH) * kTile;
+  const int64_t c = row0 / a.L;
+  const int64_t t0 = c * a.L;
+  const int st = (int)((row0 - t0) / kTile);
+  const int nrows = (int)min((int64_t)kTile, T - row0);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int jw = w & 3, zs = 2 * (w >> 2);   // score tiles: keys 16 jw.., query groups zs, zs + 1
+  const int rh = w >> 2, cw = w & 3;         // output: rows 32 rh.., columns (K / 4) cw..
+
+  const bool has_state = c > 0 || !a.zero_first;
+  const double m_prev = has_state ? a.ms[bh * a.Nc + c] : 0.0;
+  const double ref = row_stab(a, bh, row0, has_state, m_prev, nullptr);
+
+  const TI* qg = static_cast<const TI*>(a.q) + bh * T * K;
+  const TI* kg = static_cast<const TI*>(a.k) + bh * T * K;
+  const TI* vg = static_cast<const TI*>(a.v) + bh * T * V;
+
+  // ---------------- row data, Q tile, carried normaliser
+  if (tid < kTile) {
+    float r2 = 0.f, sc = 0.f, fl = 1.f;
+    int rs = 0;
+    if (tid < nrows) {
+      const int64_t t = row0 + tid;
+      bool carry;
+      const double r = row_stab(a, bh, t, has_state, m_prev, &carry);
+      r2 = (float)((r - ref) * (double)kL2e);
+      sc = carry ? expf((float)(m_prev - r)) : 0.f;
+      fl = expf((float)(-(a.gb.b[bh * T + t] + r)));
+      rs = a.gb.rs[bh * T + t];
+    }
+    s_r2[tid] = r2;
+    s_sc[tid] = sc;
+    s_den[tid] = fl;   // the floor for now
+    s_rs[tid] = rs;
+  }
+  for (int d = tid; d < K; d += kBT) s_n[d] = has_state ? a.ns[(bh * a.Nc + c) * K + d] : 0.f;
+  stage<kBT, TI, K, QP>(sQ, qg + row0 * K, K, nrows);
+
+  // ---------------- z_t = sum_j P_tj (q_t . k_j) + sc_t (q_t . n~)
+  float zrow[2] = {0.f, 0.f};
+  for (int jb = 0; jb <= st; ++jb) {
+    const int64_t key0 = t0 + (int64_t)jb * kTile;
+    __syncthreads();   // s_u2 free; sQ, row data published
+    if (tid < kTile)
+      s_u2[tid] = key0 + tid < T ? (float)((a.gb.u[bh * T + key0 + tid] - ref) * (double)kL2e) : -INFINITY;
+    f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    const int kvalid = (int)min((int64_t)kTile, T - key0);
+#pragma unroll
+    for (int ks = 0; ks < K / 32; ++ks) {
+      const vec8<TI> A = frag_rows_lim(kg + key0 * K, K, 16 * jw, 32 * ks, kvalid);
+#pragma unroll
+      for (int zz = 0; zz < 2; ++zz) sacc[zz] = mma32(A, frag_rows(sQ, QP, 16 * (zs + zz), 32 * ks), sacc[zz]);
+    }
+    __syncthreads();   // s_u2 written
+    // lane holds S^T[j = 16 jw + 4 g + r][t = 16 (zs + zz) + i]
+#pragma unroll
+    for (int zz = 0; zz < 2; ++zz) {
+      const int tl = 16 * (zs + zz) + i;
+      const int tq = st * kTile + tl;
+      const float r2 = s_r2[tl];
+      const int rs = s_rs[tl];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * jw + 4 * g + r;
+        const int jk = jb * kTile + j;
+        const bool keep = tl < nrows && jk <= tq && jk >= rs;
+        zrow[zz] += keep ? sacc[zz][r] * exp2f(s_u2[j] - r2) : 0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int zz = 0; zz < 2; ++zz) {
+    zrow[zz] += __shfl_xor(zrow[zz], 16, 64);
+    zrow[zz] += __shfl_xor(zrow[zz], 32, 64);
+    if (g == 0) s_zp[jw * 64 + 16 * (zs + zz) + i] = zrow[zz];
+  }
+  {   // q_t . n~, eight threads per row
+    const int row = tid >> 3, part = tid & 7;
+    float d = 0.f;
+    for (int kk = part * (K / 8); kk < (part + 1) * (K / 8); ++kk) d += to_f32(sQ[row * QP + kk]) * s_n[kk];
+    d += __shfl_xor(d, 1, 64);
+    d += __shfl_xor(d, 2, 64);
+    d += __shfl_xor(d, 4, 64);
+    if (part == 0) s_qd[row] = d;
+  }
+  __syncthreads();
+  if (tid < kTile) {
+    const float z = s_zp[tid] + s_zp[64 + tid] + s_zp[128 + tid] + s_zp[192 + tid] + s_sc[tid] * s_qd[tid];
+    const float fl = s_den[tid];
+    s_den[tid] = fmaxf(fmaxf(fabsf(z), fl), FLT_MIN);
+    s_sg[tid] = fabsf(z) > fl ? (z > 0.f ? 1.f : -1.f) : 0.f;
+  }
+  __syncthreads();
+
+  // ---------------- g = dh sigmoid(o~) / den, do~ = dh h (1 - sigmoid(o~)), dz; eight rows per wave
+  {
+    const TI* dhg = static_cast<const TI*>(a.dh) + (bh * T + row0) * V;
+    const TI* hg = static_cast<const TI*>(a.h) + (bh * T + row0) * V;
+    const TI* og = static_cast<const TI*>(a.o) + (bh * T + row0) * V;
+    TI* Gg = static_cast<TI*>(a.G) + (bh * T + row0) * V;
+    TI* dog = static_cast<TI*>(a.dout) + (bh * T + row0) * V;
+    for (int rr = 0; rr < 8; ++rr) {
+      const int row = 8 * w + rr;
+      const bool valid = row < nrows;
+      const float inv = 1.f / s_den[row];
+      float dot = 0.f;
+      for (int cv = lane; cv < V / 8; cv += 64) {
+        vec8<TI> gv = zero_v8<TI>();
+        if (valid) {
+          const int64_t off = (int64_t)row * V + 8 * cv;
+          const vec8<TI> dh8 = load8(dhg + off), h8 = load8(hg + off), o8 = load8(og + off);
+          vec8<TI> dov;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float dh = to_f32(dh8[e]), hv = to_f32(h8[e]);
+            const float sg = sigmoid(to_f32(o8[e]));
+            dot += dh * hv;
+            gv[e] = from_f32<TI>(dh * sg * inv);
+            dov[e] = from_f32<TI>(dh * hv * (1.f - sg));
+          }
+          store8(Gg + off, gv);
+          store8(dog + off, dov);
+        }
+        store8(sG + row * GP + 8 * cv, gv);
+      }
+      dot = wave_sum(dot);
+      if (lane == 0) s_dz[row] = valid ? -s_sg[row] * dot * inv : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---------------- carried-state term: sc_t (G C~ + dz_t n~)
+  f32x4 acc[2][CT];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < CT; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (has_state) {
+    const float* Cst = a.Cs + (bh * a.Nc + c) * V * K;
+    for (int vb = 0; vb < V / 64; ++vb) {
+      if (vb > 0) __syncthreads();   // sK free
+      // 64 rows of the float32 state, rounded once to the operand type (the
+      // carried term of dq does not cancel the way the state's products
+      // with single keys can)
+      for (int it = tid; it < kTile * (K / 8); it += kBT) {
+        const int row = it / (K / 8), cv = it % (K / 8);
+        const f32x8 x8 = load8(Cst + (int64_t)(64 * vb + row) * K + 8 * cv);
+        vec8<TI> o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = from_f32<TI>(x8[e]);
+        store8(sK + row * QP + 8 * cv, o);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        vec8<TI> A[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) A[x] = frag_rows(sG, GP, 32 * rh + 16 * x, 64 * vb + 32 * ks);
+#pragma unroll
+        for (int y = 0; y < CT; ++y) {
+          const vec8<TI> B = frag_cols(sK, QP, 32 * ks, (K / 4) * cw + 16 * y);
+#pragma unroll
+          for (int x = 0; x < 2; ++x) acc[x][y] = mma32(A[x], B, acc[x][y]);
+        }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tl = 32 * rh + 16 * x + 4 * g + r;
+        const float sc = s_sc[tl], dzt = s_dz[tl];
+#pragma unroll
+        for (int y = 0; y < CT; ++y) acc[x][y][r] = sc * (acc[x][y][r] + dzt * s_n[(K / 4) * cw + 16 * y + i]);
+      }
+  }
+
+  // ---------------- intra-chunk key tiles: dq += (P o (G V^T + dz)) K
+  for (int jb = 0; jb <= st; ++jb) {
+    const int64_t key0 = t0 + (int64_t)jb * kTile;
+    const int kvalid = (int)min((int64_t)kTile, T - key0);
+    __syncthreads();   // sK, sA, s_u2 free
+    stage<kBT, TI, K, QP>(sK, kg + key0 * K, K, kvalid);
+    if (tid < kTile)
+      s_u2[tid] = tid < kvalid ? (float)((a.gb.u[bh * T + key0 + tid] - ref) * (double)kL2e) : -INFINITY;
+    f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int ks = 0; ks < V / 32; ++ks) {
+      const vec8<TI> A = frag_rows_lim(vg + key0 * V, V, 16 * jw, 32 * ks, kvalid);
+#pragma unroll
+      for (int zz = 0; zz < 2; ++zz) sacc[zz] = mma32(A, frag_rows(sG, GP, 16 * (zs + zz), 32 * ks), sacc[zz]);
+    }
+    __syncthreads();   // s_u2, sK written
+#pragma unroll
+    for (int zz = 0; zz < 2; ++zz) {
+      const int tl = 16 * (zs + zz) + i;
+      const int tq = st * kTile + tl;
+      const float r2 = s_r2[tl], dzt = s_dz[tl];
+      const int rs = s_rs[tl];
+      f32x4 pa;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * jw + 4 * g + r;
+        const int jk = jb * kTile + j;
+        const bool keep = tl < nrows && jk <= tq && jk >= rs;
+        pa[r] = keep ? exp2f(s_u2[j] - r2) * (sacc[zz][r] + dzt) : 0.f;
+      }
+      store4(sA + tl * AP + 16 * jw + 4 * g, pa);
+    }
+    __syncthreads();   // sA complete
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      vec8<TI> A[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) A[x] = frag_rows(sA, AP, 32 * rh + 16 * x, 32 * ks);
+#pragma unroll
+      for (int y = 0; y < CT; ++y) {
+        const vec8<TI> B = frag_cols(sK, QP, 32 * ks, (K / 4) * cw + 16 * y);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) acc[x][y] = mma32(A[x], B, acc[x][y]);
+      }
+    }
+  }
+
+  // ---------------- epilogue: q . dq per row, dq through LDS, dz and q . dq out
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tl = 32 * rh + 16 * x + 4 * g + r;
+      float p = 0.f;
+#pragma unroll
+      for (int y = 0; y < CT; ++y) p += acc[x][y][r] * to_f32(sQ[tl * QP + (K / 4) * cw + 16 * y + i]);
+      p += __shfl_xor(p, 1, 64);
+      p += __shfl_xor(p, 2, 64);
+      p += __shfl_xor(p, 4, 64);
+      p += __shfl_xor(p, 8, 64);
+      if (i == 0) s_qd[64 * cw + tl] = p;
+    }
+  __syncthreads();   // all MFMA reads of sK done
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < CT; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        sK[(32 * rh + 16 * x + 4 * g + r) * QP + (K / 4) * cw + 16 * y + i] = from_f32<TI>(acc[x][y][r]);
+  __syncthreads();
+  unstage<kBT, TI, K, QP>(static_cast<TI*>(a.dq) + (bh * T + row0) * K, K, sK, nrows);
+  if (tid < nrows) {
+    a.qdq[bh * T + row0 + tid] = s_qd[tid] + s_qd[64 + tid] + s_qd[128 + tid] + s_qd[192 + tid];
+    a.dz[bh * T + row0 + tid] = s_dz[tid];
+  }
+}
+
+// ------------------------------------------------------------------ reverse state pass
+
+template <typename TI, int K>
+struct RsLds {
+  static constexpr int PAD = lds_pad<TI>();
+  static constexpr int P = kTile + PAD;
+  static constexpr int oG = 0;                                   // g tile [64 tokens][64 v]
+  static constexpr int oQ = oG + kTile * P * (int)sizeof(TI);    // w q tile [64 tokens][64 d]
+  static constexpr int oF = oQ + kTile * P * (int)sizeof(TI);    // float: w [64], wdz [64], ep [4][64]
+  static constexpr int bytes = oF + 6 * kTile * 4;
+};
+
+// One workgroup per (head, 64 v x 64 d tile), four waves of 32 x 32. Chunk c
+// (last to first): store the carried end adjoint (A, M) in float32, then add
+// the chunk's tokens s before its first zero forget gate, w_s g_s q_s^T with
+// w_s = exp(r_first - r_s) <= 1 (log scale -r_first), and fold:
+// M' = max(-r_first, g_c + M) (the second only when the chunk has no zero
+// forget gate), A' = exp(-r_first - M') acc + exp(g_c + M - M') A. The
+// normaliser adjoint a (v-tile-0 workgroups) is the same sum with g_s
+// replaced by dz_s, on the vector ALU in float32. After chunk 0 the carried
+// adjoint belongs to the initial state: dC~0 = exp(m0 + M) A.
+template <typename TI, int K>
+__global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
+  using L = RsLds<TI, K>;
+  constexpr int P = L::P;
+  __shared__ __attribute__((aligned(16))) char smem[L::bytes];
+  TI* sG = reinterpret_cast<TI*>(smem + L::oG);
+  TI* sQ = reinterpret_cast<TI*>(smem + L::oQ);
+  float* s_w = reinterpret_cast<float*>(smem + L::oF);
+  float* s_wdz = s_w + 64;
+  float* s_ep = s_w + 128;
+
+  const int64_t T = a.T, BH = a.BH, V = a.V;
+  const int64_t bh = blockIdx.x % BH;
+  const int tile = (int)(blockIdx.x / BH);
+  constexpr int KT = K / 64;
+  const int kt = tile % KT, vt = tile / KT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int wk = w & 1, wv = w >> 1;
+  const bool e_tile = vt == 0;
+
+  const TI* qg = static_cast<const TI*>(a.q) + bh * T * K + 64 * kt;
+  const TI* Gg = static_cast<const TI*>(a.G) + bh * T * V + 64 * vt;
+  const bool want_init = a.dC0 != nullptr;
+  const int64_t c_last = want_init ? 0 : 1;
+
+  f32x4 acc[2][2], lacc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float e_acc = 0.f;   // threads < 64 of e-tiles: a[64 kt + tid]
+  double M = -INFINITY;
+
+  for (int64_t c = a.Nc - 1; c >= 0; --c) {
+    // store the carried end adjoint of chunk c
+    {
+      float* Es = a.Es + (bh * a.Nc + c) * V * K;
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+          const int64_t vv = 64 * vt + 32 * wv + 16 * x + 4 * g;
+          const int dd = 64 * kt + 32 * wk + 16 * y + i;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Es[(vv + r) * K + dd] = acc[x][y][r];
+        }
+      if (e_tile && tid < kTile) a.es[(bh * a.Nc + c) * K + 64 * kt + tid] = e_acc;
+      if (tile == 0 && tid == 0) a.Ms[bh * a.Nc + c] = M;
+    }
+    if (c < c_last) break;
+    const int64_t t0 = c * a.L;
+    const int Lc = (int)min((int64_t)a.L, T - t0);
+    const bool has_state = c > 0 || !a.zero_first;
+    const double m_prev = has_state ? a.ms[bh * a.Nc + c] : 0.0;
+    const double r_first = row_stab(a, bh, t0, has_state, m_prev, nullptr);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y) lacc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float le = 0.f;
+    for (int jb = 0; jb < Lc; jb += kTile) {
+      const int64_t tb = t0 + jb;
+      const int nv = min(kTile, Lc - jb);
+      __syncthreads();   // previous block's tiles and weights consumed
+      if (tid < kTile) {
+        float wt = 0.f, wdz = 0.f;
+        if (tid < nv && a.gb.rs[bh * T + tb + tid] < 0) {
+          const double r = row_stab(a, bh, tb + tid, has_state, m_prev, nullptr);
+          wt = expf((float)(r_first - r));
+          wdz = wt * a.dz[bh * T + tb + tid];
+        }
+        s_w[tid] = wt;
+        s_wdz[tid] = wdz;
+      }
+      __syncthreads();
+      // stage w g[tokens][64 v] and q[tokens][64 d]. The weight goes on g: a
+      // rounding of w_s g_s perturbs each term in proportion to itself, so
+      // the adjoint's products with later keys (which can cancel strongly)
+      // keep their accuracy; q stays exact.
+      for (int it = tid; it < kTile * 8; it += kThreads) {
+        const int row = it >> 3, cv = it & 7;
+        vec8<TI> gv = zero_v8<TI>(), qv = zero_v8<TI>();
+        if (row < nv) {
+          const vec8<TI> g8 = load8(Gg + (tb + row) * V + 8 * cv);
+          qv = load8(qg + (tb + row) * K + 8 * cv);
+          const float wt = s_w[row];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) gv[e] = from_f32<TI>(to_f32(g8[e]) * wt);
+        }
+        store8(sG + row * P + 8 * cv, gv);
+        store8(sQ + row * P + 8 * cv, qv);
+      }
+      if (e_tile) {   // normaliser adjoint: four threads per d, 16 tokens each
+        const int d = tid & 63, part = tid >> 6;
+        float s = 0.f;
+        for (int row = 16 * part; row < 16 * part + 16; ++row)
+          if (row < nv) s += s_wdz[row] * to_f32(qg[(tb + row) * K + d]);
+        s_ep[part * 64 + d] = s;
+      }
+      __syncthreads();
+      if (e_tile && tid < kTile) le += s_ep[tid] + s_ep[64 + tid] + s_ep[128 + tid] + s_ep[192 + tid];
+#pragma unroll
+      for (int kk = 0; kk < kTile; kk += 32) {
+        vec8<TI> A[2], B[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) A[x] = frag_cols(sG, P, kk, 32 * wv + 16 * x);
+#pragma unroll
+        for (int y = 0; y < 2; ++y) B[y] = frag_cols(sQ, P, kk, 32 * wk + 16 * y);
+#pragma unroll
+        for (int x = 0; x < 2; ++x)
+#pragma unroll
+          for (int y = 0; y < 2; ++y) lacc[x][y] = mma32(A[x], B[y], lacc[x][y]);
+      }
+    }
+    // fold the chunk into the carried adjoint
+    const bool open = a.gb.R[bh * a.Nc + c] < 0;
+    const double gc = a.gb.g[bh * a.Nc + c];
+    const double Mc = (open && M != -INFINITY) ? gc + M : -INFINITY;
+    const double Mloc = -r_first;
+    const double Mn = fmax(Mloc, Mc);
+    const float al = expf((float)(Mloc - Mn));
+    const float be = Mc == -INFINITY ? 0.f : expf((float)(Mc - Mn));
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y) acc[x][y] = al * lacc[x][y] + be * acc[x][y];
+    e_acc = al * le + be * e_acc;
+    M = Mn;
+  }
+  if (want_init) {
+    const double m0 = a.C0 ? (double)a.m0[bh] : 0.0;
+    const float sc = M == -INFINITY ? 0.f : expf((float)(m0 + M));
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {
+        const int64_t vv = 64 * vt + 32 * wv + 16 * x + 4 * g;
+        const int dd = 64 * kt + 32 * wk + 16 * y + i;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a.dC0[bh * V * K + (vv + r) * K + dd] = sc * acc[x][y][r];
+      }
+    if (e_tile && tid < kTile) a.dn0[bh * K + 64 * kt + tid] = sc * e_acc;
+  }
+}
+
+// ------------------------------------------------------------------ dk / dv kernel
+
+template <typename TI, int K, int V>
+struct DkvLds {
+  static constexpr int PAD = lds_pad<TI>();
+  static constexpr int QP = K + PAD, GP = V + PAD, AP = kTile + PAD;
+  static constexpr int oQ = 0;                                    // Q tile / K_j / end-adjoint block
+  static constexpr int oG = oQ + kTile * QP * (int)sizeof(TI);    // G tile / V_j
+  static constexpr int oA = oG + kTile * GP * (int)sizeof(TI);    // (P o (G V^T + dz))^T
+  static constexpr int oB = oA + kTile * AP * (int)sizeof(TI);    // (P o S)^T
+  static constexpr int oF = oB + kTile * AP * (int)sizeof(TI);
+  // float: u2, r2, dz, wj [64]; di [4][64]; e [K]; then int rs [64]
+  static constexpr int nF = 4 * kTile + 4 * kTile + K;
+  static constexpr int oI = oF + nF * 4;
+  static constexpr int bytes = oI + kTile * 4;
+  static_assert(bytes <= 160 * 1024, "fits the LDS of a CU");
+};
+
+template <typename TI, int K, int V>
+__global__ __launch_bounds__(kBT) void bwd_dkv_kernel(BwdArgs a) {
+  using L = DkvLds<TI, K, V>;
+  constexpr int QP = L::QP, GP = L::GP, AP = L::AP;
+  constexpr int CK = K / 64, CV = V / 64;   // 16-column output tiles per wave
+  __shared__ __attribute__((aligned(16))) char smem[L::bytes];
+  TI* sQ = reinterpret_cast<TI*>(smem + L::oQ);
+  TI* sG = reinterpret_cast<TI*>(smem + L::oG);
+  TI* sA = reinterpret_cast<TI*>(smem + L::oA);
+  TI* sB = reinterpret_cast<TI*>(smem + L::oB);
+  float* f = reinterpret_cast<float*>(smem + L::oF);
+  float *s_u2 = f, *s_r2 = f + 64, *s_dz = f + 128, *s_wj = f + 192, *s_di = f + 256, *s_e = f + 512;
+  int* s_rs = reinterpret_cast<int*>(smem + L::oI);
+
+  const int64_t T = a.T, BH = a.BH;
+  const int64_t bh = blockIdx.x % BH;
+  const int64_t key0 = (int64_t)(blockIdx.x / BH) * kTile;
+  const int64_t c = key0 / a.L;
+  const int64_t t0 = c * a.L;
+  const int jt = (int)((key0 - t0) / kTile);
+  const int nkeys = (int)min((int64_t)kTile, T - key0);
+  const int ntiles = (int)((min(T, t0 + a.L) - t0 + kTile - 1) / kTile);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int jw = w & 3, zs = 2 * (w >> 2);   // score tiles: keys 16 jw.., query groups zs, zs + 1
+  const int rh = w >> 2, cw = w & 3;         // outputs: key rows 32 rh.., columns (d / 4) cw..
+
+  const bool has_state = c > 0 || !a.zero_first;
+  const double m_prev = has_state ? a.ms[bh * a.Nc + c] : 0.0;
+  const double ref = row_stab(a, bh, key0, has_state, m_prev, nullptr);
+
+  const TI* qg = static_cast<const TI*>(a.q) + bh * T * K;
+  const TI* kg = static_cast<const TI*>(a.k) + bh * T * K;
+  const TI* vg = static_cast<const TI*>(a.v) + bh * T * V;
+  const TI* Gg = static_cast<const TI*>(a.G) + bh * T * V;
+
+  f32x4 ak[2][CK], av[2][CV];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+#pragma unroll
+    for (int y = 0; y < CK; ++y) ak[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int y = 0; y < CV; ++y) av[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---------------- key data; the end adjoint's term w_j (A^T v_j + a), w_j A k_j
+  const double Mc = a.Ms[bh * a.Nc + c];
+  const bool later = Mc != -INFINITY;
+  if (tid < kTile) {
+    float u2 = -INFINITY, wj = 0.f;
+    if (tid < nkeys) {
+      const double u = a.gb.u[bh * T + key0 + tid];
+      u2 = (float)((u - ref) * (double)kL2e);
+      const int Rc = a.gb.R[bh * a.Nc + c];
+      if (later && (int)(key0 - t0) + tid >= Rc) wj = expf((float)(u + a.gb.g[bh * a.Nc + c] + Mc));
+    }
+    s_u2[tid] = u2;
+    s_wj[tid] = wj;
+  }
+  if (later) {
+    // The end adjoint is float32. Its products with a key (k_j . A) can
+    // cancel strongly (rows whose g is large because their q . k is small),
+    // so it enters the MFMAs as two bfloat16 terms, hi + lo.
+    const float* Es = a.Es + (bh * a.Nc + c) * V * K;
+    for (int d = tid; d < K; d += kBT) s_e[d] = a.es[(bh * a.Nc + c) * K + d];
+    stage<kBT, TI, K, QP>(sQ, kg + key0 * K, K, nkeys);
+    stage<kBT, TI, V, GP>(sG, vg + key0 * V, V, nkeys);
+    __syncthreads();
+    // dv[j][v] += sum_d K_j[j][d] A[v][d]  (A rows straight from memory)
+#pragma unroll
+    for (int ks = 0; ks < K / 32; ++ks) {
+      vec8<TI> A[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) A[x] = frag_rows(sQ, QP, 32 * rh + 16 * x, 32 * ks);
+#pragma unroll
+      for (int y = 0; y < CV; ++y) {
+        const f32x8 e8 = frag_rows(Es, K, (V / 4) * cw + 16 * y, 32 * ks);
+        vec8<TI> hi, lo;
+        split8(e8, hi, lo);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          av[x][y] = mma32(A[x], hi, av[x][y]);
+          if constexpr (sizeof(TI) == 2) av[x][y] = mma32(A[x], lo, av[x][y]);
+        }
+      }
+    }
+    // dk[j][d] += sum_v V_j[j][v] A[v][d], A staged 32 rows at a time: hi in
+    // rows 0..31 of sQ, lo in rows 32..63
+    for (int vb = 0; vb < V / 32; ++vb) {
+      __syncthreads();   // sQ free (K_j or the previous block consumed)
+      for (int it = tid; it < 32 * (K / 8); it += kBT) {
+        const int row = it / (K / 8), cv = it % (K / 8);
+        vec8<TI> hi, lo;
+        split8(load8(Es + (int64_t)(32 * vb + row) * K + 8 * cv), hi, lo);
+        store8(sQ + row * QP + 8 * cv, hi);
+        store8(sQ + (32 + row) * QP + 8 * cv, lo);
+      }
+      __syncthreads();
+      vec8<TI> A[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) A[x] = frag_rows(sG, GP, 32 * rh + 16 * x, 32 * vb);
+#pragma unroll
+      for (int y = 0; y < CK; ++y) {
+        const vec8<TI> Bh = frag_cols(sQ, QP, 0, (K / 4) * cw + 16 * y);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) ak[x][y] = mma32(A[x], Bh, ak[x][y]);
+        if constexpr (sizeof(TI) == 2) {
+          const vec8<TI> Bl = frag_cols(sQ, QP, 32, (K / 4) * cw + 16 * y);
+#pragma unroll
+          for (int x = 0; x < 2; ++x) ak[x][y] = mma32(A[x], Bl, ak[x][y]);
+        }
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int jl = 32 * rh + 16 * x + 4 * g + r;
+        const float wj = s_wj[jl];
+#pragma unroll
+        for (int y = 0; y < CK; ++y) ak[x][y][r] = wj * (ak[x][y][r] + s_e[(K / 4) * cw + 16 * y + i]);
+#pragma unroll
+        for (int y = 0; y < CV; ++y) av[x][y][r] *= wj;
+      }
+  }
+
+  // ---------------- the chunk's query tiles at or after this key tile
+  // this wave's 16 keys as the B operand of S = Q K^T
+  vec8<TI> Kf[K / 32];
+#pragma unroll
+  for (int ks = 0; ks < K / 32; ++ks) Kf[ks] = frag_rows_lim(kg + key0 * K, K, 16 * jw, 32 * ks, nkeys);
+  for (int sb = jt; sb < ntiles; ++sb) {
+    const int64_t qrow0 = t0 + (int64_t)sb * kTile;
+    const int nq = (int)min((int64_t)kTile, T - qrow0);
+    __syncthreads();   // sQ, sG, sA, sB and the row data free
+    stage<kBT, TI, K, QP>(sQ, qg + qrow0 * K, K, nq);
+    stage<kBT, TI, V, GP>(sG, Gg + qrow0 * V, V, nq);
+    if (tid < kTile) {
+      float r2 = 0.f, dzt = 0.f;
+      int rs = kTile * 1024;   // no key passes jk >= rs for rows beyond T
+      if (tid < nq) {
+        const int64_t t = qrow0 + tid;
+        const double r = row_stab(a, bh, t, has_state, m_prev, nullptr);
+        r2 = (float)((r - ref) * (double)kL2e);
+        dzt = a.dz[bh * T + t];
+        rs = a.gb.rs[bh * T + t];
+      }
+      s_r2[tid] = r2;
+      s_dz[tid] = dzt;
+      s_rs[tid] = rs;
+    }
+    __syncthreads();
+    // S[t][j] and (G V^T)[t][j] for this wave's keys and query groups
+    f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x4 gacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int ks = 0; ks < K / 32; ++ks)
+#pragma unroll
+      for (int zz = 0; zz < 2; ++zz) sacc[zz] = mma32(frag_rows(sQ, QP, 16 * (zs + zz), 32 * ks), Kf[ks], sacc[zz]);
+    for (int ks = 0; ks < V / 32; ++ks) {
+      const vec8<TI> B = frag_rows_lim(vg + key0 * V, V, 16 * jw, 32 * ks, nkeys);
+#pragma unroll
+      for (int zz = 0; zz < 2; ++zz) gacc[zz] = mma32(frag_rows(sG, GP, 16 * (zs + zz), 32 * ks), B, gacc[zz]);
+    }
+    // lane holds [t = 16 (zs + zz) + 4 g + r][j = 16 jw + i]
+    {
+      const int j = 16 * jw + i;
+      const int jk = jt * kTile + j;
+      const float u2 = s_u2[j];
+#pragma unroll
+      for (int zz = 0; zz < 2; ++zz) {
+        f32x4 pa, pb;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tl = 16 * (zs + zz) + 4 * g + r;
+          const int tq = sb * kTile + tl;
+          const bool keep = tl < nq && j < nkeys && jk <= tq && jk >= s_rs[tl];
+          const float p = keep ? exp2f(u2 - s_r2[tl]) : 0.f;
+          pa[r] = p * (gacc[zz][r] + s_dz[tl]);
+          pb[r] = p * sacc[zz][r];
+        }
+        store4(sA + j * AP + 16 * (zs + zz) + 4 * g, pa);
+        store4(sB + j * AP + 16 * (zs + zz) + 4 * g, pb);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      vec8<TI> A[2], B2[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        A[x] = frag_rows(sA, AP, 32 * rh + 16 * x, 32 * ks);
+        B2[x] = frag_rows(sB, AP, 32 * rh + 16 * x, 32 * ks);
+      }
+#pragma unroll
+      for (int y = 0; y < CK; ++y) {
+        const vec8<TI> B = frag_cols(sQ, QP, 32 * ks, (K / 4) * cw + 16 * y);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) ak[x][y] = mma32(A[x], B, ak[x][y]);
+      }
+#pragma unroll
+      for (int y = 0; y < CV; ++y) {
+        const vec8<TI> B = frag_cols(sG, GP, 32 * ks, (V / 4) * cw + 16 * y);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) av[x][y] = mma32(B2[x], B, av[x][y]);
+      }
+    }
+  }
+
+  // ---------------- epilogue: di = k . dk, dk and dv through LDS
+  __syncthreads();   // all MFMA reads of sQ, sG done
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int jl = 32 * rh + 16 * x + 4 * g + r;
+      float p = 0.f;
+#pragma unroll
+      for (int y = 0; y < CK; ++y) {
+        const int d = (K / 4) * cw + 16 * y + i;
+        const float kv = jl < nkeys ? to_f32(kg[(key0 + jl) * K + d]) : 0.f;
+        p += ak[x][y][r] * kv;
+        sQ[jl * QP + d] = from_f32<TI>(ak[x][y][r]);
+      }
+#pragma unroll
+      for (int y = 0; y < CV; ++y) sG[jl * GP + (V / 4) * cw + 16 * y + i] = from_f32<TI>(av[x][y][r]);
+      p += __shfl_xor(p, 1, 64);
+      p += __shfl_xor(p, 2, 64);
+      p += __shfl_xor(p, 4, 64);
+      p += __shfl_xor(p, 8, 64);
+      if (i == 0) s_di[64 * cw + jl] = p;
+    }
+  __syncthreads();
+  unstage<kBT, TI, K, QP>(static_cast<TI*>(a.dk) + (bh * T + key0) * K, K, sQ, nkeys);
+  unstage<kBT, TI, V, GP>(static_cast<TI*>(a.dv) + (bh * T + key0) * V, V, sG, nkeys);
+  if (tid < nkeys) a.di[bh * T + key0 + tid] = s_di[tid] + s_di[64 + tid] + s_di[128 + tid] + s_di[192 + tid];
+}
+
+// ------------------------------------------------------------------ forget-gate gradient
+
+// One workgroup per head. dF_t = q_t . dq_t - k_t . dk_t; the gradient of
+// log f_l is the sum of dF_t from l up to the next zero forget gate
+// (exclusive), and 0 at a zero forget gate itself and, without an initial
+// state, at the first token; df~ = dlog f sigmoid(-f~).
+// Each thread takes a contiguous run of tokens; thread 0 chains the runs
+// from the right. Float64 sums. Also dm0 = <dC~0, C~0> + dn~0 . n~0.
+__global__ __launch_bounds__(kThreads) void bwd_gate_kernel(BwdArgs a) {
+  __shared__ double s_loc[kThreads];
+  __shared__ int s_open[kThreads];
+  __shared__ double s_carry[kThreads];
+  __shared__ double s_red[kThreads / 64];
+  const int64_t bh = blockIdx.x;
+  const int64_t T = a.T;
+  const int tid = threadIdx.x;
+  const int64_t E = (T + kThreads - 1) / kThreads;
+  const int64_t lo = min((int64_t)tid * E, T), hi = min(lo + E, T);
+  const float* fp = a.f_pre + bh * T;
+  const float* qd = a.qdq + bh * T;
+  const float* di = a.di + bh * T;
+  // this run's sum from lo up to its first zero forget gate after lo, with no carry
+  double run = 0.0;
+  int open = 1;
+  for (int64_t l = hi - 1; l >= lo; --l) {
+    const bool reset = fp[l] == -INFINITY;
+    run += (double)qd[l] - (double)di[l];
+    if (reset) {
+      if (l > lo) open = 0;
+      run = (l == lo) ? run : 0.0;
+    }
+  }
+  s_loc[tid] = run;
+  s_open[tid] = open;
+  __syncthreads();
+  if (tid == 0) {
+    double carry = 0.0;   // flow into the run's last token from the right
+    for (int p = kThreads - 1; p >= 0; --p) {
+      const int64_t plo = min((int64_t)p * E, T), phi = min(plo + E, T);
+      s_carry[p] = carry;
+      if (plo < phi) {
+        const double sa = s_loc[p] + (s_open[p] ? carry : 0.0);
+        carry = (fp[plo] == -INFINITY) ? 0.0 : sa;
+      }
+    }
+  }
+  __syncthreads();
+  run = s_carry[tid];
+  for (int64_t l = hi - 1; l >= lo; --l) {
+    const double val = (double)qd[l] - (double)di[l] + run;
+    // a zero forget gate passes no gradient; neither does the first token's
+    // without an initial state (it only scales the zero state), where the sum
+    // is zero up to rounding
+    if (fp[l] == -INFINITY || (l == 0 && a.zero_first)) {
+      a.df[bh * T + l] = 0.f;
+      run = 0.0;
+    } else {
+      a.df[bh * T + l] = (float)(val * (double)sigmoid(-fp[l]));
+      run = val;
+    }
+  }
+  if (a.dm0) {
+    double s = 0.0;
+    if (a.C0) {
+      const int64_t VK = a.V * a.K;
+      for (int64_t x = tid; x < VK; x += kThreads) s += (double)a.dC0[bh * VK + x] * (double)a.C0[bh * VK + x];
+      for (int64_t x = tid; x < a.K; x += kThreads) s += (double)a.dn0[bh * a.K + x] * (double)a.n0[bh * a.K + x];
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
+    if ((tid & 63) == 0) s_red[tid >> 6] = s;
+    __syncthreads();
+    if (tid == 0) a.dm0[bh] = (float)(s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+  }
+}
+
+// T = 0: the loss does not depend on the initial state.
+__global__ void bwd_zero_init_kernel(float* dC0, float* dn0, float* dm0, int64_t nC, int64_t nn, int64_t nm) {
+  const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (x < nC) dC0[x] = 0.f;
+  if (x < nn) dn0[x] = 0.f;
+  if (x < nm) dm0[x] = 0.f;
+}
+
+template <typename TI, int K, int V>
+hipError_t run_bwd(const BwdLaunch& b, const BwdArgs& a, hipStream_t s) {
+  const int64_t nqt = (b.T + kTile - 1) / kTile;
+  mark_before(b.marks, B_DQ, s);
+  hipLaunchKernelGGL((bwd_dq_kernel<TI, K, V>), dim3((unsigned)(b.BH * nqt)), dim3(kBT), 0, s, a);
+  mark_after(b.marks, B_DQ, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  mark_before(b.marks, B_STATE, s);
+  hipLaunchKernelGGL((bwd_state_kernel<TI, K>), dim3((unsigned)(b.BH * (K / 64) * (V / 64))), dim3(kThreads), 0,
+                     s, a);
+  mark_after(b.marks, B_STATE, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  mark_before(b.marks, B_DKV, s);
+  hipLaunchKernelGGL((bwd_dkv_kernel<TI, K, V>), dim3((unsigned)(b.BH * nqt)), dim3(kBT), 0, s, a);
+  mark_after(b.marks, B_DKV, s);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  mark_before(b.marks, B_GATE, s);
+  hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)b.BH), dim3(kThreads), 0, s, a);
+  mark_after(b.marks, B_GATE, s);
+  return hipGetLastError();
+}
+
+template <typename TI, int K>
+hipError_t run_bwd_v(const BwdLaunch& b, const BwdArgs& a, hipStream_t s) {
+  switch (b.V) {
+    case 64: return run_bwd<TI, K, 64>(b, a, s);
+    case 128: return run_bwd<TI, K, 128>(b, a, s);
+    case 256: return run_bwd<TI, K, 256>(b, a, s);
+  }
+  if constexpr (sizeof(TI) == 2) {
+    if (b.V == 512) return run_bwd<TI, K, 512>(b, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool bwd_supported(int bf16, int64_t K, int64_t V) {
+  if (bf16) return (K == 64 || K == 128 || K == 256) && (V == 64 || V == 128 || V == 256 || V == 512);
+  return (K == 64 || K == 128) && (V == 64 || V == 128 || V == 256);
+}
+
+hipError_t launch_bwd(const BwdLaunch& b, const GateBuffers& gb, const ChunkStates& cs, const BwdBuffers& bb,
+                      hipStream_t s) {
+  if (b.T == 0) {
+    if (!b.dC0) return hipSuccess;
+    const int64_t nC = b.BH * b.V * b.K;
+    hipLaunchKernelGGL(bwd_zero_init_kernel, dim3((unsigned)((nC + 255) / 256)), dim3(256), 0, s, b.dC0, b.dn0,
+                       b.dm0, nC, b.BH * b.K, b.BH);
+    return hipGetLastError();
+  }
+  BwdArgs a;
+  a.q = b.q; a.k = b.k; a.v = b.v; a.o = b.o; a.h = b.h; a.dh = b.dh;
+  a.f_pre = b.f_pre;
+  a.dq = b.dq; a.dk = b.dk; a.dv = b.dv; a.dout = b.dout;
+  a.di = b.di; a.df = b.df;
+  a.gb = gb;
+  a.Cs = static_cast<const float*>(cs.Cs); a.ns = cs.ns; a.ms = cs.ms;
+  a.G = bb.G; a.dz = bb.dz; a.qdq = bb.qdq;
+  a.Es = static_cast<float*>(bb.Es); a.es = bb.es; a.Ms = bb.Ms;
+  a.C0 = b.C0; a.n0 = b.n0; a.m0 = b.m0;
+  a.dC0 = b.dC0; a.dn0 = b.dn0; a.dm0 = b.dm0;
+  a.zero_first = b.C0 == nullptr;
+  a.T = b.T; a.Nc = b.Nc; a.V = b.V; a.K = b.K; a.BH = b.BH; a.L = b.L;
+  if (b.bf16) {
+    switch (b.K) {
+      case 64: return run_bwd_v<__bf16, 64>(b, a, s);
+      case 128: return run_bwd_v<__bf16, 128>(b, a, s);
+      case 256: return run_bwd_v<__bf16, 256>(b, a, s);
+    }
+  } else {
+    switch (b.K) {
+      case 64: return run_bwd_v<float, 64>(b, a, s);
+      case 128: return run_bwd_v<float, 128>(b, a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mlstm_impl

@@ -18,8 +18,9 @@
 //                      Holds its 128 x d_qk slice of C~ (float32) in MFMA
 //                      accumulators, split over its waves by halves of d_qk
 //                      and 32-column groups, and walks the chunk in 64-token
-//                      tiles. Per tile: Q K^T and Q C~^T on MFMA (partial sums
-//                      over each half of d_qk, exchanged through LDS), the
+//                      tiles. Per tile: Q K^T and Q C~^T on MFMA (C~ as bf16
+//                      hi + lo; partial sums over each half of d_qk,
+//                      exchanged through LDS), the
 //                      state update C~ <- a C~ + K^T diag(w) V on MFMA and the
 //                      same for n~ (a two-column MFMA tile carrying the weights
 //                      as bf16 hi + lo), decay mask and stabiliser in
@@ -107,6 +108,12 @@ __device__ __forceinline__ int fresh_tid() {
 __device__ __forceinline__ float sum_xor1(float x) {
   return x + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
 }
+// x summed over the four lanes of its quad (lanes l ^ 1, l ^ 2, l ^ 3), in
+// the same order on every lane of the quad
+__device__ __forceinline__ float sum_quad(float x) {
+  const float y = sum_xor1(x);
+  return y + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, y), 0x4E, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float sum_rows(float x) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
   const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
@@ -116,11 +123,18 @@ __device__ __forceinline__ float sum_rows(float x) {
   return __builtin_bit_cast(float, (unsigned)b[0]) + __builtin_bit_cast(float, (unsigned)b[1]);
 }
 
-// exp of a float64 argument in float32: the argument is scaled by log2(e) in
-// float64 and rounded once, then the hardware base-2 exponential (about one
-// ulp) takes it; results below the float32 normal range flush to zero.
+// exp of a float64 argument in float32, accurate to a few ulp whatever the
+// argument's size: the argument is scaled by log2(e) in float64 and split
+// into an integer n and a fraction f in [0, 1); the hardware base-2
+// exponential takes f and the result is scaled by 2^n. (Rounding the whole
+// argument to float32 would lose about 6e-8 of its size, which at the
+// deferred decays' arguments of up to about 100 is several ulp of the result
+// and, in the rows whose denominators cancel strongly, far more of h.)
+// Results below about 2^-200 are 0.
 __device__ __forceinline__ float exp_f64arg(double x) {
-  return __builtin_amdgcn_exp2f((float)(x * 1.4426950408889634));
+  const double y = x * 1.4426950408889634;
+  const double n = fmin(fmax(floor(y), -200.0), 200.0);
+  return ldexpf(__builtin_amdgcn_exp2f((float)(y - n)), (int)n);
 }
 
 __device__ __forceinline__ double readlane_f64(double x, int lane) {
@@ -162,6 +176,18 @@ __device__ __forceinline__ bf16x8 pack_bf16(const f32x4& a, const f32x4& b) {
   for (int e = 0; e < 4; ++e) {
     r[e] = (__bf16)a[e];
     r[4 + e] = (__bf16)b[e];
+  }
+  return r;
+}
+
+// The bfloat16 rounding of what pack_bf16(a, b) leaves out: pack_bf16(a, b)
+// + pack_bf16_rest(a, b, pack_bf16(a, b)) carries about 16 bits of a and b.
+__device__ __forceinline__ bf16x8 pack_bf16_rest(const f32x4& a, const f32x4& b, const bf16x8& hi) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (__bf16)(a[e] - (float)hi[e]);
+    r[4 + e] = (__bf16)(b[e] - (float)hi[4 + e]);
   }
   return r;
 }
@@ -257,17 +283,17 @@ struct OutLds {
   // sQ, sK and sV are arrays of their own; the rest shares one array at these offsets
   static constexpr int oP = 0;
   // double-buffered tile data, [2] of:
-  static constexpr int nbBytes = 3 * K * 2;          // bf16 [3][K]: n~ hi, lo, zero
+  static constexpr int nbBytes = K * 4;              // float [K]: n~ at the tile's start
   static constexpr int wBytes = kTile * 4;           // float [64] key weights
-  static constexpr int wbBytes = 3 * kTile * 2;      // bf16 [3][64]: weights hi, lo, zero
+  static constexpr int wbBytes = 4 * kTile * 2;      // bf16 [4][64]: weights hi, lo, lo2, zero
   static constexpr int rowBytes = 5 * kTile * 4;     // r2, sc, fl, u2 (float), rs (int), [64] each
   static constexpr int infoBytes = 16;               // tile info: rescale flag (int), factor (float)
   static constexpr int bufBytes = nbBytes + wBytes + wbBytes + rowBytes + infoBytes;
   static constexpr int oBuf = oP + kTile * PP * 2;
   static constexpr int oDnm = oBuf + 2 * bufBytes;   // float [64] denominator max(|n~^T q|, floor) of each row
   static constexpr int oDen = oDnm + kTile * 4;      // float [4][64] row sums of P per key group
-  static constexpr int oDn = oDen + 4 * kTile * 4;   // float [8][64] q . n~ partials per wave
-  static constexpr int oX = oDn + kOutWaves * kTile * 4;     // f32x4 [8 waves][kXchg][64 lanes]
+  static constexpr int oDn = oDen + 4 * kTile * 4;   // float [64] q . n~ of each row
+  static constexpr int oX = oDn + kTile * 4;                 // f32x4 [8 waves][kXchg][64 lanes]
   static constexpr int oFin = oX + kOutWaves * kXchg * 64 * 16;   // double [2]: final m, logD
   static constexpr int restBytes = oFin + 16;
   static_assert(qBytes + kBytes + vBytes + restBytes <= 160 * 1024, "fits the LDS of a CU");
@@ -286,9 +312,12 @@ struct OutLds {
 // 32 kh .. + 31. Afterwards wave (kh, cg) holds H^T for its 32 columns and its
 // 32 rows, and S^T for keys [16 cg, +16) and its rows (register group z is
 // rows 16 zg(z) .. + 15, zg(z) = (z + 2 kh) & 3: groups 0 and 1 are the
-// wave's own rows). The normaliser n~ is carried as two MFMA columns (lane
-// i = 0: the sum weighted by the bf16 high parts of the key weights, i = 1: by
-// the low parts) in Nacc, for KXN 16-row tiles of the wave's half of d_qk.
+// wave's own rows). The normaliser n~ is carried as three MFMA columns in
+// Nacc, for KXN 16-row tiles of the wave's half of d_qk (lane i = 0: the sum
+// weighted by the bf16 high parts of the key weights, i = 1 and 2: by the two
+// further bf16 terms of the weights, i = 3: zero; summed over the quad). Rows
+// whose denominators cancel strongly need n~ to float32 accuracy, which two
+// bf16 terms of the weights do not give.
 //
 // The tiles' decays are not applied to the accumulators one by one: the
 // registers hold X with C~ = exp(logD) X, n~ = exp(logD) Xn, new keys enter
@@ -316,7 +345,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
   double* s_fin = reinterpret_cast<double*>(smem + L::oFin);
   // views of one half of the double-buffered tile data
   struct TileBuf {
-    __bf16* nb;
+    float* nf;
     float* w;
     __bf16* wb;
     float *r2, *sc, *fl, *u2;
@@ -326,7 +355,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
   auto tile_buf = [&](int b) {
     char* base = smem + L::oBuf + b * L::bufBytes;
     TileBuf t;
-    t.nb = reinterpret_cast<__bf16*>(base);
+    t.nf = reinterpret_cast<float*>(base);
     t.w = reinterpret_cast<float*>(base + L::nbBytes);
     t.wb = reinterpret_cast<__bf16*>(base + L::nbBytes + L::wBytes);
     float* row = reinterpret_cast<float*>(base + L::nbBytes + L::wBytes + L::wbBytes);
@@ -392,11 +421,10 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
   for (int x = 0; x < KXN; ++x)
     Nacc[x] = (ninit && i == 0 && n_live(x)) ? *reinterpret_cast<const f32x4*>(ninit + state_k0(kxg(nx(x)), g))
                                             : f32x4{0.f, 0.f, 0.f, 0.f};
-  // zero rows of the two-column normaliser operands, both halves
+  // zero rows of the two-column weight operands, both halves
   for (int b = 0; b < 2; ++b) {
     const TileBuf tb = tile_buf(b);
-    if (tid < kTile) tb.wb[2 * kTile + tid] = (__bf16)0.f;
-    for (int k = tid; k < K; k += 64 * NW) tb.nb[2 * K + k] = (__bf16)0.f;
+    if (tid < kTile) tb.wb[3 * kTile + tid] = (__bf16)0.f;
   }
 
   // ---------------- copies of the next tile. Rows past the sequence end are
@@ -495,29 +523,21 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
     t_R = a.gb.R[bh * Nt + tau];
   };
 
-  // n~ of the next tile as bf16 hi + lo in the fragment order of sQ (every
-  // wave its own tiles) into half b of the tile data. The byte offset is kept
-  // whole (empty asm statement), so that each store is one step from the
-  // array and the compiler can tell it from the copies in flight.
+  // n~ of the next tile in float32 (every wave its own tiles) into half b of
+  // the tile data. The byte offset is kept whole (empty asm statement), so
+  // that each store is one step from the array and the compiler can tell it
+  // from the copies in flight.
   auto put_n = [&](int b) {
     const Lanes ln = fresh_lanes();
 #pragma unroll
     for (int x = 0; x < KXN; ++x) {
       if (n_live(x)) {
-        bf16x4 hi4, lo4;
+        f32x4 n4;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float nr = sum_xor1(Nacc[x][r]);
-          const __bf16 hi = (__bf16)nr;
-          hi4[r] = hi;
-          lo4[r] = (__bf16)(nr - (float)hi);
-        }
-        int off = L::oBuf + b * L::bufBytes + 2 * state_k0(kxg(nx(x)), ln.g);
+        for (int r = 0; r < 4; ++r) n4[r] = sum_quad(Nacc[x][r]);
+        int off = L::oBuf + b * L::bufBytes + 4 * state_k0(kxg(nx(x)), ln.g);
         asm("" : "+v"(off));
-        if (ln.i == 0) {
-          *reinterpret_cast<bf16x4*>(smem + off) = hi4;
-          *reinterpret_cast<bf16x4*>(smem + off + 2 * K) = lo4;
-        }
+        if (ln.i == 0) *reinterpret_cast<f32x4*>(smem + off) = n4;
       }
     }
   };
@@ -538,14 +558,22 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
     if (w == 0) {
       const float wj = (j >= t_R && j < Lc && t_U != -INFINITY) ? exp_f64arg(r_u - Rm - logD_next) : 0.f;
       tb.w[j] = wj;
+      // the weights of the normaliser's MFMA columns: wj = hi + lo + lo2 to
+      // about 24 bits (rows whose denominators cancel strongly need n~ to
+      // float32 accuracy)
       const __bf16 whi = (__bf16)wj;
+      const float wr = wj - (float)whi;
+      const __bf16 wlo = (__bf16)wr;
       tb.wb[j] = whi;
       int jl = kTile + j;   // kept whole: one step from the array (see put_n)
       asm("" : "+v"(jl));
-      tb.wb[jl] = (__bf16)(wj - (float)whi);
+      tb.wb[jl] = wlo;
+      int jl2 = 2 * kTile + j;
+      asm("" : "+v"(jl2));
+      tb.wb[jl2] = (__bf16)(wr - (float)wlo);
       if (j == 0) {
         tb.info[0] = rescale ? 1 : 0;
-        tb.info[1] = __builtin_bit_cast(int, rescale ? expf((float)(logD + ld)) : 1.f);   // below e^-70
+        tb.info[1] = __builtin_bit_cast(int, rescale ? exp_f64arg(logD + ld) : 1.f);   // below e^-70
       }
     } else {
       const bool carry0 = state && __builtin_amdgcn_readlane(r_rs, 0) < 0;   // lane 0 holds the first token
@@ -662,11 +690,14 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
       const bf16x8 fk = *reinterpret_cast<const bf16x8*>(&sK[(16 * kg + l1.i) * KP + col]);
 #pragma unroll
       for (int z = 0; z < 4; ++z) sacc[z] = mma(fk, fa[z], sacc[z]);
+      // the carried state as two bf16 terms: rows whose q is nearly
+      // orthogonal to a dominant key make C~ q a strongly cancelling sum
 #pragma unroll
       for (int cv = 0; cv < 2; ++cv) {
         const bf16x8 Bc = pack_bf16(Ct[2 * s][cv], Ct[2 * s + 1][cv]);
+        const bf16x8 Bl = pack_bf16_rest(Ct[2 * s][cv], Ct[2 * s + 1][cv], Bc);
 #pragma unroll
-        for (int z = 0; z < 4; ++z) acc[z][cv] = mma(Bc, fa[z], acc[z][cv]);
+        for (int z = 0; z < 4; ++z) acc[z][cv] = mma(Bl, fa[z], mma(Bc, fa[z], acc[z][cv]));
       }
     });
     // the partner's rows (groups 2 and 3) to the exchange area
@@ -690,30 +721,30 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
 #pragma unroll
         for (int cv = 0; cv < 2; ++cv) Av[jb][cv] = frag_tr(sV, VP, 32 * jb, 32 * cg + 16 * cv, lv.lane);
     }
-    // ---------------- q . n~: the wave with cg < KSH takes the 32-deep step
-    // KSH kh + cg of d_qk for all rows (register group z: rows 16 zg(z) ..),
-    // the others contribute zeros
+    // ---------------- q . n~ in float32 on the vector ALU, eight threads per
+    // row. Rows where a dominant key is nearly orthogonal to q make the
+    // denominator a strongly cancelling sum, so n~ is not rounded here.
     {
-      const Lanes ln = fresh_lanes();
-      f32x4 dacc[4];
+      const int t8 = fresh_tid();
+      const int row = t8 >> 3, part = t8 & 7;
+      const __bf16* qr = sQ + row * QP + part * (K / 8);
+      const float* nr = tb.nf + part * (K / 8);
+      float d = 0.f;
 #pragma unroll
-      for (int z = 0; z < 4; ++z) dacc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (cg < KSH) {
-        const int col = KH * kh + 32 * cg + 8 * ln.g;
-        const bf16x8 Bn = *reinterpret_cast<const bf16x8*>(&tb.nb[min(ln.i, 2) * K + col]);
+      for (int kk = 0; kk < K / 8; kk += 8) {
+        const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(qr + kk);
+        const f32x4 n0 = *reinterpret_cast<const f32x4*>(nr + kk);
+        const f32x4 n1 = *reinterpret_cast<const f32x4*>(nr + kk + 4);
 #pragma unroll
-        for (int z = 0; z < 4; ++z) {
-          const bf16x8 fq = *reinterpret_cast<const bf16x8*>(&sQ[(16 * zg(z) + ln.i) * QP + col]);
-          dacc[z] = mma(fq, Bn, dacc[z]);
+        for (int e = 0; e < 4; ++e) {
+          d = fmaf((float)q8[e], n0[e], d);
+          d = fmaf((float)q8[4 + e], n1[e], d);
         }
       }
-#pragma unroll
-      for (int z = 0; z < 4; ++z) {
-        f32x4 d;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) d[r] = sum_xor1(dacc[z][r]);
-        if (ln.i == 0) *reinterpret_cast<f32x4*>(&s_dn[w * kTile + 16 * zg(z) + 4 * ln.g]) = d;
-      }
+      d += __shfl_xor(d, 1, 64);
+      d += __shfl_xor(d, 2, 64);
+      d += __shfl_xor(d, 4, 64);
+      if (part == 0) s_dn[row] = d;
     }
 
     // The registers loaded at the top of the tile are taken here, before any
@@ -802,7 +833,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
         for (int cv = 0; cv < 2; ++cv)
 #pragma unroll
           for (int e = 0; e < 8; ++e) Bv[cv][e] = (__bf16)((float)Av[jb][cv][e] * (e < 4 ? wa[e] : wb[e - 4]));
-        const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&tb.wb[min(lu.i, 2) * kTile + ts + 8 * lu.g]);
+        const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&tb.wb[min(lu.i, 3) * kTile + ts + 8 * lu.g]);
         // transposed K fragments through a ring of kRing registers: the read of
         // tile x + kRing - 1 is issued before the MFMAs of tile x
         constexpr int kRing = 4;
@@ -842,10 +873,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
     if (w == 0) {   // max(|n~^T q|, floor) of row t = lane
       const int t = fresh_lanes().lane;
       const float den = s_den[t] + s_den[kTile + t] + s_den[2 * kTile + t] + s_den[3 * kTile + t];
-      float dn = 0.f;
-#pragma unroll
-      for (int q = 0; q < NW; ++q) dn += s_dn[q * kTile + t];
-      const float d = den + tb.sc[t] * dn;
+      const float d = den + tb.sc[t] * s_dn[t];
       s_dnm[t] = fmaxf(fmaxf(fabsf(d), tb.fl[t]), FLT_MIN);
     }
     // ---------------- (P V)^T for the wave's rows; rows 0-31 have no keys
@@ -917,7 +945,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
       for (int x = 0; x < KXN; ++x) {
         f32x4 nv;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) nv[r] = fD * sum_xor1(Nacc[x][r]);
+        for (int r = 0; r < 4; ++r) nv[r] = fD * sum_quad(Nacc[x][r]);
         if (i == 0 && n_live(x)) *reinterpret_cast<f32x4*>(ndst + state_k0(kxg(nx(x)), g)) = nv;
       }
       if (tid == 0) a.m_out[bh] = (float)m_fin;
@@ -971,10 +999,10 @@ struct LocScan {
     const double logD_next = rescale ? 0.0 : logD + ld;
     const bool scale = rescale && !zero;   // rescaling a zero state is a no-op
     if ((threadIdx.x & 63) == 0) {
-      *cw = (live && Uj != -INFINITY) ? expf((float)(Uj - Rm - logD_next)) : 0.f;
+      *cw = (live && Uj != -INFINITY) ? exp_f64arg(Uj - Rm - logD_next) : 0.f;
       // the factor is below e^-70 (or zero): a float exp of the rounded
       // argument is as good as a float64 one and far cheaper
-      *rf = scale ? expf((float)(logD + ld)) : 1.f;
+      *rf = scale ? exp_f64arg(logD + ld) : 1.f;
     }
     any_rescale = any_rescale || scale;
     m = live ? gj + Rm : -INFINITY;
@@ -1036,8 +1064,8 @@ __device__ bool local_scan_batch(double g, double U, int R, int n, LocScan& c, f
   const bool zero_before = c.zero && (nzmask & ((1ull << lane) - 1ull)) == 0ull;
   const bool scale = flag && !zero_before;   // rescaling a zero state is a no-op
   if (act) {
-    cw[lane] = nonzero ? expf((float)(U - Rm - logD_next)) : 0.f;
-    rf[lane] = scale ? expf((float)(logD_before + ld)) : 1.f;   // zero: ld is -inf here
+    cw[lane] = nonzero ? exp_f64arg(U - Rm - logD_next) : 0.f;
+    rf[lane] = scale ? exp_f64arg(logD_before + ld) : 1.f;   // zero: ld is -inf here
   }
   double gs = act ? g : 0.0;
 #pragma unroll
@@ -1078,8 +1106,8 @@ struct LocLds {
   static constexpr int oK = 0;                      // [2] K tiles
   static constexpr int oV = oK + 2 * kBytes;        // [2] V tiles
   static constexpr int oW = oV + 2 * vBytes;        // [2][64] float w0
-  static constexpr int oWb = oW + 2 * kTile * 4;       // [2][3][64] bf16: w0 hi, w0 lo, zero
-  static constexpr int oCw = oWb + 2 * 3 * kTile * 2;   // [kMaxTiles] float: tile weight factor
+  static constexpr int oWb = oW + 2 * kTile * 4;       // [2][4][64] bf16: w0 hi, lo, lo2, zero
+  static constexpr int oCw = oWb + 2 * 4 * kTile * 2;   // [kMaxTiles] float: tile weight factor
   static constexpr int oRf = oCw + kMaxTiles * 4;       // [kMaxTiles] float: accumulator rescale (1 = none)
   static constexpr int bytes = oRf + kMaxTiles * 4;
 };
@@ -1129,9 +1157,9 @@ __device__ __forceinline__ void local_loader(const SegArgs& a, char* smem) {
       __builtin_amdgcn_global_load_lds((global_void*)(vt + offv[n]), (lds_void*)(vd + 1024 * n), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((global_void*)(a.gb.w0 + bh * T + tau * kTile + lane),
                                      (lds_void*)(smem + L::oW + buf * kTile * 4), 4, 0, 0);
-    if (lane < 16)   // hi and lo rows of the split weights, 256 bytes
-      __builtin_amdgcn_global_load_lds((global_void*)(a.gb.wb + (bh * Nt + tau) * 2 * kTile + 8 * lane),
-                                       (lds_void*)(smem + L::oWb + buf * 3 * kTile * 2), 16, 0, 0);
+    if (lane < 24)   // hi, lo and lo2 rows of the split weights, 384 bytes
+      __builtin_amdgcn_global_load_lds((global_void*)(a.gb.wb + (bh * Nt + tau) * 3 * kTile + 8 * lane),
+                                       (lds_void*)(smem + L::oWb + buf * 4 * kTile * 2), 16, 0, 0);
   };
   dma(tile0, 0);
   __builtin_amdgcn_s_waitcnt(0);
@@ -1177,7 +1205,7 @@ __device__ __forceinline__ void local_body(const SegArgs& a, char* smem, const L
     const __bf16* sK = reinterpret_cast<const __bf16*>(smem + L::oK + buf * L::kBytes);
     const __bf16* sV = reinterpret_cast<const __bf16*>(smem + L::oV + buf * L::vBytes);
     const float* s_w0 = reinterpret_cast<const float*>(smem + L::oW + buf * kTile * 4);
-    const __bf16* swb = reinterpret_cast<const __bf16*>(smem + L::oWb + buf * 3 * kTile * 2);
+    const __bf16* swb = reinterpret_cast<const __bf16*>(smem + L::oWb + buf * 4 * kTile * 2);
     // keys enter with weight exp(u_j - Rm - logD_next) = w0_j cw
     const float cw = s_cw[j];
     if constexpr (RESCALE) {
@@ -1198,9 +1226,9 @@ __device__ __forceinline__ void local_body(const SegArgs& a, char* smem, const L
       f32x4 wb = *reinterpret_cast<const f32x4*>(&s_w0[ts + 8 * lu.g + 4]);
       wa *= cw;
       wb *= cw;
-      // n~ operand: column 0 the bf16 high parts of w0, column 1 the low
-      // parts, the rest zero; the product is scaled by cw in float32
-      const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&swb[min(lu.i, 2) * kTile + ts + 8 * lu.g]);
+      // n~ operand: columns 0, 1, 2 the three bf16 terms of w0, the rest
+      // zero; the product is scaled by cw in float32
+      const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&swb[min(lu.i, 3) * kTile + ts + 8 * lu.g]);
       // this wave's K^T fragments: raw for n~, scaled by the key weights for C~
       bf16x8 As[KXW], Kr[KXW], Bv[4];
 #pragma unroll
@@ -1243,7 +1271,7 @@ __device__ __forceinline__ void local_body(const SegArgs& a, char* smem, const L
     for (int x = 0; x < KXW; ++x) {
       f32x4 nv;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) nv[r] = fD * sum_xor1(Nacc[x][r]);
+      for (int r = 0; r < 4; ++r) nv[r] = fD * sum_quad(Nacc[x][r]);
       if (le.i == 0) *reinterpret_cast<f32x4*>(ndst + 16 * (KXW * w + x) + 4 * le.g) = nv;
     }
     if (w == 0 && le.lane == 0) {
@@ -1267,8 +1295,8 @@ __global__ __launch_bounds__(64 * (LocWaves<K>::value + 1)) void local_kernel(Se
   // zero rows of the split-weight operands (published by the first barrier);
   // every compute wave writes the same tile table and reads only its own writes
   if (threadIdx.x < kTile) {
-    reinterpret_cast<__bf16*>(smem + L::oWb)[2 * kTile + threadIdx.x] = (__bf16)0.f;
-    reinterpret_cast<__bf16*>(smem + L::oWb + 3 * kTile * 2)[2 * kTile + threadIdx.x] = (__bf16)0.f;
+    reinterpret_cast<__bf16*>(smem + L::oWb)[3 * kTile + threadIdx.x] = (__bf16)0.f;
+    reinterpret_cast<__bf16*>(smem + L::oWb + 4 * kTile * 2)[3 * kTile + threadIdx.x] = (__bf16)0.f;
   }
   const LocScan sc = local_scan(a, bh, tile0, a.TPS, reinterpret_cast<float*>(smem + L::oCw),
                                 reinterpret_cast<float*>(smem + L::oRf));
@@ -1331,8 +1359,8 @@ __global__ __launch_bounds__(kThreads) void seg_combine_kernel(CombineArgs a) {
         const double mc = G == -INFINITY ? -INFINITY : m + G;
         double mn = fmax(mc, ml);
         if (mn == -INFINITY) mn = 0.0;
-        const float al = mc == -INFINITY ? 0.f : expf((float)(mc - mn));
-        const float be = ml == -INFINITY ? 0.f : expf((float)(ml - mn));
+        const float al = mc == -INFINITY ? 0.f : exp_f64arg(mc - mn);
+        const float be = ml == -INFINITY ? 0.f : exp_f64arg(ml - mn);
         x = al * x + be * y[e];
         *reinterpret_cast<f32x4*>(base + sidx * stride) = x;
         if (u == 0) a.mstart[sidx] = mn;

@@ -155,13 +155,16 @@ __global__ __launch_bounds__(kThreads) void gate64_kernel(GateArgs a) {
     a.gb.rs[base + lane] = rs;
     a.gb.w0[base + lane] = (lane >= Rc && Uc != -INFINITY) ? expf((float)(u - Uc)) : 0.f;
   }
-  if (a.gb.wb) {
+  if (a.gb.wb) {   // w0 = hi + lo + lo2, three bfloat16 terms (about 24 bits)
     const float w0 = (valid && lane >= Rc && Uc != -INFINITY) ? expf((float)(u - Uc)) : 0.f;
     const __bf16 hi = (__bf16)w0;
-    const __bf16 lo = (__bf16)(w0 - (float)hi);
-    uint16_t* dst = a.gb.wb + (bh * a.Nc + c) * 2 * kTile;
+    const float rest = w0 - (float)hi;
+    const __bf16 lo = (__bf16)rest;
+    const __bf16 lo2 = (__bf16)(rest - (float)lo);
+    uint16_t* dst = a.gb.wb + (bh * a.Nc + c) * 3 * kTile;
     dst[lane] = __builtin_bit_cast(uint16_t, hi);
     dst[kTile + lane] = __builtin_bit_cast(uint16_t, lo);
+    dst[2 * kTile + lane] = __builtin_bit_cast(uint16_t, lo2);
   }
   if (lane == 0) {
     a.gb.g[bh * a.Nc + c] = gc;

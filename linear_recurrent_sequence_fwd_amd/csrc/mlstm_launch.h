@@ -24,12 +24,12 @@ struct GateBuffers {
   double* U;    // mp at the chunk's last token
   int* R;       // rs at the chunk's last token
   float* w0;    // exp(u_j - U) for keys at or after the chunk's last zero forget gate, else 0
-  uint16_t* wb; // 64-token tiles only, [BH][Nt][2][64]: bfloat16 bits of w0 (hi) and of
-                // w0 - hi (lo), a two-term split of w0; null when not wanted
+  uint16_t* wb; // 64-token tiles only, [BH][Nt][3][64]: bfloat16 bits of a three-term split
+                // w0 = hi + lo + lo2 (about 24 bits); null when not wanted
 };
 
-// Chunk-start states written by the state pass: Cs [BH][Nc][V][K] (bf16 or
-// fp32), ns [BH][Nc][K] fp32, ms [BH][Nc] fp64.
+// Chunk-start states written by the state pass: Cs [BH][Nc][V][K] fp32,
+// ns [BH][Nc][K] fp32, ms [BH][Nc] fp64.
 struct ChunkStates {
   void* Cs;
   float* ns;
@@ -75,6 +75,40 @@ struct StepLaunch {
   void* h;
   const hipEvent_t* marks;   // [K_COUNT][2] events around the step kernel, or null
 };
+
+// Backward pass (mlstm_bwd.hip). The forward's gate kernel and state pass
+// run first (chunk-start states in `cs`); then the four backward kernels.
+enum BwdKernelId { B_FWD_GATE = 0, B_FWD_STATE = 1, B_DQ = 2, B_STATE = 3, B_DKV = 4, B_GATE = 5, B_COUNT = 6 };
+
+struct BwdLaunch {
+  int64_t BH, T, K, V;
+  int L;           // chunk length (multiple of 64)
+  int64_t Nc;      // number of chunks
+  int bf16;
+  const void *q, *k, *v, *o, *h, *dh;
+  const float *i_pre, *f_pre;
+  void *dq, *dk, *dv, *dout;
+  float *di, *df;
+  const float *C0, *n0, *m0;
+  float *dC0, *dn0, *dm0;
+  const hipEvent_t* marks;   // [B_COUNT][2] events around each kernel, or null
+};
+
+// Workspace of the backward kernels: g per token [BH][T][V] in the input
+// dtype; the chunk end adjoints [BH][Nc][V][K] float32; dz, q . dq [BH][T],
+// the end adjoints' normaliser part [BH][Nc][K] float32 and log scale
+// [BH][Nc] float64.
+struct BwdBuffers {
+  void* G;
+  float* dz;
+  float* qdq;
+  void* Es;
+  float* es;
+  double* Ms;
+};
+bool bwd_supported(int bf16, int64_t K, int64_t V);
+hipError_t launch_bwd(const BwdLaunch& b, const GateBuffers& gb, const ChunkStates& cs, const BwdBuffers& bb,
+                      hipStream_t s);
 
 // sLSTM forward (slstm.hip): pre [B,T,4,H,D], R [H,4,D,D], h [B,T,H,D];
 // optional state [B,H,D] in (c0 == NULL: zero state) and out (c_out == NULL:

@@ -33,9 +33,11 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 8
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mlstm_abi_version() == 1
+    assert lib.mlstm_abi_version() == 2
+    assert "mlstm_bwd_chunkwise" in names and "mlstm_bwd_chunkwise_workspace_size" in names
     prof = declared_functions(PROF_HEADER)
-    assert prof == ["mlstm_clock_probe", "mlstm_prof_fwd_chunkwise", "mlstm_prof_step"]
+    assert prof == ["mlstm_clock_probe", "mlstm_prof_bwd_chunkwise", "mlstm_prof_fwd_chunkwise",
+                    "mlstm_prof_step"]
     for n in prof:
         assert hasattr(lib, n), n
     # the product header declares only the method's calls and the status/version helpers
@@ -166,8 +168,8 @@ def test_workspace_checks_and_size():
     BH, T, Nc, K, V = 6, 1000, 8, 128, 192
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     expect = 3 * al(BH * T * 8) + 2 * al(BH * T * 4) + 2 * al(BH * Nc * 8) + al(BH * Nc * 4) \
-        + al(BH * Nc * V * K * 2) + al(BH * Nc * K * 4) + al(BH * Nc * 8)
-    assert need == expect
+        + al(BH * Nc * V * K * 4) + al(BH * Nc * K * 4) + al(BH * Nc * 8)
+    assert need == expect   # float32 chunk-start states for both dtypes
     assert chunkwise(a, chunk=128, ws=None, ws_bytes=need) == WORKSPACE
     assert chunkwise(a, chunk=128, ws=a._next(need), ws_bytes=need - 1) == WORKSPACE
     p = lib.mlstm_fwd_parallel_workspace_size(ctypes.byref(a))
@@ -191,7 +193,7 @@ def test_fused_workspace_size():
     ns = S - 1
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
     expect = 3 * al(BH * T * 8) + 2 * al(BH * T * 4) + 2 * al(BH * Nt * 8) + al(BH * Nt * 4) \
-        + al(BH * ns * V * K * 4) + al(BH * ns * K * 4) + 3 * al(BH * ns * 8) + al(BH * Nt * 2 * 64 * 2)
+        + al(BH * ns * V * K * 4) + al(BH * ns * K * 4) + 3 * al(BH * ns * 8) + al(BH * Nt * 3 * 64 * 2)
     assert need == expect
 
 
@@ -360,3 +362,102 @@ def test_slstm_empty_sequence_without_state_is_a_noop():
     a.pre = None
     a.h = None
     assert L.lib().slstm_fwd(ctypes.byref(a), None) == OK
+
+
+# ---------------------------------------------------------------- backward pass
+
+def fake_bwd(B=1, H=2, T=100, K=64, V=128, dtype=L.MLSTM_BF16, state_in=False, init_grad=False):
+    es = 2 if dtype == L.MLSTM_BF16 else 4
+    base = [0x7E0000000000]
+
+    def take(nbytes):
+        p = base[0]
+        base[0] += (nbytes + 4095) // 4096 * 4096 + 4096
+        return p
+
+    BH = B * H
+    nqk, nv, ng = BH * T * K * es, BH * T * V * es, BH * T * 4
+    a = L.BwdArgs(B, H, T, K, V, dtype, take(nqk), take(nqk), take(nv), take(nv), take(ng), take(ng),
+                  take(nv), take(nv), None, None, None,
+                  take(nqk), take(nqk), take(nv), take(nv), take(ng), take(ng), None, None, None)
+    if state_in:
+        a.C0, a.n0, a.m0 = take(BH * V * K * 4), take(BH * K * 4), take(BH * 4)
+    if init_grad:
+        a.dC0, a.dn0, a.dm0 = take(BH * V * K * 4), take(BH * K * 4), take(BH * 4)
+    a._next = take
+    return a
+
+
+def backward(a, chunk=64, ws=_AUTO, ws_bytes=None):
+    lib = L.lib()
+    need = lib.mlstm_bwd_chunkwise_workspace_size(ctypes.byref(a), chunk)
+    if ws is _AUTO:
+        ws = a._next(need) if need else None
+    if ws_bytes is None:
+        ws_bytes = need
+    code = lib.mlstm_bwd_chunkwise(ctypes.byref(a), chunk, ws, ws_bytes, None)
+    assert code != OK, "a fabricated-pointer call passed validation"
+    return code
+
+
+def test_backward_validation():
+    lib = L.lib()
+    assert lib.mlstm_bwd_chunkwise(None, 64, None, 0, None) == NULLPTR
+    a = fake_bwd(); a.dtype = 5
+    assert backward(a) == BAD_DTYPE
+    a = fake_bwd(); a.dh = None
+    assert backward(a) == NULLPTR
+    a = fake_bwd(); a.df_pre = None
+    assert backward(a) == NULLPTR
+    for chunk in (0, 32, 100, 8256):
+        assert backward(fake_bwd(), chunk=chunk) == BAD_SHAPE
+    a = fake_bwd(K=96)
+    assert backward(a) == BAD_SHAPE
+    # shapes the backward does not implement
+    assert backward(fake_bwd(K=256, V=1024)) == UNSUPPORTED
+    assert backward(fake_bwd(K=256, V=128, dtype=L.MLSTM_FP32)) == UNSUPPORTED
+    assert backward(fake_bwd(K=128, V=512, dtype=L.MLSTM_FP32)) == UNSUPPORTED
+    a = fake_bwd(state_in=True); a.m0 = None
+    assert backward(a) == NULLPTR
+    a = fake_bwd(init_grad=True); a.dn0 = None
+    assert backward(a) == NULLPTR
+    a = fake_bwd(); a.dq = a.q
+    assert backward(a) == ALIAS
+    a = fake_bwd(); a.dv = a.dk
+    assert backward(a) == ALIAS
+    a = fake_bwd(); a.dq += 2
+    assert backward(a) == MISALIGNED
+    a = fake_bwd()
+    assert backward(a, ws=None) == WORKSPACE
+    a = fake_bwd()
+    need = lib.mlstm_bwd_chunkwise_workspace_size(ctypes.byref(a), 64)
+    assert backward(a, ws_bytes=need - 1) == WORKSPACE
+    a = fake_bwd()
+    assert backward(a, ws=a.q) == ALIAS
+    # profiling variant: same checks, plus the event array
+    a = fake_bwd(); a.dh = None
+    ev = (ctypes.c_void_p * 12)()
+    assert lib.mlstm_prof_bwd_chunkwise(ctypes.byref(a), 64, None, 0, None, ev) == NULLPTR
+    assert lib.mlstm_prof_bwd_chunkwise(ctypes.byref(fake_bwd()), 64, None, 0, None, None) == NULLPTR
+
+
+def test_backward_workspace_size():
+    lib = L.lib()
+    a = fake_bwd(B=1, H=8, T=8192, K=256, V=512)
+    BH, T, K, V, es = 8, 8192, 256, 512, 2
+    for chunk in (64, 256, 1024):
+        Nc = -(-T // chunk)
+        need = lib.mlstm_bwd_chunkwise_workspace_size(ctypes.byref(a), chunk)
+        # gate data, forward chunk states, g per token, dz and q.dq, the end adjoints
+        # (the chunk states, forward and adjoint, are float32)
+        floor = (BH * T * (8 * 3 + 4 * 2) + BH * Nc * (8 * 2 + 4) + BH * Nc * (V * K * 4 + K * 4 + 8)
+                 + BH * T * V * es + BH * T * 8 + BH * Nc * (V * K * 4 + K * 4 + 8))
+        assert floor <= need <= floor + 64 * 256
+    a.T = 0
+    assert lib.mlstm_bwd_chunkwise_workspace_size(ctypes.byref(a), 64) == 0
+
+
+def test_backward_empty_sequence_without_init_grad_is_a_noop():
+    lib = L.lib()
+    a = fake_bwd(T=0)
+    assert lib.mlstm_bwd_chunkwise(ctypes.byref(a), 64, None, 0, None) == OK

@@ -291,21 +291,33 @@ def test_config_tiny(entry):
     assert rel_err(host(h), h_ref) <= TOL["fp32"]
 
 
-@pytest.mark.parametrize("seed,i_std", [(0, 1.0), (1, 6.0)])
-def test_config_mid(seed, i_std):
+_MID = {}
+
+
+@pytest.mark.parametrize("chunk", [64, 256, 1024])
+@pytest.mark.parametrize("seed,i_std", [(0, 1.0), (1, 6.0), (11, 6.0)])
+def test_config_mid(seed, i_std, chunk):
+    """The mid workload and its stress seeds (input-gate preactivations of
+    standard deviation 6, which make single keys dominate the state) at
+    several chunk lengths, whole output and final state."""
     M = _lib()
     cfg = CONFIGS["mid"]
-    say(f"config mid seed={seed} i_std={i_std}")
+    say(f"config mid seed={seed} i_std={i_std} chunk={chunk}")
     x = make_fwd_inputs(cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"], "bf16", seed=seed,
                         i_std=i_std)
-    h_ref, st_ref = oracle(x)
+    if (seed, i_std) not in _MID:
+        _MID[(seed, i_std)] = mlstm_recurrent_c(*[x[n] for n in NAMES])
+    h_ref, st_ref = _MID[(seed, i_std)]
     d = dev_inputs(x)
-    h, st = run_chunkwise(M, d, 64, return_state=True)
-    assert rel_err(host(h), h_ref) <= TOL["bf16"]
+    h, st = run_chunkwise(M, d, chunk, return_state=True)
+    err = rel_err(host(h), h_ref)
+    say(f"  h err {err:.2e}")
+    assert err <= TOL["bf16"]
     ec, en = state_err(st, st_ref)
     assert ec <= TOL["bf16"] and en <= TOL["bf16"]
-    hp = run_parallel(M, d)
-    assert rel_err(host(hp), h_ref) <= TOL["bf16"]
+    if chunk == 64:
+        hp = run_parallel(M, d)
+        assert rel_err(host(hp), h_ref) <= TOL["bf16"]
 
 
 # Full-size references are computed once per session by the C float64 oracle
