@@ -1,16 +1,33 @@
-"""Benchmark of the mLSTM cell forward on one MI355X.
+"""Benchmark of the mLSTM cell on one MI355X.
 
-One step = one full chunkwise forward (gate prefix sums per 64-token tile,
-the chunks' end states and their in-order fold, the fused tile kernel that
-produces h) over the 7B-layer-shaped workload
-(B=1, H=8, T=8192, d_qk=256, d_v=512, bf16 q/k/v/o and h, float32 gates),
-inputs resident in HBM. Prints ONE JSON line on stdout; progress goes to
-stderr.
+One step = one full chunkwise forward over the 7B-layer-shaped workload
+(B=1, H=8, T=8192, d_qk=256, d_v=512; bf16 q/k/v/o and h, float32 gates):
+gate prefix sums per 64-token tile, the chunks' end states and their
+in-order fold, and the fused tile kernel that produces h. Inputs are
+resident in HBM when a timed step starts. Prints ONE JSON line on stdout;
+progress goes to stderr.
 
-Extra keys: per-kernel average durations from HIP events recorded around
-every launch inside the timed region, the roofline of the dominant kernel,
-the chunk sweep, the decode step (B=64, H=8, float32 state) in % of HBM
-bandwidth, and the oracle timed on the host cores (a baseline, not a target).
+Timing protocol (every figure is a median over reps unless said otherwise):
+  * cold (the primary figure): before each rep a 512 MiB scratch buffer is
+    overwritten, which evicts the 256 MiB MALL and the L2s, so the step
+    reads its inputs from HBM; HIP events on the launch stream bracket the
+    step (and, in a second pass through the profiling entry point, each
+    kernel group);
+  * warm: the same steps back to back, timed on the host clock between two
+    synchronisations and with events.
+`value` and `ms_per_step` are the cold median step.
+
+Roofline: the method's algorithmic bytes (4,104 B per token-head: q, k, v,
+o, h in bf16 and the two float32 gates; workspace traffic is not counted)
+over the cold median duration of the dominant kernel, against 8 TB/s, and
+the step's flops against the dense bf16 MFMA peak (2.5 PFLOP/s). When a
+committed rocprofv3 summary of the same kernel sources exists under
+profiles/, its kernel-trace duration and HBM traffic are reported beside.
+
+Other keys: the chunk sweep, the mid workload (chunkwise and parallel
+forms), the long-context workload (T = 131072), the chunkwise backward pass,
+the decode step, the sLSTM recurrence, and the float64 C oracle timed on the
+host's cores (a baseline, not a target).
 """
 from __future__ import annotations
 
@@ -20,6 +37,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -27,16 +45,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12            # B/s, MI355X HBM3E
-MFMA_BF16_PEAK = 2.5166e15   # flop/s dense bf16: 256 CU x 2.4 GHz x 4096 flop/clk
+MFMA_BF16_PEAK = 2.5e15      # flop/s, dense bf16 MFMA
+FP32_PEAK = 157.3e12         # flop/s, float32 vector (FMA = 2 flops), 256 CUs
 METRIC = "mLSTM fwd tokens/s at 7B-layer shape, % bf16 MFMA peak; decode step % HBM BW"
 WORKLOAD = dict(B=1, H=8, T=8192, d_qk=256, d_v=512)
+MID = dict(B=4, H=8, T=2048, d_qk=128, d_v=128)
+LONG = dict(B=1, H=8, T=131072, d_qk=256, d_v=512)
 DECODE = dict(B=64, H=8, d_qk=256, d_v=512, prefill=512)
 SLSTM = dict(B=16, H=8, D=128, T=2048)   # sLSTM recurrence: 128 sequence-heads of 128 cells
-FP32_PEAK = 157.3e12          # flop/s float32 vector (FMA = 2 flops), 256 CUs
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_kernel_7b_layer_traffic.md")
-KERNEL_SRC = os.path.join(ROOT, "linear_recurrent_sequence_fwd_amd", "csrc", "mlstm_fused.hip")
 TILE = 64                    # tokens per tile: the length of the quadratic (intra-tile) form
+FLUSH_BYTES = 512 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "linear_recurrent_sequence_fwd_amd", "csrc")
 LABELS = {"gate": "gate", "state": "chunk_states", "out": "fused"}
+BWD_LABELS = {"fwd_gate": "fwd_gate", "fwd_state": "fwd_chunk_states", "dq": "dq", "adjoint": "adjoint",
+              "dkv": "dkv", "dgate": "dgate"}
 
 
 def log(*a):
@@ -52,6 +75,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self, n):
         out = []
@@ -61,6 +85,9 @@ class HipEvents:
             out.append(e.value)
         return out
 
+    def record(self, e, stream):
+        assert self.hip.hipEventRecord(e, stream) == 0
+
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
         assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
@@ -68,42 +95,39 @@ class HipEvents:
 
     def destroy(self, evs):
         for e in evs:
-            self.hip.hipEventDestroy(e)
+            if e:
+                self.hip.hipEventDestroy(e)
 
 
 # ---------------------------------------------------------------- algorithmic work
 
-def fwd_bytes(B, H, T, K, V, chunk):
-    """Algorithmic HBM bytes of the whole forward as timed (no final state
-    requested): q, k, v, o read once and h written once (bf16), float32 gates
-    read once."""
+def fwd_bytes(B, H, T, K, V):
+    """The forward's algorithmic HBM bytes (no final state requested): q, k,
+    v, o read once and h written once in bf16, the two float32 gates read
+    once; 4,104 B per token-head at d_qk = 256, d_v = 512."""
     return B * H * T * (2 * K + 2 * K + 2 * V + 2 * V + 2 * V + 4 + 4)
 
 
 def fwd_flops(B, H, T, K, V):
-    """Flops of the method as computed: per token-head 2KV (state readout
-    q C~^T) + 2KV (state update) + TILE K (causal half of Q K^T over a tile)
-    + TILE V (causal half of P V)."""
+    """Flops of the forward as computed: per token-head 2KV (readout of the
+    carried state, C~ q) + 2KV (state update) + TILE K (causal half of Q K^T
+    over a tile) + TILE V (causal half of P V)."""
     return B * H * T * (4 * K * V + TILE * (K + V))
 
 
-def kernel_bytes(name, B, H, T, K, V, chunk):
-    """Algorithmic bytes one launch of a kernel must move (inputs read once,
-    outputs written once), at the 7B-layer shape with bf16 data."""
-    BH = B * H
-    Nt = -(-T // TILE)
-    S = -(-Nt // (chunk // TILE))
-    state = 4 * (V * K + K) + 8                    # one float32 chunk state C~, n~ and its stabiliser
-    gate_tok = 3 * 8 + 4                           # u, b, mp (float64) and rs (int32)
-    if name == "gate":
-        return BH * T * (4 + 4 + gate_tok + 4) + BH * Nt * (8 + 8 + 4)
-    if name == "state":                            # chunks' end states: K, V of chunks 0..S-2; fold
-        t_loc = min(T, (S - 1) * chunk)
-        return BH * t_loc * (2 * K + 2 * V + 8) + BH * (S - 1) * (3 * state + 8)
-    if name == "out":                              # fused tiles: q, k, v, o in, h out, chunk start states
-        return BH * T * (2 * K + 2 * K + 2 * V + 2 * V + 2 * V + gate_tok) + BH * Nt * 20 \
-            + BH * (S - 1) * state
-    raise KeyError(name)
+def bwd_bytes(B, H, T, K, V):
+    """The backward's algorithmic HBM bytes: q, k, v, o, h and dh read once
+    (bf16), the two gates read once, dq, dk, dv, do written once (bf16) and
+    di, df written once (float32); 8,208 B per token-head at 256 / 512."""
+    return B * H * T * (4 * K + 8 * V + 8 + 4 * K + 4 * V + 8)
+
+
+def bwd_flops(B, H, T, K, V):
+    """Flops of the backward as computed: per token-head 8KV (dq's carried
+    term, the adjoint update, and the adjoint's terms of dk and dv) plus
+    2 TILE (K + V) for the intra-tile products (Q K^T and G V^T, then their
+    products with Q, K and G), causal halves."""
+    return B * H * T * (8 * K * V + 2 * TILE * (K + V))
 
 
 def decode_bytes(B, H, K, V):
@@ -113,7 +137,81 @@ def decode_bytes(B, H, K, V):
     return BH * (2 * (V * K + K + 1) * 4 + (2 * K + 2 * V) * 4 + 8 + V * 4)
 
 
-# ---------------------------------------------------------------- the runs
+def slstm_flops(B, H, T, D):
+    """Flops of the sLSTM recurrence as computed: per step and cell the four
+    recurrent dot products (2 * 4 * D) plus about 24 for the gates, the
+    stabiliser and the cell update."""
+    return B * H * T * D * (8 * D + 24)
+
+
+# ---------------------------------------------------------------- timing
+
+class Timer:
+    """Cold and warm step timing on the current stream."""
+
+    def __init__(self, torch, ev):
+        self.torch = torch
+        self.ev = ev
+        self.scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def flush(self, i):
+        self.scratch.fill_(i & 0xFF)
+
+    def cold(self, fn, reps, warmup=2):
+        """Median, mean and min (ms) of `reps` steps, each after a flush."""
+        for i in range(warmup):
+            self.flush(i)
+            fn()
+        evs = self.ev.create(2 * reps)
+        for i in range(reps):
+            self.flush(i)
+            self.ev.record(evs[2 * i], self.stream)
+            fn()
+            self.ev.record(evs[2 * i + 1], self.stream)
+        self.torch.cuda.synchronize()
+        ms = [self.ev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(reps)]
+        self.ev.destroy(evs)
+        return {"median_ms": statistics.median(ms), "mean_ms": statistics.fmean(ms), "min_ms": min(ms),
+                "reps": reps}
+
+    def warm(self, fn, reps, warmup=3):
+        """Back-to-back steps: host-clock time per step between two
+        synchronisations, and the median of per-step events."""
+        for _ in range(warmup):
+            fn()
+        self.torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        self.torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / reps * 1e3
+        evs = self.ev.create(2 * reps)
+        for i in range(reps):
+            self.ev.record(evs[2 * i], self.stream)
+            fn()
+            self.ev.record(evs[2 * i + 1], self.stream)
+        self.torch.cuda.synchronize()
+        ms = [self.ev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(reps)]
+        self.ev.destroy(evs)
+        return {"wall_ms": wall, "median_ms": statistics.median(ms), "reps": reps}
+
+    def groups(self, fn_prof, groups, reps, cold=True):
+        """Median duration (us) of each kernel group, from the events the
+        profiling entry point records around the groups."""
+        from linear_recurrent_sequence_fwd_amd import _lib
+        per = {g: [] for g in groups}
+        for i in range(reps):
+            evs = self.ev.create(2 * len(groups))
+            if cold:
+                self.flush(i)
+            fn_prof(_lib.event_array(evs))
+            self.torch.cuda.synchronize()
+            for k, g in enumerate(groups):
+                per[g].append(self.ev.elapsed_ms(evs[2 * k], evs[2 * k + 1]) * 1e3)
+            self.ev.destroy(evs)
+        return {g: statistics.median(v) for g, v in per.items()}
+
 
 def make_device_inputs(torch, cfg, dtype="bf16", seed=0):
     from linear_recurrent_sequence_fwd_amd.inputs import make_fwd_inputs
@@ -125,10 +223,10 @@ def make_device_inputs(torch, cfg, dtype="bf16", seed=0):
     return x, d
 
 
-def time_chunkwise(torch, M, L, ev, d, chunk, steps, warmup, kernels=("gate", "state", "out")):
-    """Wall time of `steps` forward calls with no profiling hooks, then the
-    average duration of each kernel group from HIP events recorded around its
-    launches in a second, separate pass of the same number of calls."""
+def chunkwise_callables(torch, d, chunk):
+    """(plain call, profiling call taking an event array) of one chunkwise
+    forward on the current stream; arguments are marshalled once, the calls
+    only enqueue."""
     from linear_recurrent_sequence_fwd_amd import _lib
     h = torch.empty_like(d["v"])
     args = _lib.fwd_args(d["q"], d["k"], d["v"], d["o_pre"], d["i_pre"], d["f_pre"], h)
@@ -137,56 +235,79 @@ def time_chunkwise(torch, M, L, ev, d, chunk, steps, warmup, kernels=("gate", "s
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     lib, pargs, wsp = _lib.lib(), ctypes.byref(args), ws.data_ptr()
 
-    def one():     # arguments marshalled once; the loop only enqueues
+    def one():
         code = lib.mlstm_fwd_chunkwise(pargs, chunk, wsp, nbytes, stream)
         if code:
             raise RuntimeError(lib.mlstm_last_error().decode())
 
-    for _ in range(warmup):
-        one()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        one()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    pairs = {k: ev.create(2 * steps) for k in kernels}
-    arrays = [_lib.event_array([pairs[g][2 * i + e] if g in kernels else None
-                                for g in _lib.PROF_GROUPS for e in (0, 1)]) for i in range(steps)]
-    for i in range(steps):
-        code = lib.mlstm_prof_fwd_chunkwise(pargs, chunk, wsp, nbytes, stream, arrays[i])
+    def prof(events):
+        code = lib.mlstm_prof_fwd_chunkwise(pargs, chunk, wsp, nbytes, stream, events)
         if code:
             raise RuntimeError(lib.mlstm_last_error().decode())
-    torch.cuda.synchronize()
-    per_kernel = {}
-    for k in kernels:
-        ms = [ev.elapsed_ms(pairs[k][2 * i], pairs[k][2 * i + 1]) for i in range(steps)]
-        per_kernel[k] = sum(ms) / len(ms) * 1e3      # us
-        ev.destroy(pairs[k])
-    return elapsed, per_kernel
+
+    one.keep = prof.keep = (h, ws, args)
+    return one, prof
 
 
-def time_chunkwise_graph(torch, d, chunk, steps, warmup):
-    """Wall time of `steps` replays of a HIP graph holding one forward call (its
-    four kernel launches), captured on torch's capture stream."""
+def parallel_callable(torch, d):
     from linear_recurrent_sequence_fwd_amd import _lib
     h = torch.empty_like(d["v"])
     args = _lib.fwd_args(d["q"], d["k"], d["v"], d["o_pre"], d["i_pre"], d["f_pre"], h)
-    nbytes = _lib.chunkwise_workspace_bytes(args, chunk)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    nbytes = _lib.parallel_workspace_bytes(args)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     lib, pargs, wsp = _lib.lib(), ctypes.byref(args), ws.data_ptr()
 
     def one():
-        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        code = lib.mlstm_fwd_chunkwise(pargs, chunk, wsp, nbytes, stream)
+        code = lib.mlstm_fwd_parallel(pargs, wsp, nbytes, stream)
         if code:
             raise RuntimeError(lib.mlstm_last_error().decode())
 
+    one.keep = (h, ws, args)
+    return one
+
+
+def backward_callables(torch, d, chunk, seed=0):
+    """(plain call, profiling call) of one chunkwise backward pass given the
+    forward's h and a seeded upstream gradient dh."""
+    import linear_recurrent_sequence_fwd_amd as M
+    from linear_recurrent_sequence_fwd_amd import _lib
+    from linear_recurrent_sequence_fwd_amd.inputs import make_grad_output
+    B, H, T, K = d["q"].shape
+    V = d["v"].shape[-1]
+    h = M.mlstm_fwd_chunkwise(d["q"], d["k"], d["v"], d["o_pre"], d["i_pre"], d["f_pre"], chunk=chunk)
+    dh = torch.from_numpy(make_grad_output(B, H, T, V, "bf16", seed=seed)).cuda().to(torch.bfloat16)
+    grads = _lib.bwd_outputs(d["q"], d["v"])
+    args = _lib.bwd_args(d["q"], d["k"], d["v"], d["o_pre"], d["i_pre"], d["f_pre"], h, dh, grads)
+    nbytes = _lib.bwd_workspace_bytes(args, chunk)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    lib, pargs, wsp = _lib.lib(), ctypes.byref(args), ws.data_ptr()
+
+    def one():
+        code = lib.mlstm_bwd_chunkwise(pargs, chunk, wsp, nbytes, stream)
+        if code:
+            raise RuntimeError(lib.mlstm_last_error().decode())
+
+    def prof(events):
+        code = lib.mlstm_prof_bwd_chunkwise(pargs, chunk, wsp, nbytes, stream, events)
+        if code:
+            raise RuntimeError(lib.mlstm_last_error().decode())
+
+    one.keep = prof.keep = (h, dh, grads, ws, args)
+    return one, prof
+
+
+def graph_ms(torch, d, chunk, steps, warmup):
+    """Host-clock time per replay of a HIP graph holding one chunkwise forward
+    (captured on torch's capture stream, its buffers from the graph's pool)."""
+    one, _ = chunkwise_callables(torch, d, chunk)
     one()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        one()
+        cap, _ = chunkwise_callables(torch, d, chunk)
+        cap()
     torch.cuda.synchronize()
     for _ in range(warmup):
         g.replay()
@@ -195,12 +316,16 @@ def time_chunkwise_graph(torch, d, chunk, steps, warmup):
     for _ in range(steps):
         g.replay()
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    del g
-    return elapsed
+    el = time.perf_counter() - t0
+    del g, cap
+    return el / steps * 1e3
 
 
-def time_decode(torch, M, ev, steps, warmup):
+def time_decode(torch, M, timer, steps, warmup):
+    """Host-clock time per step of `steps` back-to-back decode steps
+    (ping-ponged n, m), and the median kernel duration from events around
+    each launch."""
+    from linear_recurrent_sequence_fwd_amd import _lib
     from linear_recurrent_sequence_fwd_amd.inputs import make_step_inputs
     cfg = DECODE
     B, H, K, V = cfg["B"], cfg["H"], cfg["d_qk"], cfg["d_v"]
@@ -213,13 +338,11 @@ def time_decode(torch, M, ev, steps, warmup):
     for s in range(8):
         x = make_step_inputs(B, H, K, V, step=s, dtype="fp32", seed=4)
         pool.append({a: torch.from_numpy(x[a]).to("cuda") for a in ("q", "k", "v", "o_pre", "i_pre", "f_pre")})
-    from linear_recurrent_sequence_fwd_amd import _lib
     n2, m2 = torch.empty_like(n), torch.empty_like(m)
     h = torch.empty((B, H, V), device="cuda")
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    stream = timer.stream
     bufs = [(n, m, n2, m2), (n2, m2, n, m)]
     lib = _lib.lib()
-    # arguments marshalled once per (input set, ping-pong parity); the loop only enqueues
     structs = [[_lib.step_args(x["q"], x["k"], x["v"], x["o_pre"], x["i_pre"], x["f_pre"], C, *bufs[p], h)
                 for p in range(2)] for x in pool]
 
@@ -235,8 +358,8 @@ def time_decode(torch, M, ev, steps, warmup):
     for i in range(steps):
         one(warmup + i)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    evs = ev.create(2 * steps)     # per-launch durations: a second pass through the profiling call
+    wall_us = (time.perf_counter() - t0) / steps * 1e6
+    evs = timer.ev.create(2 * steps)
     for i in range(steps):
         j = warmup + steps + i
         code = lib.mlstm_prof_step(ctypes.byref(structs[j % len(pool)][j % 2]), stream, evs[2 * i],
@@ -244,41 +367,72 @@ def time_decode(torch, M, ev, steps, warmup):
         if code:
             raise RuntimeError(lib.mlstm_last_error().decode())
     torch.cuda.synchronize()
-    k_us = sum(ev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)) / steps * 1e3
-    ev.destroy(evs)
+    k_us = statistics.median(timer.ev.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(steps)) * 1e3
+    timer.ev.destroy(evs)
     assert bool(torch.isfinite(h).all())
-    return elapsed, k_us
+    return wall_us, k_us
 
 
-def slstm_flops(B, H, T, D):
-    """Flops of the sLSTM recurrence as computed: per step and cell the four
-    recurrent dot products (2 * 4 * D) plus about 24 for the gates, the
-    stabiliser and the cell update."""
-    return B * H * T * D * (8 * D + 24)
-
-
-def time_slstm(torch, reps, warmup):
-    """Event-timed sLSTM forward calls (one kernel each) on the current stream."""
+def time_slstm(torch, timer, reps):
     from linear_recurrent_sequence_fwd_amd import _lib
     from linear_recurrent_sequence_fwd_amd.inputs import make_slstm_inputs
     B, H, T, D = SLSTM["B"], SLSTM["H"], SLSTM["T"], SLSTM["D"]
     pre, R = make_slstm_inputs(B, H, T, D, seed=5)
     pre_d, R_d = torch.from_numpy(pre).cuda(), torch.from_numpy(R).cuda()
     h = torch.empty((B, T, H, D), dtype=torch.float32, device="cuda")
-    for _ in range(warmup):
+
+    def one():
         _lib.slstm_fwd(pre_d, R_d, h=h)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        _lib.slstm_fwd(pre_d, R_d, h=h)
-    e1.record()
-    torch.cuda.synchronize()
+
+    r = timer.warm(one, reps, warmup=2)
     assert bool(torch.isfinite(h).all())
-    return e0.elapsed_time(e1) / reps * 1e-3, pre, R
+    return r["median_ms"] * 1e-3, pre, R
 
 
-def slstm_cpu_baseline(pre, R, budget_s=8.0):
+# ---------------------------------------------------------------- host baseline
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_baseline(x):
+    """The float64 C oracle (one sequence per host thread) on the 7B-layer
+    workload: all heads on as many threads as there are heads and host
+    cores, and one head on one thread."""
+    from oracle.mlstm_ref import mlstm_recurrent_c
+    names = ("q", "k", "v", "i_pre", "f_pre", "o_pre")
+    H, T = x["q"].shape[1], x["q"].shape[2]
+    n = min(host_threads(), H)
+    t0 = time.perf_counter()
+    mlstm_recurrent_c(*[x[k] for k in names], threads=n)
+    el_n = time.perf_counter() - t0
+    one = {k: x[k][:, :1] for k in names}
+    t0 = time.perf_counter()
+    mlstm_recurrent_c(*[one[k] for k in names], threads=1)
+    el_1 = time.perf_counter() - t0
+    return {"value": T / el_n, "unit": "tokens/s", "cores": n, "kind": "oracle",
+            "sample": f"float64 C step recurrence (oracle/mlstm_ref.c) over the whole 7B-layer workload "
+                      f"(B=1 H={H} T={T}), one head per thread, {n} threads: {el_n:.2f} s",
+            "one_core": {"value": T / H / el_1, "unit": "tokens/s", "cores": 1,
+                         "sample": f"one of the {H} heads on one thread: {el_1:.2f} s"},
+            "cpu_model": cpu_model(), "host_threads_available": host_threads()}
+
+
+def slstm_cpu_baseline(pre, R, budget_s=6.0):
     """The sLSTM oracle recurrence on one host thread over all sequences and
     heads, as many leading steps as fit the budget."""
     import numpy as np
@@ -298,55 +452,56 @@ def slstm_cpu_baseline(pre, R, budget_s=8.0):
                       f"steps ({el:.1f} s, one thread)"}
 
 
-def cpu_baseline(x, budget_s=15.0):
-    """The oracle recurrence on the host, all heads, as many leading tokens as fit the budget."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-    from oracle.mlstm_oracle import mlstm_step
-    names = ("q", "k", "v", "i_pre", "f_pre", "o_pre")
-    a = {n: x[n][0].astype(np.float64) for n in names}     # [H, T, ...]
-    H, T, K = a["q"].shape
-    V = a["v"].shape[-1]
-    C = np.zeros((H, V, K)); n = np.zeros((H, K)); m = np.zeros(H)
-    done = 0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while done < T and time.perf_counter() - t0 < budget_s:
-            t = done
-            _, C, n, m = mlstm_step(a["q"][:, t], a["k"][:, t], a["v"][:, t], a["i_pre"][:, t],
-                                    a["f_pre"][:, t], a["o_pre"][:, t], C, n, m)
-            done += 1
-        el = time.perf_counter() - t0
-    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"float64 NumPy step recurrence, B=1 H={H} d_qk={K} d_v={V}, first {done} of "
-                      f"{T} tokens ({el:.1f} s, one thread)"}
+# ---------------------------------------------------------------- committed profiles
+
+def sources_sha256():
+    """sha256 over the HIP library's sources (sorted file names, contents)."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
 
 
-def traffic_from_profile():
-    """HBM bytes per launch of the output kernel from the committed counter
-    summary, if it was taken on the current kernel source; else None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def profile_figures(name):
+    """Figures of a committed rocprofv3 summary under profiles/ (`key: value`
+    lines), if it names the sha256 of the current library sources."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
-    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
-    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_sha or not m_b or m_sha.group(1) != sha:
+    text = open(path).read()
+    m = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    if not m or m.group(1) != sources_sha256():
         return None
-    return float(m_b.group(1))
+    out = {}
+    for key in ("trace_avg_us", "traffic_bytes_per_launch"):
+        mm = re.search(rf"{key}:\s*([0-9.eE+]+)", text)
+        if mm:
+            out[key] = float(mm.group(1))
+    return out
 
 
-def measure_clock(torch, d, chunk, steps=20, iters=250):
-    """Shader clock (MHz) while the chunkwise forward runs. The probe wave sleeps
-    on a side stream (default priority) while `steps` forward calls run on the
-    current stream; its shader-clock ticks over its constant-rate ticks, times
-    that counter's rate, give the clock. The rate itself (nominally 100 MHz) is
-    taken from an event-timed probe run alone, whose own clock is reported as
-    the idle figure. iters = 250 sleeps last about 1 ms, well inside the
-    forward calls."""
+def roofline(nbytes, flops, seconds, label):
+    hbm = nbytes / seconds / HBM_PEAK
+    mf = flops / seconds / MFMA_BF16_PEAK
+    if mf > hbm:
+        r = {"bound": "mfma", "achieved": flops / seconds / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
+             "unit": "TFLOP/s", "frac": mf}
+    else:
+        r = {"bound": "hbm", "achieved": nbytes / seconds / 1e9, "peak": HBM_PEAK / 1e9,
+             "unit": "GB/s", "frac": hbm}
+    return {"kernel": label, **r, "hbm_frac": hbm, "mfma_frac": mf,
+            "algorithmic_bytes": nbytes, "algorithmic_flops": flops}
+
+
+def measure_clock(torch, one, steps=20, iters=250):
+    """Shader clock (MHz) while the chunkwise forward runs: a sleeping probe
+    wave on a side stream (default priority) counts shader-clock ticks
+    against constant-rate ticks; the constant counter's rate comes from an
+    event-timed probe run alone, whose own clock is the idle figure."""
     from linear_recurrent_sequence_fwd_amd import _lib
     ticks = torch.zeros(4, dtype=torch.int64, device="cuda")
-    # rate of the constant counter, and the clock with nothing else running
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     _lib.clock_probe(ticks, iters)
     e0.record()
@@ -356,59 +511,53 @@ def measure_clock(torch, d, chunk, steps=20, iters=250):
     t = ticks.cpu().tolist()
     rt_mhz = (t[3] - t[2]) / (e0.elapsed_time(e1) * 1e3)
     idle_mhz = (t[1] - t[0]) / (t[3] - t[2]) * rt_mhz
-    # the clock under the forward pass
-    h = torch.empty_like(d["v"])
-    args = _lib.fwd_args(d["q"], d["k"], d["v"], d["o_pre"], d["i_pre"], d["f_pre"], h)
-    nbytes = _lib.chunkwise_workspace_bytes(args, chunk)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    main_stream = torch.cuda.current_stream()
-    stream = ctypes.c_void_p(main_stream.cuda_stream)
-    lib, pargs, wsp = _lib.lib(), ctypes.byref(args), ws.data_ptr()
-    torch.cuda.synchronize()
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         _lib.clock_probe(ticks, iters)
     for _ in range(steps):
-        code = lib.mlstm_fwd_chunkwise(pargs, chunk, wsp, nbytes, stream)
-        if code:
-            raise RuntimeError(lib.mlstm_last_error().decode())
+        one()
     torch.cuda.synchronize()
     t = ticks.cpu().tolist()
-    load_mhz = (t[1] - t[0]) / (t[3] - t[2]) * rt_mhz
-    return {"under_load_mhz": load_mhz, "idle_mhz": idle_mhz, "realtime_counter_mhz": rt_mhz,
+    return {"under_load_mhz": (t[1] - t[0]) / (t[3] - t[2]) * rt_mhz, "idle_mhz": idle_mhz,
+            "realtime_counter_mhz": rt_mhz,
             "method": "s_memtime over s_memrealtime of one sleeping wave beside the forward calls"}
+
+
+# ---------------------------------------------------------------- main
+
+SECTIONS = ("sweep", "graph", "clock", "bwd", "mid", "long", "decode", "slstm", "cpu")
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50, help="reps of the headline step")
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--chunk", type=int, default=1024,
                     help="chunk length: the state is materialised at chunk starts (multiple of 64)")
-    ap.add_argument("--sweep", type=str, default="512,2048", help="chunk sizes reported besides --chunk")
-    ap.add_argument("--decode-steps", type=int, default=200)
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="skip the replayed-graph timing")
-    ap.add_argument("--no-clock", action="store_true", help="skip the shader clock measurement")
-    ap.add_argument("--no-slstm", action="store_true", help="skip the sLSTM recurrence measurement")
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--sweep", type=str, default="64,256,512,2048", help="chunk sizes reported besides --chunk")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--bwd-chunk", type=int, default=256)
+    ap.add_argument("--only", type=str, default="",
+                    help="comma list of sections to run after the headline (" + ", ".join(SECTIONS) +
+                         "); empty = all, 'none' = the headline alone")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(f"bench.py runs on one GPU only: the mLSTM path here is a single-GPU build "
-              f"(--gpus {args.gpus} requested). Heads and batch shard with no exchange; see the "
-              f"design notes for the multi-GPU plan.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only: this build of the mLSTM path is single-GPU "
+              f"(--gpus {args.gpus} requested). Heads and batch shard with no exchange; the design "
+              f"notes describe the multi-GPU plan.", file=sys.stderr)
         sys.exit(2)
+    want = set(s for s in args.only.split(",") if s) or set(SECTIONS)
 
     import torch
     import linear_recurrent_sequence_fwd_amd as M
     from linear_recurrent_sequence_fwd_amd import _lib
     _lib.lib()
     ev = HipEvents()
+    timer = Timer(torch, ev)
     cfg = WORKLOAD
     B, H, T, K, V = cfg["B"], cfg["H"], cfg["T"], cfg["d_qk"], cfg["d_v"]
 
@@ -424,54 +573,28 @@ def main():
 
     log(f"[bench] inputs 7B-layer B={B} H={H} T={T} d_qk={K} d_v={V} bf16")
     x, d = make_device_inputs(torch, cfg, "bf16", seed=0)
+    nbytes, flops = fwd_bytes(B, H, T, K, V), fwd_flops(B, H, T, K, V)
 
-    log(f"[bench] chunkwise chunk={args.chunk}: warmup {args.warmup}, steps {args.steps}")
-    elapsed, per_k = time_chunkwise(torch, M, _lib, ev, d, args.chunk, args.steps, args.warmup)
-    ms_step = elapsed / args.steps * 1e3
-    tok_s = B * T * args.steps / elapsed
-    flops = fwd_flops(B, H, T, K, V)
-    flops_ci = B * H * T * 4 * K * V
-    path_bytes = fwd_bytes(B, H, T, K, V, args.chunk)
-    dom = max(per_k, key=per_k.get)
-    t_dom = per_k[dom] * 1e-6
-    kb = kernel_bytes(dom, B, H, T, K, V, args.chunk)
-    # the fused kernel carries all of the method's flops; the others are bandwidth work
-    kf = flops if dom == "out" else 0.0
-    hbm_f, mfma_f = kb / t_dom / HBM_PEAK, kf / t_dom / MFMA_BF16_PEAK
-    if mfma_f > hbm_f:
-        roof = {"bound": "mfma", "achieved": kf / t_dom / 1e12, "peak": MFMA_BF16_PEAK / 1e12,
-                "unit": "TFLOP/s", "frac": mfma_f}
-    else:
-        roof = {"bound": "hbm", "achieved": kb / t_dom / 1e9, "peak": HBM_PEAK / 1e9,
-                "unit": "GB/s", "frac": hbm_f}
-    roof = {"kernel": LABELS[dom], **roof, "hbm_frac": hbm_f, "mfma_frac": mfma_f,
-            "algorithmic_bytes": kb, "algorithmic_flops": kf,
-            "traffic": traffic_from_profile() if dom == "out" else None}
-    per_k = {LABELS[k]: v for k, v in per_k.items()}
-    log(f"[bench] {ms_step:.3f} ms/step, {tok_s:.3e} tokens/s, kernels us {per_k}")
-
-    sweep = {}
-    for L in [int(s) for s in args.sweep.split(",") if s]:
-        if L == args.chunk:
-            continue
-        el, pk = time_chunkwise(torch, M, _lib, ev, d, L, max(5, args.steps // 2), 2)
-        st = max(5, args.steps // 2)
-        sweep[str(L)] = {"ms_per_step": el / st * 1e3, "tokens_per_s": B * T * st / el,
-                         "mfma_frac": flops / (el / st) / MFMA_BF16_PEAK,
-                         "kernel_us": {LABELS[k]: v for k, v in pk.items()}}
-        log(f"[bench] sweep chunk={L}: {el / st * 1e3:.3f} ms/step")
-
-    graph_ms = None
-    if not args.no_graph:
-        g_el = time_chunkwise_graph(torch, d, args.chunk, args.steps, args.warmup)
-        graph_ms = g_el / args.steps * 1e3
-        log(f"[bench] chunkwise as a replayed HIP graph: {graph_ms:.3f} ms/step")
-
-    clock = None
-    if not args.no_clock:
-        clock = measure_clock(torch, d, args.chunk)
-        log(f"[bench] shader clock during the forward: {clock['under_load_mhz']:.0f} MHz "
-            f"(idle {clock['idle_mhz']:.0f} MHz, constant counter {clock['realtime_counter_mhz']:.1f} MHz)")
+    # ---- headline: cold step, warm beside it, per-kernel groups
+    log(f"[bench] chunkwise chunk={args.chunk}: {args.warmup} warmup, {args.steps} cold reps")
+    one, prof = chunkwise_callables(torch, d, args.chunk)
+    cold = timer.cold(one, args.steps, args.warmup)
+    warm = timer.warm(one, args.steps, args.warmup)
+    groups = timer.groups(prof, _lib.PROF_GROUPS, max(10, args.steps // 2), cold=True)
+    groups_warm = timer.groups(prof, _lib.PROF_GROUPS, max(10, args.steps // 2), cold=False)
+    ms_step = cold["median_ms"]
+    tok_s = B * T / (ms_step * 1e-3)
+    roof = roofline(nbytes, flops, groups["out"] * 1e-6, "out_kernel_fused")
+    roof["timing"] = "median cold kernel duration from events around the launch"
+    roof["kernel_us"] = groups["out"]
+    roof["kernel_us_warm"] = groups_warm["out"]
+    roof["frac_warm"] = nbytes / (groups_warm["out"] * 1e-6) / HBM_PEAK
+    pf = profile_figures("fused_kernel_7b_layer.md") or {}
+    roof["trace_us"] = pf.get("trace_avg_us")
+    roof["frac_trace"] = nbytes / (pf["trace_avg_us"] * 1e-6) / HBM_PEAK if "trace_avg_us" in pf else None
+    roof["traffic"] = pf.get("traffic_bytes_per_launch")
+    log(f"[bench] cold {ms_step:.3f} ms/step (warm {warm['wall_ms']:.3f}), {tok_s:.3e} tokens/s, "
+        f"kernels us cold {groups} warm {groups_warm}")
 
     out = {
         "metric": METRIC,
@@ -488,54 +611,134 @@ def main():
         "data": "synthetic (seeded PCG64 draws with the 7B-layer distributions)",
         "config": {"workload": "mLSTM chunkwise forward, 7B-layer shape", "B": B, "H": H, "T": T,
                    "d_qk": K, "d_v": V, "chunk": args.chunk, "tile": TILE,
-                   "inputs": "bf16 q/k/v/o, fp32 gates",
-                   "parallelism": "single GPU"},
+                   "inputs": "bf16 q/k/v/o, fp32 gates", "parallelism": "single GPU"},
+        "timing": {"cold": cold, "warm": warm,
+                   "protocol": "cold: 512 MiB scratch overwrite before each rep, events around the step; "
+                               "warm: back-to-back steps"},
         "mfma_frac": flops / (ms_step * 1e-3) / MFMA_BF16_PEAK,
-        "mfma_frac_chunk_independent": flops_ci / (ms_step * 1e-3) / MFMA_BF16_PEAK,
-        "hbm_frac_path": path_bytes / (ms_step * 1e-3) / HBM_PEAK,
-        "kernel_us": per_k,
+        "hbm_frac_step": nbytes / (ms_step * 1e-3) / HBM_PEAK,
+        "kernel_us": {LABELS[k]: v for k, v in groups.items()},
+        "kernel_us_warm": {LABELS[k]: v for k, v in groups_warm.items()},
         "roofline": roof,
-        "sweep": sweep,
-        "clock": clock,
-        "graph_ms_per_step": graph_ms,
     }
-    del d
+
+    if "sweep" in want:
+        sweep = {}
+        for L in [int(s) for s in args.sweep.split(",") if s]:
+            if L == args.chunk:
+                continue
+            o, p = chunkwise_callables(torch, d, L)
+            c = timer.cold(o, max(10, args.steps // 3), 2)
+            g = timer.groups(p, _lib.PROF_GROUPS, 10, cold=True)
+            sweep[str(L)] = {"ms_per_step": c["median_ms"], "tokens_per_s": B * T / (c["median_ms"] * 1e-3),
+                             "mfma_frac": flops / (c["median_ms"] * 1e-3) / MFMA_BF16_PEAK,
+                             "kernel_us": {LABELS[k]: v for k, v in g.items()}}
+            log(f"[bench] sweep chunk={L}: {c['median_ms']:.3f} ms/step cold")
+        out["sweep"] = sweep
+
+    if "graph" in want:
+        out["graph_ms_per_step"] = graph_ms(torch, d, args.chunk, args.steps, args.warmup)
+        log(f"[bench] chunkwise as a replayed HIP graph: {out['graph_ms_per_step']:.3f} ms/step (warm)")
+
+    if "clock" in want:
+        out["clock"] = measure_clock(torch, one)
+        log(f"[bench] shader clock during the forward: {out['clock']['under_load_mhz']:.0f} MHz")
+
+    if "bwd" in want:
+        log(f"[bench] backward chunk={args.bwd_chunk}")
+        o, p = backward_callables(torch, d, args.bwd_chunk)
+        c = timer.cold(o, max(10, args.steps // 3), 2)
+        g = timer.groups(p, _lib.BWD_PROF_GROUPS, 10, cold=True)
+        bb, bf = bwd_bytes(B, H, T, K, V), bwd_flops(B, H, T, K, V)
+        dom = max(g, key=g.get)
+        out["backward"] = {
+            "workload": f"mlstm_bwd_chunkwise, 7B-layer shape, chunk {args.bwd_chunk}, bf16",
+            "ms_per_step": c["median_ms"], "tokens_per_s": B * T / (c["median_ms"] * 1e-3),
+            "kernel_us": {BWD_LABELS[k]: v for k, v in g.items()},
+            "dominant_kernel": BWD_LABELS[dom],
+            "roofline": roofline(bb, bf, c["median_ms"] * 1e-3, "whole backward pass")}
+        log(f"[bench] backward {c['median_ms']:.3f} ms cold, kernels {g}")
+        del o, p
+
+    del d, one, prof
     torch.cuda.empty_cache()
 
-    if not args.no_decode:
+    if "mid" in want:
+        log("[bench] mid workload")
+        mc = MID
+        _, dm = make_device_inputs(torch, mc, "bf16", seed=0)
+        mb, mf = fwd_bytes(mc["B"], mc["H"], mc["T"], mc["d_qk"], mc["d_v"]), \
+            fwd_flops(mc["B"], mc["H"], mc["T"], mc["d_qk"], mc["d_v"])
+        res = {"workload": "mLSTM fwd B=4 H=8 T=2048 d_qk=d_v=128 bf16"}
+        for L in (64, 256):
+            o, _ = chunkwise_callables(torch, dm, L)
+            c = timer.cold(o, 20, 2)
+            res[f"chunkwise_{L}"] = {"ms_per_step": c["median_ms"],
+                                     "tokens_per_s": mc["B"] * mc["T"] / (c["median_ms"] * 1e-3),
+                                     "hbm_frac": mb / (c["median_ms"] * 1e-3) / HBM_PEAK,
+                                     "mfma_frac": mf / (c["median_ms"] * 1e-3) / MFMA_BF16_PEAK}
+        o = parallel_callable(torch, dm)
+        c = timer.cold(o, 20, 2)
+        res["parallel"] = {"ms_per_step": c["median_ms"],
+                           "tokens_per_s": mc["B"] * mc["T"] / (c["median_ms"] * 1e-3),
+                           "hbm_frac": mb / (c["median_ms"] * 1e-3) / HBM_PEAK}
+        out["mid"] = res
+        log(f"[bench] mid {res}")
+        del dm, o
+        torch.cuda.empty_cache()
+
+    if "long" in want:
+        log("[bench] long-context workload")
+        lc = LONG
+        _, dl = make_device_inputs(torch, lc, "bf16", seed=0)
+        lb, lf = fwd_bytes(lc["B"], lc["H"], lc["T"], lc["d_qk"], lc["d_v"]), \
+            fwd_flops(lc["B"], lc["H"], lc["T"], lc["d_qk"], lc["d_v"])
+        res = {"workload": "mLSTM fwd B=1 H=8 T=131072 d_qk=256 d_v=512 bf16", "algorithmic_bytes": lb}
+        for L in (64, 256, 1024):
+            o, p = chunkwise_callables(torch, dl, L)
+            c = timer.cold(o, 10, 2)
+            g = timer.groups(p, _lib.PROF_GROUPS, 5, cold=True)
+            res[f"chunk_{L}"] = {"ms_per_step": c["median_ms"],
+                                 "tokens_per_s": lc["B"] * lc["T"] / (c["median_ms"] * 1e-3),
+                                 "hbm_frac": lb / (c["median_ms"] * 1e-3) / HBM_PEAK,
+                                 "mfma_frac": lf / (c["median_ms"] * 1e-3) / MFMA_BF16_PEAK,
+                                 "kernel_us": {LABELS[k]: v for k, v in g.items()}}
+            log(f"[bench] long context chunk={L}: {c['median_ms']:.3f} ms cold")
+            del o, p
+        out["long_context"] = res
+        del dl
+        torch.cuda.empty_cache()
+
+    if "decode" in want:
         log(f"[bench] decode B={DECODE['B']} H={DECODE['H']} steps {args.decode_steps}")
-        el, k_us = time_decode(torch, M, ev, args.decode_steps, 20)
-        us_step = el / args.decode_steps * 1e6
+        wall_us, k_us = time_decode(torch, M, timer, args.decode_steps, 20)
         db = decode_bytes(DECODE["B"], DECODE["H"], DECODE["d_qk"], DECODE["d_v"])
         out["decode"] = {"workload": "mlstm_step B=64 H=8 d_qk=256 d_v=512 fp32 state",
-                         "us_per_step": us_step, "kernel_us": k_us,
-                         "tokens_per_s": DECODE["B"] / (us_step * 1e-6),
+                         "steps": args.decode_steps, "us_per_step": wall_us, "kernel_us": k_us,
+                         "tokens_per_s": DECODE["B"] / (wall_us * 1e-6),
                          "achieved_GBps": db / (k_us * 1e-6) / 1e9,
                          "hbm_frac": db / (k_us * 1e-6) / HBM_PEAK,
-                         "hbm_frac_wall": db / (us_step * 1e-6) / HBM_PEAK}
-        log(f"[bench] decode {us_step:.1f} us/step wall, kernel {k_us:.1f} us")
+                         "hbm_frac_wall": db / (wall_us * 1e-6) / HBM_PEAK}
+        log(f"[bench] decode {wall_us:.1f} us/step wall, kernel {k_us:.1f} us")
 
-    if not args.no_slstm:
-        B, H, T, D = SLSTM["B"], SLSTM["H"], SLSTM["T"], SLSTM["D"]
-        log(f"[bench] sLSTM B={B} H={H} T={T} D={D}")
-        sec, pre, R = time_slstm(torch, 10, 2)
-        fl = slstm_flops(B, H, T, D)
-        # one workgroup per sequence-head runs on one CU: the launch can use at
-        # most B * H of the 256 CUs' float32 peak
-        peak = FP32_PEAK * min(1.0, B * H / 256)
-        out["slstm"] = {"workload": f"slstm_fwd B={B} H={H} D={D} T={T} float32",
-                        "ms_per_call": sec * 1e3, "us_per_step": sec / T * 1e6,
-                        "tokens_per_s": B * T / sec,
-                        "roofline": {"bound": "alu", "achieved": fl / sec / 1e12, "peak": peak / 1e12,
-                                     "unit": "TFLOP/s", "frac": fl / sec / peak,
-                                     "note": "float32 vector peak of the B*H CUs the launch occupies"}}
-        log(f"[bench] sLSTM {sec * 1e3:.3f} ms per call, {sec / T * 1e6:.3f} us per step")
-        if not args.no_cpu_baseline:
+    if "slstm" in want:
+        Bs, Hs, Ts, Ds = SLSTM["B"], SLSTM["H"], SLSTM["T"], SLSTM["D"]
+        log(f"[bench] sLSTM B={Bs} H={Hs} T={Ts} D={Ds}")
+        sec, pre, R = time_slstm(torch, timer, 10)
+        fl = slstm_flops(Bs, Hs, Ts, Ds)
+        out["slstm"] = {"workload": f"slstm_fwd B={Bs} H={Hs} D={Ds} T={Ts} float32",
+                        "ms_per_call": sec * 1e3, "us_per_step": sec / Ts * 1e6,
+                        "tokens_per_s": Bs * Ts / sec,
+                        "roofline": {"bound": "alu", "achieved": fl / sec / 1e12, "peak": FP32_PEAK / 1e12,
+                                     "unit": "TFLOP/s", "frac": fl / sec / FP32_PEAK,
+                                     "note": "whole-chip float32 vector peak; the launch occupies "
+                                             f"{Bs * Hs} of 256 CUs"}}
+        if "cpu" in want:
             out["slstm"]["cpu_baseline"] = slstm_cpu_baseline(pre, R)
 
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
+    if "cpu" in want:
+        log("[bench] cpu baseline (C oracle)")
+        out["cpu_baseline"] = cpu_baseline(x)
     print(json.dumps(out), flush=True)
 
 
