@@ -331,7 +331,7 @@ namespace {
 
 struct BwdLayout {
   WsLayout fw;   // gate prefix data and the forward's chunk-start states
-  size_t G, dz, qdq, Es, es, Ms, total;
+  size_t G, dz, qdq, Es, es, Ms, L0, L0e, total;
 };
 
 BwdLayout layout_bwd(int64_t BH, int64_t T, int64_t Nc, int64_t K, int64_t V, int64_t elem) {
@@ -345,6 +345,8 @@ BwdLayout layout_bwd(int64_t BH, int64_t T, int64_t Nc, int64_t K, int64_t V, in
   b.Es = take(BH * Nc * V * K * 4);
   b.es = take(BH * Nc * K * 4);
   b.Ms = take(BH * Nc * 8);
+  b.L0 = take(BH * V * K * 4);
+  b.L0e = take(BH * K * 4);
   b.total = off;
   return b;
 }
@@ -425,7 +427,7 @@ int bwd_chunkwise(const mlstm_bwd_args* a, int chunk, void* workspace, size_t wo
   b.marks = marks;
   const mlstm_impl::GateBuffers none_gb{};
   const mlstm_impl::ChunkStates none_cs{nullptr, nullptr, nullptr};
-  const mlstm_impl::BwdBuffers none_bb{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  const mlstm_impl::BwdBuffers none_bb{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   if (a->T == 0) return hip_status(mlstm_impl::launch_bwd(b, none_gb, none_cs, none_bb, s), "backward");
   const size_t need = bwd_workspace_size(a, chunk);
   if (!workspace) return fail(MLSTM_ERR_WORKSPACE, "workspace is NULL");
@@ -464,6 +466,8 @@ int bwd_chunkwise(const mlstm_bwd_args* a, int chunk, void* workspace, size_t wo
   bb.Es = ws + w.Es;
   bb.es = reinterpret_cast<float*>(ws + w.es);
   bb.Ms = reinterpret_cast<double*>(ws + w.Ms);
+  bb.L0 = reinterpret_cast<float*>(ws + w.L0);
+  bb.L0e = reinterpret_cast<float*>(ws + w.L0e);
   // the forward's gate prefix sums and chunk-start states (the K_GATE and
   // K_STATE event slots coincide with the backward's first two groups)
   mlstm_impl::FwdLaunch f{};

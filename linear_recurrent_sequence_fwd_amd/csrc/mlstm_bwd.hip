@@ -34,9 +34,11 @@
 //                     Q K^T over the chunk's key tiles, then g, dz, do~, dq
 //                     (G V^T and (P o (G V^T + dz)) K on MFMA, plus the
 //                     carried-state term G C~); writes g for the next two
-//   bwd_state_kernel  per (head, 64 x 64 tile of A): walks the chunks from
-//                     the last to the first, storing each chunk's end adjoint
-//                     and accumulating G^T diag(w) Q on MFMA
+//   bwd_local_kernel  per (head, 64 x 64 tile of A, chunk): the chunk's own
+//                     share of the adjoint at its start, G^T diag(w) Q on MFMA
+//   bwd_fold_kernel   per head and element group: chains the shares from
+//                     the last chunk to the first into every chunk's end
+//                     adjoint (float32), and the initial state's gradient
 //   bwd_dkv_kernel    per (head, 64-key tile): the end adjoint's term, then
 //                     the chunk's later query tiles: S = Q K^T, G V^T, and
 //                     dk += (P o (G V^T + dz))^T Q, dv += (P o S)^T G
@@ -193,6 +195,8 @@ struct BwdArgs {
   float* Es;                             // end adjoint of every chunk [BH][Nc][V][K], float32
   float* es;                             // [BH][Nc][K]
   double* Ms;                            // its log scale [BH][Nc] (-inf: zero)
+  float* L0;                             // chunk 0's share [BH][V][K] (initial state's gradient)
+  float* L0e;                            // [BH][K]
   const float *C0, *n0, *m0;             // initial state, or null
   float *dC0, *dn0, *dm0;                // its gradient, or null
   int zero_first;                        // no initial state: chunk 0 starts from zero
@@ -514,19 +518,19 @@ struct RsLds {
   static constexpr int bytes = oF + 6 * kTile * 4;
 };
 
-// One workgroup per (head, 64 v x 64 d tile), four waves of 32 x 32. Chunk c
-// (last to first): store the carried end adjoint (A, M) in float32, then add
-// the chunk's tokens s before its first zero forget gate, w_s g_s q_s^T with
-// w_s = exp(r_first - r_s) <= 1 (log scale -r_first), and fold:
-// M' = max(-r_first, g_c + M) (the second only when the chunk has no zero
-// forget gate), A' = exp(-r_first - M') acc + exp(g_c + M - M') A. The
-// normaliser adjoint a (v-tile-0 workgroups) is the same sum with g_s
-// replaced by dz_s, on the vector ALU in float32. After chunk 0 the carried
-// adjoint belongs to the initial state: dC~0 = exp(m0 + M) A.
+// One workgroup per (head, 64 v x 64 d tile, chunk c), four waves of 32 x 32:
+// chunk c's own share of the adjoint at its start, the sum over its tokens s
+// before its first zero forget gate of w_s g_s q_s^T with
+// w_s = exp(r_first - r_s) <= 1 (its log scale is -r_first), float32, into
+// the slot of chunk c - 1 (chunk 0's, wanted for the initial state's
+// gradient only, into L0). The normaliser part (v-tile-0 workgroups) is the
+// same sum with g_s replaced by dz_s, on the vector ALU. Chunks are
+// independent here; bwd_fold_kernel chains them.
 template <typename TI, int K>
-__global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) void bwd_local_kernel(BwdArgs a) {
   using L = RsLds<TI, K>;
   constexpr int P = L::P;
+  constexpr int KT = K / 64;
   __shared__ __attribute__((aligned(16))) char smem[L::bytes];
   TI* sG = reinterpret_cast<TI*>(smem + L::oG);
   TI* sQ = reinterpret_cast<TI*>(smem + L::oQ);
@@ -535,9 +539,11 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
   float* s_ep = s_w + 128;
 
   const int64_t T = a.T, BH = a.BH, V = a.V;
+  const int ntile = KT * (int)(V / 64);
   const int64_t bh = blockIdx.x % BH;
-  const int tile = (int)(blockIdx.x / BH);
-  constexpr int KT = K / 64;
+  const int64_t rest = blockIdx.x / BH;
+  const int tile = (int)(rest % ntile);
+  const int64_t c = rest / ntile + (a.dC0 ? 0 : 1);
   const int kt = tile % KT, vt = tile / KT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
@@ -546,126 +552,132 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(BwdArgs a) {
 
   const TI* qg = static_cast<const TI*>(a.q) + bh * T * K + 64 * kt;
   const TI* Gg = static_cast<const TI*>(a.G) + bh * T * V + 64 * vt;
-  const bool want_init = a.dC0 != nullptr;
-  const int64_t c_last = want_init ? 0 : 1;
+  const int64_t t0 = c * a.L;
+  const int Lc = (int)min((int64_t)a.L, T - t0);
+  const bool has_state = c > 0 || !a.zero_first;
+  const double m_prev = has_state ? a.ms[bh * a.Nc + c] : 0.0;
+  const double r_first = row_stab(a, bh, t0, has_state, m_prev, nullptr);
 
-  f32x4 acc[2][2], lacc[2][2];
+  f32x4 lacc[2][2];
 #pragma unroll
   for (int x = 0; x < 2; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float e_acc = 0.f;   // threads < 64 of e-tiles: a[64 kt + tid]
-  double M = -INFINITY;
-
-  for (int64_t c = a.Nc - 1; c >= 0; --c) {
-    // store the carried end adjoint of chunk c
-    {
-      float* Es = a.Es + (bh * a.Nc + c) * V * K;
+    for (int y = 0; y < 2; ++y) lacc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float le = 0.f;
+  for (int jb = 0; jb < Lc; jb += kTile) {
+    const int64_t tb = t0 + jb;
+    const int nv = min(kTile, Lc - jb);
+    if (jb > 0) __syncthreads();   // previous block's tiles and weights consumed
+    if (tid < kTile) {
+      float wt = 0.f, wdz = 0.f;
+      if (tid < nv && a.gb.rs[bh * T + tb + tid] < 0) {
+        const double r = row_stab(a, bh, tb + tid, has_state, m_prev, nullptr);
+        wt = expf((float)(r_first - r));
+        wdz = wt * a.dz[bh * T + tb + tid];
+      }
+      s_w[tid] = wt;
+      s_wdz[tid] = wdz;
+    }
+    __syncthreads();
+    // stage w g[tokens][64 v] and q[tokens][64 d]. The weight goes on g: a
+    // rounding of w_s g_s perturbs each term in proportion to itself, so the
+    // adjoint's products with later keys (which can cancel strongly) keep
+    // their accuracy; q stays exact.
+    for (int it = tid; it < kTile * 8; it += kThreads) {
+      const int row = it >> 3, cv = it & 7;
+      vec8<TI> gv = zero_v8<TI>(), qv = zero_v8<TI>();
+      if (row < nv) {
+        const vec8<TI> g8 = load8(Gg + (tb + row) * V + 8 * cv);
+        qv = load8(qg + (tb + row) * K + 8 * cv);
+        const float wt = s_w[row];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gv[e] = from_f32<TI>(to_f32(g8[e]) * wt);
+      }
+      store8(sG + row * P + 8 * cv, gv);
+      store8(sQ + row * P + 8 * cv, qv);
+    }
+    if (e_tile) {   // normaliser part: four threads per d, 16 tokens each
+      const int d = tid & 63, part = tid >> 6;
+      float sum = 0.f;
+      for (int row = 16 * part; row < 16 * part + 16; ++row)
+        if (row < nv) sum += s_wdz[row] * to_f32(qg[(tb + row) * K + d]);
+      s_ep[part * 64 + d] = sum;
+    }
+    __syncthreads();
+    if (e_tile && tid < kTile) le += s_ep[tid] + s_ep[64 + tid] + s_ep[128 + tid] + s_ep[192 + tid];
+#pragma unroll
+    for (int kk = 0; kk < kTile; kk += 32) {
+      vec8<TI> A[2], B[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) A[x] = frag_cols(sG, P, kk, 32 * wv + 16 * x);
+#pragma unroll
+      for (int y = 0; y < 2; ++y) B[y] = frag_cols(sQ, P, kk, 32 * wk + 16 * y);
 #pragma unroll
       for (int x = 0; x < 2; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
-          const int64_t vv = 64 * vt + 32 * wv + 16 * x + 4 * g;
-          const int dd = 64 * kt + 32 * wk + 16 * y + i;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) Es[(vv + r) * K + dd] = acc[x][y][r];
-        }
-      if (e_tile && tid < kTile) a.es[(bh * a.Nc + c) * K + 64 * kt + tid] = e_acc;
-      if (tile == 0 && tid == 0) a.Ms[bh * a.Nc + c] = M;
+        for (int y = 0; y < 2; ++y) lacc[x][y] = mma32(A[x], B[y], lacc[x][y]);
     }
-    if (c < c_last) break;
-    const int64_t t0 = c * a.L;
-    const int Lc = (int)min((int64_t)a.L, T - t0);
+  }
+  float* dst = c > 0 ? a.Es + (bh * a.Nc + c - 1) * V * K : a.L0 + bh * V * K;
+  float* edst = c > 0 ? a.es + (bh * a.Nc + c - 1) * K : a.L0e + bh * K;
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int64_t vv = 64 * vt + 32 * wv + 16 * x + 4 * g;
+      const int dd = 64 * kt + 32 * wk + 16 * y + i;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(vv + r) * K + dd] = lacc[x][y][r];
+    }
+  if (e_tile && tid < kTile) edst[64 * kt + tid] = le;
+}
+
+// The chunks' end adjoints from their local shares, last chunk to first:
+// one thread per four consecutive elements of a head's d_v x d_qk adjoint
+// (and d_qk / 4 threads for its normaliser part). With A = 0, M = -inf after
+// the last chunk, for c = Nc-1 .. 1: the slot of chunk c receives A (the
+// adjoint at its end), and with chunk c's local share Lc (in slot c - 1)
+//   M' = max(-r_first(c), g_c + M if chunk c has no zero forget gate),
+//   A' = exp(-r_first(c) - M') Lc + exp(g_c + M - M') A;
+// slot 0 receives the last A. With the initial state's gradient wanted, one
+// more step with chunk 0's share gives dC~0 = exp(m0 + M) A (and dn~0).
+__global__ __launch_bounds__(kThreads) void bwd_fold_kernel(BwdArgs a) {
+  const int64_t K = a.K, V = a.V, Nc = a.Nc;
+  const int64_t vk4 = V * K / 4, k4 = K / 4, per_head = vk4 + k4;
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (gid >= a.BH * per_head) return;
+  const int64_t bh = gid / per_head, x = gid % per_head;
+  const bool is_e = x >= vk4;
+  float* base = is_e ? a.es + bh * Nc * K + 4 * (x - vk4) : a.Es + bh * Nc * V * K + 4 * x;
+  const int64_t stride = is_e ? K : V * K;
+  f32x4 A = {0.f, 0.f, 0.f, 0.f};
+  double M = -INFINITY;
+  auto fold = [&](int64_t c, const f32x4& Lc) {
     const bool has_state = c > 0 || !a.zero_first;
-    const double m_prev = has_state ? a.ms[bh * a.Nc + c] : 0.0;
-    const double r_first = row_stab(a, bh, t0, has_state, m_prev, nullptr);
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int y = 0; y < 2; ++y) lacc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float le = 0.f;
-    for (int jb = 0; jb < Lc; jb += kTile) {
-      const int64_t tb = t0 + jb;
-      const int nv = min(kTile, Lc - jb);
-      __syncthreads();   // previous block's tiles and weights consumed
-      if (tid < kTile) {
-        float wt = 0.f, wdz = 0.f;
-        if (tid < nv && a.gb.rs[bh * T + tb + tid] < 0) {
-          const double r = row_stab(a, bh, tb + tid, has_state, m_prev, nullptr);
-          wt = expf((float)(r_first - r));
-          wdz = wt * a.dz[bh * T + tb + tid];
-        }
-        s_w[tid] = wt;
-        s_wdz[tid] = wdz;
-      }
-      __syncthreads();
-      // stage w g[tokens][64 v] and q[tokens][64 d]. The weight goes on g: a
-      // rounding of w_s g_s perturbs each term in proportion to itself, so
-      // the adjoint's products with later keys (which can cancel strongly)
-      // keep their accuracy; q stays exact.
-      for (int it = tid; it < kTile * 8; it += kThreads) {
-        const int row = it >> 3, cv = it & 7;
-        vec8<TI> gv = zero_v8<TI>(), qv = zero_v8<TI>();
-        if (row < nv) {
-          const vec8<TI> g8 = load8(Gg + (tb + row) * V + 8 * cv);
-          qv = load8(qg + (tb + row) * K + 8 * cv);
-          const float wt = s_w[row];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) gv[e] = from_f32<TI>(to_f32(g8[e]) * wt);
-        }
-        store8(sG + row * P + 8 * cv, gv);
-        store8(sQ + row * P + 8 * cv, qv);
-      }
-      if (e_tile) {   // normaliser adjoint: four threads per d, 16 tokens each
-        const int d = tid & 63, part = tid >> 6;
-        float s = 0.f;
-        for (int row = 16 * part; row < 16 * part + 16; ++row)
-          if (row < nv) s += s_wdz[row] * to_f32(qg[(tb + row) * K + d]);
-        s_ep[part * 64 + d] = s;
-      }
-      __syncthreads();
-      if (e_tile && tid < kTile) le += s_ep[tid] + s_ep[64 + tid] + s_ep[128 + tid] + s_ep[192 + tid];
-#pragma unroll
-      for (int kk = 0; kk < kTile; kk += 32) {
-        vec8<TI> A[2], B[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) A[x] = frag_cols(sG, P, kk, 32 * wv + 16 * x);
-#pragma unroll
-        for (int y = 0; y < 2; ++y) B[y] = frag_cols(sQ, P, kk, 32 * wk + 16 * y);
-#pragma unroll
-        for (int x = 0; x < 2; ++x)
-#pragma unroll
-          for (int y = 0; y < 2; ++y) lacc[x][y] = mma32(A[x], B[y], lacc[x][y]);
-      }
-    }
-    // fold the chunk into the carried adjoint
-    const bool open = a.gb.R[bh * a.Nc + c] < 0;
-    const double gc = a.gb.g[bh * a.Nc + c];
-    const double Mc = (open && M != -INFINITY) ? gc + M : -INFINITY;
-    const double Mloc = -r_first;
+    const double m_prev = has_state ? a.ms[bh * Nc + c] : 0.0;
+    const double Mloc = -row_stab(a, bh, c * a.L, has_state, m_prev, nullptr);
+    const bool open = a.gb.R[bh * Nc + c] < 0;
+    const double Mc = (open && M != -INFINITY) ? a.gb.g[bh * Nc + c] + M : -INFINITY;
     const double Mn = fmax(Mloc, Mc);
     const float al = expf((float)(Mloc - Mn));
     const float be = Mc == -INFINITY ? 0.f : expf((float)(Mc - Mn));
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int y = 0; y < 2; ++y) acc[x][y] = al * lacc[x][y] + be * acc[x][y];
-    e_acc = al * le + be * e_acc;
+    A = al * Lc + be * A;
     M = Mn;
+  };
+  for (int64_t c = Nc - 1; c >= 1; --c) {
+    *reinterpret_cast<f32x4*>(base + c * stride) = A;
+    if (x == 0) a.Ms[bh * Nc + c] = M;
+    fold(c, *reinterpret_cast<const f32x4*>(base + (c - 1) * stride));
   }
-  if (want_init) {
+  *reinterpret_cast<f32x4*>(base) = A;
+  if (x == 0) a.Ms[bh * Nc] = M;
+  if (a.dC0) {
+    const float* l0 = is_e ? a.L0e + bh * K + 4 * (x - vk4) : a.L0 + bh * V * K + 4 * x;
+    fold(0, *reinterpret_cast<const f32x4*>(l0));
     const double m0 = a.C0 ? (double)a.m0[bh] : 0.0;
     const float sc = M == -INFINITY ? 0.f : expf((float)(m0 + M));
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int y = 0; y < 2; ++y) {
-        const int64_t vv = 64 * vt + 32 * wv + 16 * x + 4 * g;
-        const int dd = 64 * kt + 32 * wk + 16 * y + i;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) a.dC0[bh * V * K + (vv + r) * K + dd] = sc * acc[x][y][r];
-      }
-    if (e_tile && tid < kTile) a.dn0[bh * K + 64 * kt + tid] = sc * e_acc;
+    float* d0 = is_e ? a.dn0 + bh * K + 4 * (x - vk4) : a.dC0 + bh * V * K + 4 * x;
+    *reinterpret_cast<f32x4*>(d0) = sc * A;
   }
 }
 
@@ -930,55 +942,63 @@ __global__ __launch_bounds__(kBT) void bwd_dkv_kernel(BwdArgs a) {
 // One workgroup per head. dF_t = q_t . dq_t - k_t . dk_t; the gradient of
 // log f_l is the sum of dF_t from l up to the next zero forget gate
 // (exclusive), and 0 at a zero forget gate itself and, without an initial
-// state, at the first token; df~ = dlog f sigmoid(-f~).
-// Each thread takes a contiguous run of tokens; thread 0 chains the runs
-// from the right. Float64 sums. Also dm0 = <dC~0, C~0> + dn~0 . n~0.
+// state, at the first token; df~ = dlog f sigmoid(-f~). Each thread takes a
+// contiguous run of tokens, thread p the p-th run from the end. A run maps
+// the sum flowing into it from the right to the sum flowing out of its left
+// end by an affine map c -> alpha c + beta (alpha = 0 where a zero forget
+// gate blocks the flow); a scan of the composed maps over the threads gives
+// every run its inflow. Float64 sums. Also dm0 = <dC~0, C~0> + dn~0 . n~0.
 __global__ __launch_bounds__(kThreads) void bwd_gate_kernel(BwdArgs a) {
-  __shared__ double s_loc[kThreads];
-  __shared__ int s_open[kThreads];
-  __shared__ double s_carry[kThreads];
+  __shared__ double s_al[kThreads / 64], s_be[kThreads / 64];
   __shared__ double s_red[kThreads / 64];
   const int64_t bh = blockIdx.x;
   const int64_t T = a.T;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t E = (T + kThreads - 1) / kThreads;
-  const int64_t lo = min((int64_t)tid * E, T), hi = min(lo + E, T);
+  const int64_t run_idx = kThreads - 1 - tid;
+  const int64_t lo = min(run_idx * E, T), hi = min(lo + E, T);
   const float* fp = a.f_pre + bh * T;
   const float* qd = a.qdq + bh * T;
   const float* di = a.di + bh * T;
-  // this run's sum from lo up to its first zero forget gate after lo, with no carry
-  double run = 0.0;
-  int open = 1;
+  auto blocked = [&](int64_t l) { return fp[l] == -INFINITY || (l == 0 && a.zero_first); };
+  // the run's own map: inflow c at hi - 1 -> outflow at lo - 1
+  double be = 0.0, al = 1.0;
   for (int64_t l = hi - 1; l >= lo; --l) {
-    const bool reset = fp[l] == -INFINITY;
-    run += (double)qd[l] - (double)di[l];
-    if (reset) {
-      if (l > lo) open = 0;
-      run = (l == lo) ? run : 0.0;
+    const double v = (double)qd[l] - (double)di[l];
+    if (blocked(l)) {
+      al = 0.0;
+      be = 0.0;
+    } else {
+      be += v;   // (c -> al c + be) then + v
     }
   }
-  s_loc[tid] = run;
-  s_open[tid] = open;
-  __syncthreads();
-  if (tid == 0) {
-    double carry = 0.0;   // flow into the run's last token from the right
-    for (int p = kThreads - 1; p >= 0; --p) {
-      const int64_t plo = min((int64_t)p * E, T), phi = min(plo + E, T);
-      s_carry[p] = carry;
-      if (plo < phi) {
-        const double sa = s_loc[p] + (s_open[p] ? carry : 0.0);
-        carry = (fp[plo] == -INFINITY) ? 0.0 : sa;
-      }
+  // inclusive scan over threads (earlier threads = later runs): X_t = m_t o X_{t-1}
+  double A_ = al, B_ = be;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double ao = __shfl_up(A_, d, 64), bo = __shfl_up(B_, d, 64);
+    if (lane >= d) {
+      B_ = A_ * bo + B_;
+      A_ = A_ * ao;
     }
   }
+  if (lane == 63) { s_al[w] = A_; s_be[w] = B_; }
   __syncthreads();
-  run = s_carry[tid];
+  // the composed map of all earlier waves (applied first)
+  double Aw = 1.0, Bw = 0.0;
+  for (int q = 0; q < w; ++q) {
+    Bw = s_al[q] * Bw + s_be[q];
+    Aw = s_al[q] * Aw;
+  }
+  // exclusive: the map of the threads before this one, applied to 0
+  double Ae = __shfl_up(A_, 1, 64), Bx = __shfl_up(B_, 1, 64);
+  if (lane == 0) { Ae = 1.0; Bx = 0.0; }
+  const double carry = Ae * Bw + Bx;   // (excl o earlier waves)(0)
+  (void)Aw;
+  double run = carry;
   for (int64_t l = hi - 1; l >= lo; --l) {
     const double val = (double)qd[l] - (double)di[l] + run;
-    // a zero forget gate passes no gradient; neither does the first token's
-    // without an initial state (it only scales the zero state), where the sum
-    // is zero up to rounding
-    if (fp[l] == -INFINITY || (l == 0 && a.zero_first)) {
+    if (blocked(l)) {
       a.df[bh * T + l] = 0.f;
       run = 0.0;
     } else {
@@ -1018,8 +1038,14 @@ hipError_t run_bwd(const BwdLaunch& b, const BwdArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   mark_before(b.marks, B_STATE, s);
-  hipLaunchKernelGGL((bwd_state_kernel<TI, K>), dim3((unsigned)(b.BH * (K / 64) * (V / 64))), dim3(kThreads), 0,
-                     s, a);
+  const int64_t nloc = b.Nc - (b.dC0 ? 0 : 1);   // chunks whose share is needed
+  if (nloc > 0) {
+    hipLaunchKernelGGL((bwd_local_kernel<TI, K>), dim3((unsigned)(b.BH * (K / 64) * (V / 64) * nloc)),
+                       dim3(kThreads), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  const int64_t nfold = b.BH * (V * K / 4 + K / 4);
+  hipLaunchKernelGGL(bwd_fold_kernel, dim3((unsigned)((nfold + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, a);
   mark_after(b.marks, B_STATE, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   mark_before(b.marks, B_DKV, s);
@@ -1070,6 +1096,7 @@ hipError_t launch_bwd(const BwdLaunch& b, const GateBuffers& gb, const ChunkStat
   a.Cs = static_cast<const float*>(cs.Cs); a.ns = cs.ns; a.ms = cs.ms;
   a.G = bb.G; a.dz = bb.dz; a.qdq = bb.qdq;
   a.Es = static_cast<float*>(bb.Es); a.es = bb.es; a.Ms = bb.Ms;
+  a.L0 = bb.L0; a.L0e = bb.L0e;
   a.C0 = b.C0; a.n0 = b.n0; a.m0 = b.m0;
   a.dC0 = b.dC0; a.dn0 = b.dn0; a.dm0 = b.dm0;
   a.zero_first = b.C0 == nullptr;

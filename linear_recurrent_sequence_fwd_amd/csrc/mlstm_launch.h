@@ -105,6 +105,8 @@ struct BwdBuffers {
   void* Es;
   float* es;
   double* Ms;
+  float* L0;    // chunk 0's share of the adjoint [BH][V][K] (initial state's gradient)
+  float* L0e;   // [BH][K]
 };
 bool bwd_supported(int bf16, int64_t K, int64_t V);
 hipError_t launch_bwd(const BwdLaunch& b, const GateBuffers& gb, const ChunkStates& cs, const BwdBuffers& bb,
