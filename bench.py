@@ -567,8 +567,12 @@ def main():
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
+        for _ in range(3):
+            _lib.copy_lds(src, dst)
         torch.cuda.synchronize()
-        log(f"[bench] calibration copy: {n} bytes read and written per launch, 3 launches")
+        assert bool(torch.equal(src, dst))
+        log(f"[bench] calibration copies: {n} bytes read and written per launch, 3 plain copies and "
+            f"3 direct-to-LDS copies")
         del src, dst
 
     log(f"[bench] inputs 7B-layer B={B} H={H} T={T} d_qk={K} d_v={V} bf16")

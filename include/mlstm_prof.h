@@ -71,6 +71,18 @@ int mlstm_prof_step(const mlstm_step_args* args, void* stream, void* before, voi
  */
 int mlstm_clock_probe(unsigned long long* ticks, int iters, void* stream);
 
+/*
+ * A copy of `bytes` (a positive multiple of 16384) from device memory src to
+ * device memory dst through LDS with direct-to-LDS loads (global_load_lds,
+ * 16 bytes per lane, the instruction the fused kernels stage their tiles
+ * with) and 16-byte vector stores: a kernel of known traffic for calibrating
+ * the HBM byte counters (FETCH_SIZE, WRITE_SIZE) on that load path.
+ * Asynchronous on `stream`; MLSTM_ERR_NULLPTR, MLSTM_ERR_BAD_SHAPE,
+ * MLSTM_ERR_MISALIGNED (16 bytes) or MLSTM_ERR_ALIAS (overlap) before
+ * anything is enqueued.
+ */
+int mlstm_prof_copy_lds(const void* src, void* dst, size_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

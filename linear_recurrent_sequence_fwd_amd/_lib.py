@@ -121,6 +121,8 @@ def lib() -> ctypes.CDLL:
         L.mlstm_prof_fwd_chunkwise.restype = c_int
         L.mlstm_prof_step.argtypes = [P(StepArgs), c_void_p, c_void_p, c_void_p]
         L.mlstm_prof_step.restype = c_int
+        L.mlstm_prof_copy_lds.argtypes = [c_void_p, c_void_p, c_size_t, c_void_p]
+        L.mlstm_prof_copy_lds.restype = c_int
         L.mlstm_clock_probe.argtypes = [c_void_p, c_int, c_void_p]
         L.mlstm_clock_probe.restype = c_int
         L.slstm_fwd.argtypes = [P(SlstmArgs), c_void_p]
@@ -383,6 +385,15 @@ def clock_probe(ticks, iters: int, stream=None) -> None:
     import torch
     _require(ticks, "ticks", (4,), torch.int64)
     _check(lib().mlstm_clock_probe(_ptr(ticks), int(iters), _stream(stream)), "mlstm_clock_probe")
+
+
+def copy_lds(src, dst, stream=None) -> None:
+    """Direct-to-LDS copy of src into dst (device tensors of equal byte size,
+    a multiple of 16 KiB): the counter-calibration kernel of mlstm_prof.h."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size in bytes")
+    _check(lib().mlstm_prof_copy_lds(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "mlstm_prof_copy_lds")
 
 
 def slstm_fwd(pre, R, state=None, want_state=False, h=None, stream=None):

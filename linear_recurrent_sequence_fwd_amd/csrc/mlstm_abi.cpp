@@ -619,6 +619,17 @@ int mlstm_clock_probe(unsigned long long* ticks, int iters, void* stream) {
   return hip_status(mlstm_impl::launch_clock_probe(ticks, iters, static_cast<hipStream_t>(stream)), "clock probe");
 }
 
+int mlstm_prof_copy_lds(const void* src, void* dst, size_t bytes, void* stream) {
+  g_last_error.clear();
+  if (!src || !dst) return fail(MLSTM_ERR_NULLPTR, "src and dst are required");
+  if (bytes == 0 || bytes % 16384 != 0) return fail(MLSTM_ERR_BAD_SHAPE, "bytes must be a positive multiple of 16384");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(MLSTM_ERR_MISALIGNED, "src and dst must be 16-byte aligned");
+  if (overlap(make_range("src", src, (int64_t)bytes), make_range("dst", dst, (int64_t)bytes)))
+    return fail(MLSTM_ERR_ALIAS, "dst overlaps src");
+  return hip_status(mlstm_impl::launch_lds_copy(src, dst, (int64_t)bytes, static_cast<hipStream_t>(stream)),
+                    "direct-to-LDS copy");
+}
+
 int mlstm_prof_fwd_chunkwise(const mlstm_fwd_args* a, int chunk, void* workspace, size_t workspace_bytes,
                              void* stream, void* const* events) {
   if (!events) return fail(MLSTM_ERR_NULLPTR, "events is NULL");

@@ -812,6 +812,39 @@ __global__ __launch_bounds__(64) void clock_probe_kernel(unsigned long long* tic
   }
 }
 
+// Direct-to-LDS copy (counter calibration): each workgroup of 256 threads
+// moves 16 KiB per iteration; every lane issues four 16-byte global_load_lds
+// (the same instruction the fused kernels stage their tiles with), then the
+// tile is read back from LDS and stored with 16-byte vector stores.
+typedef __attribute__((address_space(1))) void cal_global_void;
+typedef __attribute__((address_space(3))) void cal_lds_void;
+__global__ __launch_bounds__(256) void lds_copy_kernel(const char* src, char* dst, int64_t nblk) {
+  __shared__ __attribute__((aligned(16))) char buf[16384];
+  const int tid = threadIdx.x, w = tid >> 6;
+  for (int64_t blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+    const char* s = src + blk * 16384;
+    char* d = dst + blk * 16384;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      __builtin_amdgcn_global_load_lds((cal_global_void*)(s + k * 4096 + tid * 16),
+                                       (cal_lds_void*)(buf + k * 4096 + w * 1024), 16, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<f32x4*>(d + k * 4096 + tid * 16) = *reinterpret_cast<const f32x4*>(buf + k * 4096 + tid * 16);
+    __syncthreads();
+  }
+}
+
+hipError_t launch_lds_copy(const void* src, void* dst, int64_t bytes, hipStream_t s) {
+  const int64_t nblk = bytes / 16384;
+  const int64_t grid = nblk < 2048 ? nblk : 2048;
+  hipLaunchKernelGGL(lds_copy_kernel, dim3((unsigned)grid), dim3(256), 0, s, static_cast<const char*>(src),
+                     static_cast<char*>(dst), nblk);
+  return hipGetLastError();
+}
+
 hipError_t launch_clock_probe(unsigned long long* ticks, int iters, hipStream_t s) {
   hipLaunchKernelGGL(clock_probe_kernel, dim3(1), dim3(64), 0, s, ticks, iters);
   return hipGetLastError();

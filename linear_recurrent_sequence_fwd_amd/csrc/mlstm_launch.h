@@ -140,6 +140,8 @@ hipError_t launch_step(const StepLaunch& a, hipStream_t s);
 // one sleeping wave; ticks[0..1]: shader-clock counter, ticks[2..3]:
 // constant-rate counter, at its start and end
 hipError_t launch_clock_probe(unsigned long long* ticks, int iters, hipStream_t s);
+// direct-to-LDS copy of `bytes` (a positive multiple of 16 KiB) for counter calibration
+hipError_t launch_lds_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 
 // bfloat16 kernels with transposed LDS operand loads (mlstm_bf16.hip). The
 // state pass takes any d_v multiple of 64; the output kernel needs

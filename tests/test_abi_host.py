@@ -36,8 +36,8 @@ def test_library_exports_every_declared_symbol():
     assert lib.mlstm_abi_version() == 2
     assert "mlstm_bwd_chunkwise" in names and "mlstm_bwd_chunkwise_workspace_size" in names
     prof = declared_functions(PROF_HEADER)
-    assert prof == ["mlstm_clock_probe", "mlstm_prof_bwd_chunkwise", "mlstm_prof_fwd_chunkwise",
-                    "mlstm_prof_step"]
+    assert prof == ["mlstm_clock_probe", "mlstm_prof_bwd_chunkwise", "mlstm_prof_copy_lds",
+                    "mlstm_prof_fwd_chunkwise", "mlstm_prof_step"]
     for n in prof:
         assert hasattr(lib, n), n
     # the product header declares only the method's calls and the status/version helpers
@@ -461,3 +461,13 @@ def test_backward_empty_sequence_without_init_grad_is_a_noop():
     lib = L.lib()
     a = fake_bwd(T=0)
     assert lib.mlstm_bwd_chunkwise(ctypes.byref(a), 64, None, 0, None) == OK
+
+
+def test_lds_copy_validation():
+    lib = L.lib()
+    A, B = 0x7D0000000000, 0x7D0010000000
+    assert lib.mlstm_prof_copy_lds(None, B, 16384, None) == NULLPTR
+    assert lib.mlstm_prof_copy_lds(A, B, 0, None) == BAD_SHAPE
+    assert lib.mlstm_prof_copy_lds(A, B, 16384 + 16, None) == BAD_SHAPE
+    assert lib.mlstm_prof_copy_lds(A + 4, B, 16384, None) == MISALIGNED
+    assert lib.mlstm_prof_copy_lds(A, A + 16384, 32768, None) == ALIAS
