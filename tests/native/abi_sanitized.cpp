@@ -1,0 +1,194 @@
+// Drives every entry point of the mLSTM C ABI (include/mlstm.h, slstm.h,
+// mlstm_prof.h) through its argument checks and, with host-only stand-in
+// launchers (abi_stub_launchers.cpp), through its workspace carving and
+// dispatch, in a build with AddressSanitizer and UndefinedBehaviorSanitizer
+// on the host code. Pointers are fabricated addresses that nothing
+// dereferences. Exit status 0 when every expectation holds; the sanitizers
+// abort on their own findings.
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/mlstm.h"
+#include "../../include/mlstm_prof.h"
+#include "../../include/slstm.h"
+
+namespace mlstm_impl { extern int g_calls[16]; }
+
+static int failures = 0;
+#define EXPECT(cond)                                                   \
+  do {                                                                 \
+    if (!(cond)) {                                                     \
+      fprintf(stderr, "%s:%d: expectation failed: %s\n", __FILE__, __LINE__, #cond); \
+      ++failures;                                                      \
+    }                                                                  \
+  } while (0)
+
+static uintptr_t next_addr = 0x7C0000000000ull;
+static void* take(size_t bytes) {
+  const uintptr_t p = next_addr;
+  next_addr += (bytes + 4095) / 4096 * 4096 + 4096;
+  return reinterpret_cast<void*>(p);
+}
+
+static mlstm_fwd_args fwd(int64_t B, int64_t H, int64_t T, int64_t K, int64_t V, int dtype, bool state_in,
+                          bool state_out) {
+  mlstm_fwd_args a;
+  memset(&a, 0, sizeof(a));
+  const int64_t es = dtype == MLSTM_BF16 ? 2 : 4, BH = B * H;
+  a.B = B; a.H = H; a.T = T; a.d_qk = K; a.d_v = V; a.dtype = dtype;
+  a.q = take(BH * T * K * es); a.k = take(BH * T * K * es); a.v = take(BH * T * V * es);
+  a.o_pre = take(BH * T * V * es); a.i_pre = (const float*)take(BH * T * 4); a.f_pre = (const float*)take(BH * T * 4);
+  a.h = take(BH * T * V * es);
+  if (state_in) { a.C0 = (const float*)take(BH * V * K * 4); a.n0 = (const float*)take(BH * K * 4); a.m0 = (const float*)take(BH * 4); }
+  if (state_out) { a.C_out = (float*)take(BH * V * K * 4); a.n_out = (float*)take(BH * K * 4); a.m_out = (float*)take(BH * 4); }
+  return a;
+}
+
+static mlstm_bwd_args bwd(int64_t B, int64_t H, int64_t T, int64_t K, int64_t V, int dtype, bool init) {
+  mlstm_bwd_args a;
+  memset(&a, 0, sizeof(a));
+  const int64_t es = dtype == MLSTM_BF16 ? 2 : 4, BH = B * H;
+  a.B = B; a.H = H; a.T = T; a.d_qk = K; a.d_v = V; a.dtype = dtype;
+  a.q = take(BH * T * K * es); a.k = take(BH * T * K * es); a.v = take(BH * T * V * es);
+  a.o_pre = take(BH * T * V * es); a.i_pre = (const float*)take(BH * T * 4); a.f_pre = (const float*)take(BH * T * 4);
+  a.h = take(BH * T * V * es); a.dh = take(BH * T * V * es);
+  a.dq = take(BH * T * K * es); a.dk = take(BH * T * K * es); a.dv = take(BH * T * V * es);
+  a.do_pre = take(BH * T * V * es); a.di_pre = (float*)take(BH * T * 4); a.df_pre = (float*)take(BH * T * 4);
+  if (init) { a.dC0 = (float*)take(BH * V * K * 4); a.dn0 = (float*)take(BH * K * 4); a.dm0 = (float*)take(BH * 4); }
+  return a;
+}
+
+int main() {
+  using mlstm_impl::g_calls;
+  EXPECT(mlstm_abi_version() == MLSTM_ABI_VERSION);
+  for (int s = 1; s >= -9; --s) EXPECT(mlstm_status_string(s) != nullptr);
+
+  // ---- forward, chunkwise: every dtype / shape family reaches its launchers
+  const int dts[2] = {MLSTM_FP32, MLSTM_BF16};
+  for (int di = 0; di < 2; ++di) {
+    for (int64_t V : {64, 128, 192, 512}) {
+      for (int64_t T : {1, 63, 64, 65, 1000}) {
+        for (int chunk : {64, 128, 1024}) {
+          const int64_t K = dts[di] == MLSTM_BF16 ? 256 : 128;
+          mlstm_fwd_args a = fwd(2, 3, T, K, V, dts[di], T % 2 == 0, T % 3 == 0);
+          const size_t need = mlstm_fwd_chunkwise_workspace_size(&a, chunk);
+          EXPECT(need > 0);
+          void* ws = take(need);
+          const int before = g_calls[0];
+          EXPECT(mlstm_fwd_chunkwise(&a, chunk, ws, need, nullptr) == MLSTM_OK);
+          EXPECT(g_calls[0] == before + 1);
+          EXPECT(mlstm_fwd_chunkwise(&a, chunk, ws, need - 1, nullptr) == MLSTM_ERR_WORKSPACE);
+          EXPECT(mlstm_fwd_chunkwise(&a, chunk, a.h, need, nullptr) == MLSTM_ERR_ALIAS);
+          const size_t pneed = mlstm_fwd_parallel_workspace_size(&a);
+          EXPECT(mlstm_fwd_parallel(&a, take(pneed), pneed, nullptr) == MLSTM_OK);
+          void* ev[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+          EXPECT(mlstm_prof_fwd_chunkwise(&a, chunk, ws, need, nullptr, ev) == MLSTM_OK);
+        }
+      }
+    }
+  }
+  {
+    mlstm_fwd_args a = fwd(1, 1, 0, 64, 64, MLSTM_FP32, true, true);
+    EXPECT(mlstm_fwd_chunkwise(&a, 64, nullptr, 0, nullptr) == MLSTM_OK);   // T = 0: state copy
+    a = fwd(1, 1, 10, 64, 64, MLSTM_FP32, false, false);
+    EXPECT(mlstm_fwd_chunkwise(nullptr, 64, nullptr, 0, nullptr) == MLSTM_ERR_NULLPTR);
+    a.dtype = 9;
+    EXPECT(mlstm_fwd_chunkwise(&a, 64, take(1 << 20), 1 << 20, nullptr) == MLSTM_ERR_BAD_DTYPE);
+    a.dtype = MLSTM_FP32; a.d_qk = 96;
+    EXPECT(mlstm_fwd_chunkwise(&a, 64, take(1 << 20), 1 << 20, nullptr) == MLSTM_ERR_BAD_SHAPE);
+    a.d_qk = 256;
+    EXPECT(mlstm_fwd_chunkwise(&a, 64, take(1 << 20), 1 << 20, nullptr) == MLSTM_ERR_UNSUPPORTED);
+    a.d_qk = 64;
+    EXPECT(mlstm_fwd_chunkwise(&a, 100, take(1 << 20), 1 << 20, nullptr) == MLSTM_ERR_BAD_SHAPE);
+    a.q = (const char*)a.q + 2;
+    EXPECT(mlstm_fwd_chunkwise(&a, 64, take(1 << 20), 1 << 20, nullptr) == MLSTM_ERR_MISALIGNED);
+    EXPECT(strlen(mlstm_last_error()) > 0);
+    mlstm_fwd_args p = fwd(1, 1, 9000, 64, 64, MLSTM_FP32, false, false);
+    EXPECT(mlstm_fwd_parallel(&p, take(1 << 20), 1 << 20, nullptr) == MLSTM_ERR_UNSUPPORTED);
+  }
+  // no-allocation entry point: either it finds no device (error) or runs
+  {
+    mlstm_fwd_args a = fwd(1, 2, 500, 128, 256, MLSTM_BF16, false, false);
+    const int st = mlstm_fwd_chunkwise_noalloc(&a, 128, nullptr);
+    EXPECT(st == MLSTM_OK || st == MLSTM_ERR_HIP);
+    mlstm_fwd_args big = fwd(1, 8, 131072, 256, 512, MLSTM_BF16, false, false);
+    EXPECT(mlstm_fwd_chunkwise_noalloc(&big, 64, nullptr) == MLSTM_ERR_UNSUPPORTED);
+    EXPECT(mlstm_fwd_chunkwise_noalloc_limit() == (size_t(64) << 20));
+  }
+
+  // ---- decode step
+  {
+    mlstm_step_args s;
+    memset(&s, 0, sizeof(s));
+    s.B = 4; s.H = 2; s.d_qk = 128; s.d_v = 96; s.dtype = MLSTM_BF16;
+    const int64_t BH = 8;
+    s.q = take(BH * 128 * 2); s.k = take(BH * 128 * 2); s.v = take(BH * 96 * 2); s.o_pre = take(BH * 96 * 2);
+    s.i_pre = (const float*)take(BH * 4); s.f_pre = (const float*)take(BH * 4);
+    s.C = (float*)take(BH * 96 * 128 * 4); s.n_in = (const float*)take(BH * 128 * 4); s.m_in = (const float*)take(BH * 4);
+    s.n_out = (float*)take(BH * 128 * 4); s.m_out = (float*)take(BH * 4); s.h = take(BH * 96 * 2);
+    EXPECT(mlstm_step(&s, nullptr) == MLSTM_OK);
+    EXPECT(mlstm_prof_step(&s, nullptr, nullptr, nullptr) == MLSTM_OK);
+    s.n_out = (float*)s.n_in;
+    EXPECT(mlstm_step(&s, nullptr) == MLSTM_ERR_ALIAS);
+  }
+
+  // ---- backward
+  for (int di = 0; di < 2; ++di) {
+    for (int64_t V : {64, 256}) {
+      for (int64_t T : {1, 77, 300}) {
+        for (int chunk : {64, 192}) {
+          mlstm_bwd_args b = bwd(2, 2, T, 64, V, dts[di], T > 1);
+          const size_t need = mlstm_bwd_chunkwise_workspace_size(&b, chunk);
+          EXPECT(need > 0);
+          void* ws = take(need);
+          const int before = g_calls[11];
+          EXPECT(mlstm_bwd_chunkwise(&b, chunk, ws, need, nullptr) == MLSTM_OK);
+          EXPECT(g_calls[11] == before + 1);
+          EXPECT(mlstm_bwd_chunkwise(&b, chunk, ws, need - 1, nullptr) == MLSTM_ERR_WORKSPACE);
+          void* ev[12] = {};
+          EXPECT(mlstm_prof_bwd_chunkwise(&b, chunk, ws, need, nullptr, ev) == MLSTM_OK);
+          b.dq = const_cast<void*>(b.q);
+          EXPECT(mlstm_bwd_chunkwise(&b, chunk, ws, need, nullptr) == MLSTM_ERR_ALIAS);
+        }
+      }
+    }
+  }
+  {
+    mlstm_bwd_args b = bwd(1, 1, 10, 256, 1024, MLSTM_BF16, false);
+    EXPECT(mlstm_bwd_chunkwise(&b, 64, take(1 << 20), 1 << 20, nullptr) == MLSTM_ERR_UNSUPPORTED);
+    b = bwd(1, 1, 0, 64, 64, MLSTM_FP32, true);
+    EXPECT(mlstm_bwd_chunkwise(&b, 64, nullptr, 0, nullptr) == MLSTM_OK);   // zero the state gradient
+  }
+
+  // ---- sLSTM
+  {
+    slstm_fwd_args s;
+    memset(&s, 0, sizeof(s));
+    s.B = 2; s.H = 3; s.T = 50; s.D = 64;
+    s.pre = (const float*)take(6 * 50 * 4 * 64 * 4); s.R = (const float*)take(3 * 4 * 64 * 64 * 4);
+    s.h = (float*)take(6 * 50 * 64 * 4);
+    EXPECT(slstm_fwd(&s, nullptr) == MLSTM_OK);
+    s.D = 48;
+    EXPECT(slstm_fwd(&s, nullptr) == MLSTM_ERR_UNSUPPORTED);
+  }
+
+  // ---- measurement helpers
+  {
+    unsigned long long* ticks = (unsigned long long*)take(32);
+    EXPECT(mlstm_clock_probe(ticks, 10, nullptr) == MLSTM_OK);
+    EXPECT(mlstm_clock_probe(ticks, 0, nullptr) == MLSTM_ERR_BAD_SHAPE);
+    void* src = take(1 << 20);
+    void* dst = take(1 << 20);
+    EXPECT(mlstm_prof_copy_lds(src, dst, 1 << 20, nullptr) == MLSTM_OK);
+    EXPECT(mlstm_prof_copy_lds(src, (char*)src + 16384, 32768, nullptr) == MLSTM_ERR_ALIAS);
+  }
+
+  if (failures) {
+    fprintf(stderr, "%d expectation(s) failed\n", failures);
+    return 1;
+  }
+  printf("abi_sanitized: all expectations held\n");
+  return 0;
+}
