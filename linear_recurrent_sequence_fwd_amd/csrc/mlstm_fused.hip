@@ -20,11 +20,12 @@
 //                      and 32-column groups, and walks the chunk in 64-token
 //                      tiles. Per tile: Q K^T and Q C~^T on MFMA (C~ as bf16
 //                      hi + lo; partial sums over each half of d_qk,
-//                      exchanged through LDS), the
-//                      state update C~ <- a C~ + K^T diag(w) V on MFMA and the
-//                      same for n~ (a two-column MFMA tile carrying the weights
-//                      as bf16 hi + lo), decay mask and stabiliser in
-//                      registers, P V on MFMA, normaliser and output gate.
+//                      exchanged through LDS), q . n~ in float32 on the
+//                      vector ALU, the state update C~ <- a C~ + K^T diag(w) V
+//                      on MFMA and the same for n~ (three MFMA columns
+//                      carrying the weights as three bf16 terms), decay mask
+//                      and stabiliser in registers, P V on MFMA, normaliser
+//                      and output gate.
 //                      q, k and v reach LDS by direct-to-LDS copies issued one
 //                      tile ahead.
 //
