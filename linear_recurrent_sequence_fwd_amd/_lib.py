@@ -76,6 +76,9 @@ class MlstmError(RuntimeError):
 
 _lib = None
 
+# MLSTM_ABI_VERSION of include/mlstm.h that the argument structs here follow
+ABI_VERSION = 2
+
 
 def lib() -> ctypes.CDLL:
     """The loaded library with argument types set (loaded once)."""
@@ -116,6 +119,9 @@ def lib() -> ctypes.CDLL:
         L.mlstm_last_error.restype = c_char_p
         L.mlstm_abi_version.argtypes = []
         L.mlstm_abi_version.restype = c_int
+        if L.mlstm_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.mlstm_abi_version()}, the binding "
+                               f"follows version {ABI_VERSION}: rebuild the library")
         L.mlstm_prof_fwd_chunkwise.argtypes = [P(FwdArgs), c_int, c_void_p, c_size_t, c_void_p,
                                                P(c_void_p)]
         L.mlstm_prof_fwd_chunkwise.restype = c_int
