@@ -183,14 +183,43 @@ __device__ __forceinline__ bf16x8 pack_bf16(const f32x4& a, const f32x4& b) {
 
 // The bfloat16 rounding of what pack_bf16(a, b) leaves out: pack_bf16(a, b)
 // + pack_bf16_rest(a, b, pack_bf16(a, b)) carries about 16 bits of a and b.
+// x - float(h) is exact in float32 (h is x rounded to 8 significant bits), so
+// it is formed in one bf16 dot product: (h0, h1) . (-1, 0) + x0 and
+// (h0, h1) . (0, -1) + x1 take the pair of rounded values as they lie in one
+// register, without widening them first.
+// The multipliers are bit patterns in registers (element 0 = the low 16
+// bits; bf16 -1 is 0xBF80), not inline constants, whose placement in a packed
+// bf16 operand the encoding leaves open.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+// (x0 - float(h0), x1 - float(h1)) for the pair h = (h0, h1) of bf16 roundings
+// of (x0, x1), both exact, in two bf16 dot products
+__device__ __forceinline__ void minus_rounded(const bf16x2v& h, float& x0, float& x1) {
+  unsigned u0 = 0x0000BF80u, u1 = 0xBF800000u;
+  asm("" : "+v"(u0), "+v"(u1));
+  x0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2v, u0), x0, false);
+  x1 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2v, u1), x1, false);
+}
 __device__ __forceinline__ bf16x8 pack_bf16_rest(const f32x4& a, const f32x4& b, const bf16x8& hi) {
   bf16x8 r;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    r[e] = (__bf16)(a[e] - (float)hi[e]);
-    r[4 + e] = (__bf16)(b[e] - (float)hi[4 + e]);
+  for (int e = 0; e < 4; e += 2) {
+    float a0 = a[e], a1 = a[e + 1], b0 = b[e], b1 = b[e + 1];
+    minus_rounded(bf16x2v{hi[e], hi[e + 1]}, a0, a1);
+    minus_rounded(bf16x2v{hi[4 + e], hi[5 + e]}, b0, b1);
+    r[e] = (__bf16)a0;
+    r[e + 1] = (__bf16)a1;
+    r[4 + e] = (__bf16)b0;
+    r[5 + e] = (__bf16)b1;
   }
   return r;
+}
+// x0, x1 as three bfloat16 terms each, hi + lo + lo2 (about 24 bits), as pairs
+__device__ __forceinline__ void split3(float x0, float x1, bf16x2v& hi, bf16x2v& lo, bf16x2v& lo2) {
+  hi = bf16x2v{(__bf16)x0, (__bf16)x1};
+  minus_rounded(hi, x0, x1);
+  lo = bf16x2v{(__bf16)x0, (__bf16)x1};
+  minus_rounded(lo, x0, x1);
+  lo2 = bf16x2v{(__bf16)x0, (__bf16)x1};
 }
 
 template <typename F, int... S>
@@ -284,7 +313,7 @@ struct OutLds {
   // sQ, sK and sV are arrays of their own; the rest shares one array at these offsets
   static constexpr int oP = 0;
   // double-buffered tile data, [2] of:
-  static constexpr int nbBytes = K * 4;              // float [K]: n~ at the tile's start
+  static constexpr int nbBytes = 4 * K * 2;          // bf16 [4][K]: n~ at the tile's start as hi, lo, lo2, zero
   static constexpr int wBytes = kTile * 4;           // float [64] key weights
   static constexpr int wbBytes = 4 * kTile * 2;      // bf16 [4][64]: weights hi, lo, lo2, zero
   static constexpr int rowBytes = 5 * kTile * 4;     // r2, sc, fl, u2 (float), rs (int), [64] each
@@ -293,8 +322,8 @@ struct OutLds {
   static constexpr int oBuf = oP + kTile * PP * 2;
   static constexpr int oDnm = oBuf + 2 * bufBytes;   // float [64] denominator max(|n~^T q|, floor) of each row
   static constexpr int oDen = oDnm + kTile * 4;      // float [4][64] row sums of P per key group
-  static constexpr int oDn = oDen + 4 * kTile * 4;   // float [64] q . n~ of each row
-  static constexpr int oX = oDn + kTile * 4;                 // f32x4 [8 waves][kXchg][64 lanes]
+  static constexpr int oDn = oDen + 4 * kTile * 4;   // float [2][64] q . n~ of each row over each half of d_qk
+  static constexpr int oX = oDn + 2 * kTile * 4;             // f32x4 [8 waves][kXchg][64 lanes]
   static constexpr int oFin = oX + kOutWaves * kXchg * 64 * 16;   // double [2]: final m, logD
   static constexpr int restBytes = oFin + 16;
   static_assert(qBytes + kBytes + vBytes + restBytes <= 160 * 1024, "fits the LDS of a CU");
@@ -346,7 +375,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
   double* s_fin = reinterpret_cast<double*>(smem + L::oFin);
   // views of one half of the double-buffered tile data
   struct TileBuf {
-    float* nf;
+    __bf16* nt;
     float* w;
     __bf16* wb;
     float *r2, *sc, *fl, *u2;
@@ -356,7 +385,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
   auto tile_buf = [&](int b) {
     char* base = smem + L::oBuf + b * L::bufBytes;
     TileBuf t;
-    t.nf = reinterpret_cast<float*>(base);
+    t.nt = reinterpret_cast<__bf16*>(base);
     t.w = reinterpret_cast<float*>(base + L::nbBytes);
     t.wb = reinterpret_cast<__bf16*>(base + L::nbBytes + L::wBytes);
     float* row = reinterpret_cast<float*>(base + L::nbBytes + L::wBytes + L::wbBytes);
@@ -422,10 +451,11 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
   for (int x = 0; x < KXN; ++x)
     Nacc[x] = (ninit && i == 0 && n_live(x)) ? *reinterpret_cast<const f32x4*>(ninit + state_k0(kxg(nx(x)), g))
                                             : f32x4{0.f, 0.f, 0.f, 0.f};
-  // zero rows of the two-column weight operands, both halves
+  // zero rows of the weight and normaliser operands, both halves
   for (int b = 0; b < 2; ++b) {
     const TileBuf tb = tile_buf(b);
     if (tid < kTile) tb.wb[3 * kTile + tid] = (__bf16)0.f;
+    for (int k = tid; k < K; k += 64 * kOutWaves) tb.nt[3 * K + k] = (__bf16)0.f;
   }
 
   // ---------------- copies of the next tile. Rows past the sequence end are
@@ -524,21 +554,33 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
     t_R = a.gb.R[bh * Nt + tau];
   };
 
-  // n~ of the next tile in float32 (every wave its own tiles) into half b of
-  // the tile data. The byte offset is kept whole (empty asm statement), so
-  // that each store is one step from the array and the compiler can tell it
-  // from the copies in flight.
+  // n~ of the next tile (every wave its own tiles) into half b of the tile
+  // data, as three bfloat16 terms hi + lo + lo2 (about 24 bits: the rows
+  // whose denominators cancel strongly need n~ to float32 accuracy), the
+  // operand of q . n~ on MFMA. The byte offsets are kept whole (empty asm
+  // statement), so that each store is one step from the array and the
+  // compiler can tell it from the copies in flight.
   auto put_n = [&](int b) {
     const Lanes ln = fresh_lanes();
 #pragma unroll
     for (int x = 0; x < KXN; ++x) {
       if (n_live(x)) {
-        f32x4 n4;
+        float n[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) n4[r] = sum_quad(Nacc[x][r]);
-        int off = L::oBuf + b * L::bufBytes + 4 * state_k0(kxg(nx(x)), ln.g);
+        for (int r = 0; r < 4; ++r) n[r] = sum_quad(Nacc[x][r]);
+        bf16x2v h01, l01, e01, h23, l23, e23;
+        split3(n[0], n[1], h01, l01, e01);
+        split3(n[2], n[3], h23, l23, e23);
+        const bf16x4 t0 = __builtin_shufflevector(h01, h23, 0, 1, 2, 3);
+        const bf16x4 t1 = __builtin_shufflevector(l01, l23, 0, 1, 2, 3);
+        const bf16x4 t2 = __builtin_shufflevector(e01, e23, 0, 1, 2, 3);
+        int off = L::oBuf + b * L::bufBytes + 2 * state_k0(kxg(nx(x)), ln.g);
         asm("" : "+v"(off));
-        if (ln.i == 0) *reinterpret_cast<f32x4*>(smem + off) = n4;
+        if (ln.i == 0) {
+          *reinterpret_cast<bf16x4*>(smem + off) = t0;
+          *reinterpret_cast<bf16x4*>(smem + off + 2 * K) = t1;
+          *reinterpret_cast<bf16x4*>(smem + off + 4 * K) = t2;
+        }
       }
     }
   };
@@ -681,6 +723,10 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
       sacc[z] = f32x4{0.f, 0.f, 0.f, 0.f};
       acc[z][0] = acc[z][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // q . n~ over this wave's half of d_qk for rows 16 cg .. + 15: the three
+    // terms of n~ as rows 0-2 of the A operand (row 3 onwards zero), summed
+    // below from registers 0-2 of lanes g = 0
+    f32x4 nqacc = f32x4{0.f, 0.f, 0.f, 0.f};
     const Lanes l1 = fresh_lanes();
     unroll<KSH>([&](auto s_c) {
       constexpr int s = decltype(s_c)::value;
@@ -691,6 +737,9 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
       const bf16x8 fk = *reinterpret_cast<const bf16x8*>(&sK[(16 * kg + l1.i) * KP + col]);
 #pragma unroll
       for (int z = 0; z < 4; ++z) sacc[z] = mma(fk, fa[z], sacc[z]);
+      const bf16x8 fq = *reinterpret_cast<const bf16x8*>(&sQ[(16 * cg + l1.i) * QP + col]);
+      const bf16x8 fn = *reinterpret_cast<const bf16x8*>(&tb.nt[min(l1.i, 3) * K + col]);
+      nqacc = mma(fn, fq, nqacc);
       // the carried state as two bf16 terms: rows whose q is nearly
       // orthogonal to a dominant key make C~ q a strongly cancelling sum
 #pragma unroll
@@ -722,30 +771,15 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
 #pragma unroll
         for (int cv = 0; cv < 2; ++cv) Av[jb][cv] = frag_tr(sV, VP, 32 * jb, 32 * cg + 16 * cv, lv.lane);
     }
-    // ---------------- q . n~ in float32 on the vector ALU, eight threads per
-    // row. Rows where a dominant key is nearly orthogonal to q make the
-    // denominator a strongly cancelling sum, so n~ is not rounded here.
+    // ---------------- this half's q . n~ of rows 16 cg .. + 15 (the three
+    // terms' partial sums added in float32). Register 3 (the zero row) is
+    // added too: a result register left unread may be handed to the next
+    // value at once, and an inline-asm write there (fresh_tid) is not held
+    // back until the MFMA has written it.
     {
-      const int t8 = fresh_tid();
-      const int row = t8 >> 3, part = t8 & 7;
-      const __bf16* qr = sQ + row * QP + part * (K / 8);
-      const float* nr = tb.nf + part * (K / 8);
-      float d = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < K / 8; kk += 8) {
-        const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(qr + kk);
-        const f32x4 n0 = *reinterpret_cast<const f32x4*>(nr + kk);
-        const f32x4 n1 = *reinterpret_cast<const f32x4*>(nr + kk + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          d = fmaf((float)q8[e], n0[e], d);
-          d = fmaf((float)q8[4 + e], n1[e], d);
-        }
-      }
-      d += __shfl_xor(d, 1, 64);
-      d += __shfl_xor(d, 2, 64);
-      d += __shfl_xor(d, 4, 64);
-      if (part == 0) s_dn[row] = d;
+      const float nq = (nqacc[0] + nqacc[1]) + (nqacc[2] + nqacc[3]);
+      const Lanes ln = fresh_lanes();
+      if (ln.g == 0) s_dn[kh * kTile + 16 * cg + ln.i] = nq;
     }
 
     // The registers loaded at the top of the tile are taken here, before any
@@ -859,9 +893,8 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
       }
     };
     // The two phases are independent: P is exponentials (VALU), the update
-    // matrix products. The two waves of a SIMD (the halves kh = 0 and 1 of one
-    // column group) take them in opposite orders, so that one wave's
-    // exponentials run beside the other's products.
+    // matrix products. (Taking them in opposite orders in the two waves of a
+    // SIMD, or the update first, measured slower.)
     phase_p();
     phase_u();
     // the next tile's K: after the barrier no wave reads K of tile tau
@@ -874,7 +907,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
     if (w == 0) {   // max(|n~^T q|, floor) of row t = lane
       const int t = fresh_lanes().lane;
       const float den = s_den[t] + s_den[kTile + t] + s_den[2 * kTile + t] + s_den[3 * kTile + t];
-      const float d = den + tb.sc[t] * s_dn[t];
+      const float d = den + tb.sc[t] * (s_dn[t] + s_dn[kTile + t]);
       s_dnm[t] = fmaxf(fmaxf(fabsf(d), tb.fl[t]), FLT_MIN);
     }
     // ---------------- (P V)^T for the wave's rows; rows 0-31 have no keys
@@ -1104,20 +1137,39 @@ struct LocLds {
   static constexpr int CPRV = VP / 8;
   static constexpr int kBytes = kTile * KP * 2;     // = 1024 * CPRK: CPRK direct loads
   static constexpr int vBytes = kTile * VP * 2;     // = 1024 * CPRV
-  static constexpr int oK = 0;                      // [2] K tiles
-  static constexpr int oV = oK + 2 * kBytes;        // [2] V tiles
-  static constexpr int oW = oV + 2 * vBytes;        // [2][64] float w0
-  static constexpr int oWb = oW + 2 * kTile * 4;       // [2][4][64] bf16: w0 hi, lo, lo2, zero
-  static constexpr int oCw = oWb + 2 * 4 * kTile * 2;   // [kMaxTiles] float: tile weight factor
-  static constexpr int oRf = oCw + kMaxTiles * 4;       // [kMaxTiles] float: accumulator rescale (1 = none)
+  static constexpr int kBufs = 3;                   // tiles in LDS: the one in use and two ahead
+  static constexpr int oK = 0;                      // [3] K tiles
+  static constexpr int oV = oK + kBufs * kBytes;    // [3] V tiles
+  static constexpr int oW = oV + kBufs * vBytes;    // [3][64] float w0
+  static constexpr int oWb = oW + kBufs * kTile * 4;       // [3][4][64] bf16: w0 hi, lo, lo2, zero
+  static constexpr int oCw = oWb + kBufs * 4 * kTile * 2;   // [kMaxTiles] float: tile weight factor
+  static constexpr int oRf = oCw + kMaxTiles * 4;          // [kMaxTiles] float: accumulator rescale (1 = none)
   static constexpr int bytes = oRf + kMaxTiles * 4;
+  // direct loads one tile's copy issues (a wave-wide load per 1 KiB of K and
+  // V, one for w0, one for its split): the loader waits for a tile by
+  // counting them
+  static constexpr int kLoadsPerTile = CPRK + CPRV + 2;
+  static_assert(kLoadsPerTile <= 63, "fits the vector-memory wait counter");
+  static_assert(bytes <= 160 * 1024, "fits the LDS of a CU");
 };
 // Compute waves of local_kernel: eight (two per SIMD, 32 d_qk rows each) when
 // d_qk allows, else four.
 template <int K> struct LocWaves { static constexpr int value = K >= 128 ? 8 : 4; };
 
-// The loader wave of local_kernel: tile tau + 1 into the free half of the
-// double buffer while the compute waves work on tile tau.
+// s_waitcnt that waits until at most N vector-memory operations of the wave
+// are outstanding (N <= 63; the LDS and export counters are left alone).
+template <int N>
+__device__ __forceinline__ void wait_vm_at_most() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// The loader wave of local_kernel: tiles tau + 1 and tau + 2 on their way
+// into the two free buffers of three while the compute waves work on tile
+// tau. It waits only for the tile the compute waves need next (by the count
+// of its direct loads still in flight) and meets them at barriers that wait
+// for LDS traffic alone, so the copy of the tile after next stays in flight
+// across the barrier.
 template <int K>
 __device__ __forceinline__ void local_loader(const SegArgs& a, char* smem) {
   using L = LocLds<K>;
@@ -1163,11 +1215,22 @@ __device__ __forceinline__ void local_loader(const SegArgs& a, char* smem) {
                                        (lds_void*)(smem + L::oWb + buf * 4 * kTile * 2), 16, 0, 0);
   };
   dma(tile0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
+  if (tile0 + 1 < tile1) {
+    dma(tile0 + 1, 1);
+    wait_vm_at_most<L::kLoadsPerTile>();   // tile tile0 has landed
+  } else {
+    wait_vm_at_most<0>();
+  }
+  int nbuf = 2;   // buffer of tile tau + 2
   for (int64_t tau = tile0; tau < tile1; ++tau) {
-    __syncthreads();   // tile tau published; the other buffer is free
-    if (tau + 1 < tile1) dma(tau + 1, (int)((tau + 1 - tile0) & 1));
-    __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();   // tile tau published; the buffer tile tau - 1 used is free
+    if (tau + 2 < tile1) {
+      dma(tau + 2, nbuf);
+      nbuf = nbuf == L::kBufs - 1 ? 0 : nbuf + 1;
+      wait_vm_at_most<L::kLoadsPerTile>();   // tile tau + 1 has landed, tau + 2 may be in flight
+    } else {
+      wait_vm_at_most<0>();
+    }
   }
 }
 
@@ -1200,9 +1263,10 @@ __device__ __forceinline__ void local_body(const SegArgs& a, char* smem, const L
   }
   const float* s_cw = reinterpret_cast<const float*>(smem + L::oCw);
   const float* s_rf = reinterpret_cast<const float*>(smem + L::oRf);
-  for (int64_t tau = tile0; tau < tile1; ++tau) {
-    __syncthreads();   // tile tau in buffer buf
-    const int j = (int)(tau - tile0), buf = j & 1;
+  int buf = 0;   // buffer of tile tau
+  for (int64_t tau = tile0; tau < tile1; ++tau, buf = buf == L::kBufs - 1 ? 0 : buf + 1) {
+    lds_barrier();   // tile tau in buffer buf
+    const int j = (int)(tau - tile0);
     const __bf16* sK = reinterpret_cast<const __bf16*>(smem + L::oK + buf * L::kBytes);
     const __bf16* sV = reinterpret_cast<const __bf16*>(smem + L::oV + buf * L::vBytes);
     const float* s_w0 = reinterpret_cast<const float*>(smem + L::oW + buf * kTile * 4);
@@ -1296,8 +1360,9 @@ __global__ __launch_bounds__(64 * (LocWaves<K>::value + 1)) void local_kernel(Se
   // zero rows of the split-weight operands (published by the first barrier);
   // every compute wave writes the same tile table and reads only its own writes
   if (threadIdx.x < kTile) {
-    reinterpret_cast<__bf16*>(smem + L::oWb)[3 * kTile + threadIdx.x] = (__bf16)0.f;
-    reinterpret_cast<__bf16*>(smem + L::oWb + 4 * kTile * 2)[3 * kTile + threadIdx.x] = (__bf16)0.f;
+#pragma unroll
+    for (int b = 0; b < L::kBufs; ++b)
+      reinterpret_cast<__bf16*>(smem + L::oWb + b * 4 * kTile * 2)[3 * kTile + threadIdx.x] = (__bf16)0.f;
   }
   const LocScan sc = local_scan(a, bh, tile0, a.TPS, reinterpret_cast<float*>(smem + L::oCw),
                                 reinterpret_cast<float*>(smem + L::oRf));
