@@ -155,9 +155,56 @@ __device__ __forceinline__ f32x8 frag_cols(const float* X, int P, int k0, int n0
 }
 
 // Copy rows [0, 64) x columns [0, NC) of a row-major global array (row pitch
-// gp) into LDS (row pitch SP); rows at or beyond `nrows` become zero.
+// gp) into LDS (row pitch SP); rows at or beyond `nrows` become zero. Each
+// thread issues all its loads before the first store, so the tile costs one
+// memory latency rather than one per 16-byte piece.
 template <int NT, typename T, int NC, int SP>
 __device__ __forceinline__ void stage(T* __restrict__ s, const T* __restrict__ g, int64_t gp, int nrows) {
+  constexpr int EV = 16 / sizeof(T);
+  constexpr int VPR = NC / EV;
+  constexpr int N = (kTile * VPR + NT - 1) / NT;
+  f32x4 x[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const int it = (int)threadIdx.x + n * NT;
+    const int row = it / VPR, cv = it % VPR;
+    x[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (it < kTile * VPR && row < nrows) x[n] = *reinterpret_cast<const f32x4*>(g + (int64_t)row * gp + cv * EV);
+  }
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const int it = (int)threadIdx.x + n * NT;
+    const int row = it / VPR, cv = it % VPR;
+    if (it < kTile * VPR) *reinterpret_cast<f32x4*>(s + row * SP + cv * EV) = x[n];
+  }
+}
+// The same copy as direct-to-LDS buffer loads: no registers, every load of
+// the tile in flight at once. Rows [0, nrows) of NC elements lie contiguous
+// in global memory; the LDS image (row pitch SP, a whole number of 16-byte
+// pieces) is filled 1 KiB per wave-wide load, a row's padding pieces
+// repeating its last data piece. Loads past the buffer's nrows * NC elements
+// return zero, so the rows beyond `nrows` come out zero. The caller's next
+// __syncthreads waits for the loads (a workgroup fence waits for direct-to-LDS
+// loads as for LDS stores).
+typedef __attribute__((address_space(3))) void lds_void_t;
+template <int NT, typename T, int NC, int SP>
+__device__ __forceinline__ void stage_dma(T* __restrict__ s, const T* __restrict__ g, int nrows) {
+  constexpr int CPR = SP * (int)sizeof(T) / 16;   // 16-byte pieces per LDS row
+  constexpr int DPR = NC * (int)sizeof(T) / 16;   // data pieces per row
+  static_assert(SP * sizeof(T) % 16 == 0 && NC * sizeof(T) % 16 == 0, "whole 16-byte pieces");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(g), (short)0, nrows * NC * (int)sizeof(T), 0x00020000);
+  for (int n = w; n < CPR; n += NT / 64) {
+    const int c = 64 * n + lane, row = c / CPR, ch = min(c % CPR, DPR - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(reinterpret_cast<char*>(s) + 1024 * n), 16,
+                                             row * NC * (int)sizeof(T) + 16 * ch, 0, 0, 0);
+  }
+}
+// The same copy one 16-byte piece at a time (few registers: for loops that
+// already hold many accumulators).
+template <int NT, typename T, int NC, int SP>
+__device__ __forceinline__ void stage_lean(T* __restrict__ s, const T* __restrict__ g, int64_t gp, int nrows) {
   constexpr int EV = 16 / sizeof(T);
   constexpr int VPR = NC / EV;
   for (int it = threadIdx.x; it < kTile * VPR; it += NT) {
@@ -165,6 +212,37 @@ __device__ __forceinline__ void stage(T* __restrict__ s, const T* __restrict__ g
     f32x4 x = {0.f, 0.f, 0.f, 0.f};
     if (row < nrows) x = *reinterpret_cast<const f32x4*>(g + (int64_t)row * gp + cv * EV);
     *reinterpret_cast<f32x4*>(s + row * SP + cv * EV) = x;
+  }
+}
+// Two such copies with all loads of both issued before any store.
+template <int NT, typename T, int NC1, int SP1, int NC2, int SP2>
+__device__ __forceinline__ void stage2(T* __restrict__ s1, const T* __restrict__ g1, int64_t gp1,
+                                       T* __restrict__ s2, const T* __restrict__ g2, int64_t gp2, int nrows) {
+  constexpr int EV = 16 / sizeof(T);
+  constexpr int VPR1 = NC1 / EV, VPR2 = NC2 / EV;
+  constexpr int N1 = (kTile * VPR1 + NT - 1) / NT, N2 = (kTile * VPR2 + NT - 1) / NT;
+  f32x4 x1[N1], x2[N2];
+#pragma unroll
+  for (int n = 0; n < N1; ++n) {
+    const int it = (int)threadIdx.x + n * NT, row = it / VPR1, cv = it % VPR1;
+    x1[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (it < kTile * VPR1 && row < nrows) x1[n] = *reinterpret_cast<const f32x4*>(g1 + (int64_t)row * gp1 + cv * EV);
+  }
+#pragma unroll
+  for (int n = 0; n < N2; ++n) {
+    const int it = (int)threadIdx.x + n * NT, row = it / VPR2, cv = it % VPR2;
+    x2[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (it < kTile * VPR2 && row < nrows) x2[n] = *reinterpret_cast<const f32x4*>(g2 + (int64_t)row * gp2 + cv * EV);
+  }
+#pragma unroll
+  for (int n = 0; n < N1; ++n) {
+    const int it = (int)threadIdx.x + n * NT, row = it / VPR1, cv = it % VPR1;
+    if (it < kTile * VPR1) *reinterpret_cast<f32x4*>(s1 + row * SP1 + cv * EV) = x1[n];
+  }
+#pragma unroll
+  for (int n = 0; n < N2; ++n) {
+    const int it = (int)threadIdx.x + n * NT, row = it / VPR2, cv = it % VPR2;
+    if (it < kTile * VPR2) *reinterpret_cast<f32x4*>(s2 + row * SP2 + cv * EV) = x2[n];
   }
 }
 // Copy an LDS tile (row pitch SP) to rows [0, nrows) of a global array.
@@ -288,22 +366,25 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(BwdArgs a) {
     s_rs[tid] = rs;
   }
   for (int d = tid; d < K; d += kBT) s_n[d] = has_state ? a.ns[(bh * a.Nc + c) * K + d] : 0.f;
-  stage<kBT, TI, K, QP>(sQ, qg + row0 * K, K, nrows);
+  stage_dma<kBT, TI, K, QP>(sQ, qg + row0 * K, nrows);
 
   // ---------------- z_t = sum_j P_tj (q_t . k_j) + sc_t (q_t . n~)
   float zrow[2] = {0.f, 0.f};
   for (int jb = 0; jb <= st; ++jb) {
     const int64_t key0 = t0 + (int64_t)jb * kTile;
+    const int kvalid = (int)min((int64_t)kTile, T - key0);
+    // this wave's 16 keys, all loads issued together
+    vec8<TI> Kf[K / 32];
+#pragma unroll
+    for (int ks = 0; ks < K / 32; ++ks) Kf[ks] = frag_rows_lim(kg + key0 * K, K, 16 * jw, 32 * ks, kvalid);
     __syncthreads();   // s_u2 free; sQ, row data published
     if (tid < kTile)
       s_u2[tid] = key0 + tid < T ? (float)((a.gb.u[bh * T + key0 + tid] - ref) * (double)kL2e) : -INFINITY;
     f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    const int kvalid = (int)min((int64_t)kTile, T - key0);
 #pragma unroll
     for (int ks = 0; ks < K / 32; ++ks) {
-      const vec8<TI> A = frag_rows_lim(kg + key0 * K, K, 16 * jw, 32 * ks, kvalid);
 #pragma unroll
-      for (int zz = 0; zz < 2; ++zz) sacc[zz] = mma32(A, frag_rows(sQ, QP, 16 * (zs + zz), 32 * ks), sacc[zz]);
+      for (int zz = 0; zz < 2; ++zz) sacc[zz] = mma32(Kf[ks], frag_rows(sQ, QP, 16 * (zs + zz), 32 * ks), sacc[zz]);
     }
     __syncthreads();   // s_u2 written
     // lane holds S^T[j = 16 jw + 4 g + r][t = 16 (zs + zz) + i]
@@ -391,19 +472,33 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(BwdArgs a) {
     for (int y = 0; y < CT; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (has_state) {
     const float* Cst = a.Cs + (bh * a.Nc + c) * V * K;
+    // 64 rows of the float32 state per round, rounded once to the operand type
+    // (the carried term of dq does not cancel the way the state's products
+    // with single keys can); the next round's rows are loaded into registers
+    // while this round's products run
+    constexpr int NL = (kTile * (K / 8) + kBT - 1) / kBT;
+    f32x8 pre[NL];
+    auto load_round = [&](int vb) {
+#pragma unroll
+      for (int n = 0; n < NL; ++n) {
+        const int it = tid + n * kBT, row = it / (K / 8), cv = it % (K / 8);
+        if (it < kTile * (K / 8)) pre[n] = load8(Cst + (int64_t)(64 * vb + row) * K + 8 * cv);
+      }
+    };
+    load_round(0);
     for (int vb = 0; vb < V / 64; ++vb) {
       if (vb > 0) __syncthreads();   // sK free
-      // 64 rows of the float32 state, rounded once to the operand type (the
-      // carried term of dq does not cancel the way the state's products
-      // with single keys can)
-      for (int it = tid; it < kTile * (K / 8); it += kBT) {
-        const int row = it / (K / 8), cv = it % (K / 8);
-        const f32x8 x8 = load8(Cst + (int64_t)(64 * vb + row) * K + 8 * cv);
-        vec8<TI> o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = from_f32<TI>(x8[e]);
-        store8(sK + row * QP + 8 * cv, o);
+      for (int n = 0; n < NL; ++n) {
+        const int it = tid + n * kBT, row = it / (K / 8), cv = it % (K / 8);
+        if (it < kTile * (K / 8)) {
+          vec8<TI> o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[e] = from_f32<TI>(pre[n][e]);
+          store8(sK + row * QP + 8 * cv, o);
+        }
       }
+      if (vb + 1 < V / 64) load_round(vb + 1);
       __syncthreads();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -430,18 +525,29 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(BwdArgs a) {
   }
 
   // ---------------- intra-chunk key tiles: dq += (P o (G V^T + dz)) K
+  constexpr int VGM = sizeof(TI) == 2 ? 8 : 4;       // V fragments loaded as one group
+  constexpr int VG = (V / 32) < VGM ? (V / 32) : VGM;
   for (int jb = 0; jb <= st; ++jb) {
     const int64_t key0 = t0 + (int64_t)jb * kTile;
     const int kvalid = (int)min((int64_t)kTile, T - key0);
+    vec8<TI> Vf[VG];
+#pragma unroll
+    for (int q = 0; q < VG; ++q) Vf[q] = frag_rows_lim(vg + key0 * V, V, 16 * jw, 32 * q, kvalid);
     __syncthreads();   // sK, sA, s_u2 free
-    stage<kBT, TI, K, QP>(sK, kg + key0 * K, K, kvalid);
+    stage_dma<kBT, TI, K, QP>(sK, kg + key0 * K, kvalid);
     if (tid < kTile)
       s_u2[tid] = tid < kvalid ? (float)((a.gb.u[bh * T + key0 + tid] - ref) * (double)kL2e) : -INFINITY;
     f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    for (int ks = 0; ks < V / 32; ++ks) {
-      const vec8<TI> A = frag_rows_lim(vg + key0 * V, V, 16 * jw, 32 * ks, kvalid);
 #pragma unroll
-      for (int zz = 0; zz < 2; ++zz) sacc[zz] = mma32(A, frag_rows(sG, GP, 16 * (zs + zz), 32 * ks), sacc[zz]);
+    for (int kb = 0; kb < V / 32; kb += VG) {
+      if (kb > 0) {
+#pragma unroll
+        for (int q = 0; q < VG; ++q) Vf[q] = frag_rows_lim(vg + key0 * V, V, 16 * jw, 32 * (kb + q), kvalid);
+      }
+#pragma unroll
+      for (int q = 0; q < VG; ++q)
+#pragma unroll
+        for (int zz = 0; zz < 2; ++zz) sacc[zz] = mma32(Vf[q], frag_rows(sG, GP, 16 * (zs + zz), 32 * (kb + q)), sacc[zz]);
     }
     __syncthreads();   // s_u2, sK written
 #pragma unroll
@@ -764,38 +870,60 @@ __global__ __launch_bounds__(kBT) void bwd_dkv_kernel(BwdArgs a) {
     // so it enters the MFMAs as two bfloat16 terms, hi + lo.
     const float* Es = a.Es + (bh * a.Nc + c) * V * K;
     for (int d = tid; d < K; d += kBT) s_e[d] = a.es[(bh * a.Nc + c) * K + d];
-    stage<kBT, TI, K, QP>(sQ, kg + key0 * K, K, nkeys);
-    stage<kBT, TI, V, GP>(sG, vg + key0 * V, V, nkeys);
+    stage_dma<kBT, TI, K, QP>(sQ, kg + key0 * K, nkeys);
+    stage_dma<kBT, TI, V, GP>(sG, vg + key0 * V, nkeys);
     __syncthreads();
-    // dv[j][v] += sum_d K_j[j][d] A[v][d]  (A rows straight from memory)
+    // dv[j][v] += sum_d K_j[j][d] A[v][d]  (A rows straight from memory, in
+    // groups of EG fragments whose loads are issued together)
+    constexpr int EG = CV < 4 ? CV : 4;
+    static_assert(CV % EG == 0, "whole groups");
 #pragma unroll
     for (int ks = 0; ks < K / 32; ++ks) {
       vec8<TI> A[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x) A[x] = frag_rows(sQ, QP, 32 * rh + 16 * x, 32 * ks);
 #pragma unroll
-      for (int y = 0; y < CV; ++y) {
-        const f32x8 e8 = frag_rows(Es, K, (V / 4) * cw + 16 * y, 32 * ks);
-        vec8<TI> hi, lo;
-        split8(e8, hi, lo);
+      for (int y0 = 0; y0 < CV; y0 += EG) {
+        f32x8 eb[EG];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          av[x][y] = mma32(A[x], hi, av[x][y]);
-          if constexpr (sizeof(TI) == 2) av[x][y] = mma32(A[x], lo, av[x][y]);
+        for (int q = 0; q < EG; ++q) eb[q] = frag_rows(Es, K, (V / 4) * cw + 16 * (y0 + q), 32 * ks);
+#pragma unroll
+        for (int q = 0; q < EG; ++q) {
+          vec8<TI> hi, lo;
+          split8(eb[q], hi, lo);
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            av[x][y0 + q] = mma32(A[x], hi, av[x][y0 + q]);
+            if constexpr (sizeof(TI) == 2) av[x][y0 + q] = mma32(A[x], lo, av[x][y0 + q]);
+          }
         }
       }
     }
     // dk[j][d] += sum_v V_j[j][v] A[v][d], A staged 32 rows at a time: hi in
     // rows 0..31 of sQ, lo in rows 32..63
+    constexpr int NB = (32 * (K / 8) + kBT - 1) / kBT;
+    f32x8 ep[NB];
+    auto load_blk = [&](int vb) {
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const int it = tid + n * kBT, row = it / (K / 8), cv = it % (K / 8);
+        if (it < 32 * (K / 8)) ep[n] = load8(Es + (int64_t)(32 * vb + row) * K + 8 * cv);
+      }
+    };
+    load_blk(0);
     for (int vb = 0; vb < V / 32; ++vb) {
       __syncthreads();   // sQ free (K_j or the previous block consumed)
-      for (int it = tid; it < 32 * (K / 8); it += kBT) {
-        const int row = it / (K / 8), cv = it % (K / 8);
-        vec8<TI> hi, lo;
-        split8(load8(Es + (int64_t)(32 * vb + row) * K + 8 * cv), hi, lo);
-        store8(sQ + row * QP + 8 * cv, hi);
-        store8(sQ + (32 + row) * QP + 8 * cv, lo);
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const int it = tid + n * kBT, row = it / (K / 8), cv = it % (K / 8);
+        if (it < 32 * (K / 8)) {
+          vec8<TI> hi, lo;
+          split8(ep[n], hi, lo);
+          store8(sQ + row * QP + 8 * cv, hi);
+          store8(sQ + (32 + row) * QP + 8 * cv, lo);
+        }
       }
+      if (vb + 1 < V / 32) load_blk(vb + 1);
       __syncthreads();
       vec8<TI> A[2];
 #pragma unroll
@@ -826,6 +954,8 @@ __global__ __launch_bounds__(kBT) void bwd_dkv_kernel(BwdArgs a) {
   }
 
   // ---------------- the chunk's query tiles at or after this key tile
+  constexpr int VGM = 4;   // V_j fragments loaded as one group
+  constexpr int VG = (V / 32) < VGM ? (V / 32) : VGM;
   // this wave's 16 keys as the B operand of S = Q K^T
   vec8<TI> Kf[K / 32];
 #pragma unroll
@@ -834,8 +964,8 @@ __global__ __launch_bounds__(kBT) void bwd_dkv_kernel(BwdArgs a) {
     const int64_t qrow0 = t0 + (int64_t)sb * kTile;
     const int nq = (int)min((int64_t)kTile, T - qrow0);
     __syncthreads();   // sQ, sG, sA, sB and the row data free
-    stage<kBT, TI, K, QP>(sQ, qg + qrow0 * K, K, nq);
-    stage<kBT, TI, V, GP>(sG, Gg + qrow0 * V, V, nq);
+    stage_dma<kBT, TI, K, QP>(sQ, qg + qrow0 * K, nq);
+    stage_dma<kBT, TI, V, GP>(sG, Gg + qrow0 * V, nq);
     if (tid < kTile) {
       float r2 = 0.f, dzt = 0.f;
       int rs = kTile * 1024;   // no key passes jk >= rs for rows beyond T
@@ -858,10 +988,16 @@ __global__ __launch_bounds__(kBT) void bwd_dkv_kernel(BwdArgs a) {
     for (int ks = 0; ks < K / 32; ++ks)
 #pragma unroll
       for (int zz = 0; zz < 2; ++zz) sacc[zz] = mma32(frag_rows(sQ, QP, 16 * (zs + zz), 32 * ks), Kf[ks], sacc[zz]);
-    for (int ks = 0; ks < V / 32; ++ks) {
-      const vec8<TI> B = frag_rows_lim(vg + key0 * V, V, 16 * jw, 32 * ks, nkeys);
 #pragma unroll
-      for (int zz = 0; zz < 2; ++zz) gacc[zz] = mma32(frag_rows(sG, GP, 16 * (zs + zz), 32 * ks), B, gacc[zz]);
+    for (int kb = 0; kb < V / 32; kb += VG) {
+      vec8<TI> Vf[VG];
+#pragma unroll
+      for (int q = 0; q < VG; ++q) Vf[q] = frag_rows_lim(vg + key0 * V, V, 16 * jw, 32 * (kb + q), nkeys);
+#pragma unroll
+      for (int q = 0; q < VG; ++q)
+#pragma unroll
+        for (int zz = 0; zz < 2; ++zz)
+          gacc[zz] = mma32(frag_rows(sG, GP, 16 * (zs + zz), 32 * (kb + q)), Vf[q], gacc[zz]);
     }
     // lane holds [t = 16 (zs + zz) + 4 g + r][j = 16 jw + i]
     {
