@@ -187,18 +187,20 @@ __device__ __forceinline__ void stage(T* __restrict__ s, const T* __restrict__ g
 // __syncthreads waits for the loads (a workgroup fence waits for direct-to-LDS
 // loads as for LDS stores).
 typedef __attribute__((address_space(3))) void lds_void_t;
-template <int NT, typename T, int NC, int SP>
+template <int NT, typename T, int NC, int SP, int ROWS = kTile>
 __device__ __forceinline__ void stage_dma(T* __restrict__ s, const T* __restrict__ g, int nrows) {
   constexpr int CPR = SP * (int)sizeof(T) / 16;   // 16-byte pieces per LDS row
   constexpr int DPR = NC * (int)sizeof(T) / 16;   // data pieces per row
   static_assert(SP * sizeof(T) % 16 == 0 && NC * sizeof(T) % 16 == 0, "whole 16-byte pieces");
+  constexpr int NP = ROWS * CPR;   // pieces of the LDS image; a partial last load runs on fewer lanes
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<T*>(g), (short)0, nrows * NC * (int)sizeof(T), 0x00020000);
-  for (int n = w; n < CPR; n += NT / 64) {
+  for (int n = w; n < (NP + 63) / 64; n += NT / 64) {
     const int c = 64 * n + lane, row = c / CPR, ch = min(c % CPR, DPR - 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(reinterpret_cast<char*>(s) + 1024 * n), 16,
-                                             row * NC * (int)sizeof(T) + 16 * ch, 0, 0, 0);
+    if (NP % 64 == 0 || c < NP)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void_t*)(reinterpret_cast<char*>(s) + 1024 * n), 16,
+                                               row * NC * (int)sizeof(T) + 16 * ch, 0, 0, 0);
   }
 }
 // The same copy one 16-byte piece at a time (few registers: for loops that
@@ -270,7 +272,7 @@ struct BwdArgs {
   void* G;                               // g per token [BH][T][V]
   float* dz;                             // dz per token [BH][T]
   float* qdq;                            // q . dq per token [BH][T]
-  float* Es;                             // end adjoint of every chunk [BH][Nc][V][K], float32
+  float* Es;                             // end adjoint of every chunk [BH][Nc][V][K]: float32, or its bf16 hi/lo terms
   float* es;                             // [BH][Nc][K]
   double* Ms;                            // its log scale [BH][Nc] (-inf: zero)
   float* L0;                             // chunk 0's share [BH][V][K] (initial state's gradient)
@@ -278,6 +280,7 @@ struct BwdArgs {
   const float *C0, *n0, *m0;             // initial state, or null
   float *dC0, *dn0, *dm0;                // its gradient, or null
   int zero_first;                        // no initial state: chunk 0 starts from zero
+  int es_split;                          // bfloat16: Es holds hi, lo bf16 terms interleaved by 4 (see bwd_fold_kernel)
   int64_t T, Nc, V, K, BH;
   int L;
 };
@@ -770,12 +773,31 @@ __global__ __launch_bounds__(kThreads) void bwd_fold_kernel(BwdArgs a) {
     A = al * Lc + be * A;
     M = Mn;
   };
+  // The end adjoints of the value-key matrix: for bfloat16 inputs each group
+  // of four as its bf16 terms hi (4) then lo (4), in the same 16 bytes, the
+  // operand form the dk/dv kernel multiplies with. Slot c's local share has
+  // been read before slot c is written, so the slots can be rewritten in place.
+  const bool split = a.es_split && !is_e;
+  auto put = [&](float* p, const f32x4& v) {
+    if (split) {
+      bf16x4 hi, lo;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        hi[r] = (__bf16)v[r];
+        lo[r] = (__bf16)(v[r] - (float)hi[r]);
+      }
+      *reinterpret_cast<bf16x4*>(p) = hi;
+      *reinterpret_cast<bf16x4*>(p + 2) = lo;
+    } else {
+      *reinterpret_cast<f32x4*>(p) = v;
+    }
+  };
   for (int64_t c = Nc - 1; c >= 1; --c) {
-    *reinterpret_cast<f32x4*>(base + c * stride) = A;
+    put(base + c * stride, A);
     if (x == 0) a.Ms[bh * Nc + c] = M;
     fold(c, *reinterpret_cast<const f32x4*>(base + (c - 1) * stride));
   }
-  *reinterpret_cast<f32x4*>(base) = A;
+  put(base, A);
   if (x == 0) a.Ms[bh * Nc] = M;
   if (a.dC0) {
     const float* l0 = is_e ? a.L0e + bh * K + 4 * (x - vk4) : a.L0 + bh * V * K + 4 * x;
@@ -801,9 +823,37 @@ struct DkvLds {
   // float: u2, r2, dz, wj [64]; di [4][64]; e [K]; then int rs [64]
   static constexpr int nF = 4 * kTile + 4 * kTile + K;
   static constexpr int oI = oF + nF * 4;
-  static constexpr int bytes = oI + kTile * 4;
+  // blocks of 32 end-adjoint rows: bfloat16, each row as 4-element groups of
+  // hi then lo (pitch EP elements); float32, rows of K (pitch QP). The first
+  // buffer is the Q region, the second follows.
+  static constexpr int EP = sizeof(TI) == 2 ? 2 * K + 16 : QP;
+  static constexpr int oE2 = (oI + kTile * 4 + 15) / 16 * 16;
+  static constexpr int bytes = oE2 + 32 * EP * (int)sizeof(TI);
+  static_assert(32 * EP * sizeof(TI) <= kTile * QP * sizeof(TI), "an adjoint block fits the Q region");
   static_assert(bytes <= 160 * 1024, "fits the LDS of a CU");
 };
+
+// Transposed operand fragment of an interleaved adjoint block (row pitch P):
+// lane (i, g) receives the hi (part 0) or lo (part 1) terms of column n0 + i
+// of rows k0 + 8 g .. + 7, where column d's terms sit at 2 d - d % 4 (hi)
+// and 4 further (lo) of its row, as the fold kernel stores them.
+__device__ __forceinline__ bf16x8 frag_cols_il(const __bf16* X, int P, int k0, int n0, int part) {
+  const int lane = threadIdx.x & 63, i = lane & 15, g = lane >> 4;
+  const __bf16* p = X + (k0 + 8 * g + (i >> 2)) * P + 2 * n0 + 8 * (i & 3) + 4 * part;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)p);
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_b4*)(p + 4 * P));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// Row operand fragment of an interleaved adjoint block: lane (i, g) receives
+// the hi and lo terms of row r0 + i, columns k0 + 8 g .. + 7.
+__device__ __forceinline__ void frag_rows_il(const __bf16* X, int P, int r0, int k0, bf16x8& hi, bf16x8& lo) {
+  const int lane = threadIdx.x & 63;
+  const __bf16* p = X + (r0 + (lane & 15)) * P + 2 * (k0 + 8 * (lane >> 4));
+  const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+  const bf16x8 b = *reinterpret_cast<const bf16x8*>(p + 8);
+  hi = __builtin_shufflevector(a, b, 0, 1, 2, 3, 8, 9, 10, 11);
+  lo = __builtin_shufflevector(a, b, 4, 5, 6, 7, 12, 13, 14, 15);
+}
 
 template <typename TI, int K, int V>
 __global__ __launch_bounds__(kBT) void bwd_dkv_kernel(BwdArgs a) {
@@ -841,14 +891,24 @@ __global__ __launch_bounds__(kBT) void bwd_dkv_kernel(BwdArgs a) {
   const TI* vg = static_cast<const TI*>(a.v) + bh * T * V;
   const TI* Gg = static_cast<const TI*>(a.G) + bh * T * V;
 
-  f32x4 ak[2][CK], av[2][CV];
+  // dk: wave (rh, cw) owns key rows 32 rh .. + 31, columns (K / 4) cw .. ;
+  // dv: wave w owns key rows 16 jw .. + 15 and the value tiles 2 vb + rh
+  // (16 columns each, vb = 0 .. V / 32 - 1), so that every 32-row block of
+  // the end adjoint below gives each wave the same share of the work
+  constexpr int NVT = V / 32;
+  f32x4 ak[2][CK], av[NVT];
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
+  for (int x = 0; x < 2; ++x)
 #pragma unroll
     for (int y = 0; y < CK; ++y) ak[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int y = 0; y < CV; ++y) av[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int y = 0; y < NVT; ++y) av[y] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // this wave's 16 keys: the A operand of dv's end-adjoint term and the B
+  // operand of S = Q K^T
+  vec8<TI> Kf[K / 32];
+#pragma unroll
+  for (int ks = 0; ks < K / 32; ++ks) Kf[ks] = frag_rows_lim(kg + key0 * K, K, 16 * jw, 32 * ks, nkeys);
 
   // ---------------- key data; the end adjoint's term w_j (A^T v_j + a), w_j A k_j
   const double Mc = a.Ms[bh * a.Nc + c];
@@ -865,78 +925,58 @@ __global__ __launch_bounds__(kBT) void bwd_dkv_kernel(BwdArgs a) {
     s_wj[tid] = wj;
   }
   if (later) {
-    // The end adjoint is float32. Its products with a key (k_j . A) can
+    // The end adjoint A is float32. Its products with a key (k_j . A) can
     // cancel strongly (rows whose g is large because their q . k is small),
-    // so it enters the MFMAs as two bfloat16 terms, hi + lo.
-    const float* Es = a.Es + (bh * a.Nc + c) * V * K;
+    // so for bfloat16 it enters the MFMAs as two terms, hi + lo, which the
+    // fold kernel stores interleaved in place of the float32 values. It is
+    // streamed once, 32 rows (values) at a time, through two LDS buffers,
+    // the next block's direct-to-LDS loads in flight while this one's
+    // products run; each block serves both
+    //   dk[j][d] += sum_v V_j[j][v] A[v][d]   (every wave: its dk tile)
+    //   dv[j][v] += sum_d K_j[j][d] A[v][d]   (every wave: value tile 2 vb + rh)
+    constexpr int EP = L::EP;
+    TI* Ebuf[2] = {sQ, reinterpret_cast<TI*>(smem + L::oE2)};
     for (int d = tid; d < K; d += kBT) s_e[d] = a.es[(bh * a.Nc + c) * K + d];
-    stage_dma<kBT, TI, K, QP>(sQ, kg + key0 * K, nkeys);
     stage_dma<kBT, TI, V, GP>(sG, vg + key0 * V, nkeys);
-    __syncthreads();
-    // dv[j][v] += sum_d K_j[j][d] A[v][d]  (A rows straight from memory, in
-    // groups of EG fragments whose loads are issued together)
-    constexpr int EG = CV < 4 ? CV : 4;
-    static_assert(CV % EG == 0, "whole groups");
-#pragma unroll
-    for (int ks = 0; ks < K / 32; ++ks) {
-      vec8<TI> A[2];
-#pragma unroll
-      for (int x = 0; x < 2; ++x) A[x] = frag_rows(sQ, QP, 32 * rh + 16 * x, 32 * ks);
-#pragma unroll
-      for (int y0 = 0; y0 < CV; y0 += EG) {
-        f32x8 eb[EG];
-#pragma unroll
-        for (int q = 0; q < EG; ++q) eb[q] = frag_rows(Es, K, (V / 4) * cw + 16 * (y0 + q), 32 * ks);
-#pragma unroll
-        for (int q = 0; q < EG; ++q) {
-          vec8<TI> hi, lo;
-          split8(eb[q], hi, lo);
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            av[x][y0 + q] = mma32(A[x], hi, av[x][y0 + q]);
-            if constexpr (sizeof(TI) == 2) av[x][y0 + q] = mma32(A[x], lo, av[x][y0 + q]);
-          }
-        }
-      }
-    }
-    // dk[j][d] += sum_v V_j[j][v] A[v][d], A staged 32 rows at a time: hi in
-    // rows 0..31 of sQ, lo in rows 32..63
-    constexpr int NB = (32 * (K / 8) + kBT - 1) / kBT;
-    f32x8 ep[NB];
-    auto load_blk = [&](int vb) {
-#pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        const int it = tid + n * kBT, row = it / (K / 8), cv = it % (K / 8);
-        if (it < 32 * (K / 8)) ep[n] = load8(Es + (int64_t)(32 * vb + row) * K + 8 * cv);
+    const float* Es = a.Es + (bh * a.Nc + c) * V * K;
+    auto load_block = [&](int vb, TI* dst) {
+      if constexpr (sizeof(TI) == 2) {
+        stage_dma<kBT, __bf16, 2 * K, EP, 32>(reinterpret_cast<__bf16*>(dst),
+                                              reinterpret_cast<const __bf16*>(Es) + (int64_t)32 * vb * 2 * K, 32);
+      } else {
+        stage_dma<kBT, float, K, EP, 32>(reinterpret_cast<float*>(dst), Es + (int64_t)32 * vb * K, 32);
       }
     };
-    load_blk(0);
-    for (int vb = 0; vb < V / 32; ++vb) {
-      __syncthreads();   // sQ free (K_j or the previous block consumed)
+    load_block(0, Ebuf[0]);
 #pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        const int it = tid + n * kBT, row = it / (K / 8), cv = it % (K / 8);
-        if (it < 32 * (K / 8)) {
-          vec8<TI> hi, lo;
-          split8(ep[n], hi, lo);
-          store8(sQ + row * QP + 8 * cv, hi);
-          store8(sQ + (32 + row) * QP + 8 * cv, lo);
-        }
-      }
-      if (vb + 1 < V / 32) load_blk(vb + 1);
-      __syncthreads();
+    for (int vb = 0; vb < V / 32; ++vb) {
+      __syncthreads();   // block vb (and V_j) landed; the other buffer's last readers are done
+      if (vb + 1 < V / 32) load_block(vb + 1, Ebuf[(vb + 1) & 1]);
+      const TI* Eb = Ebuf[vb & 1];
       vec8<TI> A[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x) A[x] = frag_rows(sG, GP, 32 * rh + 16 * x, 32 * vb);
 #pragma unroll
       for (int y = 0; y < CK; ++y) {
-        const vec8<TI> Bh = frag_cols(sQ, QP, 0, (K / 4) * cw + 16 * y);
-#pragma unroll
-        for (int x = 0; x < 2; ++x) ak[x][y] = mma32(A[x], Bh, ak[x][y]);
         if constexpr (sizeof(TI) == 2) {
-          const vec8<TI> Bl = frag_cols(sQ, QP, 32, (K / 4) * cw + 16 * y);
+          const bf16x8 Bh = frag_cols_il(Eb, EP, 0, (K / 4) * cw + 16 * y, 0);
+          const bf16x8 Bl = frag_cols_il(Eb, EP, 0, (K / 4) * cw + 16 * y, 1);
 #pragma unroll
-          for (int x = 0; x < 2; ++x) ak[x][y] = mma32(A[x], Bl, ak[x][y]);
+          for (int x = 0; x < 2; ++x) ak[x][y] = mma32(A[x], Bl, mma32(A[x], Bh, ak[x][y]));
+        } else {
+          const vec8<TI> B = frag_cols(Eb, EP, 0, (K / 4) * cw + 16 * y);
+#pragma unroll
+          for (int x = 0; x < 2; ++x) ak[x][y] = mma32(A[x], B, ak[x][y]);
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < K / 32; ++ks) {
+        if constexpr (sizeof(TI) == 2) {
+          bf16x8 Bh, Bl;
+          frag_rows_il(Eb, EP, 16 * rh, 32 * ks, Bh, Bl);
+          av[vb] = mma32(Kf[ks], Bl, mma32(Kf[ks], Bh, av[vb]));
+        } else {
+          av[vb] = mma32(Kf[ks], frag_rows(Eb, EP, 16 * rh, 32 * ks), av[vb]);
         }
       }
     }
@@ -948,18 +988,18 @@ __global__ __launch_bounds__(kBT) void bwd_dkv_kernel(BwdArgs a) {
         const float wj = s_wj[jl];
 #pragma unroll
         for (int y = 0; y < CK; ++y) ak[x][y][r] = wj * (ak[x][y][r] + s_e[(K / 4) * cw + 16 * y + i]);
-#pragma unroll
-        for (int y = 0; y < CV; ++y) av[x][y][r] *= wj;
       }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float wj = s_wj[16 * jw + 4 * g + r];
+#pragma unroll
+      for (int y = 0; y < NVT; ++y) av[y][r] *= wj;
+    }
   }
 
   // ---------------- the chunk's query tiles at or after this key tile
   constexpr int VGM = 4;   // V_j fragments loaded as one group
   constexpr int VG = (V / 32) < VGM ? (V / 32) : VGM;
-  // this wave's 16 keys as the B operand of S = Q K^T
-  vec8<TI> Kf[K / 32];
-#pragma unroll
-  for (int ks = 0; ks < K / 32; ++ks) Kf[ks] = frag_rows_lim(kg + key0 * K, K, 16 * jw, 32 * ks, nkeys);
   for (int sb = jt; sb < ntiles; ++sb) {
     const int64_t qrow0 = t0 + (int64_t)sb * kTile;
     const int nq = (int)min((int64_t)kTile, T - qrow0);
@@ -1023,24 +1063,18 @@ __global__ __launch_bounds__(kBT) void bwd_dkv_kernel(BwdArgs a) {
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      vec8<TI> A[2], B2[2];
+      vec8<TI> A[2];
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        A[x] = frag_rows(sA, AP, 32 * rh + 16 * x, 32 * ks);
-        B2[x] = frag_rows(sB, AP, 32 * rh + 16 * x, 32 * ks);
-      }
+      for (int x = 0; x < 2; ++x) A[x] = frag_rows(sA, AP, 32 * rh + 16 * x, 32 * ks);
 #pragma unroll
       for (int y = 0; y < CK; ++y) {
         const vec8<TI> B = frag_cols(sQ, QP, 32 * ks, (K / 4) * cw + 16 * y);
 #pragma unroll
         for (int x = 0; x < 2; ++x) ak[x][y] = mma32(A[x], B, ak[x][y]);
       }
+      const vec8<TI> B2 = frag_rows(sB, AP, 16 * jw, 32 * ks);
 #pragma unroll
-      for (int y = 0; y < CV; ++y) {
-        const vec8<TI> B = frag_cols(sG, GP, 32 * ks, (V / 4) * cw + 16 * y);
-#pragma unroll
-        for (int x = 0; x < 2; ++x) av[x][y] = mma32(B2[x], B, av[x][y]);
-      }
+      for (int y = 0; y < NVT; ++y) av[y] = mma32(B2, frag_cols(sG, GP, 32 * ks, 16 * (2 * y + rh)), av[y]);
     }
   }
 
@@ -1059,14 +1093,17 @@ __global__ __launch_bounds__(kBT) void bwd_dkv_kernel(BwdArgs a) {
         p += ak[x][y][r] * kv;
         sQ[jl * QP + d] = from_f32<TI>(ak[x][y][r]);
       }
-#pragma unroll
-      for (int y = 0; y < CV; ++y) sG[jl * GP + (V / 4) * cw + 16 * y + i] = from_f32<TI>(av[x][y][r]);
+
       p += __shfl_xor(p, 1, 64);
       p += __shfl_xor(p, 2, 64);
       p += __shfl_xor(p, 4, 64);
       p += __shfl_xor(p, 8, 64);
       if (i == 0) s_di[64 * cw + jl] = p;
     }
+#pragma unroll
+  for (int y = 0; y < NVT; ++y)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sG[(16 * jw + 4 * g + r) * GP + 16 * (2 * y + rh) + i] = from_f32<TI>(av[y][r]);
   __syncthreads();
   unstage<kBT, TI, K, QP>(static_cast<TI*>(a.dk) + (bh * T + key0) * K, K, sQ, nkeys);
   unstage<kBT, TI, V, GP>(static_cast<TI*>(a.dv) + (bh * T + key0) * V, V, sG, nkeys);
@@ -1236,6 +1273,7 @@ hipError_t launch_bwd(const BwdLaunch& b, const GateBuffers& gb, const ChunkStat
   a.C0 = b.C0; a.n0 = b.n0; a.m0 = b.m0;
   a.dC0 = b.dC0; a.dn0 = b.dn0; a.dm0 = b.dm0;
   a.zero_first = b.C0 == nullptr;
+  a.es_split = b.bf16 ? 1 : 0;
   a.T = b.T; a.Nc = b.Nc; a.V = b.V; a.K = b.K; a.BH = b.BH; a.L = b.L;
   if (b.bf16) {
     switch (b.K) {
