@@ -336,7 +336,7 @@ struct BwdLayout {
 
 BwdLayout layout_bwd(int64_t BH, int64_t T, int64_t Nc, int64_t K, int64_t V, int64_t elem) {
   BwdLayout b;
-  b.fw = layout(BH, T, Nc, K, V, 4, true);
+  b.fw = layout(BH, T, Nc, K, V, elem, true);   // chunk-start states in the input dtype
   size_t off = b.fw.total;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
   b.G = take(BH * T * V * elem);
@@ -459,6 +459,7 @@ int bwd_chunkwise(const mlstm_bwd_args* a, int chunk, void* workspace, size_t wo
   cs.Cs = ws + w.fw.Cs;
   cs.ns = reinterpret_cast<float*>(ws + w.fw.ns);
   cs.ms = reinterpret_cast<double*>(ws + w.fw.ms);
+  cs.cs_bf16 = b.bf16;
   mlstm_impl::BwdBuffers bb;
   bb.G = ws + w.G;
   bb.dz = reinterpret_cast<float*>(ws + w.dz);

@@ -77,6 +77,7 @@ struct StateArgsB {
   float *C_out, *n_out, *m_out;
   int64_t T, Nc, V, BH;
   int L;
+  int cs_bf16;   // store the chunk-start states as bf16 (Cs then points to bf16)
 };
 
 // One workgroup per (head, 64 k x 64 v tile of C^T), four waves of 32 x 32.
@@ -180,13 +181,21 @@ __global__ __launch_bounds__(kThreads) void state_kernel_bf16(StateArgsB a) {
     if (jc == 0) {   // chunk start: store the carried state, derive this chunk's scalars
       if (a.Cs) {
         float* Cs = a.Cs + (bh * a.Nc + c) * V * K;
+        __bf16* Cb = reinterpret_cast<__bf16*>(a.Cs) + (bh * a.Nc + c) * V * K;
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
           const int kk = 64 * kt + 32 * wk + 16 * x + 4 * g;
 #pragma unroll
           for (int y = 0; y < 2; ++y) {
             const int64_t vv = 64 * vt + 32 * wv + 16 * y + i;
-            *reinterpret_cast<f32x4*>(Cs + vv * K + kk) = acc[x][y];
+            if (a.cs_bf16) {
+              bf16x4 o;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) o[r] = (__bf16)acc[x][y][r];
+              *reinterpret_cast<bf16x4*>(Cb + vv * K + kk) = o;
+            } else {
+              *reinterpret_cast<f32x4*>(Cs + vv * K + kk) = acc[x][y];
+            }
           }
           if (n_tile && i == 0) *reinterpret_cast<f32x4*>(a.ns + (bh * a.Nc + c) * K + kk) = nacc[x];
         }
@@ -618,6 +627,7 @@ hipError_t run_state_b(const FwdLaunch& f, const GateBuffers& gb, const ChunkSta
   a.C0 = f.C0; a.n0 = f.n0; a.m0 = f.m0;
   a.Cs = static_cast<float*>(cs.Cs);
   a.ns = cs.ns; a.ms = cs.ms;
+  a.cs_bf16 = cs.cs_bf16;
   a.C_out = f.C_out; a.n_out = f.n_out; a.m_out = f.m_out;
   a.T = f.T; a.Nc = f.Nc; a.V = f.V; a.BH = f.BH; a.L = f.L;
   const int64_t grid = f.BH * (K / 64) * (f.V / 64);

@@ -266,7 +266,7 @@ struct BwdArgs {
   void *dq, *dk, *dv, *dout;             // [BH][T][d]
   float *di, *df;                        // [BH][T]
   GateBuffers gb;
-  const float* Cs;                       // forward chunk-start states [BH][Nc][V][K]
+  const void* Cs;                        // forward chunk-start states [BH][Nc][V][K], input dtype
   const float* ns;                       // [BH][Nc][K]
   const double* ms;                      // [BH][Nc]
   void* G;                               // g per token [BH][T][V]
@@ -437,32 +437,56 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(BwdArgs a) {
     const TI* og = static_cast<const TI*>(a.o) + (bh * T + row0) * V;
     TI* Gg = static_cast<TI*>(a.G) + (bh * T + row0) * V;
     TI* dog = static_cast<TI*>(a.dout) + (bh * T + row0) * V;
-    for (int rr = 0; rr < 8; ++rr) {
-      const int row = 8 * w + rr;
-      const bool valid = row < nrows;
-      const float inv = 1.f / s_den[row];
-      float dot = 0.f;
-      for (int cv = lane; cv < V / 8; cv += 64) {
-        vec8<TI> gv = zero_v8<TI>();
-        if (valid) {
-          const int64_t off = (int64_t)row * V + 8 * cv;
-          const vec8<TI> dh8 = load8(dhg + off), h8 = load8(hg + off), o8 = load8(og + off);
-          vec8<TI> dov;
+    // the rows' dh, h and o~ pieces for RB rows at a time are loaded before
+    // any is used (one memory latency per group of rows)
+    constexpr int RB = 4, CPL = (V / 8 + 63) / 64;   // rows per group; 8-element pieces per lane and row
+    for (int r0 = 0; r0 < 8; r0 += RB) {
+      vec8<TI> dh8[RB][CPL], h8[RB][CPL], o8[RB][CPL];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float dh = to_f32(dh8[e]), hv = to_f32(h8[e]);
-            const float sg = sigmoid(to_f32(o8[e]));
-            dot += dh * hv;
-            gv[e] = from_f32<TI>(dh * sg * inv);
-            dov[e] = from_f32<TI>(dh * hv * (1.f - sg));
+      for (int q = 0; q < RB; ++q) {
+        const int row = 8 * w + r0 + q;
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) {
+          const int cv = lane + 64 * u;
+          dh8[q][u] = h8[q][u] = o8[q][u] = zero_v8<TI>();
+          if (row < nrows && cv < V / 8) {
+            const int64_t off = (int64_t)row * V + 8 * cv;
+            dh8[q][u] = load8(dhg + off);
+            h8[q][u] = load8(hg + off);
+            o8[q][u] = load8(og + off);
           }
-          store8(Gg + off, gv);
-          store8(dog + off, dov);
         }
-        store8(sG + row * GP + 8 * cv, gv);
       }
-      dot = wave_sum(dot);
-      if (lane == 0) s_dz[row] = valid ? -s_sg[row] * dot * inv : 0.f;
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        const int row = 8 * w + r0 + q;
+        const bool valid = row < nrows;
+        const float inv = 1.f / s_den[row];
+        float dot = 0.f;
+#pragma unroll
+        for (int u = 0; u < CPL; ++u) {
+          const int cv = lane + 64 * u;
+          if (cv >= V / 8) continue;
+          vec8<TI> gv = zero_v8<TI>();
+          if (valid) {
+            const int64_t off = (int64_t)row * V + 8 * cv;
+            vec8<TI> dov;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float dh = to_f32(dh8[q][u][e]), hv = to_f32(h8[q][u][e]);
+              const float sg = sigmoid(to_f32(o8[q][u][e]));
+              dot += dh * hv;
+              gv[e] = from_f32<TI>(dh * sg * inv);
+              dov[e] = from_f32<TI>(dh * hv * (1.f - sg));
+            }
+            store8(Gg + off, gv);
+            store8(dog + off, dov);
+          }
+          store8(sG + row * GP + 8 * cv, gv);
+        }
+        dot = wave_sum(dot);
+        if (lane == 0) s_dz[row] = valid ? -s_sg[row] * dot * inv : 0.f;
+      }
     }
   }
   __syncthreads();
@@ -474,46 +498,26 @@ __global__ __launch_bounds__(kBT) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int y = 0; y < CT; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (has_state) {
-    const float* Cst = a.Cs + (bh * a.Nc + c) * V * K;
-    // 64 rows of the float32 state per round, rounded once to the operand type
-    // (the carried term of dq does not cancel the way the state's products
-    // with single keys can); the next round's rows are loaded into registers
-    // while this round's products run
-    constexpr int NL = (kTile * (K / 8) + kBT - 1) / kBT;
-    f32x8 pre[NL];
-    auto load_round = [&](int vb) {
+    // the chunk's start state, stored by the state pass in the operand type
+    // (rounded once: the carried term of dq does not cancel the way the
+    // state's products with single keys can), 32 rows (values) at a time
+    // through the two halves of the K region, the next block's
+    // direct-to-LDS loads in flight while this one's products run
+    const TI* Cst = static_cast<const TI*>(a.Cs) + (bh * a.Nc + c) * V * K;
+    TI* const Cb[2] = {sK, sK + 32 * QP};
+    stage_dma<kBT, TI, K, QP, 32>(Cb[0], Cst, 32);
 #pragma unroll
-      for (int n = 0; n < NL; ++n) {
-        const int it = tid + n * kBT, row = it / (K / 8), cv = it % (K / 8);
-        if (it < kTile * (K / 8)) pre[n] = load8(Cst + (int64_t)(64 * vb + row) * K + 8 * cv);
-      }
-    };
-    load_round(0);
-    for (int vb = 0; vb < V / 64; ++vb) {
-      if (vb > 0) __syncthreads();   // sK free
+    for (int vb = 0; vb < V / 32; ++vb) {
+      __syncthreads();   // block vb landed; the other half's readers are done
+      if (vb + 1 < V / 32) stage_dma<kBT, TI, K, QP, 32>(Cb[(vb + 1) & 1], Cst + (int64_t)32 * (vb + 1) * K, 32);
+      vec8<TI> A[2];
 #pragma unroll
-      for (int n = 0; n < NL; ++n) {
-        const int it = tid + n * kBT, row = it / (K / 8), cv = it % (K / 8);
-        if (it < kTile * (K / 8)) {
-          vec8<TI> o;
+      for (int x = 0; x < 2; ++x) A[x] = frag_rows(sG, GP, 32 * rh + 16 * x, 32 * vb);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[e] = from_f32<TI>(pre[n][e]);
-          store8(sK + row * QP + 8 * cv, o);
-        }
-      }
-      if (vb + 1 < V / 64) load_round(vb + 1);
-      __syncthreads();
+      for (int y = 0; y < CT; ++y) {
+        const vec8<TI> B = frag_cols(Cb[vb & 1], QP, 0, (K / 4) * cw + 16 * y);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        vec8<TI> A[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) A[x] = frag_rows(sG, GP, 32 * rh + 16 * x, 64 * vb + 32 * ks);
-#pragma unroll
-        for (int y = 0; y < CT; ++y) {
-          const vec8<TI> B = frag_cols(sK, QP, 32 * ks, (K / 4) * cw + 16 * y);
-#pragma unroll
-          for (int x = 0; x < 2; ++x) acc[x][y] = mma32(A[x], B, acc[x][y]);
-        }
+        for (int x = 0; x < 2; ++x) acc[x][y] = mma32(A[x], B, acc[x][y]);
       }
     }
 #pragma unroll
@@ -1266,7 +1270,7 @@ hipError_t launch_bwd(const BwdLaunch& b, const GateBuffers& gb, const ChunkStat
   a.dq = b.dq; a.dk = b.dk; a.dv = b.dv; a.dout = b.dout;
   a.di = b.di; a.df = b.df;
   a.gb = gb;
-  a.Cs = static_cast<const float*>(cs.Cs); a.ns = cs.ns; a.ms = cs.ms;
+  a.Cs = cs.Cs; a.ns = cs.ns; a.ms = cs.ms;
   a.G = bb.G; a.dz = bb.dz; a.qdq = bb.qdq;
   a.Es = static_cast<float*>(bb.Es); a.es = bb.es; a.Ms = bb.Ms;
   a.L0 = bb.L0; a.L0e = bb.L0e;

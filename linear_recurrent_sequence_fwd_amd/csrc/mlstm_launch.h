@@ -28,12 +28,14 @@ struct GateBuffers {
                 // w0 = hi + lo + lo2 (about 24 bits); null when not wanted
 };
 
-// Chunk-start states written by the state pass: Cs [BH][Nc][V][K] fp32,
+// Chunk-start states written by the state pass: Cs [BH][Nc][V][K] fp32 (or
+// bf16 when cs_bf16: the backward pass, which multiplies them as bf16),
 // ns [BH][Nc][K] fp32, ms [BH][Nc] fp64.
 struct ChunkStates {
   void* Cs;
   float* ns;
   double* ms;
+  int cs_bf16 = 0;
 };
 
 // Chunk states of the fused path (mlstm_fused.hip), S chunks of TPS 64-token

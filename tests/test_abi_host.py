@@ -449,8 +449,8 @@ def test_backward_workspace_size():
         Nc = -(-T // chunk)
         need = lib.mlstm_bwd_chunkwise_workspace_size(ctypes.byref(a), chunk)
         # gate data, forward chunk states, g per token, dz and q.dq, the end adjoints
-        # (the chunk states, forward and adjoint, are float32)
-        floor = (BH * T * (8 * 3 + 4 * 2) + BH * Nc * (8 * 2 + 4) + BH * Nc * (V * K * 4 + K * 4 + 8)
+        # (the forward chunk states in the input dtype, the adjoints float32)
+        floor = (BH * T * (8 * 3 + 4 * 2) + BH * Nc * (8 * 2 + 4) + BH * Nc * (V * K * es + K * 4 + 8)
                  + BH * T * V * es + BH * T * 8 + BH * Nc * (V * K * 4 + K * 4 + 8) + BH * (V * K + K) * 4)
         assert floor <= need <= floor + 64 * 256
     a.T = 0
