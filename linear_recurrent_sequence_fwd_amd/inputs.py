@@ -1,5 +1,6 @@
-"""Seeded synthetic inputs for the mLSTM cell forward and decode step, and
-for the sLSTM cell forward (make_slstm_inputs, make_slstm_state).
+"""Seeded synthetic inputs for the mLSTM cell forward and decode step, for
+the sLSTM cell forward (make_slstm_inputs, make_slstm_state) and for the
+mLSTM block around the cell (make_block_inputs).
 
 This module draws random numbers and nothing else of the method: it holds no
 gate activation, no recurrence and no normalisation. The same arrays feed the
@@ -33,6 +34,7 @@ __all__ = [
     "make_state",
     "make_slstm_inputs",
     "make_slstm_state",
+    "make_block_inputs",
 ]
 
 
@@ -165,3 +167,77 @@ def make_slstm_state(B: int, H: int, D: int, seed: int = 0):
     m = rng.standard_normal((B, H, D), dtype=np.float32)
     h = rng.uniform(-1.0, 1.0, (B, H, D)).astype(np.float32)
     return c, n, m, h
+
+
+def make_block_inputs(B: int, T: int, D: int, H: int, d_qk: int, d_v: int, KC: int = 4,
+                      seed: int = 0, f_mean: float = 3.0) -> tuple:
+    """Seeded input and parameters of the mLSTM block around the cell
+    (pre-up-projection residual block; inner width E = 2 D = H d_v).
+
+    Returns ``(x, p)``: x [B, T, D] and a dict of parameters. Matrices are
+    rounded to bfloat16 (kept as float32 arrays holding bf16 values, like the
+    activations above); vectors stay float32. Draws from
+    ``Generator(PCG64([seed, 0xB10C]))`` in this order, each N(0, 1) times the
+    scale given:
+
+    =========  ==============  ========================================
+    name       shape           scale
+    =========  ==============  ========================================
+    x          [B, T, D]       1
+    ln_w       [D]             0.1, plus 1
+    ln_b       [D]             0.1
+    W_up       [2E, D]         1 / sqrt(D)
+    b_up       [2E]            0.1
+    conv_w     [E, KC]         1 / sqrt(KC)
+    conv_b     [E]             0.1
+    W_q, W_k   [H, d_qk, E/H]  1 / sqrt(E/H)
+    b_q, b_k   [H d_qk]        0.1
+    W_v        [H, d_v, E/H]   1 / sqrt(E/H)
+    b_v        [E]             0.1
+    w_i, w_f   [H, E]          1.7 / sqrt(E)
+    b_i        [H]             0
+    b_f        [H]             0, plus f_mean
+    gn_w       [E]             0.1, plus 1
+    gn_b       [E]             0.1
+    skip       [E]             0.1, plus 1
+    W_down     [D, E]          1 / sqrt(E)
+    b_down     [D]             0.1
+    =========  ==============  ========================================
+
+    The 1.7 / sqrt(E) gate weights give gate preactivations of about unit
+    spread over the block's conv outputs (whose mean square is about 0.35),
+    so that the forget gate's preactivation is near N(f_mean, 1) and the
+    input gate's near N(0, 1), the spreads of the cell workloads.
+    eps_ln = eps_gn = 1e-5.
+    """
+    E = 2 * D
+    if H * d_v != E or E % H:
+        raise ValueError("need H * d_v == 2 * D")
+    rng = np.random.Generator(np.random.PCG64([seed, 0xB10C]))
+    n = lambda shape, s: rng.standard_normal(shape, dtype=np.float32) * np.float32(s)
+    x = bf16_round(n((B, T, D), 1.0))
+    p = {}
+    p["ln_w"] = n((D,), 0.1) + np.float32(1.0)
+    p["ln_b"] = n((D,), 0.1)
+    p["W_up"] = bf16_round(n((2 * E, D), 1.0 / np.sqrt(D)))
+    p["b_up"] = n((2 * E,), 0.1)
+    p["conv_w"] = n((E, KC), 1.0 / np.sqrt(KC))
+    p["conv_b"] = n((E,), 0.1)
+    p["W_q"] = bf16_round(n((H, d_qk, E // H), 1.0 / np.sqrt(E // H)))
+    p["b_q"] = n((H * d_qk,), 0.1)
+    p["W_k"] = bf16_round(n((H, d_qk, E // H), 1.0 / np.sqrt(E // H)))
+    p["b_k"] = n((H * d_qk,), 0.1)
+    p["W_v"] = bf16_round(n((H, d_v, E // H), 1.0 / np.sqrt(E // H)))
+    p["b_v"] = n((E,), 0.1)
+    p["w_i"] = bf16_round(n((H, E), 1.7 / np.sqrt(E)))
+    p["w_f"] = bf16_round(n((H, E), 1.7 / np.sqrt(E)))
+    p["b_i"] = np.zeros(H, np.float32)
+    p["b_f"] = np.full(H, f_mean, np.float32)
+    p["gn_w"] = n((E,), 0.1) + np.float32(1.0)
+    p["gn_b"] = n((E,), 0.1)
+    p["skip"] = n((E,), 0.1) + np.float32(1.0)
+    p["W_down"] = bf16_round(n((D, E), 1.0 / np.sqrt(E)))
+    p["b_down"] = n((D,), 0.1)
+    p["eps_ln"] = 1e-5
+    p["eps_gn"] = 1e-5
+    return x, p
