@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MLSTM_ABI_VERSION 2
+#define MLSTM_ABI_VERSION 3
 
 typedef enum mlstm_status {
   MLSTM_OK = 0,
@@ -70,7 +70,10 @@ typedef struct mlstm_fwd_args {
   const void* q;          /* [B,H,T,d_qk] */
   const void* k;          /* [B,H,T,d_qk] */
   const void* v;          /* [B,H,T,d_v]  */
-  const void* o_pre;      /* [B,H,T,d_v]  output-gate preactivation */
+  const void* o_pre;      /* [B,H,T,d_v]  output-gate preactivation; in mlstm_fwd_chunkwise with
+                             MLSTM_BF16 and d_v a multiple of 128 it may be NULL: no output gate,
+                             h = C q / max(|n^T q|, 1) (the block of mlstm_block.h applies its gate
+                             outside the cell) */
   const float* i_pre;     /* [B,H,T]      input-gate preactivation */
   const float* f_pre;     /* [B,H,T]      forget-gate preactivation */
   void* h;                /* [B,H,T,d_v]  output (written) */

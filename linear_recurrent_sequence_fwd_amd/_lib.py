@@ -1,5 +1,6 @@
 """ctypes binding of libmlstm.so: the C ABI declared in include/mlstm.h,
-include/slstm.h and (measurement entry points) include/mlstm_prof.h.
+include/mlstm_block.h, include/slstm.h and (measurement entry points)
+include/mlstm_prof.h.
 
 Argument marshalling only. Tensors supply device memory and the current
 stream; every step of the computation runs in the library's HIP kernels.
@@ -9,7 +10,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import c_int, c_int32, c_int64, c_size_t, c_void_p, c_char_p
+from ctypes import c_float, c_int, c_int32, c_int64, c_size_t, c_void_p, c_char_p
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmlstm.so")
@@ -59,6 +60,32 @@ class BwdArgs(ctypes.Structure):
     ]
 
 
+class GemmArgs(ctypes.Structure):
+    _fields_ = [
+        ("M", c_int64), ("N", c_int64), ("K", c_int64), ("batch1", c_int64), ("batch2", c_int64),
+        ("A", c_void_p), ("lda", c_int64), ("strideA1", c_int64), ("strideA2", c_int64),
+        ("B", c_void_p), ("ldb", c_int64), ("strideB1", c_int64), ("strideB2", c_int64),
+        ("C", c_void_p), ("ldc", c_int64), ("strideC1", c_int64), ("strideC2", c_int64),
+        ("c_dtype", c_int32), ("c_trans", c_int32), ("alpha", c_float),
+        ("bias", c_void_p), ("stride_bias2", c_int64),
+        ("R", c_void_p), ("ldr", c_int64), ("strideR1", c_int64), ("strideR2", c_int64),
+    ]
+
+
+# parameter arrays of mlstm_block_params, in struct order: (name, bf16 matrix?)
+BLOCK_ARRAYS = (("ln_w", False), ("ln_b", False), ("W_up", True), ("b_up", False), ("conv_w", False),
+                ("conv_b", False), ("W_q", True), ("W_k", True), ("b_q", False), ("b_k", False),
+                ("W_v", True), ("b_v", False), ("w_i", True), ("w_f", True), ("b_i", False), ("b_f", False),
+                ("gn_w", False), ("gn_b", False), ("skip", False), ("W_down", True), ("b_down", False))
+BLOCK_STAGES = ("xn", "xup", "xc", "q", "k", "v", "i_pre", "f_pre", "h", "y")
+
+
+class BlockParams(ctypes.Structure):
+    _fields_ = ([("D", c_int64), ("H", c_int64), ("d_qk", c_int64), ("d_v", c_int64), ("KC", c_int64),
+                 ("eps_ln", c_float), ("eps_gn", c_float)]
+                + [(name, c_void_p) for name, _ in BLOCK_ARRAYS])
+
+
 class SlstmArgs(ctypes.Structure):
     _fields_ = [
         ("B", c_int64), ("H", c_int64), ("T", c_int64), ("D", c_int64),
@@ -77,7 +104,7 @@ class MlstmError(RuntimeError):
 _lib = None
 
 # MLSTM_ABI_VERSION of include/mlstm.h that the argument structs here follow
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 def lib() -> ctypes.CDLL:
@@ -133,6 +160,24 @@ def lib() -> ctypes.CDLL:
         L.mlstm_clock_probe.restype = c_int
         L.slstm_fwd.argtypes = [P(SlstmArgs), c_void_p]
         L.slstm_fwd.restype = c_int
+        L.mlstm_gemm_bf16.argtypes = [P(GemmArgs), c_void_p]
+        L.mlstm_gemm_bf16.restype = c_int
+        L.mlstm_layernorm_bf16.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_float,
+                                           c_void_p]
+        L.mlstm_layernorm_bf16.restype = c_int
+        L.mlstm_block_conv_gates.argtypes = [P(BlockParams), c_int64, c_int64, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, c_void_p]
+        L.mlstm_block_conv_gates.restype = c_int
+        L.mlstm_block_groupnorm_gate.argtypes = [P(BlockParams), c_int64, c_int64, c_void_p, c_void_p,
+                                                 c_void_p, c_void_p, c_void_p]
+        L.mlstm_block_groupnorm_gate.restype = c_int
+        L.mlstm_block_fwd_workspace_size.argtypes = [P(BlockParams), c_int64, c_int64, c_int]
+        L.mlstm_block_fwd_workspace_size.restype = c_size_t
+        L.mlstm_block_fwd.argtypes = [P(BlockParams), c_int64, c_int64, c_void_p, c_void_p, c_int, c_void_p,
+                                      c_size_t, c_void_p]
+        L.mlstm_block_fwd.restype = c_int
+        L.mlstm_block_workspace_offsets.argtypes = [P(BlockParams), c_int64, c_int64, c_int, P(c_size_t)]
+        L.mlstm_block_workspace_offsets.restype = c_int
         _lib = L
     return _lib
 
@@ -182,8 +227,10 @@ def fwd_args(q, k, v, o_pre, i_pre, f_pre, h, C0=None, n0=None, m0=None,
     V = v.shape[-1]
     dt = q.dtype
     for name, t, shp in (("q", q, (B, H, T, K)), ("k", k, (B, H, T, K)), ("v", v, (B, H, T, V)),
-                         ("o_pre", o_pre, (B, H, T, V)), ("h", h, (B, H, T, V))):
+                         ("h", h, (B, H, T, V))):
         _require(t, name, shp, dt)
+    if o_pre is not None:   # None: no output gate (chunkwise form, bf16, d_v a multiple of 128)
+        _require(o_pre, "o_pre", (B, H, T, V), dt)
     _require(i_pre, "i_pre", (B, H, T), torch.float32)
     _require(f_pre, "f_pre", (B, H, T), torch.float32)
     if C0 is not None:
@@ -427,3 +474,137 @@ def slstm_fwd(pre, R, state=None, want_state=False, h=None, stream=None):
                      *[_ptr(t) for t in st_out])
     _check(lib().slstm_fwd(ctypes.byref(args), _stream(stream)), "slstm_fwd")
     return (h, st_out) if want_state else h
+
+
+# ------------------------------------------------------------------ mLSTM block (include/mlstm_block.h)
+
+def gemm_bf16(A, B, bias=None, R=None, alpha=1.0, out_dtype=None, c_trans=False, C=None, stream=None):
+    """C = alpha A B^T + bias (+ R) for 2-D bf16 tensors A [M, K], B [N, K]
+    (row pitches from their strides); C [M, N] (or [N, M] with c_trans) of
+    out_dtype (bfloat16 or float32). Returns C."""
+    import torch
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    M, K = A.shape
+    N = B.shape[0]
+    if C is None:
+        C = torch.empty((N, M) if c_trans else (M, N), dtype=out_dtype, device=A.device)
+    return gemm_bf16_strided(M, N, K, 1, 1, A, A.stride(0), 0, 0, B, B.stride(0), 0, 0, C, C.stride(0), 0, 0,
+                             alpha=alpha, bias=bias, R=R, ldr=R.stride(0) if R is not None else 0,
+                             c_trans=c_trans, stream=stream)
+
+
+def gemm_bf16_strided(M, N, K, batch1, batch2, A, lda, sA1, sA2, B, ldb, sB1, sB2, C, ldc, sC1, sC2,
+                      alpha=1.0, bias=None, stride_bias2=0, R=None, ldr=0, sR1=0, sR2=0, c_trans=False,
+                      stream=None):
+    """The strided-batched form of mlstm_gemm_bf16: A, B, C, bias, R are
+    tensors (their data pointers are the bases; strides count elements)."""
+    import torch
+    for name, t in (("A", A), ("B", B), ("R", R)):
+        if t is not None and t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+    if bias is not None and bias.dtype != torch.float32:
+        raise ValueError("bias must be float32")
+    if C.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("C must be bfloat16 or float32")
+    args = GemmArgs(M, N, K, batch1, batch2, _ptr(A), lda, sA1, sA2, _ptr(B), ldb, sB1, sB2,
+                    _ptr(C), ldc, sC1, sC2, MLSTM_BF16 if C.dtype == torch.bfloat16 else MLSTM_FP32,
+                    1 if c_trans else 0, float(alpha), _ptr(bias), stride_bias2, _ptr(R), ldr, sR1, sR2)
+    _check(lib().mlstm_gemm_bf16(ctypes.byref(args), _stream(stream)), "mlstm_gemm_bf16")
+    return C
+
+
+def layernorm_bf16(x, w, b, eps, y=None, stream=None):
+    """Layer norm of the rows of a bf16 tensor [..., D]; w, b float32 [D]."""
+    import torch
+    D = x.shape[-1]
+    rows = x.numel() // D if D else 0
+    if y is None:
+        y = torch.empty_like(x)
+    _require(x, "x", tuple(x.shape), torch.bfloat16)
+    _require(y, "y", tuple(x.shape), torch.bfloat16)
+    _check(lib().mlstm_layernorm_bf16(_ptr(x), _ptr(w), _ptr(b), _ptr(y), rows, D, float(eps), _stream(stream)),
+           "mlstm_layernorm_bf16")
+    return y
+
+
+def block_params(p, D, H, d_qk, d_v, KC=4, eps_ln=1e-5, eps_gn=1e-5) -> BlockParams:
+    """mlstm_block_params from a dict of device tensors named as in
+    BLOCK_ARRAYS (bfloat16 matrices, float32 vectors; shapes checked)."""
+    import torch
+    E = 2 * D
+    shapes = {"ln_w": (D,), "ln_b": (D,), "W_up": (2 * E, D), "b_up": (2 * E,), "conv_w": (E, KC),
+              "conv_b": (E,), "W_q": (H, d_qk, E // H), "W_k": (H, d_qk, E // H), "b_q": (H * d_qk,),
+              "b_k": (H * d_qk,), "W_v": (H, d_v, E // H), "b_v": (E,), "w_i": (H, E), "w_f": (H, E),
+              "b_i": (H,), "b_f": (H,), "gn_w": (E,), "gn_b": (E,), "skip": (E,), "W_down": (D, E),
+              "b_down": (D,)}
+    ptrs = []
+    for name, is_mat in BLOCK_ARRAYS:
+        _require(p[name], name, shapes[name], torch.bfloat16 if is_mat else torch.float32)
+        ptrs.append(_ptr(p[name]))
+    return BlockParams(D, H, d_qk, d_v, KC, float(eps_ln), float(eps_gn), *ptrs)
+
+
+def block_workspace_bytes(bp: BlockParams, B: int, T: int, chunk: int) -> int:
+    return int(lib().mlstm_block_fwd_workspace_size(ctypes.byref(bp), B, T, int(chunk)))
+
+
+def mlstm_block_fwd(x, bp: BlockParams, chunk=256, out=None, workspace=None, return_stages=False, stream=None):
+    """The whole block on x [B, T, D] (bf16). Returns out, or (out, stages)
+    with the intermediates as views of the workspace (names BLOCK_STAGES)."""
+    import torch
+    B, T, D = x.shape
+    _require(x, "x", (B, T, D), torch.bfloat16)
+    if out is None:
+        out = torch.empty_like(x)
+    nbytes = block_workspace_bytes(bp, B, T, chunk)
+    ws = _workspace(nbytes, x.device, workspace)
+    _check(lib().mlstm_block_fwd(ctypes.byref(bp), B, T, _ptr(x), _ptr(out), int(chunk), _ptr(ws), nbytes,
+                                 _stream(stream)), "mlstm_block_fwd")
+    if not return_stages:
+        return out
+    offs = (c_size_t * 10)()
+    _check(lib().mlstm_block_workspace_offsets(ctypes.byref(bp), B, T, int(chunk), offs),
+           "mlstm_block_workspace_offsets")
+    E, H = 2 * D, bp.H
+    shapes = {"xn": ((B, T, D), torch.bfloat16), "xup": ((B, T, 2 * E), torch.bfloat16),
+              "xc": ((B, T, E), torch.bfloat16), "q": ((B, H, T, bp.d_qk), torch.bfloat16),
+              "k": ((B, H, T, bp.d_qk), torch.bfloat16), "v": ((B, H, T, bp.d_v), torch.bfloat16),
+              "i_pre": ((B, H, T), torch.float32), "f_pre": ((B, H, T), torch.float32),
+              "h": ((B, H, T, bp.d_v), torch.bfloat16), "y": ((B, T, E), torch.bfloat16)}
+    stages = {}
+    for j, name in enumerate(BLOCK_STAGES):
+        shape, dt = shapes[name]
+        n = 1
+        for d in shape:
+            n *= d
+        es = 2 if dt == torch.bfloat16 else 4
+        stages[name] = ws[offs[j]:offs[j] + n * es].view(dt).view(shape)
+    return out, stages
+
+
+def block_conv_gates(bp: BlockParams, xup, stream=None):
+    """The block's conv step from xup [B, T, 2E]: returns xc [B, T, E] (bf16)
+    and i_pre, f_pre [B, H, T] (float32)."""
+    import torch
+    B, T, E2 = xup.shape
+    _require(xup, "xup", (B, T, E2), torch.bfloat16)
+    xc = torch.empty((B, T, E2 // 2), dtype=torch.bfloat16, device=xup.device)
+    ip = torch.empty((B, bp.H, T), dtype=torch.float32, device=xup.device)
+    fp = torch.empty_like(ip)
+    _check(lib().mlstm_block_conv_gates(ctypes.byref(bp), B, T, _ptr(xup), _ptr(xc), _ptr(ip), _ptr(fp),
+                                        _stream(stream)), "mlstm_block_conv_gates")
+    return xc, ip, fp
+
+
+def block_groupnorm_gate(bp: BlockParams, h, xc, xup, stream=None):
+    """The block's step after the cell: y [B, T, E] from the cell output h
+    [B, H, T, d_v], xc [B, T, E] and xup [B, T, 2E]."""
+    import torch
+    B, T, E = xc.shape
+    _require(h, "h", (B, bp.H, T, bp.d_v), torch.bfloat16)
+    _require(xc, "xc", (B, T, E), torch.bfloat16)
+    _require(xup, "xup", (B, T, 2 * E), torch.bfloat16)
+    y = torch.empty_like(xc)
+    _check(lib().mlstm_block_groupnorm_gate(ctypes.byref(bp), B, T, _ptr(h), _ptr(xc), _ptr(xup), _ptr(y),
+                                            _stream(stream)), "mlstm_block_groupnorm_gate")
+    return y

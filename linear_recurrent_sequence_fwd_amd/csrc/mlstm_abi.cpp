@@ -8,11 +8,13 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <vector>
 
 #include "../../include/mlstm.h"
+#include "../../include/mlstm_block.h"
 #include "../../include/mlstm_prof.h"
 #include "../../include/slstm.h"
 #include "mlstm_launch.h"
@@ -68,7 +70,9 @@ bool fwd_dqk_supported(int64_t d_qk, int32_t dtype) {
 }
 
 // Shape/dtype/pointer checks shared by both forward forms (not the workspace).
-int validate_fwd(const mlstm_fwd_args* a) {
+// `gate_optional`: o_pre may be NULL (no output gate) where the fused
+// chunkwise kernels run.
+int validate_fwd(const mlstm_fwd_args* a, bool gate_optional = false) {
   if (!a) return fail(MLSTM_ERR_NULLPTR, "args is NULL");
   if (a->dtype != MLSTM_FP32 && a->dtype != MLSTM_BF16)
     return fail(MLSTM_ERR_BAD_DTYPE, "dtype must be MLSTM_FP32 or MLSTM_BF16");
@@ -83,8 +87,12 @@ int validate_fwd(const mlstm_fwd_args* a) {
   if (any0 && !all0) return fail(MLSTM_ERR_NULLPTR, "C0, n0, m0 must be given together");
   const bool anyo = a->C_out || a->n_out || a->m_out, allo = a->C_out && a->n_out && a->m_out;
   if (anyo && !allo) return fail(MLSTM_ERR_NULLPTR, "C_out, n_out, m_out must be given together");
-  if (a->T > 0 && (!a->q || !a->k || !a->v || !a->o_pre || !a->i_pre || !a->f_pre || !a->h))
-    return fail(MLSTM_ERR_NULLPTR, "q, k, v, o_pre, i_pre, f_pre and h are required when T > 0");
+  if (a->T > 0 && (!a->q || !a->k || !a->v || !a->i_pre || !a->f_pre || !a->h))
+    return fail(MLSTM_ERR_NULLPTR, "q, k, v, i_pre, f_pre and h are required when T > 0");
+  if (a->T > 0 && !a->o_pre &&
+      !(gate_optional && mlstm_impl::fused_path(a->dtype == MLSTM_BF16, a->d_qk, a->d_v)))
+    return fail(MLSTM_ERR_NULLPTR, "o_pre is required (it may be NULL only for the chunkwise form with "
+                                   "MLSTM_BF16 and d_v a multiple of 128)");
   const void* v16[] = {a->q, a->k, a->v, a->o_pre, a->h, a->C0, a->n0, a->C_out, a->n_out};
   for (const void* p : v16)
     if (p && !aligned(p, 16)) return fail(MLSTM_ERR_MISALIGNED, "array pointers must be 16-byte aligned");
@@ -247,7 +255,7 @@ namespace {
 int fwd_chunkwise(const mlstm_fwd_args* a, int chunk, void* workspace, size_t workspace_bytes,
                   void* stream, const hipEvent_t* marks) {
   g_last_error.clear();
-  int st = validate_fwd(a);
+  int st = validate_fwd(a, true);
   if (st) return st;
   if (chunk < 64 || chunk % 64 != 0 || chunk > kMaxChunk)
     return fail(MLSTM_ERR_BAD_SHAPE, "chunk must be a multiple of 64 in [64, 8192]");
@@ -703,7 +711,7 @@ size_t mlstm_fwd_chunkwise_noalloc_limit(void) { return kScratchBytes; }
 
 int mlstm_fwd_chunkwise_noalloc(const mlstm_fwd_args* a, int chunk, void* stream) {
   g_last_error.clear();
-  int st = validate_fwd(a);
+  int st = validate_fwd(a, true);
   if (st) return st;
   if (chunk < 64 || chunk % 64 != 0 || chunk > kMaxChunk)
     return fail(MLSTM_ERR_BAD_SHAPE, "chunk must be a multiple of 64 in [64, 8192]");
@@ -715,6 +723,350 @@ int mlstm_fwd_chunkwise_noalloc(const mlstm_fwd_args* a, int chunk, void* stream
   void* ws = nullptr;
   if (need > 0 && (st = scratch_for_stream(static_cast<hipStream_t>(stream), &ws))) return st;
   return fwd_chunkwise(a, chunk, ws, kScratchBytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ mLSTM block around the cell
+
+namespace {
+
+bool a16(const void* p) { return p && aligned(p, 16); }
+
+// Bytes an operand of a strided batch can reach, from its base pointer.
+Range batch_span(const char* name, const void* p, int64_t es, int64_t nb1, int64_t s1, int64_t nb2, int64_t s2,
+                 int64_t rows, int64_t ld, int64_t cols) {
+  if (!p || rows <= 0 || cols <= 0) return make_range(name, p, 0);
+  const int64_t last = (nb1 - 1) * s1 + (nb2 - 1) * s2 + (rows - 1) * ld + cols;
+  return make_range(name, p, last * es);
+}
+
+int validate_gemm(const mlstm_gemm_args* g) {
+  if (!g) return fail(MLSTM_ERR_NULLPTR, "args is NULL");
+  if (g->M < 1 || g->N < 1 || g->K < 1 || g->batch1 < 1 || g->batch2 < 1)
+    return fail(MLSTM_ERR_BAD_SHAPE, "need M, N, K, batch1, batch2 >= 1");
+  if (g->c_dtype != MLSTM_BF16 && g->c_dtype != MLSTM_FP32)
+    return fail(MLSTM_ERR_BAD_DTYPE, "c_dtype must be MLSTM_BF16 or MLSTM_FP32");
+  if (g->K % 64) return fail(MLSTM_ERR_BAD_SHAPE, "K must be a multiple of 64");
+  if (g->N % 4) return fail(MLSTM_ERR_BAD_SHAPE, "N must be a multiple of 4");
+  if (g->c_trans && g->M % 4) return fail(MLSTM_ERR_BAD_SHAPE, "M must be a multiple of 4 with c_trans");
+  if (g->c_trans && g->R) return fail(MLSTM_ERR_UNSUPPORTED, "R is not supported with c_trans");
+  if (!g->A || !g->B || !g->C) return fail(MLSTM_ERR_NULLPTR, "A, B and C are required");
+  if (g->lda < g->K || g->ldb < g->K || g->ldc < (g->c_trans ? g->M : g->N) || (g->R && g->ldr < g->N))
+    return fail(MLSTM_ERR_BAD_SHAPE, "row pitches must cover the rows (lda, ldb >= K; ldc >= N, or M with "
+                                     "c_trans; ldr >= N)");
+  // every row starts 16-byte aligned: bf16 pitches are multiples of 8 elements, float32 ones of 4
+  const int64_t pitches[] = {g->lda, g->ldb, g->R ? g->ldr : 0, g->strideA1, g->strideA2,
+                             g->strideB1, g->strideB2, g->R ? g->strideR1 : 0, g->R ? g->strideR2 : 0};
+  for (int64_t v : pitches)
+    if (v < 0 || v % 8) return fail(MLSTM_ERR_MISALIGNED, "pitches and batch strides of A, B and R must be "
+                                                          "non-negative multiples of 8 elements");
+  const int64_t cmul = g->c_dtype == MLSTM_BF16 ? 8 : 4;
+  for (int64_t v : {g->ldc, g->strideC1, g->strideC2})
+    if (v < 0 || v % cmul) return fail(MLSTM_ERR_MISALIGNED, "pitch and batch strides of C must be non-negative "
+                                                             "multiples of 16 bytes");
+  if (g->bias && (g->stride_bias2 < 0 || g->stride_bias2 % 4))
+    return fail(MLSTM_ERR_MISALIGNED, "stride_bias2 must be a non-negative multiple of 4");
+  const void* ptrs[] = {g->A, g->B, g->C, g->bias, g->R};
+  for (const void* p : ptrs)
+    if (p && !aligned(p, 16)) return fail(MLSTM_ERR_MISALIGNED, "arrays must be 16-byte aligned");
+  const int64_t tile = mlstm_impl::gemm_tile();
+  if (g->M > INT32_MAX / 2 || g->N > INT32_MAX / 2 || g->K > INT32_MAX / 2 ||
+      g->lda > (int64_t)1 << 22 || g->ldb > (int64_t)1 << 22)
+    return fail(MLSTM_ERR_UNSUPPORTED, "sizes or row pitches beyond the kernel's 32-bit offsets");
+  const int64_t tiles = g->batch1 * g->batch2 * ((g->M + tile - 1) / tile) * ((g->N + tile - 1) / tile);
+  if (tiles > INT32_MAX) return fail(MLSTM_ERR_UNSUPPORTED, "problem too large for one launch grid");
+  const int64_t ces = g->c_dtype == MLSTM_BF16 ? 2 : 4;
+  std::vector<Range> in = {
+      batch_span("A", g->A, 2, g->batch1, g->strideA1, g->batch2, g->strideA2, g->M, g->lda, g->K),
+      batch_span("B", g->B, 2, g->batch1, g->strideB1, g->batch2, g->strideB2, g->N, g->ldb, g->K),
+      batch_span("bias", g->bias, 4, 1, 0, g->batch2, g->stride_bias2, 1, 0, g->N),
+      batch_span("R", g->R, 2, g->batch1, g->strideR1, g->batch2, g->strideR2, g->M, g->ldr, g->N)};
+  std::vector<Range> out = {g->c_trans
+      ? batch_span("C", g->C, ces, g->batch1, g->strideC1, g->batch2, g->strideC2, g->N, g->ldc, g->M)
+      : batch_span("C", g->C, ces, g->batch1, g->strideC1, g->batch2, g->strideC2, g->M, g->ldc, g->N)};
+  return check_alias(in, out);
+}
+
+mlstm_impl::GemmLaunch gemm_launch(const mlstm_gemm_args* g) {
+  mlstm_impl::GemmLaunch l;
+  l.M = g->M; l.N = g->N; l.K = g->K; l.nb1 = g->batch1; l.nb2 = g->batch2;
+  l.A = g->A; l.lda = g->lda; l.sA1 = g->strideA1; l.sA2 = g->strideA2;
+  l.B = g->B; l.ldb = g->ldb; l.sB1 = g->strideB1; l.sB2 = g->strideB2;
+  l.C = g->C; l.ldc = g->ldc; l.sC1 = g->strideC1; l.sC2 = g->strideC2;
+  l.c_fp32 = g->c_dtype == MLSTM_FP32; l.c_trans = g->c_trans;
+  l.alpha = g->alpha;
+  l.bias = g->bias; l.sbias2 = g->stride_bias2;
+  l.R = g->R; l.ldr = g->ldr; l.sR1 = g->strideR1; l.sR2 = g->strideR2;
+  return l;
+}
+
+int validate_block(const mlstm_block_params* p, int64_t B, int64_t T) {
+  if (!p) return fail(MLSTM_ERR_NULLPTR, "params is NULL");
+  if (B < 1 || T < 0) return fail(MLSTM_ERR_BAD_SHAPE, "need B >= 1 and T >= 0");
+  const int64_t D = p->D, E = 2 * p->D;
+  if (D < 64 || D % 64) return fail(MLSTM_ERR_BAD_SHAPE, "D must be a positive multiple of 64");
+  if (D > 8192) return fail(MLSTM_ERR_UNSUPPORTED, "D above 8192");
+  if (p->H < 1 || p->d_qk < 1 || p->d_v < 1 || p->H * p->d_v != E)
+    return fail(MLSTM_ERR_BAD_SHAPE, "need H, d_qk, d_v >= 1 and H d_v == 2 D");
+  if ((E / p->H) % 64) return fail(MLSTM_ERR_BAD_SHAPE, "the per-head input width 2 D / H must be a multiple of 64");
+  if (p->H > 32) return fail(MLSTM_ERR_UNSUPPORTED, "more than 32 heads");
+  if (!(p->d_qk == 64 || p->d_qk == 128 || p->d_qk == 256))
+    return fail(MLSTM_ERR_UNSUPPORTED, "d_qk must be 64, 128 or 256");
+  if (p->d_v % 128 || p->d_v > 2048) return fail(MLSTM_ERR_UNSUPPORTED, "d_v must be a multiple of 128 up to 2048");
+  if (p->KC < 1 || p->KC > 8) return fail(MLSTM_ERR_UNSUPPORTED, "KC must be in 1..8");
+  if (!(p->eps_ln >= 0.f) || !(p->eps_gn >= 0.f)) return fail(MLSTM_ERR_BAD_SHAPE, "epsilons must be >= 0");
+  const void* ptrs[] = {p->ln_w, p->ln_b, p->W_up, p->b_up, p->conv_w, p->conv_b, p->W_q, p->W_k, p->b_q,
+                        p->b_k, p->W_v, p->b_v, p->w_i, p->w_f, p->b_i, p->b_f, p->gn_w, p->gn_b, p->skip,
+                        p->W_down, p->b_down};
+  for (const void* q : ptrs) {
+    if (!q) return fail(MLSTM_ERR_NULLPTR, "every parameter array is required");
+    if (!aligned(q, 16)) return fail(MLSTM_ERR_MISALIGNED, "parameter arrays must be 16-byte aligned");
+  }
+  if (B * T > INT32_MAX / 2 || B * T * p->H / 4 > INT32_MAX)
+    return fail(MLSTM_ERR_UNSUPPORTED, "problem too large for one launch grid");
+  return MLSTM_OK;
+}
+
+// Ranges of the parameter arrays, for alias checks against outputs.
+std::vector<Range> param_ranges(const mlstm_block_params* p) {
+  const int64_t D = p->D, E = 2 * D, H = p->H, n_in = E / H;
+  return {make_range("ln_w", p->ln_w, D * 4), make_range("ln_b", p->ln_b, D * 4),
+          make_range("W_up", p->W_up, 2 * E * D * 2), make_range("b_up", p->b_up, 2 * E * 4),
+          make_range("conv_w", p->conv_w, E * p->KC * 4), make_range("conv_b", p->conv_b, E * 4),
+          make_range("W_q", p->W_q, H * p->d_qk * n_in * 2), make_range("W_k", p->W_k, H * p->d_qk * n_in * 2),
+          make_range("b_q", p->b_q, H * p->d_qk * 4), make_range("b_k", p->b_k, H * p->d_qk * 4),
+          make_range("W_v", p->W_v, H * p->d_v * n_in * 2), make_range("b_v", p->b_v, E * 4),
+          make_range("w_i", p->w_i, H * E * 2), make_range("w_f", p->w_f, H * E * 2),
+          make_range("b_i", p->b_i, H * 4), make_range("b_f", p->b_f, H * 4),
+          make_range("gn_w", p->gn_w, E * 4), make_range("gn_b", p->gn_b, E * 4),
+          make_range("skip", p->skip, E * 4), make_range("W_down", p->W_down, D * E * 2),
+          make_range("b_down", p->b_down, D * 4)};
+}
+
+mlstm_fwd_args cell_args(const mlstm_block_params* p, int64_t B, int64_t T) {
+  mlstm_fwd_args c;
+  memset(&c, 0, sizeof(c));
+  c.B = B; c.H = p->H; c.T = T; c.d_qk = p->d_qk; c.d_v = p->d_v; c.dtype = MLSTM_BF16;
+  return c;
+}
+
+struct BlockWs {
+  size_t off[10];   // xn, xup, xc, q, k, v, i_pre, f_pre, h, y
+  size_t cell, cell_bytes, total;
+};
+
+BlockWs block_layout(const mlstm_block_params* p, int64_t B, int64_t T, int chunk) {
+  BlockWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+  const int64_t D = p->D, E = 2 * D, BT = B * T, BHT = B * p->H * T;
+  w.off[0] = take(BT * D * 2);
+  w.off[1] = take(BT * 2 * E * 2);
+  w.off[2] = take(BT * E * 2);
+  w.off[3] = take(BHT * p->d_qk * 2);
+  w.off[4] = take(BHT * p->d_qk * 2);
+  w.off[5] = take(BHT * p->d_v * 2);
+  w.off[6] = take(BHT * 4);
+  w.off[7] = take(BHT * 4);
+  w.off[8] = take(BHT * p->d_v * 2);
+  w.off[9] = take(BT * E * 2);
+  const mlstm_fwd_args c = cell_args(p, B, T);
+  w.cell_bytes = mlstm_fwd_chunkwise_workspace_size(&c, chunk);
+  w.cell = take(w.cell_bytes);
+  w.total = off;
+  return w;
+}
+
+mlstm_impl::ConvLaunch conv_launch(const mlstm_block_params* p, int64_t B, int64_t T, const void* xup, void* xc,
+                                   float* i_pre, float* f_pre) {
+  mlstm_impl::ConvLaunch c;
+  c.B = B; c.T = T; c.E = 2 * p->D; c.H = p->H; c.KC = p->KC;
+  c.xm = xup; c.ldx = 4 * p->D;
+  c.cw = p->conv_w; c.cb = p->conv_b;
+  c.xc = xc;
+  c.wi = p->w_i; c.wf = p->w_f; c.bi = p->b_i; c.bf = p->b_f;
+  c.i_pre = i_pre; c.f_pre = f_pre;
+  return c;
+}
+
+mlstm_impl::GnLaunch gn_launch(const mlstm_block_params* p, int64_t B, int64_t T, const void* h, const void* xc,
+                               const void* xup, void* y) {
+  const int64_t E = 2 * p->D;
+  mlstm_impl::GnLaunch g;
+  g.B = B; g.T = T; g.H = p->H; g.dv = p->d_v;
+  g.h = h; g.xc = xc;
+  g.z = static_cast<const char*>(xup) + E * 2;
+  g.ldz = 2 * E;
+  g.gw = p->gn_w; g.gb = p->gn_b; g.skip = p->skip;
+  g.y = y;
+  g.eps = p->eps_gn;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mlstm_gemm_bf16(const mlstm_gemm_args* g, void* stream) {
+  g_last_error.clear();
+  int st = validate_gemm(g);
+  if (st) return st;
+  return hip_status(mlstm_impl::launch_gemm(gemm_launch(g), static_cast<hipStream_t>(stream)), "GEMM kernel");
+}
+
+int mlstm_layernorm_bf16(const void* x, const float* w, const float* b, void* y, int64_t rows, int64_t D,
+                         float eps, void* stream) {
+  g_last_error.clear();
+  if (rows < 0 || D < 8 || D % 8) return fail(MLSTM_ERR_BAD_SHAPE, "need rows >= 0 and D a positive multiple of 8");
+  if (D > 8192) return fail(MLSTM_ERR_UNSUPPORTED, "D above 8192");
+  if (!(eps >= 0.f)) return fail(MLSTM_ERR_BAD_SHAPE, "eps must be >= 0");
+  if (rows == 0) return MLSTM_OK;
+  if (!x || !w || !b || !y) return fail(MLSTM_ERR_NULLPTR, "x, w, b and y are required");
+  if (!a16(x) || !a16(w) || !a16(b) || !a16(y)) return fail(MLSTM_ERR_MISALIGNED, "arrays must be 16-byte aligned");
+  if (rows > (int64_t)INT32_MAX * 4) return fail(MLSTM_ERR_UNSUPPORTED, "too many rows for one launch grid");
+  {
+    std::vector<Range> in = {make_range("x", x, rows * D * 2), make_range("w", w, D * 4), make_range("b", b, D * 4)};
+    std::vector<Range> out = {make_range("y", y, rows * D * 2)};
+    const int st = check_alias(in, out);
+    if (st) return st;
+  }
+  return hip_status(mlstm_impl::launch_layernorm(x, w, b, y, rows, D, eps, static_cast<hipStream_t>(stream)),
+                    "layer norm kernel");
+}
+
+int mlstm_block_conv_gates(const mlstm_block_params* p, int64_t B, int64_t T, const void* xup, void* xc,
+                           float* i_pre, float* f_pre, void* stream) {
+  g_last_error.clear();
+  int st = validate_block(p, B, T);
+  if (st) return st;
+  if (T == 0) return MLSTM_OK;
+  if (!xup || !xc || !i_pre || !f_pre) return fail(MLSTM_ERR_NULLPTR, "xup, xc, i_pre and f_pre are required");
+  if (!a16(xup) || !a16(xc) || !a16(i_pre) || !a16(f_pre))
+    return fail(MLSTM_ERR_MISALIGNED, "arrays must be 16-byte aligned");
+  const int64_t E = 2 * p->D, BT = B * T;
+  std::vector<Range> in = param_ranges(p);
+  in.push_back(make_range("xup", xup, BT * 2 * E * 2));
+  std::vector<Range> out = {make_range("xc", xc, BT * E * 2), make_range("i_pre", i_pre, BT * p->H * 4),
+                            make_range("f_pre", f_pre, BT * p->H * 4)};
+  if ((st = check_alias(in, out))) return st;
+  return hip_status(mlstm_impl::launch_conv_gate(conv_launch(p, B, T, xup, xc, i_pre, f_pre),
+                                                 static_cast<hipStream_t>(stream)), "conv kernel");
+}
+
+int mlstm_block_groupnorm_gate(const mlstm_block_params* p, int64_t B, int64_t T, const void* h, const void* xc,
+                               const void* xup, void* y, void* stream) {
+  g_last_error.clear();
+  int st = validate_block(p, B, T);
+  if (st) return st;
+  if (T == 0) return MLSTM_OK;
+  if (!h || !xc || !xup || !y) return fail(MLSTM_ERR_NULLPTR, "h, xc, xup and y are required");
+  if (!a16(h) || !a16(xc) || !a16(xup) || !a16(y)) return fail(MLSTM_ERR_MISALIGNED, "arrays must be 16-byte aligned");
+  const int64_t E = 2 * p->D, BT = B * T;
+  std::vector<Range> in = param_ranges(p);
+  in.push_back(make_range("h", h, BT * E * 2));
+  in.push_back(make_range("xc", xc, BT * E * 2));
+  in.push_back(make_range("xup", xup, BT * 2 * E * 2));
+  std::vector<Range> out = {make_range("y", y, BT * E * 2)};
+  if ((st = check_alias(in, out))) return st;
+  return hip_status(mlstm_impl::launch_groupnorm_gate(gn_launch(p, B, T, h, xc, xup, y),
+                                                      static_cast<hipStream_t>(stream)), "group norm kernel");
+}
+
+size_t mlstm_block_fwd_workspace_size(const mlstm_block_params* p, int64_t B, int64_t T, int chunk) {
+  if (!p || B < 1 || T <= 0 || chunk < 64 || chunk % 64 || chunk > kMaxChunk) return 0;
+  if (p->D < 64 || p->H < 1 || p->d_qk < 1 || p->d_v < 1) return 0;
+  return block_layout(p, B, T, chunk).total;
+}
+
+int mlstm_block_workspace_offsets(const mlstm_block_params* p, int64_t B, int64_t T, int chunk, size_t offsets[10]) {
+  g_last_error.clear();
+  if (!offsets) return fail(MLSTM_ERR_NULLPTR, "offsets is NULL");
+  if (!p || B < 1 || T <= 0 || chunk < 64 || chunk % 64 || chunk > kMaxChunk || p->D < 64 || p->H < 1 ||
+      p->d_qk < 1 || p->d_v < 1)
+    return fail(MLSTM_ERR_BAD_SHAPE, "invalid sizes");
+  const BlockWs w = block_layout(p, B, T, chunk);
+  for (int j = 0; j < 10; ++j) offsets[j] = w.off[j];
+  return MLSTM_OK;
+}
+
+int mlstm_block_fwd(const mlstm_block_params* p, int64_t B, int64_t T, const void* x, void* out, int chunk,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int st = validate_block(p, B, T);
+  if (st) return st;
+  if (chunk < 64 || chunk % 64 != 0 || chunk > kMaxChunk)
+    return fail(MLSTM_ERR_BAD_SHAPE, "chunk must be a multiple of 64 in [64, 8192]");
+  if (T == 0) return MLSTM_OK;
+  if (!x || !out) return fail(MLSTM_ERR_NULLPTR, "x and out are required");
+  if (!a16(x) || !a16(out)) return fail(MLSTM_ERR_MISALIGNED, "x and out must be 16-byte aligned");
+  const BlockWs w = block_layout(p, B, T, chunk);
+  if (!workspace) return fail(MLSTM_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, kAlign)) return fail(MLSTM_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (workspace_bytes < w.total)
+    return fail(MLSTM_ERR_WORKSPACE, "workspace too small: need " + std::to_string(w.total) + " bytes");
+  const int64_t D = p->D, E = 2 * D, H = p->H, BT = B * T, n_in = E / H;
+  {
+    std::vector<Range> in = param_ranges(p);
+    in.push_back(make_range("x", x, BT * D * 2));
+    std::vector<Range> outs = {make_range("out", out, BT * D * 2),
+                               make_range("workspace", workspace, (int64_t)w.total)};
+    if ((st = check_alias(in, outs))) return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  void* xn = ws + w.off[0];
+  void* xup = ws + w.off[1];
+  void* xc = ws + w.off[2];
+  void* q = ws + w.off[3];
+  void* k = ws + w.off[4];
+  void* v = ws + w.off[5];
+  float* ip = reinterpret_cast<float*>(ws + w.off[6]);
+  float* fp = reinterpret_cast<float*>(ws + w.off[7]);
+  void* hc = ws + w.off[8];
+  void* y = ws + w.off[9];
+
+  if ((st = hip_status(mlstm_impl::launch_layernorm(x, p->ln_w, p->ln_b, xn, BT, D, p->eps_ln, s), "layer norm")))
+    return st;
+  mlstm_impl::GemmLaunch g{};
+  g.nb1 = g.nb2 = 1;
+  g.alpha = 1.f;
+  // up-projection [BT][2E]
+  g.M = BT; g.N = 2 * E; g.K = D;
+  g.A = xn; g.lda = D; g.B = p->W_up; g.ldb = D; g.C = xup; g.ldc = 2 * E; g.bias = p->b_up;
+  if ((st = hip_status(mlstm_impl::launch_gemm(g, s), "up-projection"))) return st;
+  if ((st = hip_status(mlstm_impl::launch_conv_gate(conv_launch(p, B, T, xup, xc, ip, fp), s), "conv kernel")))
+    return st;
+  // per-head projections, batched over (batch entry, head), into [B][H][T][d]
+  auto head_proj = [&](const void* A, int64_t lda, const void* W, int64_t n_out, const float* bias, void* C,
+                       float alpha, const char* what) {
+    mlstm_impl::GemmLaunch h{};
+    h.M = T; h.N = n_out; h.K = n_in; h.nb1 = B; h.nb2 = H;
+    h.A = A; h.lda = lda; h.sA1 = T * lda; h.sA2 = n_in;
+    h.B = W; h.ldb = n_in; h.sB1 = 0; h.sB2 = n_out * n_in;
+    h.C = C; h.ldc = n_out; h.sC1 = H * T * n_out; h.sC2 = T * n_out;
+    h.alpha = alpha; h.bias = bias; h.sbias2 = n_out;
+    return hip_status(mlstm_impl::launch_gemm(h, s), what);
+  };
+  if ((st = head_proj(xc, E, p->W_q, p->d_qk, p->b_q, q, 1.f, "q projection"))) return st;
+  if ((st = head_proj(xc, E, p->W_k, p->d_qk, p->b_k, k, (float)(1.0 / std::sqrt((double)p->d_qk)),
+                      "k projection")))
+    return st;
+  if ((st = head_proj(xup, 2 * E, p->W_v, p->d_v, p->b_v, v, 1.f, "v projection"))) return st;
+  // the cell, ungated
+  mlstm_fwd_args c = cell_args(p, B, T);
+  c.q = q; c.k = k; c.v = v; c.o_pre = nullptr; c.i_pre = ip; c.f_pre = fp; c.h = hc;
+  if ((st = fwd_chunkwise(&c, chunk, ws + w.cell, w.cell_bytes, stream, nullptr))) return st;
+  if ((st = hip_status(mlstm_impl::launch_groupnorm_gate(gn_launch(p, B, T, hc, xc, xup, y), s), "group norm")))
+    return st;
+  // down-projection with the residual
+  g = mlstm_impl::GemmLaunch{};
+  g.nb1 = g.nb2 = 1;
+  g.alpha = 1.f;
+  g.M = BT; g.N = D; g.K = E;
+  g.A = y; g.lda = E; g.B = p->W_down; g.ldb = E; g.C = out; g.ldc = D; g.bias = p->b_down;
+  g.R = x; g.ldr = D;
+  return hip_status(mlstm_impl::launch_gemm(g, s), "down-projection");
 }
 
 }  // extern "C"

@@ -89,21 +89,6 @@ __device__ __forceinline__ void store4(__bf16* p, f32x4 x) {
 }
 __device__ __forceinline__ void store4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
 
-// x = hi + lo with hi the bfloat16 rounding of x and lo that of the rest;
-// for float32 operands hi = x and lo = 0.
-__device__ __forceinline__ void split8(const f32x8& x, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    hi[e] = (__bf16)x[e];
-    lo[e] = (__bf16)(x[e] - (float)hi[e]);
-  }
-}
-__device__ __forceinline__ void split8(const f32x8& x, f32x8& hi, f32x8& lo) {
-  hi = x;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) lo[e] = 0.f;
-}
-
 template <typename T> __device__ __forceinline__ vec8<T> zero_v8() {
   vec8<T> z;
 #pragma unroll
@@ -863,7 +848,7 @@ template <typename TI, int K, int V>
 __global__ __launch_bounds__(kBT) void bwd_dkv_kernel(BwdArgs a) {
   using L = DkvLds<TI, K, V>;
   constexpr int QP = L::QP, GP = L::GP, AP = L::AP;
-  constexpr int CK = K / 64, CV = V / 64;   // 16-column output tiles per wave
+  constexpr int CK = K / 64;   // 16-column output tiles per wave
   __shared__ __attribute__((aligned(16))) char smem[L::bytes];
   TI* sQ = reinterpret_cast<TI*>(smem + L::oQ);
   TI* sG = reinterpret_cast<TI*>(smem + L::oG);

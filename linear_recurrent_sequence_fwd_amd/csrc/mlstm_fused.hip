@@ -245,6 +245,7 @@ struct SegArgs {
   int64_t T, Nt, V, BH;      // Nt = number of 64-token tiles
   int TPS;                   // tiles per chunk
   int S;                     // chunks
+  float o_bias;              // 0, or -inf with o null: no output gate (sigmoid(o~) = 1)
 };
 
 constexpr int kOutWaves = 8;   // output kernel: two halves of d_qk x four 32-column groups, two waves per SIMD
@@ -531,8 +532,12 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
   auto tile_rsrc_vo = [&](const __bf16* base, int64_t tau) {
     return buffer_rsrc(base + (bh * T + tau * kTile) * V + vcol0, (last_row(tau) * (unsigned)V + kVB) * 2u);
   };
+  // Without an output gate (o null) the resource covers no bytes: the loads
+  // return zero and touch no memory, and the exponent bias of -inf makes the
+  // gate exactly one.
   auto load_o = [&](int64_t tau, int cv) {
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(tile_rsrc_vo(a.o, tau), (int)offO[cv], 0, 0);
+    const __amdgpu_buffer_rsrc_t orsrc = a.o ? tile_rsrc_vo(a.o, tau) : buffer_rsrc(a.h, 0u);
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(orsrc, (int)offO[cv], 0, 0);
     const bf16x8 y = __builtin_bit_cast(bf16x8, x);
     po[cv][1] = __builtin_shufflevector(y, y, 0, 1, 2, 3);
     po[cv][0] = __builtin_shufflevector(y, y, 4, 5, 6, 7);
@@ -663,8 +668,8 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
       for (int z = 0; z < 2; ++z) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          // sigmoid(o) / D = 1 / ((1 + e^-o) D)
-          const float e = __builtin_amdgcn_exp2f(-kLog2eF * (float)epo[cv][z][r]);
+          // sigmoid(o) / D = 1 / ((1 + e^-o) D); e = 0 without an output gate
+          const float e = __builtin_amdgcn_exp2f(fmaf(-kLog2eF, (float)epo[cv][z][r], a.o_bias));
           h4[z][r] = (__bf16)(eacc[z][cv][r] * __builtin_amdgcn_rcpf(fmaf(e, dnm[z], dnm[z])));
         }
       }
@@ -1443,6 +1448,7 @@ hipError_t run_seg(const FwdLaunch& f, const GateBuffers& gb, const SegStates& s
   a.k = static_cast<const __bf16*>(f.k);
   a.v = static_cast<const __bf16*>(f.v);
   a.o = static_cast<const __bf16*>(f.o);
+  a.o_bias = f.o ? 0.f : -INFINITY;
   a.h = static_cast<__bf16*>(f.h);
   a.gb = gb;
   a.C0 = f.C0; a.n0 = f.n0; a.m0 = f.m0;

@@ -159,4 +159,53 @@ hipError_t launch_out_bf16(const FwdLaunch& a, const GateBuffers& gb, const Chun
 bool fused_path(int bf16, int64_t K, int64_t V);
 hipError_t launch_fused(const FwdLaunch& a, const GateBuffers& gb, const SegStates& ss, hipStream_t s);
 
+// mLSTM block around the cell (mlstm_block.hip).
+//
+// GEMM: C = alpha A B^T + bias (+ R) per batch entry (b1, b2), A [M][K] and
+// B [N][K] bf16 (k contiguous, row pitches lda, ldb), float32 accumulation;
+// C bf16 or float32, element (m, n) at C + m ldc + n (c_trans: C + n ldc + m);
+// bias [N] float32 at bias + b2 sbias2 (or null); R bf16 at
+// R + m ldr + n (or null; not with c_trans). Batch offsets in elements:
+// X + b1 sX1 + b2 sX2. Needs K % 64 == 0, N % 4 == 0 (M % 4 == 0 with
+// c_trans) and 16-byte aligned rows.
+struct GemmLaunch {
+  int64_t M, N, K, nb1, nb2;
+  const void* A; int64_t lda, sA1, sA2;
+  const void* B; int64_t ldb, sB1, sB2;
+  void* C; int64_t ldc, sC1, sC2;
+  int c_fp32, c_trans;
+  float alpha;
+  const float* bias; int64_t sbias2;
+  const void* R; int64_t ldr, sR1, sR2;
+};
+hipError_t launch_gemm(const GemmLaunch& g, hipStream_t s);
+int gemm_tile();   // output tile edge (rows and columns per workgroup)
+
+// rows x D bf16 -> bf16, D % 8 == 0, D <= 8192
+hipError_t launch_layernorm(const void* x, const float* w, const float* b, void* y, int64_t rows, int64_t D,
+                            float eps, hipStream_t s);
+
+// xc = swish(causal conv(xm)) and the gate preactivations from xc; E % 128 == 0,
+// H <= 32, KC in 1..8
+struct ConvLaunch {
+  int64_t B, T, E, H, KC;
+  const void* xm; int64_t ldx;
+  const float *cw, *cb;
+  void* xc;
+  const void *wi, *wf;
+  const float *bi, *bf;
+  float *i_pre, *f_pre;
+};
+hipError_t launch_conv_gate(const ConvLaunch& c, hipStream_t s);
+
+// y = (GroupNorm(h) + skip xc) sigmoid(z), one group per head over dv (dv % 8 == 0, dv <= 2048)
+struct GnLaunch {
+  int64_t B, T, H, dv;
+  const void *h, *xc, *z; int64_t ldz;
+  const float *gw, *gb, *skip;
+  void* y;
+  float eps;
+};
+hipError_t launch_groupnorm_gate(const GnLaunch& g, hipStream_t s);
+
 }  // namespace mlstm_impl

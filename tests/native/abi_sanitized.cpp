@@ -1,5 +1,5 @@
-// Drives every entry point of the mLSTM C ABI (include/mlstm.h, slstm.h,
-// mlstm_prof.h) through its argument checks and, with host-only stand-in
+// Drives every entry point of the mLSTM C ABI (include/mlstm.h,
+// mlstm_block.h, slstm.h, mlstm_prof.h) through its argument checks and, with host-only stand-in
 // launchers (abi_stub_launchers.cpp), through its workspace carving and
 // dispatch, in a build with AddressSanitizer and UndefinedBehaviorSanitizer
 // on the host code. Pointers are fabricated addresses that nothing
@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include "../../include/mlstm.h"
+#include "../../include/mlstm_block.h"
 #include "../../include/mlstm_prof.h"
 #include "../../include/slstm.h"
 
@@ -183,6 +184,94 @@ int main() {
     void* dst = take(1 << 20);
     EXPECT(mlstm_prof_copy_lds(src, dst, 1 << 20, nullptr) == MLSTM_OK);
     EXPECT(mlstm_prof_copy_lds(src, (char*)src + 16384, 32768, nullptr) == MLSTM_ERR_ALIAS);
+  }
+
+  // ---- mLSTM block: the whole block through its nine launches, and each step
+  {
+    const int64_t D = 256, E = 512, H = 4, dqk = 64, dv = 128, KC = 4, B = 2, T = 100;
+    mlstm_block_params p;
+    memset(&p, 0, sizeof(p));
+    p.D = D; p.H = H; p.d_qk = dqk; p.d_v = dv; p.KC = KC; p.eps_ln = 1e-5f; p.eps_gn = 1e-5f;
+    p.ln_w = (const float*)take(D * 4); p.ln_b = (const float*)take(D * 4);
+    p.W_up = take(2 * E * D * 2); p.b_up = (const float*)take(2 * E * 4);
+    p.conv_w = (const float*)take(E * KC * 4); p.conv_b = (const float*)take(E * 4);
+    p.W_q = take(H * dqk * (E / H) * 2); p.W_k = take(H * dqk * (E / H) * 2);
+    p.b_q = (const float*)take(H * dqk * 4); p.b_k = (const float*)take(H * dqk * 4);
+    p.W_v = take(H * dv * (E / H) * 2); p.b_v = (const float*)take(E * 4);
+    p.w_i = take(H * E * 2); p.w_f = take(H * E * 2);
+    p.b_i = (const float*)take(H * 4); p.b_f = (const float*)take(H * 4);
+    p.gn_w = (const float*)take(E * 4); p.gn_b = (const float*)take(E * 4); p.skip = (const float*)take(E * 4);
+    p.W_down = take(D * E * 2); p.b_down = (const float*)take(D * 4);
+    void* x = take(B * T * D * 2);
+    void* out = take(B * T * D * 2);
+    const size_t need = mlstm_block_fwd_workspace_size(&p, B, T, 64);
+    EXPECT(need > 0);
+    void* ws = take(need);
+    int before[16];
+    for (int j = 0; j < 16; ++j) before[j] = g_calls[j];
+    EXPECT(mlstm_block_fwd(&p, B, T, x, out, 64, ws, need, nullptr) == MLSTM_OK);
+    EXPECT(g_calls[12] == before[12] + 5);   // up, q, k, v, down
+    EXPECT(g_calls[13] == before[13] + 1 && g_calls[14] == before[14] + 1 && g_calls[15] == before[15] + 1);
+    EXPECT(g_calls[9] == before[9] + 1);     // the cell's fused kernels, ungated
+    size_t offs[10];
+    EXPECT(mlstm_block_workspace_offsets(&p, B, T, 64, offs) == MLSTM_OK);
+    for (int j = 1; j < 10; ++j) EXPECT(offs[j] > offs[j - 1]);
+    EXPECT(offs[9] + (size_t)(B * T * E * 2) <= need);
+    EXPECT(mlstm_block_fwd(&p, B, T, x, out, 64, ws, need - 1, nullptr) == MLSTM_ERR_WORKSPACE);
+    EXPECT(mlstm_block_fwd(&p, B, T, x, out, 64, nullptr, need, nullptr) == MLSTM_ERR_WORKSPACE);
+    EXPECT(mlstm_block_fwd(&p, B, T, x, x, 64, ws, need, nullptr) == MLSTM_ERR_ALIAS);
+    EXPECT(mlstm_block_fwd(&p, B, T, x, (void*)p.W_up, 64, ws, need, nullptr) == MLSTM_ERR_ALIAS);
+    EXPECT(mlstm_block_fwd(&p, B, T, x, out, 100, ws, need, nullptr) == MLSTM_ERR_BAD_SHAPE);
+    EXPECT(mlstm_block_fwd(&p, B, 0, x, out, 64, nullptr, 0, nullptr) == MLSTM_OK);
+    EXPECT(mlstm_block_fwd(nullptr, B, T, x, out, 64, ws, need, nullptr) == MLSTM_ERR_NULLPTR);
+    mlstm_block_params bad = p;
+    bad.d_v = 64;
+    EXPECT(mlstm_block_fwd(&bad, B, T, x, out, 64, ws, need, nullptr) == MLSTM_ERR_BAD_SHAPE);
+    bad = p; bad.d_qk = 32;
+    EXPECT(mlstm_block_fwd(&bad, B, T, x, out, 64, ws, need, nullptr) == MLSTM_ERR_UNSUPPORTED);
+    bad = p; bad.KC = 9;
+    EXPECT(mlstm_block_fwd(&bad, B, T, x, out, 64, ws, need, nullptr) == MLSTM_ERR_UNSUPPORTED);
+    bad = p; bad.skip = nullptr;
+    EXPECT(mlstm_block_fwd(&bad, B, T, x, out, 64, ws, need, nullptr) == MLSTM_ERR_NULLPTR);
+    bad = p; bad.b_up = (const float*)((const char*)p.b_up + 4);
+    EXPECT(mlstm_block_fwd(&bad, B, T, x, out, 64, ws, need, nullptr) == MLSTM_ERR_MISALIGNED);
+
+    void* xup = take(B * T * 2 * E * 2);
+    void* xc = take(B * T * E * 2);
+    float* ip = (float*)take(B * H * T * 4);
+    float* fp = (float*)take(B * H * T * 4);
+    EXPECT(mlstm_block_conv_gates(&p, B, T, xup, xc, ip, fp, nullptr) == MLSTM_OK);
+    EXPECT(mlstm_block_conv_gates(&p, B, T, xup, xup, ip, fp, nullptr) == MLSTM_ERR_ALIAS);
+    EXPECT(mlstm_block_conv_gates(&p, B, T, xup, xc, ip, nullptr, nullptr) == MLSTM_ERR_NULLPTR);
+    void* hc = take(B * H * T * dv * 2);
+    void* y = take(B * T * E * 2);
+    EXPECT(mlstm_block_groupnorm_gate(&p, B, T, hc, xc, xup, y, nullptr) == MLSTM_OK);
+    EXPECT(mlstm_block_groupnorm_gate(&p, B, T, hc, xc, xup, xc, nullptr) == MLSTM_ERR_ALIAS);
+    EXPECT(mlstm_layernorm_bf16(x, p.ln_w, p.ln_b, out, B * T, D, 1e-5f, nullptr) == MLSTM_OK);
+    EXPECT(mlstm_layernorm_bf16(x, p.ln_w, p.ln_b, out, B * T, 12, 1e-5f, nullptr) == MLSTM_ERR_BAD_SHAPE);
+    EXPECT(mlstm_layernorm_bf16(x, p.ln_w, p.ln_b, x, B * T, D, 1e-5f, nullptr) == MLSTM_ERR_ALIAS);
+
+    mlstm_gemm_args g;
+    memset(&g, 0, sizeof(g));
+    g.M = 200; g.N = 96; g.K = 128; g.batch1 = 2; g.batch2 = 3;
+    g.A = take(6 * 200 * 128 * 2); g.lda = 128; g.strideA1 = 3 * 200 * 128; g.strideA2 = 200 * 128;
+    g.B = take(3 * 96 * 128 * 2); g.ldb = 128; g.strideB1 = 0; g.strideB2 = 96 * 128;
+    g.C = take(6 * 200 * 96 * 4); g.ldc = 96; g.strideC1 = 3 * 200 * 96; g.strideC2 = 200 * 96;
+    g.c_dtype = MLSTM_FP32; g.alpha = 1.f;
+    g.bias = (const float*)take(3 * 96 * 4); g.stride_bias2 = 96;
+    EXPECT(mlstm_gemm_bf16(&g, nullptr) == MLSTM_OK);
+    mlstm_gemm_args gb = g;
+    gb.K = 100;
+    EXPECT(mlstm_gemm_bf16(&gb, nullptr) == MLSTM_ERR_BAD_SHAPE);
+    gb = g; gb.c_dtype = 5;
+    EXPECT(mlstm_gemm_bf16(&gb, nullptr) == MLSTM_ERR_BAD_DTYPE);
+    gb = g; gb.C = (char*)g.A + 64;
+    EXPECT(mlstm_gemm_bf16(&gb, nullptr) == MLSTM_ERR_ALIAS);
+    gb = g; gb.lda = 132;
+    EXPECT(mlstm_gemm_bf16(&gb, nullptr) == MLSTM_ERR_MISALIGNED);
+    gb = g; gb.c_trans = 1; gb.R = take(200 * 96 * 2); gb.ldr = 96;
+    EXPECT(mlstm_gemm_bf16(&gb, nullptr) == MLSTM_ERR_UNSUPPORTED);
+    EXPECT(mlstm_gemm_bf16(nullptr, nullptr) == MLSTM_ERR_NULLPTR);
   }
 
   if (failures) {

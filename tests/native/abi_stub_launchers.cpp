@@ -58,4 +58,22 @@ hipError_t launch_bwd(const BwdLaunch& b, const GateBuffers&, const ChunkStates&
   return seen(11, b.T == 0 || (bb.G && bb.dz && bb.qdq && bb.Es && bb.es && bb.Ms && bb.L0 && bb.L0e));
 }
 
+hipError_t launch_gemm(const GemmLaunch& g, hipStream_t) {
+  return seen(12, g.M >= 1 && g.N >= 1 && g.K % 64 == 0 && g.N % 4 == 0 && g.nb1 >= 1 && g.nb2 >= 1 && g.A &&
+                      g.B && g.C && g.lda >= g.K && g.ldb >= g.K);
+}
+int gemm_tile() { return 256; }
+hipError_t launch_layernorm(const void* x, const float* w, const float* b, void* y, int64_t rows, int64_t D, float,
+                            hipStream_t) {
+  return seen(13, x && w && b && y && rows >= 1 && D % 8 == 0);
+}
+hipError_t launch_conv_gate(const ConvLaunch& c, hipStream_t) {
+  return seen(14, c.B >= 1 && c.T >= 1 && c.E % 128 == 0 && c.H >= 1 && c.H <= 32 && c.KC >= 1 && c.KC <= 8 &&
+                      c.ldx == 2 * c.E && c.xm && c.xc && c.i_pre && c.f_pre);
+}
+hipError_t launch_groupnorm_gate(const GnLaunch& g, hipStream_t) {
+  return seen(15, g.B >= 1 && g.T >= 1 && g.H * g.dv > 0 && g.dv % 8 == 0 && g.ldz == 2 * g.H * g.dv && g.h &&
+                      g.xc && g.z && g.y);
+}
+
 }  // namespace mlstm_impl

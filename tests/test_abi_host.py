@@ -24,7 +24,7 @@ GB = 1 << 30
 def declared_functions(header=HEADER):
     text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mlstm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mlstm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 8
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mlstm_abi_version() == 2
+    assert lib.mlstm_abi_version() == L.ABI_VERSION == 3
     assert "mlstm_bwd_chunkwise" in names and "mlstm_bwd_chunkwise_workspace_size" in names
     prof = declared_functions(PROF_HEADER)
     assert prof == ["mlstm_clock_probe", "mlstm_prof_bwd_chunkwise", "mlstm_prof_copy_lds",
@@ -471,3 +471,104 @@ def test_lds_copy_validation():
     assert lib.mlstm_prof_copy_lds(A, B, 16384 + 16, None) == BAD_SHAPE
     assert lib.mlstm_prof_copy_lds(A + 4, B, 16384, None) == MISALIGNED
     assert lib.mlstm_prof_copy_lds(A, A + 16384, 32768, None) == ALIAS
+
+
+BLOCK_HEADER = os.path.join(ROOT, "include", "mlstm_block.h")
+
+
+def test_library_exports_every_block_symbol():
+    lib = L.lib()
+    names = declared_functions(BLOCK_HEADER)
+    assert names == ["mlstm_block_conv_gates", "mlstm_block_fwd", "mlstm_block_fwd_workspace_size",
+                     "mlstm_block_groupnorm_gate", "mlstm_block_workspace_offsets", "mlstm_gemm_bf16",
+                     "mlstm_layernorm_bf16"]
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def fake_block(D=256, H=4, dqk=64, dv=128, KC=4):
+    base = [0x7E0000000000]
+
+    def take(nbytes):
+        p = base[0]
+        base[0] += (nbytes + 4095) // 4096 * 4096 + 4096
+        return p
+
+    E = 2 * D
+    sizes = {"ln_w": D * 4, "ln_b": D * 4, "W_up": 2 * E * D * 2, "b_up": 2 * E * 4, "conv_w": E * KC * 4,
+             "conv_b": E * 4, "W_q": H * dqk * (E // H) * 2, "W_k": H * dqk * (E // H) * 2, "b_q": H * dqk * 4,
+             "b_k": H * dqk * 4, "W_v": H * dv * (E // H) * 2, "b_v": E * 4, "w_i": H * E * 2, "w_f": H * E * 2,
+             "b_i": H * 4, "b_f": H * 4, "gn_w": E * 4, "gn_b": E * 4, "skip": E * 4, "W_down": D * E * 2,
+             "b_down": D * 4}
+    p = L.BlockParams(D, H, dqk, dv, KC, 1e-5, 1e-5, *[take(sizes[n]) for n, _ in L.BLOCK_ARRAYS])
+    return p, take
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("D", 100, BAD_SHAPE), ("D", 0, BAD_SHAPE), ("d_v", 64, BAD_SHAPE), ("H", 0, BAD_SHAPE),
+    ("d_qk", 96, UNSUPPORTED), ("KC", 0, UNSUPPORTED), ("KC", 9, UNSUPPORTED), ("eps_gn", -1.0, BAD_SHAPE),
+])
+def test_block_validation(field, value, code):
+    lib = L.lib()
+    p, take = fake_block()
+    B, T = 2, 100
+    need = lib.mlstm_block_fwd_workspace_size(ctypes.byref(p), B, T, 64)
+    assert need > 0
+    x, out, ws = take(B * T * 256 * 2), take(B * T * 256 * 2), take(need)
+    setattr(p, field, value)
+    assert lib.mlstm_block_fwd(ctypes.byref(p), B, T, x, out, 64, ws, need, None) == code
+
+
+def test_block_pointer_and_workspace_checks():
+    lib = L.lib()
+    p, take = fake_block()
+    B, T = 1, 70
+    need = lib.mlstm_block_fwd_workspace_size(ctypes.byref(p), B, T, 64)
+    x, out, ws = take(B * T * 256 * 2), take(B * T * 256 * 2), take(need)
+    assert lib.mlstm_block_fwd(None, B, T, x, out, 64, ws, need, None) == NULLPTR
+    assert lib.mlstm_block_fwd(ctypes.byref(p), B, T, None, out, 64, ws, need, None) == NULLPTR
+    assert lib.mlstm_block_fwd(ctypes.byref(p), B, T, x, out, 64, ws, need - 256, None) == WORKSPACE
+    assert lib.mlstm_block_fwd(ctypes.byref(p), B, T, x, out, 64, ws + 16, need, None) == MISALIGNED
+    assert lib.mlstm_block_fwd(ctypes.byref(p), B, T, x, x, 64, ws, need, None) == ALIAS
+    assert lib.mlstm_block_fwd(ctypes.byref(p), B, T, x, out, 96, ws, need, None) == BAD_SHAPE
+    assert lib.mlstm_block_fwd(ctypes.byref(p), B, 0, x, out, 64, None, 0, None) == OK   # empty: nothing to do
+    p.W_q = None
+    assert lib.mlstm_block_fwd(ctypes.byref(p), B, T, x, out, 64, ws, need, None) == NULLPTR
+    assert lib.mlstm_block_fwd_workspace_size(None, B, T, 64) == 0
+    offs = (ctypes.c_size_t * 10)()
+    assert lib.mlstm_block_workspace_offsets(ctypes.byref(p), B, 0, 64, offs) == BAD_SHAPE
+
+
+def test_gemm_and_layernorm_validation():
+    lib = L.lib()
+    _, take = fake_block()
+    A, Bm, C = take(300 * 128 * 2), take(96 * 128 * 2), take(300 * 96 * 2)
+    g = L.GemmArgs(300, 96, 128, 1, 1, A, 128, 0, 0, Bm, 128, 0, 0, C, 96, 0, 0, L.MLSTM_BF16, 0, 1.0,
+                   None, 0, None, 0, 0, 0)
+    bad = [("K", 96, BAD_SHAPE), ("N", 98, BAD_SHAPE), ("M", 0, BAD_SHAPE), ("c_dtype", 3, BAD_DTYPE),
+           ("ldb", 120, BAD_SHAPE), ("ldc", 100, MISALIGNED), ("A", None, NULLPTR), ("C", A + 256, ALIAS)]
+    for field, value, code in bad:
+        h = L.GemmArgs.from_buffer_copy(g)
+        setattr(h, field, value)
+        assert lib.mlstm_gemm_bf16(ctypes.byref(h), None) == code, field
+    assert lib.mlstm_gemm_bf16(None, None) == NULLPTR
+    x, w, b, y = take(10 * 256 * 2), take(256 * 4), take(256 * 4), take(10 * 256 * 2)
+    assert lib.mlstm_layernorm_bf16(x, w, b, y, 10, 250, 1e-5, None) == BAD_SHAPE
+    assert lib.mlstm_layernorm_bf16(x, w, b, y, 10, 16384, 1e-5, None) == UNSUPPORTED
+    assert lib.mlstm_layernorm_bf16(x, w, b, x, 10, 256, 1e-5, None) == ALIAS
+    assert lib.mlstm_layernorm_bf16(None, w, b, y, 10, 256, 1e-5, None) == NULLPTR
+    assert lib.mlstm_layernorm_bf16(x, w, b, y, 0, 256, 1e-5, None) == OK   # no rows: nothing to do
+
+
+def test_ungated_cell_only_on_the_fused_chunkwise_path():
+    lib = L.lib()
+    a = fake_fwd(dtype=L.MLSTM_FP32)
+    a.o_pre = None
+    assert chunkwise(a) == NULLPTR
+    a = fake_fwd(V=64)        # bf16 but d_v not a multiple of 128: not the fused kernels
+    a.o_pre = None
+    assert chunkwise(a) == NULLPTR
+    a = fake_fwd()
+    a.o_pre = None
+    need = lib.mlstm_fwd_parallel_workspace_size(ctypes.byref(a))
+    assert lib.mlstm_fwd_parallel(ctypes.byref(a), a._next(need), need, None) == NULLPTR
