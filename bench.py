@@ -26,8 +26,10 @@ profiles/, its kernel-trace duration and HBM traffic are reported beside.
 
 Other keys: the chunk sweep, the mid workload (chunkwise and parallel
 forms), the long-context workload (T = 131072), the chunkwise backward pass,
-the decode step, the sLSTM recurrence, and the float64 C oracle timed on the
-host's cores (a baseline, not a target).
+the decode step, the sLSTM recurrence, the mLSTM block around the cell (its
+steps timed one by one, its projections beside the same products in the
+vendor library), and the float64 oracles timed on the host's cores
+(baselines, not targets).
 """
 from __future__ import annotations
 
@@ -53,6 +55,8 @@ MID = dict(B=4, H=8, T=2048, d_qk=128, d_v=128)
 LONG = dict(B=1, H=8, T=131072, d_qk=256, d_v=512)
 DECODE = dict(B=64, H=8, d_qk=256, d_v=512, prefill=512)
 SLSTM = dict(B=16, H=8, D=128, T=2048)   # sLSTM recurrence: 128 sequence-heads of 128 cells
+# the block around the cell at the 7B-layer cell shape: inner width E = 2 D = H d_v = 4096
+BLOCK = dict(B=1, T=8192, D=2048, H=8, d_qk=256, d_v=512, KC=4, chunk=1024)
 TILE = 64                    # tokens per tile: the length of the quadratic (intra-tile) form
 FLUSH_BYTES = 512 << 20
 PROFILES = os.path.join(ROOT, "profiles")
@@ -142,6 +146,27 @@ def slstm_flops(B, H, T, D):
     recurrent dot products (2 * 4 * D) plus about 24 for the gates, the
     stabiliser and the cell update."""
     return B * H * T * D * (8 * D + 24)
+
+
+def block_work(c):
+    """Algorithmic flops and HBM bytes of each step of the block (bf16
+    activations and weights, float32 vectors and gates): a step's bytes are
+    its inputs read once and its outputs written once."""
+    B, T, D, H, K, V, KC = c["B"], c["T"], c["D"], c["H"], c["d_qk"], c["d_v"], c["KC"]
+    E, BT, n_in = 2 * D, c["B"] * c["T"], 2 * c["D"] // c["H"]
+    w = {
+        "layernorm": (8 * BT * D, BT * D * 2 * 2),
+        "up_proj": (2 * BT * D * 2 * E, BT * D * 2 + 2 * E * D * 2 + BT * 2 * E * 2),
+        "conv_gates": (BT * E * (2 * KC + 4) + 2 * BT * E * 2 * H,
+                       BT * E * 2 * 2 + E * (KC + 1) * 4 + 2 * H * E * 2 + 2 * B * H * T * 4),
+        "q_proj": (2 * BT * n_in * K * H, BT * E * 2 + H * K * n_in * 2 + B * H * T * K * 2),
+        "k_proj": (2 * BT * n_in * K * H, BT * E * 2 + H * K * n_in * 2 + B * H * T * K * 2),
+        "v_proj": (2 * BT * n_in * V * H, BT * E * 2 + H * V * n_in * 2 + B * H * T * V * 2),
+        "cell": (fwd_flops(B, H, T, K, V), B * H * T * (2 * K * 2 + 2 * V * 2 + 2 * 4)),
+        "groupnorm_gate": (BT * E * 12, BT * E * 2 * 4),
+        "down_proj": (2 * BT * E * D, BT * E * 2 + D * E * 2 + 2 * BT * D * 2),
+    }
+    return w
 
 
 # ---------------------------------------------------------------- timing
@@ -389,6 +414,85 @@ def time_slstm(torch, timer, reps):
     return r["median_ms"] * 1e-3, pre, R
 
 
+def block_setup(torch, c, seed=0):
+    import numpy as np
+    from linear_recurrent_sequence_fwd_amd import _lib
+    from linear_recurrent_sequence_fwd_amd.inputs import make_block_inputs
+    x, p = make_block_inputs(c["B"], c["T"], c["D"], c["H"], c["d_qk"], c["d_v"], KC=c["KC"], seed=seed)
+    dp = {}
+    for name, is_mat in _lib.BLOCK_ARRAYS:
+        a = torch.from_numpy(np.ascontiguousarray(p[name], dtype=np.float32))
+        dp[name] = a.to("cuda", torch.bfloat16) if is_mat else a.to("cuda")
+    bp = _lib.block_params(dp, c["D"], c["H"], c["d_qk"], c["d_v"], c["KC"], p["eps_ln"], p["eps_gn"])
+    return x, p, dp, bp, torch.from_numpy(x).to("cuda", torch.bfloat16)
+
+
+def block_callables(torch, c, p, dp, bp, xd):
+    """The whole block, each of its steps alone (the same kernels and launch
+    configurations, on the intermediates of a first full run), and the same
+    projections in the vendor library (torch.addmm: hipBLASLt) for reference."""
+    from linear_recurrent_sequence_fwd_amd import _lib
+    B, T, D, H, K, V, chunk = c["B"], c["T"], c["D"], c["H"], c["d_qk"], c["d_v"], c["chunk"]
+    E, BT, n_in = 2 * D, B * T, 2 * D // H
+    out = torch.empty_like(xd)
+    ws = torch.empty(_lib.block_workspace_bytes(bp, B, T, chunk), dtype=torch.uint8, device="cuda")
+    _, st = _lib.mlstm_block_fwd(xd, bp, chunk=chunk, out=out, workspace=ws, return_stages=True)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    cell_args = _lib.fwd_args(st["q"], st["k"], st["v"], None, st["i_pre"], st["f_pre"], st["h"])
+    cell_ws = torch.empty(max(1, _lib.chunkwise_workspace_bytes(cell_args, chunk)), dtype=torch.uint8,
+                          device="cuda")
+
+    def proj(src, ld, W, n_out, bias, alpha, C):
+        return _lib.gemm_bf16_strided(T, n_out, n_in, B, H, src, ld, T * ld, n_in, W, n_in, 0, n_out * n_in,
+                                      C, n_out, H * T * n_out, T * n_out, alpha=alpha, bias=bias,
+                                      stride_bias2=n_out)
+
+    xn2, xup2, y2, out2, x2 = (st["xn"].view(BT, D), st["xup"].view(BT, 2 * E), st["y"].view(BT, E),
+                               out.view(BT, D), xd.view(BT, D))
+    steps = {
+        "layernorm": lambda: _lib.layernorm_bf16(xd, dp["ln_w"], dp["ln_b"], p["eps_ln"], y=st["xn"]),
+        "up_proj": lambda: _lib.gemm_bf16(xn2, dp["W_up"], dp["b_up"], C=xup2),
+        "conv_gates": lambda: _lib.block_conv_gates(bp, st["xup"]),
+        "q_proj": lambda: proj(st["xc"], E, dp["W_q"], K, dp["b_q"], 1.0, st["q"]),
+        "k_proj": lambda: proj(st["xc"], E, dp["W_k"], K, dp["b_k"], K ** -0.5, st["k"]),
+        "v_proj": lambda: proj(st["xup"], 2 * E, dp["W_v"], V, dp["b_v"], 1.0, st["v"]),
+        "cell": lambda: _lib.mlstm_fwd_chunkwise(st["q"], st["k"], st["v"], None, st["i_pre"], st["f_pre"],
+                                                 chunk=chunk, h=st["h"], workspace=cell_ws),
+        "groupnorm_gate": lambda: _lib.block_groupnorm_gate(bp, st["h"], st["xc"], st["xup"]),
+        "down_proj": lambda: _lib.gemm_bf16(y2, dp["W_down"], dp["b_down"], R=x2, C=out2),
+    }
+    lib_out = {"up_proj": torch.empty_like(xup2), "down_proj": torch.empty_like(out2)}
+    b_up16, b_down16 = dp["b_up"].to(torch.bfloat16), dp["b_down"].to(torch.bfloat16)
+    library = {
+        "up_proj": lambda: torch.addmm(b_up16, xn2, dp["W_up"].t(), out=lib_out["up_proj"]),
+        "down_proj": lambda: torch.addmm(b_down16, y2, dp["W_down"].t(), out=lib_out["down_proj"]),
+    }
+
+    def full():
+        _lib.mlstm_block_fwd(xd, bp, chunk=chunk, out=out, workspace=ws)
+
+    return full, steps, library
+
+
+def block_cpu_baseline(x, p, budget_tokens=512):
+    """The float64 block oracle on the first tokens of the block workload,
+    with the host's BLAS threads."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    import oracle.mlstm_block as ob
+    n = host_threads()
+    xs = x[:, :budget_tokens]
+    with threadpool_limits(limits=n):
+        t0 = time.perf_counter()
+        ob.mlstm_block(xs, p)
+        el = time.perf_counter() - t0
+    used = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    return {"value": xs.shape[0] * xs.shape[1] / el, "unit": "tokens/s", "cores": min(n, used), "kind": "oracle",
+            "sample": f"float64 NumPy block oracle (oracle/mlstm_block.py) on the first {xs.shape[1]} of "
+                      f"{x.shape[1]} tokens at the full widths: {el:.2f} s",
+            "cpu_model": cpu_model()}
+
+
 # ---------------------------------------------------------------- host baseline
 
 def cpu_model():
@@ -525,7 +629,7 @@ def measure_clock(torch, one, steps=20, iters=250):
 
 # ---------------------------------------------------------------- main
 
-SECTIONS = ("sweep", "graph", "clock", "bwd", "mid", "long", "decode", "slstm", "cpu")
+SECTIONS = ("sweep", "graph", "clock", "bwd", "block", "mid", "long", "decode", "slstm", "cpu")
 
 
 def main():
@@ -666,6 +770,54 @@ def main():
 
     del d, one, prof
     torch.cuda.empty_cache()
+
+    if "block" in want:
+        bc = BLOCK
+        log(f"[bench] block B={bc['B']} T={bc['T']} D={bc['D']} H={bc['H']} d_qk={bc['d_qk']} d_v={bc['d_v']} "
+            f"chunk={bc['chunk']}")
+        bx, bpar, bdp, bbp, bxd = block_setup(torch, bc, seed=1)
+        full, bsteps, blib = block_callables(torch, bc, bpar, bdp, bbp, bxd)
+        c = timer.cold(full, max(10, args.steps // 3), 2)
+        w = timer.warm(full, max(10, args.steps // 3), 2)
+        work = block_work(bc)
+        per = {}
+        for name, fn in bsteps.items():
+            r = timer.cold(fn, 10, 2)
+            fl, by = work[name]
+            sec = r["median_ms"] * 1e-3
+            per[name] = {"us": r["median_ms"] * 1e3, "tflops": fl / sec / 1e12, "GBps": by / sec / 1e9,
+                         "mfma_frac": fl / sec / MFMA_BF16_PEAK, "hbm_frac": by / sec / HBM_PEAK}
+        ref = {}
+        for name, fn in blib.items():
+            r = timer.cold(fn, 10, 2)
+            fl, _ = work[name]
+            ref[name] = {"us": r["median_ms"] * 1e3, "mfma_frac": fl / (r["median_ms"] * 1e-3) / MFMA_BF16_PEAK}
+        tot_fl = sum(v[0] for v in work.values())
+        dom = max(per, key=lambda k: per[k]["us"])
+        fl, by = work[dom]
+        sec = per[dom]["us"] * 1e-6
+        gemm = dom.endswith("_proj")
+        out["block"] = {
+            "workload": f"mLSTM pre-up-projection block B={bc['B']} T={bc['T']} D={bc['D']} (E={2 * bc['D']}) "
+                        f"H={bc['H']} d_qk={bc['d_qk']} d_v={bc['d_v']} KC={bc['KC']}, cell chunk {bc['chunk']}, bf16",
+            "ms_per_step": c["median_ms"], "ms_per_step_warm": w["median_ms"],
+            "tokens_per_s": bc["B"] * bc["T"] / (c["median_ms"] * 1e-3),
+            "mfma_frac": tot_fl / (c["median_ms"] * 1e-3) / MFMA_BF16_PEAK,
+            "steps_us": per, "library_reference_us": ref, "dominant_step": dom,
+            "roofline": {"kernel": dom, "bound": "mfma" if gemm else "hbm",
+                         "achieved": fl / sec / 1e12 if gemm else by / sec / 1e9,
+                         "peak": MFMA_BF16_PEAK / 1e12 if gemm else HBM_PEAK / 1e9,
+                         "unit": "TFLOP/s" if gemm else "GB/s",
+                         "frac": fl / sec / MFMA_BF16_PEAK if gemm else by / sec / HBM_PEAK,
+                         "traffic": None},
+        }
+        log(f"[bench] block {c['median_ms']:.3f} ms cold ({w['median_ms']:.3f} warm); steps us "
+            + ", ".join(f"{k} {v['us']:.1f}" for k, v in per.items())
+            + "; library " + ", ".join(f"{k} {v['us']:.1f}" for k, v in ref.items()))
+        if "cpu" in want:
+            out["block"]["cpu_baseline"] = block_cpu_baseline(bx, bpar)
+        del full, bsteps, blib, bdp, bbp, bxd
+        torch.cuda.empty_cache()
 
     if "mid" in want:
         log("[bench] mid workload")

@@ -89,7 +89,7 @@ typedef struct mlstm_block_params {
   int64_t D;              /* model width; D % 64 == 0 */
   int64_t H, d_qk, d_v;   /* heads (H <= 32), head dims of the cell (d_qk in {64, 128, 256}, d_v % 128 == 0,
                              d_v <= 2048), H d_v == 2 D, (2 D / H) % 64 == 0 */
-  int64_t KC;             /* causal conv taps, 1..8 */
+  int64_t KC;             /* causal conv taps, 1..4 */
   float eps_ln, eps_gn;   /* layer norm and group norm epsilons */
   const float *ln_w, *ln_b;            /* [D] */
   const void* W_up;                    /* [2E][D] bf16: rows 0..E-1 give xm, rows E..2E-1 give z */

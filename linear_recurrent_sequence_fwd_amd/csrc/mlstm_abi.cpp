@@ -814,7 +814,7 @@ int validate_block(const mlstm_block_params* p, int64_t B, int64_t T) {
   if (!(p->d_qk == 64 || p->d_qk == 128 || p->d_qk == 256))
     return fail(MLSTM_ERR_UNSUPPORTED, "d_qk must be 64, 128 or 256");
   if (p->d_v % 128 || p->d_v > 2048) return fail(MLSTM_ERR_UNSUPPORTED, "d_v must be a multiple of 128 up to 2048");
-  if (p->KC < 1 || p->KC > 8) return fail(MLSTM_ERR_UNSUPPORTED, "KC must be in 1..8");
+  if (p->KC < 1 || p->KC > 4) return fail(MLSTM_ERR_UNSUPPORTED, "KC must be in 1..4");
   if (!(p->eps_ln >= 0.f) || !(p->eps_gn >= 0.f)) return fail(MLSTM_ERR_BAD_SHAPE, "epsilons must be >= 0");
   const void* ptrs[] = {p->ln_w, p->ln_b, p->W_up, p->b_up, p->conv_w, p->conv_b, p->W_q, p->W_k, p->b_q,
                         p->b_k, p->W_v, p->b_v, p->w_i, p->w_f, p->b_i, p->b_f, p->gn_w, p->gn_b, p->skip,

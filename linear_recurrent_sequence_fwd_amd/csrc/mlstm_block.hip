@@ -263,68 +263,103 @@ struct ConvDev {
 
 __device__ __forceinline__ float swish_f(float y) { return y * __builtin_amdgcn_rcpf(1.f + __expf(-y)); }
 
-// One workgroup of four waves per (batch entry, 16 tokens). Wave w takes
-// channels [w E/4, (w + 1) E/4) in steps of 32; lane (i, g) forms token
-// t0 + i, channels c + 8 g .. + 7: the KC taps from rows t - KC + 1 .. t (zero
-// before the sequence start), Swish, the bf16 store, and the same eight
-// rounded values as the A operand of the gate MFMAs (B: the gate weights,
-// rows 16 nb + i of [w_i; w_f]). The four waves' partial gate sums meet in
-// LDS.
-template <int KC>
-__global__ __launch_bounds__(256) void conv_gate_kernel(ConvDev a) {
-  __shared__ f32x4 s_part[4][4][64];   // [wave][gate block][lane]
+// One workgroup of sixteen waves per (batch entry, 16 tokens). Wave w takes
+// the 32-channel steps w, w + 16, ...; lane (i, g) forms token t0 + i,
+// channels c + 8 g .. + 7 of a step: the KC taps from rows t - KC + 1 .. t
+// (zero before the sequence start), Swish, the bf16 store, and the same
+// eight rounded values as the A operand of the gate MFMAs (B: the gate
+// weights, rows 16 nb + i of [w_i; w_f]). The next step's rows and gate
+// weights are loaded before this step's arithmetic. The waves' partial gate
+// sums meet in LDS and are added in a fixed order.
+constexpr int kConvWaves = 16;
+
+template <int KC, int NB>
+__global__ __launch_bounds__(64 * kConvWaves) void conv_gate_kernel(ConvDev a) {
+  __shared__ f32x4 s_part[kConvWaves][NB][64];   // [wave][gate block][lane]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int64_t b = blockIdx.x / a.ntb;
   const int64_t t0 = (int64_t)(blockIdx.x % a.ntb) * 16;
   const int64_t t = t0 + i;
   const bool tv = t < a.T;
-  const int nb_n = (2 * a.H + 15) / 16;
-  f32x4 gacc[4];
+  const int nsteps = a.E / 32;
+  f32x4 gacc[NB];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) gacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int cq = a.E / 4;
-  for (int c0 = w * cq; c0 < (w + 1) * cq; c0 += 32) {
-    const int cc = c0 + 8 * g;
-    bf16x8 xv[KC];
+  for (int nb = 0; nb < NB; ++nb) gacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // gate weight row of this lane in block nb, or null
+  const __bf16* wrow[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = 16 * nb + i;
+    wrow[nb] = n < a.H ? a.wi + (int64_t)n * a.E : (n < 2 * a.H ? a.wf + (int64_t)(n - a.H) * a.E : nullptr);
+  }
+  auto load_x = [&](int st, bf16x8* xv) {
+    const int cc = 32 * st + 8 * g;
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
       const int64_t tt = t - (KC - 1) + j;
       xv[j] = bf16x8{};
       if (tt >= 0 && tt < a.T) xv[j] = ld8(a.xm + (b * a.T + tt) * a.ldx + cc);
     }
-    float cw[8][KC];
+  };
+  auto load_w = [&](int st, bf16x8* wv) {
+    const int cc = 32 * st + 8 * g;
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int nb = 0; nb < NB; ++nb) {
+      wv[nb] = bf16x8{};
+      if (wrow[nb]) wv[nb] = ld8(wrow[nb] + cc);
+    }
+  };
+  // with four gate blocks (17 to 32 heads) the gate weights are loaded in
+  // their own step, not a step ahead: registers
+  constexpr bool kPrefetchW = NB < 4;
+  bf16x8 xv[KC], wv[NB];
+  if (w < nsteps) {
+    load_x(w, xv);
+    if (kPrefetchW) load_w(w, wv);
+  }
+  for (int st = w; st < nsteps; st += kConvWaves) {
+    const int cc = 32 * st + 8 * g;
+    bf16x8 xn[KC], wn[NB];
+    const bool more = st + kConvWaves < nsteps;
+    if (more) {
+      load_x(st + kConvWaves, xn);
+      if (kPrefetchW) load_w(st + kConvWaves, wn);
+    }
+    if (!kPrefetchW) load_w(st, wv);
+    // taps of channels cc .. cc + 7, KC per channel, contiguous
+    f32x4 cwv[2 * KC];
 #pragma unroll
-      for (int j = 0; j < KC; ++j) cw[e][j] = a.cw[(int64_t)(cc + e) * KC + j];
+    for (int q = 0; q < 2 * KC; ++q) cwv[q] = *reinterpret_cast<const f32x4*>(a.cw + (int64_t)cc * KC + 4 * q);
     const f32x4 cb0 = *reinterpret_cast<const f32x4*>(a.cb + cc), cb1 = *reinterpret_cast<const f32x4*>(a.cb + cc + 4);
     bf16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float y = e < 4 ? cb0[e] : cb1[e - 4];
 #pragma unroll
-      for (int j = 0; j < KC; ++j) y = fmaf(cw[e][j], (float)xv[j][e], y);
+      for (int j = 0; j < KC; ++j) y = fmaf(cwv[(e * KC + j) / 4][(e * KC + j) % 4], (float)xv[j][e], y);
       o[e] = tv ? (__bf16)swish_f(y) : (__bf16)0.f;
     }
     if (tv) st8(a.xc + (b * a.T + t) * a.E + cc, o);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      if (nb < nb_n) {
-        const int n = 16 * nb + i;
-        bf16x8 wv = {};
-        if (n < a.H) wv = ld8(a.wi + (int64_t)n * a.E + cc);
-        else if (n < 2 * a.H) wv = ld8(a.wf + (int64_t)(n - a.H) * a.E + cc);
-        gacc[nb] = mma(o, wv, gacc[nb]);   // D[token 4 g + r][gate 16 nb + i]
+    for (int nb = 0; nb < NB; ++nb) gacc[nb] = mma(o, wv[nb], gacc[nb]);   // D[token 4 g + r][gate 16 nb + i]
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < KC; ++j) xv[j] = xn[j];
+      if (kPrefetchW) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) wv[nb] = wn[nb];
       }
     }
   }
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) s_part[w][nb][lane] = gacc[nb];
+  for (int nb = 0; nb < NB; ++nb) s_part[w][nb][lane] = gacc[nb];
   __syncthreads();
   // wave w finishes gate block w
-  if (w < nb_n) {
-    const f32x4 s = s_part[0][w][lane] + s_part[1][w][lane] + s_part[2][w][lane] + s_part[3][w][lane];
+  if (w < NB) {
+    f32x4 s = s_part[0][w][lane];
+#pragma unroll
+    for (int v = 1; v < kConvWaves; ++v) s += s_part[v][w][lane];
     const int n = 16 * w + i;
     if (n < 2 * a.H) {
       const bool isf = n >= a.H;
@@ -355,7 +390,9 @@ struct GnDev {
 };
 
 // One wave per (batch entry, token, head), heads fastest: the head's d_v
-// outputs normalised over d_v, then (. w + b + skip xc) sigmoid(z).
+// outputs normalised over d_v, then (. w + b + skip xc) sigmoid(z). A lane
+// takes pieces of eight channels; every load of the wave (h, xc, z and the
+// three parameter vectors) is issued before the first reduction.
 template <int CH>
 __global__ __launch_bounds__(256) void groupnorm_gate_kernel(GnDev a) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -367,19 +404,30 @@ __global__ __launch_bounds__(256) void groupnorm_gate_kernel(GnDev a) {
   const __bf16* hr = a.h + ((b * a.H + hh) * a.T + t) * a.dv;
   const int64_t E = (int64_t)a.H * a.dv;
   const int64_t col0 = (int64_t)hh * a.dv;
-  float v[CH][8];
-  float s = 0.f;
+  bf16x8 hv[CH], xv[CH], zv[CH];
+  f32x4 pw[CH][2], pb[CH][2], ps[CH][2];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int col = 8 * (lane + 64 * c);
-    bf16x8 p = {};
-    if (col < a.dv) p = ld8(hr + col);
+    hv[c] = xv[c] = zv[c] = bf16x8{};
+    if (col < a.dv) {
+      const int64_t ec = col0 + col;
+      hv[c] = ld8(hr + col);
+      xv[c] = ld8(a.xc + bt * E + ec);
+      zv[c] = ld8(a.z + bt * a.ldz + ec);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      v[c][e] = (float)p[e];
-      s += v[c][e];
+      for (int u = 0; u < 2; ++u) {
+        pw[c][u] = *reinterpret_cast<const f32x4*>(a.gw + ec + 4 * u);
+        pb[c][u] = *reinterpret_cast<const f32x4*>(a.gb + ec + 4 * u);
+        ps[c][u] = *reinterpret_cast<const f32x4*>(a.skip + ec + 4 * u);
+      }
     }
   }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += (float)hv[c][e];
   const float mean = wave_sum(s) / (float)a.dv;
   float q = 0.f;
 #pragma unroll
@@ -388,7 +436,7 @@ __global__ __launch_bounds__(256) void groupnorm_gate_kernel(GnDev a) {
     if (col < a.dv) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float d = v[c][e] - mean;
+        const float d = (float)hv[c][e] - mean;
         q += d * d;
       }
     }
@@ -398,17 +446,15 @@ __global__ __launch_bounds__(256) void groupnorm_gate_kernel(GnDev a) {
   for (int c = 0; c < CH; ++c) {
     const int col = 8 * (lane + 64 * c);
     if (col < a.dv) {
-      const int64_t ec = col0 + col;
-      const bf16x8 xv = ld8(a.xc + bt * E + ec);
-      const bf16x8 zv = ld8(a.z + bt * a.ldz + ec);
       bf16x8 o;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float gn = (v[c][e] - mean) * rstd * a.gw[ec + e] + a.gb[ec + e];
-        const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-(float)zv[e]));
-        o[e] = (__bf16)((gn + a.skip[ec + e] * (float)xv[e]) * sg);
+        const float gw = pw[c][e / 4][e % 4], gb = pb[c][e / 4][e % 4], sk = ps[c][e / 4][e % 4];
+        const float gn = ((float)hv[c][e] - mean) * rstd * gw + gb;
+        const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-(float)zv[c][e]));
+        o[e] = (__bf16)((gn + sk * (float)xv[c][e]) * sg);
       }
-      st8(a.y + bt * E + ec, o);
+      st8(a.y + bt * E + col0 + col, o);
     }
   }
 }
@@ -459,6 +505,14 @@ hipError_t launch_layernorm(const void* x, const float* w, const float* b, void*
   return hipGetLastError();
 }
 
+template <int KC>
+hipError_t launch_conv_kc(const ConvDev& a, int nb, dim3 grid, dim3 block, hipStream_t s) {
+  if (nb == 1) hipLaunchKernelGGL((conv_gate_kernel<KC, 1>), grid, block, 0, s, a);
+  else if (nb == 2) hipLaunchKernelGGL((conv_gate_kernel<KC, 2>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((conv_gate_kernel<KC, 4>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_conv_gate(const ConvLaunch& c, hipStream_t s) {
   ConvDev a;
   a.xm = static_cast<const __bf16*>(c.xm);
@@ -471,19 +525,15 @@ hipError_t launch_conv_gate(const ConvLaunch& c, hipStream_t s) {
   a.i_pre = c.i_pre; a.f_pre = c.f_pre;
   a.T = c.T; a.E = (int)c.E; a.H = (int)c.H; a.KC = (int)c.KC;
   a.ntb = (int)((c.T + 15) / 16);
-  const dim3 grid((unsigned)(c.B * a.ntb)), block(256);
+  const int nb = (int)((2 * c.H + 15) / 16);   // 16-gate blocks: 1, 2, or up to 4
+  const dim3 grid((unsigned)(c.B * a.ntb)), block(64 * kConvWaves);
   switch (c.KC) {
-    case 1: hipLaunchKernelGGL(conv_gate_kernel<1>, grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL(conv_gate_kernel<2>, grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL(conv_gate_kernel<3>, grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL(conv_gate_kernel<4>, grid, block, 0, s, a); break;
-    case 5: hipLaunchKernelGGL(conv_gate_kernel<5>, grid, block, 0, s, a); break;
-    case 6: hipLaunchKernelGGL(conv_gate_kernel<6>, grid, block, 0, s, a); break;
-    case 7: hipLaunchKernelGGL(conv_gate_kernel<7>, grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL(conv_gate_kernel<8>, grid, block, 0, s, a); break;
+    case 1: return launch_conv_kc<1>(a, nb, grid, block, s);
+    case 2: return launch_conv_kc<2>(a, nb, grid, block, s);
+    case 3: return launch_conv_kc<3>(a, nb, grid, block, s);
+    case 4: return launch_conv_kc<4>(a, nb, grid, block, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_groupnorm_gate(const GnLaunch& g, hipStream_t s) {

@@ -186,7 +186,7 @@ hipError_t launch_layernorm(const void* x, const float* w, const float* b, void*
                             float eps, hipStream_t s);
 
 // xc = swish(causal conv(xm)) and the gate preactivations from xc; E % 128 == 0,
-// H <= 32, KC in 1..8
+// H <= 32, KC in 1..4
 struct ConvLaunch {
   int64_t B, T, E, H, KC;
   const void* xm; int64_t ldx;

@@ -229,7 +229,7 @@ int main() {
     EXPECT(mlstm_block_fwd(&bad, B, T, x, out, 64, ws, need, nullptr) == MLSTM_ERR_BAD_SHAPE);
     bad = p; bad.d_qk = 32;
     EXPECT(mlstm_block_fwd(&bad, B, T, x, out, 64, ws, need, nullptr) == MLSTM_ERR_UNSUPPORTED);
-    bad = p; bad.KC = 9;
+    bad = p; bad.KC = 5;
     EXPECT(mlstm_block_fwd(&bad, B, T, x, out, 64, ws, need, nullptr) == MLSTM_ERR_UNSUPPORTED);
     bad = p; bad.skip = nullptr;
     EXPECT(mlstm_block_fwd(&bad, B, T, x, out, 64, ws, need, nullptr) == MLSTM_ERR_NULLPTR);

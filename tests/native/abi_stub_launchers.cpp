@@ -68,7 +68,7 @@ hipError_t launch_layernorm(const void* x, const float* w, const float* b, void*
   return seen(13, x && w && b && y && rows >= 1 && D % 8 == 0);
 }
 hipError_t launch_conv_gate(const ConvLaunch& c, hipStream_t) {
-  return seen(14, c.B >= 1 && c.T >= 1 && c.E % 128 == 0 && c.H >= 1 && c.H <= 32 && c.KC >= 1 && c.KC <= 8 &&
+  return seen(14, c.B >= 1 && c.T >= 1 && c.E % 128 == 0 && c.H >= 1 && c.H <= 32 && c.KC >= 1 && c.KC <= 4 &&
                       c.ldx == 2 * c.E && c.xm && c.xc && c.i_pre && c.f_pre);
 }
 hipError_t launch_groupnorm_gate(const GnLaunch& g, hipStream_t) {

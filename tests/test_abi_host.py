@@ -506,7 +506,7 @@ def fake_block(D=256, H=4, dqk=64, dv=128, KC=4):
 
 @pytest.mark.parametrize("field,value,code", [
     ("D", 100, BAD_SHAPE), ("D", 0, BAD_SHAPE), ("d_v", 64, BAD_SHAPE), ("H", 0, BAD_SHAPE),
-    ("d_qk", 96, UNSUPPORTED), ("KC", 0, UNSUPPORTED), ("KC", 9, UNSUPPORTED), ("eps_gn", -1.0, BAD_SHAPE),
+    ("d_qk", 96, UNSUPPORTED), ("KC", 0, UNSUPPORTED), ("KC", 5, UNSUPPORTED), ("eps_gn", -1.0, BAD_SHAPE),
 ])
 def test_block_validation(field, value, code):
     lib = L.lib()

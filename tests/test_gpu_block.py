@@ -175,6 +175,7 @@ CONFIGS = {
     "mid": (2, 1000, 512, 8, 64, 128, 4, 256),
     "one_token": (3, 1, 256, 4, 64, 128, 4, 64),
     "short_conv": (1, 77, 256, 2, 128, 256, 2, 128),
+    "many_heads": (1, 100, 1024, 16, 64, 128, 3, 64),    # 32 gates: two 16-gate MFMA blocks
 }
 
 
