@@ -42,9 +42,11 @@ __device__ __forceinline__ void st8(__bf16* p, bf16x8 x) { *reinterpret_cast<bf1
 // tile: wave (wm, wn) = (w & 3, w >> 2) owns rows 64 wm .. + 63 and columns
 // 128 wn .. + 127, 4 x 8 accumulator tiles of 16 x 16. The contraction runs
 // in stages of 64: both operand tiles of the next stage are copied into LDS
-// (row pitch 72 elements: 144-byte rows put the 16 rows of a fragment read
-// on distinct banks) with direct-to-LDS buffer loads while the current
-// stage's 64 MFMAs per wave run. Loads past the last valid row return zero.
+// with direct-to-LDS buffer loads while the current stage's 64 MFMAs per
+// wave run. Loads past the last valid row return zero. An LDS row is the
+// stage's 64 elements (eight 16-byte chunks) with chunk c of row r stored at
+// position c ^ (r mod 8), so the rows of a fragment read fall on different
+// banks (a padded pitch measured half of the LDS cycles in bank conflicts).
 //
 // Tiles are numbered XCD by XCD (workgroup b runs on XCD b mod 8), and
 // within an XCD in groups of four tile rows with the row fastest, so the
@@ -53,11 +55,10 @@ __device__ __forceinline__ void st8(__bf16* p, bf16x8 x) { *reinterpret_cast<bf1
 constexpr int kGT = 512;
 constexpr int kGB = 256;                     // tile rows and columns
 constexpr int kGK = 64;                      // contraction depth per stage
-constexpr int kGP = kGK + 8;                 // LDS row pitch (elements)
-constexpr int kGPieces = kGP * 2 / 16;       // 16-byte pieces per LDS row (8 of data)
-constexpr int kGLoads = kGB * kGPieces / 64; // wave-wide loads per operand tile
+constexpr int kGP = kGK;                     // LDS row pitch (elements): eight swizzled chunks
+constexpr int kGLoads = kGB * kGK * 2 / 1024; // wave-wide loads per operand tile
 constexpr int kGTileB = kGB * kGP * 2;       // bytes of one operand tile in LDS
-static_assert(kGB * kGPieces % 64 == 0, "whole wave-wide loads");
+static_assert(kGK == 64, "eight 16-byte chunks per row, swizzled by row mod 8");
 
 struct GemmDev {
   const __bf16 *A, *B;
@@ -109,17 +110,17 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(GemmDev a) {
       const_cast<__bf16*>(Bb), (short)0, (int)(rowsB * a.ldb * 2), kRsrcFlags);
   const int lda2 = (int)(a.lda * 2), ldb2 = (int)(a.ldb * 2);
 
-  // wave-wide load n fills LDS bytes 1024 n .. + 1023 of a tile image: piece
-  // c = 64 n + lane lies in row c / 9; a row's padding piece repeats its last
-  // data piece
+  // wave-wide load n fills LDS bytes 1024 n .. + 1023 of a tile image: the
+  // lane's position c = 64 n + lane is chunk c mod 8 of row c / 8 and takes
+  // the row's chunk (c mod 8) ^ (row mod 8)
   auto load_stage = [&](int kt, int buf) {
     char* la = smem + buf * 2 * kGTileB;
     char* lb = la + kGTileB;
     const int kb = kt * kGK * 2;
     for (int n = w; n < kGLoads; n += kGT / 64) {
-      const int c = 64 * n + lane, row = c / kGPieces, ch = min(c % kGPieces, kGK / 8 - 1);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_b_t*)(la + 1024 * n), 16, row * lda2 + kb + 16 * ch, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_b_t*)(lb + 1024 * n), 16, row * ldb2 + kb + 16 * ch, 0, 0, 0);
+      const int c = 64 * n + lane, row = c >> 3, lc = (c & 7) ^ (row & 7);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_b_t*)(la + 1024 * n), 16, row * lda2 + kb + 16 * lc, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_b_t*)(lb + 1024 * n), 16, row * ldb2 + kb + 16 * lc, 0, 0, 0);
     }
   };
 
@@ -140,9 +141,9 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(GemmDev a) {
     for (int ks = 0; ks < kGK / 32; ++ks) {
       bf16x8 fa[4], fb[8];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) fa[x] = ld8(sA + (64 * wm + 16 * x + i) * kGP + 32 * ks + 8 * g);
+      for (int x = 0; x < 4; ++x) fa[x] = ld8(sA + (64 * wm + 16 * x + i) * kGP + 8 * ((4 * ks + g) ^ (i & 7)));
 #pragma unroll
-      for (int y = 0; y < 8; ++y) fb[y] = ld8(sB + (128 * wn + 16 * y + i) * kGP + 32 * ks + 8 * g);
+      for (int y = 0; y < 8; ++y) fb[y] = ld8(sB + (128 * wn + 16 * y + i) * kGP + 8 * ((4 * ks + g) ^ (i & 7)));
 #pragma unroll
       for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -263,103 +264,96 @@ struct ConvDev {
 
 __device__ __forceinline__ float swish_f(float y) { return y * __builtin_amdgcn_rcpf(1.f + __expf(-y)); }
 
-// One workgroup of sixteen waves per (batch entry, 16 tokens). Wave w takes
-// the 32-channel steps w, w + 16, ...; lane (i, g) forms token t0 + i,
-// channels c + 8 g .. + 7 of a step: the KC taps from rows t - KC + 1 .. t
-// (zero before the sequence start), Swish, the bf16 store, and the same
-// eight rounded values as the A operand of the gate MFMAs (B: the gate
-// weights, rows 16 nb + i of [w_i; w_f]). The next step's rows and gate
-// weights are loaded before this step's arithmetic. The waves' partial gate
-// sums meet in LDS and are added in a fixed order.
-constexpr int kConvWaves = 16;
+// One workgroup of eight waves per (batch entry, 16 tokens). Wave w takes
+// the 512-channel blocks w, w + 8, ... of the inner width; lane l of a block
+// owns channels 8 l .. 8 l + 7 and loads, once, its taps, its bias and rows
+// t0 - KC + 1 .. t0 + 15 of those channels (each row load is 1 KiB contiguous
+// over the wave), forms the 16 tokens' outputs (Swish, bf16), stores them and
+// writes them into the wave's LDS tile [16 tokens][512] (16-byte chunk c of
+// row r at position c ^ r, so neither the row writes nor the fragment reads
+// below share banks). Read back as the A operand of the gate MFMAs (lane
+// (i, g): token i, channels 8 g .. of a 32-deep step; B: the gate weights,
+// rows 16 nb + i of [w_i; w_f]) they give the block's share of the gate
+// preactivations; the waves' shares meet in LDS (each in its own wave's
+// tile, which only that wave uses) and are added in a fixed order.
+constexpr int kConvWaves = 8;
+constexpr int kConvTok = 16;
+constexpr int kConvCh = 512;      // channels per wave and block
 
 template <int KC, int NB>
 __global__ __launch_bounds__(64 * kConvWaves) void conv_gate_kernel(ConvDev a) {
-  __shared__ f32x4 s_part[kConvWaves][NB][64];   // [wave][gate block][lane]
+  __shared__ __attribute__((aligned(16))) __bf16 s_tile[kConvWaves][kConvTok * kConvCh];
+  static_assert(NB * 64 * 16 <= kConvTok * kConvCh * 2, "the gate shares fit in a wave's tile");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int64_t b = blockIdx.x / a.ntb;
-  const int64_t t0 = (int64_t)(blockIdx.x % a.ntb) * 16;
-  const int64_t t = t0 + i;
-  const bool tv = t < a.T;
-  const int nsteps = a.E / 32;
+  const int64_t t0 = (int64_t)(blockIdx.x % a.ntb) * kConvTok;
+  const int nblk = (a.E + kConvCh - 1) / kConvCh;
+  __bf16* tile = s_tile[w];
   f32x4 gacc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) gacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // gate weight row of this lane in block nb, or null
-  const __bf16* wrow[NB];
+  for (int blk = w; blk < nblk; blk += kConvWaves) {
+    const int c0 = blk * kConvCh;
+    const int cc = c0 + 8 * lane;
+    const bool cv = cc < a.E;
+    // rows t0 - KC + 1 .. t0 + 15, all loads issued before any use
+    constexpr int NR = kConvTok + KC - 1;
+    bf16x8 xr[NR];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int n = 16 * nb + i;
-    wrow[nb] = n < a.H ? a.wi + (int64_t)n * a.E : (n < 2 * a.H ? a.wf + (int64_t)(n - a.H) * a.E : nullptr);
-  }
-  auto load_x = [&](int st, bf16x8* xv) {
-    const int cc = 32 * st + 8 * g;
-#pragma unroll
-    for (int j = 0; j < KC; ++j) {
-      const int64_t tt = t - (KC - 1) + j;
-      xv[j] = bf16x8{};
-      if (tt >= 0 && tt < a.T) xv[j] = ld8(a.xm + (b * a.T + tt) * a.ldx + cc);
+    for (int r = 0; r < NR; ++r) {
+      const int64_t tt = t0 - (KC - 1) + r;
+      xr[r] = bf16x8{};
+      if (cv && tt >= 0 && tt < a.T) xr[r] = ld8(a.xm + (b * a.T + tt) * a.ldx + cc);
     }
-  };
-  auto load_w = [&](int st, bf16x8* wv) {
-    const int cc = 32 * st + 8 * g;
+    f32x4 cwv[2 * KC], cb[2];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      wv[nb] = bf16x8{};
-      if (wrow[nb]) wv[nb] = ld8(wrow[nb] + cc);
+    for (int q = 0; q < 2 * KC; ++q)
+      cwv[q] = cv ? *reinterpret_cast<const f32x4*>(a.cw + (int64_t)cc * KC + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) cb[q] = cv ? *reinterpret_cast<const f32x4*>(a.cb + cc + 4 * q) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tk = 0; tk < kConvTok; ++tk) {
+      const int64_t t = t0 + tk;
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float y = cb[e / 4][e % 4];
+#pragma unroll
+        for (int j = 0; j < KC; ++j) y = fmaf(cwv[(e * KC + j) / 4][(e * KC + j) % 4], (float)xr[tk + j][e], y);
+        o[e] = t < a.T && cv ? (__bf16)swish_f(y) : (__bf16)0.f;
+      }
+      if (cv && t < a.T) st8(a.xc + (b * a.T + t) * a.E + cc, o);
+      *reinterpret_cast<bf16x8*>(tile + tk * kConvCh + 8 * (lane ^ tk)) = o;
     }
-  };
-  // with four gate blocks (17 to 32 heads) the gate weights are loaded in
-  // their own step, not a step ahead: registers
-  constexpr bool kPrefetchW = NB < 4;
-  bf16x8 xv[KC], wv[NB];
-  if (w < nsteps) {
-    load_x(w, xv);
-    if (kPrefetchW) load_w(w, wv);
-  }
-  for (int st = w; st < nsteps; st += kConvWaves) {
-    const int cc = 32 * st + 8 * g;
-    bf16x8 xn[KC], wn[NB];
-    const bool more = st + kConvWaves < nsteps;
-    if (more) {
-      load_x(st + kConvWaves, xn);
-      if (kPrefetchW) load_w(st + kConvWaves, wn);
-    }
-    if (!kPrefetchW) load_w(st, wv);
-    // taps of channels cc .. cc + 7, KC per channel, contiguous
-    f32x4 cwv[2 * KC];
+    // the block's gate shares: 16 steps of 32 channels (the wave's own LDS
+    // tile: its stores above are seen by its reads below)
+#pragma unroll 4
+    for (int ks = 0; ks < kConvCh / 32; ++ks) {
+      const int kc = c0 + 32 * ks + 8 * g;
+      const bf16x8 xa = *reinterpret_cast<const bf16x8*>(tile + i * kConvCh + 8 * ((4 * ks + g) ^ i));
 #pragma unroll
-    for (int q = 0; q < 2 * KC; ++q) cwv[q] = *reinterpret_cast<const f32x4*>(a.cw + (int64_t)cc * KC + 4 * q);
-    const f32x4 cb0 = *reinterpret_cast<const f32x4*>(a.cb + cc), cb1 = *reinterpret_cast<const f32x4*>(a.cb + cc + 4);
-    bf16x8 o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float y = e < 4 ? cb0[e] : cb1[e - 4];
-#pragma unroll
-      for (int j = 0; j < KC; ++j) y = fmaf(cwv[(e * KC + j) / 4][(e * KC + j) % 4], (float)xv[j][e], y);
-      o[e] = tv ? (__bf16)swish_f(y) : (__bf16)0.f;
-    }
-    if (tv) st8(a.xc + (b * a.T + t) * a.E + cc, o);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) gacc[nb] = mma(o, wv[nb], gacc[nb]);   // D[token 4 g + r][gate 16 nb + i]
-    if (more) {
-#pragma unroll
-      for (int j = 0; j < KC; ++j) xv[j] = xn[j];
-      if (kPrefetchW) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) wv[nb] = wn[nb];
+      for (int nb = 0; nb < NB; ++nb) {
+        const int n = 16 * nb + i;
+        bf16x8 wv = {};
+        if (kc < a.E) {
+          if (n < a.H) wv = ld8(a.wi + (int64_t)n * a.E + kc);
+          else if (n < 2 * a.H) wv = ld8(a.wf + (int64_t)(n - a.H) * a.E + kc);
+        }
+        gacc[nb] = mma(xa, wv, gacc[nb]);   // D[token 4 g + r][gate 16 nb + i]
       }
     }
   }
+  // the wave's gate shares, [gate block][lane], at the start of its tile
+  auto part = [&](int v, int nb) { return reinterpret_cast<f32x4*>(s_tile[v]) + nb * 64 + lane; };
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) s_part[w][nb][lane] = gacc[nb];
+  for (int nb = 0; nb < NB; ++nb) *part(w, nb) = gacc[nb];
   __syncthreads();
   // wave w finishes gate block w
   if (w < NB) {
-    f32x4 s = s_part[0][w][lane];
+    f32x4 sum = *part(0, w);
 #pragma unroll
-    for (int v = 1; v < kConvWaves; ++v) s += s_part[v][w][lane];
+    for (int v = 1; v < kConvWaves; ++v) sum += *part(v, w);
     const int n = 16 * w + i;
     if (n < 2 * a.H) {
       const bool isf = n >= a.H;
@@ -369,7 +363,7 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_gate_kernel(ConvDev a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t tt = t0 + 4 * g + r;
-        if (tt < a.T) dst[tt] = s[r] + bias;
+        if (tt < a.T) dst[tt] = sum[r] + bias;
       }
     }
   }
@@ -524,7 +518,7 @@ hipError_t launch_conv_gate(const ConvLaunch& c, hipStream_t s) {
   a.bi = c.bi; a.bf = c.bf;
   a.i_pre = c.i_pre; a.f_pre = c.f_pre;
   a.T = c.T; a.E = (int)c.E; a.H = (int)c.H; a.KC = (int)c.KC;
-  a.ntb = (int)((c.T + 15) / 16);
+  a.ntb = (int)((c.T + kConvTok - 1) / kConvTok);
   const int nb = (int)((2 * c.H + 15) / 16);   // 16-gate blocks: 1, 2, or up to 4
   const dim3 grid((unsigned)(c.B * a.ntb)), block(64 * kConvWaves);
   switch (c.KC) {
