@@ -59,6 +59,11 @@ constexpr int kGP = kGK;                     // LDS row pitch (elements): eight 
 constexpr int kGLoads = kGB * kGK * 2 / 1024; // wave-wide loads per operand tile
 constexpr int kGTileB = kGB * kGP * 2;       // bytes of one operand tile in LDS
 static_assert(kGK == 64, "eight 16-byte chunks per row, swizzled by row mod 8");
+// The output tile leaves through LDS in two halves of 128 rows, float32,
+// row pitch 264 (66 16-byte chunks: the 16-byte writes of 16 rows fall on
+// different banks), so that every store covers whole rows.
+constexpr int kGCP = kGB + 8;
+constexpr int kGSmem = 4 * kGTileB > (kGB / 2) * kGCP * 4 ? 4 * kGTileB : (kGB / 2) * kGCP * 4;
 
 struct GemmDev {
   const __bf16 *A, *B;
@@ -83,7 +88,7 @@ template <> __device__ __forceinline__ void store4v<float>(float* p, f32x4 v) { 
 // TRANS: C is written transposed, element (m, n) at C + n ldc + m (no R).
 template <typename TO, bool TRANS>
 __global__ __launch_bounds__(kGT) void gemm_kernel(GemmDev a) {
-  __shared__ __attribute__((aligned(16))) char smem[4 * kGTileB];   // [stage buffer][A, B]
+  __shared__ __attribute__((aligned(16))) char smem[kGSmem];   // [stage buffer][A, B]; then the output halves
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15, g = lane >> 4;
   const int wm = w & 3, wn = w >> 2;
@@ -155,24 +160,43 @@ __global__ __launch_bounds__(kGT) void gemm_kernel(GemmDev a) {
   TO* C = static_cast<TO*>(a.C) + b1 * a.sC1 + b2 * a.sC2;
   const float* bias = a.bias ? a.bias + b2 * a.sbias2 : nullptr;
   if constexpr (!TRANS) {
-    // register r of lane (i, g): row m0 + 64 wm + 16 x + i, column n0 + 128 wn + 16 y + 4 g + r
+    // register r of lane (i, g): row m0 + 64 wm + 16 x + i, column n0 + 128 wn + 16 y + 4 g + r.
+    // alpha acc + bias goes to LDS (float32) by the waves holding the half's
+    // rows; then wave w stores rows w, w + 8, ... of the half, each one
+    // contiguous run of the row, adding the residual before the one rounding.
     const __bf16* R = a.R ? a.R + b1 * a.sR1 + b2 * a.sR2 : nullptr;
+    float* sc = reinterpret_cast<float*>(smem);
+    __syncthreads();   // every wave's last reads of the operand tiles are done
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int m = m0 + 64 * wm + 16 * x + i;
-      if (m >= a.M) continue;
+    for (int half = 0; half < 2; ++half) {
+      if ((wm >> 1) == half) {
 #pragma unroll
-      for (int y = 0; y < 8; ++y) {
-        const int n = n0 + 128 * wn + 16 * y + 4 * g;
-        if (n >= a.N) continue;
-        f32x4 v = acc[x][y] * a.alpha;
-        if (bias) v += *reinterpret_cast<const f32x4*>(bias + n);
-        if (R) {
-          const bf16x4 r = *reinterpret_cast<const bf16x4*>(R + (int64_t)m * a.ldr + n);
-          v += f32x4{(float)r[0], (float)r[1], (float)r[2], (float)r[3]};
+        for (int x = 0; x < 4; ++x) {
+          const int row = 64 * (wm & 1) + 16 * x + i;
+#pragma unroll
+          for (int y = 0; y < 8; ++y) {
+            const int col = 128 * wn + 16 * y + 4 * g;
+            f32x4 v = acc[x][y] * a.alpha;
+            if (bias && n0 + col < a.N) v += *reinterpret_cast<const f32x4*>(bias + n0 + col);
+            *reinterpret_cast<f32x4*>(sc + row * kGCP + col) = v;
+          }
         }
-        store4v<TO>(C + (int64_t)m * a.ldc + n, v);
       }
+      __syncthreads();
+      const int n = n0 + 4 * lane;
+#pragma unroll 4
+      for (int r = w; r < kGB / 2; r += kGT / 64) {
+        const int m = m0 + (kGB / 2) * half + r;
+        if (m < a.M && n < a.N) {
+          f32x4 v = *reinterpret_cast<const f32x4*>(sc + r * kGCP + 4 * lane);
+          if (R) {
+            const bf16x4 rr = *reinterpret_cast<const bf16x4*>(R + (int64_t)m * a.ldr + n);
+            v += f32x4{(float)rr[0], (float)rr[1], (float)rr[2], (float)rr[3]};
+          }
+          store4v<TO>(C + (int64_t)m * a.ldc + n, v);
+        }
+      }
+      if (half == 0) __syncthreads();   // the second half overwrites the staging area
     }
   } else {
     // register r of lane (i, g): row m0 + 64 wm + 16 x + 4 g + r, column n0 + 128 wn + 16 y + i

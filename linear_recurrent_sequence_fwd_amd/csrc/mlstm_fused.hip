@@ -307,6 +307,13 @@ struct OutLds {
   static constexpr int KP = K + 32;       // sK row pitch: 16 dwords mod 64 banks, conflict-free for frag_trk
   static constexpr int VP = kVB + 8;      // sV row pitch (transposed reads)
   static constexpr int PP = kTile + 8;    // sP row pitch
+  // row pitch of the n~ terms: four rows read at once by 16-byte reads, which
+  // at a pitch of 512 bytes all fall on the same banks (measured 4x the
+  // cycles of 544 bytes)
+  static constexpr int NTP = K + 16;
+  // row pitch of the weight terms (the same four-row read; a 160-byte pitch
+  // measured the whole kernel 14% slower, so it stays unpadded)
+  static constexpr int WBP = kTile;
   static constexpr int qBytes = kTile * QP * 2;
   static constexpr int kBytes = kTile * KP * 2;
   static constexpr int vBytes = kTile * VP * 2;
@@ -314,9 +321,9 @@ struct OutLds {
   // sQ, sK and sV are arrays of their own; the rest shares one array at these offsets
   static constexpr int oP = 0;
   // double-buffered tile data, [2] of:
-  static constexpr int nbBytes = 4 * K * 2;          // bf16 [4][K]: n~ at the tile's start as hi, lo, lo2, zero
+  static constexpr int nbBytes = 4 * NTP * 2;        // bf16 [4][NTP]: n~ at the tile's start as hi, lo, lo2, zero
   static constexpr int wBytes = kTile * 4;           // float [64] key weights
-  static constexpr int wbBytes = 4 * kTile * 2;      // bf16 [4][64]: weights hi, lo, lo2, zero
+  static constexpr int wbBytes = 4 * WBP * 2;        // bf16 [4][WBP]: weights hi, lo, lo2, zero
   static constexpr int rowBytes = 5 * kTile * 4;     // r2, sc, fl, u2 (float), rs (int), [64] each
   static constexpr int infoBytes = 16;               // tile info: rescale flag (int), factor (float)
   static constexpr int bufBytes = nbBytes + wBytes + wbBytes + rowBytes + infoBytes;
@@ -358,7 +365,7 @@ struct OutLds {
 template <int K>
 __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, char* lv, char* smem) {
   using L = OutLds<K>;
-  constexpr int QP = L::QP, KP = L::KP, VP = L::VP, PP = L::PP;
+  constexpr int QP = L::QP, KP = L::KP, VP = L::VP, PP = L::PP, NTP = L::NTP, WBP = L::WBP;
   constexpr int KH = K / 2;                                    // d_qk rows per half
   constexpr int KSH = KH / 32;                                 // 32-deep steps per half
   constexpr int KXH = KH / 16;                                 // 16-row state tiles per half
@@ -455,8 +462,8 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
   // zero rows of the weight and normaliser operands, both halves
   for (int b = 0; b < 2; ++b) {
     const TileBuf tb = tile_buf(b);
-    if (tid < kTile) tb.wb[3 * kTile + tid] = (__bf16)0.f;
-    for (int k = tid; k < K; k += 64 * kOutWaves) tb.nt[3 * K + k] = (__bf16)0.f;
+    if (tid < kTile) tb.wb[3 * WBP + tid] = (__bf16)0.f;
+    for (int k = tid; k < K; k += 64 * kOutWaves) tb.nt[3 * NTP + k] = (__bf16)0.f;
   }
 
   // ---------------- copies of the next tile. Rows past the sequence end are
@@ -583,8 +590,8 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
         asm("" : "+v"(off));
         if (ln.i == 0) {
           *reinterpret_cast<bf16x4*>(smem + off) = t0;
-          *reinterpret_cast<bf16x4*>(smem + off + 2 * K) = t1;
-          *reinterpret_cast<bf16x4*>(smem + off + 4 * K) = t2;
+          *reinterpret_cast<bf16x4*>(smem + off + 2 * NTP) = t1;
+          *reinterpret_cast<bf16x4*>(smem + off + 4 * NTP) = t2;
         }
       }
     }
@@ -613,10 +620,10 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
       const float wr = wj - (float)whi;
       const __bf16 wlo = (__bf16)wr;
       tb.wb[j] = whi;
-      int jl = kTile + j;   // kept whole: one step from the array (see put_n)
+      int jl = WBP + j;   // kept whole: one step from the array (see put_n)
       asm("" : "+v"(jl));
       tb.wb[jl] = wlo;
-      int jl2 = 2 * kTile + j;
+      int jl2 = 2 * WBP + j;
       asm("" : "+v"(jl2));
       tb.wb[jl2] = (__bf16)(wr - (float)wlo);
       if (j == 0) {
@@ -743,7 +750,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
 #pragma unroll
       for (int z = 0; z < 4; ++z) sacc[z] = mma(fk, fa[z], sacc[z]);
       const bf16x8 fq = *reinterpret_cast<const bf16x8*>(&sQ[(16 * cg + l1.i) * QP + col]);
-      const bf16x8 fn = *reinterpret_cast<const bf16x8*>(&tb.nt[min(l1.i, 3) * K + col]);
+      const bf16x8 fn = *reinterpret_cast<const bf16x8*>(&tb.nt[min(l1.i, 3) * NTP + col]);
       nqacc = mma(fn, fq, nqacc);
       // the carried state as two bf16 terms: rows whose q is nearly
       // orthogonal to a dominant key make C~ q a strongly cancelling sum
@@ -873,7 +880,7 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
         for (int cv = 0; cv < 2; ++cv)
 #pragma unroll
           for (int e = 0; e < 8; ++e) Bv[cv][e] = (__bf16)((float)Av[jb][cv][e] * (e < 4 ? wa[e] : wb[e - 4]));
-        const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&tb.wb[min(lu.i, 3) * kTile + ts + 8 * lu.g]);
+        const bf16x8 Bw = *reinterpret_cast<const bf16x8*>(&tb.wb[min(lu.i, 3) * WBP + ts + 8 * lu.g]);
         // transposed K fragments through a ring of kRing registers: the read of
         // tile x + kRing - 1 is issued before the MFMAs of tile x
         constexpr int kRing = 4;
