@@ -51,6 +51,7 @@ extern "C" {
  * projections are this call: the up- and down-projections with one batch
  * entry, the per-head q, k, v projections batched over (batch entry, head).
  * Needs M, N, K >= 1, K % 64 == 0, N % 4 == 0 (M % 4 == 0 with c_trans),
+ * lda, ldb <= 2^21 (MLSTM_ERR_UNSUPPORTED beyond),
  * 16-byte aligned arrays and rows (lda, ldb, ldr and the strides of A, B, R
  * multiples of 8 elements; ldc and C's strides multiples of 16 bytes);
  * C must not overlap A, B, bias or R.

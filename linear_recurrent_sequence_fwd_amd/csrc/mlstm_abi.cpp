@@ -771,8 +771,10 @@ int validate_gemm(const mlstm_gemm_args* g) {
   for (const void* p : ptrs)
     if (p && !aligned(p, 16)) return fail(MLSTM_ERR_MISALIGNED, "arrays must be 16-byte aligned");
   const int64_t tile = mlstm_impl::gemm_tile();
+  // the kernel forms a tile's byte range (256 rows of lda or ldb elements) and
+  // its load offsets in 32 bits: row pitches up to 2^21 elements keep them below 2^31
   if (g->M > INT32_MAX / 2 || g->N > INT32_MAX / 2 || g->K > INT32_MAX / 2 ||
-      g->lda > (int64_t)1 << 22 || g->ldb > (int64_t)1 << 22)
+      g->lda > (int64_t)1 << 21 || g->ldb > (int64_t)1 << 21)
     return fail(MLSTM_ERR_UNSUPPORTED, "sizes or row pitches beyond the kernel's 32-bit offsets");
   const int64_t tiles = g->batch1 * g->batch2 * ((g->M + tile - 1) / tile) * ((g->N + tile - 1) / tile);
   if (tiles > INT32_MAX) return fail(MLSTM_ERR_UNSUPPORTED, "problem too large for one launch grid");

@@ -546,6 +546,7 @@ def test_gemm_and_layernorm_validation():
     g = L.GemmArgs(300, 96, 128, 1, 1, A, 128, 0, 0, Bm, 128, 0, 0, C, 96, 0, 0, L.MLSTM_BF16, 0, 1.0,
                    None, 0, None, 0, 0, 0)
     bad = [("K", 96, BAD_SHAPE), ("N", 98, BAD_SHAPE), ("M", 0, BAD_SHAPE), ("c_dtype", 3, BAD_DTYPE),
+           ("lda", (1 << 21) + 8, UNSUPPORTED),
            ("ldb", 120, BAD_SHAPE), ("ldc", 100, MISALIGNED), ("A", None, NULLPTR), ("C", A + 256, ALIAS)]
     for field, value, code in bad:
         h = L.GemmArgs.from_buffer_copy(g)
