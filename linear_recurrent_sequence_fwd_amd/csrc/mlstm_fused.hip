@@ -96,9 +96,14 @@ __device__ __forceinline__ int state_k0(int kx, int g) { return 32 * (kx >> 1) +
 // instead of being hoisted out of the tile loop, where the compiler keeps
 // dozens of them live across the whole tile (and spills them: a spill reload
 // waits for every load in flight, including the next tile's prefetch).
+// The move waits four cycles first. An MFMA reads its accumulator input over
+// its first cycles after issue; the compiler spaces its own writes into such a
+// register from the MFMA, but not an inline-asm write, and the register
+// allocator may give the move a register that an MFMA just issued reads as
+// that input (its last use).
 __device__ __forceinline__ int fresh_tid() {
   int t;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+  asm volatile("s_nop 3\n\tv_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
   return t;
 }
 
