@@ -57,6 +57,8 @@ DECODE = dict(B=64, H=8, d_qk=256, d_v=512, prefill=512)
 SLSTM = dict(B=16, H=8, D=128, T=2048)   # sLSTM recurrence: 128 sequence-heads of 128 cells
 # the block around the cell at the 7B-layer cell shape: inner width E = 2 D = H d_v = 4096
 BLOCK = dict(B=1, T=8192, D=2048, H=8, d_qk=256, d_v=512, KC=4, chunk=1024)
+# one device's share of the long-context sequence split over eight devices
+SEGMENTS = dict(B=1, H=8, T=16384, d_qk=256, d_v=512, chunk=1024, parts=8)
 TILE = 64                    # tokens per tile: the length of the quadratic (intra-tile) form
 FLUSH_BYTES = 512 << 20
 PROFILES = os.path.join(ROOT, "profiles")
@@ -272,6 +274,52 @@ def chunkwise_callables(torch, d, chunk):
 
     one.keep = prof.keep = (h, ws, args)
     return one, prof
+
+
+def segment_callables(torch, d, chunk, parts):
+    """Calls of one device's part in a sequence split into `parts` segments:
+    its summary, the fold of the other devices' summaries into its start
+    state (the last device's: parts - 1 of them), and its forward from the
+    folded start state; arguments marshalled once, the calls only enqueue."""
+    from linear_recurrent_sequence_fwd_amd import _lib
+    B, H, T, K = d["k"].shape
+    V = d["v"].shape[-1]
+    f32 = dict(dtype=torch.float32, device="cuda")
+    summ = (torch.empty((B, H, V, K), **f32), torch.empty((B, H, K), **f32), torch.empty((B, H), **f32),
+            torch.empty((B, H), dtype=torch.float64, device="cuda"))
+    sargs = _lib.summary_args(d["k"], d["v"], d["i_pre"], d["f_pre"], *summ)
+    sbytes = _lib.summary_workspace_bytes(sargs, chunk)
+    sws = torch.empty(sbytes, dtype=torch.uint8, device="cuda")
+    start = (torch.zeros((B, H, V, K), **f32), torch.zeros((B, H, K), **f32), torch.zeros((B, H), **f32))
+    folded = (torch.empty((B, H, V, K), **f32), torch.empty((B, H, K), **f32), torch.empty((B, H), **f32))
+    # the last device's start: the fold of the P - 1 summaries before it, stacked as an all-gather
+    # leaves them
+    stack = tuple(torch.zeros((parts - 1,) + tuple(t.shape), dtype=t.dtype, device="cuda") for t in summ)
+    cargs = _lib.CombineArgs(B, H, K, V, parts - 1, *[t.data_ptr() for t in start],
+                             *[t.data_ptr() for t in stack], *[t.data_ptr() for t in folded])
+    h = torch.empty_like(d["v"])
+    fargs = _lib.fwd_args(d["q"], d["k"], d["v"], d["o_pre"], d["i_pre"], d["f_pre"], h, *folded)
+    fbytes = _lib.chunkwise_workspace_bytes(fargs, chunk)
+    fws = torch.empty(fbytes, dtype=torch.uint8, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    lib = _lib.lib()
+
+    def check(code):
+        if code:
+            raise RuntimeError(lib.mlstm_last_error().decode())
+
+    def summary():
+        check(lib.mlstm_segment_summary(ctypes.byref(sargs), chunk, sws.data_ptr(), sbytes, stream))
+
+    def combine():
+        check(lib.mlstm_state_combine(ctypes.byref(cargs), stream))
+
+    def forward():
+        check(lib.mlstm_fwd_chunkwise(ctypes.byref(fargs), chunk, fws.data_ptr(), fbytes, stream))
+
+    keep = (summ, sargs, sws, start, stack, folded, cargs, h, fargs, fws)
+    summary.keep = combine.keep = forward.keep = keep
+    return summary, combine, forward
 
 
 def parallel_callable(torch, d):
@@ -629,7 +677,7 @@ def measure_clock(torch, one, steps=20, iters=250):
 
 # ---------------------------------------------------------------- main
 
-SECTIONS = ("sweep", "graph", "clock", "bwd", "block", "mid", "long", "decode", "slstm", "cpu")
+SECTIONS = ("sweep", "graph", "clock", "bwd", "block", "mid", "long", "segments", "decode", "slstm", "cpu")
 
 
 def main():
@@ -863,6 +911,37 @@ def main():
             del o, p
         out["long_context"] = res
         del dl
+        torch.cuda.empty_cache()
+
+    if "segments" in want:
+        sc = SEGMENTS
+        P, L = sc["parts"], sc["chunk"]
+        log(f"[bench] segments: one device's share of T={sc['T'] * P} over {P} devices, "
+            f"B={sc['B']} H={sc['H']} T={sc['T']} chunk={L}")
+        _, ds = make_device_inputs(torch, sc, seed=7)
+        summary, combine, forward = segment_callables(torch, ds, L, P)
+        Bq, Hq, Tq, Kq, Vq = sc["B"], sc["H"], sc["T"], sc["d_qk"], sc["d_v"]
+        t_sum = timer.cold(summary, 20, 2)["median_ms"]
+        t_comb = timer.cold(combine, 20, 2)["median_ms"]
+        t_fwd = timer.cold(forward, 20, 2)["median_ms"]
+        state_bytes = Bq * Hq * (Vq * Kq + Kq + 1) * 4 + Bq * Hq * 8
+        sum_bytes = Bq * Hq * Tq * ((Kq + Vq) * 2 + 8) + state_bytes   # k, v, two gates in; the summary out
+        total = t_sum + t_comb + t_fwd
+        out["segments"] = {
+            "workload": f"one of {P} segments of the long-context sequence: B={Bq} H={Hq} T={Tq} d_qk={Kq} "
+                        f"d_v={Vq} bf16, chunk {L}",
+            "summary_ms": t_sum, "fold_ms": t_comb, "forward_from_start_ms": t_fwd,
+            "device_ms": total, "summaries_folded": P - 1,
+            "overhead_vs_forward": (total - t_fwd) / t_fwd,
+            "summary_bytes": state_bytes,
+            "summary_hbm_frac": sum_bytes / (t_sum * 1e-3) / HBM_PEAK,
+            "fold_GBps": (P + 1) * state_bytes / (t_comb * 1e-3) / 1e9,
+            "tokens_per_s_per_device": Bq * Tq / (total * 1e-3),
+            "timing": "cold medians; the exchange of summaries between devices is not measured (one GPU)",
+        }
+        log(f"[bench] segments: summary {t_sum:.3f} ms, fold of {P - 1} summaries {t_comb * 1e3:.1f} us, "
+            f"forward from the start state {t_fwd:.3f} ms")
+        del summary, combine, forward, ds
         torch.cuda.empty_cache()
 
     if "decode" in want:

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define MLSTM_ABI_VERSION 3
+#define MLSTM_ABI_VERSION 4
 
 typedef enum mlstm_status {
   MLSTM_OK = 0,

@@ -5,7 +5,9 @@ sequences), mlstm_fwd_parallel (short sequences), mlstm_step (recurrent
 decode) and mlstm_bwd_chunkwise (the gradients for training);
 include/mlstm_block.h: mlstm_block_fwd (the residual block with
 pre-up-projection around the cell) and its steps (gemm_bf16,
-layernorm_bf16, block_conv_gates, block_groupnorm_gate); and
+layernorm_bf16, block_conv_gates, block_groupnorm_gate);
+include/mlstm_segments.h: mlstm_segment_summary and mlstm_state_combine (one
+sequence run as segments, each from the fold of the summaries before it); and
 include/slstm.h: slstm_fwd (the sLSTM scalar-memory cell's
 recurrence over a sequence). They take torch tensors for device memory and
 run only the HIP library; a missing library raises.
@@ -23,6 +25,8 @@ from ._lib import (  # noqa: F401
     mlstm_fwd_chunkwise,
     mlstm_fwd_chunkwise_noalloc,
     mlstm_fwd_parallel,
+    mlstm_segment_summary,
+    mlstm_state_combine,
     mlstm_step,
     slstm_fwd,
 )

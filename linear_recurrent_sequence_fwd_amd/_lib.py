@@ -1,6 +1,6 @@
 """ctypes binding of libmlstm.so: the C ABI declared in include/mlstm.h,
-include/mlstm_block.h, include/slstm.h and (measurement entry points)
-include/mlstm_prof.h.
+include/mlstm_block.h, include/mlstm_segments.h, include/slstm.h and
+(measurement entry points) include/mlstm_prof.h.
 
 Argument marshalling only. Tensors supply device memory and the current
 stream; every step of the computation runs in the library's HIP kernels.
@@ -86,6 +86,24 @@ class BlockParams(ctypes.Structure):
                 + [(name, c_void_p) for name, _ in BLOCK_ARRAYS])
 
 
+class SummaryArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", c_int64), ("H", c_int64), ("T", c_int64), ("d_qk", c_int64), ("d_v", c_int64),
+        ("dtype", c_int32),
+        ("k", c_void_p), ("v", c_void_p), ("i_pre", c_void_p), ("f_pre", c_void_p),
+        ("C_out", c_void_p), ("n_out", c_void_p), ("m_out", c_void_p), ("G_out", c_void_p),
+    ]
+
+
+class CombineArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", c_int64), ("H", c_int64), ("d_qk", c_int64), ("d_v", c_int64), ("count", c_int64),
+        ("C0", c_void_p), ("n0", c_void_p), ("m0", c_void_p),
+        ("Cs", c_void_p), ("ns", c_void_p), ("ms", c_void_p), ("Gs", c_void_p),
+        ("C_out", c_void_p), ("n_out", c_void_p), ("m_out", c_void_p),
+    ]
+
+
 class SlstmArgs(ctypes.Structure):
     _fields_ = [
         ("B", c_int64), ("H", c_int64), ("T", c_int64), ("D", c_int64),
@@ -104,7 +122,7 @@ class MlstmError(RuntimeError):
 _lib = None
 
 # MLSTM_ABI_VERSION of include/mlstm.h that the argument structs here follow
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 def lib() -> ctypes.CDLL:
@@ -138,6 +156,12 @@ def lib() -> ctypes.CDLL:
         L.mlstm_prof_bwd_chunkwise.argtypes = [P(BwdArgs), c_int, c_void_p, c_size_t, c_void_p,
                                                P(c_void_p)]
         L.mlstm_prof_bwd_chunkwise.restype = c_int
+        L.mlstm_segment_summary_workspace_size.argtypes = [P(SummaryArgs), c_int]
+        L.mlstm_segment_summary_workspace_size.restype = c_size_t
+        L.mlstm_segment_summary.argtypes = [P(SummaryArgs), c_int, c_void_p, c_size_t, c_void_p]
+        L.mlstm_segment_summary.restype = c_int
+        L.mlstm_state_combine.argtypes = [P(CombineArgs), c_void_p]
+        L.mlstm_state_combine.restype = c_int
         L.mlstm_step.argtypes = [P(StepArgs), c_void_p]
         L.mlstm_step.restype = c_int
         L.mlstm_status_string.argtypes = [c_int]
@@ -406,6 +430,75 @@ def step_args(q, k, v, o_pre, i_pre, f_pre, C, n_in, m_in, n_out, m_out, h) -> S
     return StepArgs(B, H, K, V, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o_pre),
                     _ptr(i_pre), _ptr(f_pre), _ptr(C), _ptr(n_in), _ptr(m_in), _ptr(n_out),
                     _ptr(m_out), _ptr(h))
+
+
+def summary_args(k, v, i_pre, f_pre, C_out, n_out, m_out, G_out) -> SummaryArgs:
+    """Fill the argument struct of a segment summary from tensors (shapes checked)."""
+    import torch
+    B, H, T, K = k.shape
+    V = v.shape[-1]
+    _require(k, "k", (B, H, T, K), k.dtype)
+    _require(v, "v", (B, H, T, V), k.dtype)
+    _require(i_pre, "i_pre", (B, H, T), torch.float32)
+    _require(f_pre, "f_pre", (B, H, T), torch.float32)
+    _require(C_out, "C_out", (B, H, V, K), torch.float32)
+    _require(n_out, "n_out", (B, H, K), torch.float32)
+    _require(m_out, "m_out", (B, H), torch.float32)
+    _require(G_out, "G_out", (B, H), torch.float64)
+    return SummaryArgs(B, H, T, K, V, _dtype_code(k), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre),
+                       _ptr(C_out), _ptr(n_out), _ptr(m_out), _ptr(G_out))
+
+
+def summary_workspace_bytes(args: SummaryArgs, chunk: int) -> int:
+    return int(lib().mlstm_segment_summary_workspace_size(ctypes.byref(args), chunk))
+
+
+def mlstm_segment_summary(k, v, i_pre, f_pre, chunk=256, out=None, workspace=None, stream=None):
+    """The summary (C~s, n~s, ms, G) of a segment: its end state from the
+    empty state and the sum of its log forget gates. T must be a multiple of
+    chunk. `out` may supply the four output tensors."""
+    import torch
+    B, H, _, K = k.shape
+    V = v.shape[-1]
+    dev = k.device
+    if out is None:
+        out = (torch.empty((B, H, V, K), dtype=torch.float32, device=dev),
+               torch.empty((B, H, K), dtype=torch.float32, device=dev),
+               torch.empty((B, H), dtype=torch.float32, device=dev),
+               torch.empty((B, H), dtype=torch.float64, device=dev))
+    args = summary_args(k, v, i_pre, f_pre, *out)
+    nbytes = summary_workspace_bytes(args, chunk)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib().mlstm_segment_summary(ctypes.byref(args), int(chunk), _ptr(ws), nbytes, _stream(stream)),
+           "mlstm_segment_summary")
+    return out
+
+
+def mlstm_state_combine(Cs, ns, ms, Gs, C0=None, n0=None, m0=None, out=None, stream=None):
+    """The state after the segments with summaries (Cs, ns, ms, Gs), folded in
+    order into (C0, n0, m0), or into the zero state (m0 = 0) when C0 is None.
+    One summary has the shapes of a state ([B,H,d_v,d_qk], [B,H,d_qk], [B,H],
+    [B,H]); a stack of P summaries has a leading dimension P. Returns (C, n, m)."""
+    import torch
+    stacked = Cs.dim() == 5
+    P = Cs.shape[0] if stacked else 1
+    B, H, V, K = Cs.shape[-4:]
+    lead = (P,) if stacked else ()
+    _require(Cs, "Cs", lead + (B, H, V, K), torch.float32)
+    _require(ns, "ns", lead + (B, H, K), torch.float32)
+    _require(ms, "ms", lead + (B, H), torch.float32)
+    _require(Gs, "Gs", lead + (B, H), torch.float64)
+    if C0 is not None:
+        _require(C0, "C0", (B, H, V, K), torch.float32)
+        _require(n0, "n0", (B, H, K), torch.float32)
+        _require(m0, "m0", (B, H), torch.float32)
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=Cs.device)
+        out = (torch.empty((B, H, V, K), **f32), torch.empty((B, H, K), **f32), torch.empty((B, H), **f32))
+    args = CombineArgs(B, H, K, V, P, _ptr(C0), _ptr(n0), _ptr(m0), _ptr(Cs), _ptr(ns), _ptr(ms), _ptr(Gs),
+                       _ptr(out[0]), _ptr(out[1]), _ptr(out[2]))
+    _check(lib().mlstm_state_combine(ctypes.byref(args), _stream(stream)), "mlstm_state_combine")
+    return out
 
 
 def mlstm_step(q, k, v, o_pre, i_pre, f_pre, C, n_in, m_in, n_out=None, m_out=None, h=None,

@@ -20,6 +20,7 @@ ARCH = "gfx950"
 SOURCES = [os.path.join(CSRC, "mlstm_kernels.hip"), os.path.join(CSRC, "mlstm_bf16.hip"),
            os.path.join(CSRC, "mlstm_fused.hip"), os.path.join(CSRC, "mlstm_bwd.hip"),
            os.path.join(CSRC, "slstm.hip"), os.path.join(CSRC, "mlstm_block.hip"),
+           os.path.join(CSRC, "mlstm_segments.hip"),
            os.path.join(CSRC, "mlstm_abi.cpp")]
 
 # Packed-fp32 VALU instructions are turned off for all device code. MFMA

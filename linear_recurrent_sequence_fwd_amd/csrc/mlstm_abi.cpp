@@ -16,6 +16,7 @@
 #include "../../include/mlstm.h"
 #include "../../include/mlstm_block.h"
 #include "../../include/mlstm_prof.h"
+#include "../../include/mlstm_segments.h"
 #include "../../include/slstm.h"
 #include "mlstm_launch.h"
 
@@ -157,12 +158,15 @@ FusedShape fused_shape(int64_t T, int chunk) {
   return f;
 }
 
-WsLayout layout_fused(int64_t BH, int64_t T, int chunk, int64_t K, int64_t V) {
+// `all_chunks`: a local state for every chunk (a segment summary), not only
+// for chunks 0..S-2 (the forward, whose last chunk's state the output pass
+// carries itself).
+WsLayout layout_fused(int64_t BH, int64_t T, int chunk, int64_t K, int64_t V, bool all_chunks = false) {
   const FusedShape fs = fused_shape(T, chunk);
   WsLayout w = layout(BH, T, fs.Nt, K, V, 4, false);
   size_t off = w.total;
   auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
-  const int64_t ns = fs.S - 1;
+  const int64_t ns = all_chunks ? fs.S : fs.S - 1;
   w.Cseg = take(BH * ns * V * K * 4);
   w.nseg = take(BH * ns * K * 4);
   w.mloc = take(BH * ns * 8);
@@ -1069,6 +1073,147 @@ int mlstm_block_fwd(const mlstm_block_params* p, int64_t B, int64_t T, const voi
   g.A = y; g.lda = E; g.B = p->W_down; g.ldb = E; g.C = out; g.ldc = D; g.bias = p->b_down;
   g.R = x; g.ldr = D;
   return hip_status(mlstm_impl::launch_gemm(g, s), "down-projection");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ segments
+
+namespace {
+
+int validate_summary(const mlstm_summary_args* a, int chunk) {
+  if (!a) return fail(MLSTM_ERR_NULLPTR, "args is NULL");
+  if (a->dtype != MLSTM_FP32 && a->dtype != MLSTM_BF16)
+    return fail(MLSTM_ERR_BAD_DTYPE, "dtype must be MLSTM_FP32 or MLSTM_BF16");
+  if (a->B < 1 || a->H < 1 || a->T < 0 || a->d_qk < 1 || a->d_v < 1)
+    return fail(MLSTM_ERR_BAD_SHAPE, "need B >= 1, H >= 1, T >= 0, d_qk >= 1, d_v >= 1");
+  if (chunk < 64 || chunk % 64 != 0 || chunk > kMaxChunk)
+    return fail(MLSTM_ERR_BAD_SHAPE, "chunk must be a multiple of 64 in [64, 8192]");
+  if (a->T % chunk != 0) return fail(MLSTM_ERR_BAD_SHAPE, "T must be a multiple of chunk (every chunk full)");
+  if (!mlstm_impl::fused_path(a->dtype == MLSTM_BF16, a->d_qk, a->d_v) || a->d_v > 16384)
+    return fail(MLSTM_ERR_UNSUPPORTED, "segment summaries need MLSTM_BF16, d_qk 64, 128 or 256 and d_v a "
+                                       "multiple of 128 (at most 16384)");
+  if (!a->C_out || !a->n_out || !a->m_out || !a->G_out)
+    return fail(MLSTM_ERR_NULLPTR, "C_out, n_out, m_out and G_out are required");
+  if (a->T > 0 && (!a->k || !a->v || !a->i_pre || !a->f_pre))
+    return fail(MLSTM_ERR_NULLPTR, "k, v, i_pre and f_pre are required when T > 0");
+  const void* v16[] = {a->k, a->v, a->C_out, a->n_out};
+  for (const void* p : v16)
+    if (p && !aligned(p, 16)) return fail(MLSTM_ERR_MISALIGNED, "array pointers must be 16-byte aligned");
+  const void* v4[] = {a->i_pre, a->f_pre, a->m_out};
+  for (const void* p : v4)
+    if (p && !aligned(p, 4)) return fail(MLSTM_ERR_MISALIGNED, "gate and m pointers must be 4-byte aligned");
+  if (!aligned(a->G_out, 8)) return fail(MLSTM_ERR_MISALIGNED, "G_out must be 8-byte aligned");
+  const int64_t BH = a->B * a->H;
+  if (BH * (a->d_v / 128) * (a->T / chunk) > INT32_MAX || BH * ((a->d_v * a->d_qk + a->d_qk) / 4 / 256 + 1) > INT32_MAX)
+    return fail(MLSTM_ERR_UNSUPPORTED, "problem too large for one launch grid");
+  const int64_t nqk = BH * a->T * a->d_qk * 2, nv = BH * a->T * a->d_v * 2, ng = BH * a->T * 4;
+  const int64_t nC = BH * a->d_v * a->d_qk * 4, nn = BH * a->d_qk * 4, nm = BH * 4;
+  std::vector<Range> in = {make_range("k", a->k, nqk), make_range("v", a->v, nv),
+                           make_range("i_pre", a->i_pre, ng), make_range("f_pre", a->f_pre, ng)};
+  std::vector<Range> out = {make_range("C_out", a->C_out, nC), make_range("n_out", a->n_out, nn),
+                            make_range("m_out", a->m_out, nm), make_range("G_out", a->G_out, BH * 8)};
+  return check_alias(in, out);
+}
+
+int validate_combine(const mlstm_combine_args* a) {
+  if (!a) return fail(MLSTM_ERR_NULLPTR, "args is NULL");
+  if (a->B < 1 || a->H < 1 || a->d_qk < 1 || a->d_v < 1 || a->count < 0)
+    return fail(MLSTM_ERR_BAD_SHAPE, "need B >= 1, H >= 1, d_qk >= 1, d_v >= 1, count >= 0");
+  if (a->d_qk % 4 != 0) return fail(MLSTM_ERR_BAD_SHAPE, "d_qk must be a multiple of 4");
+  const bool any0 = a->C0 || a->n0 || a->m0, all0 = a->C0 && a->n0 && a->m0;
+  if (any0 && !all0) return fail(MLSTM_ERR_NULLPTR, "C0, n0, m0 must be given together");
+  if (!a->C_out || !a->n_out || !a->m_out) return fail(MLSTM_ERR_NULLPTR, "C_out, n_out and m_out are required");
+  if (a->count > 0 && (!a->Cs || !a->ns || !a->ms || !a->Gs))
+    return fail(MLSTM_ERR_NULLPTR, "Cs, ns, ms and Gs are required when count > 0");
+  const void* v16[] = {a->C0, a->n0, a->Cs, a->ns, a->C_out, a->n_out};
+  for (const void* p : v16)
+    if (p && !aligned(p, 16)) return fail(MLSTM_ERR_MISALIGNED, "state arrays must be 16-byte aligned");
+  const void* v4[] = {a->m0, a->ms, a->m_out};
+  for (const void* p : v4)
+    if (p && !aligned(p, 4)) return fail(MLSTM_ERR_MISALIGNED, "m arrays must be 4-byte aligned");
+  if (a->Gs && !aligned(a->Gs, 8)) return fail(MLSTM_ERR_MISALIGNED, "Gs must be 8-byte aligned");
+  const int64_t BH = a->B * a->H;
+  if (a->d_v > (int64_t)1 << 20 || a->d_qk > (int64_t)1 << 20 || a->count > (int64_t)1 << 20 ||
+      BH * ((a->d_v * a->d_qk + a->d_qk) / 4 / 256 + 1) > INT32_MAX)
+    return fail(MLSTM_ERR_UNSUPPORTED, "problem too large for one launch grid");
+  const int64_t nC = BH * a->d_v * a->d_qk * 4, nn = BH * a->d_qk * 4, nm = BH * 4, c = a->count;
+  std::vector<Range> in = {make_range("C0", a->C0, nC), make_range("n0", a->n0, nn),
+                           make_range("m0", a->m0, nm), make_range("Cs", a->Cs, c * nC),
+                           make_range("ns", a->ns, c * nn), make_range("ms", a->ms, c * nm),
+                           make_range("Gs", a->Gs, c * BH * 8)};
+  std::vector<Range> out = {make_range("C_out", a->C_out, nC), make_range("n_out", a->n_out, nn),
+                            make_range("m_out", a->m_out, nm)};
+  return check_alias(in, out);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mlstm_segment_summary_workspace_size(const mlstm_summary_args* a, int chunk) {
+  if (!a || a->T <= 0 || a->B < 1 || a->H < 1 || chunk < 64 || chunk % 64 != 0 || chunk > kMaxChunk ||
+      a->T % chunk != 0 || !mlstm_impl::fused_path(a->dtype == MLSTM_BF16, a->d_qk, a->d_v))
+    return 0;
+  return layout_fused(a->B * a->H, a->T, chunk, a->d_qk, a->d_v, true).total;
+}
+
+int mlstm_segment_summary(const mlstm_summary_args* a, int chunk, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  g_last_error.clear();
+  int st = validate_summary(a, chunk);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t BH = a->B * a->H;
+  const mlstm_impl::SummaryOut o{a->C_out, a->n_out, a->m_out, a->G_out};
+  if (a->T == 0) return hip_status(mlstm_impl::launch_summary_empty(o, BH, a->d_qk, a->d_v, s), "summary fill");
+  const size_t need = mlstm_segment_summary_workspace_size(a, chunk);
+  if (!workspace) return fail(MLSTM_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, kAlign)) return fail(MLSTM_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(MLSTM_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  {
+    const int64_t nqk = BH * a->T * a->d_qk * 2, nv = BH * a->T * a->d_v * 2, ng = BH * a->T * 4;
+    const int64_t nC = BH * a->d_v * a->d_qk * 4, nn = BH * a->d_qk * 4, nm = BH * 4;
+    const Range wr = make_range("workspace", workspace, (int64_t)need);
+    const Range other[] = {make_range("k", a->k, nqk), make_range("v", a->v, nv),
+                           make_range("i_pre", a->i_pre, ng), make_range("f_pre", a->f_pre, ng),
+                           make_range("C_out", a->C_out, nC), make_range("n_out", a->n_out, nn),
+                           make_range("m_out", a->m_out, nm), make_range("G_out", a->G_out, BH * 8)};
+    for (const Range& r : other)
+      if (overlap(wr, r)) return fail(MLSTM_ERR_ALIAS, std::string("workspace overlaps ") + r.name);
+  }
+  const FusedShape fs = fused_shape(a->T, chunk);
+  mlstm_impl::FwdLaunch f{};
+  f.BH = BH; f.T = a->T; f.K = a->d_qk; f.V = a->d_v;
+  f.L = 64; f.Nc = fs.Nt; f.bf16 = 1;
+  f.k = a->k; f.v = a->v; f.i_pre = a->i_pre; f.f_pre = a->f_pre;
+  const WsLayout w = layout_fused(BH, a->T, chunk, a->d_qk, a->d_v, true);
+  char* ws = static_cast<char*>(workspace);
+  mlstm_impl::GateBuffers gb = gate_buffers(ws, w);
+  gb.wb = reinterpret_cast<uint16_t*>(ws + w.wb);
+  mlstm_impl::SegStates ss;
+  ss.C = reinterpret_cast<float*>(ws + w.Cseg);
+  ss.n = reinterpret_cast<float*>(ws + w.nseg);
+  ss.mloc = reinterpret_cast<double*>(ws + w.mloc);
+  ss.mstart = reinterpret_cast<double*>(ws + w.mstart);
+  ss.G = reinterpret_cast<double*>(ws + w.Gseg);
+  ss.S = (int)fs.S;
+  ss.TPS = (int)fs.TPS;
+  if ((st = hip_status(mlstm_impl::launch_gate(f, gb, s), "gate kernel"))) return st;
+  return hip_status(mlstm_impl::launch_summary(f, gb, ss, o, s), "summary kernels");
+}
+
+int mlstm_state_combine(const mlstm_combine_args* a, void* stream) {
+  g_last_error.clear();
+  const int st = validate_combine(a);
+  if (st) return st;
+  mlstm_impl::CombineLaunch c;
+  c.BH = a->B * a->H; c.K = a->d_qk; c.V = a->d_v; c.count = a->count;
+  c.C0 = a->C0; c.n0 = a->n0; c.m0 = a->m0;
+  c.Cs = a->Cs; c.ns = a->ns; c.ms = a->ms; c.Gs = a->Gs;
+  c.C = a->C_out; c.n = a->n_out; c.m = a->m_out;
+  return hip_status(mlstm_impl::launch_state_combine(c, static_cast<hipStream_t>(stream)), "combine kernel");
 }
 
 }  // extern "C"

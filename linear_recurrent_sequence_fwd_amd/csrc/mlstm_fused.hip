@@ -1392,14 +1392,17 @@ __global__ __launch_bounds__(64 * (LocWaves<K>::value + 1)) void local_kernel(Se
 // ------------------------------------------------------------------ chunk combine
 
 struct CombineArgs {
-  const float *C0, *n0, *m0;
-  float* Cseg;
-  float* nseg;
-  const double* mloc;
-  double* mstart;
-  const double* Gseg;
-  int64_t V, K, BH;
-  int S;
+  const float *C0 = nullptr, *n0 = nullptr, *m0 = nullptr;
+  float* Cseg = nullptr;
+  float* nseg = nullptr;
+  const double* mloc = nullptr;
+  double* mstart = nullptr;
+  const double* Gseg = nullptr;
+  // A segment summary instead: the fold starts from the empty state
+  // (m = -inf), its end goes to these, and the folded states are not stored.
+  SummaryOut out = {nullptr, nullptr, nullptr, nullptr};
+  int64_t V = 0, K = 0, BH = 0;
+  int S = 0;
 };
 
 // Folds the local end states of chunks 0..S-2 in order: with the start state
@@ -1407,7 +1410,9 @@ struct CombineArgs {
 // G, the start of chunk s+1 is m' = max(m + G, mloc),
 // C~' = exp(m + G - m') C~ + exp(mloc - m') C~loc (the same for n~). Each
 // thread owns four consecutive floats of one head's C~ or n~; the result
-// overwrites the local state in place.
+// overwrites the local state in place. For a segment summary (a.out.C set)
+// the fold starts from the empty state and only its end is written, with
+// the sum of the chunks' log-forget totals.
 __global__ __launch_bounds__(kThreads) void seg_combine_kernel(CombineArgs a) {
   const int64_t BH = a.BH;
   const int64_t bh = blockIdx.x % BH;
@@ -1418,8 +1423,9 @@ __global__ __launch_bounds__(kThreads) void seg_combine_kernel(CombineArgs a) {
   const int64_t off = is_n ? (u - nc4) * 4 : u * 4;
   const int64_t stride = is_n ? a.K : a.V * a.K;
   float* base = (is_n ? a.nseg : a.Cseg) + off;
+  const bool summary = a.out.C != nullptr;
   f32x4 x = {0.f, 0.f, 0.f, 0.f};
-  double m = 0.0;
+  double m = summary ? -INFINITY : 0.0, gsum = 0.0;
   if (a.C0) {
     x = *reinterpret_cast<const f32x4*>((is_n ? a.n0 + bh * a.K : a.C0 + bh * a.V * a.K) + off);
     m = (double)a.m0[bh];
@@ -1441,14 +1447,25 @@ __global__ __launch_bounds__(kThreads) void seg_combine_kernel(CombineArgs a) {
         const double G = a.Gseg[sidx], ml = a.mloc[sidx];
         const double mc = G == -INFINITY ? -INFINITY : m + G;
         double mn = fmax(mc, ml);
-        if (mn == -INFINITY) mn = 0.0;
+        // an all-zero state: m = 0 in a start state, kept at -inf in a summary
+        if (mn == -INFINITY && !summary) mn = 0.0;
         const float al = mc == -INFINITY ? 0.f : exp_f64arg(mc - mn);
         const float be = ml == -INFINITY ? 0.f : exp_f64arg(ml - mn);
         x = al * x + be * y[e];
-        *reinterpret_cast<f32x4*>(base + sidx * stride) = x;
-        if (u == 0) a.mstart[sidx] = mn;
+        gsum += G;
+        if (!summary) {
+          *reinterpret_cast<f32x4*>(base + sidx * stride) = x;
+          if (u == 0) a.mstart[sidx] = mn;
+        }
         m = mn;
       }
+    }
+  }
+  if (summary) {
+    *reinterpret_cast<f32x4*>((is_n ? a.out.n + bh * a.K : a.out.C + bh * a.V * a.K) + off) = x;
+    if (u == 0) {
+      a.out.m[bh] = (float)m;
+      a.out.G[bh] = gsum;
     }
   }
 }
@@ -1489,7 +1506,41 @@ hipError_t run_seg(const FwdLaunch& f, const GateBuffers& gb, const SegStates& s
   return hipGetLastError();
 }
 
+template <int K>
+hipError_t run_summary(const FwdLaunch& f, const GateBuffers& gb, const SegStates& ss, const SummaryOut& o,
+                       hipStream_t s) {
+  SegArgs a{};
+  a.k = static_cast<const __bf16*>(f.k);
+  a.v = static_cast<const __bf16*>(f.v);
+  a.gb = gb;
+  a.Cseg = ss.C; a.nseg = ss.n; a.mloc = ss.mloc; a.mstart = ss.mstart; a.Gseg = ss.G;
+  a.T = f.T; a.Nt = f.Nc; a.V = f.V; a.BH = f.BH;
+  // every chunk takes a local state: the states are indexed by chunk as those
+  // of chunks 0..S-2 of a sequence one chunk longer
+  a.TPS = ss.TPS; a.S = ss.S + 1;
+  const int64_t nvb = f.V / kVB;
+  hipLaunchKernelGGL((local_kernel<K>), dim3((unsigned)(f.BH * nvb * ss.S)), dim3(64 * (LocWaves<K>::value + 1)), 0, s, a);
+  CombineArgs c;
+  c.Cseg = ss.C; c.nseg = ss.n; c.mloc = ss.mloc; c.mstart = ss.mstart; c.Gseg = ss.G;
+  c.out = o;
+  c.V = f.V; c.K = K; c.BH = f.BH; c.S = ss.S + 1;
+  const int64_t units = f.V * K / 4 + K / 4;
+  const int64_t blocks = (units + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(f.BH * blocks)), dim3(kThreads), 0, s, c);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_summary(const FwdLaunch& f, const GateBuffers& gb, const SegStates& ss, const SummaryOut& o,
+                          hipStream_t s) {
+  switch (f.K) {
+    case 64: return run_summary<64>(f, gb, ss, o, s);
+    case 128: return run_summary<128>(f, gb, ss, o, s);
+    case 256: return run_summary<256>(f, gb, ss, o, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 bool fused_path(int bf16, int64_t K, int64_t V) {
   return bf16 && V % kVB == 0 && (K == 64 || K == 128 || K == 256);

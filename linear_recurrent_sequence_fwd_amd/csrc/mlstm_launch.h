@@ -159,6 +159,34 @@ hipError_t launch_out_bf16(const FwdLaunch& a, const GateBuffers& gb, const Chun
 bool fused_path(int bf16, int64_t K, int64_t V);
 hipError_t launch_fused(const FwdLaunch& a, const GateBuffers& gb, const SegStates& ss, hipStream_t s);
 
+// Segments of one sequence (mlstm_fused.hip, mlstm_segments.hip).
+// A segment's summary: its end state from the empty state (m = -inf) and the
+// sum G of its log forget gates, per head. C [BH][V][K], n [BH][K], m [BH]
+// float32, G [BH] float64.
+struct SummaryOut {
+  float *C, *n, *m;
+  double* G;
+};
+// The summary from the chunk-local states of all ss.S chunks (every chunk
+// full: T == ss.S * chunk) folded from the empty state; the gate buffers as
+// for launch_fused, ss holding ss.S (not ss.S - 1) chunk entries.
+hipError_t launch_summary(const FwdLaunch& a, const GateBuffers& gb, const SegStates& ss, const SummaryOut& o,
+                          hipStream_t s);
+// The summary of an empty segment: C = n = 0, m = -inf, G = 0.
+hipError_t launch_summary_empty(const SummaryOut& o, int64_t BH, int64_t K, int64_t V, hipStream_t s);
+// The state after `count` segments with the stacked summaries (Cs, ns, ms, Gs:
+// [count][BH][...]) folded in order into the start state (C0, n0, m0), or into
+// the zero state with m0 = 0 when C0 is null. K % 4 == 0, 16-byte aligned
+// state arrays.
+struct CombineLaunch {
+  int64_t BH, K, V, count;
+  const float *C0, *n0, *m0;
+  const float *Cs, *ns, *ms;
+  const double* Gs;
+  float *C, *n, *m;
+};
+hipError_t launch_state_combine(const CombineLaunch& c, hipStream_t s);
+
 // mLSTM block around the cell (mlstm_block.hip).
 //
 // GEMM: C = alpha A B^T + bias (+ R) per batch entry (b1, b2), A [M][K] and

@@ -1,5 +1,5 @@
 // Drives every entry point of the mLSTM C ABI (include/mlstm.h,
-// mlstm_block.h, slstm.h, mlstm_prof.h) through its argument checks and, with host-only stand-in
+// mlstm_block.h, mlstm_segments.h, slstm.h, mlstm_prof.h) through its argument checks and, with host-only stand-in
 // launchers (abi_stub_launchers.cpp), through its workspace carving and
 // dispatch, in a build with AddressSanitizer and UndefinedBehaviorSanitizer
 // on the host code. Pointers are fabricated addresses that nothing
@@ -13,9 +13,10 @@
 #include "../../include/mlstm.h"
 #include "../../include/mlstm_block.h"
 #include "../../include/mlstm_prof.h"
+#include "../../include/mlstm_segments.h"
 #include "../../include/slstm.h"
 
-namespace mlstm_impl { extern int g_calls[16]; }
+namespace mlstm_impl { extern int g_calls[20]; }
 
 static int failures = 0;
 #define EXPECT(cond)                                                   \
@@ -207,8 +208,8 @@ int main() {
     const size_t need = mlstm_block_fwd_workspace_size(&p, B, T, 64);
     EXPECT(need > 0);
     void* ws = take(need);
-    int before[16];
-    for (int j = 0; j < 16; ++j) before[j] = g_calls[j];
+    int before[20];
+    for (int j = 0; j < 20; ++j) before[j] = g_calls[j];
     EXPECT(mlstm_block_fwd(&p, B, T, x, out, 64, ws, need, nullptr) == MLSTM_OK);
     EXPECT(g_calls[12] == before[12] + 5);   // up, q, k, v, down
     EXPECT(g_calls[13] == before[13] + 1 && g_calls[14] == before[14] + 1 && g_calls[15] == before[15] + 1);
@@ -272,6 +273,72 @@ int main() {
     gb = g; gb.c_trans = 1; gb.R = take(200 * 96 * 2); gb.ldr = 96;
     EXPECT(mlstm_gemm_bf16(&gb, nullptr) == MLSTM_ERR_UNSUPPORTED);
     EXPECT(mlstm_gemm_bf16(nullptr, nullptr) == MLSTM_ERR_NULLPTR);
+  }
+
+  {   // segments: summary and fold
+    const int64_t B = 1, H = 2, T = 512, K = 128, V = 256, BH = B * H;
+    mlstm_summary_args a;
+    memset(&a, 0, sizeof(a));
+    a.B = B; a.H = H; a.T = T; a.d_qk = K; a.d_v = V; a.dtype = MLSTM_BF16;
+    a.k = take(BH * T * K * 2); a.v = take(BH * T * V * 2);
+    a.i_pre = (const float*)take(BH * T * 4); a.f_pre = (const float*)take(BH * T * 4);
+    a.C_out = (float*)take(BH * V * K * 4); a.n_out = (float*)take(BH * K * 4);
+    a.m_out = (float*)take(BH * 4); a.G_out = (double*)take(BH * 8);
+    const size_t need = mlstm_segment_summary_workspace_size(&a, 128);
+    EXPECT(need > 0);
+    void* ws = take(need);
+    int before[20];
+    for (int j = 0; j < 20; ++j) before[j] = g_calls[j];
+    EXPECT(mlstm_segment_summary(&a, 128, ws, need, nullptr) == MLSTM_OK);
+    EXPECT(g_calls[0] == before[0] + 1 && g_calls[16] == before[16] + 1);
+    EXPECT(mlstm_segment_summary(&a, 128, ws, need - 1, nullptr) == MLSTM_ERR_WORKSPACE);
+    EXPECT(mlstm_segment_summary(&a, 192, ws, need, nullptr) == MLSTM_ERR_BAD_SHAPE);   // 512 % 192
+    EXPECT(mlstm_segment_summary(&a, 100, ws, need, nullptr) == MLSTM_ERR_BAD_SHAPE);
+    mlstm_summary_args b = a;
+    b.dtype = MLSTM_FP32;
+    EXPECT(mlstm_segment_summary(&b, 128, ws, need, nullptr) == MLSTM_ERR_UNSUPPORTED);
+    b = a; b.d_v = 192;
+    EXPECT(mlstm_segment_summary(&b, 128, ws, need, nullptr) == MLSTM_ERR_UNSUPPORTED);
+    b = a; b.G_out = nullptr;
+    EXPECT(mlstm_segment_summary(&b, 128, ws, need, nullptr) == MLSTM_ERR_NULLPTR);
+    b = a; b.G_out = (double*)((char*)a.G_out + 4);
+    EXPECT(mlstm_segment_summary(&b, 128, ws, need, nullptr) == MLSTM_ERR_MISALIGNED);
+    b = a; b.n_out = (float*)a.C_out;
+    EXPECT(mlstm_segment_summary(&b, 128, ws, need, nullptr) == MLSTM_ERR_ALIAS);
+    EXPECT(mlstm_segment_summary(&a, 128, (void*)a.k, need, nullptr) == MLSTM_ERR_ALIAS);
+    b = a; b.T = 0;
+    EXPECT(mlstm_segment_summary_workspace_size(&b, 128) == 0);
+    EXPECT(mlstm_segment_summary(&b, 128, nullptr, 0, nullptr) == MLSTM_OK);
+    EXPECT(g_calls[17] == before[17] + 1);
+    EXPECT(mlstm_segment_summary(nullptr, 128, ws, need, nullptr) == MLSTM_ERR_NULLPTR);
+
+    mlstm_combine_args c;
+    memset(&c, 0, sizeof(c));
+    c.B = B; c.H = H; c.d_qk = K; c.d_v = V; c.count = 1;
+    c.Cs = a.C_out; c.ns = a.n_out; c.ms = a.m_out; c.Gs = a.G_out;
+    c.C_out = (float*)take(BH * V * K * 4); c.n_out = (float*)take(BH * K * 4); c.m_out = (float*)take(BH * 4);
+    EXPECT(mlstm_state_combine(&c, nullptr) == MLSTM_OK);   // from the zero state
+    c.C0 = (const float*)take(BH * V * K * 4); c.n0 = (const float*)take(BH * K * 4); c.m0 = (const float*)take(BH * 4);
+    EXPECT(mlstm_state_combine(&c, nullptr) == MLSTM_OK);
+    EXPECT(g_calls[18] == before[18] + 2);
+    mlstm_combine_args d = c;
+    d.m0 = nullptr;
+    EXPECT(mlstm_state_combine(&d, nullptr) == MLSTM_ERR_NULLPTR);
+    d = c; d.C_out = (float*)c.C0;
+    EXPECT(mlstm_state_combine(&d, nullptr) == MLSTM_ERR_ALIAS);
+    d = c; d.m_out = c.n_out;
+    EXPECT(mlstm_state_combine(&d, nullptr) == MLSTM_ERR_ALIAS);
+    d = c; d.Gs = (const double*)((const char*)c.Gs + 4);
+    EXPECT(mlstm_state_combine(&d, nullptr) == MLSTM_ERR_MISALIGNED);
+    d = c; d.d_v = 0;
+    EXPECT(mlstm_state_combine(&d, nullptr) == MLSTM_ERR_BAD_SHAPE);
+    d = c; d.count = -1;
+    EXPECT(mlstm_state_combine(&d, nullptr) == MLSTM_ERR_BAD_SHAPE);
+    d = c; d.count = 0; d.Cs = nullptr; d.ns = nullptr; d.ms = nullptr; d.Gs = nullptr;
+    EXPECT(mlstm_state_combine(&d, nullptr) == MLSTM_OK);   // the start state itself
+    d = c; d.C_out = (float*)((char*)c.C_out + 4);
+    EXPECT(mlstm_state_combine(&d, nullptr) == MLSTM_ERR_MISALIGNED);
+    EXPECT(mlstm_state_combine(nullptr, nullptr) == MLSTM_ERR_NULLPTR);
   }
 
   if (failures) {

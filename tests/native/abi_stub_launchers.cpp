@@ -13,7 +13,7 @@
 
 namespace mlstm_impl {
 
-int g_calls[16];
+int g_calls[20];
 
 static hipError_t seen(int id, bool ok) {
   ++g_calls[id];
@@ -70,6 +70,19 @@ hipError_t launch_layernorm(const void* x, const float* w, const float* b, void*
 hipError_t launch_conv_gate(const ConvLaunch& c, hipStream_t) {
   return seen(14, c.B >= 1 && c.T >= 1 && c.E % 128 == 0 && c.H >= 1 && c.H <= 32 && c.KC >= 1 && c.KC <= 4 &&
                       c.ldx == 2 * c.E && c.xm && c.xc && c.i_pre && c.f_pre);
+}
+hipError_t launch_summary(const FwdLaunch& a, const GateBuffers& gb, const SegStates& ss, const SummaryOut& o,
+                          hipStream_t) {
+  return seen(16, fwd_ok(a) && a.L == 64 && gb.wb && ss.S >= 1 && ss.TPS >= 1 &&
+                      (int64_t)ss.S * ss.TPS == a.Nc && a.T == a.Nc * 64 && o.C && o.n && o.m && o.G);
+}
+hipError_t launch_summary_empty(const SummaryOut& o, int64_t BH, int64_t K, int64_t V, hipStream_t) {
+  return seen(17, o.C && o.n && o.m && o.G && BH >= 1 && K >= 1 && V >= 1);
+}
+hipError_t launch_state_combine(const CombineLaunch& c, hipStream_t) {
+  return seen(18, c.BH >= 1 && c.K >= 1 && c.K % 4 == 0 && c.V >= 1 && c.count >= 0 &&
+                      (c.count == 0 || (c.Cs && c.ns && c.ms && c.Gs)) && c.C && c.n && c.m &&
+                      (c.C0 ? c.n0 && c.m0 : !c.n0 && !c.m0));
 }
 hipError_t launch_groupnorm_gate(const GnLaunch& g, hipStream_t) {
   return seen(15, g.B >= 1 && g.T >= 1 && g.H * g.dv > 0 && g.dv % 8 == 0 && g.ldz == 2 * g.H * g.dv && g.h &&

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 8
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.mlstm_abi_version() == L.ABI_VERSION == 3
+    assert lib.mlstm_abi_version() == L.ABI_VERSION == 4
     assert "mlstm_bwd_chunkwise" in names and "mlstm_bwd_chunkwise_workspace_size" in names
     prof = declared_functions(PROF_HEADER)
     assert prof == ["mlstm_clock_probe", "mlstm_prof_bwd_chunkwise", "mlstm_prof_copy_lds",
@@ -573,3 +573,92 @@ def test_ungated_cell_only_on_the_fused_chunkwise_path():
     a.o_pre = None
     need = lib.mlstm_fwd_parallel_workspace_size(ctypes.byref(a))
     assert lib.mlstm_fwd_parallel(ctypes.byref(a), a._next(need), need, None) == NULLPTR
+
+
+SEGMENTS_HEADER = os.path.join(ROOT, "include", "mlstm_segments.h")
+
+
+def test_library_exports_every_segment_symbol():
+    lib = L.lib()
+    names = declared_functions(SEGMENTS_HEADER)
+    assert names == ["mlstm_segment_summary", "mlstm_segment_summary_workspace_size", "mlstm_state_combine"]
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _fake_addresses(start):
+    base = [start]
+
+    def take(nbytes):
+        p = base[0]
+        base[0] += (nbytes + 4095) // 4096 * 4096 + 4096
+        return p
+    return take
+
+
+def test_segment_summary_validation():
+    lib = L.lib()
+    take = _fake_addresses(0x7D0000000000)
+    B, H, T, K, V = 1, 2, 512, 128, 256
+    BH = B * H
+    a = L.SummaryArgs(B, H, T, K, V, L.MLSTM_BF16, take(BH * T * K * 2), take(BH * T * V * 2),
+                      take(BH * T * 4), take(BH * T * 4), take(BH * V * K * 4), take(BH * K * 4),
+                      take(BH * 4), take(BH * 8))
+    need = lib.mlstm_segment_summary_workspace_size(ctypes.byref(a), 128)
+    # the forward's fused layout with a local state for every chunk (4 here, not 3)
+    fwd = L.FwdArgs(B, H, T, K, V, L.MLSTM_BF16, *([0x1000] * 13))
+    assert need > L.chunkwise_workspace_bytes(fwd, 128)
+    ws = take(need)
+
+    def call(args, chunk=128, w=ws, nb=need):
+        return lib.mlstm_segment_summary(ctypes.byref(args), chunk, w, nb, None)
+
+    assert call(a, nb=need - 1) == WORKSPACE
+    assert call(a, w=None) == WORKSPACE
+    assert call(a, w=ws + 128) == MISALIGNED
+    assert call(a, chunk=192) == BAD_SHAPE           # 512 is not a multiple of 192
+    assert lib.mlstm_segment_summary_workspace_size(ctypes.byref(a), 192) == 0
+    assert call(a, chunk=100) == BAD_SHAPE
+    assert call(a, chunk=16384) == BAD_SHAPE
+    bad = [("dtype", L.MLSTM_FP32, UNSUPPORTED), ("dtype", 7, BAD_DTYPE), ("d_v", 192, UNSUPPORTED),
+           ("d_qk", 96, UNSUPPORTED), ("H", 0, BAD_SHAPE), ("T", -64, BAD_SHAPE),
+           ("G_out", None, NULLPTR), ("k", None, NULLPTR), ("G_out", a.G_out + 4, MISALIGNED),
+           ("C_out", a.C_out + 8, MISALIGNED), ("n_out", a.C_out, ALIAS), ("C_out", a.k, ALIAS)]
+    for field, value, code in bad:
+        b = L.SummaryArgs.from_buffer_copy(a)
+        setattr(b, field, value)
+        assert call(b) == code, field
+    assert call(a, w=a.v) == ALIAS                    # workspace over an input
+    assert lib.mlstm_segment_summary(None, 128, ws, need, None) == NULLPTR
+    e = L.SummaryArgs.from_buffer_copy(a)
+    e.T = 0
+    assert lib.mlstm_segment_summary_workspace_size(ctypes.byref(e), 128) == 0
+
+
+def test_state_combine_validation():
+    lib = L.lib()
+    take = _fake_addresses(0x7C8000000000)
+    B, H, K, V = 2, 3, 64, 128
+    BH = B * H
+    P = 3
+    c = L.CombineArgs(B, H, K, V, P, take(BH * V * K * 4), take(BH * K * 4), take(BH * 4),
+                      take(P * BH * V * K * 4), take(P * BH * K * 4), take(P * BH * 4), take(P * BH * 8),
+                      take(BH * V * K * 4), take(BH * K * 4), take(BH * 4))
+    bad = [("m0", None, NULLPTR), ("Gs", None, NULLPTR), ("C_out", None, NULLPTR),
+           ("Gs", c.Gs + 4, MISALIGNED), ("ms", c.ms + 2, MISALIGNED), ("Cs", c.Cs + 4, MISALIGNED),
+           ("n_out", c.n_out + 8, MISALIGNED), ("d_v", 0, BAD_SHAPE), ("d_qk", 66, BAD_SHAPE),
+           ("count", -1, BAD_SHAPE), ("B", -1, BAD_SHAPE), ("C_out", c.C0, ALIAS),
+           ("C_out", c.Cs + 64, ALIAS), ("m_out", c.n_out, ALIAS), ("n_out", c.Gs, ALIAS),
+           # the third summary of the stack lies over C_out
+           ("C_out", c.Cs + 2 * BH * V * K * 4, ALIAS)]
+    for field, value, code in bad:
+        d = L.CombineArgs.from_buffer_copy(c)
+        setattr(d, field, value)
+        assert lib.mlstm_state_combine(ctypes.byref(d), None) == code, field
+    d = L.CombineArgs.from_buffer_copy(c)
+    d.C0 = None                                       # n0, m0 still given: all three or none
+    assert lib.mlstm_state_combine(ctypes.byref(d), None) == NULLPTR
+    d = L.CombineArgs.from_buffer_copy(c)
+    d.count, d.Cs, d.ns = 1, None, None               # summaries are required when count > 0
+    assert lib.mlstm_state_combine(ctypes.byref(d), None) == NULLPTR
+    assert lib.mlstm_state_combine(None, None) == NULLPTR
