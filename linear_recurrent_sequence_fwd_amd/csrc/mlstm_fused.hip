@@ -11,17 +11,20 @@
 //                      the last): the chunk's own end state from an empty
 //                      state, C~loc = sum of decayed K^T diag(w) V over its
 //                      tiles on MFMA; a loader wave streams the tiles into
-//                      double-buffered LDS with direct-to-LDS loads.
+//                      triple-buffered LDS with direct-to-LDS loads.
 //   seg_combine_kernel folds the chunks' local end states in order into the
 //                      start state of every chunk (elementwise, float32).
+//                      With every chunk's local state and the fold started
+//                      from the empty state, the two kernels also give a
+//                      segment's summary (launch_summary).
 //   out_kernel_fused   one workgroup per (head, 128 value columns, chunk).
 //                      Holds its 128 x d_qk slice of C~ (float32) in MFMA
 //                      accumulators, split over its waves by halves of d_qk
 //                      and 32-column groups, and walks the chunk in 64-token
 //                      tiles. Per tile: Q K^T and Q C~^T on MFMA (C~ as bf16
 //                      hi + lo; partial sums over each half of d_qk,
-//                      exchanged through LDS), q . n~ in float32 on the
-//                      vector ALU, the state update C~ <- a C~ + K^T diag(w) V
+//                      exchanged through LDS), q . n~ on MFMA (n~ as three
+//                      bf16 terms), the state update C~ <- a C~ + K^T diag(w) V
 //                      on MFMA and the same for n~ (three MFMA columns
 //                      carrying the weights as three bf16 terms), decay mask
 //                      and stabiliser in registers, P V on MFMA, normaliser
