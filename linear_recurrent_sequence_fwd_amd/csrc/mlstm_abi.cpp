@@ -810,6 +810,7 @@ mlstm_impl::GemmLaunch gemm_launch(const mlstm_gemm_args* g) {
 int validate_block(const mlstm_block_params* p, int64_t B, int64_t T) {
   if (!p) return fail(MLSTM_ERR_NULLPTR, "params is NULL");
   if (B < 1 || T < 0) return fail(MLSTM_ERR_BAD_SHAPE, "need B >= 1 and T >= 0");
+  if (B > 65535) return fail(MLSTM_ERR_UNSUPPORTED, "B above 65535");
   const int64_t D = p->D, E = 2 * p->D;
   if (D < 64 || D % 64) return fail(MLSTM_ERR_BAD_SHAPE, "D must be a positive multiple of 64");
   if (D > 8192) return fail(MLSTM_ERR_UNSUPPORTED, "D above 8192");

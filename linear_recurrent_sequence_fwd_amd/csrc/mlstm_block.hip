@@ -404,21 +404,23 @@ struct GnDev {
   __bf16* y;              // [B T][E]
   int64_t T, rows;        // rows = B T H
   int H, dv;
+  float inv_dv;           // 1 / dv (exact for a power of two)
   float eps;
 };
 
-// One wave per (batch entry, token, head), heads fastest: the head's d_v
-// outputs normalised over d_v, then (. w + b + skip xc) sigmoid(z). A lane
-// takes pieces of eight channels; every load of the wave (h, xc, z and the
-// three parameter vectors) is issued before the first reduction.
+// One wave per (batch entry, token, head): the head's d_v outputs normalised
+// over d_v, then (. w + b + skip xc) sigmoid(z). Grid (token, group of four
+// heads, batch entry), a wave per head of the group, so that every index is
+// a block or wave number (no division). A lane takes pieces of eight
+// channels; every load of the wave (h, xc, z and the three parameter
+// vectors) is issued before the first reduction.
 template <int CH>
 __global__ __launch_bounds__(256) void groupnorm_gate_kernel(GnDev a) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.rows) return;
+  const int hh = (int)blockIdx.y * 4 + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  if (hh >= a.H) return;
   const int lane = threadIdx.x & 63;
-  const int hh = (int)(row % a.H);
-  const int64_t bt = row / a.H;               // b T + t
-  const int64_t b = bt / a.T, t = bt - b * a.T;
+  const int64_t b = blockIdx.z, t = blockIdx.x;
+  const int64_t bt = b * a.T + t;
   const __bf16* hr = a.h + ((b * a.H + hh) * a.T + t) * a.dv;
   const int64_t E = (int64_t)a.H * a.dv;
   const int64_t col0 = (int64_t)hh * a.dv;
@@ -446,7 +448,7 @@ __global__ __launch_bounds__(256) void groupnorm_gate_kernel(GnDev a) {
   for (int c = 0; c < CH; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) s += (float)hv[c][e];
-  const float mean = wave_sum(s) / (float)a.dv;
+  const float mean = wave_sum(s) * a.inv_dv;
   float q = 0.f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
@@ -459,7 +461,7 @@ __global__ __launch_bounds__(256) void groupnorm_gate_kernel(GnDev a) {
       }
     }
   }
-  const float rstd = 1.f / sqrtf(wave_sum(q) / (float)a.dv + a.eps);
+  const float rstd = 1.f / sqrtf(wave_sum(q) * a.inv_dv + a.eps);
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int col = 8 * (lane + 64 * c);
@@ -564,8 +566,9 @@ hipError_t launch_groupnorm_gate(const GnLaunch& g, hipStream_t s) {
   a.y = static_cast<__bf16*>(g.y);
   a.T = g.T; a.rows = g.B * g.T * g.H;
   a.H = (int)g.H; a.dv = (int)g.dv;
+  a.inv_dv = 1.f / (float)g.dv;
   a.eps = g.eps;
-  const dim3 grid((unsigned)((a.rows + 3) / 4)), block(256);
+  const dim3 grid((unsigned)g.T, (unsigned)((g.H + 3) / 4), (unsigned)g.B), block(256);
   if (g.dv <= 512) hipLaunchKernelGGL(groupnorm_gate_kernel<1>, grid, block, 0, s, a);
   else if (g.dv <= 1024) hipLaunchKernelGGL(groupnorm_gate_kernel<2>, grid, block, 0, s, a);
   else hipLaunchKernelGGL(groupnorm_gate_kernel<4>, grid, block, 0, s, a);
