@@ -537,6 +537,9 @@ def test_block_pointer_and_workspace_checks():
     assert lib.mlstm_block_fwd_workspace_size(None, B, T, 64) == 0
     offs = (ctypes.c_size_t * 10)()
     assert lib.mlstm_block_workspace_offsets(ctypes.byref(p), B, 0, 64, offs) == BAD_SHAPE
+    # batch entries index the group norm's grid in its third dimension (at most 65535)
+    h, xc, xup, y = take(8), take(8), take(8), take(8)
+    assert lib.mlstm_block_groupnorm_gate(ctypes.byref(p), 65536, 1, h, xc, xup, y, None) == UNSUPPORTED
 
 
 def test_gemm_and_layernorm_validation():
