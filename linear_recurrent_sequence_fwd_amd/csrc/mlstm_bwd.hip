@@ -612,8 +612,8 @@ struct RsLds {
   static constexpr int P = kTile + PAD;
   static constexpr int oG = 0;                                   // g tile [64 tokens][64 v]
   static constexpr int oQ = oG + kTile * P * (int)sizeof(TI);    // w q tile [64 tokens][64 d]
-  static constexpr int oF = oQ + kTile * P * (int)sizeof(TI);    // float: w [64], wdz [64], ep [4][64]
-  static constexpr int bytes = oF + 6 * kTile * 4;
+  static constexpr int oF = oQ + kTile * P * (int)sizeof(TI);    // float: w [256], wdz [256], ep [4][64]
+  static constexpr int bytes = oF + (2 * kThreads + 4 * kTile) * 4;
 };
 
 // One workgroup per (head, 64 v x 64 d tile, chunk c), four waves of 32 x 32:
@@ -622,8 +622,11 @@ struct RsLds {
 // w_s = exp(r_first - r_s) <= 1 (its log scale is -r_first), float32, into
 // the slot of chunk c - 1 (chunk 0's, wanted for the initial state's
 // gradient only, into L0). The normaliser part (v-tile-0 workgroups) is the
-// same sum with g_s replaced by dz_s, on the vector ALU. Chunks are
-// independent here; bwd_fold_kernel chains them.
+// same sum with g_s replaced by dz_s, on the vector ALU from the staged q.
+// Chunks are independent here; bwd_fold_kernel chains them. The weights of
+// 256 tokens are formed in one pass, and each 64-token block's g and q are
+// loaded into registers while the previous block's products run, so a block
+// costs no memory latency of its own.
 template <typename TI, int K>
 __global__ __launch_bounds__(kThreads) void bwd_local_kernel(BwdArgs a) {
   using L = RsLds<TI, K>;
@@ -633,8 +636,8 @@ __global__ __launch_bounds__(kThreads) void bwd_local_kernel(BwdArgs a) {
   TI* sG = reinterpret_cast<TI*>(smem + L::oG);
   TI* sQ = reinterpret_cast<TI*>(smem + L::oQ);
   float* s_w = reinterpret_cast<float*>(smem + L::oF);
-  float* s_wdz = s_w + 64;
-  float* s_ep = s_w + 128;
+  float* s_wdz = s_w + kThreads;
+  float* s_ep = s_wdz + kThreads;
 
   const int64_t T = a.T, BH = a.BH, V = a.V;
   const int ntile = KT * (int)(V / 64);
@@ -662,47 +665,59 @@ __global__ __launch_bounds__(kThreads) void bwd_local_kernel(BwdArgs a) {
 #pragma unroll
     for (int y = 0; y < 2; ++y) lacc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
   float le = 0.f;
-  for (int jb = 0; jb < Lc; jb += kTile) {
+  // this thread's staging items: item it = tid + kThreads u is row it / 8,
+  // 16-byte piece it % 8 of the block's g and q tiles (rows past the chunk: zero)
+  constexpr int kItems = kTile * 8 / kThreads;
+  vec8<TI> gr[kItems], qr[kItems];
+  auto load_block = [&](int jb) {
     const int64_t tb = t0 + jb;
     const int nv = min(kTile, Lc - jb);
-    if (jb > 0) __syncthreads();   // previous block's tiles and weights consumed
-    if (tid < kTile) {
+#pragma unroll
+    for (int u = 0; u < kItems; ++u) {
+      const int it = tid + kThreads * u, row = it >> 3, cv = it & 7;
+      gr[u] = qr[u] = zero_v8<TI>();
+      if (row < nv) {
+        gr[u] = load8(Gg + (tb + row) * V + 8 * cv);
+        qr[u] = load8(qg + (tb + row) * K + 8 * cv);
+      }
+    }
+  };
+  load_block(0);
+  for (int jb = 0; jb < Lc; jb += kTile) {
+    const int nv = min(kTile, Lc - jb);
+    const int sb = jb % kThreads;   // the block's first token within its weight pass
+    if (jb > 0) {
+      __syncthreads();   // the previous block's reads of the tiles and weights are done
+      if (e_tile && tid < kTile) le += s_ep[tid] + s_ep[64 + tid] + s_ep[128 + tid] + s_ep[192 + tid];
+    }
+    if (sb == 0) {   // the weights of the next kThreads tokens, one per thread
+      const int64_t tt = t0 + jb + tid;
       float wt = 0.f, wdz = 0.f;
-      if (tid < nv && a.gb.rs[bh * T + tb + tid] < 0) {
-        const double r = row_stab(a, bh, tb + tid, has_state, m_prev, nullptr);
+      if (jb + tid < Lc && a.gb.rs[bh * T + tt] < 0) {
+        const double r = row_stab(a, bh, tt, has_state, m_prev, nullptr);
         wt = expf((float)(r_first - r));
-        wdz = wt * a.dz[bh * T + tb + tid];
+        wdz = wt * a.dz[bh * T + tt];
       }
       s_w[tid] = wt;
       s_wdz[tid] = wdz;
+      __syncthreads();
     }
-    __syncthreads();
     // stage w g[tokens][64 v] and q[tokens][64 d]. The weight goes on g: a
     // rounding of w_s g_s perturbs each term in proportion to itself, so the
     // adjoint's products with later keys (which can cancel strongly) keep
     // their accuracy; q stays exact.
-    for (int it = tid; it < kTile * 8; it += kThreads) {
-      const int row = it >> 3, cv = it & 7;
-      vec8<TI> gv = zero_v8<TI>(), qv = zero_v8<TI>();
-      if (row < nv) {
-        const vec8<TI> g8 = load8(Gg + (tb + row) * V + 8 * cv);
-        qv = load8(qg + (tb + row) * K + 8 * cv);
-        const float wt = s_w[row];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) gv[e] = from_f32<TI>(to_f32(g8[e]) * wt);
-      }
+    for (int u = 0; u < kItems; ++u) {
+      const int it = tid + kThreads * u, row = it >> 3, cv = it & 7;
+      const float wt = s_w[sb + row];
+      vec8<TI> gv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gv[e] = from_f32<TI>(to_f32(gr[u][e]) * wt);
       store8(sG + row * P + 8 * cv, gv);
-      store8(sQ + row * P + 8 * cv, qv);
+      store8(sQ + row * P + 8 * cv, qr[u]);
     }
-    if (e_tile) {   // normaliser part: four threads per d, 16 tokens each
-      const int d = tid & 63, part = tid >> 6;
-      float sum = 0.f;
-      for (int row = 16 * part; row < 16 * part + 16; ++row)
-        if (row < nv) sum += s_wdz[row] * to_f32(qg[(tb + row) * K + d]);
-      s_ep[part * 64 + d] = sum;
-    }
+    if (jb + kTile < Lc) load_block(jb + kTile);   // in flight during this block's products
     __syncthreads();
-    if (e_tile && tid < kTile) le += s_ep[tid] + s_ep[64 + tid] + s_ep[128 + tid] + s_ep[192 + tid];
 #pragma unroll
     for (int kk = 0; kk < kTile; kk += 32) {
       vec8<TI> A[2], B[2];
@@ -715,6 +730,17 @@ __global__ __launch_bounds__(kThreads) void bwd_local_kernel(BwdArgs a) {
 #pragma unroll
         for (int y = 0; y < 2; ++y) lacc[x][y] = mma32(A[x], B[y], lacc[x][y]);
     }
+    if (e_tile) {   // normaliser part from the staged q: four threads per d, 16 tokens each
+      const int d = tid & 63, part = tid >> 6;
+      float sum = 0.f;
+      for (int row = 16 * part; row < 16 * part + 16; ++row)
+        if (row < nv) sum += s_wdz[sb + row] * to_f32(sQ[row * P + d]);
+      s_ep[part * 64 + d] = sum;
+    }
+  }
+  if (e_tile) {
+    __syncthreads();
+    if (tid < kTile) le += s_ep[tid] + s_ep[64 + tid] + s_ep[128 + tid] + s_ep[192 + tid];
   }
   float* dst = c > 0 ? a.Es + (bh * a.Nc + c - 1) * V * K : a.L0 + bh * V * K;
   float* edst = c > 0 ? a.es + (bh * a.Nc + c - 1) * K : a.L0e + bh * K;
