@@ -253,10 +253,12 @@ struct SegArgs {
   int64_t T, Nt, V, BH;      // Nt = number of 64-token tiles
   int TPS;                   // tiles per chunk
   int S;                     // chunks
+  int fold_here;             // 1: the output kernel folds the chunk start states itself (no fold kernel)
   float o_bias;              // 0, or -inf with o null: no output gate (sigmoid(o~) = 1)
 };
 
 constexpr int kOutWaves = 8;   // output kernel: two halves of d_qk x four 32-column groups, two waves per SIMD
+constexpr int kFoldHere = 7;   // most local states an output workgroup folds itself
 
 // A 64-row bf16 tile (rows of E elements at a stride of RS elements in global
 // memory; rows past `last` repeat row `last`) is copied into LDS rows of pitch
@@ -447,19 +449,23 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
     ninit = a.C0 ? a.n0 + bh * K : nullptr;
     m_start = a.C0 ? (double)a.m0[bh] : 0.0;
     has_state = a.C0 != nullptr;
-  } else {
+  } else if (!a.fold_here) {
     const int64_t sidx = bh * nseg1 + seg - 1;
     Cinit = a.Cseg + sidx * V * K;
     ninit = a.nseg + sidx * K;
     m_start = a.mstart[sidx];
     has_state = true;
+  } else {
+    has_state = true;
   }
+  // the wave's share of a [V][K] state and of its n~ [K]
+  auto state_at = [&](const float* C, int x, int cv) {
+    return *reinterpret_cast<const f32x4*>(C + (vcol0 + 32 * cg + 16 * cv + i) * K + state_k0(kxg(x), g));
+  };
 #pragma unroll
   for (int x = 0; x < KXH; ++x)
 #pragma unroll
-    for (int cv = 0; cv < 2; ++cv)
-      Ct[x][cv] = Cinit ? *reinterpret_cast<const f32x4*>(Cinit + (vcol0 + 32 * cg + 16 * cv + i) * K + state_k0(kxg(x), g))
-                        : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cv = 0; cv < 2; ++cv) Ct[x][cv] = Cinit ? state_at(Cinit, x, cv) : f32x4{0.f, 0.f, 0.f, 0.f};
   // normaliser tiles of the wave: local tiles KXN cg .. + KXN - 1 of its half
   auto nx = [&](int x) { return KXN * cg + x; };
   auto n_live = [&](int x) { return nx(x) < KXH; };
@@ -467,6 +473,56 @@ __device__ __forceinline__ void out_body(const SegArgs& a, char* lq, char* lk, c
   for (int x = 0; x < KXN; ++x)
     Nacc[x] = (ninit && i == 0 && n_live(x)) ? *reinterpret_cast<const f32x4*>(ninit + state_k0(kxg(nx(x)), g))
                                             : f32x4{0.f, 0.f, 0.f, 0.f};
+  if (seg > 0 && a.fold_here) {
+    // The start state of chunk seg folded here from the local end states of
+    // chunks 0..seg-1 (and the initial state), instead of by the fold
+    // kernel. The stabiliser takes the fold's own float64 chain, m' =
+    // max(m + G_s, mloc_s) (0 for an all-zero state); unrolled, local state s
+    // enters with exp(mloc_s + G_{s+1} + ... + G_{seg-1} - m) and the initial
+    // state with exp(m0 + G_0 + ... + G_{seg-1} - m), factors of at most 1.
+    const int64_t sbase = bh * nseg1;
+    double m = a.C0 ? (double)a.m0[bh] : 0.0;
+    for (int s = 0; s < seg; ++s) {
+      const double G = a.Gseg[sbase + s];
+      const double mn = fmax(G == -INFINITY ? -INFINITY : m + G, a.mloc[sbase + s]);
+      m = mn == -INFINITY ? 0.0 : mn;
+    }
+    m_start = m;
+    double tail = 0.0;   // sum of G over the chunks after s
+    for (int s = seg - 1; s >= 0; --s) {
+      const double ml = a.mloc[sbase + s];
+      const float c = (ml == -INFINITY || tail == -INFINITY) ? 0.f : exp_f64arg(ml + tail - m);
+      if (c != 0.f) {
+        const float* Cl = a.Cseg + (sbase + s) * V * K;
+        f32x4 y[KXH][2];
+#pragma unroll
+        for (int x = 0; x < KXH; ++x)
+#pragma unroll
+          for (int cv = 0; cv < 2; ++cv) y[x][cv] = state_at(Cl, x, cv);
+#pragma unroll
+        for (int x = 0; x < KXH; ++x)
+#pragma unroll
+          for (int cv = 0; cv < 2; ++cv) Ct[x][cv] += c * y[x][cv];
+        const float* nl = a.nseg + (sbase + s) * K;
+#pragma unroll
+        for (int x = 0; x < KXN; ++x)
+          if (i == 0 && n_live(x)) Nacc[x] += c * *reinterpret_cast<const f32x4*>(nl + state_k0(kxg(nx(x)), g));
+      }
+      tail += a.Gseg[sbase + s];
+    }
+    if (a.C0 && tail != -INFINITY && a.m0[bh] != -INFINITY) {
+      const float c = exp_f64arg((double)a.m0[bh] + tail - m);
+      const float* C0 = a.C0 + bh * V * K;
+#pragma unroll
+      for (int x = 0; x < KXH; ++x)
+#pragma unroll
+        for (int cv = 0; cv < 2; ++cv) Ct[x][cv] += c * state_at(C0, x, cv);
+      const float* n0 = a.n0 + bh * K;
+#pragma unroll
+      for (int x = 0; x < KXN; ++x)
+        if (i == 0 && n_live(x)) Nacc[x] += c * *reinterpret_cast<const f32x4*>(n0 + state_k0(kxg(nx(x)), g));
+    }
+  }
   // zero rows of the weight and normaliser operands, both halves
   for (int b = 0; b < 2; ++b) {
     const TileBuf tb = tile_buf(b);
@@ -1488,17 +1544,24 @@ hipError_t run_seg(const FwdLaunch& f, const GateBuffers& gb, const SegStates& s
   a.C_out = f.C_out; a.n_out = f.n_out; a.m_out = f.m_out;
   a.T = f.T; a.Nt = f.Nc; a.V = f.V; a.BH = f.BH;
   a.TPS = ss.TPS; a.S = ss.S;
+  a.fold_here = 0;
   const int64_t nvb = f.V / kVB;
   if (ss.S > 1) {
     mark_before(f.marks, K_STATE, s);
     hipLaunchKernelGGL((local_kernel<K>), dim3((unsigned)(f.BH * nvb * (ss.S - 1))), dim3(64 * (LocWaves<K>::value + 1)), 0, s, a);
-    CombineArgs c;
-    c.C0 = f.C0; c.n0 = f.n0; c.m0 = f.m0;
-    c.Cseg = ss.C; c.nseg = ss.n; c.mloc = ss.mloc; c.mstart = ss.mstart; c.Gseg = ss.G;
-    c.V = f.V; c.K = K; c.BH = f.BH; c.S = ss.S;
-    const int64_t units = f.V * K / 4 + K / 4;
-    const int64_t blocks = (units + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(f.BH * blocks)), dim3(kThreads), 0, s, c);
+    // With few chunks each output workgroup folds its own start state (its
+    // slice of at most kFoldHere local states, read from the cache); beyond
+    // that the fold kernel writes the start states once.
+    a.fold_here = ss.S - 1 <= kFoldHere ? 1 : 0;
+    if (!a.fold_here) {
+      CombineArgs c;
+      c.C0 = f.C0; c.n0 = f.n0; c.m0 = f.m0;
+      c.Cseg = ss.C; c.nseg = ss.n; c.mloc = ss.mloc; c.mstart = ss.mstart; c.Gseg = ss.G;
+      c.V = f.V; c.K = K; c.BH = f.BH; c.S = ss.S;
+      const int64_t units = f.V * K / 4 + K / 4;
+      const int64_t blocks = (units + kThreads - 1) / kThreads;
+      hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)(f.BH * blocks)), dim3(kThreads), 0, s, c);
+    }
     mark_after(f.marks, K_STATE, s);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -253,6 +253,34 @@ def test_extreme_preactivations_fused(K, V, T):
         assert ec <= TOL["bf16"] and en <= TOL["bf16"], f"chunk {chunk}"
 
 
+@pytest.mark.parametrize("chunk", [64, 128, 192])
+def test_extreme_preactivations_fused_with_state(chunk):
+    """The fused path from a given initial state under resetting and
+    saturating gates: at chunk 64 the fold kernel writes the chunk start
+    states (fifteen local states), at 128 (seven, the most) and 192 (five)
+    each output workgroup folds its own start state from the local states
+    and the initial state."""
+    M = _lib()
+    K, V, T = 128, 256, 1000
+    say(f"extreme preactivations fused K={K} V={V} T={T} chunk={chunk} with state")
+    rng = np.random.default_rng(21)
+    B, H = 1, 2
+    x = make_fwd_inputs(B, H, T, K, V, "bf16", seed=22)
+    x["i_pre"] = rng.choice([-100.0, 100.0, 0.0, 2.0, -3.0], size=(B, H, T)).astype(np.float32)
+    x["f_pre"] = rng.choice([-100.0, 100.0, np.inf, -np.inf, 3.0, 3.0, 3.0],
+                            size=(B, H, T)).astype(np.float32)
+    st = make_state(B, H, K, V, seed=23)
+    h_ref, st_ref = oracle(x, C0=st["C"], n0=st["n"], m0=st["m"])
+    d = dev_inputs(x)
+    h, sto = run_chunkwise(M, d, chunk, C0=torch.from_numpy(st["C"]).cuda(),
+                           n0=torch.from_numpy(st["n"]).cuda(), m0=torch.from_numpy(st["m"]).cuda(),
+                           return_state=True)
+    assert bool(torch.isfinite(h.float()).all())
+    assert rel_err(host(h), h_ref) <= TOL["bf16"]
+    ec, en = state_err(sto, st_ref)
+    assert ec <= TOL["bf16"] and en <= TOL["bf16"]
+
+
 def test_empty_sequence_copies_state():
     M = _lib()
     say("T=0")
