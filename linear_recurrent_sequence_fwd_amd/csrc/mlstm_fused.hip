@@ -259,6 +259,7 @@ struct SegArgs {
 
 constexpr int kOutWaves = 8;   // output kernel: two halves of d_qk x four 32-column groups, two waves per SIMD
 constexpr int kFoldHere = 7;   // most local states an output workgroup folds itself
+constexpr int kFoldMinTiles = 8;   // fewest 64-token tiles per chunk for that fold
 
 // A 64-row bf16 tile (rows of E elements at a stride of RS elements in global
 // memory; rows past `last` repeat row `last`) is copied into LDS rows of pitch
@@ -1549,10 +1550,14 @@ hipError_t run_seg(const FwdLaunch& f, const GateBuffers& gb, const SegStates& s
   if (ss.S > 1) {
     mark_before(f.marks, K_STATE, s);
     hipLaunchKernelGGL((local_kernel<K>), dim3((unsigned)(f.BH * nvb * (ss.S - 1))), dim3(64 * (LocWaves<K>::value + 1)), 0, s, a);
-    // With few chunks each output workgroup folds its own start state (its
-    // slice of at most kFoldHere local states, read from the cache); beyond
-    // that the fold kernel writes the start states once.
-    a.fold_here = ss.S - 1 <= kFoldHere ? 1 : 0;
+    // With few, long chunks each output workgroup folds its own start state
+    // (its slice of at most kFoldHere local states, read from the cache);
+    // otherwise the fold kernel writes the start states once. Each local
+    // state costs the prologue about one memory latency, which a chunk walk
+    // of fewer than kFoldMinTiles tiles does not win back (measured at
+    // d_qk = d_v = 128, four tiles and seven states: 1.7 us slower than the
+    // fold kernel; at d_qk = 256, d_v = 512, sixteen tiles: 4.5 us faster).
+    a.fold_here = (ss.S - 1 <= kFoldHere && ss.TPS >= kFoldMinTiles) ? 1 : 0;
     if (!a.fold_here) {
       CombineArgs c;
       c.C0 = f.C0; c.n0 = f.n0; c.m0 = f.m0;
