@@ -42,8 +42,11 @@
 //   bwd_dkv_kernel    per (head, 64-key tile): the end adjoint's term, then
 //                     the chunk's later query tiles: S = Q K^T, G V^T, and
 //                     dk += (P o (G V^T + dz))^T Q, dv += (P o S)^T G
-//   bwd_gate_kernel   per head: the forget-gate suffix sums and the
-//                     initial-state stabiliser gradient
+//   bwd_gate_map_kernel, bwd_gate_kernel
+//                     per (head, chunk): the forget-gate suffix sums as a
+//                     reverse scan of affine maps (each chunk's map, then
+//                     the later chunks' maps composed into the run entering
+//                     the chunk), and the initial-state stabiliser gradient
 //
 // Operand fragments: every product is a sequence of 16x16x32 steps in which
 // lane (i, g) of the wave supplies A[i][8g .. 8g+7] and B[i][8g .. 8g+7]
@@ -1136,32 +1139,43 @@ __global__ __launch_bounds__(kBT) void bwd_dkv_kernel(BwdArgs a) {
 // end by an affine map c -> alpha c + beta (alpha = 0 where a zero forget
 // gate blocks the flow); a scan of the composed maps over the threads gives
 // every run its inflow. Float64 sums. Also dm0 = <dC~0, C~0> + dn~0 . n~0.
-__global__ __launch_bounds__(kThreads) void bwd_gate_kernel(BwdArgs a) {
-  __shared__ double s_al[kThreads / 64], s_be[kThreads / 64];
-  __shared__ double s_red[kThreads / 64];
-  const int64_t bh = blockIdx.x;
-  const int64_t T = a.T;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int64_t E = (T + kThreads - 1) / kThreads;
-  const int64_t run_idx = kThreads - 1 - tid;
-  const int64_t lo = min(run_idx * E, T), hi = min(lo + E, T);
-  const float* fp = a.f_pre + bh * T;
-  const float* qd = a.qdq + bh * T;
-  const float* di = a.di + bh * T;
-  auto blocked = [&](int64_t l) { return fp[l] == -INFINITY || (l == 0 && a.zero_first); };
-  // the run's own map: inflow c at hi - 1 -> outflow at lo - 1
-  double be = 0.0, al = 1.0;
+// The forget-gate gradient needs, per token, run_l = 0 at a blocked token (a
+// zero forget gate, or the first token without an initial state) and
+// q.dq_l - di_l + run_{l+1} otherwise: a reverse scan over the sequence. A
+// stretch of tokens acts on the run entering at its end as x -> A x + B
+// (A = 0 once a token in it is blocked), and stretches compose. Both kernels
+// below take one workgroup per (head, chunk): the first stores each chunk's
+// map, the second composes the maps of the later chunks into the run
+// entering its chunk and writes df. The maps live in the end-adjoint
+// normaliser buffer, which the dk/dv kernel has finished with.
+struct RevMap {
+  double A, B;
+};
+
+__device__ __forceinline__ double* gate_maps(const BwdArgs& a) { return reinterpret_cast<double*>(a.es); }
+
+// The map of tokens [lo, hi) of one head (the entering run applied at hi - 1).
+__device__ __forceinline__ RevMap token_run_map(const BwdArgs& a, int64_t bh, int64_t lo, int64_t hi) {
+  const float* fp = a.f_pre + bh * a.T;
+  const float* qd = a.qdq + bh * a.T;
+  const float* di = a.di + bh * a.T;
+  RevMap m{1.0, 0.0};
   for (int64_t l = hi - 1; l >= lo; --l) {
-    const double v = (double)qd[l] - (double)di[l];
-    if (blocked(l)) {
-      al = 0.0;
-      be = 0.0;
+    if (fp[l] == -INFINITY || (l == 0 && a.zero_first)) {
+      m = RevMap{0.0, 0.0};
     } else {
-      be += v;   // (c -> al c + be) then + v
+      m.B += (double)qd[l] - (double)di[l];
     }
   }
-  // inclusive scan over threads (earlier threads = later runs): X_t = m_t o X_{t-1}
-  double A_ = al, B_ = be;
+  return m;
+}
+
+// Scan of the threads' maps within the workgroup, thread 0 holding the
+// latest stretch: returns the composition of the threads before this one
+// (the later stretches) and, in *total, the whole workgroup's map.
+__device__ __forceinline__ RevMap rev_scan(RevMap m, RevMap* total, double* s_a, double* s_b) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  double A_ = m.A, B_ = m.B;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const double ao = __shfl_up(A_, d, 64), bo = __shfl_up(B_, d, 64);
@@ -1170,42 +1184,111 @@ __global__ __launch_bounds__(kThreads) void bwd_gate_kernel(BwdArgs a) {
       A_ = A_ * ao;
     }
   }
-  if (lane == 63) { s_al[w] = A_; s_be[w] = B_; }
+  if (lane == 63) { s_a[w] = A_; s_b[w] = B_; }
   __syncthreads();
-  // the composed map of all earlier waves (applied first)
-  double Aw = 1.0, Bw = 0.0;
+  double Aw = 1.0, Bw = 0.0;   // the waves before this one (later stretches), composed
   for (int q = 0; q < w; ++q) {
-    Bw = s_al[q] * Bw + s_be[q];
-    Aw = s_al[q] * Aw;
+    Bw = s_a[q] * Bw + s_b[q];
+    Aw = s_a[q] * Aw;
   }
-  // exclusive: the map of the threads before this one, applied to 0
   double Ae = __shfl_up(A_, 1, 64), Bx = __shfl_up(B_, 1, 64);
   if (lane == 0) { Ae = 1.0; Bx = 0.0; }
-  const double carry = Ae * Bw + Bx;   // (excl o earlier waves)(0)
-  (void)Aw;
-  double run = carry;
+  double At = 1.0, Bt = 0.0;
+  for (int q = 0; q < kThreads / 64; ++q) {
+    Bt = s_a[q] * Bt + s_b[q];
+    At = s_a[q] * At;
+  }
+  *total = RevMap{At, Bt};
+  return RevMap{Ae * Aw, Ae * Bw + Bx};
+}
+
+// This thread's tokens of chunk c: contiguous runs, thread 0 the last.
+__device__ __forceinline__ void chunk_run(const BwdArgs& a, int64_t c, int64_t* lo, int64_t* hi) {
+  const int64_t p0 = c * a.L, p1 = min(p0 + a.L, a.T);
+  const int64_t E = (p1 - p0 + kThreads - 1) / kThreads;
+  const int64_t run_idx = kThreads - 1 - threadIdx.x;
+  *lo = min(p0 + run_idx * E, p1);
+  *hi = min(*lo + E, p1);
+}
+
+__device__ __forceinline__ double block_sum(double s, double* s_red) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
+  __syncthreads();   // s_red free (earlier readers done)
+  if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  return s_red[0] + s_red[1] + s_red[2] + s_red[3];
+}
+
+__global__ __launch_bounds__(kThreads) void bwd_gate_map_kernel(BwdArgs a) {
+  __shared__ double s_a[kThreads / 64], s_b[kThreads / 64], s_red[kThreads / 64];
+  const int64_t bh = blockIdx.x / a.Nc, c = blockIdx.x % a.Nc;
+  int64_t lo, hi;
+  chunk_run(a, c, &lo, &hi);
+  RevMap tot;
+  rev_scan(token_run_map(a, bh, lo, hi), &tot, s_a, s_b);
+  // this chunk's share of sum(dC0 o C0) + sum(dn0 o n0), the initial
+  // stabiliser's gradient (0 without an initial state)
+  double s = 0.0;
+  if (a.dm0 && a.C0) {
+    const int64_t VK = a.V * a.K, N = VK + a.K, per = (N + a.Nc - 1) / a.Nc;
+    const int64_t x1 = min((c + 1) * per, N);
+    for (int64_t x = c * per + threadIdx.x; x < x1; x += kThreads)
+      s += x < VK ? (double)a.dC0[bh * VK + x] * (double)a.C0[bh * VK + x]
+                  : (double)a.dn0[bh * a.K + x - VK] * (double)a.n0[bh * a.K + x - VK];
+  }
+  s = block_sum(s, s_red);
+  if (threadIdx.x == 0) {
+    double* gm = gate_maps(a) + (bh * a.Nc + c) * 4;
+    gm[0] = tot.A;
+    gm[1] = tot.B;
+    gm[2] = s;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void bwd_gate_kernel(BwdArgs a) {
+  __shared__ double s_a[kThreads / 64], s_b[kThreads / 64], s_red[kThreads / 64];
+  const int64_t bh = blockIdx.x / a.Nc, c = blockIdx.x % a.Nc;
+  const double* gm = gate_maps(a) + bh * a.Nc * 4;
+  // the run entering the chunk: chunks c+1 .. Nc-1, in contiguous groups per
+  // thread (thread 0 the last), composed and applied to 0
+  RevMap carry_tot;
+  {
+    const int64_t nq = a.Nc - 1 - c, E = (nq + kThreads - 1) / kThreads;
+    const int64_t run_idx = kThreads - 1 - threadIdx.x;
+    const int64_t q0 = c + 1 + min(run_idx * E, nq), q1 = c + 1 + min((run_idx + 1) * E, nq);
+    RevMap m{1.0, 0.0};
+    for (int64_t q = q1 - 1; q >= q0; --q) {
+      const double Aq = gm[q * 4], Bq = gm[q * 4 + 1];
+      m = RevMap{Aq * m.A, Aq * m.B + Bq};
+    }
+    rev_scan(m, &carry_tot, s_a, s_b);
+  }
+  const double carry_in = carry_tot.B;
+  __syncthreads();   // s_a, s_b reused
+  int64_t lo, hi;
+  chunk_run(a, c, &lo, &hi);
+  RevMap tot;
+  const RevMap ex = rev_scan(token_run_map(a, bh, lo, hi), &tot, s_a, s_b);
+  const float* fp = a.f_pre + bh * a.T;
+  const float* qd = a.qdq + bh * a.T;
+  const float* di = a.di + bh * a.T;
+  double run = ex.A * carry_in + ex.B;
   for (int64_t l = hi - 1; l >= lo; --l) {
     const double val = (double)qd[l] - (double)di[l] + run;
-    if (blocked(l)) {
-      a.df[bh * T + l] = 0.f;
+    if (fp[l] == -INFINITY || (l == 0 && a.zero_first)) {
+      a.df[bh * a.T + l] = 0.f;
       run = 0.0;
     } else {
-      a.df[bh * T + l] = (float)(val * (double)sigmoid(-fp[l]));
+      a.df[bh * a.T + l] = (float)(val * (double)sigmoid(-fp[l]));
       run = val;
     }
   }
-  if (a.dm0) {
+  if (a.dm0 && c == 0) {
     double s = 0.0;
-    if (a.C0) {
-      const int64_t VK = a.V * a.K;
-      for (int64_t x = tid; x < VK; x += kThreads) s += (double)a.dC0[bh * VK + x] * (double)a.C0[bh * VK + x];
-      for (int64_t x = tid; x < a.K; x += kThreads) s += (double)a.dn0[bh * a.K + x] * (double)a.n0[bh * a.K + x];
-    }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
-    if ((tid & 63) == 0) s_red[tid >> 6] = s;
-    __syncthreads();
-    if (tid == 0) a.dm0[bh] = (float)(s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+    for (int64_t q = threadIdx.x; q < a.Nc; q += kThreads) s += gm[q * 4 + 2];
+    s = block_sum(s, s_red);
+    if (threadIdx.x == 0) a.dm0[bh] = (float)s;
   }
 }
 
@@ -1241,7 +1324,8 @@ hipError_t run_bwd(const BwdLaunch& b, const BwdArgs& a, hipStream_t s) {
   mark_after(b.marks, B_DKV, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   mark_before(b.marks, B_GATE, s);
-  hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)b.BH), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(bwd_gate_map_kernel, dim3((unsigned)(b.BH * b.Nc)), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(bwd_gate_kernel, dim3((unsigned)(b.BH * b.Nc)), dim3(kThreads), 0, s, a);
   mark_after(b.marks, B_GATE, s);
   return hipGetLastError();
 }

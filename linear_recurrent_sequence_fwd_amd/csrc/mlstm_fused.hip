@@ -16,8 +16,13 @@
 //                      start state of every chunk (elementwise, float32).
 //                      With every chunk's local state and the fold started
 //                      from the empty state, the two kernels also give a
-//                      segment's summary (launch_summary).
+//                      segment's summary (launch_summary). With at most
+//                      seven local states of at least eight tiles each, the
+//                      output kernel folds instead (below) and this kernel
+//                      is not launched.
 //   out_kernel_fused   one workgroup per (head, 128 value columns, chunk).
+//                      Starts from its chunk's start state (read, or folded
+//                      from the earlier chunks' local states in its prologue).
 //                      Holds its 128 x d_qk slice of C~ (float32) in MFMA
 //                      accumulators, split over its waves by halves of d_qk
 //                      and 32-column groups, and walks the chunk in 64-token
