@@ -253,15 +253,17 @@ def test_extreme_preactivations_fused(K, V, T):
         assert ec <= TOL["bf16"] and en <= TOL["bf16"], f"chunk {chunk}"
 
 
+@pytest.mark.parametrize("K,V", [(64, 128), (128, 256), (256, 128)])
 @pytest.mark.parametrize("chunk", [64, 512, 1024])
-def test_extreme_preactivations_fused_with_state(chunk):
+def test_extreme_preactivations_fused_with_state(K, V, chunk):
     """The fused path from a given initial state under resetting and
-    saturating gates: at chunk 64 the fold kernel writes the chunk start
-    states (62 local states), at 512 (seven, the most, of eight tiles each)
-    and 1024 (three) each output workgroup folds its own start state from
-    the local states and the initial state."""
+    saturating gates, for each d_qk the fused kernels are built for: at
+    chunk 64 the fold kernel writes the chunk start states (62 local
+    states), at 512 (seven, the most, of eight tiles each) and 1024 (three)
+    each output workgroup folds its own start state from the local states
+    and the initial state."""
     M = _lib()
-    K, V, T = 128, 256, 4000
+    T = 4000
     say(f"extreme preactivations fused K={K} V={V} T={T} chunk={chunk} with state")
     rng = np.random.default_rng(21)
     B, H = 1, 2
